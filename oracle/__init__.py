@@ -1,0 +1,188 @@
+"""Plain CPU reference of attention-score KV-cache eviction (ctypes wrapper).
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The product path
+(``kv_cache_eviction_qk_amd``) never imports it and shares no code with it.
+
+The arithmetic lives in ``oracle.c`` (scalar loops, double precision); this
+file only marshals numpy arrays.  Build: ``gcc -O2 -shared`` into
+``liboracle.so`` next to the source.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_HDR = os.path.join(_HERE, "oracle.h")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+SUM, POOL, DROP, ACCUMULATE = 1, 2, 4, 8
+
+
+def build(force: bool = False) -> str:
+    newest = max(os.path.getmtime(_SRC), os.path.getmtime(_HDR))
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < newest:
+        tmp = _LIB + ".tmp"
+        # -ffp-contract=off keeps every product and sum a separate double rounding
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
+                               "-pthread", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("is_bf16", ctypes.c_int32),
+                ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("seq_len", ctypes.c_void_p),
+                ("pos", ctypes.c_void_p)]
+
+
+class Window(ctypes.Structure):
+    _fields_ = [("group", ctypes.c_int32), ("obs_window", ctypes.c_int32),
+                ("q", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("a", ctypes.c_void_p),
+                ("q_pos", ctypes.c_void_p), ("scale", ctypes.c_double)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32 = ctypes.c_int32
+        L.orc_lse_a.argtypes = [P, P, P, P, P, ctypes.c_int]
+        L.orc_score.argtypes = [P, P, ctypes.c_int, ctypes.c_int, P, P, P, P, P, ctypes.c_int]
+        L.orc_select.argtypes = [P, P, i32, i32, i32, i32, P, P]
+        L.orc_compact.argtypes = [P, P, i32, i32, P, P, P, P, i32, i32, P, P, P, P, i32, P]
+        L.orc_measure.argtypes = [P, P, P, i32, i32, P]
+        for f in (L.orc_lse_a, L.orc_score, L.orc_select, L.orc_compact, L.orc_measure):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def default_threads() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _p(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data
+
+
+def _cache(case: dict) -> Cache:
+    return Cache(case["B"], case["Hkv"], case["D"], case["max_blocks"], case["num_blocks"],
+                 1 if case["dtype"] == "bf16" else 0, _p(case["k_pool"]), _p(case["v_pool"]),
+                 _p(case["block_table"]), _p(case["seq_len"]), _p(case["pos"]))
+
+
+def _window(case: dict, lse=None, a=None) -> Window:
+    return Window(case["G"], case["W"], _p(case["q"]), _p(lse), _p(a), _p(case["q_pos"]),
+                  float(case["scale"]))
+
+
+def _mask(case: dict, units) -> Optional[np.ndarray]:
+    if units is None:
+        return None
+    m = np.zeros(case["B"] * case["Hkv"], np.uint8)
+    m[np.asarray(units, dtype=np.int64)] = 1
+    return m
+
+
+def lse_a(case: dict, want_a: bool = False, units=None, nthreads: int = 0):
+    """LSE [B,Hq,W] and attention output [B,Hq,W,D] of the window queries, in double."""
+    B, Hq, W, D = case["B"], case["Hkv"] * case["G"], case["W"], case["D"]
+    lse = np.zeros((B, Hq, W), np.float64)
+    a = np.zeros((B, Hq, W, D), np.float64) if want_a else None
+    c, w = _cache(case), _window(case)
+    rc = lib().orc_lse_a(ctypes.byref(c), ctypes.byref(w), _p(lse), _p(a), _p(_mask(case, units)),
+                         nthreads or default_threads())
+    assert rc == 0, rc
+    return lse, a
+
+
+def score(case: dict, lse32: np.ndarray, flags: int, pool_kernel: int = 1, a_enc=None,
+          prev_sum: Optional[np.ndarray] = None, units=None, nthreads: int = 0):
+    """Scores in double: dict with 'sum', 'pooled', 'drop' arrays [B,Hkv,max_slots]
+    (slots >= seq_len are NaN).  Returns None for the kinds not requested."""
+    B, Hkv, ms = case["B"], case["Hkv"], case["max_blocks"] * 16
+    shape = (B, Hkv, ms)
+    # the SUM buffer is needed internally for POOL too; only returned if asked
+    s = np.full(shape, np.nan) if flags & SUM else None
+    pl = np.full(shape, np.nan) if flags & POOL else None
+    dr = np.full(shape, np.nan) if flags & DROP else None
+    lse32 = np.ascontiguousarray(lse32, dtype=np.float32)
+    prev = None if prev_sum is None else np.ascontiguousarray(prev_sum, dtype=np.float32)
+    c, w = _cache(case), _window(case, lse32, a_enc)
+    rc = lib().orc_score(ctypes.byref(c), ctypes.byref(w), flags, pool_kernel, _p(prev), _p(s),
+                         _p(pl), _p(dr), _p(_mask(case, units)), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle score refused the arguments (rc={rc})")
+    return {"sum": s, "pooled": pl, "drop": dr}
+
+
+def select(scores32: np.ndarray, seq_len: np.ndarray, budget: int, recent: int):
+    """Victims [U, max_slots] (first n_victims valid) and n_victims [U] from fp32 scores."""
+    scores32 = np.ascontiguousarray(scores32, dtype=np.float32)
+    U = int(np.prod(seq_len.shape))
+    ms = scores32.size // U
+    seq = np.ascontiguousarray(seq_len, dtype=np.int32).reshape(-1)
+    vic = np.full((U, ms), -1, np.int32)
+    nv = np.zeros(U, np.int32)
+    rc = lib().orc_select(_p(scores32), _p(seq), U, ms, budget, recent, _p(vic), _p(nv))
+    if rc != 0:
+        raise ValueError(f"oracle select refused the arguments (rc={rc})")
+    return vic, nv
+
+
+def compact(case: dict, victims: np.ndarray, n_victims: np.ndarray,
+            score_row: Optional[np.ndarray] = None, free_list: Optional[np.ndarray] = None,
+            free_count: int = 0):
+    """Compacts a COPY of the case's cache.  Returns (new_case, free_list, free_count, stats)."""
+    new = dict(case)
+    for k in ("k_pool", "v_pool", "block_table", "seq_len", "pos"):
+        new[k] = case[k].copy()
+    U = case["B"] * case["Hkv"]
+    if free_list is None:
+        free_list = np.full(case["num_blocks"], -1, np.int32)
+    free_list = free_list.copy()
+    fc = np.array([free_count], np.int32)
+    stats = np.zeros(5, np.int64)
+    sc = None if score_row is None else np.ascontiguousarray(score_row, dtype=np.float32).copy()
+    elem = 2 if case["dtype"] == "bf16" else 4
+    rc = lib().orc_compact(_p(new["k_pool"]), _p(new["v_pool"]), elem, case["D"],
+                           _p(new["block_table"]), _p(new["seq_len"]), _p(new["pos"]), _p(sc), U,
+                           case["max_blocks"], _p(np.ascontiguousarray(victims, dtype=np.int32)),
+                           _p(np.ascontiguousarray(n_victims, dtype=np.int32)), _p(free_list),
+                           _p(fc), free_list.size, _p(stats))
+    if rc != 0:
+        raise ValueError(f"oracle compact refused the arguments (rc={rc})")
+    if sc is not None:
+        new["score_row"] = sc
+    return new, free_list, int(fc[0]), stats
+
+
+def measure(seq_len_before: np.ndarray, victims: np.ndarray, n_victims: np.ndarray) -> dict:
+    U = int(np.prod(seq_len_before.shape))
+    ms = victims.size // U
+    out = np.zeros(8, np.float64)
+    rc = lib().orc_measure(_p(np.ascontiguousarray(seq_len_before, dtype=np.int32).reshape(-1)),
+                           _p(np.ascontiguousarray(victims, dtype=np.int32)),
+                           _p(np.ascontiguousarray(n_victims, dtype=np.int32)), U, ms, _p(out))
+    assert rc == 0
+    keys = ("F_naive", "F_after", "frac_le_half_naive", "frac_le_half_after", "blocks_naive",
+            "blocks_after", "live_tokens", "blocks_freed")
+    return dict(zip(keys, out.tolist()))

@@ -1,0 +1,408 @@
+/*
+ * oracle.c -- plain CPU reference of attention-score KV-cache eviction.
+ *
+ * TEST INFRASTRUCTURE (see oracle.h).  Scalar loops, double precision, no
+ * blocking and no reordering beyond what each definition states.  Threads are
+ * used only across independent KV heads (b, h).
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- helpers */
+
+static double widen(const void *base, int is_bf16, int64_t idx) {
+  if (is_bf16) {
+    uint32_t u = (uint32_t)((const uint16_t *)base)[idx] << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+  }
+  return (double)((const float *)base)[idx];
+}
+
+/* Physical row of slot s of unit u ([VTOK] section 3.4, Eq. 2 with S = 16). */
+static int64_t phys_row(const orc_cache *c, int64_t u, int64_t s) {
+  return (int64_t)c->block_table[u * c->max_blocks + s / 16] * 16 + s % 16;
+}
+
+typedef void (*unit_fn)(void *ctx, int64_t unit);
+typedef struct {
+  unit_fn fn;
+  void *ctx;
+  const uint8_t *mask;
+  int64_t units;
+  int tid, nthreads;
+} par_job;
+
+static void *par_worker(void *arg) {
+  par_job *j = (par_job *)arg;
+  for (int64_t u = j->tid; u < j->units; u += j->nthreads)
+    if (!j->mask || j->mask[u]) j->fn(j->ctx, u);
+  return NULL;
+}
+
+static void parallel_units(unit_fn fn, void *ctx, int64_t units, const uint8_t *mask,
+                           int nthreads) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if (nthreads > units) nthreads = (int)(units > 0 ? units : 1);
+  pthread_t th[256];
+  par_job jobs[256];
+  for (int t = 0; t < nthreads; ++t) {
+    par_job j = {fn, ctx, mask, units, t, nthreads};
+    jobs[t] = j;
+  }
+  for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, par_worker, &jobs[t]);
+  par_worker(&jobs[0]);
+  for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
+}
+
+/* q.k_s of one window query row against slot s of unit u, d ascending. */
+static double dot_qk(const orc_cache *c, const orc_window *w, int64_t qrow, int64_t u, int64_t s) {
+  int64_t D = c->head_dim, prow = phys_row(c, u, s);
+  double acc = 0.0;
+  for (int64_t d = 0; d < D; ++d)
+    acc += widen(w->q, c->is_bf16, qrow * D + d) * widen(c->k_pool, c->is_bf16, prow * D + d);
+  return acc;
+}
+
+/* ---------------------------------------------- LSE and output (inputs) */
+/*
+ * The log-sum-exp of a query's scaled logits over the keys it attends, and the
+ * attention output a = sum_j p_j v_j.  A forward pass produces both ([DROP]
+ * Jargon, "Log-sum-exp"); here they are built from their definitions,
+ * max-shifted, to feed the scoring step.
+ */
+typedef struct {
+  const orc_cache *c;
+  const orc_window *w;
+  double *lse, *a;
+} lse_ctx;
+
+static void lse_unit(void *vctx, int64_t u) {
+  lse_ctx *x = (lse_ctx *)vctx;
+  const orc_cache *c = x->c;
+  const orc_window *w = x->w;
+  int64_t G = w->group, W = w->obs_window, D = c->head_dim;
+  int64_t b = u / c->kv_heads, h = u % c->kv_heads, Hq = (int64_t)c->kv_heads * G;
+  int64_t n = c->seq_len[u];
+  const int32_t *pos = c->pos + u * (int64_t)c->max_blocks * 16;
+  double *s = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  for (int64_t g = 0; g < G; ++g) {
+    int64_t hq = h * G + g;
+    for (int64_t wi = 0; wi < W; ++wi) {
+      int64_t qrow = (b * Hq + hq) * W + wi;
+      int32_t qp = w->q_pos[b * W + wi];
+      double mx = -INFINITY;
+      for (int64_t j = 0; j < n; ++j) {
+        if (pos[j] > qp) continue;
+        s[j] = w->scale * dot_qk(c, w, qrow, u, j);
+        if (s[j] > mx) mx = s[j];
+      }
+      double z = 0.0;
+      for (int64_t j = 0; j < n; ++j)
+        if (pos[j] <= qp) z += exp(s[j] - mx);
+      double lse = (z > 0.0) ? mx + log(z) : -INFINITY;
+      x->lse[qrow] = lse;
+      if (x->a) {
+        double *arow = x->a + qrow * D;
+        for (int64_t d = 0; d < D; ++d) arow[d] = 0.0;
+        if (z > 0.0) {
+          for (int64_t j = 0; j < n; ++j) {
+            if (pos[j] > qp) continue;
+            double p = exp(s[j] - lse);
+            int64_t prow = phys_row(c, u, j);
+            for (int64_t d = 0; d < D; ++d) arow[d] += p * widen(c->v_pool, c->is_bf16, prow * D + d);
+          }
+        }
+      }
+    }
+  }
+  free(s);
+}
+
+int orc_lse_a(const orc_cache *c, const orc_window *w, double *lse_out, double *a_out,
+              const uint8_t *unit_mask, int nthreads) {
+  if (!c || !w || !lse_out || !w->q || !w->q_pos || w->group < 1 || w->obs_window < 1) return -1;
+  lse_ctx ctx = {c, w, lse_out, a_out};
+  parallel_units(lse_unit, &ctx, (int64_t)c->batch * c->kv_heads, unit_mask, nthreads);
+  return 0;
+}
+
+/* ------------------------------------------------------------- scoring */
+/*
+ * Attention probability of window query (g, w) for slot j:
+ *     p = exp(scale * q.k_j - LSE)     if pos_j <= q_pos_w, else 0
+ * ([H2O] "The Existence of Heavy Hitters": A = softmax(QK^T / sqrt(d)); the
+ * LSE form of the same softmax per [DROP] Jargon).  The diagonal is included,
+ * so each row is the full softmax.
+ *
+ * SUM: S_j = sum_w sum_g p  -- the accumulated attention of [H2O]
+ *   "Formulating Cumulative Attention Scores", summed over the query heads of
+ *   the KV head's GQA group ([H2O] FAQ, GQA) and over the window, which is
+ *   also the SnapKV window sum ([SNAP] "How it works").  In ACCUMULATE mode
+ *   the previous score is added ([H2O] lifecycle step "Score Accumulation").
+ * POOL: P_j = max of S_i for i in [j - r, j + r] clamped to [0, n-1],
+ *   r = (pool_kernel - 1) / 2 ([SNAP] "How it works").
+ * DROP: sum_w sum_g p / (1 - p) * ||a - v_j||  ([DROP] Lemma 1: the output
+ *   shift from removing j is p_j/(1-p_j)(a - v_j); the score is its length,
+ *   summed over the window).  1 - p is -expm1(x); when x >= 0 (p >= 1) the
+ *   removal is undefined and the term is +inf.
+ */
+typedef struct {
+  const orc_cache *c;
+  const orc_window *w;
+  int flags, pool_kernel;
+  const float *prev;
+  double *sum, *pooled, *drop;
+} score_ctx;
+
+static void score_unit(void *vctx, int64_t u) {
+  score_ctx *x = (score_ctx *)vctx;
+  const orc_cache *c = x->c;
+  const orc_window *w = x->w;
+  int64_t G = w->group, W = w->obs_window, D = c->head_dim;
+  int64_t b = u / c->kv_heads, h = u % c->kv_heads, Hq = (int64_t)c->kv_heads * G;
+  int64_t n = c->seq_len[u], max_slots = (int64_t)c->max_blocks * 16;
+  const int32_t *pos = c->pos + u * max_slots;
+  double *S = (double *)calloc((size_t)(n > 0 ? n : 1), sizeof(double));
+  double *R = (double *)calloc((size_t)(n > 0 ? n : 1), sizeof(double));
+
+  for (int64_t wi = 0; wi < W; ++wi) {
+    int32_t qp = w->q_pos[b * W + wi];
+    for (int64_t g = 0; g < G; ++g) {
+      int64_t hq = h * G + g;
+      int64_t qrow = (b * Hq + hq) * W + wi;
+      double lse = (double)w->lse[qrow];
+      for (int64_t j = 0; j < n; ++j) {
+        if (pos[j] > qp) continue;
+        double xv = w->scale * dot_qk(c, w, qrow, u, j) - lse;
+        double p = exp(xv);
+        S[j] += p;
+        if (x->flags & ORC_DROP) {
+          int64_t prow = phys_row(c, u, j);
+          double r2 = 0.0;
+          for (int64_t d = 0; d < D; ++d) {
+            double diff = widen(w->a, c->is_bf16, qrow * D + d) -
+                          widen(c->v_pool, c->is_bf16, prow * D + d);
+            r2 += diff * diff;
+          }
+          double term = (xv >= 0.0) ? INFINITY : p / (-expm1(xv)) * sqrt(r2);
+          R[j] += term;
+        }
+      }
+    }
+  }
+  double *sum_row = x->sum ? x->sum + u * max_slots : NULL;
+  if (x->flags & ORC_ACCUMULATE)
+    for (int64_t j = 0; j < n; ++j) S[j] += (double)x->prev[u * max_slots + j];
+  if (sum_row)
+    for (int64_t j = 0; j < n; ++j) sum_row[j] = S[j];
+  if (x->flags & ORC_POOL) {
+    int64_t r = (x->pool_kernel - 1) / 2;
+    double *P = x->pooled + u * max_slots;
+    for (int64_t j = 0; j < n; ++j) {
+      int64_t lo = j - r < 0 ? 0 : j - r, hi = j + r > n - 1 ? n - 1 : j + r;
+      double m = S[lo];
+      for (int64_t i = lo + 1; i <= hi; ++i)
+        if (S[i] > m) m = S[i];
+      P[j] = m;
+    }
+  }
+  if (x->flags & ORC_DROP) {
+    double *Dr = x->drop + u * max_slots;
+    for (int64_t j = 0; j < n; ++j) Dr[j] = R[j];
+  }
+  free(S);
+  free(R);
+}
+
+int orc_score(const orc_cache *c, const orc_window *w, int flags, int pool_kernel,
+              const float *prev_sum, double *sum, double *pooled, double *drop,
+              const uint8_t *unit_mask, int nthreads) {
+  if (!c || !w || !w->q || !w->lse || !w->q_pos) return -1;
+  if (w->group < 1 || w->obs_window < 1) return -1;
+  if (!(flags & (ORC_SUM | ORC_POOL | ORC_DROP))) return -1;
+  if ((flags & ORC_SUM) && !sum) return -1;
+  if ((flags & ORC_POOL) && (!pooled || pool_kernel < 1 || pool_kernel % 2 == 0)) return -1;
+  if ((flags & ORC_DROP) && (!drop || !w->a)) return -1;
+  if ((flags & ORC_ACCUMULATE) && (!prev_sum || (flags & (ORC_POOL | ORC_DROP)))) return -1;
+  score_ctx ctx = {c, w, flags, pool_kernel, prev_sum, (flags & ORC_SUM) ? sum : NULL, pooled, drop};
+  parallel_units(score_unit, &ctx, (int64_t)c->batch * c->kv_heads, unit_mask, nthreads);
+  return 0;
+}
+
+/* ----------------------------------------------------------- selection */
+/*
+ * Victims of one KV head ([H2O] "Step-by-Step Eviction Lifecycle" and
+ * "Dual-Pool Budget Partitioning"; [SNAP] "How it works", "Tie-breaking",
+ * "Parameters"; [DROP] greedy bottom-k):
+ *   m = max(0, n - budget) tokens go; the budget counts the recent window.
+ *   Candidates are slots [0, n - R): the last R slots are protected.
+ *   Order candidates by (score, position); equal scores evict the lower
+ *   position first.  -0 equals +0; NaN ranks above +inf.
+ *   The m first candidates are returned in ascending position order.
+ */
+typedef struct {
+  float v;
+  int32_t slot;
+} cand;
+
+static int score_class(float v) { return isnan(v) ? 1 : 0; }
+
+static int cand_cmp(const void *pa, const void *pb) {
+  const cand *a = (const cand *)pa, *b = (const cand *)pb;
+  int ca = score_class(a->v), cb = score_class(b->v);
+  if (ca != cb) return ca < cb ? -1 : 1;
+  if (!ca) {
+    if (a->v < b->v) return -1; /* numeric compare: -0 == +0 */
+    if (a->v > b->v) return 1;
+  }
+  return (a->slot > b->slot) - (a->slot < b->slot);
+}
+
+static int int_cmp(const void *pa, const void *pb) {
+  int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+  return (a > b) - (a < b);
+}
+
+int orc_select(const float *scores, const int32_t *seq_len, int32_t units, int32_t max_slots,
+               int32_t budget, int32_t recent_window, int32_t *victims, int32_t *n_victims) {
+  if (!scores || !seq_len || !victims || !n_victims) return -1;
+  if (budget <= 0 || recent_window < 0 || recent_window >= budget) return -1;
+  cand *buf = (cand *)malloc(sizeof(cand) * (size_t)(max_slots > 0 ? max_slots : 1));
+  for (int64_t u = 0; u < units; ++u) {
+    int64_t n = seq_len[u];
+    int64_t m = n - budget > 0 ? n - budget : 0;
+    int64_t nc = n - recent_window > 0 ? n - recent_window : 0;
+    for (int64_t j = 0; j < nc; ++j) {
+      buf[j].v = scores[u * (int64_t)max_slots + j];
+      buf[j].slot = (int32_t)j;
+    }
+    qsort(buf, (size_t)nc, sizeof(cand), cand_cmp);
+    int32_t *out = victims + u * (int64_t)max_slots;
+    for (int64_t i = 0; i < m; ++i) out[i] = buf[i].slot;
+    qsort(out, (size_t)m, sizeof(int32_t), int_cmp);
+    n_victims[u] = (int32_t)m;
+  }
+  free(buf);
+  return 0;
+}
+
+/* ---------------------------------------------------------- compaction */
+/*
+ * Order-preserving, in-place left-pack of each KV head's kept rows within its
+ * own blocks ([H2O] "PagedAttention Memory Integration": in-place overwrite
+ * within existing pages; [VTOK] section 3.3 stage 3: fill destinations fully,
+ * keep logical order).  Kept slots in ascending order take ranks 0, 1, ...;
+ * row r <- row s for K, V, pos and the optional score row.  Blocks at logical
+ * indices [ceil(n'/16), ceil(n/16)) are then empty: they are appended to the
+ * free list in (b, h, logical block) order and their table entries set to -1
+ * ([VTOK] section 1: whole emptied blocks return to the free pool).
+ * Rank <= slot, so an ascending sequential copy never overwrites a row that is
+ * still to be read.
+ */
+int orc_compact(void *k_pool, void *v_pool, int32_t elem_bytes, int32_t head_dim,
+                int32_t *block_table, int32_t *seq_len, int32_t *pos, float *score,
+                int32_t units, int32_t max_blocks, const int32_t *victims,
+                const int32_t *n_victims, int32_t *free_list, int32_t *free_count,
+                int32_t free_capacity, int64_t *stats) {
+  if (!k_pool || !v_pool || !block_table || !seq_len || !pos || !victims || !n_victims ||
+      !free_list || !free_count || !stats)
+    return -1;
+  if (elem_bytes != 2 && elem_bytes != 4) return -1;
+  int64_t max_slots = (int64_t)max_blocks * 16;
+  int64_t row_bytes = (int64_t)head_dim * elem_bytes;
+  int64_t total_free = 0;
+  for (int64_t u = 0; u < units; ++u) {
+    int64_t n = seq_len[u], m = n_victims[u];
+    if (m < 0 || m > n) return -1;
+    total_free += (n + 15) / 16 - (n - m + 15) / 16;
+  }
+  if (*free_count + total_free > free_capacity) return -2;
+
+  int64_t blocks_freed = 0, rows_moved = 0, at_risk = 0;
+  for (int64_t u = 0; u < units; ++u) {
+    int64_t n = seq_len[u], m = n_victims[u], n2 = n - m;
+    const int32_t *vic = victims + u * max_slots;
+    int32_t *bt = block_table + u * max_blocks;
+    int32_t *ps = pos + u * max_slots;
+    float *sc = score ? score + u * max_slots : NULL;
+    int64_t vi = 0, r = 0;
+    for (int64_t s = 0; s < n; ++s) {
+      if (vi < m && vic[vi] == s) {
+        ++vi;
+        continue;
+      }
+      if (r != s) {
+        int64_t dst = (int64_t)bt[r / 16] * 16 + r % 16;
+        int64_t src = (int64_t)bt[s / 16] * 16 + s % 16;
+        memcpy((char *)k_pool + dst * row_bytes, (char *)k_pool + src * row_bytes, (size_t)row_bytes);
+        memcpy((char *)v_pool + dst * row_bytes, (char *)v_pool + src * row_bytes, (size_t)row_bytes);
+        ps[r] = ps[s];
+        if (sc) sc[r] = sc[s];
+        ++rows_moved;
+        if (s < n2) ++at_risk;
+      }
+      ++r;
+    }
+    for (int64_t lb = (n2 + 15) / 16; lb < (n + 15) / 16; ++lb) {
+      free_list[(*free_count)++] = bt[lb];
+      bt[lb] = -1;
+      ++blocks_freed;
+    }
+    seq_len[u] = (int32_t)n2;
+  }
+  stats[0] = blocks_freed;
+  stats[1] = rows_moved;
+  stats[2] = rows_moved * 2 * row_bytes * 2; /* K and V rows, each read once and written once */
+  stats[3] = at_risk;
+  stats[4] = 0;
+  return 0;
+}
+
+/* --------------------------------------------------------- measurement */
+/*
+ * Intra-block waste F = 1 - sum_i n_i / (N * S) over the N allocated blocks
+ * ([VTOK] section 2, Eq. 1), and the fraction of allocated blocks at or below
+ * 50% use ([VTOK] Fig. 1).  "naive": victims are only marked dead, every block
+ * stays allocated; "after": the kept tokens are packed and emptied blocks freed.
+ */
+int orc_measure(const int32_t *seq_len_before, const int32_t *victims, const int32_t *n_victims,
+                int32_t units, int32_t max_slots, double *out) {
+  if (!seq_len_before || !victims || !n_victims || !out) return -1;
+  double live = 0, blocks_naive = 0, blocks_after = 0, half_naive = 0, half_after = 0;
+  for (int64_t u = 0; u < units; ++u) {
+    int64_t n = seq_len_before[u], m = n_victims[u], n2 = n - m;
+    const int32_t *vic = victims + u * (int64_t)max_slots;
+    int64_t vi = 0;
+    for (int64_t lb = 0; lb < (n + 15) / 16; ++lb) {
+      int64_t live_b = 0;
+      for (int64_t s = lb * 16; s < lb * 16 + 16 && s < n; ++s) {
+        while (vi < m && vic[vi] < s) ++vi;
+        if (!(vi < m && vic[vi] == s)) ++live_b;
+      }
+      blocks_naive += 1;
+      if (2 * live_b <= 16) half_naive += 1;
+    }
+    for (int64_t lb = 0; lb < (n2 + 15) / 16; ++lb) {
+      int64_t live_b = (lb + 1) * 16 <= n2 ? 16 : n2 - lb * 16;
+      blocks_after += 1;
+      if (2 * live_b <= 16) half_after += 1;
+    }
+    live += (double)n2;
+  }
+  out[0] = blocks_naive > 0 ? 1.0 - live / (blocks_naive * 16.0) : 0.0;
+  out[1] = blocks_after > 0 ? 1.0 - live / (blocks_after * 16.0) : 0.0;
+  out[2] = blocks_naive > 0 ? half_naive / blocks_naive : 0.0;
+  out[3] = blocks_after > 0 ? half_after / blocks_after : 0.0;
+  out[4] = blocks_naive;
+  out[5] = blocks_after;
+  out[6] = live;
+  out[7] = blocks_naive - blocks_after;
+  return 0;
+}

@@ -1,0 +1,89 @@
+/*
+ * oracle.h -- plain CPU reference of attention-score KV-cache eviction.
+ *
+ * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may call this library.  The product path (the HIP library
+ * and its Python binding) never links, loads or calls it, and it shares no
+ * code, header or table with that path.
+ *
+ * Everything is computed with scalar loops in double precision.  bf16 inputs
+ * are widened exactly (bits << 16), fp32 inputs exactly.  Sources:
+ *   [H2O]   "H2O Guide: Heavy Hitter Oracle KV Cache Eviction for LLMs"
+ *   [SNAP]  "SnapKV" (policy book entry, decode-time adaptation)
+ *   [VTOK]  "vToken: Turning Token-Level KV Eviction into Actually Reusable GPU Memory"
+ *   [DROP]  "DropKV paper -- Residual-output perturbation scoring for KV-cache eviction"
+ *
+ * Cache layout (one layer): K and V pools of [num_blocks][16][head_dim]; the
+ * slot s of KV head (b, h) lives in physical row
+ *     block_table[b][h][s / 16] * 16 + s % 16          ([VTOK] section 3.4, Eq. 2)
+ * pos[b][h][s] is the original position of slot s; slots are kept in
+ * ascending position order.
+ */
+#ifndef KVEV_ORACLE_H
+#define KVEV_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORC_SUM 1
+#define ORC_POOL 2
+#define ORC_DROP 4
+#define ORC_ACCUMULATE 8
+
+typedef struct {
+  int32_t batch, kv_heads, head_dim, max_blocks, num_blocks, is_bf16;
+  const void *k_pool, *v_pool;   /* [num_blocks][16][head_dim], fp32 or bf16 bits */
+  const int32_t *block_table;    /* [batch][kv_heads][max_blocks] */
+  const int32_t *seq_len;        /* [batch][kv_heads] */
+  const int32_t *pos;            /* [batch][kv_heads][max_blocks*16] */
+} orc_cache;
+
+typedef struct {
+  int32_t group, obs_window;     /* G query heads per KV head, W window queries */
+  const void *q;                 /* [batch][kv_heads*group][W][head_dim], cache dtype */
+  const float *lse;              /* [batch][kv_heads*group][W] */
+  const void *a;                 /* [batch][kv_heads*group][W][head_dim], cache dtype */
+  const int32_t *q_pos;          /* [batch][W] */
+  double scale;                  /* multiplies q.k before the LSE is subtracted */
+} orc_window;
+
+/* Input builder (not the method): LSE and attention output of each window
+ * query over the keys it attends (pos <= q_pos).  lse_out [B][Hq][W],
+ * a_out [B][Hq][W][D] (may be NULL).  unit_mask [B*Hkv] selects KV heads (NULL = all). */
+int orc_lse_a(const orc_cache *c, const orc_window *w, double *lse_out, double *a_out,
+              const uint8_t *unit_mask, int nthreads);
+
+/* Per-token scores of every live slot; outputs [B][Hkv][max_blocks*16] in
+ * double, entries at slots >= seq_len untouched.  prev_sum (fp32) is read in
+ * ACCUMULATE mode.  Returns 0, or -1 on invalid arguments. */
+int orc_score(const orc_cache *c, const orc_window *w, int flags, int pool_kernel,
+              const float *prev_sum, double *sum, double *pooled, double *drop,
+              const uint8_t *unit_mask, int nthreads);
+
+/* Victims of every KV head from fp32 scores [B][Hkv][max_slots].
+ * victims [B][Hkv][max_slots] (first n_victims entries valid, ascending slots). */
+int orc_select(const float *scores, const int32_t *seq_len, int32_t units, int32_t max_slots,
+               int32_t budget, int32_t recent_window, int32_t *victims, int32_t *n_victims);
+
+/* In-place, order-preserving compaction of every KV head; frees emptied tail
+ * blocks to the free list.  elem_bytes is 4 (fp32) or 2 (bf16).  score may be
+ * NULL.  stats[5] = {blocks_freed, rows_moved, bytes_moved, at_risk_rows, status}.
+ * Returns 0, -1 (invalid) or -2 (free list too small; nothing modified). */
+int orc_compact(void *k_pool, void *v_pool, int32_t elem_bytes, int32_t head_dim,
+                int32_t *block_table, int32_t *seq_len, int32_t *pos, float *score,
+                int32_t units, int32_t max_blocks, const int32_t *victims,
+                const int32_t *n_victims, int32_t *free_list, int32_t *free_count,
+                int32_t free_capacity, int64_t *stats);
+
+/* Block-level waste of an eviction ([VTOK] section 2, Eq. 1 and Fig. 1).
+ * out[8] = {F_naive, F_after, frac_le_half_naive, frac_le_half_after,
+ *           blocks_naive, blocks_after, live_tokens, blocks_freed}. */
+int orc_measure(const int32_t *seq_len_before, const int32_t *victims, const int32_t *n_victims,
+                int32_t units, int32_t max_slots, double *out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

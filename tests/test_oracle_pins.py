@@ -1,0 +1,556 @@
+"""Pins of the CPU oracle to what the pages and the mathematics fix.
+
+Every test here checks the oracle against something other than itself: a
+value printed on a page, a closed form, an invariant, a brute force on a tiny
+input, or a textbook routine in a special case.  CPU only.
+
+Sources:
+  [H2O]  "H2O Guide: Heavy Hitter Oracle KV Cache Eviction for LLMs"
+  [SNAP] "SnapKV" (policy book entry)
+  [VTOK] "vToken: Turning Token-Level KV Eviction into Actually Reusable GPU Memory"
+  [DROP] "DropKV paper -- Residual-output perturbation scoring for KV-cache eviction"
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.helpers import manual_case, rounded_window_inputs, logical_rows
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng
+
+
+def _softmax(x):
+    x = np.asarray(x, np.float64)
+    e = np.exp(x - x.max())
+    return e / e.sum()
+
+
+def _random_case(seed, B=1, Hkv=2, G=2, W=3, D=8, n=37, dtype="f32", ragged=True, std=0.5):
+    r = rng(seed)
+    k = r.normal(0, std, (B, Hkv, n, D))
+    v = r.normal(0, 1, (B, Hkv, n, D))
+    q = r.normal(0, std, (B, Hkv * G, W, D))
+    q_pos = np.broadcast_to(np.arange(n - W, n), (B, W)).copy()
+    seq = np.full((B, Hkv), n, np.int32)
+    if ragged:
+        seq[..., 0] = n - 5   # a head with fewer live tokens (ragged tail)
+    return manual_case(k, v, q, q_pos, seq_len=seq, dtype=dtype, scale=0.7)
+
+
+# ------------------------------------------------------------ probabilities
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_softmax_rows_sum_to_one(dtype):
+    """Each window query's probabilities are a full softmax: with the LSE of
+    the same logits, sum_j p_j = exp(LSE - LSE_fp32) ([H2O] "The Existence of
+    Heavy Hitters"; [DROP] Jargon: attention weights of one query add up to 1)."""
+    case = _random_case(1, dtype=dtype)
+    lse64, _ = oracle.lse_a(case)
+    lse32, _ = rounded_window_inputs(case, lse64)
+    out = oracle.score(case, lse32, oracle.SUM)
+    total = 0.0
+    for b in range(case["B"]):
+        for h in range(case["Hkv"]):
+            n = case["seq_len"][b, h]
+            total += out["sum"][b, h, :n].sum()
+    expect = np.exp(lse64.astype(np.float64) - lse32.astype(np.float64)).sum()
+    assert abs(total - expect) <= 1e-12 * expect
+    # every row sums to one individually as well: one row at a time (W = G = 1)
+    n_rows = case["Hkv"] * case["G"] * case["W"]
+    assert abs(expect - n_rows) < 1e-5 * n_rows
+
+
+def test_logits_known_by_construction():
+    """q = c_r * e0 and k_j = t_j * e0 give logits c_r * t_j exactly; the
+    per-slot sum over rows must equal the textbook softmax of those logits,
+    through a shuffled block table and the causal mask."""
+    B, Hkv, G, W, D, n = 1, 2, 3, 4, 64, 45
+    r = rng(2)
+    t = np.round(r.normal(0, 2, (B, Hkv, n)) * 8) / 8          # exact in fp32
+    c = np.round(r.uniform(0.25, 2.0, (B, Hkv * G, W)) * 4) / 4
+    k = np.zeros((B, Hkv, n, D)); k[..., 0] = t
+    q = np.zeros((B, Hkv * G, W, D)); q[..., 0] = c
+    v = r.normal(0, 1, (B, Hkv, n, D))
+    q_pos = np.array([[n - 9, n - 6, n - 2, n - 1]], np.int32)
+    case = manual_case(k, v, q, q_pos, dtype="f32", scale=0.5)
+    lse64, _ = oracle.lse_a(case)
+    lse32, _ = rounded_window_inputs(case, lse64)
+    got = oracle.score(case, lse32, oracle.SUM)["sum"]
+    for h in range(Hkv):
+        expect = np.zeros(n)
+        for g in range(G):
+            for w in range(W):
+                hq = h * G + g
+                live = q_pos[0, w] + 1                      # slots 0..q_pos attend
+                logits = 0.5 * c[0, hq, w] * t[0, h, :live]
+                p = _softmax(logits) * np.exp(lse64[0, hq, w] - np.float64(lse32[0, hq, w]))
+                expect[:live] += p
+        np.testing.assert_allclose(got[0, h, :n], expect, rtol=1e-12, atol=1e-300)
+
+
+def test_one_hot_logit_gives_unit_probability():
+    """A key whose logit exceeds all others by 60 takes p = 1 (to e^-60)."""
+    B, Hkv, D, n = 1, 1, 64, 20
+    k = np.zeros((B, Hkv, n, D)); k[0, 0, 13, 0] = 60.0
+    q = np.zeros((B, 1, 1, D)); q[..., 0] = 1.0
+    case = manual_case(k, np.zeros_like(k), q, np.array([[n - 1]]), dtype="f32", scale=1.0)
+    lse64, _ = oracle.lse_a(case)
+    lse32, _ = rounded_window_inputs(case, lse64)
+    s = oracle.score(case, lse32, oracle.SUM)["sum"][0, 0, :n]
+    assert abs(s[13] - 1.0) < 1e-12
+    assert np.all(s[np.arange(n) != 13] < 1e-25)
+
+
+def test_equal_keys_uniform_closed_form():
+    """All keys equal: each query at position P attends P + 1 keys with
+    p = 1/(P+1); S_j = G * sum over window queries with q_pos >= pos_j of
+    1/(q_pos + 1) ([H2O] cumulative score with uniform attention)."""
+    B, Hkv, G, W, D, n = 2, 2, 2, 5, 64, 40
+    r = rng(3)
+    krow = r.normal(0, 1, D)
+    k = np.broadcast_to(krow, (B, Hkv, n, D)).copy()
+    q = r.normal(0, 1, (B, Hkv * G, W, D))
+    q_pos = np.array([[30, 31, 35, 38, 39], [20, 25, 26, 33, 39]], np.int32)
+    case = manual_case(k, k, q, q_pos, dtype="f32", scale=0.3)
+    lse64, _ = oracle.lse_a(case)
+    np.testing.assert_allclose(lse64 - 0.3 * np.einsum("bhwd,d->bhw", q.astype(np.float32).astype(np.float64), krow.astype(np.float32).astype(np.float64)),
+                               np.log(q_pos + 1.0)[:, None, :].repeat(Hkv * G, 1), rtol=0, atol=1e-12)
+    lse32, _ = rounded_window_inputs(case, lse64)
+    s = oracle.score(case, lse32, oracle.SUM)["sum"]
+    corr = np.exp(lse64 - lse32.astype(np.float64))           # fp32 LSE rounding, per row
+    for b in range(B):
+        for h in range(Hkv):
+            for j in range(n):
+                e = sum(corr[b, h * G + g, w] / (q_pos[b, w] + 1.0)
+                        for g in range(G) for w in range(W) if q_pos[b, w] >= j)
+                assert abs(s[b, h, j] - e) <= 1e-12 * max(e, 1e-300)
+
+
+def test_accumulate_equals_one_window():
+    """[H2O] lifecycle: S_j <- S_j + sum_h A_{h,T,j} step by step equals one call
+    with all steps in the window (sum is associative; the running score is
+    stored in fp32 between steps)."""
+    B, Hkv, G, D, n, T = 1, 2, 2, 16, 30, 6
+    r = rng(4)
+    k = r.normal(0, 0.6, (B, Hkv, n, D)); v = r.normal(0, 1, (B, Hkv, n, D))
+    q = r.normal(0, 0.6, (B, Hkv * G, T, D))
+    q_pos = np.arange(n - T, n, dtype=np.int32)[None]
+    full = manual_case(k, v, q, q_pos, dtype="f32", scale=0.8)
+    lse64, _ = oracle.lse_a(full)
+    lse32, _ = rounded_window_inputs(full, lse64)
+    one = oracle.score(full, lse32, oracle.SUM)["sum"]
+    acc = np.zeros_like(one)
+    for t in range(T):
+        step = dict(full)
+        step["W"] = 1
+        step["q"] = np.ascontiguousarray(full["q"][:, :, t:t + 1])
+        step["q_pos"] = np.ascontiguousarray(full["q_pos"][:, t:t + 1])
+        prev = np.nan_to_num(acc, nan=0.0).astype(np.float32)
+        acc = oracle.score(step, np.ascontiguousarray(lse32[:, :, t:t + 1]),
+                           oracle.SUM | oracle.ACCUMULATE, prev_sum=prev)["sum"]
+    np.testing.assert_allclose(acc[..., :n], one[..., :n], rtol=2e-6)
+
+
+# --------------------------------------------------------------- max-pool
+
+
+@pytest.mark.parametrize("kernel", [1, 3, 5, 7, 9, 63])
+def test_pool_is_clamped_sliding_max(kernel):
+    """[SNAP] "How it works": pooled[i] = max(sums[i-r .. i+r]), r = (k-1)/2,
+    clamped to the live slots; kernel 1 disables pooling ([SNAP] Parameters)."""
+    case = _random_case(5, B=2, Hkv=2, G=2, W=4, n=50)
+    lse64, _ = oracle.lse_a(case)
+    lse32, _ = rounded_window_inputs(case, lse64)
+    out = oracle.score(case, lse32, oracle.SUM | oracle.POOL, pool_kernel=kernel)
+    r = (kernel - 1) // 2
+    for b in range(2):
+        for h in range(2):
+            n = case["seq_len"][b, h]
+            s = out["sum"][b, h, :n]
+            brute = np.array([max(s[max(0, j - r):min(n, j + r + 1)]) for j in range(n)])
+            assert np.array_equal(out["pooled"][b, h, :n], brute)
+            assert np.all(out["pooled"][b, h, :n] >= s)
+            if kernel == 1:
+                assert np.array_equal(out["pooled"][b, h, :n], s)
+
+
+def test_pool_refuses_even_kernel_and_accumulate():
+    case = _random_case(6)
+    lse64, _ = oracle.lse_a(case)
+    lse32, _ = rounded_window_inputs(case, lse64)
+    for k in (0, 2, 4, -1):
+        with pytest.raises(ValueError):
+            oracle.score(case, lse32, oracle.POOL, pool_kernel=k)
+    with pytest.raises(ValueError):
+        oracle.score(case, lse32, oracle.POOL | oracle.SUM | oracle.ACCUMULATE, pool_kernel=3,
+                     prev_sum=np.zeros((1, 2, case["max_blocks"] * 16), np.float32))
+
+
+# ----------------------------------------------------------------- DropKV
+
+
+def _reblend_shift(p, v, removed):
+    """||a' - a|| after removing the tokens in `removed` and renormalising the rest."""
+    p = np.asarray(p, np.float64); v = np.asarray(v, np.float64)
+    a = (p[:, None] * v).sum(0)
+    keep = np.array([i not in removed for i in range(len(p))])
+    a2 = (p[keep, None] * v[keep]).sum(0) / p[keep].sum()
+    return np.linalg.norm(a2 - a)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_dropkv_lemma1_brute_force(seed):
+    """[DROP] Lemma 1: removing j and renormalising moves the output by
+    p_j/(1-p_j)(a - v_j).  Brute force: re-run the softmax blend without j
+    (exact double) and compare the length of the shift with the oracle's
+    single-query score.  Inputs reach the oracle as fp32 (LSE, a): the LSE
+    rounding e moves p_j by a factor exp(e) and 1 - p_j by p_j*e, so the
+    bound is 1e-6 + 4|e|(1 + p_j/(1-p_j)) relative -- still far below the
+    error of any dropped term or factor."""
+    r = rng(100 + seed)
+    n, D = 6 + seed % 3, 64
+    k = np.zeros((1, 1, n, D)); k[..., :4] = r.normal(0, 1.2, (n, 4))
+    v = np.zeros((1, 1, n, D)); v[..., :4] = r.normal(0, 1, (n, 4))
+    q = np.zeros((1, 1, 1, D)); q[..., :4] = r.normal(0, 1, 4)
+    case = manual_case(k, v, q, np.array([[n - 1]]), dtype="f32", scale=1.0)
+    lse64, a64 = oracle.lse_a(case, want_a=True)
+    lse32, a_enc = rounded_window_inputs(case, lse64, a64)
+    drop = oracle.score(case, lse32, oracle.DROP, a_enc=a_enc)["drop"][0, 0, :n]
+    kk = k[0, 0].astype(np.float32).astype(np.float64)
+    vv = v[0, 0].astype(np.float32).astype(np.float64)
+    qq = q[0, 0, 0].astype(np.float32).astype(np.float64)
+    p = _softmax(kk @ qq)
+    a = p @ vv
+    for j in range(n):
+        keep = np.arange(n) != j
+        a2 = (p[keep] @ vv[keep]) / p[keep].sum()
+        np.testing.assert_allclose(a2 - a, p[j] / (1 - p[j]) * (a - vv[j]), rtol=1e-9, atol=1e-14)
+        brute = np.linalg.norm(a2 - a)
+        e = abs(float(lse64[0, 0, 0]) - float(lse32[0, 0, 0]))
+        tol = 1e-6 + 4 * e * (1 + p[j] / (1 - p[j]))
+        assert abs(drop[j] - brute) <= tol * brute + 1e-12
+
+
+def test_dropkv_worked_example():
+    """[DROP] "Worked example": p = (.50,.30,.15,.05), v = (5,5,15,5).  Embedded
+    as q = e0, k_i = ln(p_i) e0, scale 1, LSE 0, a = 6.5 e0."""
+    g = json.load(open(os.path.join(GOLDEN, "dropkv_worked_example.json")))
+    p = np.array(g["p"]); vals = np.array(g["v"]); n, D = 4, 64
+    k = np.zeros((1, 1, n, D)); k[0, 0, :, 0] = np.log(p)
+    v = np.zeros((1, 1, n, D)); v[0, 0, :, 0] = vals
+    q = np.zeros((1, 1, 1, D)); q[..., 0] = 1.0
+    case = manual_case(k, v, q, np.array([[n - 1]]), dtype="f32", scale=1.0)
+    a_page = np.zeros((1, 1, 1, D)); a_page[..., 0] = g["a"]
+    assert abs((p * vals).sum() - g["a"]) < 1e-12
+    lse32 = np.zeros((1, 1, 1), np.float32)
+    out = oracle.score(case, lse32, oracle.DROP | oracle.SUM, a_enc=a_page.astype(np.float32))
+    drop, attn = out["drop"][0, 0, :n], out["sum"][0, 0, :n]
+    # printed to two decimals
+    np.testing.assert_allclose(np.round(drop, g["printed_decimals"]), g["scores_printed"], atol=1e-12)
+    # exact values of the same arithmetic: 1.5, 0.3/0.7*1.5, 0.15/0.85*8.5, 0.05/0.95*1.5
+    np.testing.assert_allclose(drop, [1.5, 9 / 14, 1.5, 3 / 38], rtol=1e-6)
+    np.testing.assert_allclose(attn, p, rtol=1e-6)
+    budget = n - g["evict"]
+    # tokens 1 and 3 tie at 1.50 only in exact arithmetic; evicting two never reaches that tie
+    vd, nd = oracle.select(out["drop"].astype(np.float32), case["seq_len"], budget, 0)
+    va, na = oracle.select(out["sum"].astype(np.float32), case["seq_len"], budget, 0)
+    assert sorted((vd[0, :nd[0]] + 1).tolist()) == g["dropkv_victim_tokens"]
+    assert sorted((va[0, :na[0]] + 1).tolist()) == g["attention_weight_victim_tokens"]
+    # the shifts the page prints, and DropKV's pair is the best of all six pairs
+    vcol = vals[:, None]
+    sh_d = _reblend_shift(p, vcol, {1, 3})
+    sh_a = _reblend_shift(p, vcol, {2, 3})
+    assert abs(sh_a - g["attention_weight_shift"]) < 1e-12
+    assert abs(sh_d - g["dropkv_shift_approx"]) < 0.005
+    best = min(itertools.combinations(range(4), 2), key=lambda pr: _reblend_shift(p, vcol, set(pr)))
+    assert set(best) == {1, 3}
+
+
+def test_dropkv_zero_when_values_equal_output():
+    """v_j = a for every j: every residual is 0, so the score is exactly 0."""
+    r = rng(8)
+    n, D = 33, 64
+    c = np.round(r.normal(0, 1, D) * 64) / 64
+    k = r.normal(0, 1, (1, 2, n, D)); v = np.broadcast_to(c, (1, 2, n, D)).copy()
+    q = r.normal(0, 1, (1, 4, 3, D))
+    case = manual_case(k, v, q, np.array([[n - 3, n - 2, n - 1]]), dtype="f32", scale=0.125)
+    lse64, a64 = oracle.lse_a(case, want_a=True)
+    lse32, a_enc = rounded_window_inputs(case, lse64, a64)
+    assert np.array_equal(a_enc[0, 0, 0], c.astype(np.float32))
+    d = oracle.score(case, lse32, oracle.DROP, a_enc=a_enc)["drop"][0, :, :n]
+    assert np.all(d == 0.0)
+
+
+def test_dropkv_lone_key_is_never_evicted_first():
+    """p = 1 (the only attended key): removal is undefined; the score is +inf."""
+    n, D = 5, 64
+    k = np.zeros((1, 1, n, D)); v = np.ones((1, 1, n, D))
+    q = np.zeros((1, 1, 1, D))
+    case = manual_case(k, v, q, np.array([[0]]), dtype="f32")
+    lse64, a64 = oracle.lse_a(case, want_a=True)
+    lse32, a_enc = rounded_window_inputs(case, lse64, a64)
+    d = oracle.score(case, lse32, oracle.DROP, a_enc=a_enc)["drop"][0, 0, :n]
+    assert d[0] == np.inf and np.all(d[1:] == 0.0)
+
+
+# -------------------------------------------------------------- selection
+
+
+def _brute_victims(s, n, budget, R):
+    """Rank every candidate by counting the candidates that beat it."""
+    m = max(0, n - budget)
+    cands = list(range(max(0, n - R)))
+
+    def beats(i, j):   # i is evicted before j
+        a, b = s[i], s[j]
+        if np.isnan(a) or np.isnan(b):
+            if np.isnan(a) and np.isnan(b):
+                return i < j
+            return np.isnan(b)
+        return a < b or (a == b and i < j)
+
+    out = [j for j in cands if sum(beats(i, j) for i in cands if i != j) < m]
+    return sorted(out)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_select_brute_force(seed):
+    """[H2O] greedy eviction of the minimum outside the recent window, [SNAP]
+    Tie-breaking (equal scores evict the lower position; ascending output),
+    budget counting the recent window ([H2O] Dual-Pool Budget)."""
+    r = rng(200 + seed)
+    U, ms = 5, 64
+    scores = np.round(r.uniform(0, 4, (U, ms)), 0 if seed % 2 else 2).astype(np.float32)
+    if seed == 3:
+        scores[:, ::5] = -0.0
+        scores[:, 1::5] = 0.0
+        scores[:, 7] = np.inf
+        scores[:, 9] = np.nan
+    seq = r.integers(0, ms + 1, U).astype(np.int32)
+    budget, R = [(16, 4), (5, 0), (40, 39), (1, 0), (64, 8), (3, 2), (20, 19), (30, 1)][seed]
+    vic, nv = oracle.select(scores, seq, budget, R)
+    for u in range(U):
+        n = int(seq[u])
+        assert nv[u] == max(0, n - budget)
+        got = vic[u, :nv[u]].tolist()
+        assert got == _brute_victims(scores[u], n, budget, R)
+        assert all(x < y for x, y in zip(got, got[1:]))
+        assert all(x < n - R for x in got)
+
+
+def test_select_all_equal_takes_lowest_positions():
+    s = np.full((2, 48), 0.25, np.float32)
+    vic, nv = oracle.select(s, np.array([48, 30], np.int32), 10, 4)
+    assert vic[0, :nv[0]].tolist() == list(range(38))
+    assert vic[1, :nv[1]].tolist() == list(range(20))
+
+
+def test_select_refusals():
+    """[SNAP] Parameters: recentWindow >= budget is refused; budget must be positive."""
+    s = np.zeros((1, 16), np.float32)
+    for budget, R in ((4, 4), (4, 9), (0, 0), (-3, 0), (4, -1)):
+        with pytest.raises(ValueError):
+            oracle.select(s, np.array([16], np.int32), budget, R)
+
+
+# ------------------------------------------------------------- compaction
+
+
+def _row_hashes(case):
+    """Multiset of (pos, K bytes, V bytes) over the live rows of each head."""
+    out = {}
+    K = case["k_pool"]; V = case["v_pool"]
+    for b in range(case["B"]):
+        for h in range(case["Hkv"]):
+            rows = []
+            for s in range(case["seq_len"][b, h]):
+                blk = case["block_table"][b, h, s // 16]
+                rows.append((int(case["pos"][b, h, s]), K[blk, s % 16].tobytes(),
+                             V[blk, s % 16].tobytes()))
+            out[(b, h)] = rows
+    return out
+
+
+@pytest.mark.parametrize("pattern", ["random", "first_only", "every_other", "none", "all_but_recent",
+                                     "tail_only"])
+def test_compact_invariants(pattern):
+    """[VTOK] section 3.5: I1 token conservation, I2 unique mapping, I4 block
+    count falls whenever a block empties; kept tokens stay in position order
+    ([VTOK] section 3.3 stage 3); emptied tail blocks go to the free list."""
+    B, Hkv, D, n_max = 2, 3, 64, 90
+    r = rng(300)
+    k = r.normal(0, 1, (B, Hkv, n_max, D)); v = r.normal(0, 1, (B, Hkv, n_max, D))
+    seq = np.array([[90, 77, 16], [33, 0, 89]], np.int32)
+    case = manual_case(k, v, np.zeros((B, Hkv, 1, D)), np.zeros((B, 1)), seq_len=seq,
+                       dtype="bf16", spare_blocks=5)
+    U, ms = B * Hkv, case["max_blocks"] * 16
+    vic = np.full((U, ms), -1, np.int32); nv = np.zeros(U, np.int32)
+    for u in range(U):
+        n = int(seq.reshape(-1)[u])
+        if pattern == "random":
+            sel = np.sort(r.choice(n, size=n // 2, replace=False)) if n else np.array([], int)
+        elif pattern == "first_only":
+            sel = np.array([0]) if n else np.array([], int)
+        elif pattern == "every_other":
+            sel = np.arange(0, n, 2)
+        elif pattern == "none":
+            sel = np.array([], int)
+        elif pattern == "all_but_recent":
+            sel = np.arange(0, max(0, n - 3))
+        else:
+            sel = np.arange(max(0, n - 20), n)
+        vic[u, :len(sel)] = sel; nv[u] = len(sel)
+    before = _row_hashes(case)
+    score_row = np.arange(U * ms, dtype=np.float32).reshape(B, Hkv, ms)
+    free0 = np.full(case["num_blocks"], -1, np.int32)
+    free0[:2] = [10**6, 10**6 + 1]       # entries already on the free list stay first
+    new, fl, fc, stats = oracle.compact(case, vic, nv, score_row=score_row, free_list=free0,
+                                        free_count=2)
+    after = _row_hashes(new)
+    exp_freed = rows_moved = at_risk = 0
+    for b in range(B):
+        for h in range(Hkv):
+            u = b * Hkv + h
+            n = int(seq[b, h]); m = int(nv[u]); n2 = n - m
+            dead = set(vic[u, :m].tolist())
+            kept = [row for s, row in enumerate(before[(b, h)]) if s not in dead]
+            assert after[(b, h)] == kept                                   # I1 and order
+            assert new["seq_len"][b, h] == n2
+            ks = [s for s in range(n) if s not in dead]
+            assert np.array_equal(new["score_row"][b, h, :n2], score_row[b, h, ks])
+            rows_moved += sum(1 for rk, s in enumerate(ks) if rk != s)
+            at_risk += sum(1 for rk, s in enumerate(ks) if rk != s and s < n2)
+            nb, nb2 = -(-n // 16), -(-n2 // 16)
+            exp_freed += nb - nb2
+            assert np.all(new["block_table"][b, h, nb2:nb] == -1)           # I4
+            assert np.array_equal(new["block_table"][b, h, :nb2], case["block_table"][b, h, :nb2])
+            assert np.array_equal(new["block_table"][b, h, nb:], case["block_table"][b, h, nb:])
+    assert stats[0] == exp_freed and fc == 2 + exp_freed
+    assert stats[1] == rows_moved and stats[3] == at_risk
+    assert stats[2] == rows_moved * 2 * D * 2 * 2
+    # I2: each block id lives in exactly one place: a table entry or the free list
+    ids = np.concatenate([new["block_table"].reshape(-1), fl[2:fc]])
+    ids = ids[ids >= 0]
+    assert len(ids) == len(set(ids.tolist()))
+    orig = case["block_table"].reshape(-1)
+    assert sorted(ids.tolist()) == sorted(orig[orig >= 0].tolist())
+    # free list order: (b, h, logical block) ascending
+    expect_fl = []
+    for b in range(B):
+        for h in range(Hkv):
+            u = b * Hkv + h
+            n = int(seq[b, h]); n2 = n - int(nv[u])
+            expect_fl += case["block_table"][b, h, -(-n2 // 16):-(-n // 16)].tolist()
+    assert fl[2:fc].tolist() == expect_fl and fl[:2].tolist() == [10**6, 10**6 + 1]
+
+
+def test_compact_refuses_small_free_list():
+    k = np.zeros((1, 1, 64, 64))
+    case = manual_case(k, k, np.zeros((1, 1, 1, 64)), np.zeros((1, 1)))
+    vic = np.full((1, 64), -1, np.int32); vic[0, :40] = np.arange(40)
+    with pytest.raises(ValueError):
+        oracle.compact(case, vic, np.array([40], np.int32), free_list=np.zeros(1, np.int32))
+
+
+# ------------------------------------------------------------ measurement
+
+
+def test_waste_ratio_closed_forms():
+    """[VTOK] section 2, Eq. 1: F = 1 - sum n_i / (N S)."""
+    ms = 64
+    # one live token per block under naive eviction: F = 15/16
+    vic = np.array([[s for s in range(ms) if s % 16 != 0]], np.int32)
+    m = measure_one(ms, vic)
+    assert abs(m["F_naive"] - 15 / 16) < 1e-15 and m["frac_le_half_naive"] == 1.0
+    assert m["F_after"] == 0.75 and m["blocks_freed"] == 3   # 4 tokens pack into 1 block
+    # no victims, full blocks: F = 0
+    m = measure_one(ms, np.zeros((1, 0), np.int32))
+    assert m["F_naive"] == 0.0 and m["F_after"] == 0.0 and m["frac_le_half_naive"] == 0.0
+
+
+def measure_one(ms, vic_list):
+    vic = np.full((1, ms), -1, np.int32)
+    vic[0, :vic_list.shape[1]] = vic_list[0]
+    return oracle.measure(np.array([ms], np.int32), vic, np.array([vic_list.shape[1]], np.int32))
+
+
+def test_workload_sizes_match_page_formulas():
+    """[H2O] "The Anatomy of Autoregressive Memory Overhead": Memory_KV =
+    2*2*n_layers*H_kv*d_head*L*B bytes.  The block-eviction workload (70B GQA
+    shape, B 16, L 64000) holds ~4.19 GB per layer; 80 layers give the page's
+    ~335.5 GB.  The H2O decode budget is 20% = 10% heavy + 10% recent."""
+    c5 = synth.CONFIGS["block_evict_64k"]
+    per_layer = 2 * 2 * c5.Hkv * c5.D * c5.L * c5.B
+    assert per_layer == 4_194_304_000
+    assert abs(per_layer * 80 / 1e9 - 335.5) < 0.1
+    c2 = synth.CONFIGS["h2o_decode_4k"]
+    assert c2.budget == math.floor(0.2 * c2.L_final) and c2.recent == math.floor(0.1 * c2.L_final)
+    c4 = synth.CONFIGS["dropkv_128k"]
+    assert c4.budget == math.floor(0.05 * c4.L)
+
+
+# ---------------------------------------------------- H2O streaming self-test
+
+
+def _h2o_stream(plant: float, token=0, steps=16, budget=8, recent=4, G=4, D=64, seed=11):
+    """[H2O] "Step-by-Step Eviction Lifecycle" at decode time, with the
+    oracle's steps: insert the new token, accumulate its attention (GQA group
+    summed), and evict down to the budget outside the recent window; the
+    running score moves with the compacted rows.  Returns the retained
+    original positions."""
+    r = rng(seed)
+    u = r.normal(0, 1, D); u /= np.linalg.norm(u)
+    keys = r.normal(0, 1, (steps, D)); keys[token] += plant * np.sqrt(D) * u
+    vals = r.normal(0, 1, (steps, D))
+    case = manual_case(np.zeros((1, 1, steps, D)), np.zeros((1, 1, steps, D)),
+                       np.zeros((1, G, 1, D)), np.zeros((1, 1)), seq_len=[[0]], dtype="f32",
+                       scale=1 / np.sqrt(D))
+    ms = case["max_blocks"] * 16
+    acc = np.zeros((1, 1, ms), np.float32)
+    for t in range(steps):
+        n = int(case["seq_len"][0, 0])
+        blk = case["block_table"][0, 0, n // 16]
+        case["k_pool"][blk, n % 16] = keys[t]
+        case["v_pool"][blk, n % 16] = vals[t]
+        case["pos"][0, 0, n] = t
+        case["seq_len"][0, 0] = n + 1
+        acc[0, 0, n] = 0.0
+        q = (r.normal(0, 1, (1, G, 1, D)) + np.sqrt(D) * u).astype(np.float32)
+        case["q"] = q
+        case["q_pos"] = np.array([[t]], np.int32)
+        lse64, _ = oracle.lse_a(case)
+        lse32, _ = rounded_window_inputs(case, lse64)
+        acc = oracle.score(case, lse32, oracle.SUM | oracle.ACCUMULATE,
+                           prev_sum=acc)["sum"].astype(np.float32)
+        acc = np.nan_to_num(acc, nan=0.0)
+        if n + 1 > budget:
+            vic, nv = oracle.select(acc, case["seq_len"], budget, recent)
+            assert nv[0] == 1
+            new, _, _, _ = oracle.compact(case, vic, nv, score_row=acc)
+            acc = new.pop("score_row")
+            case = new
+    n = int(case["seq_len"][0, 0])
+    return sorted(case["pos"][0, 0, :n].tolist())
+
+
+def test_h2o_heavy_hitter_retained():
+    """The H2O guide's self-test (16 steps, budget 8 = 4 heavy + 4 recent,
+    4 heads, D 64): a token that draws most of the attention at every step
+    is never evicted.  Here the attention comes from q.k: token 0's key is
+    planted on the queries' shared direction."""
+    kept = _h2o_stream(plant=1.0)
+    assert len(kept) == 8
+    assert 0 in kept
+    assert kept[-4:] == [12, 13, 14, 15]          # the recent window is always kept
+    # a heavy hitter planted later in the stream is kept as well
+    assert 6 in _h2o_stream(plant=1.0, token=6)
+    # a key planted against the queries' direction draws no attention: evicted
+    assert 0 not in _h2o_stream(plant=-1.0)
