@@ -1,0 +1,202 @@
+/*
+ * kvev.h -- attention-score KV-cache eviction on MI355X (gfx950): score,
+ * select and compact one layer's paged KV cache.
+ *
+ * Sources (cited by page title and section):
+ *   [H2O]  "H2O Guide: Heavy Hitter Oracle KV Cache Eviction for LLMs"
+ *   [SNAP] "SnapKV" (policy book entry)
+ *   [VTOK] "vToken: Turning Token-Level KV Eviction into Actually Reusable GPU Memory"
+ *   [DROP] "DropKV paper -- Residual-output perturbation scoring for KV-cache eviction"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every data pointer is a DEVICE pointer owned by the caller (for example a
+ *   torch tensor's data_ptr()).  The library allocates nothing, frees nothing
+ *   and keeps no state between calls; it is reentrant.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Each
+ *   call only enqueues work on that stream and never synchronises.  Calls that
+ *   share a workspace or touch the same cache must be ordered on one stream.
+ * - Return value: KVEV_OK, or a negative kvev_status.  Argument errors are
+ *   detected on the host BEFORE anything is enqueued, so a refused call leaves
+ *   every buffer untouched.  Inconsistent device-resident data (for example a
+ *   seq_len above the head's capacity, or victims not strictly ascending) is
+ *   detected by the kernels: the affected head is left unchanged and a bit is
+ *   set in stats[4] of kvev_compact, or (score/select) the head is skipped and
+ *   its n_victims is set to -1.
+ * - Block size is fixed at 16 tokens ([VTOK] section 2 and section 5's block
+ *   size sensitivity; [H2O] "PagedAttention Memory Integration").
+ *
+ * Cache layout (one layer)
+ * ------------------------
+ * k_pool, v_pool: [num_blocks][16][head_dim] in the cache dtype (fp32 or
+ * bf16).  Each (batch b, KV head h) owns a list of blocks; logical slot s of
+ * that head lives in physical row
+ *     block_table[b][h][s / 16] * 16 + s % 16          ([VTOK] section 3.4, Eq. 2)
+ * seq_len[b][h] = n live slots; pos[b][h][s] = original token position of slot
+ * s.  Slots are always in ascending position order (compaction keeps it).
+ */
+#ifndef KVEV_H
+#define KVEV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVEV_BLOCK_SIZE 16
+#define KVEV_ABI_VERSION 1
+
+typedef enum {
+  KVEV_OK = 0,
+  KVEV_EINVAL = -1,       /* bad argument: NULL, bad shape, refused parameter */
+  KVEV_ENOSPACE = -2,     /* workspace or free list too small */
+  KVEV_EUNSUPPORTED = -3, /* dtype / head_dim / row count the kernels lack */
+  KVEV_EDEVICE = -4       /* a HIP launch or query failed */
+} kvev_status;
+
+typedef enum { KVEV_F32 = 0, KVEV_BF16 = 1 } kvev_dtype;
+
+/* score kinds (flags of kvev_score) */
+enum {
+  KVEV_SUM = 1,        /* H2O accumulated attention / SnapKV window sum */
+  KVEV_POOL = 2,       /* SnapKV window sum followed by the 1-D max-pool */
+  KVEV_DROP = 4,       /* DropKV residual score */
+  KVEV_ACCUMULATE = 8  /* add the window sum to the values already in `sum` */
+};
+
+typedef struct kvev_cache {
+  int32_t batch;        /* B */
+  int32_t kv_heads;     /* Hkv */
+  int32_t head_dim;     /* D: 64 or 128 */
+  int32_t block_size;   /* must be 16 */
+  int32_t max_blocks;   /* block-table entries per head; capacity = max_blocks*16 slots */
+  int32_t num_blocks;   /* physical blocks in each pool */
+  int32_t dtype;        /* kvev_dtype of k_pool, v_pool, q and a */
+  void *k_pool;         /* [num_blocks][16][head_dim] */
+  void *v_pool;         /* [num_blocks][16][head_dim] */
+  int32_t *block_table; /* [batch][kv_heads][max_blocks]; -1 = no block */
+  int32_t *seq_len;     /* [batch][kv_heads] live slots per head */
+  int32_t *pos;         /* [batch][kv_heads][max_blocks*16] original positions */
+} kvev_cache;
+
+typedef struct kvev_window {
+  int32_t group;        /* G query heads per KV head (GQA), >= 1 */
+  int32_t obs_window;   /* W window queries per query head, >= 1 */
+  const void *q;        /* [batch][kv_heads*group][W][head_dim], cache dtype */
+  const float *lse;     /* [batch][kv_heads*group][W]: log-sum-exp of scale*q.k */
+  const void *a;        /* [batch][kv_heads*group][W][head_dim], cache dtype; DROP only */
+  const int32_t *q_pos; /* [batch][W] positions of the window queries (causal mask) */
+  float scale;          /* softmax scale applied to q.k, usually 1/sqrt(head_dim) */
+} kvev_window;
+
+/*
+ * kvev_score -- per-token scores of every live slot of every KV head.
+ *
+ * Attention probability of window query (g, w) of KV head (b, h) for slot j
+ * ([H2O] "The Existence of Heavy Hitters"; [DROP] Jargon, "Log-sum-exp"):
+ *     p = exp(scale * q.k_j - lse)   if pos[j] <= q_pos[w], else 0.
+ * The sums run over the G query heads of the group ([H2O] FAQ on GQA) and the
+ * W window queries:
+ *   KVEV_SUM:  sum[j]  = sum_{w,g} p          ([H2O] "Formulating Cumulative
+ *              Attention Scores"; [SNAP] window sums)
+ *              with KVEV_ACCUMULATE: sum[j] += sum_{w,g} p ([H2O] lifecycle,
+ *              "Score Accumulation"); then sum must hold the previous scores.
+ *   KVEV_POOL: pooled[j] = max over i in [j-r, j+r] clamped to [0, n-1] of
+ *              sum_{w,g} p at i, r = (pool_kernel-1)/2 ([SNAP] "How it works").
+ *   KVEV_DROP: drop[j] = sum_{w,g} p/(1-p) * ||a_{g,w} - v_j|| ([DROP] Lemma 1
+ *              and the window sum), +inf for a term with p >= 1.
+ * Outputs are fp32 [batch][kv_heads][max_blocks*16]; only slots [0, n) are
+ * written.  Pass NULL for kinds not requested.  Reductions use a fixed order:
+ * results are bitwise reproducible run to run.
+ * Errors (KVEV_EINVAL): NULL cache/window/q/lse/q_pos; head_dim not 64/128;
+ * block_size != 16; group < 1; obs_window < 1 ([SNAP] Parameters: a zero
+ * window is refused); flags empty or unknown; POOL without `pooled`, or
+ * pool_kernel < 1 or even ([SNAP] Parameters); DROP without `a` or `drop`;
+ * SUM without `sum`; ACCUMULATE without SUM or combined with POOL or DROP.
+ * KVEV_EUNSUPPORTED: group*obs_window above 256 rows for DROP or 512 rows
+ * otherwise.  No workspace is used; `workspace` may be NULL.
+ */
+int kvev_score(const kvev_cache *cache, const kvev_window *win, int32_t flags,
+               int32_t pool_kernel, float *sum, float *pooled, float *drop, void *workspace,
+               size_t ws_bytes, void *stream);
+
+/*
+ * kvev_select -- each KV head's victims under a budget.
+ *
+ * With n = seq_len[b][h]: m = max(0, n - budget) tokens are evicted (the
+ * budget counts the recent window: [H2O] "Dual-Pool Budget Partitioning").
+ * Candidates are slots [0, n - recent_window): the newest recent_window slots
+ * are protected ([H2O] lifecycle; [SNAP] "drop the lowest outside the recent
+ * window").  The m candidates with the smallest (score, position) are chosen:
+ * equal scores evict the lower position ([SNAP] "Tie-breaking"), -0 equals +0
+ * and NaN ranks above +inf.  victims[b][h][0..m) receives their slot indices
+ * in ascending order, n_victims[b][h] = m.  score: fp32 [batch][kv_heads]
+ * [max_blocks*16] (for example `pooled` of kvev_score); victims: int32 with
+ * the same shape; n_victims: int32 [batch][kv_heads].  Bit-exact: the result
+ * depends only on the score bits.
+ * Errors (KVEV_EINVAL): NULL pointers; budget <= 0; recent_window < 0 or
+ * recent_window >= budget ([SNAP] Parameters).  No workspace is used.
+ */
+int kvev_select(const kvev_cache *cache, const float *score, int32_t budget,
+                int32_t recent_window, int32_t *victims, int32_t *n_victims, void *workspace,
+                size_t ws_bytes, void *stream);
+
+/*
+ * kvev_compact -- remove the victims and repack each KV head in place.
+ *
+ * Kept slots keep their order: kept slot s with rank r moves to slot r (K row,
+ * V row, pos, and score_or_null's entry), n becomes n' = n - n_victims
+ * ([H2O] "PagedAttention Memory Integration": in-place overwrite within the
+ * existing pages; [VTOK] section 3.3, stage 3: fill destinations fully, keep
+ * logical order).  The blocks at logical indices [ceil(n'/16), ceil(n/16))
+ * are then empty: their ids are appended to free_list in (b, h, logical
+ * block) order at free_list[*free_count ...], *free_count grows by their
+ * number, and their block_table entries become -1 ([VTOK] section 1: emptied
+ * blocks return to the free pool).  Slots [n', ceil(n'/16)*16) hold
+ * unspecified data afterwards.
+ * victims/n_victims: as written by kvev_select (ascending, inside [0, n)).
+ * free_list: int32 [free_capacity] device array; free_count: one int32 on
+ * the device.  stats: int64[5] on the device = {blocks_freed, rows_moved,
+ * bytes_moved (K and V rows moved, read + write), at_risk_rows (kept rows
+ * whose source lies inside the compacted range and is staged through the
+ * workspace first), status (0, or a bit set per inconsistent head: bit 0
+ * victims not ascending / out of range, bit 1 seq_len above capacity)}.
+ * Errors: KVEV_EINVAL for NULL pointers or a bad cache; KVEV_ENOSPACE when
+ * free_capacity < num_blocks (the list must be able to hold the whole pool)
+ * or ws_bytes < kvev_workspace_bytes(cache, 1, 1).
+ */
+int kvev_compact(const kvev_cache *cache, const int32_t *victims, const int32_t *n_victims,
+                 float *score_or_null, int32_t *free_list, int32_t *free_count,
+                 int32_t free_capacity, int64_t *stats, void *workspace, size_t ws_bytes,
+                 void *stream);
+
+/*
+ * kvev_window_attn -- helper outside the eviction step: the log-sum-exp and
+ * (optionally) the attention output of each window query, which a
+ * FlashAttention-style forward pass would produce ([DROP] Jargon,
+ * "Log-sum-exp"; "Why does the Triton kernel matter").
+ *     lse_out[b][hq][w] = log sum_{pos_j <= q_pos[w]} exp(scale * q.k_j)   (fp32)
+ *     a_out[b][hq][w][:] = sum_j exp(scale * q.k_j - lse) v_j           (cache dtype, may be NULL)
+ * fp32 arithmetic throughout.  A query that attends no key gets lse = -inf
+ * and a = 0.  Workspace: at least kvev_workspace_bytes(cache, group, W).
+ * Errors as for kvev_score; KVEV_ENOSPACE for a short workspace.
+ */
+int kvev_window_attn(const kvev_cache *cache, const kvev_window *win, float *lse_out,
+                     void *a_out, void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes needed by kvev_compact (group and obs_window ignored)
+ * and kvev_window_attn for this cache shape and window.  0 for a bad cache. */
+size_t kvev_workspace_bytes(const kvev_cache *cache, int32_t group, int32_t obs_window);
+
+/* Static description of a status code. */
+const char *kvev_strerror(int status);
+
+/* KVEV_ABI_VERSION of the loaded library. */
+int kvev_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVEV_H */

@@ -1,0 +1,289 @@
+"""Attention-score KV-cache eviction on MI355X: Python binding of libkvev.
+
+Thin ctypes layer over the C ABI in ``include/kvev.h``: it checks that the
+torch tensors handed over have the expected device, dtype, shape and
+layout, builds the argument structs and calls the library on the current
+torch stream.  Every step of score, select and compact runs in the HIP
+kernels of ``csrc/``; nothing here computes.  There is no fallback: if
+``libkvev.so`` is missing or cannot be loaded, importing the library raises.
+
+Names follow the C ABI: ``score``, ``select``, ``compact``,
+``window_attn``, ``workspace_bytes``.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvev.so")
+
+OK, EINVAL, ENOSPACE, EUNSUPPORTED, EDEVICE = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+SUM, POOL, DROP, ACCUMULATE = 1, 2, 4, 8
+BLOCK_SIZE = 16
+
+# the functions include/kvev.h declares
+EXPORTS = ("kvev_score", "kvev_select", "kvev_compact", "kvev_window_attn",
+           "kvev_workspace_bytes", "kvev_strerror", "kvev_abi_version")
+
+
+class KvevError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {strerror(status)} ({status})")
+        self.status = status
+
+
+class CacheStruct(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("k_pool", ctypes.c_void_p),
+                ("v_pool", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("seq_len", ctypes.c_void_p), ("pos", ctypes.c_void_p)]
+
+
+class WindowStruct(ctypes.Structure):
+    _fields_ = [("group", ctypes.c_int32), ("obs_window", ctypes.c_int32),
+                ("q", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("a", ctypes.c_void_p),
+                ("q_pos", ctypes.c_void_p), ("scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libkvev.so; raises if it is missing or lacks a declared symbol."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libkvev.so not built at {path}: run python -m "
+                          "kv_cache_eviction_qk_amd.build")
+    L = ctypes.CDLL(path)
+    for name in EXPORTS:
+        if not hasattr(L, name):
+            raise ImportError(f"{path} does not export {name}")
+    P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L.kvev_score.argtypes = [P, P, i32, i32, P, P, P, P, sz, P]
+    L.kvev_select.argtypes = [P, P, i32, i32, P, P, P, sz, P]
+    L.kvev_compact.argtypes = [P, P, P, P, P, P, i32, P, P, sz, P]
+    L.kvev_window_attn.argtypes = [P, P, P, P, P, sz, P]
+    L.kvev_workspace_bytes.argtypes = [P, i32, i32]
+    L.kvev_workspace_bytes.restype = sz
+    L.kvev_strerror.argtypes = [ctypes.c_int]
+    L.kvev_strerror.restype = ctypes.c_char_p
+    L.kvev_abi_version.argtypes = []
+    for f in (L.kvev_score, L.kvev_select, L.kvev_compact, L.kvev_window_attn,
+              L.kvev_abi_version):
+        f.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def strerror(status: int) -> str:
+    return load_library().kvev_strerror(status).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != OK:
+        raise KvevError(rc, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, numel: Optional[int] = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+
+
+@dataclasses.dataclass
+class Cache:
+    """One layer's paged KV cache on the GPU (layout of include/kvev.h)."""
+    k_pool: torch.Tensor        # [num_blocks, 16, D], float32 or bfloat16
+    v_pool: torch.Tensor
+    block_table: torch.Tensor   # int32 [B, Hkv, max_blocks]
+    seq_len: torch.Tensor       # int32 [B, Hkv]
+    pos: torch.Tensor           # int32 [B, Hkv, max_blocks*16]
+
+    @property
+    def batch(self) -> int:
+        return self.block_table.shape[0]
+
+    @property
+    def kv_heads(self) -> int:
+        return self.block_table.shape[1]
+
+    @property
+    def max_blocks(self) -> int:
+        return self.block_table.shape[2]
+
+    @property
+    def max_slots(self) -> int:
+        return self.max_blocks * BLOCK_SIZE
+
+    @property
+    def head_dim(self) -> int:
+        return self.k_pool.shape[-1]
+
+    @property
+    def units(self) -> int:
+        return self.batch * self.kv_heads
+
+    @property
+    def dtype_code(self) -> int:
+        return BF16 if self.k_pool.dtype == torch.bfloat16 else F32
+
+    def struct(self) -> CacheStruct:
+        if self.k_pool.dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("k_pool must be float32 or bfloat16")
+        _need(self.k_pool, "k_pool")
+        _need(self.v_pool, "v_pool", self.k_pool.dtype, self.k_pool.numel())
+        if self.k_pool.dim() != 3 or self.k_pool.shape[1] != BLOCK_SIZE:
+            raise ValueError("k_pool must be [num_blocks, 16, head_dim]")
+        _need(self.block_table, "block_table", torch.int32)
+        if self.block_table.dim() != 3:
+            raise ValueError("block_table must be [B, Hkv, max_blocks]")
+        _need(self.seq_len, "seq_len", torch.int32, self.units)
+        _need(self.pos, "pos", torch.int32, self.units * self.max_slots)
+        return CacheStruct(self.batch, self.kv_heads, self.head_dim, BLOCK_SIZE,
+                           self.max_blocks, self.k_pool.shape[0], self.dtype_code,
+                           _ptr(self.k_pool), _ptr(self.v_pool), _ptr(self.block_table),
+                           _ptr(self.seq_len), _ptr(self.pos))
+
+    def score_buffer(self, fill: float = 0.0) -> torch.Tensor:
+        return torch.full((self.batch, self.kv_heads, self.max_slots), fill, dtype=torch.float32,
+                          device=self.k_pool.device)
+
+
+def _window(cache: Cache, q, lse, q_pos, scale, group, a=None) -> WindowStruct:
+    B, Hkv, D = cache.batch, cache.kv_heads, cache.head_dim
+    if q.dim() != 4 or q.shape[0] != B or q.shape[1] != Hkv * group or q.shape[3] != D:
+        raise ValueError(f"q must be [B, Hkv*G, W, D] = [{B}, {Hkv * group}, W, {D}]")
+    W = q.shape[2]
+    _need(q, "q", cache.k_pool.dtype)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, B * Hkv * group * W)
+    if a is not None:
+        _need(a, "a", cache.k_pool.dtype, q.numel())
+    _need(q_pos, "q_pos", torch.int32, B * W)
+    return WindowStruct(group, W, _ptr(q), _ptr(lse), _ptr(a), _ptr(q_pos), float(scale))
+
+
+def workspace_bytes(cache: Cache, group: int = 1, obs_window: int = 1) -> int:
+    c = cache.struct()
+    return int(load_library().kvev_workspace_bytes(ctypes.byref(c), group, obs_window))
+
+
+def new_workspace(cache: Cache, group: int = 1, obs_window: int = 1) -> torch.Tensor:
+    return torch.zeros(workspace_bytes(cache, group, obs_window), dtype=torch.uint8,
+                       device=cache.k_pool.device)
+
+
+def score(cache: Cache, q: torch.Tensor, lse: torch.Tensor, q_pos: torch.Tensor, scale: float,
+          group: int, flags: int, pool_kernel: int = 1, sum: Optional[torch.Tensor] = None,
+          pooled: Optional[torch.Tensor] = None, drop: Optional[torch.Tensor] = None,
+          a: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """kvev_score.  Output buffers are allocated (filled with 0) when not given."""
+    L = load_library()
+    c = cache.struct()
+    w = _window(cache, q, lse, q_pos, scale, group, a)
+    if flags & SUM and sum is None:
+        sum = cache.score_buffer()
+    if flags & POOL and pooled is None:
+        pooled = cache.score_buffer()
+    if flags & DROP and drop is None:
+        drop = cache.score_buffer()
+    for t, nm in ((sum, "sum"), (pooled, "pooled"), (drop, "drop")):
+        if t is not None:
+            _need(t, nm, torch.float32, cache.units * cache.max_slots)
+    rc = L.kvev_score(ctypes.byref(c), ctypes.byref(w), flags, pool_kernel, _ptr(sum),
+                      _ptr(pooled), _ptr(drop), None, 0, _stream(stream))
+    _check(rc, "kvev_score")
+    return {"sum": sum, "pooled": pooled, "drop": drop}
+
+
+def select(cache: Cache, score_row: torch.Tensor, budget: int, recent_window: int,
+           victims: Optional[torch.Tensor] = None, n_victims: Optional[torch.Tensor] = None,
+           stream=None):
+    """kvev_select -> (victims [B, Hkv, max_slots] int32, n_victims [B, Hkv] int32)."""
+    L = load_library()
+    c = cache.struct()
+    _need(score_row, "score", torch.float32, cache.units * cache.max_slots)
+    dev = cache.k_pool.device
+    if victims is None:
+        victims = torch.full((cache.batch, cache.kv_heads, cache.max_slots), -1,
+                             dtype=torch.int32, device=dev)
+    if n_victims is None:
+        n_victims = torch.zeros((cache.batch, cache.kv_heads), dtype=torch.int32, device=dev)
+    _need(victims, "victims", torch.int32, cache.units * cache.max_slots)
+    _need(n_victims, "n_victims", torch.int32, cache.units)
+    rc = L.kvev_select(ctypes.byref(c), _ptr(score_row), budget, recent_window, _ptr(victims),
+                       _ptr(n_victims), None, 0, _stream(stream))
+    _check(rc, "kvev_select")
+    return victims, n_victims
+
+
+def compact(cache: Cache, victims: torch.Tensor, n_victims: torch.Tensor,
+            free_list: torch.Tensor, free_count: torch.Tensor, workspace: torch.Tensor,
+            stats: Optional[torch.Tensor] = None, score_row: Optional[torch.Tensor] = None,
+            stream=None) -> torch.Tensor:
+    """kvev_compact (mutates the cache in place) -> stats int64[5] on the GPU."""
+    L = load_library()
+    c = cache.struct()
+    _need(victims, "victims", torch.int32, cache.units * cache.max_slots)
+    _need(n_victims, "n_victims", torch.int32, cache.units)
+    _need(free_list, "free_list", torch.int32)
+    _need(free_count, "free_count", torch.int32, 1)
+    _need(workspace, "workspace", torch.uint8)
+    if stats is None:
+        stats = torch.zeros(5, dtype=torch.int64, device=cache.k_pool.device)
+    _need(stats, "stats", torch.int64, 5)
+    if score_row is not None:
+        _need(score_row, "score_row", torch.float32, cache.units * cache.max_slots)
+    rc = L.kvev_compact(ctypes.byref(c), _ptr(victims), _ptr(n_victims), _ptr(score_row),
+                        _ptr(free_list), _ptr(free_count), free_list.numel(), _ptr(stats),
+                        _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "kvev_compact")
+    return stats
+
+
+def window_attn(cache: Cache, q: torch.Tensor, q_pos: torch.Tensor, scale: float, group: int,
+                workspace: torch.Tensor, want_a: bool = False, lse_out=None, a_out=None,
+                stream=None):
+    """kvev_window_attn -> (lse fp32 [B, Hq, W], a [B, Hq, W, D] in the cache dtype or None)."""
+    L = load_library()
+    c = cache.struct()
+    w = _window(cache, q, None, q_pos, scale, group)
+    if lse_out is None:
+        lse_out = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _need(lse_out, "lse_out", torch.float32, q.shape[0] * q.shape[1] * q.shape[2])
+    if want_a and a_out is None:
+        a_out = torch.empty_like(q)
+    if a_out is not None:
+        _need(a_out, "a_out", q.dtype, q.numel())
+    _need(workspace, "workspace", torch.uint8)
+    rc = L.kvev_window_attn(ctypes.byref(c), ctypes.byref(w), _ptr(lse_out), _ptr(a_out),
+                            _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "kvev_window_attn")
+    return lse_out, a_out

@@ -1,0 +1,283 @@
+// api.hip -- the C ABI of libkvev (declared in include/kvev.h).
+//
+// Host side only: argument validation (every refusal happens before any
+// work is enqueued), launch geometry, workspace layout and error mapping.
+// All arithmetic runs in the kernels of score.hip, select.hip, compact.hip
+// and window_attn.hip.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "kvev.h"
+#include "kvev_kernels.h"
+
+namespace {
+
+constexpr int kCompactChunk = 1024;   // slots per compaction workgroup (compact.hip)
+constexpr int kWaChunk = 2048;        // keys per window-attention workgroup
+constexpr int kWaRowsPerWg = 128;     // window rows per window-attention workgroup
+constexpr size_t kMaxLds = 160 * 1024;
+constexpr int kMaxPoolKernel = 2049;  // halo of at most 64 blocks per side
+
+bool valid_cache(const kvev_cache *c) {
+  if (!c) return false;
+  if (c->batch < 1 || c->kv_heads < 1 || c->max_blocks < 1 || c->num_blocks < 1) return false;
+  if (c->block_size != KVEV_BLOCK_SIZE) return false;
+  if (c->head_dim != 64 && c->head_dim != 128) return false;
+  if (c->dtype != KVEV_F32 && c->dtype != KVEV_BF16) return false;
+  if (!c->k_pool || !c->v_pool || !c->block_table || !c->seq_len || !c->pos) return false;
+  if ((int64_t)c->max_blocks * KVEV_BLOCK_SIZE > INT32_MAX / 2) return false;
+  if ((int64_t)c->num_blocks * KVEV_BLOCK_SIZE > INT32_MAX / 2) return false;
+  if ((int64_t)c->batch * c->kv_heads > 65535) return false;
+  return true;
+}
+
+int elem_bytes(const kvev_cache *c) { return c->dtype == KVEV_BF16 ? 2 : 4; }
+
+size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct CompactLayout {
+  size_t src_of, new_pos, new_score, stage_k, stage_v, head_info, chunk_err, fc0, total;
+  int chunks, stage_rows;
+};
+
+CompactLayout compact_layout(const kvev_cache *c) {
+  CompactLayout L{};
+  const size_t units = (size_t)c->batch * c->kv_heads;
+  const size_t max_slots = (size_t)c->max_blocks * KVEV_BLOCK_SIZE;
+  const size_t row_bytes = (size_t)c->head_dim * elem_bytes(c);
+  L.chunks = (int)((max_slots + kCompactChunk - 1) / kCompactChunk);
+  // At-risk rows of a head are the kept slots in [first victim, n'): up to
+  // n' - 1 of them (evicting only slot 0 shifts every other row).
+  L.stage_rows = (int)max_slots;
+  size_t off = 0;
+  L.src_of = off; off = a256(off + units * max_slots * 4);
+  L.new_pos = off; off = a256(off + units * max_slots * 4);
+  L.new_score = off; off = a256(off + units * max_slots * 4);
+  L.stage_k = off; off = a256(off + units * (size_t)L.stage_rows * row_bytes);
+  L.stage_v = off; off = a256(off + units * (size_t)L.stage_rows * row_bytes);
+  L.head_info = off; off = a256(off + units * 4 * 4);
+  L.chunk_err = off; off = a256(off + units * (size_t)L.chunks * 4);
+  L.fc0 = off; off = a256(off + 4);
+  L.total = off;
+  return L;
+}
+
+struct WaLayout {
+  size_t part_m, part_l, part_acc, total;
+  int chunks, rows_pad;
+};
+
+WaLayout wa_layout(const kvev_cache *c, int group, int obs_window) {
+  WaLayout L{};
+  const size_t units = (size_t)c->batch * c->kv_heads;
+  const size_t max_slots = (size_t)c->max_blocks * KVEV_BLOCK_SIZE;
+  const int rows = group * obs_window;
+  L.chunks = (int)((max_slots + kWaChunk - 1) / kWaChunk);
+  L.rows_pad = ((rows + kWaRowsPerWg - 1) / kWaRowsPerWg) * kWaRowsPerWg;
+  const size_t parts = units * (size_t)L.rows_pad * L.chunks;
+  size_t off = 0;
+  L.part_m = off; off = a256(off + parts * 4);
+  L.part_l = off; off = a256(off + parts * 4);
+  L.part_acc = off; off = a256(off + parts * (size_t)c->head_dim * 4);
+  L.total = off;
+  return L;
+}
+
+int map_err(hipError_t e) { return e == hipSuccess ? KVEV_OK : KVEV_EDEVICE; }
+
+int check_window(const kvev_cache *c, const kvev_window *w) {
+  if (!w || !w->q || !w->lse || !w->q_pos) return KVEV_EINVAL;
+  if (w->group < 1 || w->obs_window < 1) return KVEV_EINVAL;
+  if ((int64_t)w->group * w->obs_window > 4096) return KVEV_EUNSUPPORTED;
+  if (!std::isfinite(w->scale)) return KVEV_EINVAL;
+  (void)c;
+  return KVEV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvev_abi_version(void) { return KVEV_ABI_VERSION; }
+
+const char *kvev_strerror(int status) {
+  switch (status) {
+    case KVEV_OK: return "ok";
+    case KVEV_EINVAL: return "invalid argument";
+    case KVEV_ENOSPACE: return "workspace or free list too small";
+    case KVEV_EUNSUPPORTED: return "shape or dtype not supported by the kernels";
+    case KVEV_EDEVICE: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t kvev_workspace_bytes(const kvev_cache *cache, int32_t group, int32_t obs_window) {
+  if (!valid_cache(cache)) return 0;
+  size_t need = compact_layout(cache).total;
+  if (group >= 1 && obs_window >= 1) {
+    const size_t wa = wa_layout(cache, group, obs_window).total;
+    if (wa > need) need = wa;
+  }
+  return need;
+}
+
+int kvev_score(const kvev_cache *cache, const kvev_window *win, int32_t flags,
+               int32_t pool_kernel, float *sum, float *pooled, float *drop, void *workspace,
+               size_t ws_bytes, void *stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  if (!valid_cache(cache)) return KVEV_EINVAL;
+  int rc = check_window(cache, win);
+  if (rc) return rc;
+  if (flags == 0 || (flags & ~(KVEV_SUM | KVEV_POOL | KVEV_DROP | KVEV_ACCUMULATE))) return KVEV_EINVAL;
+  if (!(flags & (KVEV_SUM | KVEV_POOL | KVEV_DROP))) return KVEV_EINVAL;
+  if ((flags & KVEV_SUM) && !sum) return KVEV_EINVAL;
+  if (flags & KVEV_POOL) {
+    if (!pooled || pool_kernel < 1 || pool_kernel % 2 == 0) return KVEV_EINVAL;
+    if (pool_kernel > kMaxPoolKernel) return KVEV_EUNSUPPORTED;
+  }
+  if ((flags & KVEV_DROP) && (!drop || !win->a)) return KVEV_EINVAL;
+  if ((flags & KVEV_ACCUMULATE) && (!(flags & KVEV_SUM) || (flags & (KVEV_POOL | KVEV_DROP))))
+    return KVEV_EINVAL;
+
+  kvev::ScoreArgs a{};
+  a.k_pool = static_cast<const uint8_t *>(cache->k_pool);
+  a.v_pool = static_cast<const uint8_t *>(cache->v_pool);
+  a.block_table = cache->block_table;
+  a.seq_len = cache->seq_len;
+  a.pos = cache->pos;
+  a.q = static_cast<const uint8_t *>(win->q);
+  a.a = static_cast<const uint8_t *>(win->a);
+  a.lse = win->lse;
+  a.q_pos = win->q_pos;
+  a.sum = sum;
+  a.pooled = pooled;
+  a.drop = drop;
+  a.units = cache->batch * cache->kv_heads;
+  a.Hkv = cache->kv_heads;
+  a.G = win->group;
+  a.W = win->obs_window;
+  a.max_blocks = cache->max_blocks;
+  a.num_blocks = cache->num_blocks;
+  a.rows = win->group * win->obs_window;
+  a.row_tiles = (a.rows + 15) / 16;
+  a.flags = flags & (KVEV_SUM | KVEV_POOL | KVEV_ACCUMULATE);
+  a.pool_r = (flags & KVEV_POOL) ? (pool_kernel - 1) / 2 : 0;
+  a.halo_blocks = (a.pool_r + KVEV_BLOCK_SIZE - 1) / KVEV_BLOCK_SIZE;
+  // tiles of up to 64 blocks (1024 keys); smaller when that leaves the chip underfilled
+  int tb = 64;
+  while (tb > 8 && (int64_t)a.units * ((cache->max_blocks + tb - 1) / tb) < 1024) tb /= 2;
+  a.tile_blocks = tb;
+  a.tiles_per_head = (cache->max_blocks + tb - 1) / tb;
+  a.c1 = win->scale * 1.4426950408889634f;
+  const int bf16 = cache->dtype == KVEV_BF16;
+  const int is_drop = (flags & KVEV_DROP) ? 1 : 0;
+  const size_t lds = kvev::score_lds_bytes(bf16, cache->head_dim, is_drop, a.row_tiles,
+                                           a.tile_blocks, a.halo_blocks);
+  if (lds > kMaxLds - 1024) return KVEV_EUNSUPPORTED;
+  if ((int64_t)a.units * a.tiles_per_head > INT32_MAX) return KVEV_EUNSUPPORTED;
+  return map_err(kvev::launch_score(a, bf16, cache->head_dim, is_drop,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int kvev_select(const kvev_cache *cache, const float *score, int32_t budget,
+                int32_t recent_window, int32_t *victims, int32_t *n_victims, void *workspace,
+                size_t ws_bytes, void *stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  if (!valid_cache(cache) || !score || !victims || !n_victims) return KVEV_EINVAL;
+  if (budget <= 0 || recent_window < 0 || recent_window >= budget) return KVEV_EINVAL;
+  kvev::SelectArgs a{};
+  a.score = score;
+  a.seq_len = cache->seq_len;
+  a.victims = victims;
+  a.n_victims = n_victims;
+  a.units = cache->batch * cache->kv_heads;
+  a.max_slots = cache->max_blocks * KVEV_BLOCK_SIZE;
+  a.budget = budget;
+  a.recent = recent_window;
+  return map_err(kvev::launch_select(a, static_cast<hipStream_t>(stream)));
+}
+
+int kvev_compact(const kvev_cache *cache, const int32_t *victims, const int32_t *n_victims,
+                 float *score_or_null, int32_t *free_list, int32_t *free_count,
+                 int32_t free_capacity, int64_t *stats, void *workspace, size_t ws_bytes,
+                 void *stream) {
+  if (!valid_cache(cache) || !victims || !n_victims || !free_list || !free_count || !stats)
+    return KVEV_EINVAL;
+  if (free_capacity < cache->num_blocks) return KVEV_ENOSPACE;
+  const CompactLayout L = compact_layout(cache);
+  if (!workspace || ws_bytes < L.total) return KVEV_ENOSPACE;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  kvev::CompactArgs a{};
+  a.k_pool = static_cast<uint8_t *>(cache->k_pool);
+  a.v_pool = static_cast<uint8_t *>(cache->v_pool);
+  a.block_table = cache->block_table;
+  a.seq_len = cache->seq_len;
+  a.pos = cache->pos;
+  a.score = score_or_null;
+  a.victims = victims;
+  a.n_victims = n_victims;
+  a.free_list = free_list;
+  a.free_count = free_count;
+  a.stats = stats;
+  a.src_of = reinterpret_cast<int32_t *>(ws + L.src_of);
+  a.new_pos = reinterpret_cast<int32_t *>(ws + L.new_pos);
+  a.new_score = reinterpret_cast<float *>(ws + L.new_score);
+  a.stage_k = ws + L.stage_k;
+  a.stage_v = ws + L.stage_v;
+  a.head_info = reinterpret_cast<int32_t *>(ws + L.head_info);
+  a.chunk_err = reinterpret_cast<int32_t *>(ws + L.chunk_err);
+  a.fc0 = reinterpret_cast<int32_t *>(ws + L.fc0);
+  a.units = cache->batch * cache->kv_heads;
+  a.max_blocks = cache->max_blocks;
+  a.max_slots = cache->max_blocks * KVEV_BLOCK_SIZE;
+  a.num_blocks = cache->num_blocks;
+  a.row_bytes = cache->head_dim * elem_bytes(cache);
+  a.stage_rows = L.stage_rows;
+  a.chunks = L.chunks;
+  a.free_capacity = free_capacity;
+  return map_err(kvev::launch_compact(a, static_cast<hipStream_t>(stream)));
+}
+
+int kvev_window_attn(const kvev_cache *cache, const kvev_window *win, float *lse_out,
+                     void *a_out, void *workspace, size_t ws_bytes, void *stream) {
+  if (!valid_cache(cache) || !win || !win->q || !win->q_pos || !lse_out) return KVEV_EINVAL;
+  if (win->group < 1 || win->obs_window < 1) return KVEV_EINVAL;
+  if ((int64_t)win->group * win->obs_window > 4096) return KVEV_EUNSUPPORTED;
+  if (!std::isfinite(win->scale)) return KVEV_EINVAL;
+  const WaLayout L = wa_layout(cache, win->group, win->obs_window);
+  if (!workspace || ws_bytes < L.total) return KVEV_ENOSPACE;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  kvev::WindowAttnArgs a{};
+  a.k_pool = static_cast<const uint8_t *>(cache->k_pool);
+  a.v_pool = static_cast<const uint8_t *>(cache->v_pool);
+  a.block_table = cache->block_table;
+  a.seq_len = cache->seq_len;
+  a.pos = cache->pos;
+  a.q = static_cast<const uint8_t *>(win->q);
+  a.q_pos = win->q_pos;
+  a.lse_out = lse_out;
+  a.a_out = static_cast<uint8_t *>(a_out);
+  a.part_m = reinterpret_cast<float *>(ws + L.part_m);
+  a.part_l = reinterpret_cast<float *>(ws + L.part_l);
+  a.part_acc = reinterpret_cast<float *>(ws + L.part_acc);
+  a.units = cache->batch * cache->kv_heads;
+  a.Hkv = cache->kv_heads;
+  a.G = win->group;
+  a.W = win->obs_window;
+  a.max_blocks = cache->max_blocks;
+  a.num_blocks = cache->num_blocks;
+  a.rows = win->group * win->obs_window;
+  a.chunk_slots = kWaChunk;
+  a.chunks = L.chunks;
+  a.want_a = a_out ? 1 : 0;
+  a.scale = win->scale;
+  return map_err(kvev::launch_window_attn(a, cache->dtype == KVEV_BF16, cache->head_dim,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

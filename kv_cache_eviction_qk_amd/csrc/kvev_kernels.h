@@ -1,0 +1,71 @@
+// kvev_kernels.h -- argument blocks and host-side launchers of the libkvev
+// kernels.  Internal to the library; the public interface is include/kvev.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvev {
+
+struct ScoreArgs {
+  const uint8_t *k_pool, *v_pool;
+  const int32_t *block_table, *seq_len, *pos;
+  const uint8_t *q, *a;
+  const float *lse;
+  const int32_t *q_pos;
+  float *sum, *pooled, *drop;
+  int32_t units, Hkv, G, W, max_blocks, num_blocks;
+  int32_t rows, row_tiles;       // G*W and ceil(rows / 16)
+  int32_t flags, pool_r, halo_blocks, tile_blocks, tiles_per_head;
+  float c1;                      // scale * log2(e)
+};
+
+struct SelectArgs {
+  const float *score;
+  const int32_t *seq_len;
+  int32_t *victims, *n_victims;
+  int32_t units, max_slots, budget, recent;
+};
+
+struct CompactArgs {
+  uint8_t *k_pool, *v_pool;
+  int32_t *block_table, *seq_len, *pos;
+  float *score;                 // optional score row moved with the tokens
+  const int32_t *victims, *n_victims;
+  int32_t *free_list, *free_count;
+  int64_t *stats;
+  // workspace regions
+  int32_t *src_of;              // [units][max_slots]: source of each destination rank
+  int32_t *new_pos;             // [units][max_slots]: pos of each kept rank
+  float *new_score;             // [units][max_slots]: score of each kept rank
+  uint8_t *stage_k, *stage_v;   // [units][stage_rows][row_bytes]: at-risk rows
+  int32_t *head_info;           // [units][4]: n before the call, first victim
+  int32_t *chunk_err;           // [units][chunks]
+  int32_t *fc0;                 // free_count before the call
+  int32_t units, max_blocks, max_slots, num_blocks, row_bytes, stage_rows, chunks,
+      free_capacity;
+};
+
+struct WindowAttnArgs {
+  const uint8_t *k_pool, *v_pool;
+  const int32_t *block_table, *seq_len, *pos;
+  const uint8_t *q;
+  const int32_t *q_pos;
+  float *lse_out;
+  uint8_t *a_out;
+  float *part_m, *part_l, *part_acc;   // workspace partials
+  int32_t units, Hkv, G, W, max_blocks, num_blocks, rows, chunk_slots, chunks, want_a;
+  float scale;
+};
+
+hipError_t launch_score(const ScoreArgs &a, int bf16, int head_dim, int drop, hipStream_t s);
+hipError_t launch_select(const SelectArgs &a, hipStream_t s);
+hipError_t launch_compact(const CompactArgs &a, hipStream_t s);
+hipError_t launch_window_attn(const WindowAttnArgs &a, int bf16, int head_dim, hipStream_t s);
+
+// LDS bytes of one score workgroup (0 when the row count does not fit).
+size_t score_lds_bytes(int bf16, int head_dim, int drop, int row_tiles, int tile_blocks,
+                       int halo_blocks);
+
+}  // namespace kvev

@@ -1,0 +1,326 @@
+// score.hip -- per-token eviction scores of a paged KV cache (gfx950).
+//
+// One workgroup (4 waves) scores a tile of consecutive 16-token blocks of one
+// KV head (b, h).  The G*W observation-window query rows of the head's GQA
+// group are staged once in LDS in MFMA fragment order; each wave streams its
+// own key blocks straight from HBM into registers (16-byte loads, the four
+// lane groups of a key row reading 64 contiguous bytes each) and computes
+//     s = q.k       on v_mfma_f32_16x16x32_bf16 (fp32 caches: 16x16x4 f32)
+//     p = exp(scale*s - lse) = exp2(s*c1 - lse*log2e), 0 when pos > q_pos
+// then reduces p over the rows in a fixed order (per lane, then across the
+// four lane groups).  DropKV also streams the value blocks and computes
+//     a.v on the same MFMA tiles, ||v||^2 on the VALU,
+//     ||a - v||^2 = ||a||^2 - 2 a.v + ||v||^2  (clamped at 0)
+//     term = p / (1 - p) * sqrt(||a - v||^2)     (+inf when p >= 1)
+// ([DROP] "fused Triton kernels": the expansion lets each value tile be read
+// once).  The SnapKV max-pool needs r neighbours on each side: a tile also
+// scores ceil(r/16) halo blocks on either side, so the pool is finished in
+// LDS without any exchange between workgroups ([SNAP] "How it works").
+// No float atomics: results are bitwise reproducible.
+#include <hip/hip_runtime.h>
+
+#include "kvev_device.h"
+#include "kvev_kernels.h"
+
+namespace kvev {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+template <bool BF16, int D>
+struct Geo {
+  static constexpr int EB = BF16 ? 2 : 4;   // element bytes
+  static constexpr int ROWB = D * EB;       // bytes of one key / query row
+  static constexpr int U = ROWB / 64;       // 16-byte units per lane per row
+  static constexpr int CPR = ROWB / 16;     // 16-byte chunks per row
+};
+
+__device__ __forceinline__ int remap_xcd(int id, int n) {
+  // Consecutive tiles of a head land on the same XCD (shared L2 for the
+  // query rows and the halo blocks): hardware deals workgroups to the 8 XCDs
+  // round robin.
+  if (n % 8 != 0) return id;
+  return (id % 8) * (n / 8) + id / 8;
+}
+
+}  // namespace
+
+template <bool BF16, int D, bool DROP>
+__global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
+  using G_ = Geo<BF16, D>;
+  constexpr int ROWB = G_::ROWB, U = G_::U, CPR = G_::CPR;
+  constexpr int NB = DROP ? 2 : 4;  // key blocks per wave iteration
+
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int s_minq;
+
+  const int RT = P.row_tiles;
+  uint4 *qfrag = reinterpret_cast<uint4 *>(smem);
+  uint4 *afrag = qfrag + RT * U * kWave;
+  float *lse2 = reinterpret_cast<float *>(afrag + (DROP ? RT * U * kWave : 0));
+  int *qposr = reinterpret_cast<int *>(lse2 + RT * 16);
+  float *an2 = reinterpret_cast<float *>(qposr + RT * 16);
+  float *S_lds = an2 + (DROP ? RT * 16 : 0);
+  const int span_blocks = P.tile_blocks + 2 * P.halo_blocks;
+  float *D_lds = S_lds + span_blocks * 16;
+
+  const int wg = remap_xcd(blockIdx.x, gridDim.x);
+  const int u = wg / P.tiles_per_head;
+  const int tile = wg % P.tiles_per_head;
+  if (u >= P.units) return;
+  const int b = u / P.Hkv, h = u % P.Hkv;
+  const int n = P.seq_len[u];
+  const int max_slots = P.max_blocks * kBlock;
+  if (n <= 0 || n > max_slots) return;  // empty or inconsistent head: nothing to score
+  const int nb = (n + kBlock - 1) / kBlock;
+  const int tb0 = tile * P.tile_blocks;
+  if (tb0 >= nb) return;
+  const int tb1 = min(tb0 + P.tile_blocks, nb);
+  const int cb0 = max(0, tb0 - P.halo_blocks), cb1 = min(nb, tb1 + P.halo_blocks);
+
+  // ---- stage the group's window rows in fragment order
+  const int Hq = P.Hkv * P.G;
+  const size_t row0 = ((size_t)b * Hq + (size_t)h * P.G) * P.W;  // first row of the group
+  const int rows = P.rows;
+  if (threadIdx.x == 0) s_minq = INT_MAX;
+  {
+    const uint8_t *qsrc = P.q + row0 * ROWB;
+    const uint8_t *asrc = DROP ? P.a + row0 * ROWB : nullptr;
+    const int nchunks = RT * 16 * CPR;
+    for (int c = threadIdx.x; c < nchunks; c += kThreads) {
+      const int r = c / CPR, cc = c % CPR;
+      const int lg = cc / U, j = cc % U;
+      const int dst = ((r / 16) * U + j) * kWave + lg * 16 + (r % 16);
+      uint4 v = make_uint4(0, 0, 0, 0), av = make_uint4(0, 0, 0, 0);
+      if (r < rows) {
+        v = ld16(qsrc + (size_t)r * ROWB + cc * 16);
+        if constexpr (DROP) av = ld16(asrc + (size_t)r * ROWB + cc * 16);
+      }
+      qfrag[dst] = v;
+      if constexpr (DROP) {
+        afrag[dst] = av;
+        // ||a||^2 of the row: the CPR chunks of a row sit in CPR consecutive lanes
+        float ss = sumsq_unit<BF16>(av);
+#pragma unroll
+        for (int o = CPR / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+        if (cc == 0) an2[r] = ss;
+      }
+    }
+    for (int r = threadIdx.x; r < RT * 16; r += kThreads) {
+      if (r < rows) {
+        lse2[r] = P.lse[row0 + r] * kLog2e;
+        qposr[r] = P.q_pos[(size_t)b * P.W + (r % P.W)];
+      } else {
+        lse2[r] = __builtin_inff();  // padding rows: p = exp2(-inf) = 0
+        qposr[r] = INT_MAX;
+      }
+    }
+  }
+  __syncthreads();
+  for (int w = threadIdx.x; w < P.W; w += kThreads) atomicMin(&s_minq, P.q_pos[(size_t)b * P.W + w]);
+  __syncthreads();
+  const int minq = s_minq;
+
+  // ---- stream this wave's key blocks
+  const int l = lane_id(), lr = l & 15, lg = l >> 4;
+  const int wv = threadIdx.x / kWave;
+  const int nblk = cb1 - cb0;
+  const int wb0 = cb0 + (nblk * wv) / kWaves, wb1 = cb0 + (nblk * (wv + 1)) / kWaves;
+  const int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
+  const int32_t *ps = P.pos + (size_t)u * max_slots;
+  const size_t lane_off = (size_t)lr * ROWB + (size_t)lg * (ROWB / 4);
+  const float c1 = P.c1;
+
+  uint4 kf[NB][U], vf[NB][U];
+  int kp[NB];
+  bool badb[NB];
+
+  auto load = [&](int cur) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int blk = cur + i;
+      const int id = blk < wb1 ? bt[blk] : 0;
+      badb[i] = blk < wb1 && (id < 0 || id >= P.num_blocks);
+      if (blk < wb1 && !badb[i]) {
+        const size_t base = (size_t)id * kBlock * ROWB + lane_off;
+#pragma unroll
+        for (int j = 0; j < U; ++j) kf[i][j] = ld16(P.k_pool + base + 16 * j);
+        if constexpr (DROP) {
+#pragma unroll
+          for (int j = 0; j < U; ++j) vf[i][j] = ld16(P.v_pool + base + 16 * j);
+        }
+        kp[i] = ps[blk * kBlock + lr];
+      } else {
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+          kf[i][j] = make_uint4(0, 0, 0, 0);
+          if constexpr (DROP) vf[i][j] = make_uint4(0, 0, 0, 0);
+        }
+        kp[i] = INT_MIN;
+      }
+    }
+  };
+
+  for (int cur = wb0; cur < wb1; cur += NB) {
+    load(cur);
+    float psum[NB], pdrop[NB], vn2[NB];
+    bool need_mask = false;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      psum[i] = 0.f;
+      pdrop[i] = 0.f;
+      need_mask |= kp[i] > minq;
+      if constexpr (DROP) {
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < U; ++j) ss += sumsq_unit<BF16>(vf[i][j]);
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        vn2[i] = ss;  // ||v||^2 of key lr, in every lane group
+      }
+    }
+    need_mask = __any(need_mask);
+
+    for (int rt = 0; rt < RT; ++rt) {
+      uint4 qa[U], aa[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        qa[j] = qfrag[(rt * U + j) * kWave + l];
+        if constexpr (DROP) aa[j] = afrag[(rt * U + j) * kWave + l];
+      }
+      const float4 L = *reinterpret_cast<const float4 *>(&lse2[rt * 16 + lg * 4]);
+      const int4 Qp = *reinterpret_cast<const int4 *>(&qposr[rt * 16 + lg * 4]);
+      float4 A2 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (DROP) A2 = *reinterpret_cast<const float4 *>(&an2[rt * 16 + lg * 4]);
+      floatx4 acc[NB], av[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+        av[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          acc[i] = mfma_unit<BF16>(qa[j], kf[i][j], acc[i]);
+          if constexpr (DROP) av[i] = mfma_unit<BF16>(aa[j], vf[i][j], av[i]);
+        }
+      }
+      const float Le[4] = {L.x, L.y, L.z, L.w};
+      const int Qe[4] = {Qp.x, Qp.y, Qp.z, Qp.w};
+      const float Ae[4] = {A2.x, A2.y, A2.z, A2.w};
+      if (!need_mask) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = fmaf(acc[i][e], c1, -Le[e]);
+            const float p = __builtin_amdgcn_exp2f(x);
+            psum[i] += p;
+            if constexpr (DROP) {
+              const float X = fmaxf(fmaf(-2.f, av[i][e], Ae[e] + vn2[i]), 0.f);
+              const float t = (x >= 0.f) ? __builtin_inff()
+                                         : p * __builtin_amdgcn_rcpf(1.f - p) * __builtin_sqrtf(X);
+              pdrop[i] += t;
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool live = kp[i] <= Qe[e];
+            const float x = fmaf(acc[i][e], c1, -Le[e]);
+            const float p = live ? __builtin_amdgcn_exp2f(x) : 0.f;
+            psum[i] += p;
+            if constexpr (DROP) {
+              const float X = fmaxf(fmaf(-2.f, av[i][e], Ae[e] + vn2[i]), 0.f);
+              float t = (x >= 0.f) ? __builtin_inff()
+                                   : p * __builtin_amdgcn_rcpf(1.f - p) * __builtin_sqrtf(X);
+              pdrop[i] += live ? t : 0.f;
+            }
+          }
+        }
+      }
+    }
+    // fixed-order reduction over the four lane groups (rows 4*lg .. 4*lg+3)
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      float s = psum[i];
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      float d = pdrop[i];
+      if constexpr (DROP) {
+        d += __shfl_xor(d, 16);
+        d += __shfl_xor(d, 32);
+      }
+      const int blk = cur + i;
+      if (blk < wb1 && lg == 0) {
+        // a block id outside the pool gives NaN scores for its slots
+        S_lds[(blk - cb0) * kBlock + lr] = badb[i] ? __builtin_nanf("") : s;
+        if constexpr (DROP) D_lds[(blk - cb0) * kBlock + lr] = badb[i] ? __builtin_nanf("") : d;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- outputs for the tile's own slots
+  const int s0 = tb0 * kBlock, s1 = min(tb1 * kBlock, n);
+  const int base = cb0 * kBlock;
+  const size_t orow = (size_t)u * max_slots;
+  for (int s = s0 + threadIdx.x; s < s1; s += kThreads) {
+    const float S = S_lds[s - base];
+    if (P.flags & 1) {  // SUM (with ACCUMULATE: add to the stored score)
+      float v = S;
+      if (P.flags & 8) v = P.sum[orow + s] + S;
+      P.sum[orow + s] = v;
+    }
+    if (P.flags & 2) {  // POOL: clamped max over [s - r, s + r]
+      const int lo = max(0, s - P.pool_r), hi = min(n - 1, s + P.pool_r);
+      float m = S_lds[lo - base];
+      for (int i = lo + 1; i <= hi; ++i) m = fmaxf(m, S_lds[i - base]);
+      P.pooled[orow + s] = m;
+    }
+    if constexpr (DROP) P.drop[orow + s] = D_lds[s - base];
+  }
+}
+
+size_t score_lds_bytes(int bf16, int head_dim, int drop, int row_tiles, int tile_blocks,
+                       int halo_blocks) {
+  const size_t rowb = (size_t)head_dim * (bf16 ? 2 : 4);
+  const size_t frag = (size_t)row_tiles * 16 * rowb;  // bytes of one staged row set
+  size_t bytes = frag * (drop ? 2 : 1);
+  bytes += (size_t)row_tiles * 16 * 4 * (drop ? 3 : 2);
+  bytes += (size_t)(tile_blocks + 2 * halo_blocks) * 16 * 4 * (drop ? 2 : 1);
+  return bytes;
+}
+
+template <bool BF16, int D, bool DROP>
+static hipError_t launch_t(const ScoreArgs &a, hipStream_t s) {
+  const size_t lds = score_lds_bytes(BF16, D, DROP, a.row_tiles, a.tile_blocks, a.halo_blocks);
+  auto fn = score_kernel<BF16, D, DROP>;
+  static size_t lds_set = 0;  // largest dynamic LDS size enabled for this variant
+  if (lds > 65536 && lds > lds_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    lds_set = lds;
+  }
+  const unsigned grid = (unsigned)a.units * (unsigned)a.tiles_per_head;
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_score(const ScoreArgs &a, int bf16, int head_dim, int drop, hipStream_t s) {
+  if (bf16) {
+    if (head_dim == 128) return drop ? launch_t<true, 128, true>(a, s) : launch_t<true, 128, false>(a, s);
+    return drop ? launch_t<true, 64, true>(a, s) : launch_t<true, 64, false>(a, s);
+  }
+  if (head_dim == 128) return drop ? launch_t<false, 128, true>(a, s) : launch_t<false, 128, false>(a, s);
+  return drop ? launch_t<false, 64, true>(a, s) : launch_t<false, 64, false>(a, s);
+}
+
+}  // namespace kvev

@@ -1,0 +1,169 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every function
+include/kvev.h declares, and refuses bad arguments on the host before any
+work is enqueued (no GPU is touched: every call here fails validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import torch
+
+import kv_cache_eviction_qk_amd as K
+
+# These calls pass fake device pointers and rely on host validation refusing
+# them; they are run only where no GPU can be reached.
+pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                reason="fake-pointer validation tests run only without a GPU")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000   # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "kvev.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(kvev_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_function():
+    L = K.load_library()
+    names = declared_functions()
+    assert set(names) == set(K.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.kvev_abi_version() == 1
+    for code in (0, -1, -2, -3, -4):
+        assert K.strerror(code)
+
+
+def cache(**kw):
+    d = dict(batch=2, kv_heads=2, head_dim=128, block_size=16, max_blocks=8, num_blocks=32,
+             dtype=K.BF16, k_pool=FAKE, v_pool=FAKE, block_table=FAKE, seq_len=FAKE, pos=FAKE)
+    d.update(kw)
+    return K.CacheStruct(**d)
+
+
+def window(**kw):
+    d = dict(group=2, obs_window=4, q=FAKE, lse=FAKE, a=FAKE, q_pos=FAKE, scale=0.1)
+    d.update(kw)
+    return K.WindowStruct(**d)
+
+
+def score(c, w, flags=K.SUM, pool=1, s=FAKE, p=FAKE, d=FAKE):
+    return K.load_library().kvev_score(ctypes.byref(c) if c else None,
+                                       ctypes.byref(w) if w else None, flags, pool, s, p, d,
+                                       None, 0, None)
+
+
+BAD_CACHES = [dict(head_dim=96), dict(head_dim=256), dict(block_size=32), dict(batch=0),
+              dict(kv_heads=0), dict(max_blocks=0), dict(num_blocks=0), dict(dtype=7),
+              dict(k_pool=None), dict(v_pool=None), dict(block_table=None), dict(seq_len=None),
+              dict(pos=None)]
+
+
+@pytest.mark.parametrize("kw", BAD_CACHES)
+def test_bad_cache_refused_everywhere(kw):
+    L = K.load_library()
+    c = cache(**kw)
+    assert score(c, window()) == K.EINVAL
+    assert L.kvev_select(ctypes.byref(c), FAKE, 8, 2, FAKE, FAKE, None, 0, None) == K.EINVAL
+    assert L.kvev_compact(ctypes.byref(c), FAKE, FAKE, None, FAKE, FAKE, 1 << 20, FAKE, FAKE,
+                          1 << 40, None) == K.EINVAL
+    assert L.kvev_window_attn(ctypes.byref(c), ctypes.byref(window()), FAKE, None, FAKE,
+                              1 << 40, None) == K.EINVAL
+    assert L.kvev_workspace_bytes(ctypes.byref(c), 1, 1) == 0
+
+
+@pytest.mark.parametrize("wkw,flags,pool,expect", [
+    (dict(group=0), K.SUM, 1, K.EINVAL),
+    (dict(obs_window=0), K.SUM, 1, K.EINVAL),         # SnapKV: a zero window is refused
+    (dict(q=None), K.SUM, 1, K.EINVAL),
+    (dict(lse=None), K.SUM, 1, K.EINVAL),
+    (dict(q_pos=None), K.SUM, 1, K.EINVAL),
+    (dict(scale=float("nan")), K.SUM, 1, K.EINVAL),
+    (dict(), 0, 1, K.EINVAL),                          # no score kind
+    (dict(), 16, 1, K.EINVAL),                         # unknown flag
+    (dict(), K.ACCUMULATE, 1, K.EINVAL),               # accumulate without SUM
+    (dict(), K.POOL, 0, K.EINVAL),
+    (dict(), K.POOL, 4, K.EINVAL),                     # SnapKV: poolKernel must be odd
+    (dict(), K.POOL, -3, K.EINVAL),
+    (dict(), K.POOL, 2051, K.EUNSUPPORTED),
+    (dict(), K.POOL | K.SUM | K.ACCUMULATE, 3, K.EINVAL),
+    (dict(), K.DROP | K.SUM | K.ACCUMULATE, 1, K.EINVAL),
+    (dict(a=None), K.DROP, 1, K.EINVAL),
+    (dict(group=64, obs_window=65), K.SUM, 1, K.EUNSUPPORTED),
+    (dict(group=8, obs_window=64), K.DROP, 1, K.EUNSUPPORTED),   # 512 DROP rows exceed LDS
+])
+def test_score_refusals(wkw, flags, pool, expect):
+    assert score(cache(), window(**wkw), flags, pool) == expect
+
+
+def test_score_missing_outputs():
+    assert score(cache(), window(), K.SUM, s=None) == K.EINVAL
+    assert score(cache(), window(), K.POOL, 3, p=None) == K.EINVAL
+    assert score(cache(), window(), K.DROP, d=None) == K.EINVAL
+    assert score(None, window()) == K.EINVAL
+    assert score(cache(), None) == K.EINVAL
+
+
+@pytest.mark.parametrize("budget,recent", [(0, 0), (-1, 0), (8, 8), (8, 9), (8, -1)])
+def test_select_refusals(budget, recent):
+    """recentWindow >= budget is refused; the budget must be positive."""
+    L = K.load_library()
+    c = cache()
+    assert L.kvev_select(ctypes.byref(c), FAKE, budget, recent, FAKE, FAKE, None, 0,
+                         None) == K.EINVAL
+    assert L.kvev_select(ctypes.byref(c), None, 8, 2, FAKE, FAKE, None, 0, None) == K.EINVAL
+
+
+def test_compact_refusals():
+    L = K.load_library()
+    c = cache()
+    ws = L.kvev_workspace_bytes(ctypes.byref(c), 1, 1)
+    assert ws > 0
+    args = [FAKE, FAKE, None, FAKE, FAKE, 64, FAKE, FAKE, ws, None]
+    for i in (0, 1, 3, 4, 6):
+        a = list(args); a[i] = None
+        assert L.kvev_compact(ctypes.byref(c), *a) == K.EINVAL
+    a = list(args); a[5] = 31              # free list smaller than the pool
+    assert L.kvev_compact(ctypes.byref(c), *a) == K.ENOSPACE
+    a = list(args); a[8] = ws - 1          # short workspace
+    assert L.kvev_compact(ctypes.byref(c), *a) == K.ENOSPACE
+    a = list(args); a[7] = None
+    assert L.kvev_compact(ctypes.byref(c), *a) == K.ENOSPACE
+
+
+def test_window_attn_refusals():
+    L = K.load_library()
+    c = cache()
+    w = window()
+    ws = L.kvev_workspace_bytes(ctypes.byref(c), 2, 4)
+    # a 16-byte workspace is short for any shape (the partials alone need more)
+    assert L.kvev_window_attn(ctypes.byref(c), ctypes.byref(w), FAKE, None, FAKE, 16,
+                              None) == K.ENOSPACE
+    assert L.kvev_window_attn(ctypes.byref(c), ctypes.byref(w), FAKE, None, None, ws,
+                              None) == K.ENOSPACE
+    assert L.kvev_window_attn(ctypes.byref(c), ctypes.byref(w), None, None, FAKE, ws,
+                              None) == K.EINVAL
+    w0 = window(obs_window=0)
+    assert L.kvev_window_attn(ctypes.byref(c), ctypes.byref(w0), FAKE, None, FAKE, ws,
+                              None) == K.EINVAL
+
+
+def test_workspace_grows_with_the_cache():
+    L = K.load_library()
+    small = L.kvev_workspace_bytes(ctypes.byref(cache(max_blocks=8)), 1, 1)
+    big = L.kvev_workspace_bytes(ctypes.byref(cache(max_blocks=64)), 1, 1)
+    assert big > 7 * small
+    # the staged at-risk rows may cover every slot of every head
+    assert small >= 2 * 2 * 8 * 16 * 128 * 2 * 2
+
+
+def test_binding_has_no_cpu_path():
+    """The binding only marshals: CPU tensors are refused, nothing is computed."""
+    c = K.Cache(torch.zeros(4, 16, 64), torch.zeros(4, 16, 64),
+                torch.zeros(1, 1, 4, dtype=torch.int32), torch.zeros(1, 1, dtype=torch.int32),
+                torch.zeros(1, 1, 64, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        c.struct()
