@@ -1,0 +1,300 @@
+"""Throughput of one score -> select -> compact pass of attention-score KV-cache
+eviction on one MI355X, on seeded synthetic inputs.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is the whole eviction path for one layer's cache: kvev_score (SnapKV
+window sum + max-pool over the last W prompt queries), kvev_select (budget,
+protected recent window) and kvev_compact (in-place repack, emptied blocks
+to the free list).  Every step works on its own pristine copy of the cache,
+prepared before the timed region, so the timed region holds only the
+eviction kernels; L2 and the Infinity Cache are flushed before it starts,
+so the keys come from HBM.
+
+Prints one JSON line: value = scored KV tokens per second (batch x context
+tokens, every KV head scored, selected and compacted), plus the HBM roofline
+of the dominant kernel (score) measured with HIP events on the launch stream
+and the CPU oracle timed on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="snapkv_prefill_32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-steps", action="store_true",
+                    help="only run the timed steps (for rocprofv3 runs)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(workload, kernel_src):
+    """HBM bytes per launch of the score kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"score_{workload}_hbm_counters.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except ValueError:
+        return None
+    if d.get("score_source_sha256_16") != source_hash(kernel_src):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import kv_cache_eviction_qk_amd as K
+    import synth
+
+    K.load_library()  # fails loudly when the HIP library is missing
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    cfg = synth.CONFIGS[args.workload]
+    if cfg.decode_steps:
+        print(json.dumps({"error": f"{args.workload} is a decode schedule, not a one-shot pass"}))
+        sys.exit(2)
+    kind = cfg.flags[0]
+    flag = {"sum": K.SUM, "pool": K.POOL, "drop": K.DROP}[kind]
+    steps, warm = args.steps, args.warmup
+    copies = max(steps, warm)
+
+    t0 = time.time()
+    case = synth.make_case(cfg)
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    pristine = K.Cache(dev(case["k_pool"]), dev(case["v_pool"]), dev(case["block_table"]),
+                       dev(case["seq_len"]), dev(case["pos"]))
+    q, q_pos = dev(case["q"]), dev(case["q_pos"])
+    B, Hkv, G, W, D = cfg.B, cfg.Hkv, cfg.G, cfg.W, cfg.D
+    # forward-pass outputs for the window: LSE (and a for DropKV), made by the helper kernel
+    ws_wa = K.new_workspace(pristine, G, W)
+    lse, a = K.window_attn(pristine, q, q_pos, cfg.softmax_scale, G, ws_wa, want_a=(kind == "drop"))
+    torch.cuda.synchronize()
+    del ws_wa
+    log("window LSE ready")
+
+    # one pristine copy of the mutable cache state per step
+    caches = []
+    for i in range(copies):
+        caches.append(K.Cache(pristine.k_pool.clone(), pristine.v_pool.clone(),
+                              pristine.block_table.clone(), pristine.seq_len.clone(),
+                              pristine.pos.clone()))
+    nb = case["num_blocks"]
+    free_lists = [torch.full((nb,), -1, dtype=torch.int32, device="cuda") for _ in range(copies)]
+    free_counts = [torch.zeros(1, dtype=torch.int32, device="cuda") for _ in range(copies)]
+    ws = K.new_workspace(pristine)
+    score_out = pristine.score_buffer()
+    victims = torch.empty((B, Hkv, pristine.max_slots), dtype=torch.int32, device="cuda")
+    n_victims = torch.empty((B, Hkv), dtype=torch.int32, device="cuda")
+    stats = torch.zeros(5, dtype=torch.int64, device="cuda")
+    scrub = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device="cuda")  # 1 GiB
+
+    def restore(i):
+        c = caches[i]
+        c.k_pool.copy_(pristine.k_pool)
+        c.v_pool.copy_(pristine.v_pool)
+        c.block_table.copy_(pristine.block_table)
+        c.seq_len.copy_(pristine.seq_len)
+        c.pos.copy_(pristine.pos)
+        free_lists[i].fill_(-1)
+        free_counts[i].zero_()
+
+    def flush_caches():
+        scrub.add_(1.0)  # 2 GiB of HBM traffic evicts L2 and the 256 MB Infinity Cache
+
+    outs = {"sum": None, "pooled": None, "drop": None}
+    outs[{"sum": "sum", "pool": "pooled", "drop": "drop"}[kind]] = score_out
+
+    def step(i, ev=None):
+        c = caches[i]
+        if ev is not None:
+            ev[0].record()
+        K.score(c, q, lse, q_pos, cfg.softmax_scale, G, flag, cfg.pool_kernel, sum=outs["sum"],
+                pooled=outs["pooled"], drop=outs["drop"], a=a)
+        if ev is not None:
+            ev[1].record()
+        K.select(c, score_out, cfg.budget, cfg.recent, victims, n_victims, ws)
+        if ev is not None:
+            ev[2].record()
+        K.compact(c, victims, n_victims, free_lists[i], free_counts[i], ws, stats)
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(warm):
+        step(i)
+    torch.cuda.synchronize()
+    st = stats.cpu().numpy().tolist()
+    for i in range(copies):
+        restore(i)
+    flush_caches()
+    torch.cuda.synchronize()
+    log(f"warmup done; stats of one pass {st}")
+
+    # ---- timed region: exactly `steps` passes
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_total = e0.elapsed_time(e1)
+    if args.profile_steps:
+        log(f"profile run done: {ms_total / steps:.4f} ms/step")
+        return
+    ms_step = ms_total / steps
+    tokens = B * cfg.L
+    value = tokens * steps / (ms_total / 1e3)
+
+    # ---- per-kernel durations (HIP events on the launch stream), same work again
+    for i in range(steps):
+        restore(i)
+    flush_caches()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t_score = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    t_select = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    t_compact = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
+    st = stats.cpu().numpy().tolist()
+    nv = n_victims.cpu().numpy()
+
+    # algorithmic bytes (what the method must move; see the design notes)
+    ms_ = pristine.max_slots
+    eb = 2 if cfg.dtype == "bf16" else 4
+    units = B * Hkv
+    n = cfg.L
+    key_bytes = units * n * D * eb
+    val_bytes = key_bytes if kind == "drop" else 0
+    rows = G * W
+    q_bytes = B * Hkv * rows * D * eb * (2 if kind == "drop" else 1) + B * Hkv * rows * 4
+    pos_bytes = units * n * 4
+    bt_bytes = units * math.ceil(n / 16) * 4
+    out_bytes = units * n * 4
+    score_bytes = key_bytes + val_bytes + q_bytes + pos_bytes + bt_bytes + out_bytes
+    n_vic = int(nv.sum())
+    cand = units * max(0, n - cfg.recent)
+    select_bytes = cand * 4 + n_vic * 4
+    rows_moved = int(st[1])
+    compact_bytes = n_vic * 4 + rows_moved * 2 * D * eb * 2 + rows_moved * 4 * 2
+    pass_bytes = score_bytes + select_bytes + compact_bytes
+    achieved = score_bytes / (t_score / 1e3) / 1e9
+    src = os.path.join(ROOT, "kv_cache_eviction_qk_amd", "csrc", "score.hip")
+    traffic = read_traffic(args.workload, src)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, cfg, kind)
+
+    out = {
+        "metric": "scored KV tokens/sec (score+select+compact) at 32K ctx; % of peak HBM GB/s",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; spans planted on window-query directions)",
+        "config": {"workload": args.workload, "batch": B, "kv_heads": Hkv, "group": G,
+                   "head_dim": D, "context": n, "obs_window": W, "pool_kernel": cfg.pool_kernel,
+                   "budget": cfg.budget, "recent_window": cfg.recent, "score": kind,
+                   "block_size": 16, "accumulate": "fp32"},
+        "pipeline_hbm_frac": pass_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "pipeline_bytes": pass_bytes,
+        "stage_ms": {"score": t_score, "select": t_select, "compact": t_compact},
+        "wall_s": wall,
+        "blocks_freed_per_pass": int(st[0]),
+        "rows_moved_per_pass": rows_moved,
+        "roofline": {"kernel": "score_kernel", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "algorithmic_bytes": score_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(case, cfg, kind):
+    """The oracle (score + select + compact) on the host cores, on a bounded
+    sample of the same workload; its LSE is its own (not the GPU's)."""
+    import numpy as np
+
+    import oracle
+    threads = oracle.default_threads()
+    units = cfg.B * cfg.Hkv
+    sample = list(range(min(units, max(threads, 8))))
+    log(f"cpu baseline: oracle on {len(sample)} of {units} KV heads, {threads} threads")
+    lse64, a64 = oracle.lse_a(case, want_a=(kind == "drop"), units=sample, nthreads=threads)
+    import synth
+    lse32 = lse64.astype(np.float32)
+    a_enc = synth.encode(a64, cfg.dtype) if a64 is not None else None
+    flag = {"sum": oracle.SUM, "pool": oracle.POOL, "drop": oracle.DROP}[kind]
+    t0 = time.perf_counter()
+    out = oracle.score(case, lse32, flag, cfg.pool_kernel, a_enc=a_enc, units=sample,
+                       nthreads=threads)
+    key = {"sum": "sum", "pool": "pooled", "drop": "drop"}[kind]
+    s32 = np.nan_to_num(out[key], nan=0.0).astype(np.float32)
+    seq = case["seq_len"].copy().reshape(-1)
+    mask = np.zeros(units, bool)
+    mask[sample] = True
+    seq_s = np.where(mask, seq, 0).astype(np.int32)   # heads outside the sample hold no tokens
+    vic, nv = oracle.select(s32, seq_s, cfg.budget, cfg.recent)
+    sub = dict(case)
+    sub["seq_len"] = seq_s.reshape(case["seq_len"].shape)
+    oracle.compact(sub, vic, nv)
+    dt = time.perf_counter() - t0
+    tokens = cfg.L * len(sample) / cfg.Hkv   # scored tokens the sample covers
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(sample)} of {units} KV heads (full context {cfg.L}); "
+                      f"{dt:.1f} s of score+select+compact"}
+
+
+if __name__ == "__main__":
+    main()

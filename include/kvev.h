@@ -12,7 +12,8 @@
  * ---------------------------------------
  * - Every data pointer is a DEVICE pointer owned by the caller (for example a
  *   torch tensor's data_ptr()).  The library allocates nothing, frees nothing
- *   and keeps no state between calls; it is reentrant.
+ *   and keeps no state of its own (what persists between calls lives in the
+ *   caller's workspace); calls on different workspaces are independent.
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Each
  *   call only enqueues work on that stream and never synchronises.  Calls that
  *   share a workspace or touch the same cache must be ordered on one stream.
@@ -21,10 +22,16 @@
  *   every buffer untouched.  Inconsistent device-resident data (for example a
  *   seq_len above the head's capacity, or victims not strictly ascending) is
  *   detected by the kernels: the affected head is left unchanged and a bit is
- *   set in stats[4] of kvev_compact, or (score/select) the head is skipped and
- *   its n_victims is set to -1.
+ *   set in stats[4] of kvev_compact; kvev_score skips the head and kvev_select
+ *   sets its n_victims to -1.
  * - Block size is fixed at 16 tokens ([VTOK] section 2 and section 5's block
  *   size sensitivity; [H2O] "PagedAttention Memory Integration").
+ * - Workspace: one caller-owned device buffer of kvev_workspace_bytes() bytes
+ *   serves every entry point of a cache shape.  ZERO-FILL IT ONCE before its
+ *   first use: its leading part holds state that kvev_select expects to be
+ *   zero and restores to zero before returning control of it; the rest is
+ *   scratch.  Do not modify it between calls; calls sharing it must be
+ *   ordered on one stream.  After a KVEV_EDEVICE return, zero it again.
  *
  * Cache layout (one layer)
  * ------------------------
@@ -137,7 +144,8 @@ int kvev_score(const kvev_cache *cache, const kvev_window *win, int32_t flags,
  * the same shape; n_victims: int32 [batch][kv_heads].  Bit-exact: the result
  * depends only on the score bits.
  * Errors (KVEV_EINVAL): NULL pointers; budget <= 0; recent_window < 0 or
- * recent_window >= budget ([SNAP] Parameters).  No workspace is used.
+ * recent_window >= budget ([SNAP] Parameters); KVEV_ENOSPACE for a missing or
+ * short workspace; KVEV_EUNSUPPORTED above 1M slots per head.
  */
 int kvev_select(const kvev_cache *cache, const float *score, int32_t budget,
                 int32_t recent_window, int32_t *victims, int32_t *n_victims, void *workspace,
@@ -158,14 +166,15 @@ int kvev_select(const kvev_cache *cache, const float *score, int32_t budget,
  * unspecified data afterwards.
  * victims/n_victims: as written by kvev_select (ascending, inside [0, n)).
  * free_list: int32 [free_capacity] device array; free_count: one int32 on
- * the device.  stats: int64[5] on the device = {blocks_freed, rows_moved,
+ * the device.  At most 4096 KV heads (batch * kv_heads) per call.  stats: int64[5] on the device = {blocks_freed, rows_moved,
  * bytes_moved (K and V rows moved, read + write), at_risk_rows (kept rows
  * whose source lies inside the compacted range and is staged through the
  * workspace first), status (0, or a bit set per inconsistent head: bit 0
  * victims not ascending / out of range, bit 1 seq_len above capacity)}.
  * Errors: KVEV_EINVAL for NULL pointers or a bad cache; KVEV_ENOSPACE when
  * free_capacity < num_blocks (the list must be able to hold the whole pool)
- * or ws_bytes < kvev_workspace_bytes(cache, 1, 1).
+ * or ws_bytes < kvev_workspace_bytes(cache, 1, 1); KVEV_EUNSUPPORTED above 4096
+ * KV heads.
  */
 int kvev_compact(const kvev_cache *cache, const int32_t *victims, const int32_t *n_victims,
                  float *score_or_null, int32_t *free_list, int32_t *free_count,
@@ -186,8 +195,9 @@ int kvev_compact(const kvev_cache *cache, const int32_t *victims, const int32_t 
 int kvev_window_attn(const kvev_cache *cache, const kvev_window *win, float *lse_out,
                      void *a_out, void *workspace, size_t ws_bytes, void *stream);
 
-/* Workspace bytes needed by kvev_compact (group and obs_window ignored)
- * and kvev_window_attn for this cache shape and window.  0 for a bad cache. */
+/* Workspace bytes needed by kvev_select, kvev_compact and (for this window
+ * shape; pass 1, 1 when unused) kvev_window_attn on this cache shape.
+ * 0 for a bad cache. */
 size_t kvev_workspace_bytes(const kvev_cache *cache, int32_t group, int32_t obs_window);
 
 /* Static description of a status code. */

@@ -196,6 +196,8 @@ def workspace_bytes(cache: Cache, group: int = 1, obs_window: int = 1) -> int:
 
 
 def new_workspace(cache: Cache, group: int = 1, obs_window: int = 1) -> torch.Tensor:
+    """A zero-filled workspace for every entry point (the library keeps its
+    persistent part zeroed from call to call)."""
     return torch.zeros(workspace_bytes(cache, group, obs_window), dtype=torch.uint8,
                        device=cache.k_pool.device)
 
@@ -225,10 +227,14 @@ def score(cache: Cache, q: torch.Tensor, lse: torch.Tensor, q_pos: torch.Tensor,
 
 def select(cache: Cache, score_row: torch.Tensor, budget: int, recent_window: int,
            victims: Optional[torch.Tensor] = None, n_victims: Optional[torch.Tensor] = None,
-           stream=None):
-    """kvev_select -> (victims [B, Hkv, max_slots] int32, n_victims [B, Hkv] int32)."""
+           workspace: Optional[torch.Tensor] = None, stream=None):
+    """kvev_select -> (victims [B, Hkv, max_slots] int32, n_victims [B, Hkv] int32).
+    `workspace`: a zero-filled uint8 buffer from new_workspace() (allocated here when None)."""
     L = load_library()
     c = cache.struct()
+    if workspace is None:
+        workspace = new_workspace(cache)
+    _need(workspace, "workspace", torch.uint8)
     _need(score_row, "score", torch.float32, cache.units * cache.max_slots)
     dev = cache.k_pool.device
     if victims is None:
@@ -239,7 +245,7 @@ def select(cache: Cache, score_row: torch.Tensor, budget: int, recent_window: in
     _need(victims, "victims", torch.int32, cache.units * cache.max_slots)
     _need(n_victims, "n_victims", torch.int32, cache.units)
     rc = L.kvev_select(ctypes.byref(c), _ptr(score_row), budget, recent_window, _ptr(victims),
-                       _ptr(n_victims), None, 0, _stream(stream))
+                       _ptr(n_victims), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(rc, "kvev_select")
     return victims, n_victims
 

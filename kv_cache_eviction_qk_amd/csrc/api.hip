@@ -38,6 +38,42 @@ int elem_bytes(const kvev_cache *c) { return c->dtype == KVEV_BF16 ? 2 : 4; }
 
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Workspace = [persistent state | scratch].  The state (select's histogram
+// and candidate counters) must be zero before the first call; every call
+// leaves it zero.  The scratch part is shared by all entry points.
+struct StateLayout {
+  size_t hist, cand_cnt, total;
+};
+
+StateLayout state_layout(const kvev_cache *c) {
+  StateLayout L{};
+  const size_t units = (size_t)c->batch * c->kv_heads;
+  size_t off = 0;
+  L.hist = off; off = a256(off + units * kvev::kSelectBins * 4);
+  L.cand_cnt = off; off = a256(off + units * 4);
+  L.total = off;
+  return L;
+}
+
+struct SelectLayout {
+  size_t cand, cnt_lt, chunk_off, head_sel, total;
+  int chunks;
+};
+
+SelectLayout select_layout(const kvev_cache *c) {
+  SelectLayout L{};
+  const size_t units = (size_t)c->batch * c->kv_heads;
+  const size_t max_slots = (size_t)c->max_blocks * KVEV_BLOCK_SIZE;
+  L.chunks = (int)((max_slots + kvev::kSelectChunk - 1) / kvev::kSelectChunk);
+  size_t off = state_layout(c).total;
+  L.cand = off; off = a256(off + units * max_slots * 8);
+  L.cnt_lt = off; off = a256(off + units * (size_t)L.chunks * 4);
+  L.chunk_off = off; off = a256(off + units * (size_t)L.chunks * 4);
+  L.head_sel = off; off = a256(off + units * 16);
+  L.total = off;
+  return L;
+}
+
 struct CompactLayout {
   size_t src_of, new_pos, new_score, stage_k, stage_v, head_info, chunk_err, fc0, total;
   int chunks, stage_rows;
@@ -52,7 +88,7 @@ CompactLayout compact_layout(const kvev_cache *c) {
   // At-risk rows of a head are the kept slots in [first victim, n'): up to
   // n' - 1 of them (evicting only slot 0 shifts every other row).
   L.stage_rows = (int)max_slots;
-  size_t off = 0;
+  size_t off = state_layout(c).total;
   L.src_of = off; off = a256(off + units * max_slots * 4);
   L.new_pos = off; off = a256(off + units * max_slots * 4);
   L.new_score = off; off = a256(off + units * max_slots * 4);
@@ -78,7 +114,7 @@ WaLayout wa_layout(const kvev_cache *c, int group, int obs_window) {
   L.chunks = (int)((max_slots + kWaChunk - 1) / kWaChunk);
   L.rows_pad = ((rows + kWaRowsPerWg - 1) / kWaRowsPerWg) * kWaRowsPerWg;
   const size_t parts = units * (size_t)L.rows_pad * L.chunks;
-  size_t off = 0;
+  size_t off = state_layout(c).total;
   L.part_m = off; off = a256(off + parts * 4);
   L.part_l = off; off = a256(off + parts * 4);
   L.part_acc = off; off = a256(off + parts * (size_t)c->head_dim * 4);
@@ -117,6 +153,8 @@ const char *kvev_strerror(int status) {
 size_t kvev_workspace_bytes(const kvev_cache *cache, int32_t group, int32_t obs_window) {
   if (!valid_cache(cache)) return 0;
   size_t need = compact_layout(cache).total;
+  const size_t sel = select_layout(cache).total;
+  if (sel > need) need = sel;
   if (group >= 1 && obs_window >= 1) {
     const size_t wa = wa_layout(cache, group, obs_window).total;
     if (wa > need) need = wa;
@@ -186,19 +224,29 @@ int kvev_score(const kvev_cache *cache, const kvev_window *win, int32_t flags,
 int kvev_select(const kvev_cache *cache, const float *score, int32_t budget,
                 int32_t recent_window, int32_t *victims, int32_t *n_victims, void *workspace,
                 size_t ws_bytes, void *stream) {
-  (void)workspace;
-  (void)ws_bytes;
   if (!valid_cache(cache) || !score || !victims || !n_victims) return KVEV_EINVAL;
   if (budget <= 0 || recent_window < 0 || recent_window >= budget) return KVEV_EINVAL;
+  const SelectLayout L = select_layout(cache);
+  if (L.chunks > kvev::kSelectMaxChunks) return KVEV_EUNSUPPORTED;
+  if (!workspace || ws_bytes < L.total) return KVEV_ENOSPACE;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  const StateLayout S = state_layout(cache);
   kvev::SelectArgs a{};
   a.score = score;
   a.seq_len = cache->seq_len;
   a.victims = victims;
   a.n_victims = n_victims;
+  a.hist = reinterpret_cast<uint32_t *>(ws + S.hist);
+  a.cand_cnt = reinterpret_cast<uint32_t *>(ws + S.cand_cnt);
+  a.cand = reinterpret_cast<uint2 *>(ws + L.cand);
+  a.cnt_lt = reinterpret_cast<int32_t *>(ws + L.cnt_lt);
+  a.chunk_off = reinterpret_cast<uint32_t *>(ws + L.chunk_off);
+  a.head_sel = reinterpret_cast<uint32_t *>(ws + L.head_sel);
   a.units = cache->batch * cache->kv_heads;
   a.max_slots = cache->max_blocks * KVEV_BLOCK_SIZE;
   a.budget = budget;
   a.recent = recent_window;
+  a.chunks = L.chunks;
   return map_err(kvev::launch_select(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -209,6 +257,7 @@ int kvev_compact(const kvev_cache *cache, const int32_t *victims, const int32_t 
   if (!valid_cache(cache) || !victims || !n_victims || !free_list || !free_count || !stats)
     return KVEV_EINVAL;
   if (free_capacity < cache->num_blocks) return KVEV_ENOSPACE;
+  if (cache->batch * cache->kv_heads > kvev::kCompactMaxUnits) return KVEV_EUNSUPPORTED;
   const CompactLayout L = compact_layout(cache);
   if (!workspace || ws_bytes < L.total) return KVEV_ENOSPACE;
   uint8_t *ws = static_cast<uint8_t *>(workspace);

@@ -4,16 +4,20 @@
 // one hazard: a destination row r < n' may still be the source of another
 // kept token.  Those sources are exactly the kept slots in [first victim, n')
 // ("at risk"); they are copied to the workspace first.  Three launches:
-//   prep     (slot chunk per workgroup): ranks from the sorted victim list,
-//            the source of every destination rank, the kept pos / score
-//            values, and the staging copy of the at-risk rows.  Reads the
-//            cache only.
-//   gather   (rank chunk per workgroup): every moving row is copied with
-//            16-byte vector accesses from the pool (sources >= n', never
-//            written in this launch) or from the staged copy.
-//   finalize (one workgroup): emptied tail blocks [ceil(n'/16), ceil(n/16))
-//            are appended to the free list in (b, h, block) order, their
-//            table entries cleared, seq_len set to n', stats completed.
+//   prep     (1024-slot chunk of one head per workgroup): checks the victim
+//            list and the block ids, ranks the kept slots (a two-round
+//            cooperative search gives the victims before the chunk), records
+//            for each destination rank its source (physical row, staged
+//            copy, or "stays"), the kept pos / score values, and copies the
+//            at-risk rows to the workspace.  Reads the cache only.
+//   gather   (persistent grid over (head, 64-rank) items): copies every
+//            moving K and V row with 16-byte accesses, then pos and score;
+//            the first item of each head also records the head's error
+//            state and the number of blocks it frees.
+//   finalize (256 logical blocks of one head per workgroup): appends the
+//            emptied tail blocks [ceil(n'/16), ceil(n/16)) to the free list
+//            in (b, h, block) order, clears their table entries, sets
+//            seq_len = n' and completes the stats.
 // ([H2O] "PagedAttention Memory Integration"; [VTOK] section 3.3, stage 3
 // and section 3.5, invariants I1, I2 and I4.)
 #include <hip/hip_runtime.h>
@@ -25,13 +29,15 @@ namespace kvev {
 
 namespace {
 constexpr int kThreads = 256;
-constexpr int kChunk = 1024;          // slots (prep) or ranks (gather) per workgroup
+constexpr int kChunk = 1024;          // slots per prep workgroup
 constexpr int kPerThread = kChunk / kThreads;
-constexpr int kFinThreads = 1024;
+constexpr int kRankChunk = 64;        // destination ranks per gather item
+constexpr int kFinBlocks = 256;       // logical blocks per finalize workgroup
+constexpr int kMaxUnits = kCompactMaxUnits;  // heads a gather workgroup indexes in LDS
 
-// Exclusive prefix sum over the workgroup (any size that is a multiple of 64).
+// Exclusive prefix sum over a 256-thread workgroup.
 __device__ int block_exclusive_scan(int v, int *wave_tot) {
-  const int lane = lane_id(), wv = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  const int lane = lane_id(), wv = threadIdx.x / kWave;
   int incl = v;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
@@ -43,25 +49,32 @@ __device__ int block_exclusive_scan(int v, int *wave_tot) {
   int before = 0;
   for (int w = 0; w < wv; ++w) before += wave_tot[w];
   __syncthreads();
-  (void)nw;
   return before + incl - v;
 }
 
-__device__ __forceinline__ int lower_bound(const int32_t *a, int n, int key) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (a[mid] < key) lo = mid + 1; else hi = mid;
-  }
-  return lo;
+// Number of entries of the ascending array a[0, m) below key (lower bound),
+// found by the whole workgroup in two rounds of independent loads: 256
+// evenly spaced samples bracket the answer, then the bracket is counted.
+__device__ int wg_lower_bound(const int32_t *a, int m, int key) {
+  const int tid = threadIdx.x;
+  const int S = (m + kThreads - 1) / kThreads;  // sample spacing, >= 1 when m > 0
+  const int idx = tid * S;
+  const int c = __syncthreads_count(idx < m && a[idx] < key);
+  if (c == 0) return 0;
+  // a[(c-1)*S] < key, and a[c*S] >= key (or c*S >= m)
+  const int base = (c - 1) * S + 1;
+  const int len = min(S - 1, m - base);
+  int cnt = 0;
+  for (int off = 0; off < len; off += kThreads)
+    cnt += __syncthreads_count(off + tid < len && a[base + off + tid] < key);
+  return base + cnt;
 }
 }  // namespace
 
-// head_info[u*4 + 0] = n before the call, [1] = first victim slot.
 __global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArgs P) {
   __shared__ uint8_t flag[kChunk];
   __shared__ int stage_s[kChunk], stage_i[kChunk];
-  __shared__ int s_j0, s_j1, s_err, s_nstage;
+  __shared__ int s_err, s_nstage;
   __shared__ int wave_tot[kThreads / kWave];
 
   const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
@@ -78,10 +91,7 @@ __global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArg
   if (tid == 0) {
     s_err = 0;
     s_nstage = 0;
-    if (c == 0) {
-      P.head_info[u * 4 + 0] = n;
-      P.head_info[u * 4 + 1] = (!err && m > 0) ? vic[0] : n;
-    }
+    if (c == 0) P.head_info[u * 4 + 0] = n;
   }
   __syncthreads();
   // the victim list must be strictly ascending inside [0, n): chunk c checks
@@ -103,24 +113,22 @@ __global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArg
     return;
   }
   const int s1 = min(s0 + kChunk, n);
-  if (tid == 0) {
-    s_j0 = lower_bound(vic, m, s0);
-    s_j1 = lower_bound(vic, m, s1);
-  }
+  const int j0 = wg_lower_bound(vic, m, s0);
+  const int j1 = wg_lower_bound(vic, m, s1);
   for (int i = tid; i < kChunk; i += kThreads) flag[i] = 0;
+  // every block holding a slot of this chunk must be a valid pool index
+  const int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
+  for (int lb = s0 / kBlock + tid; lb < (s1 + kBlock - 1) / kBlock; lb += kThreads) {
+    const int blk = bt[lb];
+    if (blk < 0 || blk >= P.num_blocks) atomicOr(&s_err, 1);
+  }
   __syncthreads();
-  const int j0 = s_j0, j1 = s_j1;
   for (int j = j0 + tid; j < j1; j += kThreads) {
     const int v = vic[j];
     if (v >= s0 && v < s1) flag[v - s0] = 1;
   }
   __syncthreads();
 
-  // every block holding a slot of this chunk must be a valid pool index
-  for (int lb = s0 / kBlock + tid; lb < (s1 + kBlock - 1) / kBlock; lb += kThreads) {
-    const int blk = P.block_table[(size_t)u * P.max_blocks + lb];
-    if (blk < 0 || blk >= P.num_blocks) atomicOr(&s_err, 1);
-  }
   int kept = 0;
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
@@ -132,7 +140,6 @@ __global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArg
   const int first = vic[0];
   int r = (s0 - j0) + excl;  // kept slots before s0, plus those before mine in the chunk
   const size_t urow = (size_t)u * P.max_slots;
-  const int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
   int my_err = 0;
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
@@ -149,8 +156,9 @@ __global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArg
       const int k = atomicAdd(&s_nstage, 1);
       stage_s[k] = s;
       stage_i[k] = si;
-    } else {
-      src = s;                        // read in place: slots >= n' are never written
+    } else {                          // slots >= n' are never written: read in place
+      const int blk = bt[s / kBlock];
+      src = (blk >= 0 && blk < P.num_blocks) ? blk * kBlock + s % kBlock : 0;
     }
     P.src_of[urow + r] = src;
     P.new_pos[urow + r] = P.pos[urow + s];
@@ -166,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArg
     const int k = idx / pieces, part = idx % pieces;
     const int s = stage_s[k];
     const int blk = bt[s / kBlock];
-    if (blk < 0 || blk >= P.num_blocks) { atomicOr(&s_err, 1); continue; }
+    if (blk < 0 || blk >= P.num_blocks) continue;  // flagged above
     const size_t src = ((size_t)blk * kBlock + s % kBlock) * P.row_bytes + (size_t)part * 16;
     const size_t dst = ((size_t)u * P.stage_rows + stage_i[k]) * P.row_bytes + (size_t)part * 16;
     st16(P.stage_k + dst, ld16(P.k_pool + src));
@@ -176,151 +184,165 @@ __global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArg
   if (tid == 0) P.chunk_err[(size_t)u * P.chunks + c] = err | s_err;
 }
 
+// Persistent grid: every workgroup indexes the per-head item counts in LDS.
 __global__ __launch_bounds__(kThreads) void compact_gather_kernel(const CompactArgs P) {
-  __shared__ int s_err, s_moved, s_risk;
-  const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
-  if (tid == 0) {
-    s_err = 0;
-    s_moved = 0;
-    s_risk = 0;
-  }
-  __syncthreads();
-  for (int i = tid; i < P.chunks; i += kThreads)
-    if (P.chunk_err[(size_t)u * P.chunks + i]) atomicOr(&s_err, 1);
-  __syncthreads();
-  if (s_err) return;
-  const int n = P.head_info[u * 4 + 0];
-  const int m = P.n_victims[u];
-  const int n2 = n - m;
-  const int r0 = c * kChunk;
-  if (m == 0 || r0 >= n2) return;
-  const int r1 = min(r0 + kChunk, n2);
-  const size_t urow = (size_t)u * P.max_slots;
-  const int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
-  const int pieces = P.row_bytes / 16;
-  for (int idx = tid; idx < (r1 - r0) * pieces; idx += kThreads) {
-    const int r = r0 + idx / pieces, part = idx % pieces;
-    const int src = P.src_of[urow + r];
-    if (src == -1) continue;
-    const int dblk = bt[r / kBlock];
-    const size_t dst = ((size_t)dblk * kBlock + r % kBlock) * P.row_bytes + (size_t)part * 16;
-    uint4 kv, vv;
-    if (src >= 0) {
-      const size_t so = ((size_t)bt[src / kBlock] * kBlock + src % kBlock) * P.row_bytes +
-                        (size_t)part * 16;
-      kv = ld16(P.k_pool + so);
-      vv = ld16(P.v_pool + so);
-    } else {
-      const size_t so = ((size_t)u * P.stage_rows + (-2 - src)) * P.row_bytes + (size_t)part * 16;
-      kv = ld16(P.stage_k + so);
-      vv = ld16(P.stage_v + so);
+  __shared__ int item_start[kMaxUnits + 1];
+  __shared__ int wave_tot[kThreads / kWave];
+  __shared__ int s_total;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int U = P.units;
+  // items per head: ceil(n'/64) row chunks, at least one (it records the head state)
+  int base_count = 0;
+  for (int b0 = 0; b0 < U; b0 += kThreads) {
+    const int u = b0 + tid;
+    int cnt = 0;
+    if (u < U) {
+      const int n = P.head_info[u * 4 + 0];
+      const int m = P.n_victims[u];
+      const bool ok = n >= 0 && n <= P.max_slots && m > 0 && m <= n;
+      cnt = ok ? max(1, (n - m + kRankChunk - 1) / kRankChunk) : 1;
     }
-    st16(P.k_pool + dst, kv);
-    st16(P.v_pool + dst, vv);
+    const int ex = block_exclusive_scan(cnt, wave_tot);
+    if (u < U) item_start[u] = base_count + ex;
+    if (tid == kThreads - 1) s_total = base_count + ex + cnt;
+    __syncthreads();
+    base_count = s_total;
+    __syncthreads();
   }
-  int moved = 0, risk = 0;
-  for (int r = r0 + tid; r < r1; r += kThreads) {
-    const int src = P.src_of[urow + r];
-    if (src == -1) continue;
-    P.pos[urow + r] = P.new_pos[urow + r];
-    if (P.score) P.score[urow + r] = P.new_score[urow + r];
-    ++moved;
-    risk += src <= -2 ? 1 : 0;
-  }
-  if (moved) atomicAdd(&s_moved, moved);
-  if (risk) atomicAdd(&s_risk, risk);
+  if (tid == 0) item_start[U] = base_count;
   __syncthreads();
-  if (tid == 0 && s_moved) {
-    atomicAdd(reinterpret_cast<unsigned long long *>(&P.stats[1]), (unsigned long long)s_moved);
-    atomicAdd(reinterpret_cast<unsigned long long *>(&P.stats[2]),
-              (unsigned long long)s_moved * 4ull * (unsigned long long)P.row_bytes);
-    atomicAdd(reinterpret_cast<unsigned long long *>(&P.stats[3]), (unsigned long long)s_risk);
+  const int total = base_count;
+  const int pieces = P.row_bytes / 16;
+
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    // head of this item: the last u with item_start[u] <= item
+    int lo = 0, hi = U - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (item_start[mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    const int u = lo, k = item - item_start[u];
+    const int n = P.head_info[u * 4 + 0];
+    const int m = P.n_victims[u];
+    // head error: any prep chunk flag, or n / m out of range
+    int e = 0;
+    for (int c = lane; c < P.chunks; c += kWave) e |= P.chunk_err[(size_t)u * P.chunks + c];
+    const bool nm_bad = n < 0 || n > P.max_slots || m < 0 || m > n;
+    const bool head_bad = __any(e != 0) || nm_bad;
+    if (k == 0 && tid == 0) {
+      int ev = nm_bad ? ((n < 0 || n > P.max_slots) ? 2 : 1) : 0;
+      for (int c = 0; c < P.chunks && !nm_bad; ++c) ev |= P.chunk_err[(size_t)u * P.chunks + c];
+      P.head_info[u * 4 + 2] = ev;
+      P.head_info[u * 4 + 3] = (ev || m <= 0) ? 0 : (n + kBlock - 1) / kBlock - (n - m + kBlock - 1) / kBlock;
+    }
+    if (head_bad || m <= 0) continue;
+    const int n2 = n - m;
+    const int r0 = k * kRankChunk;
+    if (r0 >= n2) continue;
+    const int r1 = min(r0 + kRankChunk, n2);
+    const size_t urow = (size_t)u * P.max_slots;
+    const int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
+    for (int idx = tid; idx < (r1 - r0) * pieces; idx += kThreads) {
+      const int r = r0 + idx / pieces, part = idx % pieces;
+      const int src = P.src_of[urow + r];
+      if (src == -1) continue;
+      const size_t dst = ((size_t)bt[r / kBlock] * kBlock + r % kBlock) * P.row_bytes + (size_t)part * 16;
+      uint4 kv, vv;
+      if (src >= 0) {
+        const size_t so = (size_t)src * P.row_bytes + (size_t)part * 16;
+        kv = ld16(P.k_pool + so);
+        vv = ld16(P.v_pool + so);
+      } else {
+        const size_t so = ((size_t)u * P.stage_rows + (-2 - src)) * P.row_bytes + (size_t)part * 16;
+        kv = ld16(P.stage_k + so);
+        vv = ld16(P.stage_v + so);
+      }
+      st16(P.k_pool + dst, kv);
+      st16(P.v_pool + dst, vv);
+    }
+    int moved = 0, risk = 0;
+    for (int r = r0 + tid; r < r1; r += kThreads) {
+      const int src = P.src_of[urow + r];
+      if (src == -1) continue;
+      P.pos[urow + r] = P.new_pos[urow + r];
+      if (P.score) P.score[urow + r] = P.new_score[urow + r];
+      ++moved;
+      risk += src <= -2 ? 1 : 0;
+    }
+    // one atomic per wave
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) {
+      moved += __shfl_xor(moved, o);
+      risk += __shfl_xor(risk, o);
+    }
+    if (lane == 0 && moved) {
+      atomicAdd(reinterpret_cast<unsigned long long *>(&P.stats[1]), (unsigned long long)moved);
+      atomicAdd(reinterpret_cast<unsigned long long *>(&P.stats[2]),
+                (unsigned long long)moved * 4ull * (unsigned long long)P.row_bytes);
+      if (risk) atomicAdd(reinterpret_cast<unsigned long long *>(&P.stats[3]), (unsigned long long)risk);
+    }
   }
 }
 
-// One workgroup: free-list append in (b, h, logical block) order.
-__global__ __launch_bounds__(kFinThreads) void compact_finalize_kernel(const CompactArgs P) {
-  __shared__ int wave_tot[kFinThreads / kWave];
-  __shared__ int s_head_off[kFinThreads], s_head_freed[kFinThreads], s_head_n2[kFinThreads];
-  __shared__ long long s_total;
-  __shared__ int s_status;
-  const int tid = threadIdx.x;
+// Workgroup (k, u): logical blocks [ceil(n'/16) + 256k, ...) of head u.
+__global__ __launch_bounds__(kThreads) void compact_finalize_kernel(const CompactArgs P) {
+  __shared__ long long s_before, s_total;
+  const int k = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
   if (tid == 0) {
+    s_before = 0;
     s_total = 0;
-    s_status = 0;
   }
   __syncthreads();
-  // pass 1: blocks freed over all consistent heads
-  auto head_state = [&](int u, int &freed, int &n2, int &err) {
-    const int n = P.head_info[u * 4 + 0];
-    const int m = P.n_victims[u];
-    err = 0;
-    for (int i = 0; i < P.chunks; ++i) err |= P.chunk_err[(size_t)u * P.chunks + i];
-    if (n < 0 || n > P.max_slots) err |= 2;
-    else if (m < 0 || m > n) err |= 1;
-    freed = 0;
-    n2 = n;
-    if (!err) {
-      n2 = n - m;
-      freed = (n + kBlock - 1) / kBlock - (n2 + kBlock - 1) / kBlock;
-    }
-  };
-  for (int base = 0; base < P.units; base += kFinThreads) {
-    const int u = base + tid;
-    int freed = 0, n2 = 0, err = 0;
-    if (u < P.units) head_state(u, freed, n2, err);
-    if (err) atomicOr(&s_status, err);
-    if (freed) atomicAdd(reinterpret_cast<unsigned long long *>(&s_total), (unsigned long long)freed);
+  long long before = 0, total = 0;
+  for (int v = tid; v < P.units; v += kThreads) {
+    const long long f = P.head_info[v * 4 + 3];
+    total += f;
+    if (v < u) before += f;
   }
+  if (before) atomicAdd(reinterpret_cast<unsigned long long *>(&s_before), (unsigned long long)before);
+  if (total) atomicAdd(reinterpret_cast<unsigned long long *>(&s_total), (unsigned long long)total);
   __syncthreads();
   const int fc0 = *P.fc0;
-  const bool room = (long long)fc0 + s_total <= (long long)P.free_capacity && fc0 >= 0;
-  // pass 2: offsets and appends, 1024 heads at a time
-  long long running = 0;
-  for (int base = 0; base < P.units; base += kFinThreads) {
-    const int u = base + tid;
-    int freed = 0, n2 = 0, err = 0;
-    if (u < P.units) head_state(u, freed, n2, err);
-    if (!room) freed = 0;
-    const int off = block_exclusive_scan(freed, wave_tot);
-    s_head_off[tid] = (int)running + off;
-    s_head_freed[tid] = freed;
-    s_head_n2[tid] = (u < P.units && !err) ? n2 : -1;
-    __syncthreads();
-    const int cnt = min(kFinThreads, P.units - base);
-    for (int k = 0; k < cnt; ++k) {
-      const int uu = base + k;
-      const int f = s_head_freed[k];
-      const int nn2 = s_head_n2[k];
-      if (nn2 < 0) continue;
-      int32_t *bt = P.block_table + (size_t)uu * P.max_blocks;
-      const int lb0 = (nn2 + kBlock - 1) / kBlock;
-      for (int i = tid; i < f; i += kFinThreads) {
-        P.free_list[fc0 + s_head_off[k] + i] = bt[lb0 + i];
-        bt[lb0 + i] = -1;
-      }
-      if (tid == 0) P.seq_len[uu] = nn2;
+  const bool room = fc0 >= 0 && (long long)fc0 + s_total <= (long long)P.free_capacity;
+  const int n = P.head_info[u * 4 + 0];
+  const int err = P.head_info[u * 4 + 2];
+  const int freed = room ? P.head_info[u * 4 + 3] : 0;
+  if (k == 0 && tid == 0) {
+    if (err) {
+      atomicOr(reinterpret_cast<unsigned long long *>(&P.stats[4]), (unsigned long long)err);
+    } else {
+      const int m = P.n_victims[u];
+      if (m > 0) P.seq_len[u] = n - m;
+      if (freed) atomicAdd(reinterpret_cast<unsigned long long *>(&P.stats[0]), (unsigned long long)freed);
     }
-    running = s_head_off[cnt - 1] + s_head_freed[cnt - 1];
-    __syncthreads();
+    if (u == P.units - 1) {
+      if (room) *P.free_count = fc0 + (int)s_total;
+      else atomicOr(reinterpret_cast<unsigned long long *>(&P.stats[4]), 4ull);
+    }
   }
-  if (tid == 0) {
-    if (room) *P.free_count = fc0 + (int)s_total;
-    int st = s_status | (room ? 0 : 4);
-    P.stats[0] = room ? s_total : 0;
-    P.stats[4] |= st;
+  if (err || freed == 0) return;
+  const int n2 = n - P.n_victims[u];
+  const int lb0 = (n2 + kBlock - 1) / kBlock;
+  int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
+  const int i = k * kFinBlocks + tid;
+  if (i < freed) {
+    P.free_list[fc0 + s_before + i] = bt[lb0 + i];
+    bt[lb0 + i] = -1;
   }
 }
 
 hipError_t launch_compact(const CompactArgs &a, hipStream_t s) {
-  dim3 grid(a.chunks, a.units);
-  hipLaunchKernelGGL(compact_prep_kernel, grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(compact_prep_kernel, dim3(a.chunks, a.units), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(compact_gather_kernel, grid, dim3(kThreads), 0, s, a);
+  // enough workgroups to cover every 64-rank item of a full cache, capped
+  const long long items = (long long)a.units * ((a.max_slots + kRankChunk - 1) / kRankChunk);
+  const int grid = (int)(items < 2048 ? (items > 0 ? items : 1) : 2048);
+  hipLaunchKernelGGL(compact_gather_kernel, dim3(grid), dim3(kThreads), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(compact_finalize_kernel, dim3(1), dim3(kFinThreads), 0, s, a);
+  const int fin_x = (a.max_blocks + kFinBlocks - 1) / kFinBlocks;
+  hipLaunchKernelGGL(compact_finalize_kernel, dim3(fin_x, a.units), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

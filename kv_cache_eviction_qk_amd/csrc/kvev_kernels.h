@@ -25,7 +25,15 @@ struct SelectArgs {
   const float *score;
   const int32_t *seq_len;
   int32_t *victims, *n_victims;
-  int32_t units, max_slots, budget, recent;
+  // workspace: persistent state (zero between calls)
+  uint32_t *hist;         // [units][2048] histogram of the top 11 key bits
+  uint32_t *cand_cnt;     // [units] candidates collected
+  // workspace: scratch
+  uint2 *cand;            // [units][max_slots] (key, slot) of the threshold bucket
+  int32_t *cnt_lt;        // [units][chunks] keys below the threshold bucket
+  uint32_t *chunk_off;    // [units][chunks] output offset of each chunk
+  uint32_t *head_sel;     // [units][4] threshold key, tie-cut slot
+  int32_t units, max_slots, budget, recent, chunks;
 };
 
 struct CompactArgs {
@@ -65,6 +73,11 @@ hipError_t launch_compact(const CompactArgs &a, hipStream_t s);
 hipError_t launch_window_attn(const WindowAttnArgs &a, int bf16, int head_dim, hipStream_t s);
 
 // LDS bytes of one score workgroup (0 when the row count does not fit).
+constexpr int kSelectChunk = 1024;      // select.hip chunk (slots)
+constexpr int kSelectBins = 2048;       // select.hip histogram bins
+constexpr int kSelectMaxChunks = 1024;  // select.hip refine step limit
+constexpr int kCompactMaxUnits = 4096;  // compact.hip gather limit
+
 size_t score_lds_bytes(int bf16, int head_dim, int drop, int row_tiles, int tile_blocks,
                        int halo_blocks);
 

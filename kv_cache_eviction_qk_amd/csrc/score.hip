@@ -133,49 +133,51 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
   const size_t lane_off = (size_t)lr * ROWB + (size_t)lg * (ROWB / 4);
   const float c1 = P.c1;
 
-  uint4 kf[NB][U], vf[NB][U];
-  int kp[NB];
-  bool badb[NB];
+  // Block ids of this wave's range, one lane each (the range never exceeds
+  // 64 blocks: tile + 2 * halo <= 256 blocks over 4 waves); read back with
+  // readlane, so no load waits on another.
+  const int nwb = wb1 - wb0;
+  int my_id = (l < nwb) ? bt[wb0 + l] : 0;
+  const bool my_bad = (l < nwb) && (my_id < 0 || my_id >= P.num_blocks);
+  const uint64_t bad_mask = __ballot(my_bad);
+  if (my_bad) my_id = 0;  // a bad id loads block 0 and yields NaN scores
 
-  auto load = [&](int cur) {
+  struct Frag {
+    uint4 k[NB][U];
+    uint4 v[NB][U];
+    int kp[NB];
+  };
+  // Loads of blocks [cur, cur + NB), clamped to the wave's last block so every
+  // issue has the same shape (the clamped re-reads hit the cache).
+  auto issue = [&](Frag &F, int cur) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int blk = cur + i;
-      const int id = blk < wb1 ? bt[blk] : 0;
-      badb[i] = blk < wb1 && (id < 0 || id >= P.num_blocks);
-      if (blk < wb1 && !badb[i]) {
-        const size_t base = (size_t)id * kBlock * ROWB + lane_off;
+      const int blk = min(cur + i, wb1 - 1);
+      const int id = __builtin_amdgcn_readlane(my_id, blk - wb0);
+      const uint8_t *ksrc = P.k_pool + (size_t)id * kBlock * ROWB + lane_off;
 #pragma unroll
-        for (int j = 0; j < U; ++j) kf[i][j] = ld16(P.k_pool + base + 16 * j);
-        if constexpr (DROP) {
+      for (int j = 0; j < U; ++j) F.k[i][j] = ld16(ksrc + 16 * j);
+      if constexpr (DROP) {
+        const uint8_t *vsrc = P.v_pool + (size_t)id * kBlock * ROWB + lane_off;
 #pragma unroll
-          for (int j = 0; j < U; ++j) vf[i][j] = ld16(P.v_pool + base + 16 * j);
-        }
-        kp[i] = ps[blk * kBlock + lr];
-      } else {
-#pragma unroll
-        for (int j = 0; j < U; ++j) {
-          kf[i][j] = make_uint4(0, 0, 0, 0);
-          if constexpr (DROP) vf[i][j] = make_uint4(0, 0, 0, 0);
-        }
-        kp[i] = INT_MIN;
+        for (int j = 0; j < U; ++j) F.v[i][j] = ld16(vsrc + 16 * j);
       }
+      F.kp[i] = ps[blk * kBlock + lr];
     }
   };
 
-  for (int cur = wb0; cur < wb1; cur += NB) {
-    load(cur);
+  auto compute = [&](const Frag &F, int cur) {
     float psum[NB], pdrop[NB], vn2[NB];
     bool need_mask = false;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       psum[i] = 0.f;
       pdrop[i] = 0.f;
-      need_mask |= kp[i] > minq;
+      need_mask |= F.kp[i] > minq;
       if constexpr (DROP) {
         float ss = 0.f;
 #pragma unroll
-        for (int j = 0; j < U; ++j) ss += sumsq_unit<BF16>(vf[i][j]);
+        for (int j = 0; j < U; ++j) ss += sumsq_unit<BF16>(F.v[i][j]);
         ss += __shfl_xor(ss, 16);
         ss += __shfl_xor(ss, 32);
         vn2[i] = ss;  // ||v||^2 of key lr, in every lane group
@@ -204,8 +206,8 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
       for (int j = 0; j < U; ++j) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-          acc[i] = mfma_unit<BF16>(qa[j], kf[i][j], acc[i]);
-          if constexpr (DROP) av[i] = mfma_unit<BF16>(aa[j], vf[i][j], av[i]);
+          acc[i] = mfma_unit<BF16>(qa[j], F.k[i][j], acc[i]);
+          if constexpr (DROP) av[i] = mfma_unit<BF16>(aa[j], F.v[i][j], av[i]);
         }
       }
       const float Le[4] = {L.x, L.y, L.z, L.w};
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
         for (int i = 0; i < NB; ++i) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const bool live = kp[i] <= Qe[e];
+            const bool live = F.kp[i] <= Qe[e];
             const float x = fmaf(acc[i][e], c1, -Le[e]);
             const float p = live ? __builtin_amdgcn_exp2f(x) : 0.f;
             psum[i] += p;
@@ -249,20 +251,33 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
     // fixed-order reduction over the four lane groups (rows 4*lg .. 4*lg+3)
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      float s = psum[i];
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
-      float d = pdrop[i];
+      float sv = psum[i];
+      sv += __shfl_xor(sv, 16);
+      sv += __shfl_xor(sv, 32);
+      float dv = pdrop[i];
       if constexpr (DROP) {
-        d += __shfl_xor(d, 16);
-        d += __shfl_xor(d, 32);
+        dv += __shfl_xor(dv, 16);
+        dv += __shfl_xor(dv, 32);
       }
       const int blk = cur + i;
       if (blk < wb1 && lg == 0) {
         // a block id outside the pool gives NaN scores for its slots
-        S_lds[(blk - cb0) * kBlock + lr] = badb[i] ? __builtin_nanf("") : s;
-        if constexpr (DROP) D_lds[(blk - cb0) * kBlock + lr] = badb[i] ? __builtin_nanf("") : d;
+        const bool bad = (bad_mask >> (blk - wb0)) & 1ull;
+        S_lds[(blk - cb0) * kBlock + lr] = bad ? __builtin_nanf("") : sv;
+        if constexpr (DROP) D_lds[(blk - cb0) * kBlock + lr] = bad ? __builtin_nanf("") : dv;
       }
+    }
+  };
+
+  // two fragment sets: the next blocks stream in while the current ones are scored
+  if (nwb > 0) {
+    Frag F0, F1;
+    issue(F0, wb0);
+    for (int cur = wb0; cur < wb1; cur += 2 * NB) {
+      issue(F1, cur + NB);
+      compute(F0, cur);
+      issue(F0, cur + 2 * NB);
+      if (cur + NB < wb1) compute(F1, cur + NB);
     }
   }
   __syncthreads();

@@ -1,15 +1,22 @@
 // select.hip -- victims of each KV head under a budget (gfx950).
 //
-// One 1024-thread workgroup per KV head.  Scores become order-preserving
-// 32-bit keys (kvev::score_key); an MSB-first radix select over four 8-bit
-// digits finds the key T of the m-th smallest candidate and how many
-// candidates equal to T are evicted (e).  Emission: each wave owns a
-// contiguous run of candidate slots; a first sweep counts keys < T and
-// keys == T per wave, a scan over the 16 waves gives each wave its output
-// offset and its tie offset, and a second sweep writes the victims with
-// ballot prefixes, so the output is in ascending slot order and equal
-// scores evict the lower position first ([SNAP] "Tie-breaking").
-// Everything is integer: the result is bit-exact for given score bits.
+// Scores become order-preserving 32-bit keys (kvev::score_key).  With m
+// victims among the candidate slots [0, nc), the victims are the keys below
+// the m-th smallest key T, plus the lowest-slot keys equal to T ([SNAP]
+// "Tie-breaking": equal scores evict the lower position).  Four launches,
+// the heavy ones spread over 1024-slot chunks of every head:
+//   hist    chunk: LDS histogram of the top 11 key bits, added into the
+//           head's 2048-bin histogram (integer atomics: exact).
+//   collect chunk: from the head histogram, the bucket b holding rank m;
+//           counts keys below b, appends (key, slot) of bucket b to the
+//           head's candidate list.
+//   refine  head: radix select over the (small) candidate list for T and
+//           the tie cut (the slot of the last evicted key equal to T), the
+//           number of victims of every chunk and its output offset; resets
+//           the histogram state for the next call.
+//   emit    chunk: marks victims, prefix sums them, writes slot indices at
+//           the chunk's offset: ascending order overall.
+// Integer throughout: the result depends only on the score bits.
 #include <hip/hip_runtime.h>
 
 #include "kvev_device.h"
@@ -18,112 +25,330 @@
 namespace kvev {
 
 namespace {
-constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kThreads = 256;
+constexpr int kChunk = kSelectChunk;         // candidate slots per chunk workgroup
+constexpr int kPerThread = kChunk / kThreads;
+constexpr int kBins = kSelectBins;           // top 11 key bits
+constexpr int kShift = 21;
+constexpr int kRefineThreads = 1024;
+constexpr int kMaxChunks = kSelectMaxChunks; // chunks per head the refine step indexes
+
+__device__ __forceinline__ bool head_params(const SelectArgs &P, int u, int &n, int &m, int &nc) {
+  n = P.seq_len[u];
+  if (n < 0 || n > P.max_slots) return false;
+  m = max(0, n - P.budget);
+  nc = max(0, n - P.recent);
+  return true;
+}
+
+// Bucket of the element of 1-based rank `rank` in a 2048-bin histogram in
+// LDS, and the count of elements in lower buckets.  Called by every thread
+// of a workgroup of 256 or more threads; threads 0..255 own 8 bins each.
+__device__ void find_bucket(const uint32_t *h, uint32_t rank, int *s_b, uint32_t *s_below,
+                            uint32_t *wave_tot) {
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
+  uint32_t mine = 0, incl = 0;
+  if (tid < 256) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mine += h[8 * tid + i];
+    incl = mine;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    if (lane == kWave - 1) wave_tot[wv] = incl;
+  }
+  __syncthreads();
+  if (tid < 256) {
+    uint32_t before = 0;
+    for (int w = 0; w < wv; ++w) before += wave_tot[w];
+    incl += before;
+    const uint32_t excl = incl - mine;
+    if (excl < rank && rank <= incl) {
+      uint32_t acc = excl;
+      int b = 8 * tid;
+      while (acc + h[b] < rank) acc += h[b++];
+      *s_b = b;
+      *s_below = acc;
+    }
+  }
+  __syncthreads();
+}
+
+// Radix refinement: the digit at `shift` (bits of `digit_mask`) of the
+// element of 1-based rank *rank among the values v with (v & pmask) == prefix;
+// hist holds (digit_mask + 1) counters.  One wave finds the digit.
+__device__ void pick_digit(const uint32_t *hist, int ndig, uint32_t rank, uint32_t *s_digit,
+                           uint32_t *s_rank) {
+  const int tid = threadIdx.x;
+  if (tid < kWave) {
+    const int per = ndig / kWave;  // 2 or 4 digits per lane
+    uint32_t c[4] = {0, 0, 0, 0};
+    uint32_t mine = 0;
+    for (int i = 0; i < per; ++i) {
+      c[i] = hist[per * tid + i];
+      mine += c[i];
+    }
+    uint32_t incl = mine;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t t = __shfl_up(incl, o);
+      if (tid >= o) incl += t;
+    }
+    const uint32_t before = incl - mine;
+    if (before < rank && rank <= incl) {
+      uint32_t r = rank - before;
+      int i = 0;
+      while (r > c[i]) r -= c[i++];
+      *s_digit = (uint32_t)(per * tid + i);
+      *s_rank = r;
+    }
+  }
+}
+
+__device__ int block_sum(int v, int *red) {
+  const int lane = lane_id(), wv = threadIdx.x / kWave, nw = blockDim.x / kWave;
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  if (lane == 0) red[wv] = v;
+  __syncthreads();
+  int t = 0;
+  for (int w = 0; w < nw; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
 }  // namespace
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectArgs P) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t s_digit, s_rank;
-  __shared__ uint32_t w_less[kSelWaves], w_eq[kSelWaves];
+__global__ __launch_bounds__(kThreads) void select_hist_kernel(const SelectArgs P) {
+  __shared__ uint32_t hl[kBins];
+  const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
+  int n, m, nc;
+  if (!head_params(P, u, n, m, nc) || m == 0) return;
+  const int s0 = c * kChunk;
+  if (s0 >= nc) return;
+  const int s1 = min(s0 + kChunk, nc);
+  for (int i = tid; i < kBins; i += kThreads) hl[i] = 0;
+  __syncthreads();
+  const float *row = P.score + (size_t)u * P.max_slots;
+  for (int s = s0 + tid; s < s1; s += kThreads) atomicAdd(&hl[score_key(row[s]) >> kShift], 1u);
+  __syncthreads();
+  uint32_t *hg = P.hist + (size_t)u * kBins;
+  for (int i = tid; i < kBins; i += kThreads)
+    if (hl[i]) atomicAdd(&hg[i], hl[i]);
+}
 
-  const int u = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int n = P.seq_len[u];
-  if (n < 0 || n > P.max_slots) {  // inconsistent head: flagged, nothing written
-    if (tid == 0) P.n_victims[u] = -1;
+__global__ __launch_bounds__(kThreads) void select_collect_kernel(const SelectArgs P) {
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t wave_tot[kThreads / kWave];
+  __shared__ int red[kThreads / kWave];
+  __shared__ int s_b;
+  __shared__ uint32_t s_below;
+  const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x, lane = lane_id();
+  int n, m, nc;
+  if (!head_params(P, u, n, m, nc) || m == 0) return;
+  const int s0 = c * kChunk;
+  if (s0 >= nc) return;
+  const int s1 = min(s0 + kChunk, nc);
+  const uint32_t *hg = P.hist + (size_t)u * kBins;
+  for (int i = tid; i < kBins; i += kThreads) h[i] = hg[i];
+  __syncthreads();
+  find_bucket(h, (uint32_t)m, &s_b, &s_below, wave_tot);
+  const uint32_t b = (uint32_t)s_b;
+  const float *row = P.score + (size_t)u * P.max_slots;
+  uint2 *cand = P.cand + (size_t)u * P.max_slots;
+  int below = 0;
+  for (int base = s0; base < s1; base += kThreads) {
+    const int s = base + tid;
+    uint32_t key = 0xffffffffu;
+    if (s < s1) key = score_key(row[s]);
+    const uint32_t bk = key >> kShift;
+    below += (s < s1 && bk < b) ? 1 : 0;
+    const bool take = s < s1 && bk == b;
+    const uint64_t mask = __ballot(take);
+    if (mask) {
+      int slot0 = 0;
+      if (lane == 0) slot0 = (int)atomicAdd(&P.cand_cnt[u], (uint32_t)__popcll(mask));
+      slot0 = __shfl(slot0, 0);
+      const int at = slot0 + ballot_prefix(mask);
+      if (take && at < P.max_slots) cand[at] = make_uint2(key, (uint32_t)s);
+    }
+  }
+  const int tot = block_sum(below, red);
+  if (tid == 0) P.cnt_lt[(size_t)u * P.chunks + c] = tot;
+}
+
+// One workgroup per head: exact threshold from the candidate list.
+__global__ __launch_bounds__(kRefineThreads) void select_refine_kernel(const SelectArgs P) {
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t wave_tot[kRefineThreads / kWave];
+  __shared__ uint32_t s_digit, s_rank, s_below;
+  __shared__ int s_b;
+  __shared__ uint32_t chunk_cnt[kMaxChunks];
+  const int u = blockIdx.x, tid = threadIdx.x;
+  int n, m, nc;
+  uint32_t *hg = P.hist + (size_t)u * kBins;
+  if (!head_params(P, u, n, m, nc)) {
+    if (tid == 0) {
+      P.n_victims[u] = -1;
+      P.cand_cnt[u] = 0;
+    }
+    return;  // inconsistent head: its histogram was not touched
+  }
+  if (m == 0) {
+    if (tid == 0) {
+      P.n_victims[u] = 0;
+      P.cand_cnt[u] = 0;
+    }
     return;
   }
-  const int m = max(0, n - P.budget);
-  const int nc = max(0, n - P.recent);  // candidates: slots [0, nc)
-  if (tid == 0) P.n_victims[u] = m;
-  if (m == 0) return;
-  const float *row = P.score + (size_t)u * P.max_slots;
-  int32_t *out = P.victims + (size_t)u * P.max_slots;
+  for (int i = tid; i < kBins; i += kRefineThreads) h[i] = hg[i];
+  __syncthreads();
+  find_bucket(h, (uint32_t)m, &s_b, &s_below, wave_tot);
+  const uint32_t bkt = (uint32_t)s_b;
+  const uint32_t need = (uint32_t)m - s_below;  // rank of T inside bucket bkt, 1-based
+  // the count stays below max_slots unless the state was not zeroed; clamp anyway
+  const int ncand = (int)min(P.cand_cnt[u], (uint32_t)P.max_slots);
+  const uint2 *cand = P.cand + (size_t)u * P.max_slots;
 
-  // ---- radix select: key T of rank m (1-based) among the candidates
-  uint32_t prefix = 0, pmask = 0, rank = (uint32_t)m;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    if (tid < 256) hist[tid] = 0;
+  // radix select over the low 21 bits of the candidates' keys (7 + 7 + 7)
+  uint32_t prefix = bkt << kShift, pmask = 0xffffffffu << kShift, rank = need;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = 14 - 7 * pass;
+    if (tid < 128) h[tid] = 0;
     __syncthreads();
-    for (int j = tid; j < nc; j += kSelThreads) {
-      const uint32_t k = score_key(row[j]);
-      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    for (int i = tid; i < ncand; i += kRefineThreads) {
+      const uint32_t k = cand[i].x;
+      if ((k & pmask) == prefix) atomicAdd(&h[(k >> shift) & 127u], 1u);
     }
     __syncthreads();
-    if (tid < kWave) {
-      // lane l owns digits 4l .. 4l+3
-      const uint32_t c0 = hist[4 * tid], c1 = hist[4 * tid + 1], c2 = hist[4 * tid + 2],
-                     c3 = hist[4 * tid + 3];
-      const uint32_t mine = c0 + c1 + c2 + c3;
-      uint32_t incl = mine;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t t = __shfl_up(incl, o);
-        if (tid >= o) incl += t;
-      }
-      const uint32_t before = incl - mine;
-      if (before < rank && rank <= incl) {  // exactly one lane
-        uint32_t r = rank - before, d = 4 * tid;
-        if (r > c0) { r -= c0; ++d; if (r > c1) { r -= c1; ++d; if (r > c2) { r -= c2; ++d; } } }
-        s_digit = d;
-        s_rank = r;
-      }
-    }
+    pick_digit(h, 128, rank, &s_digit, &s_rank);
     __syncthreads();
     prefix |= s_digit << shift;
-    pmask |= 255u << shift;
+    pmask |= 127u << shift;
     rank = s_rank;
     __syncthreads();
   }
   const uint32_t T = prefix;
-  const uint32_t e = rank;  // keys equal to T that are evicted (the lowest slots)
+  const uint32_t eT = rank;  // keys equal to T that are evicted: the eT lowest slots
 
-  // ---- emission in ascending slot order
-  const int wv = tid / kWave, lane = lane_id();
-  const int per = (nc + kSelWaves - 1) / kSelWaves;
-  const int c0 = min(nc, wv * per), c1 = min(nc, c0 + per);
-  uint32_t nless = 0, neq = 0;
-  for (int base = c0; base < c1; base += kWave) {
-    const int j = base + lane;
-    uint32_t k = 0xffffffffu;
-    if (j < c1) k = score_key(row[j]);
-    const bool valid = j < c1;
-    nless += __popcll(__ballot(valid && k < T));
-    neq += __popcll(__ballot(valid && k == T));
+  // tie cut: the eT-th smallest slot among the candidates with key T
+  uint32_t sp = 0, sm = 0, srank = eT;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    if (tid < 256) h[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < ncand; i += kRefineThreads) {
+      const uint2 cv = cand[i];
+      if (cv.x == T && (cv.y & sm) == sp) atomicAdd(&h[(cv.y >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    pick_digit(h, 256, srank, &s_digit, &s_rank);
+    __syncthreads();
+    sp |= s_digit << shift;
+    sm |= 255u << shift;
+    srank = s_rank;
+    __syncthreads();
   }
-  if (lane == 0) {
-    w_less[wv] = nless;
-    w_eq[wv] = neq;
+  const int tie_cut = (int)sp;
+
+  // victims per chunk: keys below bucket bkt (counted by collect) plus the
+  // candidates below T and the evicted ties
+  const int chunks = P.chunks;
+  const int live_chunks = (nc + kChunk - 1) / kChunk;  // collect wrote these
+  for (int i = tid; i < chunks; i += kRefineThreads)
+    chunk_cnt[i] = i < live_chunks ? (uint32_t)P.cnt_lt[(size_t)u * chunks + i] : 0u;
+  __syncthreads();
+  for (int i = tid; i < ncand; i += kRefineThreads) {
+    const uint2 cv = cand[i];
+    if (cv.y < (uint32_t)nc && (cv.x < T || (cv.x == T && (int)cv.y <= tie_cut)))
+      atomicAdd(&chunk_cnt[cv.y / kChunk], 1u);
   }
   __syncthreads();
-  uint32_t out_off = 0, eq_off = 0;
-  for (int w = 0; w < wv; ++w) {
-    const uint32_t taken = eq_off >= e ? 0u : min(w_eq[w], e - eq_off);
-    out_off += w_less[w] + taken;
-    eq_off += w_eq[w];
+  // exclusive scan of the chunk counts (chunks <= 1024: one per thread)
+  {
+    const int lane = lane_id(), wv = tid / kWave;
+    const uint32_t v = tid < chunks ? chunk_cnt[tid] : 0u;
+    uint32_t incl = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    if (lane == kWave - 1) wave_tot[wv] = incl;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int w = 0; w < wv; ++w) before += wave_tot[w];
+    if (tid < chunks) P.chunk_off[(size_t)u * chunks + tid] = before + incl - v;
   }
-  uint32_t eq_seen = eq_off;
-  for (int base = c0; base < c1; base += kWave) {
-    const int j = base + lane;
-    const bool valid = j < c1;
-    uint32_t k = 0xffffffffu;
-    if (valid) k = score_key(row[j]);
-    const bool is_eq = valid && k == T;
-    const uint64_t eqm = __ballot(is_eq);
-    const uint32_t my_tie = eq_seen + (uint32_t)ballot_prefix(eqm);
-    const bool victim = valid && (k < T || (is_eq && my_tie < e));
-    const uint64_t vm = __ballot(victim);
-    const uint32_t slot_idx = out_off + (uint32_t)ballot_prefix(vm);
-    if (victim && slot_idx < (uint32_t)m) out[slot_idx] = j;
-    out_off += (uint32_t)__popcll(vm);
-    eq_seen += (uint32_t)__popcll(eqm);
+  if (tid == 0) {
+    P.head_sel[u * 4 + 0] = T;
+    P.head_sel[u * 4 + 1] = (uint32_t)tie_cut;
+    P.n_victims[u] = m;
+    P.cand_cnt[u] = 0;
   }
+  // leave the histogram zeroed for the next call
+  for (int i = tid; i < kBins; i += kRefineThreads) hg[i] = 0;
+}
+
+__global__ __launch_bounds__(kThreads) void select_emit_kernel(const SelectArgs P) {
+  __shared__ int wave_tot[kThreads / kWave];
+  const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
+  int n, m, nc;
+  if (!head_params(P, u, n, m, nc) || m == 0) return;
+  const int s0 = c * kChunk;
+  if (s0 >= nc) return;
+  const int s1 = min(s0 + kChunk, nc);
+  const uint32_t T = P.head_sel[u * 4 + 0];
+  const int tie_cut = (int)P.head_sel[u * 4 + 1];
+  const uint32_t off = P.chunk_off[(size_t)u * P.chunks + c];
+  const float *row = P.score + (size_t)u * P.max_slots;
+  bool vic[kPerThread];
+  int cnt = 0;
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int s = s0 + tid * kPerThread + q;
+    bool v = false;
+    if (s < s1) {
+      const uint32_t k = score_key(row[s]);
+      v = k < T || (k == T && s <= tie_cut);
+    }
+    vic[q] = v;
+    cnt += v ? 1 : 0;
+  }
+  const int lane = lane_id(), wv = tid / kWave;
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == kWave - 1) wave_tot[wv] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wv; ++w) before += wave_tot[w];
+  uint32_t o = off + (uint32_t)(before + incl - cnt);
+  int32_t *out = P.victims + (size_t)u * P.max_slots;
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q)
+    if (vic[q]) {
+      if (o < (uint32_t)m) out[o] = s0 + tid * kPerThread + q;
+      ++o;
+    }
 }
 
 hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(select_kernel, dim3(a.units), dim3(kSelThreads), 0, s, a);
+  const dim3 grid(a.chunks, a.units);
+  hipLaunchKernelGGL(select_hist_kernel, grid, dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(select_collect_kernel, grid, dim3(kThreads), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(select_refine_kernel, dim3(a.units), dim3(kRefineThreads), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(select_emit_kernel, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -117,6 +117,14 @@ def test_select_refusals(budget, recent):
     assert L.kvev_select(ctypes.byref(c), None, 8, 2, FAKE, FAKE, None, 0, None) == K.EINVAL
 
 
+def test_select_needs_workspace():
+    L = K.load_library()
+    c = cache()
+    ws = L.kvev_workspace_bytes(ctypes.byref(c), 1, 1)
+    assert L.kvev_select(ctypes.byref(c), FAKE, 8, 2, FAKE, FAKE, None, ws, None) == K.ENOSPACE
+    assert L.kvev_select(ctypes.byref(c), FAKE, 8, 2, FAKE, FAKE, FAKE, 64, None) == K.ENOSPACE
+
+
 def test_compact_refusals():
     L = K.load_library()
     c = cache()
