@@ -9,7 +9,8 @@ protected recent window) and kvev_compact (in-place repack, emptied blocks
 to the free list).  Every step works on its own pristine copy of the cache,
 prepared before the timed region, so the timed region holds only the
 eviction kernels; L2 and the Infinity Cache are flushed before it starts,
-so the keys come from HBM.
+so the keys come from HBM (the flush only reads, so no dirty lines are
+left for the timed kernels to write back).
 
 Prints one JSON line: value = scored KV tokens per second (batch x context
 tokens, every KV head scored, selected and compacted), plus the HBM roofline
@@ -127,7 +128,7 @@ def main():
     victims = torch.empty((B, Hkv, pristine.max_slots), dtype=torch.int32, device="cuda")
     n_victims = torch.empty((B, Hkv), dtype=torch.int32, device="cuda")
     stats = torch.zeros(5, dtype=torch.int64, device="cuda")
-    scrub = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device="cuda")  # 1 GiB
+    scrub = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device="cuda")  # 1 GiB
 
     def restore(i):
         c = caches[i]
@@ -140,7 +141,9 @@ def main():
         free_counts[i].zero_()
 
     def flush_caches():
-        scrub.add_(1.0)  # 2 GiB of HBM traffic evicts L2 and the 256 MB Infinity Cache
+        # Read 1 GiB: evicts L2 and the 256 MB Infinity Cache without leaving
+        # dirty lines behind (a write-back flood would slow the timed kernels).
+        return scrub.sum()
 
     outs = {"sum": None, "pooled": None, "drop": None}
     outs[{"sum": "sum", "pool": "pooled", "drop": "drop"}[kind]] = score_out

@@ -15,7 +15,6 @@
 
 namespace {
 
-constexpr int kCompactChunk = 1024;   // slots per compaction workgroup (compact.hip)
 constexpr int kWaChunk = 2048;        // keys per window-attention workgroup
 constexpr int kWaRowsPerWg = 128;     // window rows per window-attention workgroup
 constexpr size_t kMaxLds = 160 * 1024;
@@ -42,7 +41,7 @@ size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 // and candidate counters) must be zero before the first call; every call
 // leaves it zero.  The scratch part is shared by all entry points.
 struct StateLayout {
-  size_t hist, cand_cnt, total;
+  size_t hist, head_err, total;
 };
 
 StateLayout state_layout(const kvev_cache *c) {
@@ -50,13 +49,13 @@ StateLayout state_layout(const kvev_cache *c) {
   const size_t units = (size_t)c->batch * c->kv_heads;
   size_t off = 0;
   L.hist = off; off = a256(off + units * kvev::kSelectBins * 4);
-  L.cand_cnt = off; off = a256(off + units * 4);
+  L.head_err = off; off = a256(off + units * 4);
   L.total = off;
   return L;
 }
 
 struct SelectLayout {
-  size_t cand, cnt_lt, chunk_off, head_sel, total;
+  size_t cand, ccount, cnt_lt, chunk_off, head_sel, total;
   int chunks;
 };
 
@@ -66,8 +65,10 @@ SelectLayout select_layout(const kvev_cache *c) {
   const size_t max_slots = (size_t)c->max_blocks * KVEV_BLOCK_SIZE;
   L.chunks = (int)((max_slots + kvev::kSelectChunk - 1) / kvev::kSelectChunk);
   size_t off = state_layout(c).total;
-  L.cand = off; off = a256(off + units * max_slots * 8);
-  L.cnt_lt = off; off = a256(off + units * (size_t)L.chunks * 4);
+  const size_t subs = (size_t)L.chunks * 4;  // 256-slot sub-chunks
+  L.cand = off; off = a256(off + units * subs * 256 * 8);
+  L.ccount = off; off = a256(off + units * subs * 4);
+  L.cnt_lt = off; off = a256(off + units * subs * 4);
   L.chunk_off = off; off = a256(off + units * (size_t)L.chunks * 4);
   L.head_sel = off; off = a256(off + units * 16);
   L.total = off;
@@ -75,7 +76,7 @@ SelectLayout select_layout(const kvev_cache *c) {
 }
 
 struct CompactLayout {
-  size_t src_of, new_pos, new_score, stage_k, stage_v, head_info, chunk_err, fc0, total;
+  size_t src_of, new_pos, new_score, stage_k, stage_v, head_info, chunk_mv, fc0, total;
   int chunks, stage_rows;
 };
 
@@ -84,7 +85,7 @@ CompactLayout compact_layout(const kvev_cache *c) {
   const size_t units = (size_t)c->batch * c->kv_heads;
   const size_t max_slots = (size_t)c->max_blocks * KVEV_BLOCK_SIZE;
   const size_t row_bytes = (size_t)c->head_dim * elem_bytes(c);
-  L.chunks = (int)((max_slots + kCompactChunk - 1) / kCompactChunk);
+  L.chunks = (int)((max_slots + kvev::kCompactChunk - 1) / kvev::kCompactChunk);
   // At-risk rows of a head are the kept slots in [first victim, n'): up to
   // n' - 1 of them (evicting only slot 0 shifts every other row).
   L.stage_rows = (int)max_slots;
@@ -95,7 +96,7 @@ CompactLayout compact_layout(const kvev_cache *c) {
   L.stage_k = off; off = a256(off + units * (size_t)L.stage_rows * row_bytes);
   L.stage_v = off; off = a256(off + units * (size_t)L.stage_rows * row_bytes);
   L.head_info = off; off = a256(off + units * 4 * 4);
-  L.chunk_err = off; off = a256(off + units * (size_t)L.chunks * 4);
+  L.chunk_mv = off; off = a256(off + units * (size_t)L.chunks * 8);
   L.fc0 = off; off = a256(off + 4);
   L.total = off;
   return L;
@@ -237,8 +238,8 @@ int kvev_select(const kvev_cache *cache, const float *score, int32_t budget,
   a.victims = victims;
   a.n_victims = n_victims;
   a.hist = reinterpret_cast<uint32_t *>(ws + S.hist);
-  a.cand_cnt = reinterpret_cast<uint32_t *>(ws + S.cand_cnt);
   a.cand = reinterpret_cast<uint2 *>(ws + L.cand);
+  a.ccount = reinterpret_cast<uint32_t *>(ws + L.ccount);
   a.cnt_lt = reinterpret_cast<int32_t *>(ws + L.cnt_lt);
   a.chunk_off = reinterpret_cast<uint32_t *>(ws + L.chunk_off);
   a.head_sel = reinterpret_cast<uint32_t *>(ws + L.head_sel);
@@ -279,8 +280,10 @@ int kvev_compact(const kvev_cache *cache, const int32_t *victims, const int32_t 
   a.stage_k = ws + L.stage_k;
   a.stage_v = ws + L.stage_v;
   a.head_info = reinterpret_cast<int32_t *>(ws + L.head_info);
-  a.chunk_err = reinterpret_cast<int32_t *>(ws + L.chunk_err);
+  a.head_err = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(workspace) +
+                                            state_layout(cache).head_err);
   a.fc0 = reinterpret_cast<int32_t *>(ws + L.fc0);
+  a.chunk_mv = reinterpret_cast<int32_t *>(ws + L.chunk_mv);
   a.units = cache->batch * cache->kv_heads;
   a.max_blocks = cache->max_blocks;
   a.max_slots = cache->max_blocks * KVEV_BLOCK_SIZE;
@@ -289,6 +292,7 @@ int kvev_compact(const kvev_cache *cache, const int32_t *victims, const int32_t 
   a.stage_rows = L.stage_rows;
   a.chunks = L.chunks;
   a.free_capacity = free_capacity;
+  a.rows_per_item = 4 * 256 / (a.row_bytes / 16);  // compact.hip: 4 rows per thread
   return map_err(kvev::launch_compact(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -5,19 +5,19 @@
 // kept token.  Those sources are exactly the kept slots in [first victim, n')
 // ("at risk"); they are copied to the workspace first.  Three launches:
 //   prep     (1024-slot chunk of one head per workgroup): checks the victim
-//            list and the block ids, ranks the kept slots (a two-round
-//            cooperative search gives the victims before the chunk), records
-//            for each destination rank its source (physical row, staged
-//            copy, or "stays"), the kept pos / score values, and copies the
-//            at-risk rows to the workspace.  Reads the cache only.
-//   gather   (persistent grid over (head, 64-rank) items): copies every
-//            moving K and V row with 16-byte accesses, then pos and score;
-//            the first item of each head also records the head's error
-//            state and the number of blocks it frees.
+//            list and the block ids, finds the victims inside the chunk
+//            (256 evenly spaced samples bracket them, one range load fetches
+//            them), ranks the kept slots, records for each destination rank
+//            its source (physical row, staged copy, or "stays") and the kept
+//            pos / score values, and copies the at-risk rows to the
+//            workspace.  Reads the cache only.
+//   gather   (persistent grid over (head, rank range) items): each thread
+//            issues all of its 16-byte K and V loads before any store.
 //   finalize (256 logical blocks of one head per workgroup): appends the
 //            emptied tail blocks [ceil(n'/16), ceil(n/16)) to the free list
 //            in (b, h, block) order, clears their table entries, sets
-//            seq_len = n' and completes the stats.
+//            seq_len = n', completes the stats and clears the head's error
+//            word for the next call.
 // ([H2O] "PagedAttention Memory Integration"; [VTOK] section 3.3, stage 3
 // and section 3.5, invariants I1, I2 and I4.)
 #include <hip/hip_runtime.h>
@@ -29,11 +29,11 @@ namespace kvev {
 
 namespace {
 constexpr int kThreads = 256;
-constexpr int kChunk = 1024;          // slots per prep workgroup
+constexpr int kChunk = kCompactChunk;   // slots per prep workgroup
 constexpr int kPerThread = kChunk / kThreads;
-constexpr int kRankChunk = 64;        // destination ranks per gather item
-constexpr int kFinBlocks = 256;       // logical blocks per finalize workgroup
-constexpr int kMaxUnits = kCompactMaxUnits;  // heads a gather workgroup indexes in LDS
+constexpr int kFinBlocks = 256;         // logical blocks per finalize workgroup
+constexpr int kMaxUnits = kCompactMaxUnits;
+constexpr int kRange = 4096;            // victims a prep workgroup stages in LDS
 
 // Exclusive prefix sum over a 256-thread workgroup.
 __device__ int block_exclusive_scan(int v, int *wave_tot) {
@@ -52,30 +52,23 @@ __device__ int block_exclusive_scan(int v, int *wave_tot) {
   return before + incl - v;
 }
 
-// Number of entries of the ascending array a[0, m) below key (lower bound),
-// found by the whole workgroup in two rounds of independent loads: 256
-// evenly spaced samples bracket the answer, then the bracket is counted.
-__device__ int wg_lower_bound(const int32_t *a, int m, int key) {
-  const int tid = threadIdx.x;
-  const int S = (m + kThreads - 1) / kThreads;  // sample spacing, >= 1 when m > 0
-  const int idx = tid * S;
-  const int c = __syncthreads_count(idx < m && a[idx] < key);
-  if (c == 0) return 0;
-  // a[(c-1)*S] < key, and a[c*S] >= key (or c*S >= m)
-  const int base = (c - 1) * S + 1;
-  const int len = min(S - 1, m - base);
+// Lower bound of key in the ascending a[0, m): counts the bracket [base,
+// base + len) after the samples placed it there (one more round of loads).
+__device__ int bracket_count(const int32_t *a, int base, int len, int key) {
   int cnt = 0;
   for (int off = 0; off < len; off += kThreads)
-    cnt += __syncthreads_count(off + tid < len && a[base + off + tid] < key);
+    cnt += __syncthreads_count(off + threadIdx.x < len && a[base + off + threadIdx.x] < key);
   return base + cnt;
 }
 }  // namespace
 
 __global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArgs P) {
   __shared__ uint8_t flag[kChunk];
+  __shared__ int vr[kRange];
   __shared__ int stage_s[kChunk], stage_i[kChunk];
   __shared__ int s_err, s_nstage;
   __shared__ int wave_tot[kThreads / kWave];
+  __shared__ int r0s[kThreads / kWave], r1s[kThreads / kWave];
 
   const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
   if (u == 0 && c == 0 && tid == 0) {
@@ -84,48 +77,99 @@ __global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArg
   }
   const int n = P.seq_len[u];
   const int m = P.n_victims[u];
-  int err = 0;
-  if (n < 0 || n > P.max_slots) err = 2;
-  else if (m < 0 || m > n) err = 1;
+  if (c == 0 && tid == 0) P.head_info[u * 4 + 0] = n;
+  // n or m out of range: the gather sees it from seq_len / n_victims directly
+  if (n < 0 || n > P.max_slots || m < 0 || m > n || m == 0) return;
+  const int s0 = c * kChunk;
   const int32_t *vic = P.victims + (size_t)u * P.max_slots;
+  const size_t urow = (size_t)u * P.max_slots;
+  const int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
   if (tid == 0) {
     s_err = 0;
     s_nstage = 0;
-    if (c == 0) P.head_info[u * 4 + 0] = n;
   }
-  __syncthreads();
-  // the victim list must be strictly ascending inside [0, n): chunk c checks
-  // the pairs starting at indices [m*c/chunks, m*(c+1)/chunks)
-  if (!err && m > 0) {
+  for (int i = tid; i < kChunk; i += kThreads) flag[i] = 0;
+
+  // ---- one round of independent loads: the victim-list check of this
+  // chunk's index share, the samples, the chunk's block ids, pos and score
+  int bad = 0;
+  {
     const int i0 = (int)((int64_t)m * c / P.chunks), i1 = (int)((int64_t)m * (c + 1) / P.chunks);
-    int bad = 0;
     for (int i = i0 + tid; i < i1; i += kThreads) {
       const int v = vic[i];
       if (v < 0 || v >= n || (i + 1 < m && vic[i + 1] <= v)) bad = 1;
     }
-    if (bad) atomicOr(&s_err, 1);
   }
-  __syncthreads();
-  err |= s_err;
-  const int s0 = c * kChunk;
-  if (err || m == 0 || s0 >= n) {
-    if (tid == 0) P.chunk_err[(size_t)u * P.chunks + c] = err;
-    return;
+  const bool live_chunk = s0 < n;
+  const int s1 = live_chunk ? min(s0 + kChunk, n) : s0;
+  int posv[kPerThread];
+  float scv[kPerThread];
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int s = s0 + tid * kPerThread + q;
+    posv[q] = (s < s1) ? P.pos[urow + s] : 0;
+    scv[q] = (s < s1 && P.score) ? P.score[urow + s] : 0.f;
   }
-  const int s1 = min(s0 + kChunk, n);
-  const int j0 = wg_lower_bound(vic, m, s0);
-  const int j1 = wg_lower_bound(vic, m, s1);
-  for (int i = tid; i < kChunk; i += kThreads) flag[i] = 0;
-  // every block holding a slot of this chunk must be a valid pool index
-  const int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
   for (int lb = s0 / kBlock + tid; lb < (s1 + kBlock - 1) / kBlock; lb += kThreads) {
     const int blk = bt[lb];
-    if (blk < 0 || blk >= P.num_blocks) atomicOr(&s_err, 1);
+    if (blk < 0 || blk >= P.num_blocks) bad = 1;
   }
-  __syncthreads();
-  for (int j = j0 + tid; j < j1; j += kThreads) {
-    const int v = vic[j];
-    if (v >= s0 && v < s1) flag[v - s0] = 1;
+  const int S = (m + kThreads - 1) / kThreads;  // sample spacing
+  const int samp = (tid * S < m) ? vic[tid * S] : INT_MAX;
+  const int first = vic[0];
+  if (bad) atomicOr(&s_err, 1);
+  const int c0 = __syncthreads_count(samp < s0);
+  const int c1 = __syncthreads_count(samp < s1);
+  if (!live_chunk) {
+    if (tid == 0 && s_err) atomicOr(&P.head_err[u], 1u);
+    return;
+  }
+  // victims before s0 lie in [lo0, hi0], victims before s1 in [lo1, hi1]
+  const int lo0 = c0 ? (c0 - 1) * S + 1 : 0, hi0 = min(c0 * S, m);
+  const int lo1 = c1 ? (c1 - 1) * S + 1 : 0, hi1 = min(c1 * S, m);
+  int j0, j1;
+  if (hi1 - lo0 <= kRange) {
+    // ---- one range load covers both brackets and every victim in the chunk
+    for (int i = tid; i < hi1 - lo0; i += kThreads) vr[i] = vic[lo0 + i];
+    __syncthreads();
+    int cnt0 = 0, cnt1 = 0;
+    for (int i = tid; i < hi1 - lo0; i += kThreads) {
+      cnt0 += vr[i] < s0;
+      cnt1 += vr[i] < s1;
+    }
+    // block sums of the per-thread counts
+    {
+      int a0 = cnt0, a1 = cnt1;
+#pragma unroll
+      for (int o = kWave / 2; o >= 1; o >>= 1) {
+        a0 += __shfl_xor(a0, o);
+        a1 += __shfl_xor(a1, o);
+      }
+      if (lane_id() == 0) {
+        r0s[tid / kWave] = a0;
+        r1s[tid / kWave] = a1;
+      }
+      __syncthreads();
+      int t0 = 0, t1 = 0;
+      for (int w = 0; w < kThreads / kWave; ++w) {
+        t0 += r0s[w];
+        t1 += r1s[w];
+      }
+      j0 = lo0 + t0;
+      j1 = lo0 + t1;
+    }
+    for (int i = j0 - lo0 + tid; i < j1 - lo0; i += kThreads) {
+      const int v = vr[i];
+      if (v >= s0 && v < s1) flag[v - s0] = 1;
+    }
+  } else {
+    // long brackets (very sparse victims): count them, then mark
+    j0 = bracket_count(vic, lo0, hi0 - lo0, s0);
+    j1 = bracket_count(vic, lo1, hi1 - lo1, s1);
+    for (int j = j0 + tid; j < j1; j += kThreads) {
+      const int v = vic[j];
+      if (v >= s0 && v < s1) flag[v - s0] = 1;
+    }
   }
   __syncthreads();
 
@@ -137,10 +181,8 @@ __global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArg
   }
   const int excl = block_exclusive_scan(kept, wave_tot);
   const int n2 = n - m;
-  const int first = vic[0];
   int r = (s0 - j0) + excl;  // kept slots before s0, plus those before mine in the chunk
-  const size_t urow = (size_t)u * P.max_slots;
-  int my_err = 0;
+  int my_err = 0, my_moved = 0, my_staged = 0;
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
     const int s = s0 + tid * kPerThread + q;
@@ -153,6 +195,7 @@ __global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArg
       const int si = r - first;
       if (si < 0 || si >= P.stage_rows) { my_err = 1; ++r; continue; }
       src = -2 - si;
+      ++my_staged;
       const int k = atomicAdd(&s_nstage, 1);
       stage_s[k] = s;
       stage_i[k] = si;
@@ -160,13 +203,35 @@ __global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArg
       const int blk = bt[s / kBlock];
       src = (blk >= 0 && blk < P.num_blocks) ? blk * kBlock + s % kBlock : 0;
     }
+    my_moved += src != -1 ? 1 : 0;
     P.src_of[urow + r] = src;
-    P.new_pos[urow + r] = P.pos[urow + s];
-    if (P.score) P.new_score[urow + r] = P.score[urow + s];
+    P.new_pos[urow + r] = posv[q];
+    if (P.score) P.new_score[urow + r] = scv[q];
     ++r;
   }
   if (my_err) atomicOr(&s_err, 1);
+  // per-chunk counts for the stats (summed per head by the finalize step)
+  {
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) {
+      my_moved += __shfl_xor(my_moved, o);
+      my_staged += __shfl_xor(my_staged, o);
+    }
+    if (lane_id() == 0) {
+      r0s[tid / kWave] = my_moved;
+      r1s[tid / kWave] = my_staged;
+    }
+  }
   __syncthreads();
+  if (tid == 0) {
+    int a0 = 0, a1 = 0;
+    for (int w = 0; w < kThreads / kWave; ++w) {
+      a0 += r0s[w];
+      a1 += r1s[w];
+    }
+    P.chunk_mv[((size_t)u * P.chunks + c) * 2 + 0] = a0;
+    P.chunk_mv[((size_t)u * P.chunks + c) * 2 + 1] = a1;
+  }
   // staging copy of the at-risk K and V rows (16-byte pieces)
   const int pieces = P.row_bytes / 16;
   const int ns = s_nstage;
@@ -180,27 +245,26 @@ __global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArg
     st16(P.stage_k + dst, ld16(P.k_pool + src));
     st16(P.stage_v + dst, ld16(P.v_pool + src));
   }
-  __syncthreads();
-  if (tid == 0) P.chunk_err[(size_t)u * P.chunks + c] = err | s_err;
+  if (tid == 0 && s_err) atomicOr(&P.head_err[u], 1u);
 }
 
-// Persistent grid: every workgroup indexes the per-head item counts in LDS.
+// Persistent grid over (head, rank range) items; every head has at least one
+// item, which records the head's error state and the blocks it frees.
 __global__ __launch_bounds__(kThreads) void compact_gather_kernel(const CompactArgs P) {
   __shared__ int item_start[kMaxUnits + 1];
   __shared__ int wave_tot[kThreads / kWave];
   __shared__ int s_total;
   const int tid = threadIdx.x, lane = lane_id();
-  const int U = P.units;
-  // items per head: ceil(n'/64) row chunks, at least one (it records the head state)
+  const int U = P.units, RC = P.rows_per_item;
   int base_count = 0;
   for (int b0 = 0; b0 < U; b0 += kThreads) {
     const int u = b0 + tid;
     int cnt = 0;
     if (u < U) {
-      const int n = P.head_info[u * 4 + 0];
+      const int n = P.seq_len[u];
       const int m = P.n_victims[u];
       const bool ok = n >= 0 && n <= P.max_slots && m > 0 && m <= n;
-      cnt = ok ? max(1, (n - m + kRankChunk - 1) / kRankChunk) : 1;
+      cnt = ok ? max(1, (n - m + RC - 1) / RC) : 1;
     }
     const int ex = block_exclusive_scan(cnt, wave_tot);
     if (u < U) item_start[u] = base_count + ex;
@@ -209,77 +273,75 @@ __global__ __launch_bounds__(kThreads) void compact_gather_kernel(const CompactA
     base_count = s_total;
     __syncthreads();
   }
-  if (tid == 0) item_start[U] = base_count;
-  __syncthreads();
   const int total = base_count;
-  const int pieces = P.row_bytes / 16;
+  const int pieces = P.row_bytes / 16;  // 16-byte pieces per row (8, 16 or 32)
 
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    // head of this item: the last u with item_start[u] <= item
     int lo = 0, hi = U - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (item_start[mid] <= item) lo = mid; else hi = mid - 1;
     }
     const int u = lo, k = item - item_start[u];
-    const int n = P.head_info[u * 4 + 0];
+    const int n = P.seq_len[u];
     const int m = P.n_victims[u];
-    // head error: any prep chunk flag, or n / m out of range
-    int e = 0;
-    for (int c = lane; c < P.chunks; c += kWave) e |= P.chunk_err[(size_t)u * P.chunks + c];
-    const bool nm_bad = n < 0 || n > P.max_slots || m < 0 || m > n;
-    const bool head_bad = __any(e != 0) || nm_bad;
+    const uint32_t herr = P.head_err[u];
+    int ev = (int)herr;
+    if (n < 0 || n > P.max_slots) ev = 2;
+    else if (m < 0 || m > n) ev = 1;
     if (k == 0 && tid == 0) {
-      int ev = nm_bad ? ((n < 0 || n > P.max_slots) ? 2 : 1) : 0;
-      for (int c = 0; c < P.chunks && !nm_bad; ++c) ev |= P.chunk_err[(size_t)u * P.chunks + c];
       P.head_info[u * 4 + 2] = ev;
       P.head_info[u * 4 + 3] = (ev || m <= 0) ? 0 : (n + kBlock - 1) / kBlock - (n - m + kBlock - 1) / kBlock;
     }
-    if (head_bad || m <= 0) continue;
+    if (ev || m <= 0) continue;
     const int n2 = n - m;
-    const int r0 = k * kRankChunk;
+    const int r0 = k * RC;
     if (r0 >= n2) continue;
-    const int r1 = min(r0 + kRankChunk, n2);
+    const int r1 = min(r0 + RC, n2);
     const size_t urow = (size_t)u * P.max_slots;
-    const int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
-    for (int idx = tid; idx < (r1 - r0) * pieces; idx += kThreads) {
-      const int r = r0 + idx / pieces, part = idx % pieces;
-      const int src = P.src_of[urow + r];
-      if (src == -1) continue;
-      const size_t dst = ((size_t)bt[r / kBlock] * kBlock + r % kBlock) * P.row_bytes + (size_t)part * 16;
-      uint4 kv, vv;
-      if (src >= 0) {
-        const size_t so = (size_t)src * P.row_bytes + (size_t)part * 16;
-        kv = ld16(P.k_pool + so);
-        vv = ld16(P.v_pool + so);
-      } else {
-        const size_t so = ((size_t)u * P.stage_rows + (-2 - src)) * P.row_bytes + (size_t)part * 16;
-        kv = ld16(P.stage_k + so);
-        vv = ld16(P.stage_v + so);
-      }
-      st16(P.k_pool + dst, kv);
-      st16(P.v_pool + dst, vv);
-    }
-    int moved = 0, risk = 0;
-    for (int r = r0 + tid; r < r1; r += kThreads) {
-      const int src = P.src_of[urow + r];
-      if (src == -1) continue;
-      P.pos[urow + r] = P.new_pos[urow + r];
-      if (P.score) P.score[urow + r] = P.new_score[urow + r];
-      ++moved;
-      risk += src <= -2 ? 1 : 0;
-    }
-    // one atomic per wave
+    // lane group of `pieces` threads per row, one 16-byte piece each, so an
+    // instruction covers whole rows; 4 rows per thread, all loads first
+    const int rpr = kThreads / pieces;  // rows per round
+    const int part = tid % pieces;
+    int rr[4], srcv[4], dblk[4], npos[4];
+    float nsc[4];
 #pragma unroll
-    for (int o = kWave / 2; o >= 1; o >>= 1) {
-      moved += __shfl_xor(moved, o);
-      risk += __shfl_xor(risk, o);
+    for (int i = 0; i < 4; ++i) {
+      rr[i] = r0 + i * rpr + tid / pieces;
+      const bool in = rr[i] < r1;
+      srcv[i] = in ? P.src_of[urow + rr[i]] : -1;
+      dblk[i] = in ? P.block_table[(size_t)u * P.max_blocks + rr[i] / kBlock] : 0;
+      npos[i] = (in && part == 0) ? P.new_pos[urow + rr[i]] : 0;
+      nsc[i] = (in && part == 0 && P.score) ? P.new_score[urow + rr[i]] : 0.f;
     }
-    if (lane == 0 && moved) {
-      atomicAdd(reinterpret_cast<unsigned long long *>(&P.stats[1]), (unsigned long long)moved);
-      atomicAdd(reinterpret_cast<unsigned long long *>(&P.stats[2]),
-                (unsigned long long)moved * 4ull * (unsigned long long)P.row_bytes);
-      if (risk) atomicAdd(reinterpret_cast<unsigned long long *>(&P.stats[3]), (unsigned long long)risk);
+    uint4 kv[4], vv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int src = srcv[i];
+      if (src != -1) {
+        const uint8_t *ks, *vs;
+        if (src >= 0) {
+          ks = P.k_pool + (size_t)src * P.row_bytes;
+          vs = P.v_pool + (size_t)src * P.row_bytes;
+        } else {
+          const size_t so = ((size_t)u * P.stage_rows + (-2 - src)) * P.row_bytes;
+          ks = P.stage_k + so;
+          vs = P.stage_v + so;
+        }
+        kv[i] = ld16(ks + (size_t)part * 16);
+        vv[i] = ld16(vs + (size_t)part * 16);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (srcv[i] == -1) continue;
+      const size_t dst = ((size_t)dblk[i] * kBlock + rr[i] % kBlock) * P.row_bytes + (size_t)part * 16;
+      st16(P.k_pool + dst, kv[i]);
+      st16(P.v_pool + dst, vv[i]);
+      if (part == 0) {
+        P.pos[urow + rr[i]] = npos[i];
+        if (P.score) P.score[urow + rr[i]] = nsc[i];
+      }
     }
   }
 }
@@ -308,11 +370,26 @@ __global__ __launch_bounds__(kThreads) void compact_finalize_kernel(const Compac
   const int err = P.head_info[u * 4 + 2];
   const int freed = room ? P.head_info[u * 4 + 3] : 0;
   if (k == 0 && tid == 0) {
+    P.head_err[u] = 0u;  // state for the next call
     if (err) {
       atomicOr(reinterpret_cast<unsigned long long *>(&P.stats[4]), (unsigned long long)err);
     } else {
       const int m = P.n_victims[u];
-      if (m > 0) P.seq_len[u] = n - m;
+      if (m > 0) {
+        P.seq_len[u] = n - m;
+        long long mv = 0, st = 0;
+        const int live = (n + kChunk - 1) / kChunk;  // chunks prep wrote
+        for (int c = 0; c < live; ++c) {
+          mv += P.chunk_mv[((size_t)u * P.chunks + c) * 2 + 0];
+          st += P.chunk_mv[((size_t)u * P.chunks + c) * 2 + 1];
+        }
+        if (mv) {
+          atomicAdd(reinterpret_cast<unsigned long long *>(&P.stats[1]), (unsigned long long)mv);
+          atomicAdd(reinterpret_cast<unsigned long long *>(&P.stats[2]),
+                    (unsigned long long)mv * 4ull * (unsigned long long)P.row_bytes);
+        }
+        if (st) atomicAdd(reinterpret_cast<unsigned long long *>(&P.stats[3]), (unsigned long long)st);
+      }
       if (freed) atomicAdd(reinterpret_cast<unsigned long long *>(&P.stats[0]), (unsigned long long)freed);
     }
     if (u == P.units - 1) {
@@ -335,8 +412,9 @@ hipError_t launch_compact(const CompactArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(compact_prep_kernel, dim3(a.chunks, a.units), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // enough workgroups to cover every 64-rank item of a full cache, capped
-  const long long items = (long long)a.units * ((a.max_slots + kRankChunk - 1) / kRankChunk);
+  // enough workgroups to cover every item of a full cache, capped
+  const long long items =
+      (long long)a.units * ((a.max_slots + a.rows_per_item - 1) / a.rows_per_item);
   const int grid = (int)(items < 2048 ? (items > 0 ? items : 1) : 2048);
   hipLaunchKernelGGL(compact_gather_kernel, dim3(grid), dim3(kThreads), 0, s, a);
   e = hipGetLastError();

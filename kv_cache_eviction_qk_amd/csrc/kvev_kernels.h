@@ -27,11 +27,11 @@ struct SelectArgs {
   int32_t *victims, *n_victims;
   // workspace: persistent state (zero between calls)
   uint32_t *hist;         // [units][2048] histogram of the top 11 key bits
-  uint32_t *cand_cnt;     // [units] candidates collected
   // workspace: scratch
-  uint2 *cand;            // [units][max_slots] (key, slot) of the threshold bucket
-  int32_t *cnt_lt;        // [units][chunks] keys below the threshold bucket
-  uint32_t *chunk_off;    // [units][chunks] output offset of each chunk
+  uint2 *cand;            // [units][subs][256] (key, slot) of the threshold bucket
+  uint32_t *ccount;       // [units][subs] candidates of each 256-slot sub-chunk
+  int32_t *cnt_lt;        // [units][subs] keys below the threshold bucket
+  uint32_t *chunk_off;    // [units][chunks] output offset of each 1024-slot chunk
   uint32_t *head_sel;     // [units][4] threshold key, tie-cut slot
   int32_t units, max_slots, budget, recent, chunks;
 };
@@ -48,11 +48,12 @@ struct CompactArgs {
   int32_t *new_pos;             // [units][max_slots]: pos of each kept rank
   float *new_score;             // [units][max_slots]: score of each kept rank
   uint8_t *stage_k, *stage_v;   // [units][stage_rows][row_bytes]: at-risk rows
-  int32_t *head_info;           // [units][4]: n before the call, first victim
-  int32_t *chunk_err;           // [units][chunks]
+  int32_t *head_info;           // [units][4]: n before the call, -, error, blocks freed
+  uint32_t *head_err;           // [units] persistent state (zero between calls)
+  int32_t *chunk_mv;            // [units][chunks][2]: rows moved, rows staged
   int32_t *fc0;                 // free_count before the call
   int32_t units, max_blocks, max_slots, num_blocks, row_bytes, stage_rows, chunks,
-      free_capacity;
+      free_capacity, rows_per_item;
 };
 
 struct WindowAttnArgs {
@@ -77,6 +78,7 @@ constexpr int kSelectChunk = 1024;      // select.hip chunk (slots)
 constexpr int kSelectBins = 2048;       // select.hip histogram bins
 constexpr int kSelectMaxChunks = 1024;  // select.hip refine step limit
 constexpr int kCompactMaxUnits = 4096;  // compact.hip gather limit
+constexpr int kCompactChunk = 1024;     // compact.hip prep chunk (slots)
 
 size_t score_lds_bytes(int bf16, int head_dim, int drop, int row_tiles, int tile_blocks,
                        int halo_blocks);

@@ -51,10 +51,9 @@ template <bool BF16, int D, bool DROP>
 __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
   using G_ = Geo<BF16, D>;
   constexpr int ROWB = G_::ROWB, U = G_::U, CPR = G_::CPR;
-  constexpr int NB = DROP ? 2 : 4;  // key blocks per wave iteration
+  constexpr int NB = 2;  // key blocks per pipeline stage (two stages in flight)
 
   extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ int s_minq;
 
   const int RT = P.row_tiles;
   uint4 *qfrag = reinterpret_cast<uint4 *>(smem);
@@ -80,50 +79,9 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
   const int tb1 = min(tb0 + P.tile_blocks, nb);
   const int cb0 = max(0, tb0 - P.halo_blocks), cb1 = min(nb, tb1 + P.halo_blocks);
 
-  // ---- stage the group's window rows in fragment order
-  const int Hq = P.Hkv * P.G;
-  const size_t row0 = ((size_t)b * Hq + (size_t)h * P.G) * P.W;  // first row of the group
-  const int rows = P.rows;
-  if (threadIdx.x == 0) s_minq = INT_MAX;
-  {
-    const uint8_t *qsrc = P.q + row0 * ROWB;
-    const uint8_t *asrc = DROP ? P.a + row0 * ROWB : nullptr;
-    const int nchunks = RT * 16 * CPR;
-    for (int c = threadIdx.x; c < nchunks; c += kThreads) {
-      const int r = c / CPR, cc = c % CPR;
-      const int lg = cc / U, j = cc % U;
-      const int dst = ((r / 16) * U + j) * kWave + lg * 16 + (r % 16);
-      uint4 v = make_uint4(0, 0, 0, 0), av = make_uint4(0, 0, 0, 0);
-      if (r < rows) {
-        v = ld16(qsrc + (size_t)r * ROWB + cc * 16);
-        if constexpr (DROP) av = ld16(asrc + (size_t)r * ROWB + cc * 16);
-      }
-      qfrag[dst] = v;
-      if constexpr (DROP) {
-        afrag[dst] = av;
-        // ||a||^2 of the row: the CPR chunks of a row sit in CPR consecutive lanes
-        float ss = sumsq_unit<BF16>(av);
-#pragma unroll
-        for (int o = CPR / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-        if (cc == 0) an2[r] = ss;
-      }
-    }
-    for (int r = threadIdx.x; r < RT * 16; r += kThreads) {
-      if (r < rows) {
-        lse2[r] = P.lse[row0 + r] * kLog2e;
-        qposr[r] = P.q_pos[(size_t)b * P.W + (r % P.W)];
-      } else {
-        lse2[r] = __builtin_inff();  // padding rows: p = exp2(-inf) = 0
-        qposr[r] = INT_MAX;
-      }
-    }
-  }
-  __syncthreads();
-  for (int w = threadIdx.x; w < P.W; w += kThreads) atomicMin(&s_minq, P.q_pos[(size_t)b * P.W + w]);
-  __syncthreads();
-  const int minq = s_minq;
-
-  // ---- stream this wave's key blocks
+  // ---- this wave's key blocks: ids first, then the first stage of loads is
+  // issued before the window rows are staged, so its latency overlaps the
+  // prologue
   const int l = lane_id(), lr = l & 15, lg = l >> 4;
   const int wv = threadIdx.x / kWave;
   const int nblk = cb1 - cb0;
@@ -165,6 +123,53 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
       F.kp[i] = ps[blk * kBlock + lr];
     }
   };
+  Frag F0, F1;
+  if (nwb > 0) issue(F0, wb0);
+
+  // ---- stage the group's window rows in fragment order: LDS unit
+  // (rt * U + j) * 64 + lane holds row rt*16 + lane%16, 16-byte chunk
+  // (lane/16) * U + j of that row (consecutive threads write consecutive
+  // LDS units)
+  const int Hq = P.Hkv * P.G;
+  const size_t row0 = ((size_t)b * Hq + (size_t)h * P.G) * P.W;  // first row of the group
+  const int rows = P.rows;
+  {
+    const uint8_t *qsrc = P.q + row0 * ROWB;
+    const uint8_t *asrc = DROP ? P.a + row0 * ROWB : nullptr;
+    const int nunits = RT * U * kWave;
+    for (int d = threadIdx.x; d < nunits; d += kThreads) {
+      const int ln = d % kWave, j = (d / kWave) % U, rt = d / (kWave * U);
+      const int r = rt * 16 + (ln & 15), cc = (ln >> 4) * U + j;
+      uint4 v = make_uint4(0, 0, 0, 0), av = make_uint4(0, 0, 0, 0);
+      if (r < rows) {
+        v = ld16(qsrc + (size_t)r * ROWB + cc * 16);
+        if constexpr (DROP) av = ld16(asrc + (size_t)r * ROWB + cc * 16);
+      }
+      qfrag[d] = v;
+      if constexpr (DROP) afrag[d] = av;
+    }
+    for (int r = threadIdx.x; r < RT * 16; r += kThreads) {
+      if (r < rows) {
+        lse2[r] = P.lse[row0 + r] * kLog2e;
+        qposr[r] = P.q_pos[(size_t)b * P.W + (r % P.W)];
+        if constexpr (DROP) {
+          float ss = 0.f;  // ||a||^2 of the row, chunks in order
+          for (int cc = 0; cc < CPR; ++cc) ss += sumsq_unit<BF16>(ld16(asrc + (size_t)r * ROWB + cc * 16));
+          an2[r] = ss;
+        }
+      } else {
+        lse2[r] = __builtin_inff();  // padding rows: p = exp2(-inf) = 0
+        qposr[r] = INT_MAX;
+        if constexpr (DROP) an2[r] = 0.f;
+      }
+    }
+  }
+  // earliest window query: keys at or before it are never masked
+  int minq = INT_MAX;
+  for (int w = l; w < P.W; w += kWave) minq = min(minq, P.q_pos[(size_t)b * P.W + w]);
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) minq = min(minq, __shfl_xor(minq, o));
+  __syncthreads();
 
   auto compute = [&](const Frag &F, int cur) {
     float psum[NB], pdrop[NB], vn2[NB];
@@ -271,8 +276,6 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
 
   // two fragment sets: the next blocks stream in while the current ones are scored
   if (nwb > 0) {
-    Frag F0, F1;
-    issue(F0, wb0);
     for (int cur = wb0; cur < wb1; cur += 2 * NB) {
       issue(F1, cur + NB);
       compute(F0, cur);

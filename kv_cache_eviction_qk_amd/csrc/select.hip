@@ -8,12 +8,12 @@
 //   hist    chunk: LDS histogram of the top 11 key bits, added into the
 //           head's 2048-bin histogram (integer atomics: exact).
 //   collect chunk: from the head histogram, the bucket b holding rank m;
-//           counts keys below b, appends (key, slot) of bucket b to the
-//           head's candidate list.
-//   refine  head: radix select over the (small) candidate list for T and
-//           the tie cut (the slot of the last evicted key equal to T), the
-//           number of victims of every chunk and its output offset; resets
-//           the histogram state for the next call.
+//           each wave counts the keys below b in its 256 slots and writes
+//           the (key, slot) pairs of bucket b to its own region.
+//   refine  head: gathers the candidate regions (into LDS when they fit),
+//           radix-selects T and the tie cut (the slot of the last evicted
+//           key equal to T), the number of victims of every chunk and its
+//           output offset; resets the histogram state for the next call.
 //   emit    chunk: marks victims, prefix sums them, writes slot indices at
 //           the chunk's offset: ascending order overall.
 // Integer throughout: the result depends only on the score bits.
@@ -32,6 +32,7 @@ constexpr int kBins = kSelectBins;           // top 11 key bits
 constexpr int kShift = 21;
 constexpr int kRefineThreads = 1024;
 constexpr int kMaxChunks = kSelectMaxChunks; // chunks per head the refine step indexes
+constexpr int kStaged = 6144;                // candidates the refine step keeps in LDS
 
 __device__ __forceinline__ bool head_params(const SelectArgs &P, int u, int &n, int &m, int &nc) {
   n = P.seq_len[u];
@@ -141,7 +142,6 @@ __global__ __launch_bounds__(kThreads) void select_hist_kernel(const SelectArgs 
 __global__ __launch_bounds__(kThreads) void select_collect_kernel(const SelectArgs P) {
   __shared__ uint32_t h[kBins];
   __shared__ uint32_t wave_tot[kThreads / kWave];
-  __shared__ int red[kThreads / kWave];
   __shared__ int s_b;
   __shared__ uint32_t s_below;
   const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x, lane = lane_id();
@@ -149,77 +149,122 @@ __global__ __launch_bounds__(kThreads) void select_collect_kernel(const SelectAr
   if (!head_params(P, u, n, m, nc) || m == 0) return;
   const int s0 = c * kChunk;
   if (s0 >= nc) return;
-  const int s1 = min(s0 + kChunk, nc);
   const uint32_t *hg = P.hist + (size_t)u * kBins;
   for (int i = tid; i < kBins; i += kThreads) h[i] = hg[i];
   __syncthreads();
   find_bucket(h, (uint32_t)m, &s_b, &s_below, wave_tot);
   const uint32_t b = (uint32_t)s_b;
+  // each wave owns a 256-slot sub-chunk and its own candidate region: no
+  // atomics, no workgroup barrier
+  const int wv = tid / kWave;
+  const int subs = P.chunks * 4, sub = c * 4 + wv;
   const float *row = P.score + (size_t)u * P.max_slots;
-  uint2 *cand = P.cand + (size_t)u * P.max_slots;
+  uint2 *cand = P.cand + ((size_t)u * subs + sub) * 256;
+  const int w0 = s0 + wv * 256;
+  uint32_t k = 0;
   int below = 0;
-  for (int base = s0; base < s1; base += kThreads) {
-    const int s = base + tid;
-    uint32_t key = 0xffffffffu;
-    if (s < s1) key = score_key(row[s]);
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int s = w0 + it * kWave + lane;
+    const bool valid = s < nc;
+    const uint32_t key = valid ? score_key(row[s]) : 0xffffffffu;
     const uint32_t bk = key >> kShift;
-    below += (s < s1 && bk < b) ? 1 : 0;
-    const bool take = s < s1 && bk == b;
+    below += (valid && bk < b) ? 1 : 0;
+    const bool take = valid && bk == b;
     const uint64_t mask = __ballot(take);
-    if (mask) {
-      int slot0 = 0;
-      if (lane == 0) slot0 = (int)atomicAdd(&P.cand_cnt[u], (uint32_t)__popcll(mask));
-      slot0 = __shfl(slot0, 0);
-      const int at = slot0 + ballot_prefix(mask);
-      if (take && at < P.max_slots) cand[at] = make_uint2(key, (uint32_t)s);
-    }
+    if (take) cand[k + ballot_prefix(mask)] = make_uint2(key, (uint32_t)s);
+    k += (uint32_t)__popcll(mask);
   }
-  const int tot = block_sum(below, red);
-  if (tid == 0) P.cnt_lt[(size_t)u * P.chunks + c] = tot;
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) below += __shfl_xor(below, o);
+  if (lane == 0) {
+    P.cnt_lt[(size_t)u * subs + sub] = below;
+    P.ccount[(size_t)u * subs + sub] = k;
+  }
 }
 
-// One workgroup per head: exact threshold from the candidate list.
+// One workgroup per head: exact threshold from the candidate lists.
 __global__ __launch_bounds__(kRefineThreads) void select_refine_kernel(const SelectArgs P) {
   __shared__ uint32_t h[kBins];
   __shared__ uint32_t wave_tot[kRefineThreads / kWave];
   __shared__ uint32_t s_digit, s_rank, s_below;
   __shared__ int s_b;
   __shared__ uint32_t chunk_cnt[kMaxChunks];
-  const int u = blockIdx.x, tid = threadIdx.x;
+  __shared__ uint32_t soff[4 * kMaxChunks + 1];
+  __shared__ uint2 cl[kStaged];
+  const int u = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
   int n, m, nc;
   uint32_t *hg = P.hist + (size_t)u * kBins;
   if (!head_params(P, u, n, m, nc)) {
-    if (tid == 0) {
-      P.n_victims[u] = -1;
-      P.cand_cnt[u] = 0;
-    }
+    if (tid == 0) P.n_victims[u] = -1;
     return;  // inconsistent head: its histogram was not touched
   }
   if (m == 0) {
-    if (tid == 0) {
-      P.n_victims[u] = 0;
-      P.cand_cnt[u] = 0;
-    }
+    if (tid == 0) P.n_victims[u] = 0;
     return;
   }
+  const int subs = P.chunks * 4;
+  const int live = (nc + kChunk - 1) / kChunk;  // chunks collect wrote
+  const int nsub = live * 4;
   for (int i = tid; i < kBins; i += kRefineThreads) h[i] = hg[i];
+  // exclusive scan of the sub-chunk candidate counts (up to 4 per thread)
+  {
+    uint32_t v[4], mine = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = tid * 4 + q;
+      v[q] = i < nsub ? min(P.ccount[(size_t)u * subs + i], 256u) : 0u;
+      mine += v[q];
+    }
+    uint32_t incl = mine;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    if (lane == kWave - 1) wave_tot[wv] = incl;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int w = 0; w < wv; ++w) before += wave_tot[w];
+    uint32_t e = before + incl - mine;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = tid * 4 + q;
+      if (i < nsub) soff[i] = e;
+      e += v[q];
+    }
+    if (tid == kRefineThreads - 1) soff[nsub] = e;  // total
+    __syncthreads();
+  }
+  const int ncand = (int)soff[nsub];
+  const uint2 *cand = P.cand + (size_t)u * subs * 256;
+  // candidate i: sub-chunk by binary search over the offsets
+  auto cand_at = [&](int i) -> uint2 {
+    int lo = 0, hi = nsub - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int)soff[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    return cand[(size_t)lo * 256 + (i - (int)soff[lo])];
+  };
+  const bool staged = ncand <= kStaged;
+  if (staged)
+    for (int i = tid; i < ncand; i += kRefineThreads) cl[i] = cand_at(i);
+  auto get = [&](int i) -> uint2 { return staged ? cl[i] : cand_at(i); };
   __syncthreads();
   find_bucket(h, (uint32_t)m, &s_b, &s_below, wave_tot);
   const uint32_t bkt = (uint32_t)s_b;
   const uint32_t need = (uint32_t)m - s_below;  // rank of T inside bucket bkt, 1-based
-  // the count stays below max_slots unless the state was not zeroed; clamp anyway
-  const int ncand = (int)min(P.cand_cnt[u], (uint32_t)P.max_slots);
-  const uint2 *cand = P.cand + (size_t)u * P.max_slots;
 
   // radix select over the low 21 bits of the candidates' keys (7 + 7 + 7)
-  uint32_t prefix = bkt << kShift, pmask = 0xffffffffu << kShift, rank = need;
+  uint32_t prefix = bkt << kShift, pmask = 0xffffffffu << kShift, rank = need, cnt_t = 0;
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = 14 - 7 * pass;
     if (tid < 128) h[tid] = 0;
     __syncthreads();
     for (int i = tid; i < ncand; i += kRefineThreads) {
-      const uint32_t k = cand[i].x;
-      if ((k & pmask) == prefix) atomicAdd(&h[(k >> shift) & 127u], 1u);
+      const uint32_t key = get(i).x;
+      if ((key & pmask) == prefix) atomicAdd(&h[(key >> shift) & 127u], 1u);
     }
     __syncthreads();
     pick_digit(h, 128, rank, &s_digit, &s_rank);
@@ -227,47 +272,54 @@ __global__ __launch_bounds__(kRefineThreads) void select_refine_kernel(const Sel
     prefix |= s_digit << shift;
     pmask |= 127u << shift;
     rank = s_rank;
+    cnt_t = h[s_digit];  // after the last pass: the number of keys equal to T
     __syncthreads();
   }
   const uint32_t T = prefix;
   const uint32_t eT = rank;  // keys equal to T that are evicted: the eT lowest slots
 
-  // tie cut: the eT-th smallest slot among the candidates with key T
-  uint32_t sp = 0, sm = 0, srank = eT;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    if (tid < 256) h[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < ncand; i += kRefineThreads) {
-      const uint2 cv = cand[i];
-      if (cv.x == T && (cv.y & sm) == sp) atomicAdd(&h[(cv.y >> shift) & 255u], 1u);
+  // tie cut: the eT-th smallest slot among the candidates with key T (all of
+  // them when every key equal to T is evicted)
+  int tie_cut = INT_MAX;
+  if (eT < cnt_t) {
+    uint32_t sp = 0, sm = 0, srank = eT;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      if (tid < 256) h[tid] = 0;
+      __syncthreads();
+      for (int i = tid; i < ncand; i += kRefineThreads) {
+        const uint2 cv = get(i);
+        if (cv.x == T && (cv.y & sm) == sp) atomicAdd(&h[(cv.y >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      pick_digit(h, 256, srank, &s_digit, &s_rank);
+      __syncthreads();
+      sp |= s_digit << shift;
+      sm |= 255u << shift;
+      srank = s_rank;
+      __syncthreads();
     }
-    __syncthreads();
-    pick_digit(h, 256, srank, &s_digit, &s_rank);
-    __syncthreads();
-    sp |= s_digit << shift;
-    sm |= 255u << shift;
-    srank = s_rank;
-    __syncthreads();
+    tie_cut = (int)sp;
   }
-  const int tie_cut = (int)sp;
 
-  // victims per chunk: keys below bucket bkt (counted by collect) plus the
-  // candidates below T and the evicted ties
+  // victims per 1024-slot chunk: keys below bucket bkt (counted by collect)
+  // plus the candidates below T and the evicted ties
   const int chunks = P.chunks;
-  const int live_chunks = (nc + kChunk - 1) / kChunk;  // collect wrote these
-  for (int i = tid; i < chunks; i += kRefineThreads)
-    chunk_cnt[i] = i < live_chunks ? (uint32_t)P.cnt_lt[(size_t)u * chunks + i] : 0u;
+  for (int i = tid; i < chunks; i += kRefineThreads) {
+    uint32_t t = 0;
+    if (i < live)
+      for (int q = 0; q < 4; ++q) t += (uint32_t)P.cnt_lt[(size_t)u * subs + i * 4 + q];
+    chunk_cnt[i] = t;
+  }
   __syncthreads();
   for (int i = tid; i < ncand; i += kRefineThreads) {
-    const uint2 cv = cand[i];
+    const uint2 cv = get(i);
     if (cv.y < (uint32_t)nc && (cv.x < T || (cv.x == T && (int)cv.y <= tie_cut)))
       atomicAdd(&chunk_cnt[cv.y / kChunk], 1u);
   }
   __syncthreads();
   // exclusive scan of the chunk counts (chunks <= 1024: one per thread)
   {
-    const int lane = lane_id(), wv = tid / kWave;
     const uint32_t v = tid < chunks ? chunk_cnt[tid] : 0u;
     uint32_t incl = v;
 #pragma unroll
@@ -285,7 +337,6 @@ __global__ __launch_bounds__(kRefineThreads) void select_refine_kernel(const Sel
     P.head_sel[u * 4 + 0] = T;
     P.head_sel[u * 4 + 1] = (uint32_t)tie_cut;
     P.n_victims[u] = m;
-    P.cand_cnt[u] = 0;
   }
   // leave the histogram zeroed for the next call
   for (int i = tid; i < kBins; i += kRefineThreads) hg[i] = 0;
