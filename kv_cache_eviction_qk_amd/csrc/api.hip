@@ -18,6 +18,12 @@ namespace {
 constexpr int kWaChunk = 2048;        // keys per window-attention workgroup
 constexpr int kWaRowsPerWg = 128;     // window rows per window-attention workgroup
 constexpr size_t kMaxLds = 160 * 1024;
+#ifndef KV_TILE_MAX
+#define KV_TILE_MAX 256
+#endif
+#ifndef KV_THREADS_MAX
+#define KV_THREADS_MAX 512
+#endif
 constexpr int kMaxPoolKernel = 2049;  // halo of at most 64 blocks per side
 
 bool valid_cache(const kvev_cache *c) {
@@ -206,10 +212,16 @@ int kvev_score(const kvev_cache *cache, const kvev_window *win, int32_t flags,
   a.flags = flags & (KVEV_SUM | KVEV_POOL | KVEV_ACCUMULATE);
   a.pool_r = (flags & KVEV_POOL) ? (pool_kernel - 1) / 2 : 0;
   a.halo_blocks = (a.pool_r + KVEV_BLOCK_SIZE - 1) / KVEV_BLOCK_SIZE;
-  // tiles of up to 64 blocks (1024 keys); smaller when that leaves the chip underfilled
-  int tb = 64;
-  while (tb > 8 && (int64_t)a.units * ((cache->max_blocks + tb - 1) / tb) < 1024) tb /= 2;
+  // Up to 8 waves (512 threads) share one staging of the window rows and
+  // split a tile of up to 256 blocks; smaller tiles and workgroups when the
+  // tiles would not cover the 256 CUs.
+  int tb = KV_TILE_MAX, threads = KV_THREADS_MAX;
+  while (tb > 16 && (int64_t)a.units * ((cache->max_blocks + tb - 1) / tb) < 256) tb /= 2;
+  while (threads > 256 && tb < 16 * (threads / 64)) threads /= 2;
+  // a wave indexes its block range by lane: at most 64 blocks per wave
+  while (tb > 1 && (tb + 2 * a.halo_blocks + threads / 64 - 1) / (threads / 64) > 64) tb /= 2;
   a.tile_blocks = tb;
+  a.threads = threads;
   a.tiles_per_head = (cache->max_blocks + tb - 1) / tb;
   a.c1 = win->scale * 1.4426950408889634f;
   const int bf16 = cache->dtype == KVEV_BF16;

@@ -94,11 +94,22 @@ __global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArg
   // chunk's index share, the samples, the chunk's block ids, pos and score
   int bad = 0;
   {
+    // index share of this chunk: at most ceil(m / chunks) <= 1024 entries, so
+    // four per thread, all loads issued before any check
     const int i0 = (int)((int64_t)m * c / P.chunks), i1 = (int)((int64_t)m * (c + 1) / P.chunks);
-    for (int i = i0 + tid; i < i1; i += kThreads) {
-      const int v = vic[i];
-      if (v < 0 || v >= n || (i + 1 < m && vic[i + 1] <= v)) bad = 1;
+    int va[4], vb[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = i0 + tid + q * kThreads;
+      va[q] = i < i1 ? vic[i] : 0;
+      vb[q] = (i < i1 && i + 1 < m) ? vic[i + 1] : INT_MAX;
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = i0 + tid + q * kThreads;
+      if (i < i1 && (va[q] < 0 || va[q] >= n || vb[q] <= va[q])) bad = 1;
+    }
+    if (i1 - i0 > 4 * kThreads) bad = 1;  // cannot happen: m <= max_slots <= 1024 * chunks
   }
   const bool live_chunk = s0 < n;
   const int s1 = live_chunk ? min(s0 + kChunk, n) : s0;
@@ -130,7 +141,21 @@ __global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArg
   int j0, j1;
   if (hi1 - lo0 <= kRange) {
     // ---- one range load covers both brackets and every victim in the chunk
-    for (int i = tid; i < hi1 - lo0; i += kThreads) vr[i] = vic[lo0 + i];
+    // (at most kRange entries: 16 per thread, all issued before any store)
+    {
+      const int len = hi1 - lo0;
+      int t[kRange / kThreads];
+#pragma unroll
+      for (int q = 0; q < kRange / kThreads; ++q) {
+        const int i = tid + q * kThreads;
+        t[q] = i < len ? vic[lo0 + i] : 0;
+      }
+#pragma unroll
+      for (int q = 0; q < kRange / kThreads; ++q) {
+        const int i = tid + q * kThreads;
+        if (i < len) vr[i] = t[q];
+      }
+    }
     __syncthreads();
     int cnt0 = 0, cnt1 = 0;
     for (int i = tid; i < hi1 - lo0; i += kThreads) {
@@ -348,11 +373,13 @@ __global__ __launch_bounds__(kThreads) void compact_gather_kernel(const CompactA
 
 // Workgroup (k, u): logical blocks [ceil(n'/16) + 256k, ...) of head u.
 __global__ __launch_bounds__(kThreads) void compact_finalize_kernel(const CompactArgs P) {
-  __shared__ long long s_before, s_total;
+  __shared__ long long s_before, s_total, s_mv, s_st;
   const int k = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
   if (tid == 0) {
     s_before = 0;
     s_total = 0;
+    s_mv = 0;
+    s_st = 0;
   }
   __syncthreads();
   long long before = 0, total = 0;
@@ -369,6 +396,25 @@ __global__ __launch_bounds__(kThreads) void compact_finalize_kernel(const Compac
   const int n = P.head_info[u * 4 + 0];
   const int err = P.head_info[u * 4 + 2];
   const int freed = room ? P.head_info[u * 4 + 3] : 0;
+  // rows moved and staged of this head: the prep chunks' counts, summed in parallel
+  long long mv = 0, st = 0;
+  if (k == 0 && !err && n > 0 && n <= P.max_slots) {
+    const int live = (n + kChunk - 1) / kChunk;  // chunks prep wrote
+    for (int c = tid; c < live; c += kThreads) {
+      mv += P.chunk_mv[((size_t)u * P.chunks + c) * 2 + 0];
+      st += P.chunk_mv[((size_t)u * P.chunks + c) * 2 + 1];
+    }
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) {
+      mv += __shfl_xor(mv, o);
+      st += __shfl_xor(st, o);
+    }
+    if (lane_id() == 0 && (mv || st)) {
+      atomicAdd(reinterpret_cast<unsigned long long *>(&s_mv), (unsigned long long)mv);
+      atomicAdd(reinterpret_cast<unsigned long long *>(&s_st), (unsigned long long)st);
+    }
+  }
+  __syncthreads();
   if (k == 0 && tid == 0) {
     P.head_err[u] = 0u;  // state for the next call
     if (err) {
@@ -377,12 +423,7 @@ __global__ __launch_bounds__(kThreads) void compact_finalize_kernel(const Compac
       const int m = P.n_victims[u];
       if (m > 0) {
         P.seq_len[u] = n - m;
-        long long mv = 0, st = 0;
-        const int live = (n + kChunk - 1) / kChunk;  // chunks prep wrote
-        for (int c = 0; c < live; ++c) {
-          mv += P.chunk_mv[((size_t)u * P.chunks + c) * 2 + 0];
-          st += P.chunk_mv[((size_t)u * P.chunks + c) * 2 + 1];
-        }
+        const long long mv = s_mv, st = s_st;
         if (mv) {
           atomicAdd(reinterpret_cast<unsigned long long *>(&P.stats[1]), (unsigned long long)mv);
           atomicAdd(reinterpret_cast<unsigned long long *>(&P.stats[2]),

@@ -17,7 +17,7 @@ struct ScoreArgs {
   float *sum, *pooled, *drop;
   int32_t units, Hkv, G, W, max_blocks, num_blocks;
   int32_t rows, row_tiles;       // G*W and ceil(rows / 16)
-  int32_t flags, pool_r, halo_blocks, tile_blocks, tiles_per_head;
+  int32_t flags, pool_r, halo_blocks, tile_blocks, tiles_per_head, threads;
   float c1;                      // scale * log2(e)
 };
 

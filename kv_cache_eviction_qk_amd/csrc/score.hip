@@ -26,8 +26,6 @@ namespace kvev {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
 
 template <bool BF16, int D>
 struct Geo {
@@ -47,8 +45,9 @@ __device__ __forceinline__ int remap_xcd(int id, int n) {
 
 }  // namespace
 
-template <bool BF16, int D, bool DROP>
+template <bool BF16, int D, bool DROP, int kThreads>
 __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
+  constexpr int kWaves = kThreads / kWave;
   using G_ = Geo<BF16, D>;
   constexpr int ROWB = G_::ROWB, U = G_::U, CPR = G_::CPR;
   constexpr int NB = 2;  // key blocks per pipeline stage (two stages in flight)
@@ -316,10 +315,10 @@ size_t score_lds_bytes(int bf16, int head_dim, int drop, int row_tiles, int tile
   return bytes;
 }
 
-template <bool BF16, int D, bool DROP>
+template <bool BF16, int D, bool DROP, int T>
 static hipError_t launch_t(const ScoreArgs &a, hipStream_t s) {
   const size_t lds = score_lds_bytes(BF16, D, DROP, a.row_tiles, a.tile_blocks, a.halo_blocks);
-  auto fn = score_kernel<BF16, D, DROP>;
+  auto fn = score_kernel<BF16, D, DROP, T>;
   static size_t lds_set = 0;  // largest dynamic LDS size enabled for this variant
   if (lds > 65536 && lds > lds_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
@@ -328,17 +327,26 @@ static hipError_t launch_t(const ScoreArgs &a, hipStream_t s) {
     lds_set = lds;
   }
   const unsigned grid = (unsigned)a.units * (unsigned)a.tiles_per_head;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(T), lds, s, a);
   return hipGetLastError();
+}
+
+template <bool BF16, int D, bool DROP>
+static hipError_t launch_threads(const ScoreArgs &a, hipStream_t s) {
+  if (a.threads == 1024) return launch_t<BF16, D, DROP, 1024>(a, s);
+  if (a.threads == 512) return launch_t<BF16, D, DROP, 512>(a, s);
+  return launch_t<BF16, D, DROP, 256>(a, s);
 }
 
 hipError_t launch_score(const ScoreArgs &a, int bf16, int head_dim, int drop, hipStream_t s) {
   if (bf16) {
-    if (head_dim == 128) return drop ? launch_t<true, 128, true>(a, s) : launch_t<true, 128, false>(a, s);
-    return drop ? launch_t<true, 64, true>(a, s) : launch_t<true, 64, false>(a, s);
+    if (head_dim == 128)
+      return drop ? launch_threads<true, 128, true>(a, s) : launch_threads<true, 128, false>(a, s);
+    return drop ? launch_threads<true, 64, true>(a, s) : launch_threads<true, 64, false>(a, s);
   }
-  if (head_dim == 128) return drop ? launch_t<false, 128, true>(a, s) : launch_t<false, 128, false>(a, s);
-  return drop ? launch_t<false, 64, true>(a, s) : launch_t<false, 64, false>(a, s);
+  if (head_dim == 128)
+    return drop ? launch_threads<false, 128, true>(a, s) : launch_threads<false, 128, false>(a, s);
+  return drop ? launch_threads<false, 64, true>(a, s) : launch_threads<false, 64, false>(a, s);
 }
 
 }  // namespace kvev

@@ -206,16 +206,27 @@ __global__ __launch_bounds__(kRefineThreads) void select_refine_kernel(const Sel
   const int subs = P.chunks * 4;
   const int live = (nc + kChunk - 1) / kChunk;  // chunks collect wrote
   const int nsub = live * 4;
-  for (int i = tid; i < kBins; i += kRefineThreads) h[i] = hg[i];
-  // exclusive scan of the sub-chunk candidate counts (up to 4 per thread)
-  {
-    uint32_t v[4], mine = 0;
+  const int chunks = P.chunks;
+  // one round of independent loads: histogram, candidate counts and the
+  // below-bucket counts of this thread's chunk
+  uint32_t hv[2], v[4], below_c = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = tid * 4 + q;
-      v[q] = i < nsub ? min(P.ccount[(size_t)u * subs + i], 256u) : 0u;
-      mine += v[q];
-    }
+  for (int q = 0; q < 2; ++q) hv[q] = hg[tid + q * kRefineThreads];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = tid * 4 + q;
+    v[q] = i < nsub ? min(P.ccount[(size_t)u * subs + i], 256u) : 0u;
+  }
+  if (tid < live) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) below_c += (uint32_t)P.cnt_lt[(size_t)u * subs + tid * 4 + q];
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) h[tid + q * kRefineThreads] = hv[q];
+  if (tid < chunks) chunk_cnt[tid] = below_c;
+  // exclusive scan of the sub-chunk candidate counts (4 per thread)
+  {
+    uint32_t mine = v[0] + v[1] + v[2] + v[3];
     uint32_t incl = mine;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -248,8 +259,19 @@ __global__ __launch_bounds__(kRefineThreads) void select_refine_kernel(const Sel
     return cand[(size_t)lo * 256 + (i - (int)soff[lo])];
   };
   const bool staged = ncand <= kStaged;
-  if (staged)
-    for (int i = tid; i < ncand; i += kRefineThreads) cl[i] = cand_at(i);
+  if (staged) {
+    uint2 t[kStaged / kRefineThreads];
+#pragma unroll
+    for (int q = 0; q < kStaged / kRefineThreads; ++q) {
+      const int i = tid + q * kRefineThreads;
+      if (i < ncand) t[q] = cand_at(i);
+    }
+#pragma unroll
+    for (int q = 0; q < kStaged / kRefineThreads; ++q) {
+      const int i = tid + q * kRefineThreads;
+      if (i < ncand) cl[i] = t[q];
+    }
+  }
   auto get = [&](int i) -> uint2 { return staged ? cl[i] : cand_at(i); };
   __syncthreads();
   find_bucket(h, (uint32_t)m, &s_b, &s_below, wave_tot);
@@ -304,14 +326,6 @@ __global__ __launch_bounds__(kRefineThreads) void select_refine_kernel(const Sel
 
   // victims per 1024-slot chunk: keys below bucket bkt (counted by collect)
   // plus the candidates below T and the evicted ties
-  const int chunks = P.chunks;
-  for (int i = tid; i < chunks; i += kRefineThreads) {
-    uint32_t t = 0;
-    if (i < live)
-      for (int q = 0; q < 4; ++q) t += (uint32_t)P.cnt_lt[(size_t)u * subs + i * 4 + q];
-    chunk_cnt[i] = t;
-  }
-  __syncthreads();
   for (int i = tid; i < ncand; i += kRefineThreads) {
     const uint2 cv = get(i);
     if (cv.y < (uint32_t)nc && (cv.x < T || (cv.x == T && (int)cv.y <= tie_cut)))
