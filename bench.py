@@ -1,12 +1,15 @@
 """Throughput of one score -> select -> compact pass of attention-score KV-cache
 eviction on one MI355X, on seeded synthetic inputs.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--path fused|separate]
+                    [--no-cpu-baseline]
 
-A step is the whole eviction path for one layer's cache: kvev_score (SnapKV
-window sum + max-pool over the last W prompt queries), kvev_select (budget,
-protected recent window) and kvev_compact (in-place repack, emptied blocks
-to the free list).  Every step works on its own pristine copy of the cache,
+A step is the whole eviction path for one layer's cache: scoring (SnapKV
+window sum + max-pool over the last W prompt queries), selection (budget,
+protected recent window) and compaction (in-place repack, emptied blocks to
+the free list).  The default path is the fused call kvev_evict; --path
+separate times kvev_score, kvev_select and kvev_compact called one after the
+other (same results).  Every step works on its own pristine copy of the cache,
 prepared before the timed region, so the timed region holds only the
 eviction kernels; L2 and the Infinity Cache are flushed before it starts,
 so the keys come from HBM (the flush only reads, so no dirty lines are
@@ -14,8 +17,9 @@ left for the timed kernels to write back).
 
 Prints one JSON line: value = scored KV tokens per second (batch x context
 tokens, every KV head scored, selected and compacted), plus the HBM roofline
-of the dominant kernel (score) measured with HIP events on the launch stream
-and the CPU oracle timed on the host cores.
+of the dominant kernel (the scoring kernel, timed alone through kvev_score
+with HIP events on its launch stream) and the CPU oracle timed on the host
+cores.
 """
 from __future__ import annotations
 
@@ -39,6 +43,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="snapkv_prefill_32k")
+    ap.add_argument("--path", choices=("fused", "separate"), default="fused")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", action="store_true",
                     help="only run the timed steps (for rocprofv3 runs)")
@@ -148,7 +153,15 @@ def main():
     outs = {"sum": None, "pooled": None, "drop": None}
     outs[{"sum": "sum", "pool": "pooled", "drop": "drop"}[kind]] = score_out
 
+    def step_fused(i):
+        K.evict(caches[i], q, lse, q_pos, cfg.softmax_scale, G, flag, cfg.budget, cfg.recent,
+                score_out, victims, n_victims, free_lists[i], free_counts[i], ws,
+                pool_kernel=cfg.pool_kernel, a=a, stats=stats)
+
     def step(i, ev=None):
+        if ev is None and args.path == "fused":
+            step_fused(i)
+            return
         c = caches[i]
         if ev is not None:
             ev[0].record()
@@ -163,9 +176,19 @@ def main():
         if ev is not None:
             ev[3].record()
 
+    def warm_path(fused):
+        for i in range(warm):
+            if fused:
+                step_fused(i)
+            else:
+                step(i, [torch.cuda.Event() for _ in range(4)])
+        torch.cuda.synchronize()
+
+    # warm both paths (first launches load code objects); the timed path last
+    warm_path(args.path != "fused")
     for i in range(warm):
-        step(i)
-    torch.cuda.synchronize()
+        restore(i)
+    warm_path(args.path == "fused")
     st = stats.cpu().numpy().tolist()
     for i in range(copies):
         restore(i)
@@ -191,9 +214,26 @@ def main():
     tokens = B * cfg.L
     value = tokens * steps / (ms_total / 1e3)
 
-    # ---- per-kernel durations (HIP events on the launch stream), same work again
+    st = stats.cpu().numpy().tolist()
+    nv = n_victims.cpu().numpy()
+
+    # ---- the scoring kernel alone (kvev_score, same launch configuration),
+    # one HIP event pair per launch on its stream; each launch reads its own
+    # copy of the cache after one flush, so its keys come from HBM
     for i in range(steps):
         restore(i)
+    flush_caches()
+    torch.cuda.synchronize()
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        sev[i][0].record()
+        K.score(caches[i], q, lse, q_pos, cfg.softmax_scale, G, flag, cfg.pool_kernel,
+                sum=outs["sum"], pooled=outs["pooled"], drop=outs["drop"], a=a)
+        sev[i][1].record()
+    torch.cuda.synchronize()
+    t_score_alone = sum(e[0].elapsed_time(e[1]) for e in sev) / steps
+
+    # ---- the separate calls with an event between stages (same work again)
     flush_caches()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
@@ -203,8 +243,6 @@ def main():
     t_score = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
     t_select = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
     t_compact = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
-    st = stats.cpu().numpy().tolist()
-    nv = n_victims.cpu().numpy()
 
     # algorithmic bytes (what the method must move; see the design notes)
     ms_ = pristine.max_slots
@@ -225,7 +263,7 @@ def main():
     rows_moved = int(st[1])
     compact_bytes = n_vic * 4 + rows_moved * 2 * D * eb * 2 + rows_moved * 4 * 2
     pass_bytes = score_bytes + select_bytes + compact_bytes
-    achieved = score_bytes / (t_score / 1e3) / 1e9
+    achieved = score_bytes / (t_score_alone / 1e3) / 1e9
     src = os.path.join(ROOT, "kv_cache_eviction_qk_amd", "csrc", "score.hip")
     traffic = read_traffic(args.workload, src)
 
@@ -246,19 +284,21 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded; spans planted on window-query directions)",
-        "config": {"workload": args.workload, "batch": B, "kv_heads": Hkv, "group": G,
+        "config": {"workload": args.workload, "path": args.path, "batch": B, "kv_heads": Hkv,
+                   "group": G,
                    "head_dim": D, "context": n, "obs_window": W, "pool_kernel": cfg.pool_kernel,
                    "budget": cfg.budget, "recent_window": cfg.recent, "score": kind,
                    "block_size": 16, "accumulate": "fp32"},
         "pipeline_hbm_frac": pass_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS,
         "pipeline_bytes": pass_bytes,
-        "stage_ms": {"score": t_score, "select": t_select, "compact": t_compact},
+        "separate_calls_ms": {"score": t_score, "select": t_select, "compact": t_compact},
         "wall_s": wall,
         "blocks_freed_per_pass": int(st[0]),
         "rows_moved_per_pass": rows_moved,
-        "roofline": {"kernel": "score_kernel", "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "algorithmic_bytes": score_bytes},
+        "roofline": {"kernel": "score_kernel (kvev_score)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": score_bytes, "launch_ms": t_score_alone},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -272,7 +312,8 @@ def cpu_baseline(case, cfg, kind):
     import oracle
     threads = oracle.default_threads()
     units = cfg.B * cfg.Hkv
-    sample = list(range(min(units, max(threads, 8))))
+    # every head of the workload when that stays within about 20 thread-seconds
+    sample = list(range(units))
     log(f"cpu baseline: oracle on {len(sample)} of {units} KV heads, {threads} threads")
     lse64, a64 = oracle.lse_a(case, want_a=(kind == "drop"), units=sample, nthreads=threads)
     import synth

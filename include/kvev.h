@@ -28,8 +28,9 @@
  *   size sensitivity; [H2O] "PagedAttention Memory Integration").
  * - Workspace: one caller-owned device buffer of kvev_workspace_bytes() bytes
  *   serves every entry point of a cache shape.  ZERO-FILL IT ONCE before its
- *   first use: its leading part holds state that kvev_select expects to be
- *   zero and restores to zero before returning control of it; the rest is
+ *   first use: its leading part holds state (selection histograms, per-head
+ *   compaction accumulators) that kvev_select, kvev_compact and kvev_evict
+ *   expect to be zero and leave zero when their work completes; the rest is
  *   scratch.  Do not modify it between calls; calls sharing it must be
  *   ordered on one stream.  After a KVEV_EDEVICE return, zero it again.
  *
@@ -53,7 +54,7 @@ extern "C" {
 #endif
 
 #define KVEV_BLOCK_SIZE 16
-#define KVEV_ABI_VERSION 1
+#define KVEV_ABI_VERSION 2
 
 typedef enum {
   KVEV_OK = 0,
@@ -122,8 +123,9 @@ typedef struct kvev_window {
  * window is refused); flags empty or unknown; POOL without `pooled`, or
  * pool_kernel < 1 or even ([SNAP] Parameters); DROP without `a` or `drop`;
  * SUM without `sum`; ACCUMULATE without SUM or combined with POOL or DROP.
- * KVEV_EUNSUPPORTED: group*obs_window above 256 rows for DROP or 512 rows
- * otherwise.  No workspace is used; `workspace` may be NULL.
+ * KVEV_EUNSUPPORTED: group*obs_window above 4096, or window rows that do not
+ * fit a workgroup's 160 KB of LDS with the tile (bf16, head_dim 128: about
+ * 540 rows, 270 with DROP).  No workspace is used; `workspace` may be NULL.
  */
 int kvev_score(const kvev_cache *cache, const kvev_window *win, int32_t flags,
                int32_t pool_kernel, float *sum, float *pooled, float *drop, void *workspace,
@@ -174,12 +176,36 @@ int kvev_select(const kvev_cache *cache, const float *score, int32_t budget,
  * Errors: KVEV_EINVAL for NULL pointers or a bad cache; KVEV_ENOSPACE when
  * free_capacity < num_blocks (the list must be able to hold the whole pool)
  * or ws_bytes < kvev_workspace_bytes(cache, 1, 1); KVEV_EUNSUPPORTED above 4096
- * KV heads.
+ * KV heads or 1M slots per head.
  */
 int kvev_compact(const kvev_cache *cache, const int32_t *victims, const int32_t *n_victims,
                  float *score_or_null, int32_t *free_list, int32_t *free_count,
                  int32_t free_capacity, int64_t *stats, void *workspace, size_t ws_bytes,
                  void *stream);
+
+/*
+ * kvev_evict -- one whole eviction step: kvev_score with `flags`, then
+ * kvev_select on that score, then kvev_compact with the score as
+ * score_or_null, with the same results as those three calls ([SNAP] "How it
+ * works": score the window, keep the top budget, drop the rest; [VTOK]
+ * section 3.3 for the repack).  Fused: the scoring pass also builds the
+ * selection histogram and the last tile of each head finds the threshold,
+ * and the compaction's first step marks the victims against it, so the
+ * scores are not re-read to select them.
+ * flags: exactly one of KVEV_SUM, KVEV_POOL, KVEV_DROP (KVEV_ACCUMULATE with
+ * KVEV_SUM); score: fp32 [batch][kv_heads][max_blocks*16] receives that kind
+ * (with ACCUMULATE it holds the running sums on entry) and is compacted with
+ * the tokens, so after the call its slots [0, n') hold the kept tokens'
+ * scores.  victims, n_victims, free_list, free_count, stats: as written by
+ * kvev_select and kvev_compact.  Errors: the union of those three calls'
+ * (KVEV_EINVAL also for several score kinds in flags); workspace as for
+ * kvev_compact.
+ */
+int kvev_evict(const kvev_cache *cache, const kvev_window *win, int32_t flags,
+               int32_t pool_kernel, int32_t budget, int32_t recent_window, float *score,
+               int32_t *victims, int32_t *n_victims, int32_t *free_list, int32_t *free_count,
+               int32_t free_capacity, int64_t *stats, void *workspace, size_t ws_bytes,
+               void *stream);
 
 /*
  * kvev_window_attn -- helper outside the eviction step: the log-sum-exp and
@@ -195,7 +221,7 @@ int kvev_compact(const kvev_cache *cache, const int32_t *victims, const int32_t 
 int kvev_window_attn(const kvev_cache *cache, const kvev_window *win, float *lse_out,
                      void *a_out, void *workspace, size_t ws_bytes, void *stream);
 
-/* Workspace bytes needed by kvev_select, kvev_compact and (for this window
+/* Workspace bytes needed by kvev_select, kvev_compact, kvev_evict and (for this window
  * shape; pass 1, 1 when unused) kvev_window_attn on this cache shape.
  * 0 for a bad cache. */
 size_t kvev_workspace_bytes(const kvev_cache *cache, int32_t group, int32_t obs_window);

@@ -7,8 +7,9 @@ torch stream.  Every step of score, select and compact runs in the HIP
 kernels of ``csrc/``; nothing here computes.  There is no fallback: if
 ``libkvev.so`` is missing or cannot be loaded, importing the library raises.
 
-Names follow the C ABI: ``score``, ``select``, ``compact``,
-``window_attn``, ``workspace_bytes``.
+Names follow the C ABI: ``score``, ``select``, ``compact``, ``evict``
+(score + select + compact in one fused call), ``window_attn``,
+``workspace_bytes``.
 """
 from __future__ import annotations
 
@@ -28,8 +29,9 @@ SUM, POOL, DROP, ACCUMULATE = 1, 2, 4, 8
 BLOCK_SIZE = 16
 
 # the functions include/kvev.h declares
-EXPORTS = ("kvev_score", "kvev_select", "kvev_compact", "kvev_window_attn",
+EXPORTS = ("kvev_score", "kvev_select", "kvev_compact", "kvev_evict", "kvev_window_attn",
            "kvev_workspace_bytes", "kvev_strerror", "kvev_abi_version")
+ABI_VERSION = 2
 
 
 class KvevError(RuntimeError):
@@ -72,15 +74,19 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kvev_score.argtypes = [P, P, i32, i32, P, P, P, P, sz, P]
     L.kvev_select.argtypes = [P, P, i32, i32, P, P, P, sz, P]
     L.kvev_compact.argtypes = [P, P, P, P, P, P, i32, P, P, sz, P]
+    L.kvev_evict.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P, P, i32, P, P, sz, P]
     L.kvev_window_attn.argtypes = [P, P, P, P, P, sz, P]
     L.kvev_workspace_bytes.argtypes = [P, i32, i32]
     L.kvev_workspace_bytes.restype = sz
     L.kvev_strerror.argtypes = [ctypes.c_int]
     L.kvev_strerror.restype = ctypes.c_char_p
     L.kvev_abi_version.argtypes = []
-    for f in (L.kvev_score, L.kvev_select, L.kvev_compact, L.kvev_window_attn,
+    for f in (L.kvev_score, L.kvev_select, L.kvev_compact, L.kvev_evict, L.kvev_window_attn,
               L.kvev_abi_version):
         f.restype = ctypes.c_int
+    if L.kvev_abi_version() != ABI_VERSION:
+        raise ImportError(f"{path} has ABI version {L.kvev_abi_version()}, expected "
+                          f"{ABI_VERSION}: rebuild it")
     _lib = L
     return L
 
@@ -271,6 +277,35 @@ def compact(cache: Cache, victims: torch.Tensor, n_victims: torch.Tensor,
                         _ptr(free_list), _ptr(free_count), free_list.numel(), _ptr(stats),
                         _ptr(workspace), workspace.numel(), _stream(stream))
     _check(rc, "kvev_compact")
+    return stats
+
+
+def evict(cache: Cache, q: torch.Tensor, lse: torch.Tensor, q_pos: torch.Tensor, scale: float,
+          group: int, flags: int, budget: int, recent_window: int, score_row: torch.Tensor,
+          victims: torch.Tensor, n_victims: torch.Tensor, free_list: torch.Tensor,
+          free_count: torch.Tensor, workspace: torch.Tensor, pool_kernel: int = 1,
+          a: Optional[torch.Tensor] = None, stats: Optional[torch.Tensor] = None,
+          stream=None) -> torch.Tensor:
+    """kvev_evict: score + select + compact of one layer in one call (mutates the
+    cache, score_row, the free list) -> stats int64[5] on the GPU."""
+    L = load_library()
+    c = cache.struct()
+    w = _window(cache, q, lse, q_pos, scale, group, a)
+    n = cache.units * cache.max_slots
+    _need(score_row, "score_row", torch.float32, n)
+    _need(victims, "victims", torch.int32, n)
+    _need(n_victims, "n_victims", torch.int32, cache.units)
+    _need(free_list, "free_list", torch.int32)
+    _need(free_count, "free_count", torch.int32, 1)
+    _need(workspace, "workspace", torch.uint8)
+    if stats is None:
+        stats = torch.zeros(5, dtype=torch.int64, device=cache.k_pool.device)
+    _need(stats, "stats", torch.int64, 5)
+    rc = L.kvev_evict(ctypes.byref(c), ctypes.byref(w), flags, pool_kernel, budget,
+                      recent_window, _ptr(score_row), _ptr(victims), _ptr(n_victims),
+                      _ptr(free_list), _ptr(free_count), free_list.numel(), _ptr(stats),
+                      _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "kvev_evict")
     return stats
 
 

@@ -22,7 +22,7 @@ constexpr size_t kMaxLds = 160 * 1024;
 #define KV_TILE_MAX 256
 #endif
 #ifndef KV_THREADS_MAX
-#define KV_THREADS_MAX 512
+#define KV_THREADS_MAX 512  // score workgroups: 256 or 512 threads
 #endif
 constexpr int kMaxPoolKernel = 2049;  // halo of at most 64 blocks per side
 
@@ -43,11 +43,13 @@ int elem_bytes(const kvev_cache *c) { return c->dtype == KVEV_BF16 ? 2 : 4; }
 
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace = [persistent state | scratch].  The state (select's histogram
-// and candidate counters) must be zero before the first call; every call
-// leaves it zero.  The scratch part is shared by all entry points.
+// Workspace = [persistent state | scratch].  The state (selection
+// histograms, per-head compaction accumulators) must be zero before
+// the first call; every call leaves it zero.  The scratch part is shared by
+// all entry points; selection and compaction use disjoint parts of it, so
+// the fused call can pass the threshold from one to the other.
 struct StateLayout {
-  size_t hist, head_err, total;
+  size_t hist, head_acc, total;
 };
 
 StateLayout state_layout(const kvev_cache *c) {
@@ -55,13 +57,13 @@ StateLayout state_layout(const kvev_cache *c) {
   const size_t units = (size_t)c->batch * c->kv_heads;
   size_t off = 0;
   L.hist = off; off = a256(off + units * kvev::kSelectBins * 4);
-  L.head_err = off; off = a256(off + units * 4);
+  L.head_acc = off; off = a256(off + units * 8);
   L.total = off;
   return L;
 }
 
 struct SelectLayout {
-  size_t cand, ccount, cnt_lt, chunk_off, head_sel, total;
+  size_t chunk_off, head_sel, total;
   int chunks;
 };
 
@@ -71,10 +73,6 @@ SelectLayout select_layout(const kvev_cache *c) {
   const size_t max_slots = (size_t)c->max_blocks * KVEV_BLOCK_SIZE;
   L.chunks = (int)((max_slots + kvev::kSelectChunk - 1) / kvev::kSelectChunk);
   size_t off = state_layout(c).total;
-  const size_t subs = (size_t)L.chunks * 4;  // 256-slot sub-chunks
-  L.cand = off; off = a256(off + units * subs * 256 * 8);
-  L.ccount = off; off = a256(off + units * subs * 4);
-  L.cnt_lt = off; off = a256(off + units * subs * 4);
   L.chunk_off = off; off = a256(off + units * (size_t)L.chunks * 4);
   L.head_sel = off; off = a256(off + units * 16);
   L.total = off;
@@ -82,7 +80,7 @@ SelectLayout select_layout(const kvev_cache *c) {
 }
 
 struct CompactLayout {
-  size_t src_of, new_pos, new_score, stage_k, stage_v, head_info, chunk_mv, fc0, total;
+  size_t src_of, new_pos, new_score, stage_k, stage_v, head_info, fc0, total;
   int chunks, stage_rows;
 };
 
@@ -92,17 +90,16 @@ CompactLayout compact_layout(const kvev_cache *c) {
   const size_t max_slots = (size_t)c->max_blocks * KVEV_BLOCK_SIZE;
   const size_t row_bytes = (size_t)c->head_dim * elem_bytes(c);
   L.chunks = (int)((max_slots + kvev::kCompactChunk - 1) / kvev::kCompactChunk);
-  // At-risk rows of a head are the kept slots in [first victim, n'): up to
-  // n' - 1 of them (evicting only slot 0 shifts every other row).
+  // At-risk rows are staged at their destination rank: up to n' - 1 rows of
+  // a head (evicting only slot 0 shifts every other row).
   L.stage_rows = (int)max_slots;
-  size_t off = state_layout(c).total;
+  size_t off = select_layout(c).total;
   L.src_of = off; off = a256(off + units * max_slots * 4);
   L.new_pos = off; off = a256(off + units * max_slots * 4);
   L.new_score = off; off = a256(off + units * max_slots * 4);
   L.stage_k = off; off = a256(off + units * (size_t)L.stage_rows * row_bytes);
   L.stage_v = off; off = a256(off + units * (size_t)L.stage_rows * row_bytes);
-  L.head_info = off; off = a256(off + units * 4 * 4);
-  L.chunk_mv = off; off = a256(off + units * (size_t)L.chunks * 8);
+  L.head_info = off; off = a256(off + units * 8 * 4);
   L.fc0 = off; off = a256(off + 4);
   L.total = off;
   return L;
@@ -159,9 +156,7 @@ const char *kvev_strerror(int status) {
 
 size_t kvev_workspace_bytes(const kvev_cache *cache, int32_t group, int32_t obs_window) {
   if (!valid_cache(cache)) return 0;
-  size_t need = compact_layout(cache).total;
-  const size_t sel = select_layout(cache).total;
-  if (sel > need) need = sel;
+  size_t need = compact_layout(cache).total;  // includes the selection scratch
   if (group >= 1 && obs_window >= 1) {
     const size_t wa = wa_layout(cache, group, obs_window).total;
     if (wa > need) need = wa;
@@ -169,11 +164,15 @@ size_t kvev_workspace_bytes(const kvev_cache *cache, int32_t group, int32_t obs_
   return need;
 }
 
-int kvev_score(const kvev_cache *cache, const kvev_window *win, int32_t flags,
-               int32_t pool_kernel, float *sum, float *pooled, float *drop, void *workspace,
-               size_t ws_bytes, void *stream) {
-  (void)workspace;
-  (void)ws_bytes;
+}  // extern "C"
+
+namespace {
+
+// Validates the score arguments and fills the kernel's argument block and
+// its LDS size.  Nothing is enqueued.
+int build_score_args(const kvev_cache *cache, const kvev_window *win, int32_t flags,
+                     int32_t pool_kernel, float *sum, float *pooled, float *drop, int fused,
+                     kvev::ScoreArgs &a) {
   if (!valid_cache(cache)) return KVEV_EINVAL;
   int rc = check_window(cache, win);
   if (rc) return rc;
@@ -188,7 +187,7 @@ int kvev_score(const kvev_cache *cache, const kvev_window *win, int32_t flags,
   if ((flags & KVEV_ACCUMULATE) && (!(flags & KVEV_SUM) || (flags & (KVEV_POOL | KVEV_DROP))))
     return KVEV_EINVAL;
 
-  kvev::ScoreArgs a{};
+  a = kvev::ScoreArgs{};
   a.k_pool = static_cast<const uint8_t *>(cache->k_pool);
   a.v_pool = static_cast<const uint8_t *>(cache->v_pool);
   a.block_table = cache->block_table;
@@ -227,11 +226,77 @@ int kvev_score(const kvev_cache *cache, const kvev_window *win, int32_t flags,
   const int bf16 = cache->dtype == KVEV_BF16;
   const int is_drop = (flags & KVEV_DROP) ? 1 : 0;
   const size_t lds = kvev::score_lds_bytes(bf16, cache->head_dim, is_drop, a.row_tiles,
-                                           a.tile_blocks, a.halo_blocks);
+                                           a.tile_blocks, a.halo_blocks, fused);
   if (lds > kMaxLds - 1024) return KVEV_EUNSUPPORTED;
   if ((int64_t)a.units * a.tiles_per_head > INT32_MAX) return KVEV_EUNSUPPORTED;
-  return map_err(kvev::launch_score(a, bf16, cache->head_dim, is_drop,
-                                    static_cast<hipStream_t>(stream)));
+  return KVEV_OK;
+}
+
+// Fills the compaction argument block (workspace pointers included).
+void fill_compact_args(kvev_cache *cache, float *score_or_null, int32_t *free_list,
+                       int32_t *free_count, int32_t free_capacity, int64_t *stats,
+                       void *workspace, kvev::CompactArgs &a) {
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  const CompactLayout L = compact_layout(cache);
+  const StateLayout S = state_layout(cache);
+  a.k_pool = static_cast<uint8_t *>(cache->k_pool);
+  a.v_pool = static_cast<uint8_t *>(cache->v_pool);
+  a.block_table = cache->block_table;
+  a.seq_len = cache->seq_len;
+  a.pos = cache->pos;
+  a.score = score_or_null;
+  a.free_list = free_list;
+  a.free_count = free_count;
+  a.stats = stats;
+  a.src_of = reinterpret_cast<int32_t *>(ws + L.src_of);
+  a.new_pos = reinterpret_cast<int32_t *>(ws + L.new_pos);
+  a.new_score = reinterpret_cast<float *>(ws + L.new_score);
+  a.stage_k = ws + L.stage_k;
+  a.stage_v = ws + L.stage_v;
+  a.head_info = reinterpret_cast<int32_t *>(ws + L.head_info);
+  a.head_acc = reinterpret_cast<unsigned long long *>(ws + S.head_acc);
+  a.fc0 = reinterpret_cast<int32_t *>(ws + L.fc0);
+  a.units = cache->batch * cache->kv_heads;
+  a.max_blocks = cache->max_blocks;
+  a.max_slots = cache->max_blocks * KVEV_BLOCK_SIZE;
+  a.num_blocks = cache->num_blocks;
+  a.row_bytes = cache->head_dim * elem_bytes(cache);
+  a.stage_rows = L.stage_rows;
+  a.chunks = L.chunks;
+  a.free_capacity = free_capacity;
+  a.rows_per_item = 4 * 256 / (a.row_bytes / 16);  // compact.hip: 4 rows per thread
+}
+
+kvev::SelHead sel_head(const kvev_cache *cache, int32_t *n_victims, int32_t budget,
+                       int32_t recent_window, void *workspace) {
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  const StateLayout S = state_layout(cache);
+  const SelectLayout L = select_layout(cache);
+  kvev::SelHead h{};
+  h.n_victims = n_victims;
+  h.hist = reinterpret_cast<uint32_t *>(ws + S.hist);
+  h.head_sel = reinterpret_cast<uint32_t *>(ws + L.head_sel);
+  h.chunk_off = reinterpret_cast<uint32_t *>(ws + L.chunk_off);
+  h.budget = budget;
+  h.recent = recent_window;
+  h.chunks = L.chunks;
+  return h;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvev_score(const kvev_cache *cache, const kvev_window *win, int32_t flags,
+               int32_t pool_kernel, float *sum, float *pooled, float *drop, void *workspace,
+               size_t ws_bytes, void *stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  kvev::ScoreArgs a;
+  const int rc = build_score_args(cache, win, flags, pool_kernel, sum, pooled, drop, 0, a);
+  if (rc) return rc;
+  return map_err(kvev::launch_score(a, cache->dtype == KVEV_BF16, cache->head_dim,
+                                    (flags & KVEV_DROP) ? 1 : 0, static_cast<hipStream_t>(stream)));
 }
 
 int kvev_select(const kvev_cache *cache, const float *score, int32_t budget,
@@ -242,24 +307,13 @@ int kvev_select(const kvev_cache *cache, const float *score, int32_t budget,
   const SelectLayout L = select_layout(cache);
   if (L.chunks > kvev::kSelectMaxChunks) return KVEV_EUNSUPPORTED;
   if (!workspace || ws_bytes < L.total) return KVEV_ENOSPACE;
-  uint8_t *ws = static_cast<uint8_t *>(workspace);
-  const StateLayout S = state_layout(cache);
   kvev::SelectArgs a{};
   a.score = score;
   a.seq_len = cache->seq_len;
   a.victims = victims;
-  a.n_victims = n_victims;
-  a.hist = reinterpret_cast<uint32_t *>(ws + S.hist);
-  a.cand = reinterpret_cast<uint2 *>(ws + L.cand);
-  a.ccount = reinterpret_cast<uint32_t *>(ws + L.ccount);
-  a.cnt_lt = reinterpret_cast<int32_t *>(ws + L.cnt_lt);
-  a.chunk_off = reinterpret_cast<uint32_t *>(ws + L.chunk_off);
-  a.head_sel = reinterpret_cast<uint32_t *>(ws + L.head_sel);
+  a.sel = sel_head(cache, n_victims, budget, recent_window, workspace);
   a.units = cache->batch * cache->kv_heads;
   a.max_slots = cache->max_blocks * KVEV_BLOCK_SIZE;
-  a.budget = budget;
-  a.recent = recent_window;
-  a.chunks = L.chunks;
   return map_err(kvev::launch_select(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -272,40 +326,63 @@ int kvev_compact(const kvev_cache *cache, const int32_t *victims, const int32_t 
   if (free_capacity < cache->num_blocks) return KVEV_ENOSPACE;
   if (cache->batch * cache->kv_heads > kvev::kCompactMaxUnits) return KVEV_EUNSUPPORTED;
   const CompactLayout L = compact_layout(cache);
+  if (L.chunks > kvev::kSelectMaxChunks) return KVEV_EUNSUPPORTED;  // 1M slots per head
   if (!workspace || ws_bytes < L.total) return KVEV_ENOSPACE;
-  uint8_t *ws = static_cast<uint8_t *>(workspace);
   kvev::CompactArgs a{};
-  a.k_pool = static_cast<uint8_t *>(cache->k_pool);
-  a.v_pool = static_cast<uint8_t *>(cache->v_pool);
-  a.block_table = cache->block_table;
-  a.seq_len = cache->seq_len;
-  a.pos = cache->pos;
-  a.score = score_or_null;
+  fill_compact_args(const_cast<kvev_cache *>(cache), score_or_null, free_list, free_count,
+                    free_capacity, stats, workspace, a);
   a.victims = victims;
   a.n_victims = n_victims;
-  a.free_list = free_list;
-  a.free_count = free_count;
-  a.stats = stats;
-  a.src_of = reinterpret_cast<int32_t *>(ws + L.src_of);
-  a.new_pos = reinterpret_cast<int32_t *>(ws + L.new_pos);
-  a.new_score = reinterpret_cast<float *>(ws + L.new_score);
-  a.stage_k = ws + L.stage_k;
-  a.stage_v = ws + L.stage_v;
-  a.head_info = reinterpret_cast<int32_t *>(ws + L.head_info);
-  a.head_err = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(workspace) +
-                                            state_layout(cache).head_err);
-  a.fc0 = reinterpret_cast<int32_t *>(ws + L.fc0);
-  a.chunk_mv = reinterpret_cast<int32_t *>(ws + L.chunk_mv);
-  a.units = cache->batch * cache->kv_heads;
-  a.max_blocks = cache->max_blocks;
-  a.max_slots = cache->max_blocks * KVEV_BLOCK_SIZE;
-  a.num_blocks = cache->num_blocks;
-  a.row_bytes = cache->head_dim * elem_bytes(cache);
-  a.stage_rows = L.stage_rows;
-  a.chunks = L.chunks;
-  a.free_capacity = free_capacity;
-  a.rows_per_item = 4 * 256 / (a.row_bytes / 16);  // compact.hip: 4 rows per thread
   return map_err(kvev::launch_compact(a, static_cast<hipStream_t>(stream)));
+}
+
+int kvev_evict(const kvev_cache *cache, const kvev_window *win, int32_t flags,
+               int32_t pool_kernel, int32_t budget, int32_t recent_window, float *score,
+               int32_t *victims, int32_t *n_victims, int32_t *free_list, int32_t *free_count,
+               int32_t free_capacity, int64_t *stats, void *workspace, size_t ws_bytes,
+               void *stream) {
+  if (!valid_cache(cache) || !score || !victims || !n_victims || !free_list || !free_count ||
+      !stats)
+    return KVEV_EINVAL;
+  const int kind = flags & (KVEV_SUM | KVEV_POOL | KVEV_DROP);
+  if (kind != KVEV_SUM && kind != KVEV_POOL && kind != KVEV_DROP) return KVEV_EINVAL;
+  if (budget <= 0 || recent_window < 0 || recent_window >= budget) return KVEV_EINVAL;
+  kvev::ScoreArgs a;
+  int rc = build_score_args(cache, win, flags, pool_kernel, kind == KVEV_SUM ? score : nullptr,
+                            kind == KVEV_POOL ? score : nullptr, kind == KVEV_DROP ? score : nullptr,
+                            1, a);
+  if (rc) return rc;
+  if (free_capacity < cache->num_blocks) return KVEV_ENOSPACE;
+  if (cache->batch * cache->kv_heads > kvev::kCompactMaxUnits) return KVEV_EUNSUPPORTED;
+  const CompactLayout L = compact_layout(cache);
+  if (L.chunks > kvev::kSelectMaxChunks) return KVEV_EUNSUPPORTED;
+  if (!workspace || ws_bytes < L.total) return KVEV_ENOSPACE;
+  a.sel = sel_head(cache, n_victims, budget, recent_window, workspace);
+  a.sel_kind = kind;
+  kvev::CompactArgs c{};
+  fill_compact_args(const_cast<kvev_cache *>(cache), score, free_list, free_count, free_capacity,
+                    stats, workspace, c);
+  c.victims = victims;
+  c.n_victims = n_victims;
+  c.victims_out = victims;
+  c.head_sel = a.sel.head_sel;
+  c.chunk_off = a.sel.chunk_off;
+  c.sel_score = score;
+  c.recent = recent_window;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  kvev::SelectArgs sa{};
+  sa.score = score;
+  sa.seq_len = cache->seq_len;
+  sa.victims = victims;
+  sa.sel = a.sel;
+  sa.units = cache->batch * cache->kv_heads;
+  sa.max_slots = cache->max_blocks * KVEV_BLOCK_SIZE;
+  rc = map_err(kvev::launch_score(a, cache->dtype == KVEV_BF16, cache->head_dim,
+                                  kind == KVEV_DROP, st));
+  if (rc) return rc;
+  rc = map_err(kvev::launch_select_head(sa, st));
+  if (rc) return rc;
+  return map_err(kvev::launch_evict_compact(c, st));
 }
 
 int kvev_window_attn(const kvev_cache *cache, const kvev_window *win, float *lse_out,

@@ -3,21 +3,25 @@
 // Kept slot s of rank r moves to slot r (r <= s).  Done in parallel this has
 // one hazard: a destination row r < n' may still be the source of another
 // kept token.  Those sources are exactly the kept slots in [first victim, n')
-// ("at risk"); they are copied to the workspace first.  Three launches:
-//   prep     (1024-slot chunk of one head per workgroup): checks the victim
-//            list and the block ids, finds the victims inside the chunk
-//            (256 evenly spaced samples bracket them, one range load fetches
-//            them), ranks the kept slots, records for each destination rank
-//            its source (physical row, staged copy, or "stays") and the kept
-//            pos / score values, and copies the at-risk rows to the
-//            workspace.  Reads the cache only.
-//   gather   (persistent grid over (head, rank range) items): each thread
-//            issues all of its 16-byte K and V loads before any store.
-//   finalize (256 logical blocks of one head per workgroup): appends the
-//            emptied tail blocks [ceil(n'/16), ceil(n/16)) to the free list
-//            in (b, h, block) order, clears their table entries, sets
-//            seq_len = n', completes the stats and clears the head's error
-//            word for the next call.
+// ("at risk"); they are copied to the workspace first.  Two launches:
+//   prep    (1024-slot chunk of one head per workgroup): finds the chunk's
+//           victims, ranks the kept slots, records for each destination rank
+//           its source (physical row, staged copy, or "stays") and the kept
+//           pos / score values, and copies the at-risk rows to the workspace.
+//           Reads the cache only.  Each chunk adds its counts into one 64-bit
+//           word of the head (arrivals, chunks with errors, rows moved, rows
+//           staged) with a single atomic; the chunk that arrives last records
+//           the head's totals, so no chunk reads another's memory.
+//           Two forms: from a caller's ascending victim list (256 evenly
+//           spaced samples bracket the chunk's victims, one range load
+//           fetches them), or from the threshold the selection left in the
+//           workspace, which then also writes the victim list.
+//   gather  (persistent grid over (head, rank range) items): each thread
+//           issues all of its 16-byte K and V loads before any store.  The
+//           first item of a head also appends the emptied tail blocks
+//           [ceil(n'/16), ceil(n/16)) to the free list in (b, h, block)
+//           order, clears their table entries, sets seq_len = n' and adds the
+//           head's stats.
 // ([H2O] "PagedAttention Memory Integration"; [VTOK] section 3.3, stage 3
 // and section 3.5, invariants I1, I2 and I4.)
 #include <hip/hip_runtime.h>
@@ -31,9 +35,16 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChunk = kCompactChunk;   // slots per prep workgroup
 constexpr int kPerThread = kChunk / kThreads;
-constexpr int kFinBlocks = 256;         // logical blocks per finalize workgroup
 constexpr int kMaxUnits = kCompactMaxUnits;
 constexpr int kRange = 4096;            // victims a prep workgroup stages in LDS
+
+struct PrepLds {
+  int stage_s[kChunk], stage_i[kChunk];  // at-risk slots and their staging rows
+  int blk_l[kChunk / kBlock];            // block ids of the chunk's logical blocks
+  int wave_tot[kThreads / kWave];
+  int r0s[kThreads / kWave], r1s[kThreads / kWave];
+  int s_err, s_nstage;
+};
 
 // Exclusive prefix sum over a 256-thread workgroup.
 __device__ int block_exclusive_scan(int v, int *wave_tot) {
@@ -52,6 +63,27 @@ __device__ int block_exclusive_scan(int v, int *wave_tot) {
   return before + incl - v;
 }
 
+// Sums of a and b over a 256-thread workgroup (every thread gets them).
+__device__ void block_sum2(int &a, int &b, PrepLds &S) {
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) {
+    a += __shfl_xor(a, o);
+    b += __shfl_xor(b, o);
+  }
+  __syncthreads();
+  if (lane_id() == 0) {
+    S.r0s[threadIdx.x / kWave] = a;
+    S.r1s[threadIdx.x / kWave] = b;
+  }
+  __syncthreads();
+  a = 0;
+  b = 0;
+  for (int w = 0; w < kThreads / kWave; ++w) {
+    a += S.r0s[w];
+    b += S.r1s[w];
+  }
+}
+
 // Lower bound of key in the ascending a[0, m): counts the bracket [base,
 // base + len) after the samples placed it there (one more round of loads).
 __device__ int bracket_count(const int32_t *a, int base, int len, int key) {
@@ -60,33 +92,178 @@ __device__ int bracket_count(const int32_t *a, int base, int len, int key) {
     cnt += __syncthreads_count(off + threadIdx.x < len && a[base + off + threadIdx.x] < key);
   return base + cnt;
 }
-}  // namespace
 
-__global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArgs P) {
-  __shared__ uint8_t flag[kChunk];
-  __shared__ int vr[kRange];
-  __shared__ int stage_s[kChunk], stage_i[kChunk];
-  __shared__ int s_err, s_nstage;
-  __shared__ int wave_tot[kThreads / kWave];
-  __shared__ int r0s[kThreads / kWave], r1s[kThreads / kWave];
+__device__ __forceinline__ int blocks_of(int n) { return (n + kBlock - 1) / kBlock; }
 
-  const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
-  if (u == 0 && c == 0 && tid == 0) {
+// Blocks a head frees: 0 unless it is consistent, error free and loses tokens.
+__device__ __forceinline__ int head_freed(const CompactArgs &P, int n, int m, int err) {
+  if (err || n < 0 || n > P.max_slots || m <= 0 || m > n) return 0;
+  return blocks_of(n) - blocks_of(n - m);
+}
+
+// Heads that are inconsistent, or lose nothing, are settled by chunk 0 alone.
+__device__ bool settle_trivial(const CompactArgs &P, int u, int c, int n, int m) {
+  int err = 0;
+  if (n < 0 || n > P.max_slots) err = 2;
+  else if (m < 0 || m > n) err = 1;
+  if (!err && m > 0) return false;
+  if (c == 0 && threadIdx.x == 0) {
+    int32_t *hi = P.head_info + (size_t)u * 8;
+    hi[0] = n;
+    hi[1] = m;
+    hi[2] = err;
+    hi[3] = 0;
+    hi[4] = 0;
+    hi[5] = 0;
+  }
+  return true;
+}
+
+// Ranks the kept slots of the chunk [s0, s1) (thread t owns the slots
+// s0 + 4t .. s0 + 4t + 3), records their sources and new pos / score, copies
+// the at-risk rows to the workspace and the chunk's moved / staged counts.
+// j0: victims of the head before s0.  With victims_out, also writes the
+// chunk's victims at their list positions.
+__device__ void rank_and_stage(const CompactArgs &P, int u, int s0, int s1, int n2, int m, int j0,
+                               const bool (&vic)[kPerThread], const int (&posv)[kPerThread],
+                               const float (&scv)[kPerThread], int32_t *victims_out, PrepLds &S,
+                               int &moved, int &staged) {
+  const int tid = threadIdx.x;
+  const size_t urow = (size_t)u * P.max_slots;
+  int kept = 0;
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int s = s0 + tid * kPerThread + q;
+    kept += (s < s1 && !vic[q]) ? 1 : 0;
+  }
+  const int excl = block_exclusive_scan(kept, S.wave_tot);
+  int r = (s0 - j0) + excl;  // kept slots before s0, plus those before mine in the chunk
+  int jv = j0 + (min(tid * kPerThread, max(0, s1 - s0)) - excl);  // victims before mine
+  int my_err = 0, my_moved = 0, my_staged = 0;
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int s = s0 + tid * kPerThread + q;
+    if (s >= s1) continue;
+    if (vic[q]) {
+      if (victims_out) {
+        if (jv >= 0 && jv < m) victims_out[urow + jv] = s;
+        else my_err = 1;
+      }
+      ++jv;
+      continue;
+    }
+    if (r < 0 || r >= n2) { my_err = 1; ++r; continue; }
+    int src;
+    if (r == s) {
+      src = -1;                       // stays in place
+    } else if (s < n2) {              // at risk: staged (at row r) before the gather
+      src = -2 - r;
+      ++my_staged;
+      const int k = atomicAdd(&S.s_nstage, 1);
+      S.stage_s[k] = s;
+      S.stage_i[k] = r;
+    } else {                          // slots >= n' are never written: read in place
+      const int blk = S.blk_l[(s - s0) / kBlock];
+      src = (blk >= 0 && blk < P.num_blocks) ? blk * kBlock + s % kBlock : 0;
+    }
+    my_moved += src != -1 ? 1 : 0;
+    P.src_of[urow + r] = src;
+    P.new_pos[urow + r] = posv[q];
+    if (P.score) P.new_score[urow + r] = scv[q];
+    ++r;
+  }
+  if (my_err) atomicOr(&S.s_err, 1);
+  block_sum2(my_moved, my_staged, S);  // includes barriers: s_nstage is complete after it
+  moved = my_moved;
+  staged = my_staged;
+  // staging copy of the at-risk K and V rows in 16-byte pieces: each round
+  // issues four K and four V loads per thread before its stores
+  const int pieces = P.row_bytes / 16;
+  const int total = S.s_nstage * pieces;
+  for (int base = 0; base < total; base += 4 * kThreads) {
+    uint4 kv[4], vv[4];
+    size_t dst[4];
+    bool ok[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = base + q * kThreads + tid;
+      ok[q] = false;
+      if (idx < total) {
+        const int k = idx / pieces, part = idx % pieces;
+        const int s = S.stage_s[k];
+        const int blk = S.blk_l[(s - s0) / kBlock];
+        if (blk >= 0 && blk < P.num_blocks) {  // else flagged by the caller
+          const size_t src = ((size_t)blk * kBlock + s % kBlock) * P.row_bytes + (size_t)part * 16;
+          dst[q] = ((size_t)u * P.stage_rows + S.stage_i[k]) * P.row_bytes + (size_t)part * 16;
+          kv[q] = ld16(P.k_pool + src);
+          vv[q] = ld16(P.v_pool + src);
+          ok[q] = true;
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (ok[q]) {
+        st16(P.stage_k + dst[q], kv[q]);
+        st16(P.stage_v + dst[q], vv[q]);
+      }
+  }
+}
+
+// Every chunk of a head with victims arrives here with one 64-bit atomic
+// add: bits 0-10 count the chunks, 11-21 the chunks with errors, 22-42 the
+// rows moved and 43-63 the rows staged (each at most 2^20 per head).  The
+// chunk that arrives last has the totals in the returned value: it records
+// the head's error state, freed blocks and counts, and clears the word.
+__device__ void prep_finish(const CompactArgs &P, int u, int n, int m, int moved, int staged,
+                            PrepLds &S) {
+  __syncthreads();  // s_err is final
+  if (threadIdx.x != 0) return;
+  const unsigned long long mine = 1ull | ((unsigned long long)(S.s_err ? 1 : 0) << 11) |
+                                  ((unsigned long long)moved << 22) |
+                                  ((unsigned long long)staged << 43);
+  const unsigned long long old = atomicAdd(&P.head_acc[u], mine);
+  if ((old & 2047ull) != (unsigned long long)(P.chunks - 1)) return;
+  const unsigned long long tot = old + mine;
+  const int err = ((tot >> 11) & 2047ull) ? 1 : 0;
+  int32_t *hi = P.head_info + (size_t)u * 8;
+  hi[2] = err;
+  hi[3] = err ? 0 : blocks_of(n) - blocks_of(n - m);
+  hi[4] = (int)((tot >> 22) & 0x1fffffull);
+  hi[5] = (int)(tot >> 43);
+  atomicExch(&P.head_acc[u], 0ull);  // state for the next call
+}
+
+__device__ void prep_common_start(const CompactArgs &P, int u, int c) {
+  if (u == 0 && c == 0 && threadIdx.x == 0) {
     *P.fc0 = *P.free_count;
     for (int i = 0; i < 5; ++i) P.stats[i] = 0;
   }
+}
+}  // namespace
+
+// Prep from a caller's victim list.
+__global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArgs P) {
+  __shared__ PrepLds S;
+  __shared__ uint8_t flag[kChunk];
+  __shared__ int vr[kRange];
+
+  const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
+  prep_common_start(P, u, c);
   const int n = P.seq_len[u];
   const int m = P.n_victims[u];
-  if (c == 0 && tid == 0) P.head_info[u * 4 + 0] = n;
-  // n or m out of range: the gather sees it from seq_len / n_victims directly
-  if (n < 0 || n > P.max_slots || m < 0 || m > n || m == 0) return;
+  if (settle_trivial(P, u, c, n, m)) return;
+  if (c == 0 && tid == 0) {
+    P.head_info[(size_t)u * 8 + 0] = n;
+    P.head_info[(size_t)u * 8 + 1] = m;
+  }
   const int s0 = c * kChunk;
   const int32_t *vic = P.victims + (size_t)u * P.max_slots;
   const size_t urow = (size_t)u * P.max_slots;
   const int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
   if (tid == 0) {
-    s_err = 0;
-    s_nstage = 0;
+    S.s_err = 0;
+    S.s_nstage = 0;
   }
   for (int i = tid; i < kChunk; i += kThreads) flag[i] = 0;
 
@@ -113,6 +290,7 @@ __global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArg
   }
   const bool live_chunk = s0 < n;
   const int s1 = live_chunk ? min(s0 + kChunk, n) : s0;
+  int moved = 0, staged = 0;
   int posv[kPerThread];
   float scv[kPerThread];
 #pragma unroll
@@ -121,164 +299,138 @@ __global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArg
     posv[q] = (s < s1) ? P.pos[urow + s] : 0;
     scv[q] = (s < s1 && P.score) ? P.score[urow + s] : 0.f;
   }
-  for (int lb = s0 / kBlock + tid; lb < (s1 + kBlock - 1) / kBlock; lb += kThreads) {
-    const int blk = bt[lb];
+  if (tid < kChunk / kBlock) {
+    const int lb = s0 / kBlock + tid;
+    const int blk = lb < blocks_of(s1) ? bt[lb] : 0;
     if (blk < 0 || blk >= P.num_blocks) bad = 1;
+    S.blk_l[tid] = blk;
   }
-  const int S = (m + kThreads - 1) / kThreads;  // sample spacing
-  const int samp = (tid * S < m) ? vic[tid * S] : INT_MAX;
-  const int first = vic[0];
-  if (bad) atomicOr(&s_err, 1);
+  const int SP = (m + kThreads - 1) / kThreads;  // sample spacing
+  const int samp = (tid * SP < m) ? vic[tid * SP] : INT_MAX;
   const int c0 = __syncthreads_count(samp < s0);
+  if (bad) atomicOr(&S.s_err, 1);  // after a barrier: s_err is initialised
   const int c1 = __syncthreads_count(samp < s1);
-  if (!live_chunk) {
-    if (tid == 0 && s_err) atomicOr(&P.head_err[u], 1u);
-    return;
-  }
-  // victims before s0 lie in [lo0, hi0], victims before s1 in [lo1, hi1]
-  const int lo0 = c0 ? (c0 - 1) * S + 1 : 0, hi0 = min(c0 * S, m);
-  const int lo1 = c1 ? (c1 - 1) * S + 1 : 0, hi1 = min(c1 * S, m);
-  int j0, j1;
-  if (hi1 - lo0 <= kRange) {
-    // ---- one range load covers both brackets and every victim in the chunk
-    // (at most kRange entries: 16 per thread, all issued before any store)
-    {
-      const int len = hi1 - lo0;
-      int t[kRange / kThreads];
+  if (live_chunk) {
+    // victims before s0 lie in [lo0, hi0], victims before s1 in [lo1, hi1]
+    const int lo0 = c0 ? (c0 - 1) * SP + 1 : 0, hi0 = min(c0 * SP, m);
+    const int lo1 = c1 ? (c1 - 1) * SP + 1 : 0, hi1 = min(c1 * SP, m);
+    int j0, j1;
+    if (hi1 - lo0 <= kRange) {
+      // ---- one range load covers both brackets and every victim in the
+      // chunk (at most kRange entries: 16 per thread, all issued first)
+      {
+        const int len = hi1 - lo0;
+        int t[kRange / kThreads];
 #pragma unroll
-      for (int q = 0; q < kRange / kThreads; ++q) {
-        const int i = tid + q * kThreads;
-        t[q] = i < len ? vic[lo0 + i] : 0;
+        for (int q = 0; q < kRange / kThreads; ++q) {
+          const int i = tid + q * kThreads;
+          t[q] = i < len ? vic[lo0 + i] : 0;
+        }
+#pragma unroll
+        for (int q = 0; q < kRange / kThreads; ++q) {
+          const int i = tid + q * kThreads;
+          if (i < len) vr[i] = t[q];
+        }
       }
-#pragma unroll
-      for (int q = 0; q < kRange / kThreads; ++q) {
-        const int i = tid + q * kThreads;
-        if (i < len) vr[i] = t[q];
+      __syncthreads();
+      int cnt0 = 0, cnt1 = 0;
+      for (int i = tid; i < hi1 - lo0; i += kThreads) {
+        cnt0 += vr[i] < s0;
+        cnt1 += vr[i] < s1;
+      }
+      block_sum2(cnt0, cnt1, S);
+      j0 = lo0 + cnt0;
+      j1 = lo0 + cnt1;
+      for (int i = j0 - lo0 + tid; i < j1 - lo0; i += kThreads) {
+        const int v = vr[i];
+        if (v >= s0 && v < s1) flag[v - s0] = 1;
+      }
+    } else {
+      // long brackets (very sparse victims): count them, then mark
+      j0 = bracket_count(vic, lo0, hi0 - lo0, s0);
+      j1 = bracket_count(vic, lo1, hi1 - lo1, s1);
+      for (int j = j0 + tid; j < j1; j += kThreads) {
+        const int v = vic[j];
+        if (v >= s0 && v < s1) flag[v - s0] = 1;
       }
     }
     __syncthreads();
-    int cnt0 = 0, cnt1 = 0;
-    for (int i = tid; i < hi1 - lo0; i += kThreads) {
-      cnt0 += vr[i] < s0;
-      cnt1 += vr[i] < s1;
-    }
-    // block sums of the per-thread counts
-    {
-      int a0 = cnt0, a1 = cnt1;
+    bool vf[kPerThread];
 #pragma unroll
-      for (int o = kWave / 2; o >= 1; o >>= 1) {
-        a0 += __shfl_xor(a0, o);
-        a1 += __shfl_xor(a1, o);
-      }
-      if (lane_id() == 0) {
-        r0s[tid / kWave] = a0;
-        r1s[tid / kWave] = a1;
-      }
-      __syncthreads();
-      int t0 = 0, t1 = 0;
-      for (int w = 0; w < kThreads / kWave; ++w) {
-        t0 += r0s[w];
-        t1 += r1s[w];
-      }
-      j0 = lo0 + t0;
-      j1 = lo0 + t1;
+    for (int q = 0; q < kPerThread; ++q) {
+      const int s = s0 + tid * kPerThread + q;
+      vf[q] = s < s1 && flag[s - s0];
     }
-    for (int i = j0 - lo0 + tid; i < j1 - lo0; i += kThreads) {
-      const int v = vr[i];
-      if (v >= s0 && v < s1) flag[v - s0] = 1;
-    }
-  } else {
-    // long brackets (very sparse victims): count them, then mark
-    j0 = bracket_count(vic, lo0, hi0 - lo0, s0);
-    j1 = bracket_count(vic, lo1, hi1 - lo1, s1);
-    for (int j = j0 + tid; j < j1; j += kThreads) {
-      const int v = vic[j];
-      if (v >= s0 && v < s1) flag[v - s0] = 1;
-    }
+    rank_and_stage(P, u, s0, s1, n - m, m, j0, vf, posv, scv, nullptr, S, moved, staged);
   }
-  __syncthreads();
+  prep_finish(P, u, n, m, moved, staged, S);
+}
 
-  int kept = 0;
-#pragma unroll
-  for (int q = 0; q < kPerThread; ++q) {
-    const int s = s0 + tid * kPerThread + q;
-    kept += (s < s1 && !flag[s - s0]) ? 1 : 0;
+// Prep from the selection's threshold: slot s < nc is a victim iff its key
+// is below T, or equal to T with s <= cut; the chunk's first victim index
+// comes from the selection's per-chunk offsets.
+__global__ __launch_bounds__(kThreads) void evict_prep_kernel(const CompactArgs P) {
+  __shared__ PrepLds S;
+  const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
+  prep_common_start(P, u, c);
+  const int n = P.seq_len[u];
+  const int m = P.n_victims[u];
+  if (settle_trivial(P, u, c, n, m)) return;
+  if (c == 0 && tid == 0) {
+    P.head_info[(size_t)u * 8 + 0] = n;
+    P.head_info[(size_t)u * 8 + 1] = m;
   }
-  const int excl = block_exclusive_scan(kept, wave_tot);
-  const int n2 = n - m;
-  int r = (s0 - j0) + excl;  // kept slots before s0, plus those before mine in the chunk
-  int my_err = 0, my_moved = 0, my_staged = 0;
-#pragma unroll
-  for (int q = 0; q < kPerThread; ++q) {
-    const int s = s0 + tid * kPerThread + q;
-    if (s >= s1 || flag[s - s0]) continue;
-    if (r < 0 || r >= n2) { my_err = 1; ++r; continue; }
-    int src;
-    if (r == s) {
-      src = -1;                       // stays in place
-    } else if (s < n2) {              // at risk: staged before the gather
-      const int si = r - first;
-      if (si < 0 || si >= P.stage_rows) { my_err = 1; ++r; continue; }
-      src = -2 - si;
-      ++my_staged;
-      const int k = atomicAdd(&s_nstage, 1);
-      stage_s[k] = s;
-      stage_i[k] = si;
-    } else {                          // slots >= n' are never written: read in place
-      const int blk = bt[s / kBlock];
-      src = (blk >= 0 && blk < P.num_blocks) ? blk * kBlock + s % kBlock : 0;
-    }
-    my_moved += src != -1 ? 1 : 0;
-    P.src_of[urow + r] = src;
-    P.new_pos[urow + r] = posv[q];
-    if (P.score) P.new_score[urow + r] = scv[q];
-    ++r;
-  }
-  if (my_err) atomicOr(&s_err, 1);
-  // per-chunk counts for the stats (summed per head by the finalize step)
-  {
-#pragma unroll
-    for (int o = kWave / 2; o >= 1; o >>= 1) {
-      my_moved += __shfl_xor(my_moved, o);
-      my_staged += __shfl_xor(my_staged, o);
-    }
-    if (lane_id() == 0) {
-      r0s[tid / kWave] = my_moved;
-      r1s[tid / kWave] = my_staged;
-    }
-  }
-  __syncthreads();
   if (tid == 0) {
-    int a0 = 0, a1 = 0;
-    for (int w = 0; w < kThreads / kWave; ++w) {
-      a0 += r0s[w];
-      a1 += r1s[w];
+    S.s_err = 0;
+    S.s_nstage = 0;
+  }
+  const int s0 = c * kChunk;
+  const int nc = max(0, n - P.recent);
+  const size_t urow = (size_t)u * P.max_slots;
+  int moved = 0, staged = 0;
+  if (s0 < n) {
+    const int s1 = min(s0 + kChunk, n);
+    const uint32_t T = P.head_sel[u * 4 + 0];
+    const int cut = (int)P.head_sel[u * 4 + 1];
+    const int j0 = s0 < nc ? (int)P.chunk_off[(size_t)u * P.chunks + c] : m;
+    const int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
+    int posv[kPerThread];
+    float scv[kPerThread], sel[kPerThread];
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+      const int s = s0 + tid * kPerThread + q;
+      posv[q] = (s < s1) ? P.pos[urow + s] : 0;
+      scv[q] = (s < s1 && P.score) ? P.score[urow + s] : 0.f;
+      sel[q] = (s < s1 && s < nc) ? P.sel_score[urow + s] : 0.f;
     }
-    P.chunk_mv[((size_t)u * P.chunks + c) * 2 + 0] = a0;
-    P.chunk_mv[((size_t)u * P.chunks + c) * 2 + 1] = a1;
+    int bad = 0;
+    if (tid < kChunk / kBlock) {
+      const int lb = s0 / kBlock + tid;
+      const int blk = lb < blocks_of(s1) ? bt[lb] : 0;
+      if (blk < 0 || blk >= P.num_blocks) bad = 1;
+      S.blk_l[tid] = blk;
+    }
+    bool vf[kPerThread];
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+      const int s = s0 + tid * kPerThread + q;
+      const uint32_t k = score_key(sel[q]);
+      vf[q] = s < s1 && s < nc && (k < T || (k == T && s <= cut));
+    }
+    __syncthreads();  // block ids, s_err and s_nstage initialised
+    if (bad) atomicOr(&S.s_err, 1);
+    rank_and_stage(P, u, s0, s1, n - m, m, j0, vf, posv, scv, P.victims_out, S, moved, staged);
   }
-  // staging copy of the at-risk K and V rows (16-byte pieces)
-  const int pieces = P.row_bytes / 16;
-  const int ns = s_nstage;
-  for (int idx = tid; idx < ns * pieces; idx += kThreads) {
-    const int k = idx / pieces, part = idx % pieces;
-    const int s = stage_s[k];
-    const int blk = bt[s / kBlock];
-    if (blk < 0 || blk >= P.num_blocks) continue;  // flagged above
-    const size_t src = ((size_t)blk * kBlock + s % kBlock) * P.row_bytes + (size_t)part * 16;
-    const size_t dst = ((size_t)u * P.stage_rows + stage_i[k]) * P.row_bytes + (size_t)part * 16;
-    st16(P.stage_k + dst, ld16(P.k_pool + src));
-    st16(P.stage_v + dst, ld16(P.v_pool + src));
-  }
-  if (tid == 0 && s_err) atomicOr(&P.head_err[u], 1u);
+  prep_finish(P, u, n, m, moved, staged, S);
 }
 
 // Persistent grid over (head, rank range) items; every head has at least one
-// item, which records the head's error state and the blocks it frees.
+// item, and its first item settles the head (free list, table, seq_len, stats).
 __global__ __launch_bounds__(kThreads) void compact_gather_kernel(const CompactArgs P) {
   __shared__ int item_start[kMaxUnits + 1];
   __shared__ int wave_tot[kThreads / kWave];
   __shared__ int s_total;
+  __shared__ int s_red[2][kThreads / kWave];
   const int tid = threadIdx.x, lane = lane_id();
   const int U = P.units, RC = P.rows_per_item;
   int base_count = 0;
@@ -286,10 +438,9 @@ __global__ __launch_bounds__(kThreads) void compact_gather_kernel(const CompactA
     const int u = b0 + tid;
     int cnt = 0;
     if (u < U) {
-      const int n = P.seq_len[u];
-      const int m = P.n_victims[u];
-      const bool ok = n >= 0 && n <= P.max_slots && m > 0 && m <= n;
-      cnt = ok ? max(1, (n - m + RC - 1) / RC) : 1;
+      const int32_t *hi = P.head_info + (size_t)u * 8;
+      const int n = hi[0], m = hi[1], err = hi[2];
+      cnt = (!err && m > 0) ? max(1, (n - m + RC - 1) / RC) : 1;
     }
     const int ex = block_exclusive_scan(cnt, wave_tot);
     if (u < U) item_start[u] = base_count + ex;
@@ -298,25 +449,77 @@ __global__ __launch_bounds__(kThreads) void compact_gather_kernel(const CompactA
     base_count = s_total;
     __syncthreads();
   }
-  const int total = base_count;
+  const int total_items = base_count;
   const int pieces = P.row_bytes / 16;  // 16-byte pieces per row (8, 16 or 32)
 
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    int lo = 0, hi = U - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (item_start[mid] <= item) lo = mid; else hi = mid - 1;
+  for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
+    int lo = 0, hi_u = U - 1;
+    while (lo < hi_u) {
+      const int mid = (lo + hi_u + 1) >> 1;
+      if (item_start[mid] <= item) lo = mid; else hi_u = mid - 1;
     }
     const int u = lo, k = item - item_start[u];
-    const int n = P.seq_len[u];
-    const int m = P.n_victims[u];
-    const uint32_t herr = P.head_err[u];
-    int ev = (int)herr;
-    if (n < 0 || n > P.max_slots) ev = 2;
-    else if (m < 0 || m > n) ev = 1;
-    if (k == 0 && tid == 0) {
-      P.head_info[u * 4 + 2] = ev;
-      P.head_info[u * 4 + 3] = (ev || m <= 0) ? 0 : (n + kBlock - 1) / kBlock - (n - m + kBlock - 1) / kBlock;
+    const int32_t *hi = P.head_info + (size_t)u * 8;
+    const int n = hi[0], m = hi[1], ev = hi[2];
+    if (k == 0) {
+      // ---- settle the head: its place in the free list is the sum of the
+      // blocks freed by the heads before it
+      // (freed blocks recomputed from n, m and the error word: in range for
+      // any workspace contents)
+      int before = 0, total = 0;
+      for (int v = tid; v < U; v += kThreads) {
+        const int32_t *hv = P.head_info + (size_t)v * 8;
+        const int f = head_freed(P, hv[0], hv[1], hv[2]);
+        total += f;
+        if (v < u) before += f;
+      }
+#pragma unroll
+      for (int o = kWave / 2; o >= 1; o >>= 1) {
+        before += __shfl_xor(before, o);
+        total += __shfl_xor(total, o);
+      }
+      if (lane == 0) {
+        s_red[0][tid / kWave] = before;
+        s_red[1][tid / kWave] = total;
+      }
+      __syncthreads();
+      before = 0;
+      total = 0;
+      for (int w = 0; w < kThreads / kWave; ++w) {
+        before += s_red[0][w];
+        total += s_red[1][w];
+      }
+      __syncthreads();
+      const int fc0 = *P.fc0;
+      const bool room = fc0 >= 0 && (long long)fc0 + total <= (long long)P.free_capacity;
+      const int freed = room ? head_freed(P, n, m, ev) : 0;
+      if (tid == 0) {
+        unsigned long long *st = reinterpret_cast<unsigned long long *>(P.stats);
+        if (ev) {
+          atomicOr(&st[4], (unsigned long long)ev);
+        } else if (m > 0) {
+          P.seq_len[u] = n - m;
+          const long long mv = hi[4], sg = hi[5];
+          if (mv) {
+            atomicAdd(&st[1], (unsigned long long)mv);
+            atomicAdd(&st[2], (unsigned long long)mv * 4ull * (unsigned long long)P.row_bytes);
+          }
+          if (sg) atomicAdd(&st[3], (unsigned long long)sg);
+        }
+        if (freed) atomicAdd(&st[0], (unsigned long long)freed);
+        if (u == U - 1) {
+          if (room) *P.free_count = fc0 + total;
+          else atomicOr(&st[4], 4ull);
+        }
+      }
+      if (freed) {
+        const int lb0 = blocks_of(n - m);
+        int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
+        for (int i = tid; i < freed; i += kThreads) {
+          P.free_list[fc0 + before + i] = bt[lb0 + i];
+          bt[lb0 + i] = -1;
+        }
+      }
     }
     if (ev || m <= 0) continue;
     const int n2 = n - m;
@@ -340,8 +543,12 @@ __global__ __launch_bounds__(kThreads) void compact_gather_kernel(const CompactA
       nsc[i] = (in && part == 0 && P.score) ? P.new_score[urow + rr[i]] : 0.f;
     }
     uint4 kv[4], vv[4];
+    const int pool_rows = P.num_blocks * kBlock;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      // a source outside the pool or the staging rows is skipped (cannot
+      // happen with a workspace these kernels wrote)
+      if (srcv[i] >= pool_rows || (srcv[i] < -1 && -2 - srcv[i] >= P.stage_rows)) srcv[i] = -1;
       const int src = srcv[i];
       if (src != -1) {
         const uint8_t *ks, *vs;
@@ -371,98 +578,27 @@ __global__ __launch_bounds__(kThreads) void compact_gather_kernel(const CompactA
   }
 }
 
-// Workgroup (k, u): logical blocks [ceil(n'/16) + 256k, ...) of head u.
-__global__ __launch_bounds__(kThreads) void compact_finalize_kernel(const CompactArgs P) {
-  __shared__ long long s_before, s_total, s_mv, s_st;
-  const int k = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
-  if (tid == 0) {
-    s_before = 0;
-    s_total = 0;
-    s_mv = 0;
-    s_st = 0;
-  }
-  __syncthreads();
-  long long before = 0, total = 0;
-  for (int v = tid; v < P.units; v += kThreads) {
-    const long long f = P.head_info[v * 4 + 3];
-    total += f;
-    if (v < u) before += f;
-  }
-  if (before) atomicAdd(reinterpret_cast<unsigned long long *>(&s_before), (unsigned long long)before);
-  if (total) atomicAdd(reinterpret_cast<unsigned long long *>(&s_total), (unsigned long long)total);
-  __syncthreads();
-  const int fc0 = *P.fc0;
-  const bool room = fc0 >= 0 && (long long)fc0 + s_total <= (long long)P.free_capacity;
-  const int n = P.head_info[u * 4 + 0];
-  const int err = P.head_info[u * 4 + 2];
-  const int freed = room ? P.head_info[u * 4 + 3] : 0;
-  // rows moved and staged of this head: the prep chunks' counts, summed in parallel
-  long long mv = 0, st = 0;
-  if (k == 0 && !err && n > 0 && n <= P.max_slots) {
-    const int live = (n + kChunk - 1) / kChunk;  // chunks prep wrote
-    for (int c = tid; c < live; c += kThreads) {
-      mv += P.chunk_mv[((size_t)u * P.chunks + c) * 2 + 0];
-      st += P.chunk_mv[((size_t)u * P.chunks + c) * 2 + 1];
-    }
-#pragma unroll
-    for (int o = kWave / 2; o >= 1; o >>= 1) {
-      mv += __shfl_xor(mv, o);
-      st += __shfl_xor(st, o);
-    }
-    if (lane_id() == 0 && (mv || st)) {
-      atomicAdd(reinterpret_cast<unsigned long long *>(&s_mv), (unsigned long long)mv);
-      atomicAdd(reinterpret_cast<unsigned long long *>(&s_st), (unsigned long long)st);
-    }
-  }
-  __syncthreads();
-  if (k == 0 && tid == 0) {
-    P.head_err[u] = 0u;  // state for the next call
-    if (err) {
-      atomicOr(reinterpret_cast<unsigned long long *>(&P.stats[4]), (unsigned long long)err);
-    } else {
-      const int m = P.n_victims[u];
-      if (m > 0) {
-        P.seq_len[u] = n - m;
-        const long long mv = s_mv, st = s_st;
-        if (mv) {
-          atomicAdd(reinterpret_cast<unsigned long long *>(&P.stats[1]), (unsigned long long)mv);
-          atomicAdd(reinterpret_cast<unsigned long long *>(&P.stats[2]),
-                    (unsigned long long)mv * 4ull * (unsigned long long)P.row_bytes);
-        }
-        if (st) atomicAdd(reinterpret_cast<unsigned long long *>(&P.stats[3]), (unsigned long long)st);
-      }
-      if (freed) atomicAdd(reinterpret_cast<unsigned long long *>(&P.stats[0]), (unsigned long long)freed);
-    }
-    if (u == P.units - 1) {
-      if (room) *P.free_count = fc0 + (int)s_total;
-      else atomicOr(reinterpret_cast<unsigned long long *>(&P.stats[4]), 4ull);
-    }
-  }
-  if (err || freed == 0) return;
-  const int n2 = n - P.n_victims[u];
-  const int lb0 = (n2 + kBlock - 1) / kBlock;
-  int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
-  const int i = k * kFinBlocks + tid;
-  if (i < freed) {
-    P.free_list[fc0 + s_before + i] = bt[lb0 + i];
-    bt[lb0 + i] = -1;
-  }
+static hipError_t launch_gather(const CompactArgs &a, hipStream_t s) {
+  // enough workgroups to cover every item of a full cache, capped
+  const long long items =
+      (long long)a.units * ((a.max_slots + a.rows_per_item - 1) / a.rows_per_item);
+  const int grid = (int)(items < 2048 ? (items > 0 ? items : 1) : 2048);
+  hipLaunchKernelGGL(compact_gather_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_compact(const CompactArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(compact_prep_kernel, dim3(a.chunks, a.units), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // enough workgroups to cover every item of a full cache, capped
-  const long long items =
-      (long long)a.units * ((a.max_slots + a.rows_per_item - 1) / a.rows_per_item);
-  const int grid = (int)(items < 2048 ? (items > 0 ? items : 1) : 2048);
-  hipLaunchKernelGGL(compact_gather_kernel, dim3(grid), dim3(kThreads), 0, s, a);
-  e = hipGetLastError();
+  return launch_gather(a, s);
+}
+
+hipError_t launch_evict_compact(const CompactArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(evict_prep_kernel, dim3(a.chunks, a.units), dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int fin_x = (a.max_blocks + kFinBlocks - 1) / kFinBlocks;
-  hipLaunchKernelGGL(compact_finalize_kernel, dim3(fin_x, a.units), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  return launch_gather(a, s);
 }
 
 }  // namespace kvev

@@ -8,6 +8,16 @@
 
 namespace kvev {
 
+// Per-head selection state and outputs, shared by the select kernels and the
+// fused score path (kvev_select_head.h).
+struct SelHead {
+  int32_t *n_victims;
+  uint32_t *hist;         // state [units][2048]: top 11 key bits (zero between calls)
+  uint32_t *head_sel;     // scratch [units][4]: threshold key T, cut slot
+  uint32_t *chunk_off;    // scratch [units][chunks]: first victim index of each chunk
+  int32_t budget, recent, chunks;  // chunks: 1024-slot chunks per head
+};
+
 struct ScoreArgs {
   const uint8_t *k_pool, *v_pool;
   const int32_t *block_table, *seq_len, *pos;
@@ -19,28 +29,33 @@ struct ScoreArgs {
   int32_t rows, row_tiles;       // G*W and ceil(rows / 16)
   int32_t flags, pool_r, halo_blocks, tile_blocks, tiles_per_head, threads;
   float c1;                      // scale * log2(e)
+  // fused selection (sel.hist != nullptr): the score kind sel_kind (1 sum,
+  // 2 pooled, 4 drop) is histogrammed into sel.hist as it is written
+  SelHead sel;
+  int32_t sel_kind;
 };
 
 struct SelectArgs {
   const float *score;
   const int32_t *seq_len;
-  int32_t *victims, *n_victims;
-  // workspace: persistent state (zero between calls)
-  uint32_t *hist;         // [units][2048] histogram of the top 11 key bits
-  // workspace: scratch
-  uint2 *cand;            // [units][subs][256] (key, slot) of the threshold bucket
-  uint32_t *ccount;       // [units][subs] candidates of each 256-slot sub-chunk
-  int32_t *cnt_lt;        // [units][subs] keys below the threshold bucket
-  uint32_t *chunk_off;    // [units][chunks] output offset of each 1024-slot chunk
-  uint32_t *head_sel;     // [units][4] threshold key, tie-cut slot
-  int32_t units, max_slots, budget, recent, chunks;
+  int32_t *victims;
+  SelHead sel;
+  int32_t units, max_slots;
 };
+
+// The per-head threshold step alone (the fused path: the histogram comes
+// from the score kernel).
+hipError_t launch_select_head(const SelectArgs &a, hipStream_t s);
 
 struct CompactArgs {
   uint8_t *k_pool, *v_pool;
   int32_t *block_table, *seq_len, *pos;
   float *score;                 // optional score row moved with the tokens
   const int32_t *victims, *n_victims;
+  int32_t *victims_out;         // fused path: victims written by the prep step
+  const uint32_t *head_sel, *chunk_off;  // fused path: threshold and chunk offsets
+  const float *sel_score;       // fused path: the score row the threshold applies to
+  int32_t recent;               // fused path: protected recent window
   int32_t *free_list, *free_count;
   int64_t *stats;
   // workspace regions
@@ -48,9 +63,9 @@ struct CompactArgs {
   int32_t *new_pos;             // [units][max_slots]: pos of each kept rank
   float *new_score;             // [units][max_slots]: score of each kept rank
   uint8_t *stage_k, *stage_v;   // [units][stage_rows][row_bytes]: at-risk rows
-  int32_t *head_info;           // [units][4]: n before the call, -, error, blocks freed
-  uint32_t *head_err;           // [units] persistent state (zero between calls)
-  int32_t *chunk_mv;            // [units][chunks][2]: rows moved, rows staged
+  int32_t *head_info;           // [units][8]: n, m, error, blocks freed, rows moved, staged
+  unsigned long long *head_acc; // [units] persistent state (zero between calls): prep
+                                // chunks done, chunks with errors, rows moved, staged
   int32_t *fc0;                 // free_count before the call
   int32_t units, max_blocks, max_slots, num_blocks, row_bytes, stage_rows, chunks,
       free_capacity, rows_per_item;
@@ -71,16 +86,19 @@ struct WindowAttnArgs {
 hipError_t launch_score(const ScoreArgs &a, int bf16, int head_dim, int drop, hipStream_t s);
 hipError_t launch_select(const SelectArgs &a, hipStream_t s);
 hipError_t launch_compact(const CompactArgs &a, hipStream_t s);
+hipError_t launch_evict_compact(const CompactArgs &a, hipStream_t s);
 hipError_t launch_window_attn(const WindowAttnArgs &a, int bf16, int head_dim, hipStream_t s);
 
-// LDS bytes of one score workgroup (0 when the row count does not fit).
-constexpr int kSelectChunk = 1024;      // select.hip chunk (slots)
-constexpr int kSelectBins = 2048;       // select.hip histogram bins
-constexpr int kSelectMaxChunks = 1024;  // select.hip refine step limit
+constexpr int kSelectChunk = 1024;      // victim offsets are kept per chunk of slots
+constexpr int kSelectBins = 2048;       // histogram bins (top 11 key bits)
+constexpr int kSelectMaxChunks = 1024;  // chunks per head: up to 1M slots
+constexpr int kHistChunk = 4096;        // slots per select histogram workgroup
 constexpr int kCompactMaxUnits = 4096;  // compact.hip gather limit
 constexpr int kCompactChunk = 1024;     // compact.hip prep chunk (slots)
 
-size_t score_lds_bytes(int bf16, int head_dim, int drop, int row_tiles, int tile_blocks,
-                       int halo_blocks);
+// LDS bytes of one score workgroup (fused: room for the tile histogram and
+// the head selection).
+__host__ __device__ size_t score_lds_bytes(int bf16, int head_dim, int drop, int row_tiles,
+                                            int tile_blocks, int halo_blocks, int fused);
 
 }  // namespace kvev

@@ -1,7 +1,7 @@
 // score.hip -- per-token eviction scores of a paged KV cache (gfx950).
 //
-// One workgroup (4 waves) scores a tile of consecutive 16-token blocks of one
-// KV head (b, h).  The G*W observation-window query rows of the head's GQA
+// One workgroup (4 or 8 waves) scores a tile of consecutive 16-token
+// blocks of one KV head (b, h).  The G*W observation-window query rows of the head's GQA
 // group are staged once in LDS in MFMA fragment order; each wave streams its
 // own key blocks straight from HBM into registers (16-byte loads, the four
 // lane groups of a key row reading 64 contiguous bytes each) and computes
@@ -17,6 +17,11 @@
 // scores ceil(r/16) halo blocks on either side, so the pool is finished in
 // LDS without any exchange between workgroups ([SNAP] "How it works").
 // No float atomics: results are bitwise reproducible.
+//
+// Fused with selection (kvev_evict), the tile also adds the top 11 key bits
+// of the score kind that drives eviction, over its candidate slots, into the
+// head's selection histogram (integer atomics), so no separate pass re-reads
+// the scores to build it.
 #include <hip/hip_runtime.h>
 
 #include "kvev_device.h"
@@ -45,7 +50,7 @@ __device__ __forceinline__ int remap_xcd(int id, int n) {
 
 }  // namespace
 
-template <bool BF16, int D, bool DROP, int kThreads>
+template <bool BF16, int D, bool DROP, int kThreads, bool FUSED>
 __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
   constexpr int kWaves = kThreads / kWave;
   using G_ = Geo<BF16, D>;
@@ -63,6 +68,10 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
   float *S_lds = an2 + (DROP ? RT * 16 : 0);
   const int span_blocks = P.tile_blocks + 2 * P.halo_blocks;
   float *D_lds = S_lds + span_blocks * 16;
+  // fused selection: the tile's histogram after the score layout
+  uint32_t *hl = reinterpret_cast<uint32_t *>(
+      smem + ((score_lds_bytes(BF16, D, DROP, RT, P.tile_blocks, P.halo_blocks, 0) + 15) & ~size_t(15)));
+  constexpr bool fused = FUSED;
 
   const int wg = remap_xcd(blockIdx.x, gridDim.x);
   const int u = wg / P.tiles_per_head;
@@ -75,6 +84,10 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
   const int nb = (n + kBlock - 1) / kBlock;
   const int tb0 = tile * P.tile_blocks;
   if (tb0 >= nb) return;
+  const int sel_m = fused ? max(0, n - P.sel.budget) : 0;  // victims of the head
+  const int sel_nc = max(0, n - P.sel.recent);             // candidate slots
+  if (sel_m > 0)
+    for (int i = threadIdx.x; i < kSelectBins; i += kThreads) hl[i] = 0;
   const int tb1 = min(tb0 + P.tile_blocks, nb);
   const int cb0 = max(0, tb0 - P.halo_blocks), cb1 = min(nb, tb1 + P.halo_blocks);
 
@@ -290,35 +303,51 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
   const size_t orow = (size_t)u * max_slots;
   for (int s = s0 + threadIdx.x; s < s1; s += kThreads) {
     const float S = S_lds[s - base];
+    float selv = 0.f;
     if (P.flags & 1) {  // SUM (with ACCUMULATE: add to the stored score)
       float v = S;
       if (P.flags & 8) v = P.sum[orow + s] + S;
       P.sum[orow + s] = v;
+      selv = v;
     }
     if (P.flags & 2) {  // POOL: clamped max over [s - r, s + r]
       const int lo = max(0, s - P.pool_r), hi = min(n - 1, s + P.pool_r);
       float m = S_lds[lo - base];
       for (int i = lo + 1; i <= hi; ++i) m = fmaxf(m, S_lds[i - base]);
       P.pooled[orow + s] = m;
+      if (P.sel_kind == 2) selv = m;
     }
-    if constexpr (DROP) P.drop[orow + s] = D_lds[s - base];
+    if constexpr (DROP) {
+      P.drop[orow + s] = D_lds[s - base];
+      if (P.sel_kind == 4) selv = D_lds[s - base];
+    }
+    if (sel_m > 0 && s < sel_nc) atomicAdd(&hl[score_key(selv) >> 21], 1u);
   }
+  if (sel_m == 0) return;
+
+  // ---- fused selection: add the tile histogram to the head's
+  __syncthreads();
+  uint32_t *hg = P.sel.hist + (size_t)u * kSelectBins;
+  for (int i = threadIdx.x; i < kSelectBins; i += kThreads)
+    if (hl[i]) atomicAdd(&hg[i], hl[i]);
 }
 
-size_t score_lds_bytes(int bf16, int head_dim, int drop, int row_tiles, int tile_blocks,
-                       int halo_blocks) {
+__host__ __device__ size_t score_lds_bytes(int bf16, int head_dim, int drop, int row_tiles,
+                                            int tile_blocks, int halo_blocks, int fused) {
   const size_t rowb = (size_t)head_dim * (bf16 ? 2 : 4);
   const size_t frag = (size_t)row_tiles * 16 * rowb;  // bytes of one staged row set
   size_t bytes = frag * (drop ? 2 : 1);
   bytes += (size_t)row_tiles * 16 * 4 * (drop ? 3 : 2);
   bytes += (size_t)(tile_blocks + 2 * halo_blocks) * 16 * 4 * (drop ? 2 : 1);
+  if (fused) bytes = ((bytes + 15) & ~size_t(15)) + kSelectBins * 4;  // tile histogram
   return bytes;
 }
 
-template <bool BF16, int D, bool DROP, int T>
+template <bool BF16, int D, bool DROP, int T, bool FUSED>
 static hipError_t launch_t(const ScoreArgs &a, hipStream_t s) {
-  const size_t lds = score_lds_bytes(BF16, D, DROP, a.row_tiles, a.tile_blocks, a.halo_blocks);
-  auto fn = score_kernel<BF16, D, DROP, T>;
+  const size_t lds = score_lds_bytes(BF16, D, DROP, a.row_tiles, a.tile_blocks, a.halo_blocks,
+                                     FUSED);
+  auto fn = score_kernel<BF16, D, DROP, T, FUSED>;
   static size_t lds_set = 0;  // largest dynamic LDS size enabled for this variant
   if (lds > 65536 && lds > lds_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
@@ -333,9 +362,10 @@ static hipError_t launch_t(const ScoreArgs &a, hipStream_t s) {
 
 template <bool BF16, int D, bool DROP>
 static hipError_t launch_threads(const ScoreArgs &a, hipStream_t s) {
-  if (a.threads == 1024) return launch_t<BF16, D, DROP, 1024>(a, s);
-  if (a.threads == 512) return launch_t<BF16, D, DROP, 512>(a, s);
-  return launch_t<BF16, D, DROP, 256>(a, s);
+  const bool fused = a.sel.hist != nullptr;
+  if (a.threads == 512)
+    return fused ? launch_t<BF16, D, DROP, 512, true>(a, s) : launch_t<BF16, D, DROP, 512, false>(a, s);
+  return fused ? launch_t<BF16, D, DROP, 256, true>(a, s) : launch_t<BF16, D, DROP, 256, false>(a, s);
 }
 
 hipError_t launch_score(const ScoreArgs &a, int bf16, int head_dim, int drop, hipStream_t s) {

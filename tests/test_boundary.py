@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
     assert set(names) == set(K.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvev_abi_version() == 1
+    assert L.kvev_abi_version() == K.ABI_VERSION == 2
     for code in (0, -1, -2, -3, -4):
         assert K.strerror(code)
 
@@ -56,6 +56,17 @@ def score(c, w, flags=K.SUM, pool=1, s=FAKE, p=FAKE, d=FAKE):
                                        None, 0, None)
 
 
+def evict(c, w, flags=K.POOL, pool=3, budget=8, recent=2, ptrs=None, cap=1 << 20,
+          ws=FAKE, ws_bytes=1 << 40):
+    p = dict(score=FAKE, victims=FAKE, n_victims=FAKE, free_list=FAKE, free_count=FAKE,
+             stats=FAKE)
+    p.update(ptrs or {})
+    return K.load_library().kvev_evict(
+        ctypes.byref(c) if c else None, ctypes.byref(w) if w else None, flags, pool, budget,
+        recent, p["score"], p["victims"], p["n_victims"], p["free_list"], p["free_count"], cap,
+        p["stats"], ws, ws_bytes, None)
+
+
 BAD_CACHES = [dict(head_dim=96), dict(head_dim=256), dict(block_size=32), dict(batch=0),
               dict(kv_heads=0), dict(max_blocks=0), dict(num_blocks=0), dict(dtype=7),
               dict(k_pool=None), dict(v_pool=None), dict(block_table=None), dict(seq_len=None),
@@ -72,6 +83,7 @@ def test_bad_cache_refused_everywhere(kw):
                           1 << 40, None) == K.EINVAL
     assert L.kvev_window_attn(ctypes.byref(c), ctypes.byref(window()), FAKE, None, FAKE,
                               1 << 40, None) == K.EINVAL
+    assert evict(c, window()) == K.EINVAL
     assert L.kvev_workspace_bytes(ctypes.byref(c), 1, 1) == 0
 
 
@@ -175,3 +187,35 @@ def test_binding_has_no_cpu_path():
                 torch.zeros(1, 1, 64, dtype=torch.int32))
     with pytest.raises(ValueError):
         c.struct()
+
+
+@pytest.mark.parametrize("flags", [0, K.SUM | K.POOL, K.POOL | K.DROP, K.SUM | K.DROP,
+                                   K.ACCUMULATE, K.POOL | K.ACCUMULATE, 16])
+def test_evict_needs_one_score_kind(flags):
+    assert evict(cache(), window(), flags=flags) == K.EINVAL
+
+
+@pytest.mark.parametrize("budget,recent", [(0, 0), (-1, 0), (8, 8), (8, 9), (8, -1)])
+def test_evict_budget_refusals(budget, recent):
+    assert evict(cache(), window(), budget=budget, recent=recent) == K.EINVAL
+
+
+@pytest.mark.parametrize("name", ["score", "victims", "n_victims", "free_list", "free_count",
+                                  "stats"])
+def test_evict_null_pointers(name):
+    assert evict(cache(), window(), ptrs={name: None}) == K.EINVAL
+
+
+def test_evict_refusals_of_the_parts():
+    L = K.load_library()
+    c = cache()
+    ws = L.kvev_workspace_bytes(ctypes.byref(c), 1, 1)
+    assert evict(None, window()) == K.EINVAL
+    assert evict(c, None) == K.EINVAL
+    assert evict(c, window(obs_window=0)) == K.EINVAL        # SnapKV: zero window refused
+    assert evict(c, window(), pool=4) == K.EINVAL            # SnapKV: even pool kernel refused
+    assert evict(c, window(a=None), flags=K.DROP) == K.EINVAL
+    assert evict(c, window(), cap=31) == K.ENOSPACE          # free list smaller than the pool
+    assert evict(c, window(), ws=None, ws_bytes=ws) == K.ENOSPACE
+    assert evict(c, window(), ws_bytes=ws - 1) == K.ENOSPACE
+    assert evict(c, window(group=8, obs_window=64), flags=K.DROP, pool=1) == K.EUNSUPPORTED
