@@ -142,10 +142,10 @@ int kvev_score(const kvev_cache *cache, const kvev_window *win, int32_t flags,
  * equal scores evict the lower position ([SNAP] "Tie-breaking"), -0 equals +0
  * and NaN ranks above +inf.  victims[b][h][0..m) receives their slot indices
  * in ascending order, n_victims[b][h] = m.  score: fp32 [batch][kv_heads]
- * [max_blocks*16] (for example `pooled` of kvev_score); victims: int32 with
+ * [max_blocks*16], 16-byte aligned (for example `pooled` of kvev_score); victims: int32 with
  * the same shape; n_victims: int32 [batch][kv_heads].  Bit-exact: the result
  * depends only on the score bits.
- * Errors (KVEV_EINVAL): NULL pointers; budget <= 0; recent_window < 0 or
+ * Errors (KVEV_EINVAL): NULL pointers; a score pointer not 16-byte aligned; budget <= 0; recent_window < 0 or
  * recent_window >= budget ([SNAP] Parameters); KVEV_ENOSPACE for a missing or
  * short workspace; KVEV_EUNSUPPORTED above 1M slots per head.
  */
@@ -193,7 +193,7 @@ int kvev_compact(const kvev_cache *cache, const int32_t *victims, const int32_t 
  * and the compaction's first step marks the victims against it, so the
  * scores are not re-read to select them.
  * flags: exactly one of KVEV_SUM, KVEV_POOL, KVEV_DROP (KVEV_ACCUMULATE with
- * KVEV_SUM); score: fp32 [batch][kv_heads][max_blocks*16] receives that kind
+ * KVEV_SUM); score: fp32 [batch][kv_heads][max_blocks*16], 16-byte aligned, receives that kind
  * (with ACCUMULATE it holds the running sums on entry) and is compacted with
  * the tokens, so after the call its slots [0, n') hold the kept tokens'
  * scores.  victims, n_victims, free_list, free_count, stats: as written by

@@ -63,8 +63,8 @@ StateLayout state_layout(const kvev_cache *c) {
 }
 
 struct SelectLayout {
-  size_t chunk_off, head_sel, total;
-  int chunks;
+  size_t chunk_off, chunk_below, head_sel, cand, ccount, total;
+  int chunks, nwg;
 };
 
 SelectLayout select_layout(const kvev_cache *c) {
@@ -72,9 +72,13 @@ SelectLayout select_layout(const kvev_cache *c) {
   const size_t units = (size_t)c->batch * c->kv_heads;
   const size_t max_slots = (size_t)c->max_blocks * KVEV_BLOCK_SIZE;
   L.chunks = (int)((max_slots + kvev::kSelectChunk - 1) / kvev::kSelectChunk);
+  L.nwg = (int)((max_slots + kvev::kHistChunk - 1) / kvev::kHistChunk);
   size_t off = state_layout(c).total;
   L.chunk_off = off; off = a256(off + units * (size_t)L.chunks * 4);
+  L.chunk_below = off; off = a256(off + units * (size_t)L.chunks * 4);
   L.head_sel = off; off = a256(off + units * 16);
+  L.cand = off; off = a256(off + units * (size_t)L.nwg * kvev::kHistChunk * 8);
+  L.ccount = off; off = a256(off + units * (size_t)L.nwg * 4);
   L.total = off;
   return L;
 }
@@ -277,9 +281,13 @@ kvev::SelHead sel_head(const kvev_cache *cache, int32_t *n_victims, int32_t budg
   h.hist = reinterpret_cast<uint32_t *>(ws + S.hist);
   h.head_sel = reinterpret_cast<uint32_t *>(ws + L.head_sel);
   h.chunk_off = reinterpret_cast<uint32_t *>(ws + L.chunk_off);
+  h.chunk_below = reinterpret_cast<uint32_t *>(ws + L.chunk_below);
+  h.cand = reinterpret_cast<uint2 *>(ws + L.cand);
+  h.ccount = reinterpret_cast<uint32_t *>(ws + L.ccount);
   h.budget = budget;
   h.recent = recent_window;
   h.chunks = L.chunks;
+  h.nwg = L.nwg;
   return h;
 }
 
@@ -303,6 +311,7 @@ int kvev_select(const kvev_cache *cache, const float *score, int32_t budget,
                 int32_t recent_window, int32_t *victims, int32_t *n_victims, void *workspace,
                 size_t ws_bytes, void *stream) {
   if (!valid_cache(cache) || !score || !victims || !n_victims) return KVEV_EINVAL;
+  if (reinterpret_cast<uintptr_t>(score) & 15) return KVEV_EINVAL;
   if (budget <= 0 || recent_window < 0 || recent_window >= budget) return KVEV_EINVAL;
   const SelectLayout L = select_layout(cache);
   if (L.chunks > kvev::kSelectMaxChunks) return KVEV_EUNSUPPORTED;
@@ -344,6 +353,7 @@ int kvev_evict(const kvev_cache *cache, const kvev_window *win, int32_t flags,
   if (!valid_cache(cache) || !score || !victims || !n_victims || !free_list || !free_count ||
       !stats)
     return KVEV_EINVAL;
+  if (reinterpret_cast<uintptr_t>(score) & 15) return KVEV_EINVAL;
   const int kind = flags & (KVEV_SUM | KVEV_POOL | KVEV_DROP);
   if (kind != KVEV_SUM && kind != KVEV_POOL && kind != KVEV_DROP) return KVEV_EINVAL;
   if (budget <= 0 || recent_window < 0 || recent_window >= budget) return KVEV_EINVAL;
@@ -380,7 +390,7 @@ int kvev_evict(const kvev_cache *cache, const kvev_window *win, int32_t flags,
   rc = map_err(kvev::launch_score(a, cache->dtype == KVEV_BF16, cache->head_dim,
                                   kind == KVEV_DROP, st));
   if (rc) return rc;
-  rc = map_err(kvev::launch_select_head(sa, st));
+  rc = map_err(kvev::launch_select_threshold(sa, st));
   if (rc) return rc;
   return map_err(kvev::launch_evict_compact(c, st));
 }

@@ -13,9 +13,12 @@ namespace kvev {
 struct SelHead {
   int32_t *n_victims;
   uint32_t *hist;         // state [units][2048]: top 11 key bits (zero between calls)
-  uint32_t *head_sel;     // scratch [units][4]: threshold key T, cut slot
+  uint32_t *head_sel;     // scratch [units][4]: T, cut slot, bucket, keys below the bucket
   uint32_t *chunk_off;    // scratch [units][chunks]: first victim index of each chunk
-  int32_t budget, recent, chunks;  // chunks: 1024-slot chunks per head
+  uint32_t *chunk_below;  // scratch [units][chunks]: keys below the bucket per chunk
+  uint2 *cand;            // scratch [units][nwg][4096]: (key, slot) pairs of the bucket
+  uint32_t *ccount;       // scratch [units][nwg]: pairs in each collect region
+  int32_t budget, recent, chunks, nwg;  // chunks: 1024-slot chunks; nwg: 4096-slot regions
 };
 
 struct ScoreArgs {
@@ -43,9 +46,9 @@ struct SelectArgs {
   int32_t units, max_slots;
 };
 
-// The per-head threshold step alone (the fused path: the histogram comes
-// from the score kernel).
-hipError_t launch_select_head(const SelectArgs &a, hipStream_t s);
+// The threshold steps after the histogram (collect, refine); the fused
+// path runs them after the score kernel built the histogram.
+hipError_t launch_select_threshold(const SelectArgs &a, hipStream_t s);
 
 struct CompactArgs {
   uint8_t *k_pool, *v_pool;

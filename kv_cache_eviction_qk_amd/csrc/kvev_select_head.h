@@ -1,21 +1,23 @@
-// kvev_select_head.h -- exact victim threshold of one KV head, computed by a
-// single workgroup once the head's 2048-bin histogram of the top 11 key bits
-// is complete (a kernel boundary after the histogram's last atomic).
+// kvev_select_head.h -- exact victim threshold of each KV head from its
+// complete 2048-bin histogram of the top 11 key bits (device code of
+// select.hip; the fused path runs the same two kernels).
 //
 // Victims are the m smallest (key, slot) pairs among the candidate slots
 // [0, nc): ties on the score evict the lower position first ([SNAP]
 // "Tie-breaking").  Writing T for the key of the m-th pair and cut for its
 // slot, slot s < nc is a victim iff key < T, or key == T and s <= cut.
-//   1. bucket b of rank m from the histogram;
-//   2. one pass over the keys: per 1024-slot chunk the count of keys below
-//      bucket b, and the (key, slot) pairs of bucket b into LDS;
-//   3. two radix passes over those pairs (key bits 20..10, then 9..0) give T
-//      and the rank of the m-th pair among the keys equal to T;
-//   4. the cut slot: rank counting among the keys equal to T;
-//   5. per-chunk victim counts, their exclusive scan (the chunk's first
-//      output index), T and cut to the workspace, n_victims; the histogram
-//      is left zero for the next call.
-// A bucket larger than the LDS list is re-read from the score row instead.
+//   collect (4096 slots of a head per 1024-thread workgroup): the bucket b
+//           of rank m from the histogram (the keys are already in flight);
+//           per 1024-slot chunk the count of keys below b (ballot counts);
+//           the (key, slot) pairs of bucket b to this workgroup's region.
+//   refine  (one 1024-thread workgroup per head): the bucket's pairs into
+//           LDS; two radix passes (key bits 20..10, then 9..0) give T and
+//           the rank of the m-th pair among the keys equal to T; rank
+//           counting among those gives the cut slot; per-chunk victim
+//           counts and their exclusive scan (each chunk's first output
+//           index); T, cut and n_victims to the workspace; the histogram is
+//           left zero for the next call.
+// A bucket with more pairs than LDS holds is re-read from the regions.
 #pragma once
 
 #include "kvev_device.h"
@@ -23,16 +25,9 @@
 
 namespace kvev {
 
-constexpr int kHeadCand = 4096;  // bucket pairs kept in LDS
-constexpr int kHeadTie = 2048;   // keys equal to T ranked in LDS
-
-struct HeadSelLds {
-  uint32_t h[kSelectBins];
-  uint32_t chunk_cnt[kSelectMaxChunks];
-  uint2 cand[kHeadCand];
-  uint32_t wave_tot[16];
-  uint32_t s_ncand, s_bin, s_below, s_cut, s_nt;
-};
+constexpr int kSelThreads = 1024;   // collect and refine workgroups
+constexpr int kHeadCand = 4096;     // bucket pairs refine keeps in LDS
+constexpr int kHeadTie = 2048;      // keys equal to T ranked in LDS
 
 // Inclusive scan of v over the 64 lanes of a wave.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
@@ -45,154 +40,209 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
-// Bin of h[0, nbins) that holds the element of 1-based rank `rank`, and the
-// number of elements in lower bins (requires 1 <= rank <= total).  Every
-// thread of the workgroup calls it; thread t owns a run of consecutive bins.
-__device__ inline void wg_rank_bin(const uint32_t *h, int nbins, uint32_t rank, HeadSelLds &L) {
-  const int NT = blockDim.x, tid = threadIdx.x, wv = tid / kWave, lane = lane_id();
-  const int per = (nbins + NT - 1) / NT;
-  const int b0 = min(tid * per, nbins), b1 = min(b0 + per, nbins);
-  uint32_t mine = 0;
-  for (int i = b0; i < b1; ++i) mine += h[i];
-  uint32_t incl = wave_incl_scan(mine);
-  if (tid == 0) {
-    L.s_bin = 0;
-    L.s_below = 0;
-  }
-  if (lane == kWave - 1) L.wave_tot[wv] = incl;
-  __syncthreads();
-  uint32_t before = 0;
-  for (int w = 0; w < wv; ++w) before += L.wave_tot[w];
-  incl += before;
-  const uint32_t excl = incl - mine;
-  if (excl < rank && rank <= incl) {
-    uint32_t acc = excl;
-    int i = b0;
-    while (acc + h[i] < rank) acc += h[i++];
-    L.s_bin = (uint32_t)i;
-    L.s_below = acc;
+struct RankOut {
+  uint32_t bin, below;
+};
+
+// Bin of h[0, NBINS) that holds the element of 1-based rank `rank`, and the
+// number of elements in lower bins ({0, 0} if the total is below the rank).
+// Wave 0 computes: lane l owns NBINS/64 consecutive bins, summed in a
+// rotated order (the lanes spread over the LDS banks); the owning lane reads
+// its bins into registers at once and finds the bin there.  Every thread of
+// the workgroup calls it and leaves after one barrier.
+template <int NBINS>
+__device__ inline void wg_rank_bin(const uint32_t *h, uint32_t rank, RankOut *out) {
+  constexpr int PER = NBINS / kWave;
+  static_assert(PER >= 1 && (PER & (PER - 1)) == 0, "bins per lane: a power of two");
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const int b0 = lane * PER;
+    uint32_t mine = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) mine += h[b0 + ((i + lane) & (PER - 1))];
+    const uint32_t incl = wave_incl_scan(mine);
+    const uint32_t excl = incl - mine;
+    const bool own = excl < rank && rank <= incl;
+    if (own) {
+      uint32_t x[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) x[i] = h[b0 + i];
+      uint32_t acc = excl, bin = (uint32_t)(b0 + PER - 1);
+      bool found = false;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        if (!found && acc + x[i] >= rank) {
+          bin = (uint32_t)(b0 + i);
+          found = true;
+        }
+        if (!found) acc += x[i];
+      }
+      out->bin = bin;
+      out->below = acc;
+    }
+    if (__ballot(own) == 0 && lane == 0) *out = RankOut{0, 0};
   }
   __syncthreads();
 }
 
-struct HeadSel {
-  const float *score;  // row of this head: score + u * max_slots
-  uint32_t *hist;      // 2048 bins of this head (complete on entry)
-  int u, m, nc, chunks;
+// ---------------------------------------------------------------- collect
+
+struct CollectLds {
+  uint32_t h[kSelectBins];
+  uint32_t cb[kHistChunk / kSelectChunk];  // keys below the bucket per chunk
+  RankOut r;
+  uint32_t s_ncand;
 };
 
-// Requires 0 < m < nc.  Call with every thread of the workgroup; uses only
-// the LDS it is given.
-__device__ inline void head_select(const SelHead &S, const HeadSel &H, HeadSelLds &L) {
-  const int NT = blockDim.x, tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
-  const int nw = NT / kWave;
-  const int nc = H.nc;
-  const uint32_t m = (uint32_t)H.m;
-  const float *row = H.score;
-  const int live = (nc + kSelectChunk - 1) / kSelectChunk;  // chunks with candidates
-  const bool al16 = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
-
-  // ---- 1. bucket of rank m
-  for (int i = tid; i < kSelectBins; i += NT) L.h[i] = H.hist[i];
-  for (int i = tid; i < live; i += NT) L.chunk_cnt[i] = 0;
+// Workgroup c of head u: slots [c*4096, c*4096 + 4096) of [0, nc).
+__device__ inline void collect_chunk(const SelHead &S, const float *row, const uint32_t *hist,
+                                     int u, int c, int m, int nc, int max_slots, CollectLds &L) {
+  constexpr int NT = kSelThreads;
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
+  const int s0 = c * kHistChunk;
+  // the histogram first, then this thread's four keys (in flight meanwhile)
+  uint32_t hv[kSelectBins / NT];
+#pragma unroll
+  for (int q = 0; q < kSelectBins / NT; ++q) hv[q] = hist[tid + q * NT];
+  // 16-byte aligned rows of a multiple of 16 floats: the clamped float4 is
+  // inside the row (slots past nc are masked below)
+  const float4 v = *reinterpret_cast<const float4 *>(row + min(s0 + 4 * tid, max_slots - 4));
+#pragma unroll
+  for (int q = 0; q < kSelectBins / NT; ++q) L.h[tid + q * NT] = hv[q];
+  if (tid < kHistChunk / kSelectChunk) L.cb[tid] = 0;
   if (tid == 0) L.s_ncand = 0;
   __syncthreads();
-  wg_rank_bin(L.h, kSelectBins, m, L);
-  const uint32_t b = L.s_bin;
-  const uint32_t need = m - L.s_below;  // rank of the m-th pair inside bucket b
-
-  // ---- 2. keys below bucket b per chunk; bucket members to LDS.  A wave
-  // takes 256 consecutive slots (4 per lane) per step, four steps per round
-  // with every load issued first.
-  for (int g0 = wv * 256; g0 < nc; g0 += 4 * nw * 256) {
-    float4 v[4];
+  wg_rank_bin<kSelectBins>(L.h, (uint32_t)m, &L.r);
+  const uint32_t b = L.r.bin;
+  if (c == 0 && tid == 0) {
+    S.head_sel[u * 4 + 2] = b;
+    S.head_sel[u * 4 + 3] = L.r.below;
+  }
+  // a wave covers 256 consecutive slots: one chunk
+  const int s = s0 + 4 * tid;
+  const float e4[4] = {v.x, v.y, v.z, v.w};
+  uint32_t key[4];
+  uint64_t msk[4];
+  uint32_t below = 0, total = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int s = g0 + k * nw * 256 + lane * 4;
-      if (al16 && s + 3 < nc) {
-        v[k] = *reinterpret_cast<const float4 *>(row + s);
-      } else {
-        v[k].x = s + 0 < nc ? row[s + 0] : 0.f;
-        v[k].y = s + 1 < nc ? row[s + 1] : 0.f;
-        v[k].z = s + 2 < nc ? row[s + 2] : 0.f;
-        v[k].w = s + 3 < nc ? row[s + 3] : 0.f;
-      }
-    }
+  for (int e = 0; e < 4; ++e) {
+    const bool in = s + e < nc;
+    key[e] = score_key(e4[e]);
+    const uint32_t bk = key[e] >> 21;
+    below += (uint32_t)__popcll(__ballot(in && bk < b));
+    msk[e] = __ballot(in && bk == b);
+    total += (uint32_t)__popcll(msk[e]);
+  }
+  uint32_t base = 0;
+  if (lane == 0) {
+    if (below) atomicAdd(&L.cb[wv / (kSelectChunk / 256)], below);
+    if (total) base = atomicAdd(&L.s_ncand, total);
+  }
+  base = __builtin_amdgcn_readfirstlane(base);
+  uint2 *cand = S.cand + ((size_t)u * S.nwg + c) * kHistChunk;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int gs = g0 + k * nw * 256;
-      if (gs >= nc) break;
-      const int s = gs + lane * 4;
-      const float e4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-      uint32_t key[4];
-      uint64_t msk[4];
-      int below = 0, tot = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool in = s + e < nc;
-        key[e] = score_key(e4[e]);
-        const uint32_t bk = key[e] >> 21;
-        below += (in && bk < b) ? 1 : 0;
-        msk[e] = __ballot(in && bk == b);
-        tot += __popcll(msk[e]);
-      }
-#pragma unroll
-      for (int o = kWave / 2; o >= 1; o >>= 1) below += __shfl_xor(below, o);
-      uint32_t base = 0;
-      if (lane == 0) {
-        if (below) atomicAdd(&L.chunk_cnt[gs / kSelectChunk], (uint32_t)below);
-        if (tot) base = atomicAdd(&L.s_ncand, (uint32_t)tot);
-      }
-      base = __shfl(base, 0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if ((msk[e] >> lane) & 1ull) {
-          const uint32_t p = base + (uint32_t)ballot_prefix(msk[e]);
-          if (p < (uint32_t)kHeadCand) L.cand[p] = make_uint2(key[e], (uint32_t)(s + e));
-        }
-        base += (uint32_t)__popcll(msk[e]);
-      }
-    }
+  for (int e = 0; e < 4; ++e) {
+    if ((msk[e] >> lane) & 1ull)
+      cand[base + (uint32_t)ballot_prefix(msk[e])] = make_uint2(key[e], (uint32_t)(s + e));
+    base += (uint32_t)__popcll(msk[e]);
   }
   __syncthreads();
-  const int ncand = (int)L.s_ncand;
+  if (tid == 0) S.ccount[(size_t)u * S.nwg + c] = L.s_ncand;
+  if (tid < kHistChunk / kSelectChunk) {
+    const int ch = s0 / kSelectChunk + tid;
+    if (ch * kSelectChunk < nc) S.chunk_below[(size_t)u * S.chunks + ch] = L.cb[tid];
+  }
+}
+
+// ----------------------------------------------------------------- refine
+
+struct RefineLds {
+  uint32_t h[kSelectBins];
+  uint32_t chunk_cnt[kSelectMaxChunks];
+  uint32_t coff[kSelectMaxChunks / (kHistChunk / kSelectChunk) + 1];  // region offsets
+  uint2 cand[kHeadCand];
+  RankOut r;
+  uint32_t s_cut, s_nt;
+};
+
+// One workgroup per head, after collect.  Requires 0 < m < nc.
+__device__ inline void refine_head(const SelHead &S, uint32_t *hist, int u, int m, int nc,
+                                   RefineLds &L) {
+  constexpr int NT = kSelThreads;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int live = (nc + kSelectChunk - 1) / kSelectChunk;  // chunks with candidates
+  const int nw = (nc + kHistChunk - 1) / kHistChunk;        // collect regions written
+  const uint32_t b = S.head_sel[u * 4 + 2];
+  const uint32_t need = (uint32_t)m - S.head_sel[u * 4 + 3];  // rank inside bucket b
+  const uint32_t *cc = S.ccount + (size_t)u * S.nwg;
+  const uint2 *reg = S.cand + (size_t)u * S.nwg * kHistChunk;
+  // counts: the chunks' below-bucket counts, the regions' pair counts
+  for (int i = tid; i < live; i += NT) L.chunk_cnt[i] = S.chunk_below[(size_t)u * S.chunks + i];
+  if (tid < kWave) {  // exclusive scan of the region counts (nw <= 256: 4 per lane)
+    const int per = (nw + kWave - 1) / kWave;
+    const int w0 = min(lane * per, nw), w1 = min(w0 + per, nw);
+    uint32_t mine = 0;
+    for (int w = w0; w < w1; ++w) mine += min(cc[w], (uint32_t)kHistChunk);
+    uint32_t e = wave_incl_scan(mine) - mine;
+    for (int w = w0; w < w1; ++w) {
+      L.coff[w] = e;
+      e += min(cc[w], (uint32_t)kHistChunk);
+    }
+    if (lane == kWave - 1) L.coff[nw] = e;
+  }
+  __syncthreads();
+  const int ncand = (int)L.coff[nw];
+  // pair i: its region by binary search over the offsets
+  auto pair_at = [&](int i) -> uint2 {
+    int lo = 0, hi = nw - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int)L.coff[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    return reg[(size_t)lo * kHistChunk + (i - (int)L.coff[lo])];
+  };
   const bool staged = ncand <= kHeadCand;
-  // visits every (key, slot) of bucket b: from LDS, or from the score row
+  if (staged) {
+    uint2 t[kHeadCand / NT];
+#pragma unroll
+    for (int q = 0; q < kHeadCand / NT; ++q) {
+      const int i = tid + q * NT;
+      if (i < ncand) t[q] = pair_at(i);
+    }
+#pragma unroll
+    for (int q = 0; q < kHeadCand / NT; ++q) {
+      const int i = tid + q * NT;
+      if (i < ncand) L.cand[i] = t[q];
+    }
+  }
+  for (int i = tid; i < kSelectBins; i += NT) L.h[i] = 0;
+  __syncthreads();
   auto for_cand = [&](auto &&f) {
-    if (staged) {
-      for (int i = tid; i < ncand; i += NT) {
-        const uint2 c = L.cand[i];
-        f(c.x, (int)c.y);
-      }
-    } else {
-      for (int s = tid; s < nc; s += NT) {
-        const uint32_t k = score_key(row[s]);
-        if ((k >> 21) == b) f(k, s);
-      }
+    for (int i = tid; i < ncand; i += NT) {
+      const uint2 c = staged ? L.cand[i] : pair_at(i);
+      f(c.x, (int)c.y);
     }
   };
 
-  // ---- 3. radix passes over the bucket: bits 20..10, then 9..0
-  for (int i = tid; i < kSelectBins; i += NT) L.h[i] = 0;
-  __syncthreads();
+  // ---- radix passes over the bucket: bits 20..10, then 9..0
   for_cand([&](uint32_t k, int) { atomicAdd(&L.h[(k >> 10) & 2047u], 1u); });
   __syncthreads();
-  wg_rank_bin(L.h, 2048, need, L);
-  const uint32_t pre = (b << 11) | L.s_bin;  // key >> 10 of T
-  const uint32_t need2 = need - L.s_below;
+  wg_rank_bin<2048>(L.h, need, &L.r);
+  const uint32_t pre = (b << 11) | L.r.bin;  // key >> 10 of T
+  const uint32_t need2 = need - L.r.below;
   for (int i = tid; i < 1024; i += NT) L.h[i] = 0;
   __syncthreads();
   for_cand([&](uint32_t k, int) {
     if ((k >> 10) == pre) atomicAdd(&L.h[k & 1023u], 1u);
   });
   __syncthreads();
-  wg_rank_bin(L.h, 1024, need2, L);
-  const uint32_t T = (pre << 10) | L.s_bin;
-  const uint32_t eT = need2 - L.s_below;  // keys equal to T that are victims
-  const uint32_t cnt_t = L.h[L.s_bin];     // keys equal to T
+  wg_rank_bin<1024>(L.h, need2, &L.r);
+  const uint32_t T = (pre << 10) | L.r.bin;
+  const uint32_t eT = need2 - L.r.below;  // keys equal to T that are victims
+  const uint32_t cnt_t = L.h[L.r.bin];     // keys equal to T
   __syncthreads();
 
-  // ---- 4. cut slot: the eT-th smallest slot among the keys equal to T
+  // ---- cut slot: the eT-th smallest slot among the keys equal to T
   int cut = INT_MAX;
   if (eT < cnt_t) {
     if (cnt_t <= (uint32_t)kHeadTie) {
@@ -222,44 +272,39 @@ __device__ inline void head_select(const SelHead &S, const HeadSel &H, HeadSelLd
           if (k == T && ((uint32_t)s & sm) == sp) atomicAdd(&L.h[((uint32_t)s >> shift) & 255u], 1u);
         });
         __syncthreads();
-        wg_rank_bin(L.h, 256, rank, L);
-        sp |= L.s_bin << shift;
+        wg_rank_bin<256>(L.h, rank, &L.r);
+        sp |= L.r.bin << shift;
         sm |= 255u << shift;
-        rank -= L.s_below;
+        rank -= L.r.below;
         __syncthreads();
       }
       cut = (int)sp;
     }
   }
 
-  // ---- 5. victims per chunk, their offsets, the head's threshold
+  // ---- victims per chunk, their offsets, the head's threshold
   for_cand([&](uint32_t k, int s) {
     if (k < T || (k == T && s <= cut)) atomicAdd(&L.chunk_cnt[s / kSelectChunk], 1u);
   });
   __syncthreads();
-  {
-    const int per = (live + NT - 1) / NT;
-    const int c0 = min(tid * per, live), c1 = min(c0 + per, live);
+  if (tid < kWave) {  // one wave: exclusive scan of the chunk counts
+    const int per = (live + kWave - 1) / kWave;
+    const int c0 = min(lane * per, live), c1 = min(c0 + per, live);
     uint32_t mine = 0;
     for (int c = c0; c < c1; ++c) mine += L.chunk_cnt[c];
-    uint32_t incl = wave_incl_scan(mine);
-    if (lane == kWave - 1) L.wave_tot[wv] = incl;
-    __syncthreads();
-    uint32_t before = 0;
-    for (int w = 0; w < wv; ++w) before += L.wave_tot[w];
-    uint32_t e = before + incl - mine;
-    uint32_t *off = S.chunk_off + (size_t)H.u * H.chunks;
+    uint32_t e = wave_incl_scan(mine) - mine;
+    uint32_t *off = S.chunk_off + (size_t)u * S.chunks;
     for (int c = c0; c < c1; ++c) {
       off[c] = e;
       e += L.chunk_cnt[c];
     }
   }
   if (tid == 0) {
-    S.head_sel[H.u * 4 + 0] = T;
-    S.head_sel[H.u * 4 + 1] = (uint32_t)cut;
-    S.n_victims[H.u] = H.m;
+    S.head_sel[u * 4 + 0] = T;
+    S.head_sel[u * 4 + 1] = (uint32_t)cut;
+    S.n_victims[u] = m;
   }
-  for (int i = tid; i < kSelectBins; i += NT) H.hist[i] = 0;
+  for (int i = tid; i < kSelectBins; i += NT) hist[i] = 0;
 }
 
 }  // namespace kvev

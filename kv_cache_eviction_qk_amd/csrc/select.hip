@@ -3,13 +3,14 @@
 // Scores become order-preserving 32-bit keys (kvev::score_key).  With
 // m = max(0, n - budget) victims among the candidate slots [0, nc),
 // nc = n - recent, the victims are the m smallest (key, slot) pairs: equal
-// scores evict the lower position first ([SNAP] "Tie-breaking").  Three
+// scores evict the lower position first ([SNAP] "Tie-breaking").  Four
 // launches:
-//   hist  4096 slots of one head per workgroup: LDS histogram of the top 11
-//         key bits, added into the head's 2048-bin histogram (integer
-//         atomics: exact).
-//   head  one workgroup per head: the exact threshold (kvev_select_head.h).
-//   emit  1024 slots per workgroup: marks the victims against the threshold,
+//   hist     4096 slots of one head per workgroup: LDS histogram of the top
+//            11 key bits, added into the head's 2048-bin histogram (integer
+//            atomics: exact).
+//   collect  4096 slots per workgroup, refine one workgroup per head: the
+//            exact threshold (kvev_select_head.h).
+//   emit     1024 slots per workgroup: marks the victims against the threshold,
 //         prefix-sums them and writes their slots from the chunk's offset,
 //         so the list is in ascending slot order.
 // Integer throughout: the result depends only on the score bits.
@@ -23,7 +24,6 @@ namespace kvev {
 
 namespace {
 constexpr int kHistThreads = 1024;
-constexpr int kHeadThreads = 1024;
 constexpr int kEmitThreads = 256;
 constexpr int kEmitPer = kSelectChunk / kEmitThreads;
 }  // namespace
@@ -59,10 +59,22 @@ __global__ __launch_bounds__(kHistThreads) void select_hist_kernel(const SelectA
     if (hl[i]) atomicAdd(&hg[i], hl[i]);
 }
 
-// One workgroup per head: the exact threshold from the complete histogram.
-__global__ __launch_bounds__(kHeadThreads) void select_head_kernel(const SelectArgs P) {
+__global__ __launch_bounds__(kSelThreads) void select_collect_kernel(const SelectArgs P) {
+  __shared__ CollectLds L;
+  const int c = blockIdx.x, u = blockIdx.y;
+  const int n = P.seq_len[u];
+  if (n < 0 || n > P.max_slots) return;
+  const int m = max(0, n - P.sel.budget);
+  const int nc = max(0, n - P.sel.recent);
+  if (m == 0 || c * kHistChunk >= nc) return;
+  collect_chunk(P.sel, P.score + (size_t)u * P.max_slots, P.sel.hist + (size_t)u * kSelectBins, u,
+                c, m, nc, P.max_slots, L);
+}
+
+// One workgroup per head: the exact threshold from the collected bucket.
+__global__ __launch_bounds__(kSelThreads) void select_refine_kernel(const SelectArgs P) {
   extern __shared__ __align__(16) uint8_t smem[];
-  HeadSelLds &L = *reinterpret_cast<HeadSelLds *>(smem);
+  RefineLds &L = *reinterpret_cast<RefineLds *>(smem);
   const int u = blockIdx.x, tid = threadIdx.x;
   const int n = P.seq_len[u];
   if (n < 0 || n > P.max_slots) {  // inconsistent head
@@ -75,8 +87,7 @@ __global__ __launch_bounds__(kHeadThreads) void select_head_kernel(const SelectA
     if (tid == 0) P.sel.n_victims[u] = 0;
     return;
   }
-  head_select(P.sel, HeadSel{P.score + (size_t)u * P.max_slots,
-                             P.sel.hist + (size_t)u * kSelectBins, u, m, nc, P.sel.chunks}, L);
+  refine_head(P.sel, P.sel.hist + (size_t)u * kSelectBins, u, m, nc, L);
 }
 
 __global__ __launch_bounds__(kEmitThreads) void select_emit_kernel(const SelectArgs P) {
@@ -125,18 +136,20 @@ __global__ __launch_bounds__(kEmitThreads) void select_emit_kernel(const SelectA
     }
 }
 
-hipError_t launch_select_head(const SelectArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(select_head_kernel, dim3(a.units), dim3(kHeadThreads), sizeof(HeadSelLds), s,
+hipError_t launch_select_threshold(const SelectArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(select_collect_kernel, dim3(a.sel.nwg, a.units), dim3(kSelThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(select_refine_kernel, dim3(a.units), dim3(kSelThreads), sizeof(RefineLds), s,
                      a);
   return hipGetLastError();
 }
 
 hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
-  const int hist_x = (a.max_slots + kHistChunk - 1) / kHistChunk;
-  hipLaunchKernelGGL(select_hist_kernel, dim3(hist_x, a.units), dim3(kHistThreads), 0, s, a);
+  hipLaunchKernelGGL(select_hist_kernel, dim3(a.sel.nwg, a.units), dim3(kHistThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_select_head(a, s);
+  e = launch_select_threshold(a, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(select_emit_kernel, dim3(a.sel.chunks, a.units), dim3(kEmitThreads), 0, s, a);
   return hipGetLastError();
