@@ -6,6 +6,7 @@
 // and window_attn.hip.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -269,6 +270,7 @@ void fill_compact_args(kvev_cache *cache, float *score_or_null, int32_t *free_li
   a.chunks = L.chunks;
   a.free_capacity = free_capacity;
   a.rows_per_item = 4 * 256 / (a.row_bytes / 16);  // compact.hip: 4 rows per thread
+  a.rows_cap = a.max_slots;
 }
 
 kvev::SelHead sel_head(const kvev_cache *cache, int32_t *n_victims, int32_t budget,
@@ -379,6 +381,7 @@ int kvev_evict(const kvev_cache *cache, const kvev_window *win, int32_t flags,
   c.chunk_off = a.sel.chunk_off;
   c.sel_score = score;
   c.recent = recent_window;
+  c.rows_cap = std::min(budget, c.max_slots);  // n' = min(n, budget)
   const hipStream_t st = static_cast<hipStream_t>(stream);
   kvev::SelectArgs sa{};
   sa.score = score;

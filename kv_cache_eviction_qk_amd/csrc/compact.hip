@@ -26,6 +26,8 @@
 // and section 3.5, invariants I1, I2 and I4.)
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "kvev_device.h"
 #include "kvev_kernels.h"
 
@@ -121,9 +123,11 @@ __device__ bool settle_trivial(const CompactArgs &P, int u, int c, int n, int m)
 
 // Ranks the kept slots of the chunk [s0, s1) (thread t owns the slots
 // s0 + 4t .. s0 + 4t + 3), records their sources and new pos / score, copies
-// the at-risk rows to the workspace and the chunk's moved / staged counts.
-// j0: victims of the head before s0.  With victims_out, also writes the
-// chunk's victims at their list positions.
+// the at-risk rows to the workspace and returns the chunk's moved / staged
+// counts.  j0: victims of the head before s0.  With victims_out, also writes
+// the chunk's victims at their list positions.  The at-risk list is built
+// first, so the staging loads are in flight while the rank records are
+// stored.
 __device__ void rank_and_stage(const CompactArgs &P, int u, int s0, int s1, int n2, int m, int j0,
                                const bool (&vic)[kPerThread], const int (&posv)[kPerThread],
                                const float (&scv)[kPerThread], int32_t *victims_out, PrepLds &S,
@@ -137,18 +141,22 @@ __device__ void rank_and_stage(const CompactArgs &P, int u, int s0, int s1, int 
     kept += (s < s1 && !vic[q]) ? 1 : 0;
   }
   const int excl = block_exclusive_scan(kept, S.wave_tot);
+  // classify: destination rank and source of each kept slot, list position
+  // of each victim; at-risk slots to the staging list
   int r = (s0 - j0) + excl;  // kept slots before s0, plus those before mine in the chunk
   int jv = j0 + (min(tid * kPerThread, max(0, s1 - s0)) - excl);  // victims before mine
+  int rq[kPerThread], srcq[kPerThread], jq[kPerThread];
   int my_err = 0, my_moved = 0, my_staged = 0;
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
     const int s = s0 + tid * kPerThread + q;
+    rq[q] = -1;
+    jq[q] = -1;
+    srcq[q] = -1;
     if (s >= s1) continue;
     if (vic[q]) {
-      if (victims_out) {
-        if (jv >= 0 && jv < m) victims_out[urow + jv] = s;
-        else my_err = 1;
-      }
+      if (jv >= 0 && jv < m) jq[q] = jv;
+      else my_err = 1;
       ++jv;
       continue;
     }
@@ -167,46 +175,60 @@ __device__ void rank_and_stage(const CompactArgs &P, int u, int s0, int s1, int 
       src = (blk >= 0 && blk < P.num_blocks) ? blk * kBlock + s % kBlock : 0;
     }
     my_moved += src != -1 ? 1 : 0;
-    P.src_of[urow + r] = src;
-    P.new_pos[urow + r] = posv[q];
-    if (P.score) P.new_score[urow + r] = scv[q];
+    rq[q] = r;
+    srcq[q] = src;
     ++r;
   }
   if (my_err) atomicOr(&S.s_err, 1);
-  block_sum2(my_moved, my_staged, S);  // includes barriers: s_nstage is complete after it
+  block_sum2(my_moved, my_staged, S);  // barriers: the list and s_err are complete
   moved = my_moved;
   staged = my_staged;
-  // staging copy of the at-risk K and V rows in 16-byte pieces: each round
-  // issues four K and four V loads per thread before its stores
-  const int pieces = P.row_bytes / 16;
-  const int total = S.s_nstage * pieces;
-  for (int base = 0; base < total; base += 4 * kThreads) {
-    uint4 kv[4], vv[4];
-    size_t dst[4];
-    bool ok[4];
+
+  // staging copy of the at-risk K and V rows in 16-byte pieces, four K and
+  // four V pieces per thread and round: indices past the end repeat the last
+  // piece (the same bytes again), a block id outside the pool (flagged
+  // above) reads block 0, so loads and stores need no branches
+  const int pshift = __ffs(P.row_bytes / 16) - 1;  // 16-byte pieces per row: 8, 16 or 32
+  const int total = S.s_nstage << pshift;
+  uint4 kv[4], vv[4];
+  size_t dst[4];
+  auto stage_load = [&](int base) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int idx = base + q * kThreads + tid;
-      ok[q] = false;
-      if (idx < total) {
-        const int k = idx / pieces, part = idx % pieces;
-        const int s = S.stage_s[k];
-        const int blk = S.blk_l[(s - s0) / kBlock];
-        if (blk >= 0 && blk < P.num_blocks) {  // else flagged by the caller
-          const size_t src = ((size_t)blk * kBlock + s % kBlock) * P.row_bytes + (size_t)part * 16;
-          dst[q] = ((size_t)u * P.stage_rows + S.stage_i[k]) * P.row_bytes + (size_t)part * 16;
-          kv[q] = ld16(P.k_pool + src);
-          vv[q] = ld16(P.v_pool + src);
-          ok[q] = true;
-        }
-      }
+      const int idx = min(base + q * kThreads + tid, total - 1);
+      const int k = idx >> pshift, part = idx & ((1 << pshift) - 1);
+      const int s = S.stage_s[k];
+      int blk = S.blk_l[(s - s0) / kBlock];
+      blk = (blk >= 0 && blk < P.num_blocks) ? blk : 0;
+      const size_t src = ((size_t)blk * kBlock + s % kBlock) * P.row_bytes + (size_t)part * 16;
+      dst[q] = ((size_t)u * P.stage_rows + S.stage_i[k]) * P.row_bytes + (size_t)part * 16;
+      kv[q] = ld16(P.k_pool + src);
+      vv[q] = ld16(P.v_pool + src);
     }
+  };
+  auto stage_store = [&]() {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (ok[q]) {
-        st16(P.stage_k + dst[q], kv[q]);
-        st16(P.stage_v + dst[q], vv[q]);
-      }
+    for (int q = 0; q < 4; ++q) {
+      st16(P.stage_k + dst[q], kv[q]);
+      st16(P.stage_v + dst[q], vv[q]);
+    }
+  };
+  if (total > 0) stage_load(0);
+  // the rank records while the first staging loads are in flight
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int s = s0 + tid * kPerThread + q;
+    if (victims_out && jq[q] >= 0) victims_out[urow + jq[q]] = s;
+    if (rq[q] >= 0) {
+      P.src_of[urow + rq[q]] = srcq[q];
+      P.new_pos[urow + rq[q]] = posv[q];
+      if (P.score) P.new_score[urow + rq[q]] = scv[q];
+    }
+  }
+  if (total > 0) stage_store();
+  for (int base = 4 * kThreads; base < total; base += 4 * kThreads) {
+    stage_load(base);
+    stage_store();
   }
 }
 
@@ -217,7 +239,9 @@ __device__ void rank_and_stage(const CompactArgs &P, int u, int s0, int s1, int 
 // the head's error state, freed blocks and counts, and clears the word.
 __device__ void prep_finish(const CompactArgs &P, int u, int n, int m, int moved, int staged,
                             PrepLds &S) {
-  __syncthreads();  // s_err is final
+  // s_err is final: its last writes precede a barrier (rank_and_stage's
+  // sums, or the sample counts of the victim-list form); no barrier here, so
+  // no wait for the staging stores
   if (threadIdx.x != 0) return;
   const unsigned long long mine = 1ull | ((unsigned long long)(S.s_err ? 1 : 0) << 11) |
                                   ((unsigned long long)moved << 22) |
@@ -373,8 +397,35 @@ __global__ __launch_bounds__(kThreads) void evict_prep_kernel(const CompactArgs 
   __shared__ PrepLds S;
   const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
   prep_common_start(P, u, c);
+  // one round of loads: the head's length and victim count, threshold and
+  // chunk offset, and the chunk's pos, scores and block ids (indices clamped
+  // inside the rows, so none waits on another)
+  const size_t urow = (size_t)u * P.max_slots;
+  const int s0 = c * kChunk;
   const int n = P.seq_len[u];
   const int m = P.n_victims[u];
+  const uint32_t T = P.head_sel[u * 4 + 0];
+  const int cut = (int)P.head_sel[u * 4 + 1];
+  const uint32_t coff = P.chunk_off[(size_t)u * P.chunks + c];
+  int posv[kPerThread];
+  float scv[kPerThread], sel[kPerThread];
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const size_t i = urow + min(s0 + tid * kPerThread + q, P.max_slots - 1);
+    posv[q] = P.pos[i];
+    sel[q] = P.sel_score[i];
+  }
+  if (P.score) {
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q)
+      scv[q] = P.score[urow + min(s0 + tid * kPerThread + q, P.max_slots - 1)];
+  } else {
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) scv[q] = 0.f;
+  }
+  const int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
+  const int blk_raw = tid < kChunk / kBlock ? bt[min(s0 / kBlock + tid, P.max_blocks - 1)] : 0;
+
   if (settle_trivial(P, u, c, n, m)) return;
   if (c == 0 && tid == 0) {
     P.head_info[(size_t)u * 8 + 0] = n;
@@ -384,29 +435,14 @@ __global__ __launch_bounds__(kThreads) void evict_prep_kernel(const CompactArgs 
     S.s_err = 0;
     S.s_nstage = 0;
   }
-  const int s0 = c * kChunk;
   const int nc = max(0, n - P.recent);
-  const size_t urow = (size_t)u * P.max_slots;
   int moved = 0, staged = 0;
   if (s0 < n) {
     const int s1 = min(s0 + kChunk, n);
-    const uint32_t T = P.head_sel[u * 4 + 0];
-    const int cut = (int)P.head_sel[u * 4 + 1];
-    const int j0 = s0 < nc ? (int)P.chunk_off[(size_t)u * P.chunks + c] : m;
-    const int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
-    int posv[kPerThread];
-    float scv[kPerThread], sel[kPerThread];
-#pragma unroll
-    for (int q = 0; q < kPerThread; ++q) {
-      const int s = s0 + tid * kPerThread + q;
-      posv[q] = (s < s1) ? P.pos[urow + s] : 0;
-      scv[q] = (s < s1 && P.score) ? P.score[urow + s] : 0.f;
-      sel[q] = (s < s1 && s < nc) ? P.sel_score[urow + s] : 0.f;
-    }
+    const int j0 = s0 < nc ? (int)coff : m;
     int bad = 0;
     if (tid < kChunk / kBlock) {
-      const int lb = s0 / kBlock + tid;
-      const int blk = lb < blocks_of(s1) ? bt[lb] : 0;
+      const int blk = s0 / kBlock + tid < blocks_of(s1) ? blk_raw : 0;
       if (blk < 0 || blk >= P.num_blocks) bad = 1;
       S.blk_l[tid] = blk;
     }
@@ -424,33 +460,56 @@ __global__ __launch_bounds__(kThreads) void evict_prep_kernel(const CompactArgs 
   prep_finish(P, u, n, m, moved, staged, S);
 }
 
-// Persistent grid over (head, rank range) items; every head has at least one
-// item, and its first item settles the head (free list, table, seq_len, stats).
+// Persistent grid over (head, row range) items.  A prefix pass reads each
+// head's record once and keeps in LDS the item and free-list offsets of every
+// head.  Item 0 of a head records its stats and seq_len; every item appends
+// its share of the head's freed blocks and moves up to rows_per_item rows.
 __global__ __launch_bounds__(kThreads) void compact_gather_kernel(const CompactArgs P) {
-  __shared__ int item_start[kMaxUnits + 1];
-  __shared__ int wave_tot[kThreads / kWave];
-  __shared__ int s_total;
-  __shared__ int s_red[2][kThreads / kWave];
-  const int tid = threadIdx.x, lane = lane_id();
+  extern __shared__ int gsm[];
   const int U = P.units, RC = P.rows_per_item;
-  int base_count = 0;
+  int *item_start = gsm;            // [U + 1]
+  int *free_start = gsm + U + 1;    // [U + 1]
+  int *n2_l = gsm + 2 * (U + 1);    // [U]: rows kept, -1 = the head does not move
+  __shared__ int wave_tot[kThreads / kWave];
+  __shared__ int s_tot[2];
+  const int tid = threadIdx.x;
+  const int fc0 = *P.fc0;
+  int base_items = 0, base_freed = 0;
   for (int b0 = 0; b0 < U; b0 += kThreads) {
     const int u = b0 + tid;
-    int cnt = 0;
+    int cnt = 0, fr = 0;
     if (u < U) {
       const int32_t *hi = P.head_info + (size_t)u * 8;
       const int n = hi[0], m = hi[1], err = hi[2];
-      cnt = (!err && m > 0) ? max(1, (n - m + RC - 1) / RC) : 1;
+      fr = head_freed(P, n, m, err);
+      const bool moves = !err && n >= 0 && n <= P.max_slots && m > 0 && m <= n;
+      cnt = moves ? max(1, (n - m + RC - 1) / RC) : 1;
+      n2_l[u] = moves ? n - m : -1;
     }
-    const int ex = block_exclusive_scan(cnt, wave_tot);
-    if (u < U) item_start[u] = base_count + ex;
-    if (tid == kThreads - 1) s_total = base_count + ex + cnt;
+    const int ex_i = block_exclusive_scan(cnt, wave_tot);
+    const int ex_f = block_exclusive_scan(fr, wave_tot);
+    if (u < U) {
+      item_start[u] = base_items + ex_i;
+      free_start[u] = base_freed + ex_f;
+    }
+    if (tid == kThreads - 1) {
+      s_tot[0] = base_items + ex_i + cnt;
+      s_tot[1] = base_freed + ex_f + fr;
+    }
     __syncthreads();
-    base_count = s_total;
+    base_items = s_tot[0];
+    base_freed = s_tot[1];
     __syncthreads();
   }
-  const int total_items = base_count;
-  const int pieces = P.row_bytes / 16;  // 16-byte pieces per row (8, 16 or 32)
+  if (tid == 0) {
+    item_start[U] = base_items;
+    free_start[U] = base_freed;
+  }
+  __syncthreads();
+  const int total_items = base_items, total_freed = base_freed;
+  const bool room = fc0 >= 0 && (long long)fc0 + total_freed <= (long long)P.free_capacity;
+  const int pshift = __ffs(P.row_bytes / 16) - 1;  // 16-byte pieces per row: 8, 16 or 32
+  const int pool_rows = P.num_blocks * kBlock;
 
   for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
     int lo = 0, hi_u = U - 1;
@@ -459,120 +518,126 @@ __global__ __launch_bounds__(kThreads) void compact_gather_kernel(const CompactA
       if (item_start[mid] <= item) lo = mid; else hi_u = mid - 1;
     }
     const int u = lo, k = item - item_start[u];
-    const int32_t *hi = P.head_info + (size_t)u * 8;
-    const int n = hi[0], m = hi[1], ev = hi[2];
-    if (k == 0) {
-      // ---- settle the head: its place in the free list is the sum of the
-      // blocks freed by the heads before it
-      // (freed blocks recomputed from n, m and the error word: in range for
-      // any workspace contents)
-      int before = 0, total = 0;
-      for (int v = tid; v < U; v += kThreads) {
-        const int32_t *hv = P.head_info + (size_t)v * 8;
-        const int f = head_freed(P, hv[0], hv[1], hv[2]);
-        total += f;
-        if (v < u) before += f;
-      }
+    const int nitems = item_start[u + 1] - item_start[u];
+    const int n2 = n2_l[u];
+    const int fr = room ? free_start[u + 1] - free_start[u] : 0;  // > 0 only if the head moves
+    const int r0 = k * RC;
+    const bool rows = n2 > 0 && r0 < n2;
+    const int r1 = rows ? min(r0 + RC, n2) : 0;
+    // this item's share of the head's emptied tail blocks [lb0, lb0 + fr)
+    const int f0 = fr > 0 ? (int)((long long)fr * k / nitems) : 0;
+    const int f1 = fr > 0 ? (int)((long long)fr * (k + 1) / nitems) : 0;
+    const int lb0 = blocks_of(max(n2, 0));
+    int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
+    const size_t urow = (size_t)u * P.max_slots;
+    // lane group of 2^pshift threads per row, one 16-byte piece each, so an
+    // instruction covers whole rows; 4 rows per thread
+    const int rpr = kThreads >> pshift;  // rows per round
+    const int part = tid & ((1 << pshift) - 1);
+
+    // ---- one round of loads: sources, destination blocks, pos and score of
+    // the rows (past the item: its last row again), the first freed ids
+    int rr[4], srcv[4], dblk[4], npos[4], fid[4];
+    float nsc[4];
+    if (rows) {
 #pragma unroll
-      for (int o = kWave / 2; o >= 1; o >>= 1) {
-        before += __shfl_xor(before, o);
-        total += __shfl_xor(total, o);
+      for (int i = 0; i < 4; ++i) {
+        rr[i] = min(r0 + i * rpr + (tid >> pshift), r1 - 1);
+        srcv[i] = P.src_of[urow + rr[i]];
+        dblk[i] = bt[rr[i] / kBlock];
+        npos[i] = P.new_pos[urow + rr[i]];
+        nsc[i] = P.new_score[urow + rr[i]];
       }
-      if (lane == 0) {
-        s_red[0][tid / kWave] = before;
-        s_red[1][tid / kWave] = total;
-      }
-      __syncthreads();
-      before = 0;
-      total = 0;
-      for (int w = 0; w < kThreads / kWave; ++w) {
-        before += s_red[0][w];
-        total += s_red[1][w];
-      }
-      __syncthreads();
-      const int fc0 = *P.fc0;
-      const bool room = fc0 >= 0 && (long long)fc0 + total <= (long long)P.free_capacity;
-      const int freed = room ? head_freed(P, n, m, ev) : 0;
-      if (tid == 0) {
-        unsigned long long *st = reinterpret_cast<unsigned long long *>(P.stats);
-        if (ev) {
-          atomicOr(&st[4], (unsigned long long)ev);
-        } else if (m > 0) {
-          P.seq_len[u] = n - m;
-          const long long mv = hi[4], sg = hi[5];
-          if (mv) {
-            atomicAdd(&st[1], (unsigned long long)mv);
-            atomicAdd(&st[2], (unsigned long long)mv * 4ull * (unsigned long long)P.row_bytes);
-          }
-          if (sg) atomicAdd(&st[3], (unsigned long long)sg);
+    }
+    if (f1 > f0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) fid[q] = bt[lb0 + min(f0 + q * kThreads + tid, f1 - 1)];
+    }
+
+    if (k == 0 && tid == 0) {  // the head's record: stats, seq_len, free count
+      const int32_t *hi = P.head_info + (size_t)u * 8;
+      const int n = hi[0], m = hi[1], ev = hi[2];
+      unsigned long long *st = reinterpret_cast<unsigned long long *>(P.stats);
+      if (ev) {
+        atomicOr(&st[4], (unsigned long long)ev);
+      } else if (n2 >= 0) {
+        P.seq_len[u] = n - m;
+        const long long mv = hi[4], sg = hi[5];
+        if (mv) {
+          atomicAdd(&st[1], (unsigned long long)mv);
+          atomicAdd(&st[2], (unsigned long long)mv * 4ull * (unsigned long long)P.row_bytes);
         }
-        if (freed) atomicAdd(&st[0], (unsigned long long)freed);
-        if (u == U - 1) {
-          if (room) *P.free_count = fc0 + total;
-          else atomicOr(&st[4], 4ull);
+        if (sg) atomicAdd(&st[3], (unsigned long long)sg);
+      }
+      if (fr) atomicAdd(&st[0], (unsigned long long)fr);
+      if (u == U - 1) {
+        if (room) *P.free_count = fc0 + total_freed;
+        else atomicOr(&st[4], 4ull);
+      }
+    }
+
+    if (rows) {
+      // No branches between the K/V loads and stores (a branch there makes
+      // every store wait for the previous one): a row that stays copies onto
+      // itself (same bytes); a wave whose rows all stay skips the copy.
+      size_t dsto[4];
+      const uint8_t *ksrc[4], *vsrc[4];
+      bool moving = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dsto[i] = ((size_t)dblk[i] * kBlock + rr[i] % kBlock) * P.row_bytes + ((size_t)part << 4);
+        const int src = srcv[i];
+        const int si = -2 - src;
+        const bool staged = src <= -2 && si < P.stage_rows;
+        const bool pooled = src >= 0 && src < pool_rows;
+        moving |= staged || pooled;
+        const size_t so = staged ? ((size_t)u * P.stage_rows + si) * P.row_bytes + ((size_t)part << 4)
+                                 : pooled ? (size_t)src * P.row_bytes + ((size_t)part << 4) : dsto[i];
+        ksrc[i] = (staged ? P.stage_k : P.k_pool) + so;
+        vsrc[i] = (staged ? P.stage_v : P.v_pool) + so;
+      }
+      if (__any(moving)) {  // wave-uniform
+        uint4 kv[4], vv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          kv[i] = ld16(ksrc[i]);
+          vv[i] = ld16(vsrc[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          st16(P.k_pool + dsto[i], kv[i]);
+          st16(P.v_pool + dsto[i], vv[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) P.pos[urow + rr[i]] = npos[i];
+        if (P.score) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) P.score[urow + rr[i]] = nsc[i];
         }
       }
-      if (freed) {
-        const int lb0 = blocks_of(n - m);
-        int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
-        for (int i = tid; i < freed; i += kThreads) {
-          P.free_list[fc0 + before + i] = bt[lb0 + i];
+    }
+
+    if (f1 > f0) {  // freed ids to the free list, their table entries to -1
+      int32_t *fl = P.free_list + fc0 + free_start[u];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = f0 + q * kThreads + tid;
+        if (i < f1) {
+          fl[i] = fid[q];
           bt[lb0 + i] = -1;
         }
       }
-    }
-    if (ev || m <= 0) continue;
-    const int n2 = n - m;
-    const int r0 = k * RC;
-    if (r0 >= n2) continue;
-    const int r1 = min(r0 + RC, n2);
-    const size_t urow = (size_t)u * P.max_slots;
-    // lane group of `pieces` threads per row, one 16-byte piece each, so an
-    // instruction covers whole rows; 4 rows per thread, all loads first
-    const int rpr = kThreads / pieces;  // rows per round
-    const int part = tid % pieces;
-    int rr[4], srcv[4], dblk[4], npos[4];
-    float nsc[4];
+      for (int i0 = f0 + 4 * kThreads; i0 < f1; i0 += 4 * kThreads) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      rr[i] = r0 + i * rpr + tid / pieces;
-      const bool in = rr[i] < r1;
-      srcv[i] = in ? P.src_of[urow + rr[i]] : -1;
-      dblk[i] = in ? P.block_table[(size_t)u * P.max_blocks + rr[i] / kBlock] : 0;
-      npos[i] = (in && part == 0) ? P.new_pos[urow + rr[i]] : 0;
-      nsc[i] = (in && part == 0 && P.score) ? P.new_score[urow + rr[i]] : 0.f;
-    }
-    uint4 kv[4], vv[4];
-    const int pool_rows = P.num_blocks * kBlock;
+        for (int q = 0; q < 4; ++q) fid[q] = bt[lb0 + min(i0 + q * kThreads + tid, f1 - 1)];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // a source outside the pool or the staging rows is skipped (cannot
-      // happen with a workspace these kernels wrote)
-      if (srcv[i] >= pool_rows || (srcv[i] < -1 && -2 - srcv[i] >= P.stage_rows)) srcv[i] = -1;
-      const int src = srcv[i];
-      if (src != -1) {
-        const uint8_t *ks, *vs;
-        if (src >= 0) {
-          ks = P.k_pool + (size_t)src * P.row_bytes;
-          vs = P.v_pool + (size_t)src * P.row_bytes;
-        } else {
-          const size_t so = ((size_t)u * P.stage_rows + (-2 - src)) * P.row_bytes;
-          ks = P.stage_k + so;
-          vs = P.stage_v + so;
+        for (int q = 0; q < 4; ++q) {
+          const int i = i0 + q * kThreads + tid;
+          if (i < f1) {
+            fl[i] = fid[q];
+            bt[lb0 + i] = -1;
+          }
         }
-        kv[i] = ld16(ks + (size_t)part * 16);
-        vv[i] = ld16(vs + (size_t)part * 16);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (srcv[i] == -1) continue;
-      const size_t dst = ((size_t)dblk[i] * kBlock + rr[i] % kBlock) * P.row_bytes + (size_t)part * 16;
-      st16(P.k_pool + dst, kv[i]);
-      st16(P.v_pool + dst, vv[i]);
-      if (part == 0) {
-        P.pos[urow + rr[i]] = npos[i];
-        if (P.score) P.score[urow + rr[i]] = nsc[i];
       }
     }
   }
@@ -580,10 +645,12 @@ __global__ __launch_bounds__(kThreads) void compact_gather_kernel(const CompactA
 
 static hipError_t launch_gather(const CompactArgs &a, hipStream_t s) {
   // enough workgroups to cover every item of a full cache, capped
+  // kept rows per head are at most rows_cap (the fused path: the budget)
   const long long items =
-      (long long)a.units * ((a.max_slots + a.rows_per_item - 1) / a.rows_per_item);
+      (long long)a.units * std::max(1, (a.rows_cap + a.rows_per_item - 1) / a.rows_per_item);
   const int grid = (int)(items < 2048 ? (items > 0 ? items : 1) : 2048);
-  hipLaunchKernelGGL(compact_gather_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+  const size_t lds = sizeof(int) * (3 * (size_t)a.units + 2);  // item / free offsets, rows kept
+  hipLaunchKernelGGL(compact_gather_kernel, dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 

@@ -19,6 +19,14 @@ constexpr int kWave = 64;      // CDNA wavefront size
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// 16 bytes from global memory straight into LDS (global_load_lds_dwordx4):
+// lane l's bytes land at lds_wave_base + 16 * l; lds_wave_base must be the
+// same for every lane of the wave.  Completion is counted like a load.
+__device__ __forceinline__ void ld16_to_lds(const void *g, void *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                   (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
+}
 __device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
 
 // 16x16 tile, contraction 32, bf16 inputs, fp32 accumulate (v_mfma_f32_16x16x32_bf16).

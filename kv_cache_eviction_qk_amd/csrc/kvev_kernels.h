@@ -72,6 +72,7 @@ struct CompactArgs {
   int32_t *fc0;                 // free_count before the call
   int32_t units, max_blocks, max_slots, num_blocks, row_bytes, stage_rows, chunks,
       free_capacity, rows_per_item;
+  int32_t rows_cap;             // kept rows per head are at most this (sizes the gather grid)
 };
 
 struct WindowAttnArgs {

@@ -78,36 +78,57 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
   const int tile = wg % P.tiles_per_head;
   if (u >= P.units) return;
   const int b = u / P.Hkv, h = u % P.Hkv;
-  const int n = P.seq_len[u];
   const int max_slots = P.max_blocks * kBlock;
-  if (n <= 0 || n > max_slots) return;  // empty or inconsistent head: nothing to score
-  const int nb = (n + kBlock - 1) / kBlock;
   const int tb0 = tile * P.tile_blocks;
-  if (tb0 >= nb) return;
-  const int sel_m = fused ? max(0, n - P.sel.budget) : 0;  // victims of the head
-  const int sel_nc = max(0, n - P.sel.recent);             // candidate slots
-  if (sel_m > 0)
-    for (int i = threadIdx.x; i < kSelectBins; i += kThreads) hl[i] = 0;
-  const int tb1 = min(tb0 + P.tile_blocks, nb);
-  const int cb0 = max(0, tb0 - P.halo_blocks), cb1 = min(nb, tb1 + P.halo_blocks);
-
-  // ---- this wave's key blocks: ids first, then the first stage of loads is
-  // issued before the window rows are staged, so its latency overlaps the
-  // prologue
+  // The tile's block range over the whole list (the head's length is not
+  // known before the first loads return): waves split [cb0, cb1s) evenly and
+  // later skip blocks past the head's last one.
+  const int tb1s = min(tb0 + P.tile_blocks, P.max_blocks);
+  const int cb0 = max(0, tb0 - P.halo_blocks), cb1s = min(P.max_blocks, tb1s + P.halo_blocks);
   const int l = lane_id(), lr = l & 15, lg = l >> 4;
   const int wv = threadIdx.x / kWave;
-  const int nblk = cb1 - cb0;
-  const int wb0 = cb0 + (nblk * wv) / kWaves, wb1 = cb0 + (nblk * (wv + 1)) / kWaves;
+  const int nblk = cb1s - cb0;
+  const int wb0 = cb0 + (nblk * wv) / kWaves, wb1s = cb0 + (nblk * (wv + 1)) / kWaves;
   const int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
   const int32_t *ps = P.pos + (size_t)u * max_slots;
   const size_t lane_off = (size_t)lr * ROWB + (size_t)lg * (ROWB / 4);
   const float c1 = P.c1;
+  const int Hq = P.Hkv * P.G;
+  const size_t row0 = ((size_t)b * Hq + (size_t)h * P.G) * P.W;  // first row of the group
+  const int rows = P.rows;
+  const uint8_t *qsrc = P.q + row0 * ROWB;
+  const uint8_t *asrc = DROP ? P.a + row0 * ROWB : nullptr;
+  const int nunits = RT * U * kWave;  // 16-byte units of the staged rows
 
-  // Block ids of this wave's range, one lane each (the range never exceeds
-  // 64 blocks: tile + 2 * halo <= 256 blocks over 4 waves); read back with
-  // readlane, so no load waits on another.
-  const int nwb = wb1 - wb0;
-  int my_id = (l < nwb) ? bt[wb0 + l] : 0;
+  // ---- one round of loads at entry, none waiting on another: the head's
+  // length, this wave's block ids (one lane each; at most 64 blocks per wave),
+  // the LSE and positions of the window rows.  The window rows themselves go
+  // straight into LDS in MFMA fragment order (stage_pair): LDS unit
+  // (rt * U + j) * 64 + lane holds row rt*16 + lane%16, 16-byte chunk
+  // (lane/16) * U + j.  Indices are clamped in range; rows past the group
+  // repeat the last row (their LSE is +inf, so p = 0 for them).
+  const int n = P.seq_len[u];
+  int my_id = bt[min(wb0 + l, P.max_blocks - 1)];
+  const int lrow = min((int)threadIdx.x, rows - 1);
+  const float lse_v = P.lse[row0 + lrow];
+  const int qpos_v = P.q_pos[(size_t)b * P.W + (lrow % P.W)];
+  const int qpw = P.q_pos[(size_t)b * P.W + min(l, P.W - 1)];
+  const int npairs = RT * U;  // (row tile, chunk) pairs: 64 LDS units each
+  auto stage_pair = [&](int pr_) {
+    const int rt = pr_ / U, j = pr_ % U;
+    const int r = min(rt * 16 + lr, rows - 1), cc = lg * U + j;
+    ld16_to_lds(qsrc + (size_t)r * ROWB + cc * 16, qfrag + (size_t)pr_ * kWave);
+    if constexpr (DROP) ld16_to_lds(asrc + (size_t)r * ROWB + cc * 16, afrag + (size_t)pr_ * kWave);
+  };
+  if (n <= 0 || n > max_slots) return;  // empty or inconsistent head: nothing to score
+  const int nb = (n + kBlock - 1) / kBlock;
+  if (tb0 >= nb) return;
+  const int sel_m = fused ? max(0, n - P.sel.budget) : 0;  // victims of the head
+  const int sel_nc = max(0, n - P.sel.recent);             // candidate slots
+  const int tb1 = min(tb0 + P.tile_blocks, nb);
+  const int cb1 = min(nb, tb1 + P.halo_blocks);
+  const int wb1 = min(wb1s, cb1);  // this wave's live blocks: [wb0, wb1)
+  const int nwb = max(0, wb1 - wb0);
   const bool my_bad = (l < nwb) && (my_id < 0 || my_id >= P.num_blocks);
   const uint64_t bad_mask = __ballot(my_bad);
   if (my_bad) my_id = 0;  // a bad id loads block 0 and yields NaN scores
@@ -118,12 +139,15 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
     int kp[NB];
   };
   // Loads of blocks [cur, cur + NB), clamped to the wave's last block so every
-  // issue has the same shape (the clamped re-reads hit the cache).
+  // issue has the same shape (the clamped re-reads hit the cache).  A wave
+  // without live blocks still issues (block 0): no branch around the loads,
+  // so the compiler counts the loads in flight exactly.
   auto issue = [&](Frag &F, int cur) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int blk = min(cur + i, wb1 - 1);
-      const int id = __builtin_amdgcn_readlane(my_id, blk - wb0);
+      const int blk = max(wb0, min(cur + i, wb1 - 1));
+      int id = __builtin_amdgcn_readlane(my_id, blk - wb0);
+      id = (id >= 0 && id < P.num_blocks) ? id : 0;
       const uint8_t *ksrc = P.k_pool + (size_t)id * kBlock * ROWB + lane_off;
 #pragma unroll
       for (int j = 0; j < U; ++j) F.k[i][j] = ld16(ksrc + 16 * j);
@@ -136,49 +160,43 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
     }
   };
   Frag F0, F1;
-  if (nwb > 0) issue(F0, wb0);
+  issue(F0, wb0);
+  // the window rows into LDS right behind the first key blocks (a load into
+  // LDS issued earlier would make the compiler wait for it before any other
+  // load's result is used)
+  constexpr int kQ = 4;  // pairs per wave issued here (later pairs repeat the last)
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) stage_pair(min(wv + q * kWaves, npairs - 1));
 
-  // ---- stage the group's window rows in fragment order: LDS unit
-  // (rt * U + j) * 64 + lane holds row rt*16 + lane%16, 16-byte chunk
-  // (lane/16) * U + j of that row (consecutive threads write consecutive
-  // LDS units)
-  const int Hq = P.Hkv * P.G;
-  const size_t row0 = ((size_t)b * Hq + (size_t)h * P.G) * P.W;  // first row of the group
-  const int rows = P.rows;
-  {
-    const uint8_t *qsrc = P.q + row0 * ROWB;
-    const uint8_t *asrc = DROP ? P.a + row0 * ROWB : nullptr;
-    const int nunits = RT * U * kWave;
-    for (int d = threadIdx.x; d < nunits; d += kThreads) {
-      const int ln = d % kWave, j = (d / kWave) % U, rt = d / (kWave * U);
-      const int r = rt * 16 + (ln & 15), cc = (ln >> 4) * U + j;
-      uint4 v = make_uint4(0, 0, 0, 0), av = make_uint4(0, 0, 0, 0);
-      if (r < rows) {
-        v = ld16(qsrc + (size_t)r * ROWB + cc * 16);
-        if constexpr (DROP) av = ld16(asrc + (size_t)r * ROWB + cc * 16);
-      }
-      qfrag[d] = v;
-      if constexpr (DROP) afrag[d] = av;
-    }
+  // ---- the rest of the window-row staging while the first key blocks stream in
+  if ((int)threadIdx.x < RT * 16) {
+    const bool live = (int)threadIdx.x < rows;
+    lse2[threadIdx.x] = live ? lse_v * kLog2e : __builtin_inff();  // padding rows: p = 0
+    qposr[threadIdx.x] = live ? qpos_v : INT_MAX;
+  }
+  for (int pr_ = wv + kQ * kWaves; pr_ < npairs; pr_ += kWaves) stage_pair(pr_);  // large windows
+  for (int r = threadIdx.x + kThreads; r < RT * 16; r += kThreads) {
+    const bool live = r < rows;
+    const int rr = min(r, rows - 1);
+    lse2[r] = live ? P.lse[row0 + rr] * kLog2e : __builtin_inff();
+    qposr[r] = live ? P.q_pos[(size_t)b * P.W + (rr % P.W)] : INT_MAX;
+  }
+  if constexpr (DROP) {
+    // ||a||^2 of each row from the staged units, chunks in order
+    __syncthreads();
     for (int r = threadIdx.x; r < RT * 16; r += kThreads) {
-      if (r < rows) {
-        lse2[r] = P.lse[row0 + r] * kLog2e;
-        qposr[r] = P.q_pos[(size_t)b * P.W + (r % P.W)];
-        if constexpr (DROP) {
-          float ss = 0.f;  // ||a||^2 of the row, chunks in order
-          for (int cc = 0; cc < CPR; ++cc) ss += sumsq_unit<BF16>(ld16(asrc + (size_t)r * ROWB + cc * 16));
-          an2[r] = ss;
-        }
-      } else {
-        lse2[r] = __builtin_inff();  // padding rows: p = exp2(-inf) = 0
-        qposr[r] = INT_MAX;
-        if constexpr (DROP) an2[r] = 0.f;
-      }
+      const int rt = r >> 4, lr16 = r & 15;
+      float ss = 0.f;
+      for (int g = 0; g < 4; ++g)
+        for (int j = 0; j < U; ++j) ss += sumsq_unit<BF16>(afrag[(rt * U + j) * kWave + g * 16 + lr16]);
+      an2[r] = r < rows ? ss : 0.f;
     }
   }
+  if (sel_m > 0)
+    for (int i = threadIdx.x; i < kSelectBins; i += kThreads) hl[i] = 0;
   // earliest window query: keys at or before it are never masked
-  int minq = INT_MAX;
-  for (int w = l; w < P.W; w += kWave) minq = min(minq, P.q_pos[(size_t)b * P.W + w]);
+  int minq = qpw;
+  for (int w = l + kWave; w < P.W; w += kWave) minq = min(minq, P.q_pos[(size_t)b * P.W + w]);
 #pragma unroll
   for (int o = kWave / 2; o >= 1; o >>= 1) minq = min(minq, __shfl_xor(minq, o));
   __syncthreads();
@@ -297,31 +315,86 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
   }
   __syncthreads();
 
-  // ---- outputs for the tile's own slots
+  // ---- outputs for the tile's own slots [s0, s1): thread t owns 8
+  // consecutive slots (two 16-byte stores when the row is aligned)
   const int s0 = tb0 * kBlock, s1 = min(tb1 * kBlock, n);
-  const int base = cb0 * kBlock;
+  const int base = cb0 * kBlock, span_end = cb1 * kBlock;  // S_lds holds slots [base, span_end)
   const size_t orow = (size_t)u * max_slots;
-  for (int s = s0 + threadIdx.x; s < s1; s += kThreads) {
-    const float S = S_lds[s - base];
-    float selv = 0.f;
+  const int pr = P.pool_r;
+  for (int g0 = s0 + (int)threadIdx.x * 8; g0 < s1; g0 += kThreads * 8) {
+    const bool full = g0 + 8 <= s1;
+    float S8[8], selv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) S8[e] = S_lds[min(g0 + e, span_end - 1) - base];
+    auto put8 = [&](float *dst, const float (&v)[8]) {
+      float *o = dst + orow + g0;
+      if (full && (reinterpret_cast<uintptr_t>(o) & 15) == 0) {
+        *reinterpret_cast<float4 *>(o) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4 *>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (g0 + e < s1) o[e] = v[e];
+      }
+    };
     if (P.flags & 1) {  // SUM (with ACCUMULATE: add to the stored score)
-      float v = S;
-      if (P.flags & 8) v = P.sum[orow + s] + S;
-      P.sum[orow + s] = v;
-      selv = v;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[e] = S8[e];
+        if (P.flags & 8) v[e] += g0 + e < s1 ? P.sum[orow + g0 + e] : 0.f;
+        selv[e] = v[e];
+      }
+      put8(P.sum, v);
     }
-    if (P.flags & 2) {  // POOL: clamped max over [s - r, s + r]
-      const int lo = max(0, s - P.pool_r), hi = min(n - 1, s + P.pool_r);
-      float m = S_lds[lo - base];
-      for (int i = lo + 1; i <= hi; ++i) m = fmaxf(m, S_lds[i - base]);
-      P.pooled[orow + s] = m;
-      if (P.sel_kind == 2) selv = m;
+    if (P.flags & 2) {  // POOL: max over [s - r, s + r] clamped to [0, n - 1]
+      float v[8];
+      if (pr <= 8) {
+        // the 8 + 2r window values from registers; slots outside [0, n) are -inf
+        float w[24];
+#pragma unroll
+        for (int i = 0; i < 24; ++i) {
+          const int sl = g0 - pr + i;
+          w[i] = (i < 8 + 2 * pr && sl >= 0 && sl < n) ? S_lds[min(max(sl, base), span_end - 1) - base]
+                                                        : -__builtin_inff();
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float mx = w[e];
+#pragma unroll
+          for (int i = 1; i <= 16; ++i)
+            if (i <= 2 * pr) mx = fmaxf(mx, w[e + i]);
+          v[e] = mx;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int sl = min(g0 + e, s1 - 1);
+          const int lo = max(0, sl - pr), hi = min(n - 1, sl + pr);
+          float mx = S_lds[lo - base];
+          for (int i = lo + 1; i <= hi; ++i) mx = fmaxf(mx, S_lds[i - base]);
+          v[e] = mx;
+        }
+      }
+      put8(P.pooled, v);
+      if (P.sel_kind == 2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) selv[e] = v[e];
     }
     if constexpr (DROP) {
-      P.drop[orow + s] = D_lds[s - base];
-      if (P.sel_kind == 4) selv = D_lds[s - base];
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = D_lds[min(g0 + e, span_end - 1) - base];
+      put8(P.drop, v);
+      if (P.sel_kind == 4)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) selv[e] = v[e];
     }
-    if (sel_m > 0 && s < sel_nc) atomicAdd(&hl[score_key(selv) >> 21], 1u);
+    if (sel_m > 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (g0 + e < s1 && g0 + e < sel_nc) atomicAdd(&hl[score_key(selv[e]) >> 21], 1u);
+    }
   }
   if (sel_m == 0) return;
 
