@@ -217,10 +217,20 @@ int build_score_args(const kvev_cache *cache, const kvev_window *win, int32_t fl
   a.pool_r = (flags & KVEV_POOL) ? (pool_kernel - 1) / 2 : 0;
   a.halo_blocks = (a.pool_r + KVEV_BLOCK_SIZE - 1) / KVEV_BLOCK_SIZE;
   // Up to 8 waves (512 threads) share one staging of the window rows and
-  // split a tile of up to 256 blocks; smaller tiles and workgroups when the
-  // tiles would not cover the 256 CUs.
+  // split a tile of up to 256 blocks; smaller tiles when the tiles would not
+  // cover the 256 CUs or when the staged window rows plus the tile's score
+  // rows exceed a workgroup's LDS (large G*W windows); fewer waves for small
+  // tiles.
+  const int bf16 = cache->dtype == KVEV_BF16;
+  const int is_drop = (flags & KVEV_DROP) ? 1 : 0;
+  auto lds_of = [&](int t) {
+    return kvev::score_lds_bytes(bf16, cache->head_dim, is_drop, a.row_tiles, t, a.halo_blocks,
+                                 fused);
+  };
   int tb = KV_TILE_MAX, threads = KV_THREADS_MAX;
   while (tb > 16 && (int64_t)a.units * ((cache->max_blocks + tb - 1) / tb) < 256) tb /= 2;
+  while (tb > 1 && lds_of(tb) > kMaxLds - 1024) tb /= 2;
+  if (lds_of(tb) > kMaxLds - 1024) return KVEV_EUNSUPPORTED;
   while (threads > 256 && tb < 16 * (threads / 64)) threads /= 2;
   // a wave indexes its block range by lane: at most 64 blocks per wave
   while (tb > 1 && (tb + 2 * a.halo_blocks + threads / 64 - 1) / (threads / 64) > 64) tb /= 2;
@@ -228,11 +238,6 @@ int build_score_args(const kvev_cache *cache, const kvev_window *win, int32_t fl
   a.threads = threads;
   a.tiles_per_head = (cache->max_blocks + tb - 1) / tb;
   a.c1 = win->scale * 1.4426950408889634f;
-  const int bf16 = cache->dtype == KVEV_BF16;
-  const int is_drop = (flags & KVEV_DROP) ? 1 : 0;
-  const size_t lds = kvev::score_lds_bytes(bf16, cache->head_dim, is_drop, a.row_tiles,
-                                           a.tile_blocks, a.halo_blocks, fused);
-  if (lds > kMaxLds - 1024) return KVEV_EUNSUPPORTED;
   if ((int64_t)a.units * a.tiles_per_head > INT32_MAX) return KVEV_EUNSUPPORTED;
   return KVEV_OK;
 }

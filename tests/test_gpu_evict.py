@@ -13,20 +13,14 @@ workspace.
 """
 import numpy as np
 import pytest
-import torch
 
 import kv_cache_eviction_qk_amd as K
 import oracle
 import synth
-from tests.gpu_helpers import (TOL, assert_scores_close, dev, device_cache, device_window, host,
-                               victims_agree_up_to_tolerance)
+from tests.gpu_helpers import KIND, TOL, Run, check_eviction_vs_oracle_chain, dev
 from tests.helpers import rounded_window_inputs
 
 pytestmark = pytest.mark.gpu
-
-KIND = {"sum": (K.SUM, oracle.SUM, "sum"), "pool": (K.POOL, oracle.POOL, "pooled"),
-        "drop": (K.DROP, oracle.DROP, "drop")}
-
 
 def _ragged(B, H, L, seed=0):
     r = np.random.default_rng(seed)
@@ -40,49 +34,6 @@ def _ragged(B, H, L, seed=0):
 def _inputs(case, kind):
     lse64, a64 = oracle.lse_a(case, want_a=(kind == "drop"))
     return rounded_window_inputs(case, lse64, a64)
-
-
-class Run:
-    """One device copy of the case plus every buffer an eviction step touches."""
-
-    def __init__(self, case, prev=None, free_prefix=3):
-        self.case = case
-        self.dc = device_cache(case)
-        self.q, self.qp = device_window(case)
-        B, H, ms = case["B"], case["Hkv"], case["max_blocks"] * 16
-        self.ws = K.new_workspace(self.dc)
-        free0 = np.full(case["num_blocks"] + 8, -1, np.int32)
-        free0[:free_prefix] = np.arange(free_prefix) + 10**6
-        self.fl = dev(free0)
-        self.fc = dev(np.array([free_prefix], np.int32))
-        self.score = dev(prev.copy()) if prev is not None else dev(np.zeros((B, H, ms), np.float32))
-        self.vic = dev(np.full((B, H, ms), -1, np.int32))
-        self.nv = dev(np.zeros((B, H), np.int32))
-        self.stats = None
-
-    def fused(self, kind, lse32, a_enc, pool, budget, recent, accumulate=False):
-        flags = KIND[kind][0] | (K.ACCUMULATE if accumulate else 0)
-        self.stats = K.evict(self.dc, self.q, dev(lse32), self.qp, self.case["scale"],
-                             self.case["G"], flags, budget, recent, self.score, self.vic, self.nv,
-                             self.fl, self.fc, self.ws, pool_kernel=pool,
-                             a=dev(a_enc) if a_enc is not None else None)
-        torch.cuda.synchronize()
-
-    def three_calls(self, kind, lse32, a_enc, pool, budget, recent, accumulate=False):
-        flags = KIND[kind][0] | (K.ACCUMULATE if accumulate else 0)
-        kw = {KIND[kind][2]: self.score}
-        K.score(self.dc, self.q, dev(lse32), self.qp, self.case["scale"], self.case["G"], flags,
-                pool, a=dev(a_enc) if a_enc is not None else None, **kw)
-        K.select(self.dc, self.score, budget, recent, self.vic, self.nv, self.ws)
-        self.stats = K.compact(self.dc, self.vic, self.nv, self.fl, self.fc, self.ws,
-                               score_row=self.score)
-        torch.cuda.synchronize()
-
-    def state(self):
-        return dict(k=host(self.dc.k_pool), v=host(self.dc.v_pool), bt=host(self.dc.block_table),
-                    seq=host(self.dc.seq_len), pos=host(self.dc.pos), fl=host(self.fl),
-                    fc=int(host(self.fc)[0]), stats=host(self.stats), score=host(self.score),
-                    vic=host(self.vic), nv=host(self.nv))
 
 
 def _assert_same(a, b, seq_before):
@@ -204,29 +155,10 @@ def test_evict_matches_oracle(name, over, kind, pool, budget, recent):
     f = Run(case, free_prefix=0)
     f.fused(kind, lse32, a_enc, pool, budget, recent)
     st = f.state()
-    U = case["B"] * case["Hkv"]
-    nd = victims_agree_up_to_tolerance(st["vic"], st["nv"], ov, on, o32, case["seq_len"], budget,
-                                       recent, TOL[cfg.dtype])
-    print(f"{name}: {nd} victims differ inside the tolerance band", flush=True)
-    # the oracle's compaction of the GPU's victims, carrying the oracle's scores
-    new, ofl, ofc, ostats = oracle.compact(case, st["vic"].reshape(U, -1), st["nv"].reshape(-1),
-                                           score_row=np.nan_to_num(o32, nan=0.0),
+    # the oracle's own chain: its victims, then its compaction of them carrying its scores
+    new, ofl, ofc, ostats = oracle.compact(case, ov, on, score_row=np.nan_to_num(o32, nan=0.0),
                                            free_list=np.full(case["num_blocks"] + 8, -1, np.int32),
                                            free_count=0)
-    assert np.array_equal(st["seq"], new["seq_len"])
-    assert np.array_equal(st["bt"], new["block_table"])
-    assert st["fc"] == ofc and np.array_equal(st["fl"][:ofc], ofl[:ofc])
-    assert np.array_equal(st["stats"], ostats)
-    B, H = case["B"], case["Hkv"]
-    for b in range(B):
-        for h in range(H):
-            n2 = int(new["seq_len"][b, h])
-            assert np.array_equal(st["pos"][b, h, :n2], new["pos"][b, h, :n2])
-            for s in range(0, n2, 16):
-                blk = new["block_table"][b, h, s // 16]
-                e = min(16, n2 - s)
-                assert np.array_equal(st["k"][blk, :e], new["k_pool"][blk, :e])
-                assert np.array_equal(st["v"][blk, :e], new["v_pool"][blk, :e])
-    # the compacted score row carries the kept tokens' scores (to the score tolerance)
-    assert_scores_close(st["score"], new["score_row"].astype(np.float64), new["seq_len"],
-                        TOL[cfg.dtype], "compacted score")
+    nd = check_eviction_vs_oracle_chain(case, st, ov, on, new, ofl, ofc, ostats, o32,
+                                        TOL[cfg.dtype])
+    print(f"{name}: {nd} heads with victims differing inside the tolerance band", flush=True)

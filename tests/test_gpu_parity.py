@@ -14,8 +14,8 @@ import torch
 import kv_cache_eviction_qk_amd as K
 import oracle
 import synth
-from tests.gpu_helpers import (TOL, assert_scores_close, dev, device_cache, device_window, host,
-                               victims_agree_up_to_tolerance)
+from tests.gpu_helpers import (TOL, assert_scores_close, check_eviction_vs_oracle_chain, dev,
+                               device_cache, device_window, host)
 from tests.helpers import manual_case, rounded_window_inputs
 
 pytestmark = pytest.mark.gpu
@@ -284,18 +284,25 @@ def test_end_to_end(name, over, kinds, pool, budget, recent):
     orc, gpu, lse32, a_enc = _run_score(case, kinds, pool, want_a="drop" in kinds)
     key = {"sum": "sum", "pool": "pooled", "drop": "drop"}[kinds[0]]
     o32 = orc[key].astype(np.float32)
-    ov, on = oracle.select(np.nan_to_num(o32, nan=0.0), case["seq_len"], budget, recent)
     dc = device_cache(case)
     gv, gn = K.select(dc, dev(gpu[key]), budget, recent)
-    gv, gn = host(gv), host(gn)
-    nd = victims_agree_up_to_tolerance(gv, gn, ov, on, o32, case["seq_len"], budget, recent,
-                                       TOL[cfg.dtype])
-    print(f"{name}: {nd} victims differ inside the tolerance band", flush=True)
-    # compaction of the GPU's own victims matches the oracle's compaction of them
-    new, ofl, ofc, ostats, g = _compact_both(case, gv.reshape(case["B"] * case["Hkv"], -1),
-                                             gn.reshape(-1), with_score=False, free_prefix=0)
-    _assert_compaction_equal(case, new, ofl, ofc, ostats, g)
-    m = oracle.measure(case["seq_len"], gv.reshape(case["B"] * case["Hkv"], -1), gn.reshape(-1))
+    gvh, gnh = host(gv), host(gn)
+    # compaction of the GPU's own victims on the device
+    fl = dev(np.full(case["num_blocks"] + 8, -1, np.int32))
+    fc = dev(np.zeros(1, np.int32))
+    stats = K.compact(dc, gv, gn, fl, fc, K.new_workspace(dc))
+    torch.cuda.synchronize()
+    st = dict(k=host(dc.k_pool), v=host(dc.v_pool), bt=host(dc.block_table), seq=host(dc.seq_len),
+              pos=host(dc.pos), fl=host(fl), fc=int(host(fc)[0]), stats=host(stats), vic=gvh,
+              nv=gnh)
+    # the oracle's own chain: its scores -> its victims -> its compaction
+    ov, on = oracle.select(np.nan_to_num(o32, nan=0.0), case["seq_len"], budget, recent)
+    new, ofl, ofc, ostats = oracle.compact(case, ov, on,
+                                           free_list=np.full(case["num_blocks"] + 8, -1, np.int32))
+    nd = check_eviction_vs_oracle_chain(case, st, ov, on, new, ofl, ofc, ostats, o32,
+                                        TOL[cfg.dtype])
+    print(f"{name}: {nd} heads with victims differing inside the tolerance band", flush=True)
+    m = oracle.measure(case["seq_len"], ov, on)
     assert m["blocks_freed"] == ostats[0]
 
 
