@@ -17,7 +17,10 @@
 //           fetches them), or from the threshold the selection left in the
 //           workspace, which then also writes the victim list.
 //   gather  (persistent grid over (head, rank range) items): each thread
-//           issues all of its 16-byte K and V loads before any store.  The
+//           issues all of its 16-byte K and V loads before any store; the
+//           moved rows are stored with the nontemporal hint, so they reach
+//           HBM during this latency-bound step rather than being written
+//           back from the Infinity Cache while a later pass streams.  The
 //           first item of a head also appends the emptied tail blocks
 //           [ceil(n'/16), ceil(n/16)) to the free list in (b, h, block)
 //           order, clears their table entries, sets seq_len = n' and adds the
@@ -605,8 +608,8 @@ __global__ __launch_bounds__(kThreads) void compact_gather_kernel(const CompactA
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          st16(P.k_pool + dsto[i], kv[i]);
-          st16(P.v_pool + dsto[i], vv[i]);
+          st16_nt(P.k_pool + dsto[i], kv[i]);
+          st16_nt(P.v_pool + dsto[i], vv[i]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) P.pos[urow + rr[i]] = npos[i];

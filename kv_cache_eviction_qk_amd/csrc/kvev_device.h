@@ -28,6 +28,14 @@ __device__ __forceinline__ void ld16_to_lds(const void *g, void *lds_wave_base) 
                                    (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
 }
 __device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
+// 16-byte store with the nontemporal hint (global_store_dwordx4 ... nt): for
+// rows written once and not read again soon, so they go out to HBM now
+// instead of staying as dirty lines in the Infinity Cache, whose later
+// write-back would take bandwidth from whatever streams through next.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st16_nt(void *p, uint4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v), reinterpret_cast<u32x4_t *>(p));
+}
 
 // 16x16 tile, contraction 32, bf16 inputs, fp32 accumulate (v_mfma_f32_16x16x32_bf16).
 // A operand: lane l supplies row (l % 16), 8 consecutive contraction slots of
