@@ -50,7 +50,7 @@ size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 // all entry points; selection and compaction use disjoint parts of it, so
 // the fused call can pass the threshold from one to the other.
 struct StateLayout {
-  size_t hist, head_acc, total;
+  size_t hist, hist2, head_acc, total;
 };
 
 StateLayout state_layout(const kvev_cache *c) {
@@ -58,6 +58,7 @@ StateLayout state_layout(const kvev_cache *c) {
   const size_t units = (size_t)c->batch * c->kv_heads;
   size_t off = 0;
   L.hist = off; off = a256(off + units * kvev::kSelectBins * 4);
+  L.hist2 = off; off = a256(off + units * kvev::kSelectBins * 4);
   L.head_acc = off; off = a256(off + units * 8);
   L.total = off;
   return L;
@@ -286,6 +287,7 @@ kvev::SelHead sel_head(const kvev_cache *cache, int32_t *n_victims, int32_t budg
   kvev::SelHead h{};
   h.n_victims = n_victims;
   h.hist = reinterpret_cast<uint32_t *>(ws + S.hist);
+  h.hist2 = reinterpret_cast<uint32_t *>(ws + S.hist2);
   h.head_sel = reinterpret_cast<uint32_t *>(ws + L.head_sel);
   h.chunk_off = reinterpret_cast<uint32_t *>(ws + L.chunk_off);
   h.chunk_below = reinterpret_cast<uint32_t *>(ws + L.chunk_below);

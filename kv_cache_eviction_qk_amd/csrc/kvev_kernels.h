@@ -13,6 +13,7 @@ namespace kvev {
 struct SelHead {
   int32_t *n_victims;
   uint32_t *hist;         // state [units][2048]: top 11 key bits (zero between calls)
+  uint32_t *hist2;        // state [units][2048]: key bits 20..10 of the bucket's keys (zero between calls)
   uint32_t *head_sel;     // scratch [units][4]: T, cut slot, bucket, keys below the bucket
   uint32_t *chunk_off;    // scratch [units][chunks]: first victim index of each chunk
   uint32_t *chunk_below;  // scratch [units][chunks]: keys below the bucket per chunk

@@ -9,15 +9,21 @@
 //   collect (4096 slots of a head per 1024-thread workgroup): the bucket b
 //           of rank m from the histogram (the keys are already in flight);
 //           per 1024-slot chunk the count of keys below b (ballot counts);
-//           the (key, slot) pairs of bucket b to this workgroup's region.
-//   refine  (one 1024-thread workgroup per head): the bucket's pairs into
-//           LDS; two radix passes (key bits 20..10, then 9..0) give T and
-//           the rank of the m-th pair among the keys equal to T; rank
-//           counting among those gives the cut slot; per-chunk victim
-//           counts and their exclusive scan (each chunk's first output
-//           index); T, cut and n_victims to the workspace; the histogram is
-//           left zero for the next call.
-// A bucket with more pairs than LDS holds is re-read from the regions.
+//           the (key, slot) pairs of bucket b to this workgroup's region,
+//           and the histogram of their key bits 20..10 added into the head's
+//           second-level histogram.
+//   refine  (one 1024-thread workgroup per head): the sub-bucket of the
+//           remaining rank from the second-level histogram; one pass over
+//           the bucket's pairs counts the pairs below the sub-bucket per
+//           chunk and keeps the sub-bucket's pairs in LDS; a radix pass over
+//           key bits 9..0 gives T and the rank of the m-th pair among the
+//           keys equal to T; rank counting among those gives the cut slot;
+//           per-chunk victim counts and their exclusive scan (each chunk's
+//           first output index); T, cut and n_victims to the workspace; both
+//           histograms are left zero for the next call.
+// Concentrated score distributions put many pairs in one bucket; they are
+// streamed once, with eight loads in flight per thread.  A sub-bucket with
+// more pairs than LDS holds is re-read from the regions.
 #pragma once
 
 #include "kvev_device.h"
@@ -43,6 +49,21 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
 struct RankOut {
   uint32_t bin, below;
 };
+
+// cnt[idx] += 1 for every lane with pred, one LDS atomic per distinct idx
+// among those lanes (pairs that sit next to each other mostly share a
+// chunk, and per-lane atomics on one counter would serialise the wave).
+// Every lane of the wave must call it.
+__device__ __forceinline__ void wave_count_add(uint32_t *cnt, int idx, bool pred) {
+  uint64_t pending = __ballot(pred);
+  while (pending) {
+    const int leader = __ffsll((unsigned long long)pending) - 1;
+    const int lidx = __shfl(idx, leader);
+    const uint64_t same = __ballot(pred && idx == lidx);
+    if (lane_id() == leader) atomicAdd(&cnt[lidx], (uint32_t)__popcll(same));
+    pending &= ~same;
+  }
+}
 
 // Bin of h[0, NBINS) that holds the element of 1-based rank `rank`, and the
 // number of elements in lower bins ({0, 0} if the total is below the rank).
@@ -118,6 +139,10 @@ __device__ inline void collect_chunk(const SelHead &S, const float *row, const u
     S.head_sel[u * 4 + 2] = b;
     S.head_sel[u * 4 + 3] = L.r.below;
   }
+  // L.h becomes the histogram of key bits 20..10 over the bucket's pairs
+#pragma unroll
+  for (int q = 0; q < kSelectBins / NT; ++q) L.h[tid + q * NT] = 0;
+  __syncthreads();
   // a wave covers 256 consecutive slots: one chunk
   const int s = s0 + 4 * tid;
   const float e4[4] = {v.x, v.y, v.z, v.w};
@@ -133,6 +158,9 @@ __device__ inline void collect_chunk(const SelHead &S, const float *row, const u
     msk[e] = __ballot(in && bk == b);
     total += (uint32_t)__popcll(msk[e]);
   }
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if ((msk[e] >> lane) & 1ull) atomicAdd(&L.h[(key[e] >> 10) & 2047u], 1u);
   uint32_t base = 0;
   if (lane == 0) {
     if (below) atomicAdd(&L.cb[wv / (kSelectChunk / 256)], below);
@@ -148,6 +176,10 @@ __device__ inline void collect_chunk(const SelHead &S, const float *row, const u
   }
   __syncthreads();
   if (tid == 0) S.ccount[(size_t)u * S.nwg + c] = L.s_ncand;
+  uint32_t *h2 = S.hist2 + (size_t)u * kSelectBins;
+#pragma unroll
+  for (int q = 0; q < kSelectBins / NT; ++q)
+    if (L.h[tid + q * NT]) atomicAdd(&h2[tid + q * NT], L.h[tid + q * NT]);
   if (tid < kHistChunk / kSelectChunk) {
     const int ch = s0 / kSelectChunk + tid;
     if (ch * kSelectChunk < nc) S.chunk_below[(size_t)u * S.chunks + ch] = L.cb[tid];
@@ -160,18 +192,23 @@ struct RefineLds {
   uint32_t h[kSelectBins];
   uint32_t chunk_cnt[kSelectMaxChunks];
   uint32_t coff[kSelectMaxChunks / (kHistChunk / kSelectChunk) + 1];  // region offsets
-  uint2 cand[kHeadCand];
+  uint2 cand[kHeadCand];  // the sub-bucket's pairs
   RankOut r;
-  uint32_t s_cut, s_nt;
+  uint32_t s_cut, s_nt, s_nsub;
 };
 
 // One workgroup per head, after collect.  Requires 0 < m < nc.
 __device__ inline void refine_head(const SelHead &S, uint32_t *hist, int u, int m, int nc,
                                    RefineLds &L) {
   constexpr int NT = kSelThreads;
+  constexpr int kBatch = 8;  // pair loads in flight per thread
   const int tid = threadIdx.x, lane = lane_id();
   const int live = (nc + kSelectChunk - 1) / kSelectChunk;  // chunks with candidates
   const int nw = (nc + kHistChunk - 1) / kHistChunk;        // collect regions written
+  uint32_t *h2 = S.hist2 + (size_t)u * kSelectBins;
+  uint32_t h2v[kSelectBins / NT];
+#pragma unroll
+  for (int q = 0; q < kSelectBins / NT; ++q) h2v[q] = h2[tid + q * NT];
   const uint32_t b = S.head_sel[u * 4 + 2];
   const uint32_t need = (uint32_t)m - S.head_sel[u * 4 + 3];  // rank inside bucket b
   const uint32_t *cc = S.ccount + (size_t)u * S.nwg;
@@ -190,51 +227,89 @@ __device__ inline void refine_head(const SelHead &S, uint32_t *hist, int u, int 
     }
     if (lane == kWave - 1) L.coff[nw] = e;
   }
+#pragma unroll
+  for (int q = 0; q < kSelectBins / NT; ++q) {
+    L.h[tid + q * NT] = h2v[q];
+    h2[tid + q * NT] = 0;  // state for the next call
+  }
+  if (tid == 0) L.s_nsub = 0;
   __syncthreads();
   const int ncand = (int)L.coff[nw];
-  // pair i: its region by binary search over the offsets
-  auto pair_at = [&](int i) -> uint2 {
-    int lo = 0, hi = nw - 1;
+  // the sub-bucket: key bits 20..10 of the pair of rank `need` in bucket b
+  wg_rank_bin<kSelectBins>(L.h, need, &L.r);
+  const uint32_t pre = (b << 11) | L.r.bin;  // key >> 10 of T
+  const uint32_t need2 = need - L.r.below;
+
+  // pair i: its region by binary search over the offsets, starting from the
+  // region of this thread's previous pair (its indices only grow)
+  auto pair_at = [&](int i, int &lo) -> uint2 {
+    int hi = nw - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if ((int)L.coff[mid] <= i) lo = mid; else hi = mid - 1;
     }
     return reg[(size_t)lo * kHistChunk + (i - (int)L.coff[lo])];
   };
-  const bool staged = ncand <= kHeadCand;
-  if (staged) {
-    uint2 t[kHeadCand / NT];
+  // every pair of the bucket, kBatch loads in flight per thread
+  auto for_all = [&](auto &&f) {
+    int lo = 0;
+    for (int i0 = 0; i0 < ncand; i0 += kBatch * NT) {
+      uint2 t[kBatch];
 #pragma unroll
-    for (int q = 0; q < kHeadCand / NT; ++q) {
-      const int i = tid + q * NT;
-      if (i < ncand) t[q] = pair_at(i);
+      for (int q = 0; q < kBatch; ++q) {
+        const int i = i0 + q * NT + tid;
+        t[q] = i < ncand ? pair_at(i, lo) : make_uint2(0u, 0u);
+      }
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q)
+        if (i0 + q * NT + tid < ncand) f(t[q].x, (int)t[q].y);
     }
+  };
+  // ---- one pass over the bucket: pairs below the sub-bucket are victims
+  // (counted per chunk); the sub-bucket's pairs go to LDS (wave-uniform
+  // loop: the counts and appends are aggregated per wave)
+  {
+    int lo = 0;
+    for (int i0 = 0; i0 < ncand; i0 += kBatch * NT) {
+      uint2 t[kBatch];
 #pragma unroll
-    for (int q = 0; q < kHeadCand / NT; ++q) {
-      const int i = tid + q * NT;
-      if (i < ncand) L.cand[i] = t[q];
+      for (int q = 0; q < kBatch; ++q) {
+        const int i = i0 + q * NT + tid;
+        t[q] = i < ncand ? pair_at(i, lo) : make_uint2(0u, 0u);
+      }
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        const bool valid = i0 + q * NT + tid < ncand;
+        const uint32_t p = t[q].x >> 10;
+        wave_count_add(L.chunk_cnt, (int)t[q].y / kSelectChunk, valid && p < pre);
+        const bool sub = valid && p == pre;
+        const uint64_t sm = __ballot(sub);
+        if (sm) {
+          uint32_t base = 0;
+          if (lane == 0) base = atomicAdd(&L.s_nsub, (uint32_t)__popcll(sm));
+          base = __shfl(base, 0);
+          const uint32_t j = base + (uint32_t)ballot_prefix(sm);
+          if (sub && j < (uint32_t)kHeadCand) L.cand[j] = t[q];
+        }
+      }
     }
   }
-  for (int i = tid; i < kSelectBins; i += NT) L.h[i] = 0;
+  for (int i = tid; i < 1024; i += NT) L.h[i] = 0;
   __syncthreads();
-  auto for_cand = [&](auto &&f) {
-    for (int i = tid; i < ncand; i += NT) {
-      const uint2 c = staged ? L.cand[i] : pair_at(i);
-      f(c.x, (int)c.y);
+  const int nsub = (int)L.s_nsub;
+  const bool in_lds = nsub <= kHeadCand;
+  auto for_sub = [&](auto &&f) {
+    if (in_lds) {
+      for (int i = tid; i < nsub; i += NT) f(L.cand[i].x, (int)L.cand[i].y);
+    } else {
+      for_all([&](uint32_t k, int s) {
+        if ((k >> 10) == pre) f(k, s);
+      });
     }
   };
 
-  // ---- radix passes over the bucket: bits 20..10, then 9..0
-  for_cand([&](uint32_t k, int) { atomicAdd(&L.h[(k >> 10) & 2047u], 1u); });
-  __syncthreads();
-  wg_rank_bin<2048>(L.h, need, &L.r);
-  const uint32_t pre = (b << 11) | L.r.bin;  // key >> 10 of T
-  const uint32_t need2 = need - L.r.below;
-  for (int i = tid; i < 1024; i += NT) L.h[i] = 0;
-  __syncthreads();
-  for_cand([&](uint32_t k, int) {
-    if ((k >> 10) == pre) atomicAdd(&L.h[k & 1023u], 1u);
-  });
+  // ---- radix pass over the sub-bucket: key bits 9..0
+  for_sub([&](uint32_t k, int) { atomicAdd(&L.h[k & 1023u], 1u); });
   __syncthreads();
   wg_rank_bin<1024>(L.h, need2, &L.r);
   const uint32_t T = (pre << 10) | L.r.bin;
@@ -249,7 +324,7 @@ __device__ inline void refine_head(const SelHead &S, uint32_t *hist, int u, int 
       int *tie = reinterpret_cast<int *>(L.h);
       if (tid == 0) L.s_nt = 0;
       __syncthreads();
-      for_cand([&](uint32_t k, int s) {
+      for_sub([&](uint32_t k, int s) {
         if (k == T) tie[atomicAdd(&L.s_nt, 1u)] = s;
       });
       __syncthreads();
@@ -268,7 +343,7 @@ __device__ inline void refine_head(const SelHead &S, uint32_t *hist, int u, int 
         const int shift = 24 - 8 * pass;
         for (int i = tid; i < 256; i += NT) L.h[i] = 0;
         __syncthreads();
-        for_cand([&](uint32_t k, int s) {
+        for_sub([&](uint32_t k, int s) {
           if (k == T && ((uint32_t)s & sm) == sp) atomicAdd(&L.h[((uint32_t)s >> shift) & 255u], 1u);
         });
         __syncthreads();
@@ -282,10 +357,19 @@ __device__ inline void refine_head(const SelHead &S, uint32_t *hist, int u, int 
     }
   }
 
-  // ---- victims per chunk, their offsets, the head's threshold
-  for_cand([&](uint32_t k, int s) {
-    if (k < T || (k == T && s <= cut)) atomicAdd(&L.chunk_cnt[s / kSelectChunk], 1u);
-  });
+  // ---- victims of the sub-bucket per chunk, the offsets, the threshold
+  if (in_lds) {
+    for (int i0 = 0; i0 < nsub; i0 += NT) {  // wave-uniform
+      const int i = i0 + tid;
+      const uint2 c2 = i < nsub ? L.cand[i] : make_uint2(0u, 0u);
+      const bool v = i < nsub && (c2.x < T || (c2.x == T && (int)c2.y <= cut));
+      wave_count_add(L.chunk_cnt, (int)c2.y / kSelectChunk, v);
+    }
+  } else {
+    for_sub([&](uint32_t k, int s) {
+      if (k < T || (k == T && s <= cut)) atomicAdd(&L.chunk_cnt[s / kSelectChunk], 1u);
+    });
+  }
   __syncthreads();
   if (tid < kWave) {  // one wave: exclusive scan of the chunk counts
     const int per = (live + kWave - 1) / kWave;
