@@ -12,6 +12,8 @@
 //     a.v on the same MFMA tiles, ||v||^2 on the VALU,
 //     ||a - v||^2 = ||a||^2 - 2 a.v + ||v||^2  (clamped at 0)
 //     term = p / (1 - p) * sqrt(||a - v||^2)     (+inf when p >= 1)
+// (v_rcp_f32 and v_sqrt_f32, 1 ulp each: the correctly rounded library
+// square root costs about a dozen more VALU instructions per element)
 // ([DROP] "fused Triton kernels": the expansion lets each value tile be read
 // once).  The SnapKV max-pool needs r neighbours on each side: a tile also
 // scores ceil(r/16) halo blocks on either side, so the pool is finished in
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
             if constexpr (DROP) {
               const float X = fmaxf(fmaf(-2.f, av[i][e], Ae[e] + vn2[i]), 0.f);
               const float t = (x >= 0.f) ? __builtin_inff()
-                                         : p * __builtin_amdgcn_rcpf(1.f - p) * __builtin_sqrtf(X);
+                                         : p * __builtin_amdgcn_rcpf(1.f - p) * __builtin_amdgcn_sqrtf(X);
               pdrop[i] += t;
             }
           }
@@ -276,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
             if constexpr (DROP) {
               const float X = fmaxf(fmaf(-2.f, av[i][e], Ae[e] + vn2[i]), 0.f);
               float t = (x >= 0.f) ? __builtin_inff()
-                                   : p * __builtin_amdgcn_rcpf(1.f - p) * __builtin_sqrtf(X);
+                                   : p * __builtin_amdgcn_rcpf(1.f - p) * __builtin_amdgcn_sqrtf(X);
               pdrop[i] += live ? t : 0.f;
             }
           }
