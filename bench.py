@@ -216,6 +216,9 @@ def main():
 
     st = stats.cpu().numpy().tolist()
     nv = n_victims.cpu().numpy()
+    # block-level waste of the pass's eviction, by kvev_measure on the last
+    # step's victims: naive (holes left in place) vs after compaction
+    waste = K.measure(pristine.seq_len, victims, n_victims)
 
     # ---- the scoring kernel alone (kvev_score, same launch configuration):
     # `steps` back-to-back launches between two HIP events on their stream,
@@ -295,6 +298,8 @@ def main():
         "separate_calls_ms": {"score": t_score, "select": t_select, "compact": t_compact},
         "wall_s": wall,
         "blocks_freed_per_pass": int(st[0]),
+        "block_waste": {k: waste[k] for k in ("F_naive", "F_after", "frac_le_half_naive",
+                                              "frac_le_half_after")},
         "rows_moved_per_pass": rows_moved,
         "roofline": {"kernel": "score_kernel (kvev_score)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -54,7 +54,7 @@ extern "C" {
 #endif
 
 #define KVEV_BLOCK_SIZE 16
-#define KVEV_ABI_VERSION 2
+#define KVEV_ABI_VERSION 3
 
 typedef enum {
   KVEV_OK = 0,
@@ -206,6 +206,32 @@ int kvev_evict(const kvev_cache *cache, const kvev_window *win, int32_t flags,
                int32_t *victims, int32_t *n_victims, int32_t *free_list, int32_t *free_count,
                int32_t free_capacity, int64_t *stats, void *workspace, size_t ws_bytes,
                void *stream);
+
+/*
+ * kvev_measure -- block-level waste of an eviction ([VTOK] section 2, Eq. 1
+ * and Fig. 1: F = 1 - live tokens / (blocks * 16), and the share of blocks at
+ * half use or less).
+ *
+ * For every KV head u with a consistent record (0 <= n <= max_slots, 0 <= m
+ * <= n, where n = seq_len_before[u] and m = n_victims[u]):
+ *   before compaction ("naive" eviction, emptied slots stay in their blocks)
+ *   block b of [0, ceil(n/16)) holds min(16, n - 16b) slots, minus the victims
+ *   among them; after compaction the n' = n - m kept tokens fill
+ *   ceil(n'/16) blocks from the front.
+ * out: int64[6] on the device = {live tokens (sum of n'), blocks before,
+ * blocks after, blocks before with 2 * live <= 16, blocks after with
+ * 2 * live <= 16, blocks freed}.  F_naive = 1 - out[0] / (16 * out[1]),
+ * F_after = 1 - out[0] / (16 * out[2]).  Heads with an inconsistent record
+ * add nothing.  seq_len_before: int32 [units] (the lengths before
+ * kvev_compact or kvev_evict); victims: int32 [units][max_slots], ascending
+ * per head as kvev_select writes them; n_victims: int32 [units].  All device
+ * pointers; the call only enqueues (two kernels) on `stream`.
+ * Errors: KVEV_EINVAL for NULL pointers, units < 0 or max_slots not a
+ * positive multiple of 16.
+ */
+int kvev_measure(const int32_t *seq_len_before, const int32_t *victims,
+                 const int32_t *n_victims, int32_t units, int32_t max_slots, int64_t *out,
+                 void *stream);
 
 /*
  * kvev_window_attn -- helper outside the eviction step: the log-sum-exp and

@@ -29,9 +29,9 @@ SUM, POOL, DROP, ACCUMULATE = 1, 2, 4, 8
 BLOCK_SIZE = 16
 
 # the functions include/kvev.h declares
-EXPORTS = ("kvev_score", "kvev_select", "kvev_compact", "kvev_evict", "kvev_window_attn",
-           "kvev_workspace_bytes", "kvev_strerror", "kvev_abi_version")
-ABI_VERSION = 2
+EXPORTS = ("kvev_score", "kvev_select", "kvev_compact", "kvev_evict", "kvev_measure",
+           "kvev_window_attn", "kvev_workspace_bytes", "kvev_strerror", "kvev_abi_version")
+ABI_VERSION = 3
 
 
 class KvevError(RuntimeError):
@@ -76,6 +76,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kvev_compact.argtypes = [P, P, P, P, P, P, i32, P, P, sz, P]
     L.kvev_evict.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P, P, i32, P, P, sz, P]
     L.kvev_window_attn.argtypes = [P, P, P, P, P, sz, P]
+    L.kvev_measure.argtypes = [P, P, P, i32, i32, P, P]
     L.kvev_workspace_bytes.argtypes = [P, i32, i32]
     L.kvev_workspace_bytes.restype = sz
     L.kvev_strerror.argtypes = [ctypes.c_int]
@@ -307,6 +308,35 @@ def evict(cache: Cache, q: torch.Tensor, lse: torch.Tensor, q_pos: torch.Tensor,
                       _ptr(workspace), workspace.numel(), _stream(stream))
     _check(rc, "kvev_evict")
     return stats
+
+
+def measure(seq_len_before: torch.Tensor, victims: torch.Tensor, n_victims: torch.Tensor,
+            out: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """kvev_measure: block-level waste of an eviction.  seq_len_before and
+    n_victims: int32 [B, Hkv]; victims: int32 [B, Hkv, max_slots].  Returns the
+    six integer sums (synchronising to read them) and the ratios derived from
+    them: F_naive, F_after, frac_le_half_naive, frac_le_half_after."""
+    L = load_library()
+    units = seq_len_before.numel()
+    _need(seq_len_before, "seq_len_before", torch.int32, units)
+    _need(n_victims, "n_victims", torch.int32, units)
+    _need(victims, "victims", torch.int32)
+    if units == 0 or victims.numel() % units:
+        raise ValueError("victims must hold max_slots entries per head")
+    max_slots = victims.numel() // units
+    if out is None:
+        out = torch.empty(6, dtype=torch.int64, device=victims.device)
+    _need(out, "out", torch.int64, 6)
+    rc = L.kvev_measure(_ptr(seq_len_before), _ptr(victims), _ptr(n_victims), units, max_slots,
+                        _ptr(out), _stream(stream))
+    _check(rc, "kvev_measure")
+    live, bn, ba, hn, ha, freed = (int(x) for x in out.cpu().tolist())
+    return dict(live_tokens=live, blocks_naive=bn, blocks_after=ba, le_half_naive=hn,
+                le_half_after=ha, blocks_freed=freed,
+                F_naive=1.0 - live / (bn * 16.0) if bn else 0.0,
+                F_after=1.0 - live / (ba * 16.0) if ba else 0.0,
+                frac_le_half_naive=hn / bn if bn else 0.0,
+                frac_le_half_after=ha / ba if ba else 0.0)
 
 
 def window_attn(cache: Cache, q: torch.Tensor, q_pos: torch.Tensor, scale: float, group: int,

@@ -147,6 +147,24 @@ int check_window(const kvev_cache *c, const kvev_window *w) {
 
 extern "C" {
 
+int kvev_measure(const int32_t *seq_len_before, const int32_t *victims,
+                 const int32_t *n_victims, int32_t units, int32_t max_slots, int64_t *out,
+                 void *stream) {
+  if (!seq_len_before || !victims || !n_victims || !out || units < 0 || max_slots <= 0 ||
+      max_slots % KVEV_BLOCK_SIZE != 0)
+    return KVEV_EINVAL;
+  if ((int64_t)max_slots / KVEV_BLOCK_SIZE > (int64_t)65535 * 256 || units > 65535)
+    return KVEV_EUNSUPPORTED;
+  kvev::MeasureArgs a{};
+  a.seq_len_before = seq_len_before;
+  a.victims = victims;
+  a.n_victims = n_victims;
+  a.out = out;
+  a.units = units;
+  a.max_slots = max_slots;
+  return map_err(kvev::launch_measure(a, static_cast<hipStream_t>(stream)));
+}
+
 int kvev_abi_version(void) { return KVEV_ABI_VERSION; }
 
 const char *kvev_strerror(int status) {

@@ -76,6 +76,13 @@ struct CompactArgs {
   int32_t rows_cap;             // kept rows per head are at most this (sizes the gather grid)
 };
 
+struct MeasureArgs {
+  const int32_t *seq_len_before, *victims, *n_victims;
+  int64_t *out;  // [6]
+  int32_t units, max_slots;
+};
+hipError_t launch_measure(const MeasureArgs &a, hipStream_t s);
+
 struct WindowAttnArgs {
   const uint8_t *k_pool, *v_pool;
   const int32_t *block_table, *seq_len, *pos;

@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
     assert set(names) == set(K.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvev_abi_version() == K.ABI_VERSION == 2
+    assert L.kvev_abi_version() == K.ABI_VERSION == 3
     for code in (0, -1, -2, -3, -4):
         assert K.strerror(code)
 
@@ -229,3 +229,14 @@ def test_misaligned_score_refused():
     ws = L.kvev_workspace_bytes(ctypes.byref(c), 1, 1)
     assert L.kvev_select(ctypes.byref(c), FAKE + 4, 8, 2, FAKE, FAKE, FAKE, ws, None) == K.EINVAL
     assert evict(c, window(), ptrs={"score": FAKE + 8}) == K.EINVAL
+
+
+def test_measure_refusals():
+    L = K.load_library()
+    args = [FAKE, FAKE, FAKE, 4, 64, FAKE, None]
+    for i in (0, 1, 2, 5):
+        a = list(args); a[i] = None
+        assert L.kvev_measure(*a) == K.EINVAL
+    for units, ms in ((-1, 64), (4, 0), (4, 40)):  # max_slots: a positive multiple of 16
+        a = list(args); a[3] = units; a[4] = ms
+        assert L.kvev_measure(*a) == K.EINVAL

@@ -352,3 +352,38 @@ def test_inconsistent_seq_len_is_flagged_not_used():
     scores = dev(np.ones((1, 2, case["max_blocks"] * 16), np.float32))
     _, nv = K.select(dc, scores, 100, 8)
     assert host(nv).tolist() == [[300, -1]]
+
+
+# ------------------------------------------------------------ measurement
+
+
+@pytest.mark.parametrize("pattern", ["random", "first_only", "every_other", "none", "keep_recent",
+                                     "tail", "sparse"])
+def test_measure_matches_oracle(pattern):
+    """kvev_measure against the oracle's Eq. 1 waste and half-use shares on
+    test-made victim lists (ragged heads, heads of 0, 1, 16 and 17 tokens)."""
+    seq = np.array([[3001, 0, 1, 16], [17, 2048, 777, 4099]], np.int32)
+    ms = 4112
+    vic, nv = _pattern_victims(seq, ms, pattern, seed=3)
+    g = K.measure(dev(seq), dev(vic.reshape(2, 4, ms)), dev(nv.reshape(2, 4)))
+    o = oracle.measure(seq, vic, nv)
+    for k in ("blocks_naive", "blocks_after", "live_tokens", "blocks_freed"):
+        assert g[k] == int(o[k]), k
+    for k in ("F_naive", "F_after", "frac_le_half_naive", "frac_le_half_after"):
+        assert g[k] == o[k], k
+
+
+def test_measure_full_size_block_evict_layer():
+    """One 64000-token layer of the 70B GQA shape (B16, 8 KV heads): half of
+    every head evicted at random, as the block-evict workload does."""
+    B, H, L = 16, 8, 64000
+    ms = 4000 * 16
+    seq = np.full((B, H), L, np.int32)
+    vic, nv = _pattern_victims(seq, ms, "random", seed=5)
+    g = K.measure(dev(seq), dev(vic.reshape(B, H, ms)), dev(nv.reshape(B, H)))
+    o = oracle.measure(seq, vic, nv)
+    assert g["blocks_freed"] == int(o["blocks_freed"]) == B * H * (4000 - 2000)
+    for k in ("blocks_naive", "blocks_after", "live_tokens"):
+        assert g[k] == int(o[k]), k
+    for k in ("F_naive", "F_after", "frac_le_half_naive", "frac_le_half_after"):
+        assert g[k] == o[k], k
