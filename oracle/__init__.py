@@ -66,7 +66,10 @@ def lib():
         L.orc_select.argtypes = [P, P, i32, i32, i32, i32, P, P]
         L.orc_compact.argtypes = [P, P, i32, i32, P, P, P, P, i32, i32, P, P, P, P, i32, P]
         L.orc_measure.argtypes = [P, P, P, i32, i32, P]
-        for f in (L.orc_lse_a, L.orc_score, L.orc_select, L.orc_compact, L.orc_measure):
+        L.orc_h2o_step.argtypes = [P, P, i32, i32, P, P, P, P, i32, i32, i32, i32, i32, P, P, P,
+                                   P, ctypes.c_double, i32, i32, P, P, P]
+        for f in (L.orc_lse_a, L.orc_score, L.orc_select, L.orc_compact, L.orc_measure,
+                  L.orc_h2o_step):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -186,3 +189,36 @@ def measure(seq_len_before: np.ndarray, victims: np.ndarray, n_victims: np.ndarr
     keys = ("F_naive", "F_after", "frac_le_half_naive", "frac_le_half_after", "blocks_naive",
             "blocks_after", "live_tokens", "blocks_freed")
     return dict(zip(keys, out.tolist()))
+
+
+def h2o_step(state: dict, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+             t_pos: np.ndarray, budget: int, recent: int, free_list: Optional[np.ndarray] = None,
+             free_count: int = 0):
+    """One H2O decode step on a COPY of `state` (a case dict plus 'score', the
+    running fp32 score [B,Hkv,max_slots]).  q [B,Hq,D], k_new / v_new
+    [B,Hkv,D] in the cache dtype, t_pos [B].  Returns (new_state, evicted_pos
+    [B,Hkv], free_list, free_count)."""
+    new = dict(state)
+    for k in ("k_pool", "v_pool", "block_table", "seq_len", "pos"):
+        new[k] = state[k].copy()
+    new["score"] = np.ascontiguousarray(state["score"], dtype=np.float32).copy()
+    B, Hkv = state["B"], state["Hkv"]
+    if free_list is None:
+        free_list = np.full(max(1, state["num_blocks"]), -1, np.int32)
+    free_list = np.ascontiguousarray(free_list, dtype=np.int32).copy()
+    fc = np.array([free_count], np.int32)
+    ev = np.zeros((B, Hkv), np.int32)
+    edt = np.uint16 if state["dtype"] == "bf16" else np.float32
+    rc = lib().orc_h2o_step(_p(new["k_pool"]), _p(new["v_pool"]),
+                            1 if state["dtype"] == "bf16" else 0, state["D"],
+                            _p(new["block_table"]), _p(new["seq_len"]), _p(new["pos"]),
+                            _p(new["score"]), B, Hkv, state["max_blocks"], state["num_blocks"],
+                            state["G"], _p(np.ascontiguousarray(q, dtype=edt)),
+                            _p(np.ascontiguousarray(k_new, dtype=edt)),
+                            _p(np.ascontiguousarray(v_new, dtype=edt)),
+                            _p(np.ascontiguousarray(t_pos, dtype=np.int32)), float(state["scale"]),
+                            budget, recent, _p(free_list), _p(fc), _p(ev))
+    if rc != 0:
+        raise ValueError(f"oracle h2o_step refused the arguments (rc={rc})")
+    return new, ev, free_list, int(fc[0])
+

@@ -406,3 +406,150 @@ int orc_measure(const int32_t *seq_len_before, const int32_t *victims, const int
   out[7] = blocks_naive - blocks_after;
   return 0;
 }
+
+/* ----------------------------------------------------- H2O decode step */
+/*
+ * [H2O] "Step-by-Step Eviction Lifecycle": the new token's query attends to
+ * the cached tokens and to itself; the attention weights, summed over the G
+ * query heads of the KV head (GQA), are added to the running scores; if the
+ * cache holds more tokens than the budget, the token with the smallest
+ * running score outside the recent window is pruned.  [H2O] "PagedAttention
+ * Memory Integration": the pruned token's slot is overwritten in place by the
+ * new token, so the cache never grows past the budget.  The recent window is
+ * the `recent` most recent positions t - recent + 1 .. t; ties on the score
+ * evict the lower position.  Heads are processed in (b, h) order, so the
+ * blocks taken from the free list (top of the stack first) go to the heads in
+ * that order.
+ */
+static void copy_row(void *pool, int64_t row, const void *src, int64_t row_bytes) {
+  memcpy((char *)pool + row * row_bytes, src, (size_t)row_bytes);
+}
+
+int orc_h2o_step(void *k_pool, void *v_pool, int32_t is_bf16, int32_t head_dim,
+                 int32_t *block_table, int32_t *seq_len, int32_t *pos, float *score,
+                 int32_t batch, int32_t kv_heads, int32_t max_blocks, int32_t num_blocks,
+                 int32_t group, const void *q, const void *k_new, const void *v_new,
+                 const int32_t *t_pos, double scale, int32_t budget, int32_t recent,
+                 int32_t *free_list, int32_t *free_count, int32_t *evicted_pos) {
+  if (!k_pool || !v_pool || !block_table || !seq_len || !pos || !score || !q || !k_new || !v_new ||
+      !t_pos || !free_list || !free_count || !evicted_pos)
+    return -1;
+  if (group < 1 || budget <= 0 || recent < 0 || recent >= budget) return -1;
+  if (budget > max_blocks * 16) return -1;
+  const int64_t D = head_dim, G = group, max_slots = (int64_t)max_blocks * 16;
+  const int64_t row_bytes = D * (is_bf16 ? 2 : 4);
+  double *s = (double *)malloc(sizeof(double) * (size_t)(G * (budget + 1)));
+  double *lse = (double *)malloc(sizeof(double) * (size_t)G);
+  for (int64_t u = 0; u < (int64_t)batch * kv_heads; ++u) {
+    const int64_t b = u / kv_heads, h = u % kv_heads;
+    const int64_t n = seq_len[u], t = t_pos[b];
+    int32_t *bt = block_table + u * max_blocks;
+    int32_t *ps = pos + u * max_slots;
+    float *sc = score + u * max_slots;
+    if (n < 0 || n > budget) {
+      evicted_pos[u] = -2;
+      continue;
+    }
+    int bad = 0;
+    for (int64_t lb = 0; lb < (n + 15) / 16; ++lb)
+      if (bt[lb] < 0 || bt[lb] >= num_blocks) bad = 1;
+    const int need_block = n < budget && n % 16 == 0 && bt[n / 16] < 0;
+    if (!need_block && n < budget && bt[n / 16] >= num_blocks) bad = 1;
+    if (bad) {
+      evicted_pos[u] = -4;
+      continue;
+    }
+    if (need_block) {
+      if (*free_count <= 0) {
+        evicted_pos[u] = -3;
+        continue;
+      }
+      const int32_t blk = free_list[*free_count - 1];
+      if (blk < 0 || blk >= num_blocks) {
+        evicted_pos[u] = -4;
+        continue;
+      }
+      --*free_count;
+      bt[n / 16] = blk;
+    }
+    /* logits of the G query rows: cached tokens (slot j), then the new token (index n) */
+    const char *knew = (const char *)k_new + u * row_bytes;
+    for (int64_t g = 0; g < G; ++g) {
+      const int64_t qrow = (b * kv_heads + h) * G + g;
+      double mx = -INFINITY;
+      for (int64_t j = 0; j <= n; ++j) {
+        double acc = 0.0;
+        if (j < n && ps[j] > t) {
+          s[g * (budget + 1) + j] = -INFINITY; /* a later position is not attended */
+          continue;
+        }
+        const int64_t prow = j < n ? (int64_t)bt[j / 16] * 16 + j % 16 : -1;
+        for (int64_t d = 0; d < D; ++d) {
+          const double kd = j < n ? widen(k_pool, is_bf16, prow * D + d) : widen(knew, is_bf16, d);
+          acc += widen(q, is_bf16, qrow * D + d) * kd;
+        }
+        s[g * (budget + 1) + j] = scale * acc;
+        if (s[g * (budget + 1) + j] > mx) mx = s[g * (budget + 1) + j];
+      }
+      double z = 0.0;
+      for (int64_t j = 0; j <= n; ++j) z += exp(s[g * (budget + 1) + j] - mx);
+      lse[g] = mx + log(z);
+    }
+    /* the running scores after this step's attention (g ascending) */
+    float s_new;
+    {
+      double pn = 0.0;
+      for (int64_t g = 0; g < G; ++g) pn += exp(s[g * (budget + 1) + n] - lse[g]);
+      s_new = (float)pn;
+    }
+    for (int64_t j = 0; j < n; ++j) {
+      double pj = 0.0;
+      for (int64_t g = 0; g < G; ++g) pj += exp(s[g * (budget + 1) + j] - lse[g]);
+      sc[j] = (float)((double)sc[j] + pj);
+    }
+    int64_t dst;
+    if (n < budget) {
+      dst = n;
+      seq_len[u] = (int32_t)(n + 1);
+      evicted_pos[u] = -1;
+    } else {
+      /* argmin of (score, position) over the tokens outside the recent window */
+      int64_t best = -2; /* -2: none yet, -1: the new token, >= 0: a slot */
+      float bv = 0.f;
+      int64_t bp = 0;
+      for (int64_t j = 0; j <= n; ++j) {
+        const int64_t pj = j < n ? ps[j] : t;
+        if (t - pj < recent) continue;
+        const float v = j < n ? sc[j] : s_new;
+        const cand a = {v, 0}, c = {bv, 0};
+        int less;
+        if (best == -2) {
+          less = 1;
+        } else {
+          const int cmp = cand_cmp(&a, &c); /* value order, NaN above every number */
+          less = cmp < 0 || (cmp == 0 && pj < bp);
+        }
+        if (less) {
+          best = j < n ? j : -1;
+          bv = v;
+          bp = pj;
+        }
+      }
+      if (best == -1) {
+        evicted_pos[u] = (int32_t)t; /* the new token itself is dropped */
+        continue;
+      }
+      dst = best;
+      evicted_pos[u] = ps[dst];
+    }
+    const int64_t row = (int64_t)bt[dst / 16] * 16 + dst % 16;
+    copy_row(k_pool, row, knew, row_bytes);
+    copy_row(v_pool, row, (const char *)v_new + u * row_bytes, row_bytes);
+    ps[dst] = (int32_t)t;
+    sc[dst] = s_new;
+  }
+  free(lse);
+  free(s);
+  return 0;
+}
+

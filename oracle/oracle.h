@@ -83,6 +83,27 @@ int orc_compact(void *k_pool, void *v_pool, int32_t elem_bytes, int32_t head_dim
 int orc_measure(const int32_t *seq_len_before, const int32_t *victims, const int32_t *n_victims,
                 int32_t units, int32_t max_slots, double *out);
 
+/* One H2O decode step of every KV head ([H2O] "Step-by-Step Eviction
+ * Lifecycle" and "PagedAttention Memory Integration").  The new token of
+ * sequence b sits at position t_pos[b]; its key and value k_new / v_new are
+ * [batch][kv_heads][head_dim] and its G query rows q [batch][kv_heads*G][head_dim]
+ * (cache dtype).  The query attends to every cached token with pos <= t and to
+ * itself; score [batch][kv_heads][max_blocks*16] is the running fp32 score.
+ * Below the budget the token is appended (a block popped from the free list
+ * when its logical block has none); at the budget the smallest (score, pos)
+ * among the tokens at least `recent` positions older than t (the new token
+ * included when recent == 0) is evicted and the new token overwrites its
+ * slot.  evicted_pos[u] = -1 (appended), the evicted position (t when the
+ * new token itself was dropped), or -2 (n < 0 or n > budget), -3 (no free
+ * block), -4 (block id out of range): on a negative code other than -1 the
+ * head is left unchanged.  Returns 0, or -1 on invalid arguments. */
+int orc_h2o_step(void *k_pool, void *v_pool, int32_t is_bf16, int32_t head_dim,
+                 int32_t *block_table, int32_t *seq_len, int32_t *pos, float *score,
+                 int32_t batch, int32_t kv_heads, int32_t max_blocks, int32_t num_blocks,
+                 int32_t group, const void *q, const void *k_new, const void *v_new,
+                 const int32_t *t_pos, double scale, int32_t budget, int32_t recent,
+                 int32_t *free_list, int32_t *free_count, int32_t *evicted_pos);
+
 #ifdef __cplusplus
 }
 #endif
