@@ -41,7 +41,8 @@
  * that head lives in physical row
  *     block_table[b][h][s / 16] * 16 + s % 16          ([VTOK] section 3.4, Eq. 2)
  * seq_len[b][h] = n live slots; pos[b][h][s] = original token position of slot
- * s.  Slots are always in ascending position order (compaction keeps it).
+ * s.  Slots are in ascending position order (compaction keeps it), except
+ * after kvev_h2o_step, which places each new token in the slot it frees.
  */
 #ifndef KVEV_H
 #define KVEV_H
@@ -54,7 +55,7 @@ extern "C" {
 #endif
 
 #define KVEV_BLOCK_SIZE 16
-#define KVEV_ABI_VERSION 3
+#define KVEV_ABI_VERSION 4
 
 typedef enum {
   KVEV_OK = 0,
@@ -232,6 +233,48 @@ int kvev_evict(const kvev_cache *cache, const kvev_window *win, int32_t flags,
 int kvev_measure(const int32_t *seq_len_before, const int32_t *victims,
                  const int32_t *n_victims, int32_t units, int32_t max_slots, int64_t *out,
                  void *stream);
+
+/*
+ * kvev_h2o_step -- one H2O decode step of every KV head ([H2O] "Step-by-Step
+ * Eviction Lifecycle"; "PagedAttention Memory Integration" for the in-place
+ * overwrite).  Sequence b's new token sits at position t_pos[b].  For each KV
+ * head u = (b, h) with n = seq_len[u] tokens:
+ *   - the token's G query rows attend to every cached token with pos <= t
+ *     and to the token itself: p_g,j = exp(scale * q_g.k_j - lse_g), lse_g
+ *     the log-sum-exp over those keys (computed here, fp32);
+ *   - score[u][j] += sum_g p_g,j for each cached slot j (g ascending, fp32),
+ *     and the new token's score is sum_g p_g,new;
+ *   - if n < budget the token is appended at slot n (seq_len becomes n + 1);
+ *     when slot n opens a logical block whose table entry is -1, one block
+ *     is taken from the top of the free list (free_list[free_count - 1],
+ *     free_count decremented atomically; heads taking blocks in the same call
+ *     get them in an unspecified order);
+ *   - if n == budget, among the cached tokens with t - pos >= recent_window
+ *     (and the new token itself when recent_window == 0) the one with the
+ *     smallest score is pruned, ties to the lower position (scores compared
+ *     as numbers, -0 == +0, NaN above every number); the new token's K, V,
+ *     position and score overwrite the pruned slot.  If the new token itself
+ *     is the smallest it is dropped and the cache keeps its tokens.
+ * Slot order then no longer follows position order: do not pool (KVEV_POOL)
+ * or compact such a cache expecting positional neighbours.
+ * q: [batch][kv_heads*group][head_dim], k_new / v_new:
+ * [batch][kv_heads][head_dim], all in the cache dtype; t_pos: int32 [batch];
+ * score: fp32 [batch][kv_heads][max_blocks*16], the running scores (read and
+ * written); evicted_pos: int32 [batch][kv_heads] out = -1 (appended), the
+ * pruned token's position (t when the new token was dropped), or, with the
+ * head left unchanged, -2 (seq_len < 0 or > budget), -3 (free list empty),
+ * -4 (a block id of the head, or the one taken from the free list, outside
+ * [0, num_blocks); a bad free-list entry stays taken).  Device pointers; one
+ * kernel on `stream`; no workspace.
+ * Errors: KVEV_EINVAL for NULL pointers, a bad cache, group < 1,
+ * budget <= 0 or above max_blocks * 16, recent_window < 0 or >= budget;
+ * KVEV_EUNSUPPORTED for group > 16, budget > 4096 or group * budget (rounded
+ * up to 16) > 16384.
+ */
+int kvev_h2o_step(const kvev_cache *cache, const void *q, const void *k_new, const void *v_new,
+                  const int32_t *t_pos, int32_t group, float scale, float *score,
+                  int32_t budget, int32_t recent_window, int32_t *free_list,
+                  int32_t *free_count, int32_t *evicted_pos, void *stream);
 
 /*
  * kvev_window_attn -- helper outside the eviction step: the log-sum-exp and

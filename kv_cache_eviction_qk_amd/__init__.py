@@ -30,8 +30,9 @@ BLOCK_SIZE = 16
 
 # the functions include/kvev.h declares
 EXPORTS = ("kvev_score", "kvev_select", "kvev_compact", "kvev_evict", "kvev_measure",
-           "kvev_window_attn", "kvev_workspace_bytes", "kvev_strerror", "kvev_abi_version")
-ABI_VERSION = 3
+           "kvev_h2o_step", "kvev_window_attn", "kvev_workspace_bytes", "kvev_strerror",
+           "kvev_abi_version")
+ABI_VERSION = 4
 
 
 class KvevError(RuntimeError):
@@ -77,13 +78,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kvev_evict.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P, P, i32, P, P, sz, P]
     L.kvev_window_attn.argtypes = [P, P, P, P, P, sz, P]
     L.kvev_measure.argtypes = [P, P, P, i32, i32, P, P]
+    L.kvev_h2o_step.argtypes = [P, P, P, P, P, i32, ctypes.c_float, P, i32, i32, P, P, P, P]
     L.kvev_workspace_bytes.argtypes = [P, i32, i32]
     L.kvev_workspace_bytes.restype = sz
     L.kvev_strerror.argtypes = [ctypes.c_int]
     L.kvev_strerror.restype = ctypes.c_char_p
     L.kvev_abi_version.argtypes = []
     for f in (L.kvev_score, L.kvev_select, L.kvev_compact, L.kvev_evict, L.kvev_window_attn,
-              L.kvev_abi_version):
+              L.kvev_measure, L.kvev_h2o_step, L.kvev_abi_version):
         f.restype = ctypes.c_int
     if L.kvev_abi_version() != ABI_VERSION:
         raise ImportError(f"{path} has ABI version {L.kvev_abi_version()}, expected "
@@ -337,6 +339,35 @@ def measure(seq_len_before: torch.Tensor, victims: torch.Tensor, n_victims: torc
                 F_after=1.0 - live / (ba * 16.0) if ba else 0.0,
                 frac_le_half_naive=hn / bn if bn else 0.0,
                 frac_le_half_after=ha / ba if ba else 0.0)
+
+
+def h2o_step(cache: Cache, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+             t_pos: torch.Tensor, group: int, scale: float, score: torch.Tensor, budget: int,
+             recent: int, free_list: torch.Tensor, free_count: torch.Tensor,
+             evicted: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kvev_h2o_step: one decode step of every KV head.  q [B, Hq, D], k_new and
+    v_new [B, Hkv, D] in the cache dtype; t_pos int32 [B]; score fp32 [B, Hkv,
+    max_slots] (running scores, updated); free_list int32, free_count int32
+    [1].  Returns evicted int32 [B, Hkv] (-1 appended, else the pruned
+    position; -2, -3, -4 for a head left unchanged)."""
+    L = load_library()
+    c = cache.struct()
+    B, Hkv, D = cache.batch, cache.kv_heads, cache.head_dim
+    _need(q, "q", cache.k_pool.dtype, B * Hkv * group * D)
+    _need(k_new, "k_new", cache.k_pool.dtype, B * Hkv * D)
+    _need(v_new, "v_new", cache.k_pool.dtype, B * Hkv * D)
+    _need(t_pos, "t_pos", torch.int32, B)
+    _need(score, "score", torch.float32, B * Hkv * cache.max_slots)
+    _need(free_list, "free_list", torch.int32)
+    _need(free_count, "free_count", torch.int32, 1)
+    if evicted is None:
+        evicted = torch.empty((B, Hkv), dtype=torch.int32, device=q.device)
+    _need(evicted, "evicted", torch.int32, B * Hkv)
+    rc = L.kvev_h2o_step(ctypes.byref(c), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(t_pos), group,
+                         scale, _ptr(score), budget, recent, _ptr(free_list), _ptr(free_count),
+                         _ptr(evicted), _stream(stream))
+    _check(rc, "kvev_h2o_step")
+    return evicted
 
 
 def window_attn(cache: Cache, q: torch.Tensor, q_pos: torch.Tensor, scale: float, group: int,

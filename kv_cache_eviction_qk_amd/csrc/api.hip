@@ -165,6 +165,47 @@ int kvev_measure(const int32_t *seq_len_before, const int32_t *victims,
   return map_err(kvev::launch_measure(a, static_cast<hipStream_t>(stream)));
 }
 
+int kvev_h2o_step(const kvev_cache *cache, const void *q, const void *k_new, const void *v_new,
+                  const int32_t *t_pos, int32_t group, float scale, float *score,
+                  int32_t budget, int32_t recent_window, int32_t *free_list,
+                  int32_t *free_count, int32_t *evicted_pos, void *stream) {
+  if (!valid_cache(cache) || !q || !k_new || !v_new || !t_pos || !score || !free_list ||
+      !free_count || !evicted_pos)
+    return KVEV_EINVAL;
+  if (group < 1 || budget <= 0 || recent_window < 0 || recent_window >= budget)
+    return KVEV_EINVAL;
+  if ((int64_t)budget > (int64_t)cache->max_blocks * KVEV_BLOCK_SIZE) return KVEV_EINVAL;
+  const int np = (budget + KVEV_BLOCK_SIZE - 1) / KVEV_BLOCK_SIZE * KVEV_BLOCK_SIZE;
+  if (group > 16 || budget > kvev::kH2oMaxBudget || (int64_t)group * np > kvev::kH2oMaxLogits)
+    return KVEV_EUNSUPPORTED;
+  kvev::H2oArgs a{};
+  a.k_pool = static_cast<uint8_t *>(cache->k_pool);
+  a.v_pool = static_cast<uint8_t *>(cache->v_pool);
+  a.block_table = cache->block_table;
+  a.seq_len = cache->seq_len;
+  a.pos = cache->pos;
+  a.score = score;
+  a.q = static_cast<const uint8_t *>(q);
+  a.k_new = static_cast<const uint8_t *>(k_new);
+  a.v_new = static_cast<const uint8_t *>(v_new);
+  a.t_pos = t_pos;
+  a.free_list = free_list;
+  a.free_count = free_count;
+  a.evicted = evicted_pos;
+  a.units = cache->batch * cache->kv_heads;
+  a.Hkv = cache->kv_heads;
+  a.G = group;
+  a.max_blocks = cache->max_blocks;
+  a.max_slots = cache->max_blocks * KVEV_BLOCK_SIZE;
+  a.num_blocks = cache->num_blocks;
+  a.budget = budget;
+  a.recent = recent_window;
+  a.np = np;
+  a.c1 = scale * 1.4426950408889634f;
+  return map_err(kvev::launch_h2o_step(a, cache->dtype == KVEV_BF16, cache->head_dim,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 int kvev_abi_version(void) { return KVEV_ABI_VERSION; }
 
 const char *kvev_strerror(int status) {

@@ -83,6 +83,20 @@ struct MeasureArgs {
 };
 hipError_t launch_measure(const MeasureArgs &a, hipStream_t s);
 
+struct H2oArgs {
+  uint8_t *k_pool, *v_pool;
+  int32_t *block_table, *seq_len, *pos;
+  float *score;                        // running scores [units][max_slots]
+  const uint8_t *q, *k_new, *v_new;    // [B][Hq][D], [B][Hkv][D], [B][Hkv][D]
+  const int32_t *t_pos;                // [B]
+  int32_t *free_list, *free_count;
+  int32_t *evicted;                    // [units]
+  int32_t units, Hkv, G, max_blocks, max_slots, num_blocks, budget, recent;
+  int32_t np;                          // LDS row stride of the logits (budget rounded up to 16)
+  float c1;                            // scale * log2(e)
+};
+hipError_t launch_h2o_step(const H2oArgs &a, int bf16, int head_dim, hipStream_t s);
+
 struct WindowAttnArgs {
   const uint8_t *k_pool, *v_pool;
   const int32_t *block_table, *seq_len, *pos;
@@ -107,6 +121,8 @@ constexpr int kSelectMaxChunks = 1024;  // chunks per head: up to 1M slots
 constexpr int kHistChunk = 4096;        // slots per select histogram workgroup
 constexpr int kCompactMaxUnits = 4096;  // compact.hip gather limit
 constexpr int kCompactChunk = 1024;     // compact.hip prep chunk (slots)
+constexpr int kH2oMaxBudget = 4096;    // h2o_step.hip: tokens per head
+constexpr int kH2oMaxLogits = 16384;   // h2o_step.hip: G * budget (64 KB of LDS)
 
 // LDS bytes of one score workgroup (fused: room for the tile histogram and
 // the head selection).

@@ -464,12 +464,11 @@ int orc_h2o_step(void *k_pool, void *v_pool, int32_t is_bf16, int32_t head_dim,
         evicted_pos[u] = -3;
         continue;
       }
-      const int32_t blk = free_list[*free_count - 1];
+      const int32_t blk = free_list[--*free_count]; /* taken even if it is out of range */
       if (blk < 0 || blk >= num_blocks) {
         evicted_pos[u] = -4;
         continue;
       }
-      --*free_count;
       bt[n / 16] = blk;
     }
     /* logits of the G query rows: cached tokens (slot j), then the new token (index n) */
@@ -535,8 +534,10 @@ int orc_h2o_step(void *k_pool, void *v_pool, int32_t is_bf16, int32_t head_dim,
           bp = pj;
         }
       }
-      if (best == -1) {
-        evicted_pos[u] = (int32_t)t; /* the new token itself is dropped */
+      if (best < 0) {
+        /* the new token itself is dropped (or, with positions that leave no
+         * candidate at all, cannot be placed) */
+        evicted_pos[u] = (int32_t)t;
         continue;
       }
       dst = best;

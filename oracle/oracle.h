@@ -94,9 +94,10 @@ int orc_measure(const int32_t *seq_len_before, const int32_t *victims, const int
  * among the tokens at least `recent` positions older than t (the new token
  * included when recent == 0) is evicted and the new token overwrites its
  * slot.  evicted_pos[u] = -1 (appended), the evicted position (t when the
- * new token itself was dropped), or -2 (n < 0 or n > budget), -3 (no free
- * block), -4 (block id out of range): on a negative code other than -1 the
- * head is left unchanged.  Returns 0, or -1 on invalid arguments. */
+ * new token itself was dropped, or no cached token is a candidate), or -2
+ * (n < 0 or n > budget), -3 (no free block), -4 (block id out of range; a
+ * bad id taken from the free list stays taken): on a negative code other
+ * than -1 the head is left unchanged.  Returns 0, or -1 on invalid arguments. */
 int orc_h2o_step(void *k_pool, void *v_pool, int32_t is_bf16, int32_t head_dim,
                  int32_t *block_table, int32_t *seq_len, int32_t *pos, float *score,
                  int32_t batch, int32_t kv_heads, int32_t max_blocks, int32_t num_blocks,

@@ -199,6 +199,12 @@ CONFIGS = {
     "block_evict_64k": Config("block_evict_64k", B=16, Hkv=8, G=8, D=128, L=64000, W=16,
                               dtype="bf16", recipe="heavy_hitters", flags=("sum",), budget=32000,
                               recent=16, layers=8, plant_frac=0.02, seed=1005),
+    # Decode-time H2O lifecycle at the decode workload's final budget (870 of
+    # 4352 tokens, 435 recent): the cache enters with 806 tokens, so the first
+    # 64 steps append and every later step prunes one token.
+    "h2o_stream_870": Config("h2o_stream_870", B=8, Hkv=8, G=4, D=128, L=806, W=1, dtype="bf16",
+                             recipe="heavy_hitters", flags=("sum",), decode_steps=256,
+                             budget=870, recent=435, plant_frac=0.02, seed=1006),
 }
 
 
@@ -332,3 +338,16 @@ def make_queries(cfg: Config, layer: int, W: int, dirs: Optional[np.ndarray],
     else:
         q_pos = np.full((B, W), cfg.L + step, np.int32)
     return q, q_pos
+
+
+def decode_token_kv(case: dict, step: int) -> tuple:
+    """Key and value rows [B, Hkv, D] (cache dtype) of the token a decode step
+    appends: position L + step, generated in place at that slot by make_case."""
+    cfg = case["cfg"]
+    s = cfg.L + step
+    B, Hkv = case["B"], case["Hkv"]
+    blk = case["block_table"][:, :, s // BLOCK]          # [B, Hkv]
+    k = case["k_pool"][blk.reshape(-1), s % BLOCK].reshape(B, Hkv, -1)
+    v = case["v_pool"][blk.reshape(-1), s % BLOCK].reshape(B, Hkv, -1)
+    return np.ascontiguousarray(k), np.ascontiguousarray(v)
+

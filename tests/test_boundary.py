@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
     assert set(names) == set(K.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvev_abi_version() == K.ABI_VERSION == 3
+    assert L.kvev_abi_version() == K.ABI_VERSION == 4
     for code in (0, -1, -2, -3, -4):
         assert K.strerror(code)
 
@@ -240,3 +240,29 @@ def test_measure_refusals():
     for units, ms in ((-1, 64), (4, 0), (4, 40)):  # max_slots: a positive multiple of 16
         a = list(args); a[3] = units; a[4] = ms
         assert L.kvev_measure(*a) == K.EINVAL
+
+
+def test_h2o_step_refusals():
+    """Every refusal of kvev_h2o_step is decided on the host, before a launch."""
+    L = K.load_library()
+
+    def call(c=None, group=4, budget=64, recent=8, ptrs=None):
+        c = cache(max_blocks=8) if c is None else c
+        p = dict(q=FAKE, k=FAKE, v=FAKE, t=FAKE, s=FAKE, fl=FAKE, fc=FAKE, ev=FAKE)
+        p.update(ptrs or {})
+        return L.kvev_h2o_step(ctypes.byref(c), p["q"], p["k"], p["v"], p["t"], group, 0.1,
+                               p["s"], budget, recent, p["fl"], p["fc"], p["ev"], None)
+
+    for name in ("q", "k", "v", "t", "s", "fl", "fc", "ev"):
+        assert call(ptrs={name: None}) == K.EINVAL, name
+    assert call(c=cache(head_dim=96)) == K.EINVAL
+    assert call(c=cache(k_pool=None)) == K.EINVAL
+    assert call(group=0) == K.EINVAL
+    assert call(budget=0) == K.EINVAL
+    assert call(budget=129) == K.EINVAL          # above max_blocks * 16 = 128
+    assert call(recent=-1) == K.EINVAL
+    assert call(recent=64) == K.EINVAL           # recent window must leave room: < budget
+    assert call(group=17) == K.EUNSUPPORTED
+    big = cache(max_blocks=300)
+    assert call(c=big, group=1, budget=4097) == K.EUNSUPPORTED
+    assert call(c=big, group=8, budget=2050) == K.EUNSUPPORTED  # 8 * 2064 logits > 16384

@@ -1,0 +1,289 @@
+"""GPU parity of kvev_h2o_step, the H2O decode step, against oracle.h2o_step.
+
+Two ways of running a stream of decode steps:
+
+* isolated steps: before every step the GPU receives the oracle's state, so
+  each step is compared on its own (positions, K / V rows slot by slot
+  bit-exact, running scores to the score tolerance);
+* a free-running chain: the GPU's state evolves by its own steps.  The two
+  sides prune the same token unless two candidates' scores lie within the
+  tolerance of each other; then the GPU's choice must lie in that band of the
+  oracle's cutoff (the oracle's own scores, from a run of the same step with
+  room for one more token, which appends instead of pruning), and that head
+  is followed by invariants only from then on.
+
+Blocks taken from the free list by heads appending in the same step may come
+out in any order on the GPU: the taken set and the remaining list are
+compared, the rows through each side's own block table.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_eviction_qk_amd as K
+import oracle
+import synth
+from tests.gpu_helpers import FLT_MIN, TOL, dev, device_cache, host
+
+pytestmark = pytest.mark.gpu
+rng = np.random.default_rng
+
+
+def _say(msg):
+    print(f"[h2o] {msg}", flush=True)
+
+
+# ------------------------------------------------------------------ states
+
+
+def _scaled_state(seed, dtype, B, Hkv, G, D, budget, n0, spare=8, bad_head=None):
+    """A stream state with per-head lengths n0 [B, Hkv] (positions 0..n-1),
+    running scores drawn around what one step adds (G / budget), heads at a
+    block boundary with no block allocated there, a free list of spare pool
+    blocks, and optionally one head whose first block id is out of range."""
+    r = rng(seed)
+    cap_blocks = (budget + 1 + 15) // 16 + 1
+    U = B * Hkv
+    num_blocks = U * cap_blocks + spare
+    perm = synth.shuffled(num_blocks, seed, 7)
+    bt = perm[:U * cap_blocks].reshape(B, Hkv, cap_blocks).astype(np.int32).copy()
+    edt = np.uint16 if dtype == "bf16" else np.float32
+    k_pool = synth.encode(r.normal(0, 0.5, (num_blocks, 16, D)), dtype).astype(edt)
+    v_pool = synth.encode(r.normal(0, 1.0, (num_blocks, 16, D)), dtype).astype(edt)
+    pos = np.zeros((B, Hkv, cap_blocks * 16), np.int32)
+    score = np.zeros((B, Hkv, cap_blocks * 16), np.float32)
+    for b in range(B):
+        for h in range(Hkv):
+            n = int(n0[b, h])
+            m = max(0, min(n, cap_blocks * 16))
+            pos[b, h, :m] = np.arange(m)
+            score[b, h, :m] = r.uniform(0.0, 2.0 * G / budget, m).astype(np.float32)
+            if 0 <= n < budget and n % 16 == 0:
+                bt[b, h, n // 16:] = -1   # the append opens a block from the free list
+    if bad_head is not None:
+        bt.reshape(U, cap_blocks)[bad_head, 0] = num_blocks + 3
+    free = np.full(num_blocks, -1, np.int32)
+    spare_ids = perm[U * cap_blocks:]
+    free[:spare_ids.size] = spare_ids
+    return dict(dtype=dtype, B=B, Hkv=Hkv, G=G, D=D, W=1, max_blocks=cap_blocks,
+                num_blocks=num_blocks, k_pool=k_pool, v_pool=v_pool, block_table=bt,
+                seq_len=np.ascontiguousarray(n0, dtype=np.int32).copy(), pos=pos, score=score,
+                scale=1.0 / np.sqrt(D)), free, int(spare_ids.size)
+
+
+def _step_inputs(seed, step, dtype, B, Hkv, G, D, u_dirs):
+    """Query rows (with the heads' planted direction), new key and value."""
+    r = rng([seed, step])
+    q = r.normal(0, 0.5, (B, Hkv * G, D))
+    q += np.repeat(u_dirs, G, axis=1) * np.sqrt(D) * 0.5
+    k = r.normal(0, 0.5, (B, Hkv, D))
+    hot = r.uniform(0, 1, (B, Hkv)) < 0.1             # a tenth of the tokens: heavy hitters
+    k += hot[..., None] * u_dirs * np.sqrt(D) * 0.5
+    v = r.normal(0, 1.0, (B, Hkv, D))
+    return synth.encode(q, dtype), synth.encode(k, dtype), synth.encode(v, dtype)
+
+
+class Dev:
+    """Device copy of a stream state and its free list."""
+
+    def __init__(self, st, free, fc):
+        self.c = device_cache(st)
+        self.score = dev(st["score"])
+        self.fl = dev(free)
+        self.fc = dev(np.array([fc], np.int32))
+
+    def step(self, st, q, k, v, t, budget, recent):
+        return K.h2o_step(self.c, dev(q), dev(k), dev(v), dev(t), st["G"], st["scale"],
+                          self.score, budget, recent, self.fl, self.fc)
+
+    def state(self, like):
+        out = dict(like)
+        out.update(k_pool=host(self.c.k_pool), v_pool=host(self.c.v_pool),
+                   block_table=host(self.c.block_table), seq_len=host(self.c.seq_len),
+                   pos=host(self.c.pos), score=host(self.score))
+        return out, host(self.fl), int(host(self.fc)[0])
+
+
+# ------------------------------------------------------------- comparisons
+
+
+def _row(st, which, u, s):
+    return st[which][st["block_table"].reshape(-1, st["max_blocks"])[u, s // 16], s % 16]
+
+
+def _flat(st, key):
+    return st[key].reshape(st["B"] * st["Hkv"], -1)
+
+
+def _close(g, o, tol):
+    return abs(float(g) - float(o)) <= tol * max(abs(float(o)), FLT_MIN)
+
+
+def _same_slots(g, o, u, n, tol, what):
+    """Slots [0, n) of head u: positions and K / V rows equal, scores close."""
+    gp, op = _flat(g, "pos")[u, :n], _flat(o, "pos")[u, :n]
+    assert np.array_equal(gp, op), f"{what}: positions differ"
+    for s in range(n):
+        for which in ("k_pool", "v_pool"):
+            assert np.array_equal(_row(g, which, u, s), _row(o, which, u, s)), \
+                f"{what}: {which} row of slot {s} differs"
+        assert _close(_flat(g, "score")[u, s], _flat(o, "score")[u, s], tol), \
+            f"{what}: score of slot {s}: gpu {_flat(g, 'score')[u, s]!r} " \
+            f"oracle {_flat(o, 'score')[u, s]!r}"
+
+
+def _all_scores(before, q, k, v, t, budget, recent):
+    """The oracle's running scores after the step's attention for every cached
+    slot: the same step with room for one more token appends, pruning none."""
+    spare = np.arange(before["num_blocks"], dtype=np.int32)  # any ids: the copy is discarded
+    st, _, _, _ = oracle.h2o_step(before, q, k, v, t, budget + 1, recent, free_list=spare,
+                                  free_count=spare.size)
+    return st["score"].reshape(before["B"] * before["Hkv"], -1)
+
+
+def compare_step(before, g, o, ev_g, ev_o, allsc, t, budget, recent, tol, what, heads=None):
+    """Verdict per head of one step taken from the same `before` state: 'same',
+    or 'band' (the pruned tokens differ, inside the tolerance band)."""
+    U = before["B"] * before["Hkv"]
+    ev_g, ev_o = ev_g.reshape(-1), ev_o.reshape(-1)
+    verdict = {}
+    for u in (range(U) if heads is None else heads):
+        b = u // before["Hkv"]
+        n = int(_flat(before, "seq_len")[u, 0])
+        tag = f"{what} head {u}"
+        if ev_o[u] < -1:  # refused: the head is untouched on both sides
+            assert ev_g[u] == ev_o[u], f"{tag}: code {ev_g[u]} vs {ev_o[u]}"
+            m = max(0, min(n, _flat(before, "pos").shape[1]))
+            assert np.array_equal(_flat(g, "pos")[u, :m], _flat(before, "pos")[u, :m]), tag
+            for j in range(m):
+                assert _close(_flat(g, "score")[u, j], _flat(before, "score")[u, j], tol), tag
+            assert _flat(g, "seq_len")[u, 0] == n, tag
+            verdict[u] = "same"
+            continue
+        if ev_g[u] == ev_o[u]:
+            n_after = int(_flat(o, "seq_len")[u, 0])
+            assert int(_flat(g, "seq_len")[u, 0]) == n_after, tag
+            _same_slots(g, o, u, n_after, tol, tag)
+            verdict[u] = "same"
+            continue
+        # different pruned tokens: both candidates, the GPU's inside the band
+        # of the oracle's cutoff (scores after this step's attention)
+        assert ev_o[u] >= 0 and ev_g[u] >= 0, f"{tag}: {ev_g[u]} vs {ev_o[u]}"
+        tb = int(t[b])
+        assert tb - ev_g[u] >= recent, f"{tag}: pruned {ev_g[u]} inside the recent window"
+        pos_b = _flat(before, "pos")[u, :n]
+
+        def score_of(p):  # the new token sits at slot n of the appending run
+            if p == tb:
+                return float(allsc[u, n])
+            return float(allsc[u, int(np.flatnonzero(pos_b == p)[0])])
+        c, x = score_of(int(ev_o[u])), score_of(int(ev_g[u]))
+        assert abs(x - c) <= tol * max(abs(c), FLT_MIN), \
+            f"{tag}: pruned {ev_g[u]} (score {x!r}) against {ev_o[u]} (cutoff {c!r})"
+        for s in range(n):  # the GPU's own state: new token in the slot it pruned
+            if pos_b[s] == ev_g[u]:
+                assert int(_flat(g, "pos")[u, s]) == tb, tag
+            else:
+                assert _flat(g, "pos")[u, s] == pos_b[s], tag
+                assert _close(_flat(g, "score")[u, s], allsc[u, s], tol), tag
+        verdict[u] = "band"
+    return verdict
+
+
+def check_free_lists(before_bt, g, o, fl_g, fc_g, fl_o, fc_o):
+    """Same number taken, the same remaining list, the same set of taken blocks."""
+    assert fc_g == fc_o
+    assert np.array_equal(fl_g[:fc_o], fl_o[:fc_o])
+    new_g = g["block_table"][(before_bt < 0) & (g["block_table"] >= 0)]
+    new_o = o["block_table"][(before_bt < 0) & (o["block_table"] >= 0)]
+    assert sorted(new_g.tolist()) == sorted(new_o.tolist())
+
+
+# ------------------------------------------------------------------- cases
+
+CASES = [
+    # dtype, D, G, budget, recent, head with a bad block id
+    ("bf16", 128, 4, 100, 20, None),
+    ("f32", 64, 2, 40, 0, None),
+    ("bf16", 64, 8, 57, 1, 7),
+]
+
+
+def _lengths(B, Hkv, budget):
+    """Ragged starts: appends, a full head, an empty one, one on a block
+    boundary, one above the budget (refused at every step)."""
+    pick = [budget - 10, budget, 0, 32, budget + 3, budget - 1, 16, 5]
+    return np.array([pick[i % len(pick)] for i in range(B * Hkv)], np.int32).reshape(B, Hkv)
+
+
+@pytest.mark.parametrize("dtype,D,G,budget,recent,bad", CASES)
+def test_isolated_steps(dtype, D, G, budget, recent, bad):
+    B, Hkv, steps = 2, 4, 48
+    seed = 100 + D + budget
+    st, free, fc = _scaled_state(seed, dtype, B, Hkv, G, D, budget, _lengths(B, Hkv, budget),
+                                 bad_head=bad)
+    dirs = rng(seed).normal(0, 1, (B, Hkv, D))
+    dirs /= np.linalg.norm(dirs, axis=-1, keepdims=True)
+    t0 = budget + 8
+    counts = {"same": 0, "band": 0}
+    _say(f"{dtype} D{D} G{G} budget {budget} recent {recent}: {steps} isolated steps")
+    for i in range(steps):
+        q, k, v = _step_inputs(seed, i, dtype, B, Hkv, G, D, dirs)
+        t = np.full(B, t0 + i, np.int32)
+        o, ev_o, fl_o, fc_o = oracle.h2o_step(st, q, k, v, t, budget, recent, free_list=free,
+                                              free_count=fc)
+        d = Dev(st, free, fc)
+        ev_g = host(d.step(st, q, k, v, t, budget, recent))
+        torch.cuda.synchronize()
+        g, fl_g, fc_g = d.state(st)
+        allsc = _all_scores(st, q, k, v, t, budget, recent)
+        for vv in compare_step(st, g, o, ev_g, ev_o, allsc, t, budget, recent, TOL[dtype],
+                               f"step {i}").values():
+            counts[vv] += 1
+        check_free_lists(st["block_table"], g, o, fl_g, fc_g, fl_o, fc_o)
+        st, free, fc = o, fl_o, fc_o
+    _say(f"heads x steps: {counts}")
+    assert counts["same"] >= 0.95 * (counts["same"] + counts["band"])
+
+
+@pytest.mark.parametrize("dtype,D,G,budget,recent,bad", CASES[:2])
+def test_free_running_chain(dtype, D, G, budget, recent, bad):
+    B, Hkv, steps = 2, 4, 64
+    seed = 200 + D + budget
+    st, free, fc = _scaled_state(seed, dtype, B, Hkv, G, D, budget, _lengths(B, Hkv, budget))
+    dirs = rng(seed).normal(0, 1, (B, Hkv, D))
+    dirs /= np.linalg.norm(dirs, axis=-1, keepdims=True)
+    t0 = budget + 8
+    d = Dev(st, free, fc)
+    o, fl_o, fc_o = st, free, fc
+    U = B * Hkv
+    diverged = set()
+    _say(f"{dtype} D{D} G{G} budget {budget} recent {recent}: {steps} free-running steps")
+    for i in range(steps):
+        q, k, v = _step_inputs(seed, i, dtype, B, Hkv, G, D, dirs)
+        t = np.full(B, t0 + i, np.int32)
+        before_o = o
+        o, ev_o, fl_o, fc_o = oracle.h2o_step(o, q, k, v, t, budget, recent, free_list=fl_o,
+                                              free_count=fc_o)
+        ev_g = host(d.step(st, q, k, v, t, budget, recent))
+        torch.cuda.synchronize()
+        g, fl_g, fc_g = d.state(st)
+        allsc = _all_scores(before_o, q, k, v, t, budget, recent)
+        live = [u for u in range(U) if u not in diverged]
+        for u, vv in compare_step(before_o, g, o, ev_g, ev_o, allsc, t, budget, recent,
+                                  TOL[dtype], f"step {i}", heads=live).items():
+            if vv == "band":
+                diverged.add(u)
+        for u in diverged:  # followed by invariants only
+            n = int(_flat(g, "seq_len")[u, 0])
+            e = int(ev_g.reshape(-1)[u])
+            tb = t0 + i
+            assert n <= budget and e >= -1
+            p = set(_flat(g, "pos")[u, :n].tolist())
+            assert len(p) == n                       # positions unique
+            assert tb in p or e == tb                # the new token placed or dropped
+            assert e < 0 or tb - e >= recent         # nothing pruned inside the window
+        check_free_lists(before_o["block_table"], g, o, fl_g, fc_g, fl_o, fc_o)
+    _say(f"{dtype} D{D}: {len(diverged)} of {U} heads pruned a different token inside the "
+         f"tolerance band")
+    assert len(diverged) <= U // 2
