@@ -4,6 +4,9 @@ eviction on one MI355X, on seeded synthetic inputs.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--path fused|separate]
                     [--no-cpu-baseline]
 
+(--workload h2o_stream_870 times the H2O decode step instead: one
+kvev_h2o_step launch per decoded token of every sequence.)
+
 A step is the whole eviction path for one layer's cache: scoring (SnapKV
 window sum + max-pool over the last W prompt queries), selection (budget,
 protected recent window) and compaction (in-place repack, emptied blocks to
@@ -90,6 +93,8 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     cfg = synth.CONFIGS[args.workload]
+    if args.workload == "h2o_stream_870":
+        return bench_h2o_stream(args, cfg)
     if cfg.decode_steps:
         print(json.dumps({"error": f"{args.workload} is a decode schedule, not a one-shot pass"}))
         sys.exit(2)
@@ -308,6 +313,164 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_h2o_stream(args, cfg):
+    """The H2O decode lifecycle, one kvev_h2o_step launch per step over every
+    KV head (attend with the new token's query rows, accumulate, prune to the
+    budget, overwrite in place).  The stream's first budget - L steps fill the
+    cache (untimed, with the warmup steps); the timed steps each prune one
+    token per head.  value = decoded tokens (one per sequence) per second."""
+    import numpy as np
+    import torch
+
+    import kv_cache_eviction_qk_amd as K
+    import synth
+
+    B, Hkv, G, D = cfg.B, cfg.Hkv, cfg.G, cfg.D
+    fill = cfg.budget - cfg.L
+    warm = args.warmup
+    steps = min(args.steps, cfg.decode_steps - fill - warm)
+    if steps < 1:
+        print(json.dumps({"error": f"{cfg.decode_steps} steps in the stream: lower --warmup"}))
+        sys.exit(2)
+    case = synth.make_case(cfg)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    cache = K.Cache(dev(case["k_pool"]), dev(case["v_pool"]), dev(case["block_table"]),
+                    dev(case["seq_len"]), dev(case["pos"]))
+    score = cache.score_buffer()
+    free_list = torch.full((case["num_blocks"],), -1, dtype=torch.int32, device="cuda")
+    free_count = torch.zeros(1, dtype=torch.int32, device="cuda")
+    total = fill + warm + steps
+    qs, ks, vs = [], [], []
+    for i in range(total):  # every step's inputs resident before the timed region
+        q, _ = synth.make_queries(cfg, 0, 1, case["dirs"], step=i)
+        k, v = synth.decode_token_kv(case, i)
+        qs.append(dev(q.reshape(B, cfg.Hq, D)))
+        ks.append(dev(k))
+        vs.append(dev(v))
+    tpos = [torch.full((B,), cfg.L + i, dtype=torch.int32, device="cuda") for i in range(total)]
+    evicted = torch.empty((B, Hkv), dtype=torch.int32, device="cuda")
+    ws = K.new_h2o_workspace(cache, G, cfg.budget)
+
+    def step(i):
+        K.h2o_step(cache, qs[i], ks[i], vs[i], tpos[i], G, cfg.softmax_scale, score, cfg.budget,
+                   cfg.recent, free_list, free_count, ws, evicted)
+
+    for i in range(fill + warm):
+        step(i)
+    torch.cuda.synchronize()
+    assert int(cache.seq_len.min()) == cfg.budget
+    log(f"stream filled to {cfg.budget} tokens per head; {warm} warmup steps")
+    # the timed steps as one HIP graph (a decode loop is replayed, not
+    # re-issued from the host; each step is one kernel); a copy of the state
+    # lets the same steps also run eagerly for comparison
+    snap = [t.clone() for t in (cache.k_pool, cache.v_pool, cache.block_table, cache.seq_len,
+                                cache.pos, score, free_list, free_count)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(fill + warm, total):
+            step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = e0.elapsed_time(e1) / steps
+    if args.profile_steps:
+        log(f"profile run done: {ms_step:.4f} ms/step")
+        return
+    ev = evicted.cpu().numpy()
+    assert (ev >= 0).all(), "a timed step did not prune"
+    after = [t.clone() for t in (cache.k_pool, cache.pos, score)]
+    for t, v in zip((cache.k_pool, cache.v_pool, cache.block_table, cache.seq_len, cache.pos,
+                     score, free_list, free_count), snap):
+        t.copy_(v)
+    torch.cuda.synchronize()
+    x0, x1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    x0.record()
+    for i in range(fill + warm, total):
+        step(i)
+    x1.record()
+    torch.cuda.synchronize()
+    ms_eager = x0.elapsed_time(x1) / steps
+    same = all(bool(torch.equal(a, b)) for a, b in zip(after, (cache.k_pool, cache.pos, score)))
+    assert same, "graph replay and eager steps differ"
+    # algorithmic bytes of one step (the launch is the whole step)
+    eb = 2 if cfg.dtype == "bf16" else 4
+    units, n = B * Hkv, cfg.budget
+    step_bytes = (units * n * D * eb                # cached keys
+                  + B * cfg.Hq * D * eb             # query rows
+                  + units * n * (4 + 4 + 4)         # scores read and written, positions read
+                  + units * math.ceil(n / 16) * 4   # block ids
+                  + units * 2 * D * eb * 2)         # new K / V row, read and written
+    achieved = step_bytes / (ms_step / 1e3) / 1e9
+    cpu = None if args.no_cpu_baseline else cpu_baseline_h2o(case, cfg, fill)
+    out = {
+        "metric": "H2O decode steps: tokens/sec (attend+accumulate+prune+overwrite per step)",
+        "value": B / (ms_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; 2% heavy hitters planted on the query direction)",
+        "config": {"workload": args.workload, "batch": B, "kv_heads": Hkv, "group": G,
+                   "head_dim": D, "budget": cfg.budget, "recent_window": cfg.recent,
+                   "start_tokens": cfg.L, "block_size": 16, "accumulate": "fp32"},
+        "wall_s": wall,
+        "timing": "one HIP graph of the timed steps, replayed once",
+        "eager_ms_per_step": ms_eager,
+        "roofline": {"kernel": "h2o_step_kernel (kvev_h2o_step)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": step_bytes, "launch_ms": ms_step},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_h2o(case, cfg, fill):
+    """The oracle's decode step on the host (one thread: it walks the heads in
+    order), for a bounded sample: the fill steps untimed, then 24 pruning
+    steps timed."""
+    import numpy as np
+
+    import oracle
+    import synth
+    st = dict(case)
+    st["score"] = np.zeros((cfg.B, cfg.Hkv, case["max_blocks"] * 16), np.float32)
+    fl = np.full(case["num_blocks"], -1, np.int32)
+
+    def one(i):
+        q, _ = synth.make_queries(cfg, 0, 1, case["dirs"], step=i)
+        k, v = synth.decode_token_kv(case, i)
+        return oracle.h2o_step(st, q.reshape(cfg.B, cfg.Hq, cfg.D), k, v,
+                               np.full(cfg.B, cfg.L + i, np.int32), cfg.budget, cfg.recent,
+                               free_list=fl, free_count=0)[0]
+    for i in range(fill):
+        st = one(i)
+    n = 24
+    t0 = time.perf_counter()
+    for i in range(fill, fill + n):
+        st = one(i)
+    dt = time.perf_counter() - t0
+    return {"value": cfg.B * n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} pruning steps of all {cfg.B * cfg.Hkv} KV heads at {cfg.budget} "
+                      f"tokens; {dt:.1f} s"}
 
 
 def cpu_baseline(case, cfg, kind):

@@ -55,7 +55,7 @@ extern "C" {
 #endif
 
 #define KVEV_BLOCK_SIZE 16
-#define KVEV_ABI_VERSION 4
+#define KVEV_ABI_VERSION 5
 
 typedef enum {
   KVEV_OK = 0,
@@ -265,16 +265,26 @@ int kvev_measure(const int32_t *seq_len_before, const int32_t *victims,
  * head left unchanged, -2 (seq_len < 0 or > budget), -3 (free list empty),
  * -4 (a block id of the head, or the one taken from the free list, outside
  * [0, num_blocks); a bad free-list entry stays taken).  Device pointers; one
- * kernel on `stream`; no workspace.
+ * kernel on `stream`.  Workspace: at least kvev_h2o_workspace_bytes(cache,
+ * group, budget) bytes, zero-filled once before its first use (its leading
+ * part holds per-head counters that every call leaves zero); it is separate
+ * from, and may not alias, the workspace of the other entry points while
+ * both are in use.  Each KV head is split over several workgroups that hand
+ * their partial results to the last one through the workspace.
  * Errors: KVEV_EINVAL for NULL pointers, a bad cache, group < 1,
  * budget <= 0 or above max_blocks * 16, recent_window < 0 or >= budget;
  * KVEV_EUNSUPPORTED for group > 16, budget > 4096 or group * budget (rounded
- * up to 16) > 16384.
+ * up to 16) > 16384; KVEV_ENOSPACE for a missing or short workspace.
  */
 int kvev_h2o_step(const kvev_cache *cache, const void *q, const void *k_new, const void *v_new,
                   const int32_t *t_pos, int32_t group, float scale, float *score,
                   int32_t budget, int32_t recent_window, int32_t *free_list,
-                  int32_t *free_count, int32_t *evicted_pos, void *stream);
+                  int32_t *free_count, int32_t *evicted_pos, void *workspace,
+                  size_t ws_bytes, void *stream);
+
+/* Workspace bytes kvev_h2o_step needs for this cache, group and budget; 0
+ * for a bad cache or a group / budget it refuses. */
+size_t kvev_h2o_workspace_bytes(const kvev_cache *cache, int32_t group, int32_t budget);
 
 /*
  * kvev_window_attn -- helper outside the eviction step: the log-sum-exp and

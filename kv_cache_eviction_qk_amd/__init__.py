@@ -30,9 +30,9 @@ BLOCK_SIZE = 16
 
 # the functions include/kvev.h declares
 EXPORTS = ("kvev_score", "kvev_select", "kvev_compact", "kvev_evict", "kvev_measure",
-           "kvev_h2o_step", "kvev_window_attn", "kvev_workspace_bytes", "kvev_strerror",
-           "kvev_abi_version")
-ABI_VERSION = 4
+           "kvev_h2o_step", "kvev_h2o_workspace_bytes", "kvev_window_attn",
+           "kvev_workspace_bytes", "kvev_strerror", "kvev_abi_version")
+ABI_VERSION = 5
 
 
 class KvevError(RuntimeError):
@@ -78,7 +78,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kvev_evict.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P, P, i32, P, P, sz, P]
     L.kvev_window_attn.argtypes = [P, P, P, P, P, sz, P]
     L.kvev_measure.argtypes = [P, P, P, i32, i32, P, P]
-    L.kvev_h2o_step.argtypes = [P, P, P, P, P, i32, ctypes.c_float, P, i32, i32, P, P, P, P]
+    L.kvev_h2o_step.argtypes = [P, P, P, P, P, i32, ctypes.c_float, P, i32, i32, P, P, P, P,
+                                sz, P]
+    L.kvev_h2o_workspace_bytes.argtypes = [P, i32, i32]
+    L.kvev_h2o_workspace_bytes.restype = sz
     L.kvev_workspace_bytes.argtypes = [P, i32, i32]
     L.kvev_workspace_bytes.restype = sz
     L.kvev_strerror.argtypes = [ctypes.c_int]
@@ -341,15 +344,24 @@ def measure(seq_len_before: torch.Tensor, victims: torch.Tensor, n_victims: torc
                 frac_le_half_after=ha / ba if ba else 0.0)
 
 
+def new_h2o_workspace(cache: Cache, group: int, budget: int) -> torch.Tensor:
+    """A zero-filled workspace for kvev_h2o_step on this cache shape."""
+    n = load_library().kvev_h2o_workspace_bytes(ctypes.byref(cache.struct()), group, budget)
+    if n == 0:
+        raise KvevError(EUNSUPPORTED, "kvev_h2o_workspace_bytes")
+    return torch.zeros(n, dtype=torch.uint8, device=cache.k_pool.device)
+
+
 def h2o_step(cache: Cache, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
              t_pos: torch.Tensor, group: int, scale: float, score: torch.Tensor, budget: int,
              recent: int, free_list: torch.Tensor, free_count: torch.Tensor,
-             evicted: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+             workspace: torch.Tensor, evicted: Optional[torch.Tensor] = None,
+             stream=None) -> torch.Tensor:
     """kvev_h2o_step: one decode step of every KV head.  q [B, Hq, D], k_new and
     v_new [B, Hkv, D] in the cache dtype; t_pos int32 [B]; score fp32 [B, Hkv,
     max_slots] (running scores, updated); free_list int32, free_count int32
-    [1].  Returns evicted int32 [B, Hkv] (-1 appended, else the pruned
-    position; -2, -3, -4 for a head left unchanged)."""
+    [1]; workspace from new_h2o_workspace.  Returns evicted int32 [B, Hkv] (-1
+    appended, else the pruned position; -2, -3, -4 for a head left unchanged)."""
     L = load_library()
     c = cache.struct()
     B, Hkv, D = cache.batch, cache.kv_heads, cache.head_dim
@@ -360,12 +372,13 @@ def h2o_step(cache: Cache, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Te
     _need(score, "score", torch.float32, B * Hkv * cache.max_slots)
     _need(free_list, "free_list", torch.int32)
     _need(free_count, "free_count", torch.int32, 1)
+    _need(workspace, "workspace", torch.uint8)
     if evicted is None:
         evicted = torch.empty((B, Hkv), dtype=torch.int32, device=q.device)
     _need(evicted, "evicted", torch.int32, B * Hkv)
     rc = L.kvev_h2o_step(ctypes.byref(c), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(t_pos), group,
                          scale, _ptr(score), budget, recent, _ptr(free_list), _ptr(free_count),
-                         _ptr(evicted), _stream(stream))
+                         _ptr(evicted), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(rc, "kvev_h2o_step")
     return evicted
 

@@ -165,19 +165,52 @@ int kvev_measure(const int32_t *seq_len_before, const int32_t *victims,
   return map_err(kvev::launch_measure(a, static_cast<hipStream_t>(stream)));
 }
 
+// Workspace of kvev_h2o_step: [arrival counters | error flags] (state, zero
+// between calls) then the parts' e values and (max, sum) per row.
+struct H2oLayout {
+  size_t arrive, err, e, ml, total;
+  int np, nbmax;
+};
+
+H2oLayout h2o_layout(const kvev_cache *c, int32_t group, int32_t budget) {
+  H2oLayout L{};
+  const size_t units = (size_t)c->batch * c->kv_heads;
+  L.nbmax = (budget + KVEV_BLOCK_SIZE - 1) / KVEV_BLOCK_SIZE;
+  L.np = (L.nbmax + 1) * KVEV_BLOCK_SIZE;  // every slot, then the new token's e
+  size_t off = 0;
+  L.arrive = off; off = a256(off + units * 4);
+  L.err = off; off = a256(off + units * 4);
+  L.e = off; off = a256(off + units * (size_t)group * L.np * 4);
+  L.ml = off; off = a256(off + units * (size_t)kvev::kH2oMaxSplit * 32 * 4);
+  L.total = off;
+  return L;
+}
+
+size_t kvev_h2o_workspace_bytes(const kvev_cache *cache, int32_t group, int32_t budget) {
+  if (!valid_cache(cache) || group < 1 || group > 16 || budget <= 0 ||
+      budget > kvev::kH2oMaxBudget)
+    return 0;
+  return h2o_layout(cache, group, budget).total;
+}
+
 int kvev_h2o_step(const kvev_cache *cache, const void *q, const void *k_new, const void *v_new,
                   const int32_t *t_pos, int32_t group, float scale, float *score,
                   int32_t budget, int32_t recent_window, int32_t *free_list,
-                  int32_t *free_count, int32_t *evicted_pos, void *stream) {
+                  int32_t *free_count, int32_t *evicted_pos, void *workspace, size_t ws_bytes,
+                  void *stream) {
   if (!valid_cache(cache) || !q || !k_new || !v_new || !t_pos || !score || !free_list ||
       !free_count || !evicted_pos)
     return KVEV_EINVAL;
   if (group < 1 || budget <= 0 || recent_window < 0 || recent_window >= budget)
     return KVEV_EINVAL;
   if ((int64_t)budget > (int64_t)cache->max_blocks * KVEV_BLOCK_SIZE) return KVEV_EINVAL;
-  const int np = (budget + KVEV_BLOCK_SIZE - 1) / KVEV_BLOCK_SIZE * KVEV_BLOCK_SIZE;
-  if (group > 16 || budget > kvev::kH2oMaxBudget || (int64_t)group * np > kvev::kH2oMaxLogits)
+  if (group > 16 || budget > kvev::kH2oMaxBudget ||
+      (int64_t)group * ((budget + KVEV_BLOCK_SIZE - 1) / KVEV_BLOCK_SIZE * KVEV_BLOCK_SIZE) >
+          kvev::kH2oMaxLogits)
     return KVEV_EUNSUPPORTED;
+  const H2oLayout L = h2o_layout(cache, group, budget);
+  if (!workspace || ws_bytes < L.total) return KVEV_ENOSPACE;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
   kvev::H2oArgs a{};
   a.k_pool = static_cast<uint8_t *>(cache->k_pool);
   a.v_pool = static_cast<uint8_t *>(cache->v_pool);
@@ -192,6 +225,10 @@ int kvev_h2o_step(const kvev_cache *cache, const void *q, const void *k_new, con
   a.free_list = free_list;
   a.free_count = free_count;
   a.evicted = evicted_pos;
+  a.arrive = reinterpret_cast<uint32_t *>(ws + L.arrive);
+  a.err = reinterpret_cast<uint32_t *>(ws + L.err);
+  a.e = reinterpret_cast<uint32_t *>(ws + L.e);
+  a.ml = reinterpret_cast<uint32_t *>(ws + L.ml);
   a.units = cache->batch * cache->kv_heads;
   a.Hkv = cache->kv_heads;
   a.G = group;
@@ -200,7 +237,10 @@ int kvev_h2o_step(const kvev_cache *cache, const void *q, const void *k_new, con
   a.num_blocks = cache->num_blocks;
   a.budget = budget;
   a.recent = recent_window;
-  a.np = np;
+  a.np = L.np;
+  // enough workgroups to cover the CUs, at most one per block of the budget
+  const int want = (256 + a.units - 1) / a.units;
+  a.split = std::max(1, std::min({want, kvev::kH2oMaxSplit, L.nbmax}));
   a.c1 = scale * 1.4426950408889634f;
   return map_err(kvev::launch_h2o_step(a, cache->dtype == KVEV_BF16, cache->head_dim,
                                        static_cast<hipStream_t>(stream)));

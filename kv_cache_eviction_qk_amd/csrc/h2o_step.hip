@@ -8,23 +8,26 @@
 // ([H2O] "PagedAttention Memory Integration").  Below the budget the token is
 // appended, taking a block from the free list when its logical block has none.
 //
-// One 1024-thread workgroup per KV head, one launch per step:
-//   1. block ids of the head to LDS (checked), the running scores and
-//      positions of the thread's slots, the new K / V row: one round of loads;
-//   2. logits: the G query rows (padded to 16) against 16 keys per MFMA
-//      (v_mfma 16x16, bf16 or fp32), each wave a strided set of blocks with
-//      up to 16 / U blocks in flight; the new key by one wave; log2 units
-//      into LDS;
-//   3. per query row (one wave each) the log-sum-exp over the cached tokens
-//      and the new one;
-//   4. p = exp2(logit - lse) summed over the rows in order and added to the
-//      thread's scores; the candidates' (score key, position) packed into 64
-//      bits, the workgroup minimum found by wave shuffles;
-//   5. writes: every score once, the new token's K / V row, position and
-//      score at the pruned slot (or slot n), seq_len on append.
-// Every global address is written by one thread of one workgroup, so no
-// cross-workgroup ordering is involved; the free list is the only shared
-// state (one atomic per head that appends into a fresh block).
+// One launch per step; each KV head is split over `split` 1024-thread
+// workgroups (one CU streams its share of the keys at a few tens of GB/s, so
+// a head alone on one CU would be bound by that):
+//   part  (every workgroup of the head, a contiguous range of its blocks):
+//         block ids (checked), logits of the G query rows (padded to 16)
+//         against 16 keys per MFMA, the workgroup's maximum m and sum
+//         l = sum exp2(logit - m) per row, and e = exp2(logit - m) of its
+//         slots (the first workgroup also the new token's), published to the
+//         workspace with agent-scope stores; then one agent-scope atomic on
+//         the head's arrival counter;
+//   final (the workgroup that arrives last): lse of each row from the
+//         workgroups' (m, l) in order, p = e * exp2(m - lse) summed over the
+//         rows (fixed order) and added to each running score, the minimum of
+//         the packed (score key, position) of the candidates, and every
+//         write of the step: each score once, the new token's K / V row,
+//         position and score at the pruned slot (or slot n), seq_len on
+//         append, the arrival counter reset.
+// Data handed between workgroups of the launch uses agent-scope atomic
+// loads and stores only, ordered by waiting for completion before the
+// counter atomic; the cache itself is written by the final workgroup alone.
 #include <hip/hip_runtime.h>
 
 #include "kvev_device.h"
@@ -37,6 +40,8 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;             // 16
 constexpr int kPer = kH2oMaxBudget / kThreads;       // slots per thread (4)
 constexpr int kMaxBlocksH = kH2oMaxBudget / kBlock;  // 256
+constexpr int kMaxSplit = kH2oMaxSplit;            // workgroups per head at most
+constexpr int kEBatch = 8;  // e values per thread per round of loads in the final step
 
 __device__ __forceinline__ unsigned long long pack_min(float v, int p) {
   // (score key, position) ordered as one unsigned word; the sign flip keeps
@@ -53,38 +58,67 @@ __device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v)
   }
   return v;
 }
+// ---- agent-scope accesses for data another workgroup of the launch reads
+__device__ __forceinline__ void cst(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t cld(const uint32_t *p) {
+  return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// every memory operation this wave issued has completed
+__device__ __forceinline__ void drain() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 }  // namespace
 
 template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void h2o_step_kernel(const H2oArgs P) {
   constexpr int EB = BF16 ? 2 : 4, ROWB = D * EB, U = ROWB / 64, CPR = ROWB / 16;
-  constexpr int NBK = (16 / U) > 0 ? 16 / U : 1;  // blocks per load batch of a wave
-  extern __shared__ float lgt[];                  // [G][np] logits, log2 units
-  __shared__ int s_bt[kMaxBlocksH + 1];
+  constexpr int NBK = U >= 8 ? 1 : 16 / U;  // blocks per load batch of a wave (register budget)
+  extern __shared__ float lgt[];  // part: [G][cb*16] logits (log2 units); final: [G][np] e values
+  __shared__ int s_bt[kMaxBlocksH];
   __shared__ unsigned long long s_wmin[kWaves];
-  __shared__ float s_lse[16], s_newlg[16];
+  __shared__ float s_m[16], s_newlg[16], s_r[16 * kMaxSplit];
   __shared__ float s_snew;
-  __shared__ int s_bad, s_dst, s_fresh;
+  __shared__ int s_last, s_dst, s_code, s_blk;
 
-  const int u = blockIdx.x, tid = threadIdx.x, l = lane_id(), lr = l & 15, lg = l >> 4;
-  const int wv = tid / kWave;
+  const int S = P.split;
+  const int u = blockIdx.x / S, w = blockIdx.x % S;
+  const int tid = threadIdx.x, l = lane_id(), lr = l & 15, lg = l >> 4, wv = tid / kWave;
   const int b = u / P.Hkv, h = u % P.Hkv;
-  const int G = P.G, budget = P.budget, NP = P.np;
+  const int G = P.G, budget = P.budget;
   int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
   int32_t *ps = P.pos + (size_t)u * P.max_slots;
   float *sc = P.score + (size_t)u * P.max_slots;
+  uint32_t *E = P.e + (size_t)u * G * P.np;         // [G][np]: e of every slot, then the new token
+  uint32_t *ML = P.ml + (size_t)u * kMaxSplit * 32;  // [split][16 m, 16 l]
 
-  // ---- one round of loads: length, position, block ids, scores, the new row
   const int n = P.seq_len[u];
   const int t = P.t_pos[b];
-  if (n < 0 || n > budget) {  // inconsistent head: left unchanged
-    if (tid == 0) P.evicted[u] = -2;
+  if (n < 0 || n > budget) {  // inconsistent head: left unchanged, no workgroup arrives
+    if (w == 0 && tid == 0) P.evicted[u] = -2;
     return;
   }
   const bool append = n < budget;
-  const int nb = (n + kBlock - 1) / kBlock;      // blocks holding cached tokens
-  const int nbt = append ? n / kBlock + 1 : nb;  // entries the step touches
-  const int my_id = tid < nbt ? bt[tid] : 0;     // nbt <= 257 <= kThreads
+  const int nb = (n + kBlock - 1) / kBlock;  // blocks holding cached tokens
+  const int cb = (nb + S - 1) / S;           // blocks per part
+  const int lb0 = min(w * cb, nb), lb1 = min(lb0 + cb, nb);
+  const int pnb = lb1 - lb0;                 // this part's blocks (may be 0)
+  const int CS = cb * kBlock;                // LDS row stride of the logits
+
+  // ---------------------------------------------------------------- part
+  const int my_id = tid < pnb ? bt[lb0 + tid] : 0;
+  const int Hq = P.Hkv * G;
+  const uint8_t *qbase = P.q + ((size_t)b * Hq + (size_t)h * G + min(lr, G - 1)) * ROWB;
+  uint4 qa[U];
+#pragma unroll
+  for (int j = 0; j < U; ++j) qa[j] = ld16(qbase + (lg * U + j) * 16);
+  // what the final step needs, loaded by every part so that the one
+  // arriving last has it at hand: the running scores and positions of the
+  // thread's slots, the new K / V row (lanes 0..CPR-1 of wave 0 hold K
+  // pieces, 32..32+CPR-1 V)
   float scv[kPer];
   int psv[kPer];
 #pragma unroll
@@ -93,58 +127,22 @@ __global__ __launch_bounds__(kThreads) void h2o_step_kernel(const H2oArgs P) {
     scv[k] = j < n ? sc[j] : 0.f;
     psv[k] = j < n ? ps[j] : 0;
   }
-  // the new K / V row: lanes 0..CPR-1 of wave 0 hold K pieces, 32..32+CPR-1 V
   uint4 newrow = make_uint4(0u, 0u, 0u, 0u);
   if (wv == 0 && (l & 31) < CPR)
     newrow = ld16((l < 32 ? P.k_new : P.v_new) + (size_t)u * ROWB + (size_t)(l & 31) * 16);
-  if (tid == 0) {
-    s_bad = 0;
-    s_fresh = -1;
+  if (tid == 0) s_code = 0;
+  __syncthreads();
+  if (tid < pnb) {
+    const bool bad = my_id < 0 || my_id >= P.num_blocks;
+    if (bad) s_code = -4;
+    s_bt[tid] = bad ? 0 : my_id;  // a bad id reads block 0; the head is refused below
   }
   __syncthreads();
-  if (tid < nbt) {
-    // the append slot's entry may be -1: a block is taken from the free list
-    const bool fresh_ok = append && tid == n / kBlock && n % kBlock == 0 && my_id < 0;
-    if (!fresh_ok && (my_id < 0 || my_id >= P.num_blocks)) s_bad = 1;
-    s_bt[tid] = my_id;
-  }
-  __syncthreads();
-  if (s_bad) {
-    if (tid == 0) P.evicted[u] = -4;
-    return;
-  }
-  if (tid == 0 && append && n % kBlock == 0 && s_bt[n / kBlock] < 0) {
-    const int old = atomicSub(P.free_count, 1);
-    int code = 0;
-    if (old <= 0) {
-      atomicAdd(P.free_count, 1);
-      code = -3;
-    } else {
-      const int blk = P.free_list[old - 1];
-      if (blk < 0 || blk >= P.num_blocks) code = -4;  // a bad entry stays taken
-      else {
-        s_bt[n / kBlock] = blk;
-        bt[n / kBlock] = blk;
-      }
-    }
-    s_fresh = code;
-  }
-  __syncthreads();
-  if (s_fresh < -1) {
-    if (tid == 0) P.evicted[u] = s_fresh;
-    return;
-  }
+  if (s_code && tid == 0) atomicOr(P.err + u, 1u);
 
-  // ---- logits of the G query rows (rows past G repeat the last one and are
-  // not stored): A = query rows, B = 16 keys of a block
-  const int Hq = P.Hkv * G;
-  const uint8_t *qbase = P.q + ((size_t)b * Hq + (size_t)h * G + min(lr, G - 1)) * ROWB;
-  uint4 qa[U];
-#pragma unroll
-  for (int j = 0; j < U; ++j) qa[j] = ld16(qbase + (lg * U + j) * 16);
   const float c1 = P.c1;
   const size_t lane_off = (size_t)lr * ROWB + (size_t)lg * (ROWB / 4);
-  if (wv == kWaves - 1) {
+  if (w == 0 && wv == kWaves - 1) {
     // the new key against every row: all 16 B columns are the same key
     uint4 kn[U];
 #pragma unroll
@@ -158,58 +156,162 @@ __global__ __launch_bounds__(kThreads) void h2o_step_kernel(const H2oArgs P) {
         if (4 * lg + e < G) s_newlg[4 * lg + e] = acc[e] * c1;
     }
   }
-  for (int lb0 = wv; lb0 < nb; lb0 += kWaves * NBK) {  // wave-uniform
+  for (int ib = wv; ib < pnb; ib += kWaves * NBK) {  // wave-uniform
+    // up to NBK blocks in flight; none past the part's last (each 16-byte
+    // load of this layout touches 32 cache lines, so address processing,
+    // not bandwidth, bounds a burst of them)
     uint4 kf[NBK][U];
     int kp[NBK];
 #pragma unroll
     for (int i = 0; i < NBK; ++i) {
-      const int lb = min(lb0 + i * kWaves, nb - 1);
-      const uint8_t *src = P.k_pool + (size_t)s_bt[lb] * kBlock * ROWB + lane_off;
+      const int lb = ib + i * kWaves;
+      if (lb < pnb) {
+        const uint8_t *src = P.k_pool + (size_t)s_bt[lb] * kBlock * ROWB + lane_off;
 #pragma unroll
-      for (int j = 0; j < U; ++j) kf[i][j] = ld16(src + 16 * j);
-      kp[i] = ps[lb * kBlock + lr];
+        for (int j = 0; j < U; ++j) kf[i][j] = ld16(src + 16 * j);
+        kp[i] = ps[(lb0 + lb) * kBlock + lr];
+      }
     }
 #pragma unroll
     for (int i = 0; i < NBK; ++i) {
-      const int lb = lb0 + i * kWaves;
-      if (lb >= nb) break;
+      const int lb = ib + i * kWaves;
+      if (lb >= pnb) break;
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < U; ++j) acc = mfma_unit<BF16>(qa[j], kf[i][j], acc);
-      const int slot = lb * kBlock + lr;
+      const int slot = (lb0 + lb) * kBlock + lr;
       const bool live = slot < n && kp[i] <= t;  // later positions are not attended
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (4 * lg + e < G) lgt[(4 * lg + e) * NP + slot] = live ? acc[e] * c1 : -__builtin_inff();
+        if (4 * lg + e < G) lgt[(4 * lg + e) * CS + lb * kBlock + lr] = live ? acc[e] * c1 : -__builtin_inff();
     }
   }
   __syncthreads();
-
-  // ---- log-sum-exp of each query row (log2 units), one wave per row
+  // the part's maximum and sum per row (one wave per row), then e of its slots
+  const int ps0 = lb0 * kBlock, pslots = max(0, min(lb1 * kBlock, n) - ps0);
   for (int g = wv; g < G; g += kWaves) {
-    const float *row = lgt + (size_t)g * NP;
-    float mx = s_newlg[g];
-    for (int j = l; j < n; j += kWave) mx = fmaxf(mx, row[j]);
+    const float *row = lgt + (size_t)g * CS;
+    float mx = w == 0 ? s_newlg[g] : -__builtin_inff();
+    for (int j = l; j < pslots; j += kWave) mx = fmaxf(mx, row[j]);
 #pragma unroll
     for (int o = kWave / 2; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
     float z = 0.f;
-    for (int j = l; j < n; j += kWave) z += __builtin_amdgcn_exp2f(row[j] - mx);
+    if (mx != -__builtin_inff()) {  // a part whose keys are all masked holds no weight
+      for (int j = l; j < pslots; j += kWave) z += __builtin_amdgcn_exp2f(row[j] - mx);
+    }
 #pragma unroll
     for (int o = kWave / 2; o >= 1; o >>= 1) z += __shfl_xor(z, o);
-    z += __builtin_amdgcn_exp2f(s_newlg[g] - mx);
-    if (l == 0) s_lse[g] = mx + __builtin_amdgcn_logf(z);
+    if (w == 0 && mx != -__builtin_inff()) z += __builtin_amdgcn_exp2f(s_newlg[g] - mx);
+    if (l == 0) {
+      s_m[g] = mx;
+      cst(ML + w * 32 + g, __float_as_uint(mx));
+      cst(ML + w * 32 + 16 + g, __float_as_uint(z));
+      if (w == 0) cst(E + (size_t)g * P.np + n, __float_as_uint(__builtin_amdgcn_exp2f(s_newlg[g] - mx)));
+    }
   }
   __syncthreads();
+  for (int i = tid; i < G * pslots; i += kThreads) {
+    const int g = i / pslots, j = i % pslots;
+    const float m = s_m[g];
+    const float e = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(lgt[(size_t)g * CS + j] - m);
+    cst(E + (size_t)g * P.np + ps0 + j, __float_as_uint(e));
+  }
+  // every published value has completed before the arrival is counted
+  drain();
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(P.arrive + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (uint32_t)(S - 1);
+  __syncthreads();
+  if (!s_last) return;
 
-  // ---- running scores, the new token's score, the candidates' minimum
+  // --------------------------------------------------------------- final
+  // one round of loads: every part's e values (into LDS, over the logits)
+  // and (m, l) of each row; thread 0 then settles the append block
+  const int etot = G * P.np;
+  float *EL = lgt;  // [G][np]
+  auto load_e = [&](int k0) {  // kEBatch loads per thread in flight, then to LDS
+    uint32_t ebuf[kEBatch];
+#pragma unroll
+    for (int k = 0; k < kEBatch; ++k) {
+      const int i = tid + (k0 + k) * kThreads;
+      ebuf[k] = i < etot ? cld(E + i) : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < kEBatch; ++k) {
+      const int i = tid + (k0 + k) * kThreads;
+      if (i < etot) EL[i] = __uint_as_float(ebuf[k]);
+    }
+  };
+  load_e(0);
+  float mq[kMaxSplit], lq[kMaxSplit];
+  if (tid < G) {
+#pragma unroll
+    for (int q = 0; q < kMaxSplit; ++q) {
+      mq[q] = q < S ? __uint_as_float(cld(ML + q * 32 + tid)) : -__builtin_inff();
+      lq[q] = q < S ? __uint_as_float(cld(ML + q * 32 + 16 + tid)) : 0.f;
+    }
+  }
+  if (tid == 0) {
+    cst(P.arrive + u, 0u);  // state for the next call
+    int code = 0;
+    if (cld(P.err + u)) {
+      cst(P.err + u, 0u);
+      code = -4;
+    }
+    int blk = -1;
+    if (!code && append) {
+      const int e = bt[n / kBlock];
+      if (e >= P.num_blocks || (e < 0 && n % kBlock != 0)) {
+        code = -4;
+      } else if (e >= 0) {
+        blk = e;
+      } else {  // the append opens a block: one from the top of the free list
+        const int old = atomicSub(P.free_count, 1);
+        if (old <= 0) {
+          atomicAdd(P.free_count, 1);
+          code = -3;
+        } else {
+          blk = P.free_list[old - 1];
+          if (blk < 0 || blk >= P.num_blocks) code = -4;  // a bad entry stays taken
+          else bt[n / kBlock] = blk;
+        }
+      }
+    }
+    s_code = code;
+    s_blk = blk;
+  }
+  for (int k0 = kEBatch; k0 * kThreads < etot; k0 += kEBatch) load_e(k0);  // large G * budget
+  // lse of each row from the parts' (m, l), parts in order; r = exp2(m - lse)
+  if (tid < G) {
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int q = 0; q < kMaxSplit; ++q) M = fmaxf(M, mq[q]);
+    float Z = 0.f;
+#pragma unroll
+    for (int q = 0; q < kMaxSplit; ++q)
+      if (mq[q] != -__builtin_inff()) Z += lq[q] * __builtin_amdgcn_exp2f(mq[q] - M);
+    const float lse = M + __builtin_amdgcn_logf(Z);
+#pragma unroll
+    for (int q = 0; q < kMaxSplit; ++q)
+      s_r[tid * kMaxSplit + q] = mq[q] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mq[q] - lse);
+  }
+  __syncthreads();
+  if (s_code) {
+    if (tid == 0) P.evicted[u] = s_code;
+    return;
+  }
+
+  // running scores, the new token's score, the candidates' minimum
   unsigned long long best = ~0ull;
   const long long R = P.recent;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int j = tid + k * kThreads;
     if (j < n) {
+      const int q = (j / kBlock) / cb;
       float p = 0.f;
-      for (int g = 0; g < G; ++g) p += __builtin_amdgcn_exp2f(lgt[(size_t)g * NP + j] - s_lse[g]);
+      for (int g = 0; g < G; ++g) p += EL[(size_t)g * P.np + j] * s_r[g * kMaxSplit + q];
       scv[k] += p;
       if ((long long)t - psv[k] >= R) {
         const unsigned long long c = pack_min(scv[k], psv[k]);
@@ -217,9 +319,9 @@ __global__ __launch_bounds__(kThreads) void h2o_step_kernel(const H2oArgs P) {
       }
     }
   }
-  float snew = 0.f;
   if (tid == 0) {
-    for (int g = 0; g < G; ++g) snew += __builtin_amdgcn_exp2f(s_newlg[g] - s_lse[g]);
+    float snew = 0.f;
+    for (int g = 0; g < G; ++g) snew += EL[(size_t)g * P.np + n] * s_r[g * kMaxSplit];
     s_snew = snew;
     if (R == 0) {  // the new token competes too
       const unsigned long long c = pack_min(snew, t);
@@ -232,7 +334,7 @@ __global__ __launch_bounds__(kThreads) void h2o_step_kernel(const H2oArgs P) {
   __syncthreads();
   unsigned long long m = s_wmin[0];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) m = s_wmin[w] < m ? s_wmin[w] : m;
+  for (int q = 1; q < kWaves; ++q) m = s_wmin[q] < m ? s_wmin[q] : m;
   int victim_k = -1;  // which of this thread's slots is pruned
   if (!append && m != ~0ull) {
 #pragma unroll
@@ -246,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void h2o_step_kernel(const H2oArgs P) {
   }
   __syncthreads();
 
-  // ---- writes: each score once; the new token at slot dst
+  // writes: each score once; the new token at slot dst
   const int dst = s_dst;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
@@ -267,14 +369,16 @@ __global__ __launch_bounds__(kThreads) void h2o_step_kernel(const H2oArgs P) {
     }
   }
   if (wv == 0 && dst >= 0 && (l & 31) < CPR) {
-    const size_t row = (size_t)s_bt[dst / kBlock] * kBlock + dst % kBlock;
+    const int blk = append ? s_blk : bt[dst / kBlock];
+    const size_t row = (size_t)blk * kBlock + dst % kBlock;
     st16((l < 32 ? P.k_pool : P.v_pool) + row * ROWB + (size_t)(l & 31) * 16, newrow);
   }
 }
 
 hipError_t launch_h2o_step(const H2oArgs &a, int bf16, int head_dim, hipStream_t s) {
+  // the final step's e values ([G][np]) exceed any part's logits ([G][cb*16])
   const size_t lds = (size_t)a.G * a.np * sizeof(float);
-  const dim3 grid((unsigned)a.units), block(kThreads);
+  const dim3 grid((unsigned)(a.units * a.split)), block(kThreads);
   if (bf16) {
     if (head_dim == 128) hipLaunchKernelGGL((h2o_step_kernel<true, 128>), grid, block, lds, s, a);
     else hipLaunchKernelGGL((h2o_step_kernel<true, 64>), grid, block, lds, s, a);

@@ -91,8 +91,12 @@ struct H2oArgs {
   const int32_t *t_pos;                // [B]
   int32_t *free_list, *free_count;
   int32_t *evicted;                    // [units]
+  // workspace: e values [units][G][np], part maxima and sums [units][8][32],
+  // state (zero between calls) arrival counters and error flags [units]
+  uint32_t *e, *ml, *arrive, *err;
   int32_t units, Hkv, G, max_blocks, max_slots, num_blocks, budget, recent;
-  int32_t np;                          // LDS row stride of the logits (budget rounded up to 16)
+  int32_t np;                          // budget rounded up to 16, plus 16 (the new token's e)
+  int32_t split;                       // workgroups per head
   float c1;                            // scale * log2(e)
 };
 hipError_t launch_h2o_step(const H2oArgs &a, int bf16, int head_dim, hipStream_t s);
@@ -123,6 +127,7 @@ constexpr int kCompactMaxUnits = 4096;  // compact.hip gather limit
 constexpr int kCompactChunk = 1024;     // compact.hip prep chunk (slots)
 constexpr int kH2oMaxBudget = 4096;    // h2o_step.hip: tokens per head
 constexpr int kH2oMaxLogits = 16384;   // h2o_step.hip: G * budget (64 KB of LDS)
+constexpr int kH2oMaxSplit = 8;        // h2o_step.hip: workgroups per head
 
 // LDS bytes of one score workgroup (fused: room for the tile histogram and
 // the head selection).

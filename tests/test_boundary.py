@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
     assert set(names) == set(K.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvev_abi_version() == K.ABI_VERSION == 4
+    assert L.kvev_abi_version() == K.ABI_VERSION == 5
     for code in (0, -1, -2, -3, -4):
         assert K.strerror(code)
 
@@ -246,12 +246,13 @@ def test_h2o_step_refusals():
     """Every refusal of kvev_h2o_step is decided on the host, before a launch."""
     L = K.load_library()
 
-    def call(c=None, group=4, budget=64, recent=8, ptrs=None):
+    def call(c=None, group=4, budget=64, recent=8, ptrs=None, ws_bytes=1 << 30):
         c = cache(max_blocks=8) if c is None else c
-        p = dict(q=FAKE, k=FAKE, v=FAKE, t=FAKE, s=FAKE, fl=FAKE, fc=FAKE, ev=FAKE)
+        p = dict(q=FAKE, k=FAKE, v=FAKE, t=FAKE, s=FAKE, fl=FAKE, fc=FAKE, ev=FAKE, ws=FAKE)
         p.update(ptrs or {})
         return L.kvev_h2o_step(ctypes.byref(c), p["q"], p["k"], p["v"], p["t"], group, 0.1,
-                               p["s"], budget, recent, p["fl"], p["fc"], p["ev"], None)
+                               p["s"], budget, recent, p["fl"], p["fc"], p["ev"], p["ws"],
+                               ws_bytes, None)
 
     for name in ("q", "k", "v", "t", "s", "fl", "fc", "ev"):
         assert call(ptrs={name: None}) == K.EINVAL, name
@@ -266,3 +267,11 @@ def test_h2o_step_refusals():
     big = cache(max_blocks=300)
     assert call(c=big, group=1, budget=4097) == K.EUNSUPPORTED
     assert call(c=big, group=8, budget=2050) == K.EUNSUPPORTED  # 8 * 2064 logits > 16384
+    need = L.kvev_h2o_workspace_bytes(ctypes.byref(cache(max_blocks=8)), 4, 64)
+    assert need > 0
+    assert call(ptrs={"ws": None}) == K.ENOSPACE
+    assert call(ws_bytes=need - 1) == K.ENOSPACE
+    # the size query refuses what the step refuses
+    assert L.kvev_h2o_workspace_bytes(ctypes.byref(cache(max_blocks=8)), 0, 64) == 0
+    assert L.kvev_h2o_workspace_bytes(ctypes.byref(cache(max_blocks=8)), 4, 5000) == 0
+    assert L.kvev_h2o_workspace_bytes(None, 4, 64) == 0
