@@ -61,17 +61,17 @@ def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def read_traffic(workload, kernel_src):
-    """HBM bytes per launch of the score kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
-    p = os.path.join(ROOT, "profiles", f"score_{workload}_hbm_counters.json")
+def read_traffic(workload, kernel_src, kernel="score", sha_key="score_source_sha256_16"):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.json")
     if not os.path.exists(p):
         return None
     try:
         d = json.load(open(p))
     except ValueError:
         return None
-    if d.get("score_source_sha256_16") != source_hash(kernel_src):
+    if d.get(sha_key) != source_hash(kernel_src):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -414,6 +414,9 @@ def bench_h2o_stream(args, cfg):
                   + units * math.ceil(n / 16) * 4   # block ids
                   + units * 2 * D * eb * 2)         # new K / V row, read and written
     achieved = step_bytes / (ms_step / 1e3) / 1e9
+    traffic = read_traffic(args.workload,
+                           os.path.join(ROOT, "kv_cache_eviction_qk_amd", "csrc", "h2o_step.hip"),
+                           kernel="h2o_step", sha_key="source_sha256_16")
     cpu = None if args.no_cpu_baseline else cpu_baseline_h2o(case, cfg, fill)
     out = {
         "metric": "H2O decode steps: tokens/sec (attend+accumulate+prune+overwrite per step)",
@@ -436,7 +439,7 @@ def bench_h2o_stream(args, cfg):
         "eager_ms_per_step": ms_eager,
         "roofline": {"kernel": "h2o_step_kernel (kvev_h2o_step)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": step_bytes, "launch_ms": ms_step},
         "cpu_baseline": cpu,
     }
