@@ -67,7 +67,7 @@ def lib():
         L.orc_compact.argtypes = [P, P, i32, i32, P, P, P, P, i32, i32, P, P, P, P, i32, P]
         L.orc_measure.argtypes = [P, P, P, i32, i32, P]
         L.orc_h2o_step.argtypes = [P, P, i32, i32, P, P, P, P, i32, i32, i32, i32, i32, P, P, P,
-                                   P, ctypes.c_double, i32, i32, P, P, P]
+                                   P, ctypes.c_double, i32, i32, P, P, P, P, P]
         for f in (L.orc_lse_a, L.orc_score, L.orc_select, L.orc_compact, L.orc_measure,
                   L.orc_h2o_step):
             f.restype = ctypes.c_int
@@ -193,11 +193,13 @@ def measure(seq_len_before: np.ndarray, victims: np.ndarray, n_victims: np.ndarr
 
 def h2o_step(state: dict, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
              t_pos: np.ndarray, budget: int, recent: int, free_list: Optional[np.ndarray] = None,
-             free_count: int = 0):
+             free_count: int = 0, want_attn: bool = False):
     """One H2O decode step on a COPY of `state` (a case dict plus 'score', the
     running fp32 score [B,Hkv,max_slots]).  q [B,Hq,D], k_new / v_new
     [B,Hkv,D] in the cache dtype, t_pos [B].  Returns (new_state, evicted_pos
-    [B,Hkv], free_list, free_count)."""
+    [B,Hkv], free_list, free_count), plus, with want_attn, the attention
+    output [B,Hq,D] and its sum_j p_j |v_j| [B,Hq,D] (double; NaN for heads
+    that were refused)."""
     new = dict(state)
     for k in ("k_pool", "v_pool", "block_table", "seq_len", "pos"):
         new[k] = state[k].copy()
@@ -209,6 +211,8 @@ def h2o_step(state: dict, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
     fc = np.array([free_count], np.int32)
     ev = np.zeros((B, Hkv), np.int32)
     edt = np.uint16 if state["dtype"] == "bf16" else np.float32
+    attn = np.full((B, Hkv * state["G"], state["D"]), np.nan) if want_attn else None
+    aabs = np.full((B, Hkv * state["G"], state["D"]), np.nan) if want_attn else None
     rc = lib().orc_h2o_step(_p(new["k_pool"]), _p(new["v_pool"]),
                             1 if state["dtype"] == "bf16" else 0, state["D"],
                             _p(new["block_table"]), _p(new["seq_len"]), _p(new["pos"]),
@@ -217,8 +221,10 @@ def h2o_step(state: dict, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
                             _p(np.ascontiguousarray(k_new, dtype=edt)),
                             _p(np.ascontiguousarray(v_new, dtype=edt)),
                             _p(np.ascontiguousarray(t_pos, dtype=np.int32)), float(state["scale"]),
-                            budget, recent, _p(free_list), _p(fc), _p(ev))
+                            budget, recent, _p(free_list), _p(fc), _p(ev), _p(attn), _p(aabs))
     if rc != 0:
         raise ValueError(f"oracle h2o_step refused the arguments (rc={rc})")
+    if want_attn:
+        return new, ev, free_list, int(fc[0]), attn, aabs
     return new, ev, free_list, int(fc[0])
 

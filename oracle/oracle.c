@@ -430,7 +430,8 @@ int orc_h2o_step(void *k_pool, void *v_pool, int32_t is_bf16, int32_t head_dim,
                  int32_t batch, int32_t kv_heads, int32_t max_blocks, int32_t num_blocks,
                  int32_t group, const void *q, const void *k_new, const void *v_new,
                  const int32_t *t_pos, double scale, int32_t budget, int32_t recent,
-                 int32_t *free_list, int32_t *free_count, int32_t *evicted_pos) {
+                 int32_t *free_list, int32_t *free_count, int32_t *evicted_pos,
+                 double *attn_out, double *attn_abs) {
   if (!k_pool || !v_pool || !block_table || !seq_len || !pos || !score || !q || !k_new || !v_new ||
       !t_pos || !free_list || !free_count || !evicted_pos)
     return -1;
@@ -493,6 +494,25 @@ int orc_h2o_step(void *k_pool, void *v_pool, int32_t is_bf16, int32_t head_dim,
       double z = 0.0;
       for (int64_t j = 0; j <= n; ++j) z += exp(s[g * (budget + 1) + j] - mx);
       lse[g] = mx + log(z);
+    }
+    /* the step's attention output: the same weights on the values */
+    if (attn_out || attn_abs) {
+      const char *vnew = (const char *)v_new + u * row_bytes;
+      for (int64_t g = 0; g < G; ++g) {
+        const int64_t qrow = (b * kv_heads + h) * G + g;
+        for (int64_t d = 0; d < D; ++d) {
+          double acc = 0.0, aabs = 0.0;
+          for (int64_t j = 0; j <= n; ++j) {
+            const double p = exp(s[g * (budget + 1) + j] - lse[g]);
+            const double vd = j < n ? widen(v_pool, is_bf16, ((int64_t)bt[j / 16] * 16 + j % 16) * D + d)
+                                    : widen(vnew, is_bf16, d);
+            acc += p * vd;
+            aabs += p * fabs(vd);
+          }
+          if (attn_out) attn_out[qrow * D + d] = acc;
+          if (attn_abs) attn_abs[qrow * D + d] = aabs;
+        }
+      }
     }
     /* the running scores after this step's attention (g ascending) */
     float s_new;

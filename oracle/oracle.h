@@ -97,13 +97,18 @@ int orc_measure(const int32_t *seq_len_before, const int32_t *victims, const int
  * new token itself was dropped, or no cached token is a candidate), or -2
  * (n < 0 or n > budget), -3 (no free block), -4 (block id out of range; a
  * bad id taken from the free list stays taken): on a negative code other
- * than -1 the head is left unchanged.  Returns 0, or -1 on invalid arguments. */
+ * than -1 the head is left unchanged.  attn_out (may be NULL): the step's
+ * attention output of each query row, sum_j p_j v_j over the same keys and
+ * the new token ([B][kv_heads*G][head_dim], double, written for the heads
+ * that are not refused); attn_abs (may be NULL): sum_j p_j |v_j| alike, the
+ * scale of its rounding error.  Returns 0, or -1 on invalid arguments. */
 int orc_h2o_step(void *k_pool, void *v_pool, int32_t is_bf16, int32_t head_dim,
                  int32_t *block_table, int32_t *seq_len, int32_t *pos, float *score,
                  int32_t batch, int32_t kv_heads, int32_t max_blocks, int32_t num_blocks,
                  int32_t group, const void *q, const void *k_new, const void *v_new,
                  const int32_t *t_pos, double scale, int32_t budget, int32_t recent,
-                 int32_t *free_list, int32_t *free_count, int32_t *evicted_pos);
+                 int32_t *free_list, int32_t *free_count, int32_t *evicted_pos,
+                 double *attn_out, double *attn_abs);
 
 #ifdef __cplusplus
 }

@@ -15,6 +15,9 @@ the mathematics fix.  CPU only.
     plus the new token.
   * Edge cases: recent = 0 (the new token itself can be pruned), appends that
     take a block from the free list in (b, h) order, and the refusals.
+  * The step's attention output equals the input builder's (oracle.lse_a, an
+    independent function) on the chain's appended cache; equal keys give the
+    mean of the value rows; a dominant key gives its own value row.
 """
 import numpy as np
 import pytest
@@ -57,6 +60,12 @@ def _state(keys, vals, n0, capacity, G, dtype="f32", scale=None, seq_len=None, *
 
 def _enc(x, st):
     return synth.encode(np.asarray(x, np.float64), st["dtype"])
+
+
+def _step_attn(st, keys, vals, qs, t, budget, recent, **kw):
+    B = st["B"]
+    return oracle.h2o_step(st, _enc(qs[t], st), _enc(keys[:, :, t], st), _enc(vals[:, :, t], st),
+                           np.full(B, t, np.int32), budget, recent, want_attn=True, **kw)
 
 
 def _step(st, keys, vals, qs, t, budget, recent, **kw):
@@ -102,7 +111,7 @@ def test_step_equals_append_accumulate_select_compact(seed, budget, recent):
     ch = _state(keys, vals, 0, budget + 1, G)  # one slot past the budget for the append
     acc = np.zeros((B, Hkv, ch["max_blocks"] * 16), np.float32)
     for t in range(T):
-        st, ev, _, _ = _step(st, keys, vals, qs, t, budget, recent)
+        st, ev, _, _, attn, aabs = _step_attn(st, keys, vals, qs, t, budget, recent)
         # the chain: append at slot n, accumulate, then evict down to the budget
         n = int(ch["seq_len"][0, 0])
         for b in range(B):
@@ -115,7 +124,9 @@ def test_step_equals_append_accumulate_select_compact(seed, budget, recent):
         acc[:, :, n] = 0.0
         ch["q"] = np.ascontiguousarray(qs[t][:, :, None, :], np.float32)
         ch["q_pos"] = np.full((B, 1), t, np.int32)
-        lse64, _ = oracle.lse_a(ch)
+        lse64, a64 = oracle.lse_a(ch, want_a=True)
+        # the step's attention output is the input builder's, over the same keys
+        assert np.all(np.abs(attn - a64[:, :, 0, :]) <= 1e-12 * aabs + 1e-300), t
         lse32, _ = rounded_window_inputs(ch, lse64)
         acc = oracle.score(ch, lse32, oracle.SUM | oracle.ACCUMULATE, prev_sum=acc)["sum"]
         acc = np.nan_to_num(acc, nan=0.0).astype(np.float32)
@@ -257,3 +268,31 @@ def test_refusals_leave_heads_unchanged():
     with pytest.raises(ValueError):
         oracle.h2o_step(st2, _enc(qs[0], st2), _enc(keys[:, :, 0], st2), _enc(vals[:, :, 0], st2),
                         np.array([0], np.int32), budget, budget)  # recent >= budget
+
+
+def test_attention_output_closed_forms():
+    """Equal keys: the output is the mean of the n cached value rows and the new
+    one.  One key far above the others: the output is that key's value row."""
+    B, Hkv, G, D, n, budget = 1, 2, 3, 16, 10, 12
+    keys = np.ones((B, Hkv, n + 1, D)) * 0.25
+    vals = rng(61).normal(0, 1, (B, Hkv, n + 1, D))
+    qs = rng(62).normal(0, 1, (n + 1, B, Hkv * G, D))
+    st = _state(keys, vals, n, budget, G)
+    _, ev, _, _, attn, aabs = oracle.h2o_step(st, _enc(qs[n], st), _enc(keys[:, :, n], st),
+                                              _enc(vals[:, :, n], st), np.full(B, n, np.int32),
+                                              budget, 2, want_attn=True)
+    assert (ev == -1).all()
+    v32 = synth.decode(_enc(vals, st), "f32").astype(np.float64)
+    mean = v32.mean(axis=2)                                   # [B, Hkv, D]
+    want = np.repeat(mean, G, axis=1)                         # every row of the group
+    assert np.allclose(attn, want, rtol=1e-12, atol=1e-12)
+    assert np.all(aabs >= np.abs(attn) - 1e-12)
+    # a dominant key: the planted token draws all the weight
+    keys2, vals2, qs2 = _stream_inputs(63, 1, 1, 4, 32, 9, plant=4.0, plant_at=3)
+    st2 = _state(keys2, vals2, 8, 12, 4, scale=1.0)
+    _, _, _, _, attn2, _ = oracle.h2o_step(st2, _enc(qs2[8], st2), _enc(keys2[:, :, 8], st2),
+                                           _enc(vals2[:, :, 8], st2), np.full(1, 8, np.int32),
+                                           12, 2, want_attn=True)
+    v3 = synth.decode(_enc(vals2[0, 0, 3], st2), "f32").astype(np.float64)
+    assert np.allclose(attn2[0], np.repeat(v3[None], 4, axis=0), rtol=0, atol=1e-9)
+
