@@ -55,7 +55,7 @@ extern "C" {
 #endif
 
 #define KVEV_BLOCK_SIZE 16
-#define KVEV_ABI_VERSION 5
+#define KVEV_ABI_VERSION 6
 
 typedef enum {
   KVEV_OK = 0,
@@ -257,6 +257,12 @@ int kvev_measure(const int32_t *seq_len_before, const int32_t *victims,
  *     is the smallest it is dropped and the cache keeps its tokens.
  * Slot order then no longer follows position order: do not pool (KVEV_POOL)
  * or compact such a cache expecting positional neighbours.
+ * attn_out (may be NULL): fp32 [batch][kv_heads*group][head_dim], the step's
+ * attention output sum_j p_g,j v_j over the same keys and the new token (the
+ * value rows are read only when it is given), so one pass over the cache
+ * serves the decode attention and the eviction ([H2O] "Score Accumulation":
+ * the scores come from the attention softmax itself); not written for a
+ * refused head.
  * q: [batch][kv_heads*group][head_dim], k_new / v_new:
  * [batch][kv_heads][head_dim], all in the cache dtype; t_pos: int32 [batch];
  * score: fp32 [batch][kv_heads][max_blocks*16], the running scores (read and
@@ -274,13 +280,15 @@ int kvev_measure(const int32_t *seq_len_before, const int32_t *victims,
  * Errors: KVEV_EINVAL for NULL pointers, a bad cache, group < 1,
  * budget <= 0 or above max_blocks * 16, recent_window < 0 or >= budget;
  * KVEV_EUNSUPPORTED for group > 16, budget > 4096 or group * budget (rounded
- * up to 16) > 16384; KVEV_ENOSPACE for a missing or short workspace.
+ * up to 16) > 16384, or, with attn_out, a shape whose workgroup would need
+ * more than 156 KiB of LDS (large groups with large budgets and few heads);
+ * KVEV_ENOSPACE for a missing or short workspace.
  */
 int kvev_h2o_step(const kvev_cache *cache, const void *q, const void *k_new, const void *v_new,
                   const int32_t *t_pos, int32_t group, float scale, float *score,
                   int32_t budget, int32_t recent_window, int32_t *free_list,
-                  int32_t *free_count, int32_t *evicted_pos, void *workspace,
-                  size_t ws_bytes, void *stream);
+                  int32_t *free_count, int32_t *evicted_pos, float *attn_out,
+                  void *workspace, size_t ws_bytes, void *stream);
 
 /* Workspace bytes kvev_h2o_step needs for this cache, group and budget; 0
  * for a bad cache or a group / budget it refuses. */

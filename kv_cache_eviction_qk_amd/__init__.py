@@ -32,7 +32,7 @@ BLOCK_SIZE = 16
 EXPORTS = ("kvev_score", "kvev_select", "kvev_compact", "kvev_evict", "kvev_measure",
            "kvev_h2o_step", "kvev_h2o_workspace_bytes", "kvev_window_attn",
            "kvev_workspace_bytes", "kvev_strerror", "kvev_abi_version")
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class KvevError(RuntimeError):
@@ -78,7 +78,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kvev_evict.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P, P, i32, P, P, sz, P]
     L.kvev_window_attn.argtypes = [P, P, P, P, P, sz, P]
     L.kvev_measure.argtypes = [P, P, P, i32, i32, P, P]
-    L.kvev_h2o_step.argtypes = [P, P, P, P, P, i32, ctypes.c_float, P, i32, i32, P, P, P, P,
+    L.kvev_h2o_step.argtypes = [P, P, P, P, P, i32, ctypes.c_float, P, i32, i32, P, P, P, P, P,
                                 sz, P]
     L.kvev_h2o_workspace_bytes.argtypes = [P, i32, i32]
     L.kvev_h2o_workspace_bytes.restype = sz
@@ -356,12 +356,14 @@ def h2o_step(cache: Cache, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Te
              t_pos: torch.Tensor, group: int, scale: float, score: torch.Tensor, budget: int,
              recent: int, free_list: torch.Tensor, free_count: torch.Tensor,
              workspace: torch.Tensor, evicted: Optional[torch.Tensor] = None,
-             stream=None) -> torch.Tensor:
+             attn_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """kvev_h2o_step: one decode step of every KV head.  q [B, Hq, D], k_new and
     v_new [B, Hkv, D] in the cache dtype; t_pos int32 [B]; score fp32 [B, Hkv,
     max_slots] (running scores, updated); free_list int32, free_count int32
-    [1]; workspace from new_h2o_workspace.  Returns evicted int32 [B, Hkv] (-1
-    appended, else the pruned position; -2, -3, -4 for a head left unchanged)."""
+    [1]; workspace from new_h2o_workspace; attn_out (optional) fp32 [B, Hq,
+    D] receives the step's attention output.  Returns evicted int32 [B, Hkv]
+    (-1 appended, else the pruned position; -2, -3, -4 for a head left
+    unchanged)."""
     L = load_library()
     c = cache.struct()
     B, Hkv, D = cache.batch, cache.kv_heads, cache.head_dim
@@ -376,9 +378,12 @@ def h2o_step(cache: Cache, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Te
     if evicted is None:
         evicted = torch.empty((B, Hkv), dtype=torch.int32, device=q.device)
     _need(evicted, "evicted", torch.int32, B * Hkv)
+    if attn_out is not None:
+        _need(attn_out, "attn_out", torch.float32, B * Hkv * group * D)
     rc = L.kvev_h2o_step(ctypes.byref(c), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(t_pos), group,
                          scale, _ptr(score), budget, recent, _ptr(free_list), _ptr(free_count),
-                         _ptr(evicted), _ptr(workspace), workspace.numel(), _stream(stream))
+                         _ptr(evicted), _ptr(attn_out), _ptr(workspace), workspace.numel(),
+                         _stream(stream))
     _check(rc, "kvev_h2o_step")
     return evicted
 

@@ -168,7 +168,7 @@ int kvev_measure(const int32_t *seq_len_before, const int32_t *victims,
 // Workspace of kvev_h2o_step: [arrival counters | error flags] (state, zero
 // between calls) then the parts' e values and (max, sum) per row.
 struct H2oLayout {
-  size_t arrive, err, e, ml, total;
+  size_t arrive, err, e, ml, o, total;
   int np, nbmax;
 };
 
@@ -182,6 +182,7 @@ H2oLayout h2o_layout(const kvev_cache *c, int32_t group, int32_t budget) {
   L.err = off; off = a256(off + units * 4);
   L.e = off; off = a256(off + units * (size_t)group * L.np * 4);
   L.ml = off; off = a256(off + units * (size_t)kvev::kH2oMaxSplit * 32 * 4);
+  L.o = off; off = a256(off + units * (size_t)kvev::kH2oMaxSplit * group * c->head_dim * 4);
   L.total = off;
   return L;
 }
@@ -196,8 +197,8 @@ size_t kvev_h2o_workspace_bytes(const kvev_cache *cache, int32_t group, int32_t 
 int kvev_h2o_step(const kvev_cache *cache, const void *q, const void *k_new, const void *v_new,
                   const int32_t *t_pos, int32_t group, float scale, float *score,
                   int32_t budget, int32_t recent_window, int32_t *free_list,
-                  int32_t *free_count, int32_t *evicted_pos, void *workspace, size_t ws_bytes,
-                  void *stream) {
+                  int32_t *free_count, int32_t *evicted_pos, float *attn_out, void *workspace,
+                  size_t ws_bytes, void *stream) {
   if (!valid_cache(cache) || !q || !k_new || !v_new || !t_pos || !score || !free_list ||
       !free_count || !evicted_pos)
     return KVEV_EINVAL;
@@ -229,6 +230,8 @@ int kvev_h2o_step(const kvev_cache *cache, const void *q, const void *k_new, con
   a.err = reinterpret_cast<uint32_t *>(ws + L.err);
   a.e = reinterpret_cast<uint32_t *>(ws + L.e);
   a.ml = reinterpret_cast<uint32_t *>(ws + L.ml);
+  a.o = reinterpret_cast<float *>(ws + L.o);
+  a.attn = attn_out;
   a.units = cache->batch * cache->kv_heads;
   a.Hkv = cache->kv_heads;
   a.G = group;
@@ -242,6 +245,9 @@ int kvev_h2o_step(const kvev_cache *cache, const void *q, const void *k_new, con
   const int want = (256 + a.units - 1) / a.units;
   a.split = std::max(1, std::min({want, kvev::kH2oMaxSplit, L.nbmax}));
   a.c1 = scale * 1.4426950408889634f;
+  // the shapes the limits above admit can still need more LDS with the
+  // attention output (rows rounded up to 4, few parts): refuse those
+  if (kvev::h2o_lds_bytes(a, cache->head_dim) > kMaxLds - 4096) return KVEV_EUNSUPPORTED;
   return map_err(kvev::launch_h2o_step(a, cache->dtype == KVEV_BF16, cache->head_dim,
                                        static_cast<hipStream_t>(stream)));
 }

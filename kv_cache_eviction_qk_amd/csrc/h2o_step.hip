@@ -30,6 +30,9 @@
 // counter atomic; the cache itself is written by the final workgroup alone.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <type_traits>
+
 #include "kvev_device.h"
 #include "kvev_kernels.h"
 
@@ -42,6 +45,7 @@ constexpr int kPer = kH2oMaxBudget / kThreads;       // slots per thread (4)
 constexpr int kMaxBlocksH = kH2oMaxBudget / kBlock;  // 256
 constexpr int kMaxSplit = kH2oMaxSplit;            // workgroups per head at most
 constexpr int kEBatch = 8;  // e values per thread per round of loads in the final step
+
 
 __device__ __forceinline__ unsigned long long pack_min(float v, int p) {
   // (score key, position) ordered as one unsigned word; the sign flip keeps
@@ -76,11 +80,16 @@ __device__ __forceinline__ void drain() {
 template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void h2o_step_kernel(const H2oArgs P) {
   constexpr int EB = BF16 ? 2 : 4, ROWB = D * EB, U = ROWB / 64, CPR = ROWB / 16;
-  constexpr int NBK = U >= 8 ? 1 : 16 / U;  // blocks per load batch of a wave (register budget)
+  constexpr int NBK = U >= 8 ? 1 : 8 / U;  // blocks per load batch of a wave (register budget)
+  // the value rows for the attention output: thread = (key group, column
+  // pair), VB keys per thread per batch, the first batch loaded with the keys
+  constexpr int NCP = D / 2, NKG = kThreads / NCP;
+  constexpr int VB = BF16 ? 16 : 8;
+  using VRaw = typename std::conditional<BF16, uint32_t, float2>::type;
   extern __shared__ float lgt[];  // part: [G][cb*16] logits (log2 units); final: [G][np] e values
   __shared__ int s_bt[kMaxBlocksH];
   __shared__ unsigned long long s_wmin[kWaves];
-  __shared__ float s_m[16], s_newlg[16], s_r[16 * kMaxSplit];
+  __shared__ float s_m[16], s_newlg[16], s_enew[16], s_r[16 * kMaxSplit];
   __shared__ float s_snew;
   __shared__ int s_last, s_dst, s_code, s_blk;
 
@@ -139,6 +148,27 @@ __global__ __launch_bounds__(kThreads) void h2o_step_kernel(const H2oArgs P) {
   }
   __syncthreads();
   if (s_code && tid == 0) atomicOr(P.err + u, 1u);
+  const int ps0 = lb0 * kBlock, pslots = max(0, min(lb1 * kBlock, n) - ps0);
+  const int cp = tid % NCP, kg = tid / NCP;
+  VRaw vpre[VB];
+  auto load_v = [&](int j0, VRaw (&vr)[VB]) {
+#pragma unroll
+    for (int q = 0; q < VB; ++q) {
+      const int j = min(j0 + q * NKG, max(pslots - 1, 0));  // past the end: a repeat, not used
+      const size_t row = (size_t)s_bt[j / kBlock] * kBlock + j % kBlock;
+      vr[q] = *reinterpret_cast<const VRaw *>(P.v_pool + row * ROWB + cp * sizeof(VRaw));
+    }
+  };
+  if (P.attn && pslots > 0) load_v(kg, vpre);
+  // the new token's value at column tid % D (part 0 adds e_new * v_new)
+  float vnew = 0.f;
+  if (P.attn && w == 0) {
+    const int d = tid % D;
+    if constexpr (BF16)
+      vnew = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(P.v_new + (size_t)u * ROWB)[d] << 16);
+    else
+      vnew = reinterpret_cast<const float *>(P.v_new + (size_t)u * ROWB)[d];
+  }
 
   const float c1 = P.c1;
   const size_t lane_off = (size_t)lr * ROWB + (size_t)lg * (ROWB / 4);
@@ -188,7 +218,6 @@ __global__ __launch_bounds__(kThreads) void h2o_step_kernel(const H2oArgs P) {
   }
   __syncthreads();
   // the part's maximum and sum per row (one wave per row), then e of its slots
-  const int ps0 = lb0 * kBlock, pslots = max(0, min(lb1 * kBlock, n) - ps0);
   for (int g = wv; g < G; g += kWaves) {
     const float *row = lgt + (size_t)g * CS;
     float mx = w == 0 ? s_newlg[g] : -__builtin_inff();
@@ -206,7 +235,9 @@ __global__ __launch_bounds__(kThreads) void h2o_step_kernel(const H2oArgs P) {
       s_m[g] = mx;
       cst(ML + w * 32 + g, __float_as_uint(mx));
       cst(ML + w * 32 + 16 + g, __float_as_uint(z));
-      if (w == 0) cst(E + (size_t)g * P.np + n, __float_as_uint(__builtin_amdgcn_exp2f(s_newlg[g] - mx)));
+      const float enew = w == 0 ? __builtin_amdgcn_exp2f(s_newlg[g] - mx) : 0.f;
+      s_enew[g] = enew;
+      if (w == 0) cst(E + (size_t)g * P.np + n, __float_as_uint(enew));
     }
   }
   __syncthreads();
@@ -215,6 +246,66 @@ __global__ __launch_bounds__(kThreads) void h2o_step_kernel(const H2oArgs P) {
     const float m = s_m[g];
     const float e = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(lgt[(size_t)g * CS + j] - m);
     cst(E + (size_t)g * P.np + ps0 + j, __float_as_uint(e));
+    if (P.attn) lgt[(size_t)g * CS + j] = e;  // the P.V product below reads them
+  }
+  if (P.attn) {
+    // the part's share of the attention output, o[g][d] = sum_j e[g][j] v[j][d]
+    // (plus e_new v_new in part 0), in fp32 on the VALU: thread = (key
+    // group, column pair); a wave reads whole value rows; rows four at a
+    // time; the key groups summed in order through LDS
+    __syncthreads();
+    float *red = lgt + (size_t)G * P.np;  // [NKG][4][D], after the e values
+    float *O = P.o + ((size_t)u * kMaxSplit + w) * G * D;
+    for (int g0 = 0; g0 < G; g0 += 4) {
+      float a0[4] = {0.f, 0.f, 0.f, 0.f}, a1[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int j0 = kg; j0 < pslots; j0 += NKG * VB) {
+        VRaw vr[VB];
+        if (j0 == kg) {
+#pragma unroll
+          for (int q = 0; q < VB; ++q) vr[q] = vpre[q];
+        } else {
+          load_v(j0, vr);  // heads longer than one batch per part
+        }
+        // branch-free, so the LDS reads of the batch can all be in flight:
+        // keys past the part and rows past G read a valid address and weigh 0
+#pragma unroll
+        for (int q = 0; q < VB; ++q) {
+          const int j = j0 + q * NKG;
+          const bool jin = j < pslots;
+          const int jc = jin ? j : 0;
+          float v0, v1;
+          if constexpr (BF16) {
+            v0 = __uint_as_float(vr[q] << 16);
+            v1 = __uint_as_float(vr[q] & 0xffff0000u);
+          } else {
+            v0 = vr[q].x;
+            v1 = vr[q].y;
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool in = jin && g0 + r < G;
+            const float e = lgt[(size_t)min(g0 + r, G - 1) * CS + jc];
+            a0[r] = fmaf(in ? e : 0.f, v0, a0[r]);
+            a1[r] = fmaf(in ? e : 0.f, v1, a1[r]);
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        red[((size_t)kg * 4 + r) * D + 2 * cp] = a0[r];
+        red[((size_t)kg * 4 + r) * D + 2 * cp + 1] = a1[r];
+      }
+      __syncthreads();
+      for (int i = tid; i < 4 * D; i += kThreads) {
+        const int r = i / D, d = i % D;
+        if (g0 + r >= G) continue;
+        float acc = 0.f;
+        for (int k = 0; k < NKG; ++k) acc += red[((size_t)k * 4 + r) * D + d];
+        if (w == 0) acc = fmaf(s_enew[g0 + r], vnew, acc);  // i == tid (4 * D <= kThreads)
+        cst(reinterpret_cast<uint32_t *>(O) + (size_t)(g0 + r) * D + d, __float_as_uint(acc));
+      }
+      __syncthreads();
+    }
   }
   // every published value has completed before the arrival is counted
   drain();
@@ -244,6 +335,19 @@ __global__ __launch_bounds__(kThreads) void h2o_step_kernel(const H2oArgs P) {
     }
   };
   load_e(0);
+  // the parts' attention shares of this thread's (row, column) outputs
+  constexpr int kOPer = 16 * D / kThreads;  // outputs per thread at most (G <= 16)
+  float oq[kOPer][kMaxSplit];
+  if (P.attn) {
+    const uint32_t *O = reinterpret_cast<const uint32_t *>(P.o + (size_t)u * kMaxSplit * G * D);
+#pragma unroll
+    for (int k = 0; k < kOPer; ++k) {
+      const int i = tid + k * kThreads;
+#pragma unroll
+      for (int q = 0; q < kMaxSplit; ++q)
+        oq[k][q] = (i < G * D && q < S) ? __uint_as_float(cld(O + (size_t)q * G * D + i)) : 0.f;
+    }
+  }
   float mq[kMaxSplit], lq[kMaxSplit];
   if (tid < G) {
 #pragma unroll
@@ -300,6 +404,22 @@ __global__ __launch_bounds__(kThreads) void h2o_step_kernel(const H2oArgs P) {
   if (s_code) {
     if (tid == 0) P.evicted[u] = s_code;
     return;
+  }
+
+  // the attention output of each query row: the parts' o combined in order
+  if (P.attn) {
+#pragma unroll
+    for (int k = 0; k < kOPer; ++k) {
+      const int i = tid + k * kThreads;
+      if (i < G * D) {
+        const int g = i / D;
+        float acc = 0.f;
+#pragma unroll
+        for (int q = 0; q < kMaxSplit; ++q)
+          if (q < S) acc = fmaf(oq[k][q], s_r[g * kMaxSplit + q], acc);
+        P.attn[((size_t)b * Hq + (size_t)h * G) * D + i] = acc;
+      }
+    }
   }
 
   // running scores, the new token's score, the candidates' minimum
@@ -375,9 +495,15 @@ __global__ __launch_bounds__(kThreads) void h2o_step_kernel(const H2oArgs P) {
   }
 }
 
+size_t h2o_lds_bytes(const H2oArgs &a, int head_dim) {
+  // the final step's e values ([G][np]) bound any part's logits ([G][cb*16]);
+  // with the attention output the P.V reduction buffer ([key groups][4][D]) follows
+  const size_t red = a.attn ? (size_t)kThreads / (head_dim / 2) * 4 * head_dim : 0;
+  return ((size_t)a.G * a.np + red) * sizeof(float);
+}
+
 hipError_t launch_h2o_step(const H2oArgs &a, int bf16, int head_dim, hipStream_t s) {
-  // the final step's e values ([G][np]) exceed any part's logits ([G][cb*16])
-  const size_t lds = (size_t)a.G * a.np * sizeof(float);
+  const size_t lds = h2o_lds_bytes(a, head_dim);
   const dim3 grid((unsigned)(a.units * a.split)), block(kThreads);
   if (bf16) {
     if (head_dim == 128) hipLaunchKernelGGL((h2o_step_kernel<true, 128>), grid, block, lds, s, a);

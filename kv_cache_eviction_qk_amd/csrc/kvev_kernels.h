@@ -91,15 +91,19 @@ struct H2oArgs {
   const int32_t *t_pos;                // [B]
   int32_t *free_list, *free_count;
   int32_t *evicted;                    // [units]
+  float *attn;                         // optional attention output [B][Hq][D] (fp32)
   // workspace: e values [units][G][np], part maxima and sums [units][8][32],
-  // state (zero between calls) arrival counters and error flags [units]
+  // parts' attention shares [units][8][G][D], state (zero between calls)
+  // arrival counters and error flags [units]
   uint32_t *e, *ml, *arrive, *err;
+  float *o;
   int32_t units, Hkv, G, max_blocks, max_slots, num_blocks, budget, recent;
   int32_t np;                          // budget rounded up to 16, plus 16 (the new token's e)
   int32_t split;                       // workgroups per head
   float c1;                            // scale * log2(e)
 };
 hipError_t launch_h2o_step(const H2oArgs &a, int bf16, int head_dim, hipStream_t s);
+size_t h2o_lds_bytes(const H2oArgs &a, int head_dim);  // dynamic LDS of one workgroup
 
 struct WindowAttnArgs {
   const uint8_t *k_pool, *v_pool;

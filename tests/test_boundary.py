@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
     assert set(names) == set(K.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvev_abi_version() == K.ABI_VERSION == 5
+    assert L.kvev_abi_version() == K.ABI_VERSION == 6
     for code in (0, -1, -2, -3, -4):
         assert K.strerror(code)
 
@@ -251,8 +251,8 @@ def test_h2o_step_refusals():
         p = dict(q=FAKE, k=FAKE, v=FAKE, t=FAKE, s=FAKE, fl=FAKE, fc=FAKE, ev=FAKE, ws=FAKE)
         p.update(ptrs or {})
         return L.kvev_h2o_step(ctypes.byref(c), p["q"], p["k"], p["v"], p["t"], group, 0.1,
-                               p["s"], budget, recent, p["fl"], p["fc"], p["ev"], p["ws"],
-                               ws_bytes, None)
+                               p["s"], budget, recent, p["fl"], p["fc"], p["ev"], None,
+                               p["ws"], ws_bytes, None)
 
     for name in ("q", "k", "v", "t", "s", "fl", "fc", "ev"):
         assert call(ptrs={name: None}) == K.EINVAL, name

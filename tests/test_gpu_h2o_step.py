@@ -97,12 +97,13 @@ class Dev:
         self.fc = dev(np.array([fc], np.int32))
         self.ws = {}
 
-    def step(self, st, q, k, v, t, budget, recent):
+    def step(self, st, q, k, v, t, budget, recent, attn=None):
         key = (st["G"], budget)
         if key not in self.ws:  # zero-filled once, left zero by every call
             self.ws[key] = K.new_h2o_workspace(self.c, st["G"], budget)
         return K.h2o_step(self.c, dev(q), dev(k), dev(v), dev(t), st["G"], st["scale"],
-                          self.score, budget, recent, self.fl, self.fc, self.ws[key])
+                          self.score, budget, recent, self.fl, self.fc, self.ws[key],
+                          attn_out=attn)
 
     def state(self, like):
         out = dict(like)
@@ -228,6 +229,23 @@ def _lazy(fn):
     return get
 
 
+def check_attention(g_attn, o_attn, o_abs, ev_o, Hkv, G, tol, what):
+    """The step's attention output of the heads that were not refused:
+    |g - o| <= tol * sum_j p_j |v_j| per element (the error bound of a weighted
+    sum whose weights carry relative error up to tol)."""
+    B = g_attn.shape[0]
+    for b in range(B):
+        for h in range(Hkv):
+            if ev_o[b, h] < -1:
+                continue
+            rows = slice(h * G, (h + 1) * G)
+            err = np.abs(g_attn[b, rows].astype(np.float64) - o_attn[b, rows])
+            bound = tol * o_abs[b, rows] + 1e-30
+            assert (err <= bound).all(), (
+                f"{what} head ({b},{h}): attention output off by {float((err / bound).max()):.2f}x "
+                f"the bound")
+
+
 def check_free_lists(before_bt, g, o, fl_g, fc_g, fl_o, fc_o):
     """Same number taken, the same remaining list, the same set of taken blocks."""
     assert fc_g == fc_o
@@ -269,12 +287,15 @@ def test_isolated_steps(dtype, D, G, budget, recent, bad):
     for i in range(steps):
         q, k, v = _step_inputs(seed, i, dtype, B, Hkv, G, D, dirs)
         t = np.full(B, t0 + i, np.int32)
-        o, ev_o, fl_o, fc_o = oracle.h2o_step(st, q, k, v, t, budget, recent, free_list=free,
-                                              free_count=fc)
+        o, ev_o, fl_o, fc_o, o_attn, o_abs = oracle.h2o_step(st, q, k, v, t, budget, recent,
+                                                             free_list=free, free_count=fc,
+                                                             want_attn=True)
         d = Dev(st, free, fc)
-        ev_g = host(d.step(st, q, k, v, t, budget, recent))
+        attn = torch.full((B, Hkv * G, D), float("nan"), dtype=torch.float32, device="cuda")
+        ev_g = host(d.step(st, q, k, v, t, budget, recent, attn=attn))
         torch.cuda.synchronize()
         g, fl_g, fc_g = d.state(st)
+        check_attention(host(attn), o_attn, o_abs, ev_o, Hkv, G, TOL[dtype], f"step {i}")
         allsc = _lazy(lambda: _all_scores(st, q, k, v, t, budget, recent))
         for vv in compare_step(st, g, o, ev_g, ev_o, allsc, t, budget, recent, TOL[dtype],
                                f"step {i}").values():
