@@ -68,8 +68,11 @@ def lib():
         L.orc_measure.argtypes = [P, P, P, i32, i32, P]
         L.orc_h2o_step.argtypes = [P, P, i32, i32, P, P, P, P, i32, i32, i32, i32, i32, P, P, P,
                                    P, ctypes.c_double, i32, i32, P, P, P, P, P]
+        L.orc_vtok_evict.argtypes = [P, P, P, P, i32, i32, P, P, P]
+        L.orc_vtok_reclaim.argtypes = [P, P, i32, i32, P, P, P, P, P, P, i32, i32, i32,
+                                       ctypes.c_double, i32, P, P, i32, P]
         for f in (L.orc_lse_a, L.orc_score, L.orc_select, L.orc_compact, L.orc_measure,
-                  L.orc_h2o_step):
+                  L.orc_h2o_step, L.orc_vtok_evict, L.orc_vtok_reclaim):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -227,4 +230,61 @@ def h2o_step(state: dict, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
     if want_attn:
         return new, ev, free_list, int(fc[0]), attn, aabs
     return new, ev, free_list, int(fc[0])
+
+
+def vtok_liveness(state: dict):
+    """The vToken liveness view of a dense state: every slot below seq_len is
+    live.  Returns (live uint8 [B,Hkv,max_slots], block_live int32
+    [B,Hkv,max_blocks])."""
+    B, Hkv, mb = state["B"], state["Hkv"], state["max_blocks"]
+    live = np.zeros((B, Hkv, mb * 16), np.uint8)
+    for b in range(B):
+        for h in range(Hkv):
+            live[b, h, :int(state["seq_len"][b, h])] = 1
+    block_live = live.reshape(B, Hkv, mb, 16).sum(axis=-1).astype(np.int32)
+    return live, block_live
+
+
+def vtok_evict(state: dict, victims: np.ndarray, n_victims: np.ndarray):
+    """Marks victim slots dead on a COPY of state's 'live' / 'block_live'.
+    Returns (new_state, status)."""
+    new = dict(state)
+    new["live"] = state["live"].copy()
+    new["block_live"] = state["block_live"].copy()
+    U = state["B"] * state["Hkv"]
+    st = np.zeros(1, np.int32)
+    rc = lib().orc_vtok_evict(_p(np.ascontiguousarray(state["block_table"], dtype=np.int32)),
+                              _p(np.ascontiguousarray(state["seq_len"], dtype=np.int32)),
+                              _p(new["live"]), _p(new["block_live"]), U, state["max_blocks"],
+                              _p(np.ascontiguousarray(victims, dtype=np.int32)),
+                              _p(np.ascontiguousarray(n_victims, dtype=np.int32)), _p(st))
+    assert rc == 0
+    return new, int(st[0])
+
+
+def vtok_reclaim(state: dict, theta_f: float, max_sources: int, free_list: np.ndarray,
+                 free_count: int, with_score: bool = False):
+    """Lazy reclamation on a COPY of state (pools, block_table, pos, live,
+    block_live and, with with_score, 'score').  Returns (new_state,
+    free_list, free_count, stats[10])."""
+    new = dict(state)
+    for k in ("k_pool", "v_pool", "block_table", "pos", "live", "block_live"):
+        new[k] = state[k].copy()
+    sc = None
+    if with_score:
+        sc = new["score"] = np.ascontiguousarray(state["score"], dtype=np.float32).copy()
+    fl = np.ascontiguousarray(free_list, dtype=np.int32).copy()
+    fc = np.array([free_count], np.int32)
+    stats = np.zeros(10, np.int64)
+    U = state["B"] * state["Hkv"]
+    elem = 2 if state["dtype"] == "bf16" else 4
+    rc = lib().orc_vtok_reclaim(_p(new["k_pool"]), _p(new["v_pool"]), elem, state["D"],
+                                _p(new["block_table"]),
+                                _p(np.ascontiguousarray(state["seq_len"], dtype=np.int32)),
+                                _p(new["pos"]), _p(sc), _p(new["live"]), _p(new["block_live"]), U,
+                                state["max_blocks"], state["num_blocks"], float(theta_f),
+                                max_sources, _p(fl), _p(fc), fl.size, _p(stats))
+    if rc != 0:
+        raise ValueError(f"oracle vtok_reclaim refused the arguments (rc={rc})")
+    return new, fl, int(fc[0]), stats
 

@@ -574,3 +574,170 @@ int orc_h2o_step(void *k_pool, void *v_pool, int32_t is_bf16, int32_t head_dim,
   return 0;
 }
 
+/* --------------------------------------------- vToken lazy reclamation */
+/*
+ * [VTOK] section 3.2: a token table keeps, per token, its physical place and
+ * a liveness bit; evicting a token only clears the bit.  Section 3.3: the
+ * reclamation backend later packs the live tokens of several under-used
+ * blocks into fewer destination blocks taken from the free pool (out of
+ * place), fills each destination completely, keeps the logical order, and
+ * returns the emptied source blocks; it refuses plans that would not free
+ * anything (section 3.5, I4).  Here the token table of a head is its block
+ * list plus the per-slot liveness and position, so a relocation rewrites the
+ * block list entries of the sources.
+ */
+int orc_vtok_evict(const int32_t *block_table, const int32_t *seq_len, uint8_t *live,
+                   int32_t *block_live, int32_t units, int32_t max_blocks,
+                   const int32_t *victims, const int32_t *n_victims, int32_t *status) {
+  if (!block_table || !seq_len || !live || !block_live || !victims || !n_victims || !status)
+    return -1;
+  const int64_t max_slots = (int64_t)max_blocks * 16;
+  *status = 0;
+  for (int64_t u = 0; u < units; ++u) {
+    const int64_t n = seq_len[u], m = n_victims[u];
+    for (int64_t i = 0; i < m; ++i) {
+      const int64_t v = victims[u * max_slots + i];
+      if (v < 0 || v >= n || v >= max_slots || block_table[u * max_blocks + v / 16] < 0 ||
+          !live[u * max_slots + v]) {
+        *status |= 1;
+        continue;
+      }
+      live[u * max_slots + v] = 0;
+      block_live[u * max_blocks + v / 16] -= 1;
+    }
+  }
+  return 0;
+}
+
+int orc_vtok_reclaim(void *k_pool, void *v_pool, int32_t elem_bytes, int32_t head_dim,
+                     int32_t *block_table, const int32_t *seq_len, int32_t *pos, float *score,
+                     uint8_t *live, int32_t *block_live, int32_t units, int32_t max_blocks,
+                     int32_t num_blocks, double theta_f, int32_t max_sources,
+                     int32_t *free_list, int32_t *free_count, int32_t free_capacity,
+                     int64_t *stats) {
+  if (!k_pool || !v_pool || !block_table || !seq_len || !pos || !live || !block_live ||
+      !free_list || !free_count || !stats || max_sources < 1)
+    return -1;
+  if (elem_bytes != 2 && elem_bytes != 4) return -1;
+  if (*free_count < 0 || *free_count > free_capacity) return -1;
+  const int64_t max_slots = (int64_t)max_blocks * 16, row_bytes = (int64_t)head_dim * elem_bytes;
+  for (int i = 0; i < 10; ++i) stats[i] = 0;
+  /* every head's plan: sources and the destination count */
+  int32_t *src = (int32_t *)malloc(sizeof(int32_t) * (size_t)(units * (int64_t)max_sources + 1));
+  int32_t *nsrc = (int32_t *)calloc((size_t)units + 1, sizeof(int32_t));
+  int32_t *ndst = (int32_t *)calloc((size_t)units + 1, sizeof(int32_t));
+  int64_t total_free = *free_count;
+  for (int64_t u = 0; u < units; ++u) {
+    const int64_t n = seq_len[u];
+    const int32_t *bt = block_table + u * max_blocks;
+    if (n < 0 || n > max_slots) {
+      stats[9] |= 2;
+      continue;
+    }
+    const int64_t nb = (n + 15) / 16;
+    int64_t alloc = 0, livec = 0;
+    for (int64_t lb = 0; lb < nb; ++lb)
+      if (bt[lb] >= 0) {
+        ++alloc;
+        livec += block_live[u * max_blocks + lb];
+      }
+    stats[6] += livec;
+    stats[7] += alloc;
+    const double F = alloc > 0 ? 1.0 - (double)livec / (16.0 * (double)alloc) : 0.0;
+    if (!(F > theta_f)) {
+      ++stats[2];
+      continue;
+    }
+    int64_t k = 0, T = 0;
+    for (int64_t lb = 0; lb + 1 < nb && k < max_sources; ++lb) {
+      if (bt[lb] < 0 || block_live[u * max_blocks + lb] >= 16) continue;
+      src[u * max_sources + k++] = (int32_t)lb;
+      T += block_live[u * max_blocks + lb];
+    }
+    const int64_t D = (T + 15) / 16;
+    if (k < 2 || D >= k) {
+      ++stats[2]; /* nothing to gain: counted with the heads left as they are */
+      continue;
+    }
+    nsrc[u] = (int32_t)k;
+    ndst[u] = (int32_t)D;
+  }
+  /* headroom: destinations from the top of the free list, heads in order */
+  int64_t fc = *free_count, taken = 0, pushed = 0;
+  int64_t *dst_off = (int64_t *)calloc((size_t)units + 1, sizeof(int64_t));
+  for (int64_t u = 0; u < units; ++u) {
+    if (!nsrc[u]) continue;
+    if (taken + ndst[u] > fc) {
+      ++stats[1];
+      nsrc[u] = 0;
+      continue;
+    }
+    dst_off[u] = taken;
+    taken += ndst[u];
+    pushed += nsrc[u];
+  }
+  if (fc - taken + pushed > free_capacity) {
+    free(src); free(nsrc); free(ndst); free(dst_off);
+    return -2;
+  }
+  (void)total_free;
+  /* moves, in head order; destinations are free_list[fc - 1 - dst_off - d] */
+  int32_t *dst_ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)(taken + 1));
+  for (int64_t i = 0; i < taken; ++i) dst_ids[i] = free_list[fc - 1 - i];
+  int64_t top = fc - taken;
+  int32_t *tpos = (int32_t *)malloc(sizeof(int32_t) * (size_t)(max_sources * 16 + 1));
+  float *tsc = (float *)malloc(sizeof(float) * (size_t)(max_sources * 16 + 1));
+  for (int64_t u = 0; u < units; ++u) {
+    const int64_t k = nsrc[u];
+    if (!k) continue;
+    int32_t *bt = block_table + u * max_blocks;
+    int32_t *ps = pos + u * max_slots;
+    uint8_t *lv = live + u * max_slots;
+    int32_t *bl = block_live + u * max_blocks;
+    float *sc = score ? score + u * max_slots : NULL;
+    const int32_t *sv = src + u * max_sources;
+    const int64_t D = ndst[u];
+    int64_t i = 0;
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t lb = sv[j];
+      for (int64_t o = 0; o < 16; ++o) {
+        const int64_t s = lb * 16 + o;
+        if (!lv[s]) continue;
+        const int64_t from = (int64_t)bt[lb] * 16 + o;
+        const int64_t to = (int64_t)dst_ids[dst_off[u] + i / 16] * 16 + i % 16;
+        memcpy((char *)k_pool + to * row_bytes, (char *)k_pool + from * row_bytes, (size_t)row_bytes);
+        memcpy((char *)v_pool + to * row_bytes, (char *)v_pool + from * row_bytes, (size_t)row_bytes);
+        tpos[i] = ps[s];
+        if (sc) tsc[i] = sc[s];
+        ++i;
+      }
+    }
+    const int64_t T = i;
+    /* the block list and the per-slot table of the source positions */
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t lb = sv[j];
+      free_list[top++] = bt[lb];
+      bt[lb] = j < D ? dst_ids[dst_off[u] + j] : -1;
+      const int64_t cnt = j < D ? (T - 16 * j < 16 ? T - 16 * j : 16) : 0;
+      bl[lb] = (int32_t)cnt;
+      for (int64_t o = 0; o < 16; ++o) {
+        const int64_t s = lb * 16 + o, t = 16 * j + o;
+        lv[s] = o < cnt ? 1 : 0;
+        if (o < cnt) {
+          ps[s] = tpos[t];
+          if (sc) sc[s] = tsc[t];
+        }
+      }
+    }
+    ++stats[0];
+    stats[3] += k - D;
+    stats[4] += T;
+    stats[5] += T * 2 * row_bytes * 2;
+    stats[8] -= k - D;
+  }
+  stats[8] += stats[7];
+  *free_count = (int32_t)top;
+  free(tpos); free(tsc); free(dst_ids); free(src); free(nsrc); free(ndst); free(dst_off);
+  return 0;
+}
+

@@ -110,6 +110,44 @@ int orc_h2o_step(void *k_pool, void *v_pool, int32_t is_bf16, int32_t head_dim,
                  int32_t *free_list, int32_t *free_count, int32_t *evicted_pos,
                  double *attn_out, double *attn_abs);
 
+/* vToken liveness ([VTOK] section 3.2): mark the victim slots of every head
+ * dead.  live [units][max_blocks*16] (1 live, 0 dead), block_live
+ * [units][max_blocks] (live slots per logical block).  A victim that is out
+ * of range, not live or in a block without a physical block sets bit 0 of
+ * *status and is skipped. */
+int orc_vtok_evict(const int32_t *block_table, const int32_t *seq_len, uint8_t *live,
+                   int32_t *block_live, int32_t units, int32_t max_blocks,
+                   const int32_t *victims, const int32_t *n_victims, int32_t *status);
+
+/* vToken lazy reclamation ([VTOK] section 3.3, stages 1-3, and section 3.5,
+ * I1, I2, I4), one call over every head in (b, h) order:
+ *   - eligibility: the head's waste F = 1 - live / (16 * allocated blocks)
+ *     (Eq. 1 over the head) above theta_f;
+ *   - sources: the first max_sources allocated, not full blocks in logical
+ *     order, the block holding the head's last slot excluded (it still takes
+ *     appends);
+ *   - T = their live tokens; the plan needs D = ceil(T / 16) destination
+ *     blocks and proceeds only if D < the number of sources;
+ *   - headroom: D blocks from the top of the free list while enough remain;
+ *     a head that does not fit is deferred;
+ *   - moves: the sources' live tokens in logical order fill the destination
+ *     blocks completely, one after the other; the first D source positions of
+ *     the block list take the destination blocks, the other source positions
+ *     become -1 (so the moved tokens keep their relative order, passing over
+ *     any full block between two sources); K, V, pos, live, block_live and
+ *     the optional score row follow; after every head has planned, the source
+ *     blocks are appended to the free list in (b, h, block) order.
+ * stats[10] = {heads reclaimed, heads deferred, heads below the threshold,
+ * blocks freed, rows moved, bytes moved (K+V read+write), live tokens,
+ * allocated blocks before, after, status}.  Returns 0, -1 (invalid), -2
+ * (free list capacity too small; nothing modified). */
+int orc_vtok_reclaim(void *k_pool, void *v_pool, int32_t elem_bytes, int32_t head_dim,
+                     int32_t *block_table, const int32_t *seq_len, int32_t *pos, float *score,
+                     uint8_t *live, int32_t *block_live, int32_t units, int32_t max_blocks,
+                     int32_t num_blocks, double theta_f, int32_t max_sources,
+                     int32_t *free_list, int32_t *free_count, int32_t free_capacity,
+                     int64_t *stats);
+
 #ifdef __cplusplus
 }
 #endif
