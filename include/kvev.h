@@ -55,7 +55,7 @@ extern "C" {
 #endif
 
 #define KVEV_BLOCK_SIZE 16
-#define KVEV_ABI_VERSION 6
+#define KVEV_ABI_VERSION 7
 
 typedef enum {
   KVEV_OK = 0,
@@ -293,6 +293,72 @@ int kvev_h2o_step(const kvev_cache *cache, const void *q, const void *k_new, con
 /* Workspace bytes kvev_h2o_step needs for this cache, group and budget; 0
  * for a bad cache or a group / budget it refuses. */
 size_t kvev_h2o_workspace_bytes(const kvev_cache *cache, int32_t group, int32_t budget);
+
+/*
+ * kvev_vtok_evict -- vToken's evict_token for a batch ([VTOK] section 3.2:
+ * evicting a token only marks it dead in the token table; no KV memory moves
+ * or is freed).  The token table of a head is its block list, pos, and
+ * live: uint8 [batch][kv_heads][max_blocks*16] (1 live, 0 dead), with
+ * block_live: int32 [batch][kv_heads][max_blocks] the live slots of each
+ * logical block.  For every head u and i < n_victims[u], slot victims[u][i]
+ * (int32 [batch][kv_heads][max_blocks*16], any order) is marked dead and its
+ * block's count decremented.  A victim that is out of [0, seq_len), in a
+ * block whose table entry is -1, or already dead (a repeat included) sets
+ * *status (int32 on the device, written by the call: 0 or 1) and is skipped.
+ * Device pointers; live must be 4-byte aligned.  Two kernels on `stream`.
+ * Errors: KVEV_EINVAL for NULL pointers, a bad cache or a misaligned live.
+ */
+int kvev_vtok_evict(const kvev_cache *cache, uint8_t *live, int32_t *block_live,
+                    const int32_t *victims, const int32_t *n_victims, int32_t *status,
+                    void *stream);
+
+/*
+ * kvev_vtok_reclaim -- vToken's lazy reclamation ([VTOK] section 3.3, stages
+ * 1-3, and section 3.5: I1 conservation, I2 unique mapping, I4 strictly
+ * fewer blocks), over every head in (b, h) order:
+ *   - a head is eligible when its waste F = 1 - live / (16 * allocated
+ *     blocks) (Eq. 1 over the head's blocks whose entry is not -1) exceeds
+ *     theta_f;
+ *   - its sources are its first max_sources allocated blocks that are not
+ *     full, in logical order, excluding the block of slot seq_len - 1 (it
+ *     still takes appends); T = their live tokens; the plan needs
+ *     D = ceil(T / 16) destination blocks and goes ahead only if D is less
+ *     than the number of sources;
+ *   - heads take their D destinations from the top of the free list in
+ *     (b, h) order while enough remain; a head that does not fit is deferred;
+ *   - the sources' live tokens, in logical order, fill the destinations
+ *     completely one after the other (K, V, pos, the optional score row);
+ *     the first D source entries of the block list take the destination
+ *     blocks and the others become -1, so moved tokens keep their relative
+ *     order (passing over any full block between two sources); live and
+ *     block_live follow; the source blocks are appended to the free list in
+ *     (b, h, block) order after every head has taken its destinations.
+ * seq_len does not change: slots in a -1 block are holes.  The copies run on
+ * `stream`; a caller that overlaps them with decoding issues the call on a
+ * stream of its own and makes the next attention wait for an event recorded
+ * after it ([VTOK] section 3.3, stage 4).
+ * stats: int64[10] on the device = {heads reclaimed, heads deferred, heads
+ * left as they are (F at or below theta_f, or no plan that frees a block),
+ * blocks freed, rows moved, bytes moved (K and V, read + write), live
+ * tokens, allocated blocks before, after, status (an OR of 2: a seq_len
+ * out of range, 4: a block id past the pool or a live count outside
+ * [0, 16] -- such heads are skipped and not counted; 8: a free count outside
+ * [0, min(free_capacity, num_blocks)] -- nothing is admitted -- or a list
+ * too small for the returned sources, whose excess is dropped)}.
+ * Workspace: at least kvev_vtok_workspace_bytes(cache, max_sources) bytes
+ * (scratch only).  live: 4-byte aligned.
+ * Errors: KVEV_EINVAL for NULL pointers, a bad cache, theta_f outside
+ * [0, 1) or max_sources outside [2, 4096]; KVEV_EUNSUPPORTED above 8192 KV
+ * heads; KVEV_ENOSPACE when free_capacity < num_blocks or the workspace is
+ * missing or short.
+ */
+int kvev_vtok_reclaim(const kvev_cache *cache, uint8_t *live, int32_t *block_live,
+                      float *score_or_null, double theta_f, int32_t max_sources,
+                      int32_t *free_list, int32_t *free_count, int32_t free_capacity,
+                      int64_t *stats, void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes of kvev_vtok_reclaim; 0 for a bad cache or max_sources. */
+size_t kvev_vtok_workspace_bytes(const kvev_cache *cache, int32_t max_sources);
 
 /*
  * kvev_window_attn -- helper outside the eviction step: the log-sum-exp and

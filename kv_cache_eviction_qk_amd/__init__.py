@@ -30,9 +30,10 @@ BLOCK_SIZE = 16
 
 # the functions include/kvev.h declares
 EXPORTS = ("kvev_score", "kvev_select", "kvev_compact", "kvev_evict", "kvev_measure",
-           "kvev_h2o_step", "kvev_h2o_workspace_bytes", "kvev_window_attn",
+           "kvev_h2o_step", "kvev_h2o_workspace_bytes", "kvev_vtok_evict",
+           "kvev_vtok_reclaim", "kvev_vtok_workspace_bytes", "kvev_window_attn",
            "kvev_workspace_bytes", "kvev_strerror", "kvev_abi_version")
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 
 class KvevError(RuntimeError):
@@ -82,13 +83,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                 sz, P]
     L.kvev_h2o_workspace_bytes.argtypes = [P, i32, i32]
     L.kvev_h2o_workspace_bytes.restype = sz
+    L.kvev_vtok_evict.argtypes = [P, P, P, P, P, P, P]
+    L.kvev_vtok_reclaim.argtypes = [P, P, P, P, ctypes.c_double, i32, P, P, i32, P, P, sz, P]
+    L.kvev_vtok_workspace_bytes.argtypes = [P, i32]
+    L.kvev_vtok_workspace_bytes.restype = sz
     L.kvev_workspace_bytes.argtypes = [P, i32, i32]
     L.kvev_workspace_bytes.restype = sz
     L.kvev_strerror.argtypes = [ctypes.c_int]
     L.kvev_strerror.restype = ctypes.c_char_p
     L.kvev_abi_version.argtypes = []
     for f in (L.kvev_score, L.kvev_select, L.kvev_compact, L.kvev_evict, L.kvev_window_attn,
-              L.kvev_measure, L.kvev_h2o_step, L.kvev_abi_version):
+              L.kvev_measure, L.kvev_h2o_step, L.kvev_vtok_evict, L.kvev_vtok_reclaim,
+              L.kvev_abi_version):
         f.restype = ctypes.c_int
     if L.kvev_abi_version() != ABI_VERSION:
         raise ImportError(f"{path} has ABI version {L.kvev_abi_version()}, expected "
@@ -386,6 +392,67 @@ def h2o_step(cache: Cache, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Te
                          _stream(stream))
     _check(rc, "kvev_h2o_step")
     return evicted
+
+
+def vtok_evict(cache: Cache, live: torch.Tensor, block_live: torch.Tensor,
+               victims: torch.Tensor, n_victims: torch.Tensor, status: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """kvev_vtok_evict: mark the victim slots dead.  live uint8 [B, Hkv,
+    max_slots], block_live int32 [B, Hkv, max_blocks] (both updated); victims
+    int32 [B, Hkv, max_slots], n_victims int32 [B, Hkv].  Returns status int32
+    [1] (1 when a victim was out of range or already dead)."""
+    L = load_library()
+    c = cache.struct()
+    B, Hkv = cache.batch, cache.kv_heads
+    _need(live, "live", torch.uint8, B * Hkv * cache.max_slots)
+    _need(block_live, "block_live", torch.int32, B * Hkv * cache.max_blocks)
+    _need(victims, "victims", torch.int32, B * Hkv * cache.max_slots)
+    _need(n_victims, "n_victims", torch.int32, B * Hkv)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=live.device)
+    _need(status, "status", torch.int32, 1)
+    rc = L.kvev_vtok_evict(ctypes.byref(c), _ptr(live), _ptr(block_live), _ptr(victims),
+                           _ptr(n_victims), _ptr(status), _stream(stream))
+    _check(rc, "kvev_vtok_evict")
+    return status
+
+
+def new_vtok_workspace(cache: Cache, max_sources: int) -> torch.Tensor:
+    """A workspace for kvev_vtok_reclaim on this cache shape."""
+    n = load_library().kvev_vtok_workspace_bytes(ctypes.byref(cache.struct()), max_sources)
+    if n == 0:
+        raise KvevError(EINVAL, "kvev_vtok_workspace_bytes")
+    return torch.zeros(n, dtype=torch.uint8, device=cache.k_pool.device)
+
+
+def vtok_reclaim(cache: Cache, live: torch.Tensor, block_live: torch.Tensor, theta_f: float,
+                 max_sources: int, free_list: torch.Tensor, free_count: torch.Tensor,
+                 workspace: torch.Tensor, score: Optional[torch.Tensor] = None,
+                 stats: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kvev_vtok_reclaim: lazy, threshold-gated reclamation of every head.  live,
+    block_live as in vtok_evict; score (optional) fp32 [B, Hkv, max_slots]
+    moves with the tokens; free_list int32 (capacity >= num_blocks),
+    free_count int32 [1]; workspace from new_vtok_workspace.  Returns stats
+    int64 [10]."""
+    L = load_library()
+    c = cache.struct()
+    B, Hkv = cache.batch, cache.kv_heads
+    _need(live, "live", torch.uint8, B * Hkv * cache.max_slots)
+    _need(block_live, "block_live", torch.int32, B * Hkv * cache.max_blocks)
+    if score is not None:
+        _need(score, "score", torch.float32, B * Hkv * cache.max_slots)
+    _need(free_list, "free_list", torch.int32)
+    _need(free_count, "free_count", torch.int32, 1)
+    _need(workspace, "workspace", torch.uint8)
+    if stats is None:
+        stats = torch.empty(10, dtype=torch.int64, device=live.device)
+    _need(stats, "stats", torch.int64, 10)
+    rc = L.kvev_vtok_reclaim(ctypes.byref(c), _ptr(live), _ptr(block_live), _ptr(score),
+                             float(theta_f), max_sources, _ptr(free_list), _ptr(free_count),
+                             free_list.numel(), _ptr(stats), _ptr(workspace), workspace.numel(),
+                             _stream(stream))
+    _check(rc, "kvev_vtok_reclaim")
+    return stats
 
 
 def window_attn(cache: Cache, q: torch.Tensor, q_pos: torch.Tensor, scale: float, group: int,

@@ -252,6 +252,97 @@ int kvev_h2o_step(const kvev_cache *cache, const void *q, const void *k_new, con
                                        static_cast<hipStream_t>(stream)));
 }
 
+// Workspace of kvev_vtok_reclaim (scratch only).
+struct VtokLayout {
+  size_t plan, src, srcoff, dst_off, push_off, dst_ids, tpos, tscore, misc, total;
+};
+
+VtokLayout vtok_layout(const kvev_cache *c, int32_t max_sources) {
+  VtokLayout L{};
+  const size_t units = (size_t)c->batch * c->kv_heads, ms = (size_t)max_sources;
+  size_t off = 0;
+  L.plan = off; off = a256(off + units * 8 * 4);
+  L.src = off; off = a256(off + units * ms * 4);
+  L.srcoff = off; off = a256(off + units * ms * 4);
+  L.dst_off = off; off = a256(off + units * 4);
+  L.push_off = off; off = a256(off + units * 4);
+  L.dst_ids = off; off = a256(off + (size_t)c->num_blocks * 4);
+  L.tpos = off; off = a256(off + units * ms * KVEV_BLOCK_SIZE * 4);
+  L.tscore = off; off = a256(off + units * ms * KVEV_BLOCK_SIZE * 4);
+  L.misc = off; off = a256(off + 8 * 4);
+  L.total = off;
+  return L;
+}
+
+kvev::VtokArgs vtok_args(const kvev_cache *cache, uint8_t *live, int32_t *block_live) {
+  kvev::VtokArgs a{};
+  a.k_pool = static_cast<uint8_t *>(cache->k_pool);
+  a.v_pool = static_cast<uint8_t *>(cache->v_pool);
+  a.block_table = cache->block_table;
+  a.seq_len = cache->seq_len;
+  a.pos = cache->pos;
+  a.live = live;
+  a.block_live = block_live;
+  a.units = cache->batch * cache->kv_heads;
+  a.max_blocks = cache->max_blocks;
+  a.max_slots = cache->max_blocks * KVEV_BLOCK_SIZE;
+  a.num_blocks = cache->num_blocks;
+  a.row_bytes = cache->head_dim * elem_bytes(cache);
+  return a;
+}
+
+int kvev_vtok_evict(const kvev_cache *cache, uint8_t *live, int32_t *block_live,
+                    const int32_t *victims, const int32_t *n_victims, int32_t *status,
+                    void *stream) {
+  if (!valid_cache(cache) || !live || !block_live || !victims || !n_victims || !status)
+    return KVEV_EINVAL;
+  if (reinterpret_cast<uintptr_t>(live) & 3) return KVEV_EINVAL;
+  kvev::VtokArgs a = vtok_args(cache, live, block_live);
+  a.victims = victims;
+  a.n_victims = n_victims;
+  a.status = status;
+  return map_err(kvev::launch_vtok_evict(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t kvev_vtok_workspace_bytes(const kvev_cache *cache, int32_t max_sources) {
+  if (!valid_cache(cache) || max_sources < 2 || max_sources > kvev::kVtokMaxSources) return 0;
+  return vtok_layout(cache, max_sources).total;
+}
+
+int kvev_vtok_reclaim(const kvev_cache *cache, uint8_t *live, int32_t *block_live,
+                      float *score_or_null, double theta_f, int32_t max_sources,
+                      int32_t *free_list, int32_t *free_count, int32_t free_capacity,
+                      int64_t *stats, void *workspace, size_t ws_bytes, void *stream) {
+  if (!valid_cache(cache) || !live || !block_live || !free_list || !free_count || !stats)
+    return KVEV_EINVAL;
+  if (reinterpret_cast<uintptr_t>(live) & 3) return KVEV_EINVAL;
+  if (!(theta_f >= 0.0 && theta_f < 1.0)) return KVEV_EINVAL;  // NaN refused too
+  if (max_sources < 2 || max_sources > kvev::kVtokMaxSources) return KVEV_EINVAL;
+  if ((int64_t)cache->batch * cache->kv_heads > kvev::kVtokMaxUnits) return KVEV_EUNSUPPORTED;
+  if (free_capacity < cache->num_blocks) return KVEV_ENOSPACE;
+  const VtokLayout L = vtok_layout(cache, max_sources);
+  if (!workspace || ws_bytes < L.total) return KVEV_ENOSPACE;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  kvev::VtokArgs a = vtok_args(cache, live, block_live);
+  a.score = score_or_null;
+  a.free_list = free_list;
+  a.free_count = free_count;
+  a.stats = stats;
+  a.max_sources = max_sources;
+  a.free_capacity = free_capacity;
+  a.theta_f = theta_f;
+  a.plan = reinterpret_cast<int32_t *>(ws + L.plan);
+  a.src = reinterpret_cast<int32_t *>(ws + L.src);
+  a.srcoff = reinterpret_cast<int32_t *>(ws + L.srcoff);
+  a.dst_off = reinterpret_cast<int32_t *>(ws + L.dst_off);
+  a.push_off = reinterpret_cast<int32_t *>(ws + L.push_off);
+  a.dst_ids = reinterpret_cast<int32_t *>(ws + L.dst_ids);
+  a.tpos = reinterpret_cast<int32_t *>(ws + L.tpos);
+  a.tscore = reinterpret_cast<float *>(ws + L.tscore);
+  a.misc = reinterpret_cast<int32_t *>(ws + L.misc);
+  return map_err(kvev::launch_vtok_reclaim(a, static_cast<hipStream_t>(stream)));
+}
+
 int kvev_abi_version(void) { return KVEV_ABI_VERSION; }
 
 const char *kvev_strerror(int status) {

@@ -502,17 +502,24 @@ size_t h2o_lds_bytes(const H2oArgs &a, int head_dim) {
   return ((size_t)a.G * a.np + red) * sizeof(float);
 }
 
+template <bool BF16, int D>
+static hipError_t launch_t(const H2oArgs &a, size_t lds, hipStream_t s) {
+  auto fn = h2o_step_kernel<BF16, D>;
+  static size_t lds_set = 0;  // largest dynamic LDS size enabled for this variant
+  if (lds > 65536 && lds > lds_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    lds_set = lds;
+  }
+  hipLaunchKernelGGL(fn, dim3((unsigned)(a.units * a.split)), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_h2o_step(const H2oArgs &a, int bf16, int head_dim, hipStream_t s) {
   const size_t lds = h2o_lds_bytes(a, head_dim);
-  const dim3 grid((unsigned)(a.units * a.split)), block(kThreads);
-  if (bf16) {
-    if (head_dim == 128) hipLaunchKernelGGL((h2o_step_kernel<true, 128>), grid, block, lds, s, a);
-    else hipLaunchKernelGGL((h2o_step_kernel<true, 64>), grid, block, lds, s, a);
-  } else {
-    if (head_dim == 128) hipLaunchKernelGGL((h2o_step_kernel<false, 128>), grid, block, lds, s, a);
-    else hipLaunchKernelGGL((h2o_step_kernel<false, 64>), grid, block, lds, s, a);
-  }
-  return hipGetLastError();
+  if (bf16) return head_dim == 128 ? launch_t<true, 128>(a, lds, s) : launch_t<true, 64>(a, lds, s);
+  return head_dim == 128 ? launch_t<false, 128>(a, lds, s) : launch_t<false, 64>(a, lds, s);
 }
 
 }  // namespace kvev

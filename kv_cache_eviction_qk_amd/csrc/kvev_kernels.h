@@ -105,6 +105,29 @@ struct H2oArgs {
 hipError_t launch_h2o_step(const H2oArgs &a, int bf16, int head_dim, hipStream_t s);
 size_t h2o_lds_bytes(const H2oArgs &a, int head_dim);  // dynamic LDS of one workgroup
 
+struct VtokArgs {
+  uint8_t *k_pool, *v_pool;
+  int32_t *block_table;
+  const int32_t *seq_len;
+  int32_t *pos;
+  float *score;                        // optional score row moved with the tokens
+  uint8_t *live;                       // [units][max_slots] liveness bytes
+  int32_t *block_live;                 // [units][max_blocks] live slots per block
+  const int32_t *victims, *n_victims;  // marks
+  int32_t *status;                     // marks: bit 0, a victim that was not live
+  int32_t *free_list, *free_count;
+  int64_t *stats;                      // reclamation [10]
+  // workspace: plan records [units][8], sources and their live offsets
+  // [units][max_sources], destination / push offsets [units], destination ids
+  // [num_blocks], staged positions and scores [units][max_sources*16], misc [8]
+  int32_t *plan, *src, *srcoff, *dst_off, *push_off, *dst_ids, *tpos, *misc;
+  float *tscore;
+  int32_t units, max_blocks, max_slots, num_blocks, row_bytes, max_sources, free_capacity;
+  double theta_f;
+};
+hipError_t launch_vtok_evict(const VtokArgs &a, hipStream_t s);
+hipError_t launch_vtok_reclaim(const VtokArgs &a, hipStream_t s);
+
 struct WindowAttnArgs {
   const uint8_t *k_pool, *v_pool;
   const int32_t *block_table, *seq_len, *pos;
@@ -132,6 +155,8 @@ constexpr int kCompactChunk = 1024;     // compact.hip prep chunk (slots)
 constexpr int kH2oMaxBudget = 4096;    // h2o_step.hip: tokens per head
 constexpr int kH2oMaxLogits = 16384;   // h2o_step.hip: G * budget (64 KB of LDS)
 constexpr int kH2oMaxSplit = 8;        // h2o_step.hip: workgroups per head
+constexpr int kVtokMaxUnits = 8192;    // vtoken.hip: heads per reclamation call (admission in LDS)
+constexpr int kVtokMaxSources = 4096;  // vtoken.hip: sources per head and call
 
 // LDS bytes of one score workgroup (fused: room for the tile histogram and
 // the head selection).

@@ -1,0 +1,437 @@
+// vtoken.hip -- vToken liveness marks and lazy, threshold-gated reclamation
+// of each KV head's blocks (gfx950).
+//
+// [VTOK] section 3.2: the token table of a head is its block list plus, per
+// slot, the token's position and a liveness byte; evicting a token clears the
+// byte and the live count of its block, and moves nothing.  Section 3.3,
+// stages 1-3, and section 3.5 (I1, I2, I4): a head whose waste
+// F = 1 - live / (16 * allocated blocks) exceeds theta_F packs the live tokens
+// of its first non-full blocks (the growing tail block excluded) into
+// ceil(T / 16) destination blocks from the top of the free list, filled
+// completely in logical order, only when that frees strictly more blocks than
+// it takes; heads that find no headroom are deferred.
+//
+// Reclamation is four launches, each a global step of the plan:
+//   plan   (one workgroup per head): allocated blocks, live tokens, F, the
+//          sources (ordered selection over the block list), T and D;
+//   admit  (one workgroup): heads in (b, h) order take D destinations from
+//          the top of the free list while enough remain (a sequential scan
+//          over LDS); copies the destination ids to the workspace (the free
+//          list's top is overwritten by the pushes later); push offsets of
+//          the sources; every statistic; the new free count;
+//   move   (a wave per source slot): each live source token's K and V row to
+//          its destination row, its position and score staged by rank;
+//   apply  (one workgroup per admitted head): the block list entries of the
+//          sources, liveness, live counts, positions and scores of their
+//          slots, and the sources appended to the free list.
+// Destination rows are fresh blocks, so no copy reads what another writes;
+// the per-slot table of the sources is rewritten only after every copy.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "kvev_device.h"
+#include "kvev_kernels.h"
+
+namespace kvev {
+
+namespace {
+constexpr int kPlanThreads = 256;
+constexpr int kAdmitThreads = 1024;
+constexpr int kMoveWaves = 4;  // source blocks per move workgroup (a wave each)
+constexpr size_t kNoRow = ~(size_t)0;
+
+// Exclusive prefix sum over the workgroup (every thread calls it).
+__device__ __forceinline__ int wg_excl_scan(int v, int *wave_tot) {
+  const int lane = lane_id(), wv = threadIdx.x / kWave;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == kWave - 1) wave_tot[wv] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wv; ++w) before += wave_tot[w];
+  __syncthreads();
+  return before + incl - v;
+}
+}  // namespace
+
+// ------------------------------------------------------------------ marks
+
+__global__ void vtok_zero_kernel(int32_t *status) { *status = 0; }
+
+__global__ __launch_bounds__(256) void vtok_evict_kernel(const VtokArgs P) {
+  const int u = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int m = P.n_victims[u];
+  if (i == 0 && m > P.max_slots) atomicOr(P.status, 1);  // the list holds max_slots entries
+  if (i >= m || i >= P.max_slots) return;
+  const int n = P.seq_len[u];
+  const int v = P.victims[(size_t)u * P.max_slots + i];
+  if (v < 0 || v >= n || v >= P.max_slots || P.block_table[(size_t)u * P.max_blocks + v / kBlock] < 0) {
+    atomicOr(P.status, 1);
+    return;
+  }
+  // clear the byte with one atomic on its word: of two equal victims, one
+  // sees it set
+  const size_t at = (size_t)u * P.max_slots + v;
+  uint32_t *word = reinterpret_cast<uint32_t *>(P.live + (at & ~(size_t)3));
+  const int shift = (int)(at & 3) * 8;
+  const uint32_t old = atomicAnd(word, ~(0xffu << shift));
+  if (((old >> shift) & 0xffu) == 0) {
+    atomicOr(P.status, 1);
+    return;
+  }
+  atomicSub(P.block_live + (size_t)u * P.max_blocks + v / kBlock, 1);
+}
+
+hipError_t launch_vtok_evict(const VtokArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(vtok_zero_kernel, dim3(1), dim3(1), 0, s, a.status);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.units == 0) return hipSuccess;
+  hipLaunchKernelGGL(vtok_evict_kernel, dim3((unsigned)((a.max_slots + 255) / 256), (unsigned)a.units),
+                     dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------- reclamation
+
+// plan record per head: {kind, nsrc, T, D, alloc, live, ...}; kind 0 skip
+// (bad head), 1 left as it is, 2 wants a plan
+__global__ __launch_bounds__(kPlanThreads) void vtok_plan_kernel(const VtokArgs P) {
+  __shared__ int wave_tot[kPlanThreads / kWave];
+  __shared__ int s_alloc, s_live, s_bad, s_k, s_T;
+  const int u = blockIdx.x, tid = threadIdx.x;
+  const int n = P.seq_len[u];
+  int32_t *plan = P.plan + (size_t)u * 8;
+  if (n < 0 || n > P.max_slots) {
+    if (tid == 0) {
+      plan[0] = 0;
+      plan[6] = 2;  // status bit
+    }
+    return;
+  }
+  const int nb = (n + kBlock - 1) / kBlock;
+  const int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
+  const int32_t *bl = P.block_live + (size_t)u * P.max_blocks;
+  if (tid == 0) {
+    s_alloc = 0;
+    s_live = 0;
+    s_bad = 0;
+    s_k = 0;
+    s_T = 0;
+  }
+  __syncthreads();
+  // allocated blocks, live tokens, and the ordered selection of sources: the
+  // first max_sources allocated blocks that are not full, the tail excluded
+  int32_t *src = P.src + (size_t)u * P.max_sources;
+  int32_t *srcoff = P.srcoff + (size_t)u * P.max_sources;
+  int k_base = 0, t_base = 0;
+  int my_alloc = 0, my_live = 0, my_bad = 0;
+  for (int lb0 = 0; lb0 < nb; lb0 += kPlanThreads) {
+    const int lb = lb0 + tid;
+    const int e = lb < nb ? bt[lb] : -1;
+    const int c = lb < nb ? bl[lb] : 0;
+    if (e >= 0) {
+      ++my_alloc;
+      my_live += c;
+      if (e >= P.num_blocks || c < 0 || c > kBlock) my_bad = 1;
+    }
+    const int cand = (lb < nb - 1 && e >= 0 && c < kBlock) ? 1 : 0;
+    const int rank = k_base + wg_excl_scan(cand, wave_tot);
+    const int toff = t_base + wg_excl_scan(cand ? c : 0, wave_tot);
+    if (cand && rank < P.max_sources) {
+      src[rank] = lb;
+      srcoff[rank] = toff;
+    }
+    // the chunk's totals (the last thread's inclusive values)
+    if (tid == kPlanThreads - 1) {
+      s_k = rank + cand;
+      s_T = toff + (cand ? c : 0);
+    }
+    __syncthreads();
+    k_base = s_k;
+    t_base = s_T;
+    __syncthreads();
+  }
+  // T counts only the first max_sources candidates
+  if (my_alloc) atomicAdd(&s_alloc, my_alloc);
+  if (my_live) atomicAdd(&s_live, my_live);
+  if (my_bad) atomicOr(&s_bad, 1);
+  __syncthreads();
+  if (tid != 0) return;
+  const int k = min(k_base, P.max_sources);
+  int T = 0;
+  if (k_base > P.max_sources) {
+    // the live tokens of the first max_sources candidates: the offset of the
+    // next one, or (all of them) the chunk totals
+    T = srcoff[k - 1] + bl[src[k - 1]];
+  } else {
+    T = t_base;
+  }
+  const int D = (T + kBlock - 1) / kBlock;
+  const int alloc = s_alloc, live = s_live;
+  plan[4] = alloc;
+  plan[5] = live;
+  plan[6] = 0;
+  if (s_bad) {
+    plan[0] = 0;
+    plan[6] = 4;
+    return;
+  }
+  // Eq. 1 over the head, in double, against the threshold
+  const double F = alloc > 0 ? 1.0 - (double)live / (16.0 * (double)alloc) : 0.0;
+  if (!(F > P.theta_f) || k < 2 || D >= k) {
+    plan[0] = 1;
+    return;
+  }
+  plan[0] = 2;
+  plan[1] = k;
+  plan[2] = T;
+  plan[3] = D;
+}
+
+__global__ __launch_bounds__(kAdmitThreads) void vtok_admit_kernel(const VtokArgs P) {
+  extern __shared__ int adm[];  // [units] D (-1: no plan), then [units] destination offsets
+  __shared__ int wave_tot[kAdmitThreads / kWave];
+  __shared__ int s_tot, s_taken;
+  const int U = P.units, tid = threadIdx.x;
+  int *dl = adm, *doff = adm + U;
+  const int fc = *P.free_count;
+  // a list holds at most every block once
+  const bool fc_ok = fc >= 0 && fc <= P.free_capacity && fc <= P.num_blocks;
+  // D of every head that wants a plan, and its offset if every plan fits
+  int dsum = 0;
+  for (int u0 = 0; u0 < U; u0 += kAdmitThreads) {
+    const int u = u0 + tid;
+    int d = -1;
+    if (u < U && P.plan[(size_t)u * 8] == 2) d = P.plan[(size_t)u * 8 + 3];
+    const int dd = d > 0 ? d : 0;
+    const int ex = wg_excl_scan(dd, wave_tot);
+    if (u < U) {
+      dl[u] = d;
+      doff[u] = d >= 0 ? dsum + ex : -1;
+    }
+    if (tid == kAdmitThreads - 1) s_tot = dsum + ex + dd;
+    __syncthreads();
+    dsum = s_tot;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    int taken = dsum;
+    if (!fc_ok) {  // an unusable free count: every plan waits
+      for (int u = 0; u < U; ++u)
+        if (dl[u] >= 0) doff[u] = -2;
+      taken = 0;
+    } else if (dsum > fc) {  // first fit in (b, h) order; a head that does not fit is deferred
+      taken = 0;
+      for (int u = 0; u < U; ++u) {
+        const int d = dl[u];
+        if (d < 0) continue;
+        if (taken + d > fc) {
+          doff[u] = -2;
+        } else {
+          doff[u] = taken;
+          taken += d;
+        }
+      }
+    }
+    s_taken = taken;
+  }
+  __syncthreads();
+  const int taken = s_taken;
+  // the destination ids, before the pushes overwrite the list's top
+  for (int i = tid; i < taken; i += kAdmitThreads) P.dst_ids[i] = P.free_list[fc - 1 - i];
+  // push offsets and statistics, heads in order
+  long long st[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+  int status = fc_ok ? 0 : 8, pbase = 0;
+  for (int u0 = 0; u0 < U; u0 += kAdmitThreads) {
+    const int u = u0 + tid;
+    int push = 0;
+    if (u < U) {
+      const int32_t *plan = P.plan + (size_t)u * 8;
+      const int kind = plan[0];
+      status |= plan[6];
+      if (kind != 0) {
+        st[6] += plan[5];
+        st[7] += plan[4];
+        st[8] += plan[4];
+      }
+      if (kind == 1) st[2] += 1;
+      if (kind == 2) {
+        if (doff[u] == -2) {
+          st[1] += 1;
+        } else {
+          push = plan[1];
+          st[0] += 1;
+          st[3] += plan[1] - plan[3];
+          st[4] += plan[2];
+          st[8] -= plan[1] - plan[3];
+        }
+      }
+      P.dst_off[u] = kind == 2 ? doff[u] : -1;
+    }
+    const int ex = wg_excl_scan(push, wave_tot);
+    if (u < U) P.push_off[u] = pbase + ex;
+    if (tid == kAdmitThreads - 1) s_tot = pbase + ex + push;  // running total
+    __syncthreads();
+    pbase = s_tot;
+    __syncthreads();
+  }
+  // workgroup sums of the statistics (fixed order)
+  __shared__ long long s_st[9][kAdmitThreads / kWave];
+  __shared__ int s_status[kAdmitThreads / kWave];
+#pragma unroll
+  for (int c = 0; c < 9; ++c) {
+    long long v = st[c];
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    if (lane_id() == 0) s_st[c][tid / kWave] = v;
+  }
+  int sv = status;
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) sv |= __shfl_xor(sv, o);
+  if (lane_id() == 0) s_status[tid / kWave] = sv;
+  __syncthreads();
+  if (tid == 0) {
+    long long tot[9];
+    int stat = 0;
+    for (int c = 0; c < 9; ++c) {
+      tot[c] = 0;
+      for (int w = 0; w < kAdmitThreads / kWave; ++w) tot[c] += s_st[c][w];
+    }
+    for (int w = 0; w < kAdmitThreads / kWave; ++w) stat |= s_status[w];
+    // a list that cannot hold the returned sources (block ids shared between
+    // the tables and the list): the pushes past its capacity are dropped
+    const long long end = (long long)(fc_ok ? fc : 0) - taken + pbase;
+    if (end > P.free_capacity) stat |= 8;
+    for (int c = 0; c < 9; ++c) P.stats[c] = tot[c];
+    P.stats[5] = tot[4] * 2 * P.row_bytes * 2;
+    P.stats[9] = stat;
+    P.misc[0] = fc_ok ? fc : 0;
+    P.misc[1] = taken;
+    if (fc_ok) *P.free_count = (int32_t)min(end, (long long)P.free_capacity);
+  }
+}
+
+// A wave per source block: its live rows (K and V) go to consecutive rows of
+// the destinations; positions and scores are staged by their place among the
+// moved tokens.
+__global__ __launch_bounds__(kMoveWaves * kWave) void vtok_move_kernel(const VtokArgs P) {
+  const int u = blockIdx.y;
+  const int off = P.dst_off[u];
+  if (off < 0) return;  // not reclaimed
+  const int k = P.plan[(size_t)u * 8 + 1];
+  const int l = lane_id(), pieces = P.row_bytes / 16;
+  const size_t urow = (size_t)u * P.max_slots;
+  const size_t tbase = (size_t)u * P.max_sources * kBlock;
+  for (int j = blockIdx.x * kMoveWaves + (int)(threadIdx.x / kWave); j < k;
+       j += (int)gridDim.x * kMoveWaves) {
+    const int lb = P.src[(size_t)u * P.max_sources + j];
+    const int i0 = P.srcoff[(size_t)u * P.max_sources + j];  // first moved index of this block
+    const int from_blk = P.block_table[(size_t)u * P.max_blocks + lb];
+    const bool mine = l < kBlock && P.live[urow + (size_t)lb * kBlock + l] != 0;
+    const uint64_t mask = __ballot(mine);
+    const int c = __popcll(mask);
+    const int rank = __popcll(mask & ((1ull << l) - 1));
+    const int T = P.plan[(size_t)u * 8 + 2];
+    if (mine && i0 + rank < T) {  // (always, when the live counts match the marks)
+      P.tpos[tbase + i0 + rank] = P.pos[urow + (size_t)lb * kBlock + l];
+      if (P.score) P.tscore[tbase + i0 + rank] = P.score[urow + (size_t)lb * kBlock + l];
+    }
+    // lane r < c learns the offset of the r-th live slot
+    const int o_of_rank =
+        __builtin_amdgcn_ds_permute((mine ? rank : (l | 32)) * 4, l);
+    const int n16 = c * pieces;  // 16-byte pieces per pool
+    for (int t0 = 0; t0 < 2 * n16; t0 += 4 * kWave) {
+      uint4 v[4];
+      size_t to[4];
+      uint8_t *pool[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = t0 + q * kWave + l;
+        const int which = t >= n16 ? 1 : 0;
+        const int rem = t - which * n16;
+        const int r = rem / pieces, p = rem - r * pieces;
+        const int o = __shfl(o_of_rank, r < kBlock ? r : 0);
+        pool[q] = which ? P.v_pool : P.k_pool;
+        to[q] = kNoRow;
+        if (t < 2 * n16 && i0 + r < T) {
+          const int i = i0 + r;
+          const int to_blk = P.dst_ids[off + i / kBlock];
+          to[q] = (((size_t)to_blk * kBlock + i % kBlock) * P.row_bytes) + (size_t)p * 16;
+          v[q] = ld16(pool[q] + ((size_t)from_blk * kBlock + o) * P.row_bytes + (size_t)p * 16);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (t0 + q * kWave + l < 2 * n16 && to[q] != kNoRow) st16(pool[q] + to[q], v[q]);
+    }
+  }
+}
+
+// The per-slot table and the block list of the source positions; the sources
+// go to the free list.  Runs after every copy, so no slot is read after it is
+// rewritten.
+__global__ __launch_bounds__(256) void vtok_apply_kernel(const VtokArgs P) {
+  const int u = blockIdx.y;
+  const int off = P.dst_off[u];
+  if (off < 0) return;
+  const int32_t *plan = P.plan + (size_t)u * 8;
+  const int k = plan[1], T = plan[2], D = plan[3];
+  const size_t urow = (size_t)u * P.max_slots;
+  const size_t tbase = (size_t)u * P.max_sources * kBlock;
+  int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
+  const int32_t *src = P.src + (size_t)u * P.max_sources;
+  const int base = P.misc[0] - P.misc[1] + P.push_off[u];  // where this head's sources go
+  for (int x = blockIdx.x * 256 + (int)threadIdx.x; x < k * kBlock; x += (int)gridDim.x * 256) {
+    const int j = x / kBlock, o = x % kBlock;
+    const int lb = src[j];
+    // the first D source positions take the moved tokens in order
+    const int cnt = j < D ? min(kBlock, T - kBlock * j) : 0;
+    const size_t s = urow + (size_t)lb * kBlock + o;
+    P.live[s] = o < cnt ? 1 : 0;
+    if (o < cnt) {
+      P.pos[s] = P.tpos[tbase + (size_t)kBlock * j + o];
+      if (P.score) P.score[s] = P.tscore[tbase + (size_t)kBlock * j + o];
+    }
+    if (o == 0) {
+      if (base + j < P.free_capacity) P.free_list[base + j] = bt[lb];
+      bt[lb] = j < D ? P.dst_ids[off + j] : -1;
+      P.block_live[(size_t)u * P.max_blocks + lb] = cnt;
+    }
+  }
+}
+
+hipError_t launch_vtok_reclaim(const VtokArgs &a, hipStream_t s) {
+  if (a.units == 0) return hipSuccess;
+  hipLaunchKernelGGL(vtok_plan_kernel, dim3((unsigned)a.units), dim3(kPlanThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t adm_lds = (size_t)a.units * 2 * sizeof(int);
+  static size_t lds_set = 0;  // largest dynamic LDS size enabled for the admission kernel
+  if (adm_lds > 49152 && adm_lds > lds_set) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(vtok_admit_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)adm_lds);
+    if (e != hipSuccess) return e;
+    lds_set = adm_lds;
+  }
+  hipLaunchKernelGGL(vtok_admit_kernel, dim3(1), dim3(kAdmitThreads), adm_lds, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // source blocks of a head: a wave each, striding when there are many
+  const unsigned move_x = (unsigned)std::min((a.max_sources + kMoveWaves - 1) / kMoveWaves, 256);
+  hipLaunchKernelGGL(vtok_move_kernel, dim3(move_x, (unsigned)a.units), dim3(kMoveWaves * kWave), 0,
+                     s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned apply_x = (unsigned)std::min((a.max_sources * kBlock + 255) / 256, 64);
+  hipLaunchKernelGGL(vtok_apply_kernel, dim3(apply_x, (unsigned)a.units), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvev

@@ -594,7 +594,12 @@ int orc_vtok_evict(const int32_t *block_table, const int32_t *seq_len, uint8_t *
   const int64_t max_slots = (int64_t)max_blocks * 16;
   *status = 0;
   for (int64_t u = 0; u < units; ++u) {
-    const int64_t n = seq_len[u], m = n_victims[u];
+    const int64_t n = seq_len[u];
+    int64_t m = n_victims[u];
+    if (m > max_slots) { /* the list holds max_slots entries */
+      *status |= 1;
+      m = max_slots;
+    }
     for (int64_t i = 0; i < m; ++i) {
       const int64_t v = victims[u * max_slots + i];
       if (v < 0 || v >= n || v >= max_slots || block_table[u * max_blocks + v / 16] < 0 ||
@@ -635,12 +640,19 @@ int orc_vtok_reclaim(void *k_pool, void *v_pool, int32_t elem_bytes, int32_t hea
       continue;
     }
     const int64_t nb = (n + 15) / 16;
-    int64_t alloc = 0, livec = 0;
+    int64_t alloc = 0, livec = 0, bad = 0;
     for (int64_t lb = 0; lb < nb; ++lb)
       if (bt[lb] >= 0) {
         ++alloc;
         livec += block_live[u * max_blocks + lb];
+        if (bt[lb] >= num_blocks || block_live[u * max_blocks + lb] < 0 ||
+            block_live[u * max_blocks + lb] > 16)
+          bad = 1;
       }
+    if (bad) {
+      stats[9] |= 4;
+      continue;
+    }
     stats[6] += livec;
     stats[7] += alloc;
     const double F = alloc > 0 ? 1.0 - (double)livec / (16.0 * (double)alloc) : 0.0;

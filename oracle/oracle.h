@@ -137,10 +137,13 @@ int orc_vtok_evict(const int32_t *block_table, const int32_t *seq_len, uint8_t *
  *     any full block between two sources); K, V, pos, live, block_live and
  *     the optional score row follow; after every head has planned, the source
  *     blocks are appended to the free list in (b, h, block) order.
- * stats[10] = {heads reclaimed, heads deferred, heads below the threshold,
- * blocks freed, rows moved, bytes moved (K+V read+write), live tokens,
- * allocated blocks before, after, status}.  Returns 0, -1 (invalid), -2
- * (free list capacity too small; nothing modified). */
+ * stats[10] = {heads reclaimed, heads deferred, heads left as they are (waste
+ * at or below theta_f, or no plan that frees a block), blocks freed, rows
+ * moved, bytes moved (K+V read+write), live tokens, allocated blocks before,
+ * after, status (an OR of 2: a seq_len out of range, 4: a block id past the
+ * pool or a live count outside [0, 16]; such heads are skipped and not
+ * counted)}.  Returns 0, -1 (invalid),
+ * -2 (free list capacity too small; nothing modified). */
 int orc_vtok_reclaim(void *k_pool, void *v_pool, int32_t elem_bytes, int32_t head_dim,
                      int32_t *block_table, const int32_t *seq_len, int32_t *pos, float *score,
                      uint8_t *live, int32_t *block_live, int32_t units, int32_t max_blocks,

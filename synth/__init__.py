@@ -35,7 +35,7 @@ _LIB = os.path.join(_HERE, "libsynth.so")
 BLOCK = 16
 
 # tensor ids for the counter streams
-T_Q, T_K, T_V, T_DIR, T_PLANT, T_NEARMEAN, T_PERM, T_SPAN, T_DECODE_Q, T_MISC = range(1, 11)
+T_Q, T_K, T_V, T_DIR, T_PLANT, T_NEARMEAN, T_PERM, T_SPAN, T_DECODE_Q, T_MISC, T_VICTIM = range(1, 12)
 
 
 def build(force: bool = False) -> str:
@@ -351,3 +351,26 @@ def decode_token_kv(case: dict, step: int) -> tuple:
     v = case["v_pool"][blk.reshape(-1), s % BLOCK].reshape(B, Hkv, -1)
     return np.ascontiguousarray(k), np.ascontiguousarray(v)
 
+
+
+def random_victims(case: dict, budget: int, recent: int) -> tuple:
+    """Victims of a uniform random eviction policy: for every KV head of
+    length n, n - budget positions drawn without replacement from the first
+    n - recent (none when n <= budget), ascending.  Returns (victims int32
+    [B, Hkv, max_slots], -1 past the count; n_victims int32 [B, Hkv])."""
+    cfg = case["cfg"]
+    B, Hkv = case["B"], case["Hkv"]
+    ms = case["max_blocks"] * BLOCK
+    vic = np.full((B, Hkv, ms), -1, np.int32)
+    nv = np.zeros((B, Hkv), np.int32)
+    for b in range(B):
+        for h in range(Hkv):
+            n = int(case["seq_len"][b, h])
+            m = n - budget
+            if m <= 0:
+                continue
+            pool = n - recent
+            perm = shuffled(pool, cfg.seed, stream_id(T_VICTIM, b * Hkv + h, case["layer"]))
+            vic[b, h, :m] = np.sort(perm[:m])
+            nv[b, h] = m
+    return vic, nv

@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
     assert set(names) == set(K.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvev_abi_version() == K.ABI_VERSION == 6
+    assert L.kvev_abi_version() == K.ABI_VERSION == 7
     for code in (0, -1, -2, -3, -4):
         assert K.strerror(code)
 
@@ -275,3 +275,50 @@ def test_h2o_step_refusals():
     assert L.kvev_h2o_workspace_bytes(ctypes.byref(cache(max_blocks=8)), 0, 64) == 0
     assert L.kvev_h2o_workspace_bytes(ctypes.byref(cache(max_blocks=8)), 4, 5000) == 0
     assert L.kvev_h2o_workspace_bytes(None, 4, 64) == 0
+
+
+def test_vtok_refusals():
+    """Every refusal of kvev_vtok_evict and kvev_vtok_reclaim is decided on the
+    host, before a launch."""
+    L = K.load_library()
+
+    def evict(c=None, ptrs=None):
+        c = cache(max_blocks=8) if c is None else c
+        p = dict(live=FAKE, bl=FAKE, vic=FAKE, nv=FAKE, st=FAKE)
+        p.update(ptrs or {})
+        return L.kvev_vtok_evict(ctypes.byref(c), p["live"], p["bl"], p["vic"], p["nv"], p["st"],
+                                 None)
+
+    for name in ("live", "bl", "vic", "nv", "st"):
+        assert evict(ptrs={name: None}) == K.EINVAL, name
+    assert evict(ptrs={"live": FAKE + 1}) == K.EINVAL      # live must be 4-byte aligned
+    assert evict(c=cache(head_dim=96)) == K.EINVAL
+
+    def reclaim(c=None, theta=0.25, max_sources=8, cap=None, ptrs=None, ws_bytes=1 << 30):
+        c = cache(max_blocks=8) if c is None else c
+        p = dict(live=FAKE, bl=FAKE, fl=FAKE, fc=FAKE, st=FAKE, ws=FAKE)
+        p.update(ptrs or {})
+        cap = c.num_blocks if cap is None else cap
+        return L.kvev_vtok_reclaim(ctypes.byref(c), p["live"], p["bl"], None, theta, max_sources,
+                                   p["fl"], p["fc"], cap, p["st"], p["ws"], ws_bytes, None)
+
+    for name in ("live", "bl", "fl", "fc", "st"):
+        assert reclaim(ptrs={name: None}) == K.EINVAL, name
+    assert reclaim(ptrs={"live": FAKE + 2}) == K.EINVAL
+    for theta in (-0.1, 1.0, float("nan"), float("inf")):
+        assert reclaim(theta=theta) == K.EINVAL, theta
+    assert reclaim(max_sources=1) == K.EINVAL
+    assert reclaim(max_sources=4097) == K.EINVAL
+    assert reclaim(c=cache(batch=8193, kv_heads=1)) == K.EUNSUPPORTED
+    c = cache(max_blocks=8)
+    assert reclaim(c=c, cap=c.num_blocks - 1) == K.ENOSPACE
+    need = L.kvev_vtok_workspace_bytes(ctypes.byref(c), 8)
+    assert need > 0
+    assert reclaim(ptrs={"ws": None}) == K.ENOSPACE
+    assert reclaim(ws_bytes=need - 1) == K.ENOSPACE
+    # the size query refuses what the call refuses
+    assert L.kvev_vtok_workspace_bytes(ctypes.byref(c), 1) == 0
+    assert L.kvev_vtok_workspace_bytes(ctypes.byref(c), 4097) == 0
+    assert L.kvev_vtok_workspace_bytes(None, 8) == 0
+    # it grows with max_sources (staged rows of every source)
+    assert L.kvev_vtok_workspace_bytes(ctypes.byref(c), 64) > need

@@ -1,0 +1,333 @@
+"""GPU parity of vToken's liveness marks (kvev_vtok_evict) and lazy,
+threshold-gated reclamation (kvev_vtok_reclaim) against oracle.vtok_evict and
+oracle.vtok_reclaim.
+
+Both sides are integer work and copies, and both take the same decisions in
+the same order (first fit in (b, h) order, destinations from the top of the
+free list, sources appended after every head has planned), so every output
+is compared bit for bit: both pools whole, block tables, positions, liveness,
+live counts, score rows, the free list and its count, and the statistics.
+
+States are built here: shuffled block ids, ragged lengths (empty heads and
+partial tail blocks among them), random liveness with some full and some
+empty blocks, -1 entries left by earlier reclamations, and a few heads the
+call must skip (a length past the capacity, a block id past the pool, a live
+count out of range).
+"""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_eviction_qk_amd as K
+import oracle
+import synth
+from tests.gpu_helpers import dev, device_cache, host
+
+pytestmark = pytest.mark.gpu
+rng = np.random.default_rng
+
+
+def _say(msg):
+    print(f"[vtok] {msg}", flush=True)
+
+
+def _state(seed, dtype="bf16", D=128, B=2, Hkv=3, max_blocks=12, spare=40, holes=True,
+           bad=()):
+    """A vToken state with shuffled ids and a free list of the unused ids.
+    bad: (kind, unit) pairs with kind "len", "id" or "count"."""
+    r = rng(seed)
+    U = B * Hkv
+    num_blocks = U * max_blocks + spare
+    perm = synth.shuffled(num_blocks, seed, 11)
+    bt = perm[:U * max_blocks].reshape(B, Hkv, max_blocks).astype(np.int32).copy()
+    edt = np.uint16 if dtype == "bf16" else np.float32
+    k_pool = synth.encode(r.normal(0, 1, (num_blocks, 16, D)), dtype).astype(edt)
+    v_pool = synth.encode(r.normal(0, 1, (num_blocks, 16, D)), dtype).astype(edt)
+    ms = max_blocks * 16
+    seq = r.integers(0, ms + 1, size=(B, Hkv)).astype(np.int32)
+    seq.reshape(-1)[0] = ms                # a head at capacity
+    if U > 2:
+        seq.reshape(-1)[1] = 0             # an empty head
+        seq.reshape(-1)[2] = ms - 5        # a partial tail block
+    pos = np.zeros((B, Hkv, ms), np.int32)
+    live = np.zeros((B, Hkv, ms), np.uint8)
+    for u in range(U):
+        b, h = divmod(u, Hkv)
+        n = int(seq[b, h])
+        pos[b, h] = r.permutation(1 << 20)[:ms].astype(np.int32)   # any unique positions
+        nb = (n + 15) // 16
+        for lb in range(nb):
+            lo, hi = lb * 16, min(n, lb * 16 + 16)
+            kind = r.integers(0, 5)
+            if kind == 0:
+                keep = np.ones(hi - lo, bool)                     # full
+            elif kind == 1:
+                keep = np.zeros(hi - lo, bool)                    # every token evicted
+            else:
+                keep = r.uniform(0, 1, hi - lo) < r.uniform(0.1, 0.9)
+            live[b, h, lo:hi] = keep
+        bt[b, h, nb:] = -1
+        if holes and nb > 3:               # entries freed by an earlier reclamation
+            for lb in r.choice(nb - 1, size=min(2, nb - 2), replace=False):
+                bt[b, h, lb] = -1
+                live[b, h, lb * 16:lb * 16 + 16] = 0
+    block_live = live.reshape(B, Hkv, max_blocks, 16).sum(-1).astype(np.int32)
+    for kind, u in bad:
+        b, h = divmod(u, Hkv)
+        if kind == "len":
+            seq[b, h] = ms + 16
+        elif kind == "id":
+            bt[b, h, 0] = num_blocks + 5
+        elif kind == "count":
+            seq[b, h] = ms
+            bt[b, h, 1] = perm[u * max_blocks + 1]
+            block_live[b, h, 1] = 17
+    used = set(bt[bt >= 0].tolist())
+    free = np.array([x for x in perm.tolist() if x not in used and x < num_blocks], np.int32)
+    fl = np.full(num_blocks + 8, -1, np.int32)
+    fl[:free.size] = free
+    score = r.uniform(0, 1, (B, Hkv, ms)).astype(np.float32)
+    st = dict(dtype=dtype, B=B, Hkv=Hkv, D=D, max_blocks=max_blocks, num_blocks=num_blocks,
+              k_pool=k_pool, v_pool=v_pool, block_table=bt, seq_len=seq, pos=pos, live=live,
+              block_live=block_live, score=score)
+    return st, fl, int(free.size)
+
+
+class Dev:
+    """Device copy of a vToken state."""
+
+    def __init__(self, st, fl, fc):
+        self.c = device_cache(st)
+        self.live = dev(st["live"])
+        self.block_live = dev(st["block_live"])
+        self.score = dev(st["score"])
+        self.fl = dev(fl)
+        self.fc = dev(np.array([fc], np.int32))
+        self.ws = None
+
+    def reclaim(self, theta, max_sources, with_score=True, stream=None):
+        if self.ws is None or self.ws_ms < max_sources:
+            self.ws = K.new_vtok_workspace(self.c, max_sources)
+            self.ws_ms = max_sources
+        return K.vtok_reclaim(self.c, self.live, self.block_live, theta, max_sources, self.fl,
+                              self.fc, self.ws, score=self.score if with_score else None,
+                              stream=stream)
+
+    def evict(self, vic, nv):
+        return K.vtok_evict(self.c, self.live, self.block_live, dev(vic), dev(nv))
+
+    def state(self, like):
+        out = dict(like)
+        out.update(k_pool=host(self.c.k_pool), v_pool=host(self.c.v_pool),
+                   block_table=host(self.c.block_table), pos=host(self.c.pos),
+                   live=host(self.live), block_live=host(self.block_live),
+                   score=host(self.score))
+        return out, host(self.fl), int(host(self.fc)[0])
+
+
+def _same(o, g, keys, what=""):
+    for k in keys:
+        if not np.array_equal(o[k], g[k]):
+            bad = np.argwhere(o[k] != g[k])
+            raise AssertionError(f"{what}: {k} differs at {len(bad)} places, first "
+                                 f"{bad[0].tolist()}: oracle {o[k][tuple(bad[0])]!r} "
+                                 f"gpu {g[k][tuple(bad[0])]!r}")
+
+
+STATE_KEYS = ("k_pool", "v_pool", "block_table", "pos", "live", "block_live", "score")
+
+
+def _compare_reclaim(st, fl, fc, d, theta, max_sources, stats_g, with_score=True, what=""):
+    o, ofl, ofc, ost = oracle.vtok_reclaim(st, theta, max_sources, fl, fc, with_score=with_score)
+    torch.cuda.synchronize()
+    g, gfl, gfc = d.state(st)
+    keys = STATE_KEYS if with_score else STATE_KEYS[:-1]
+    _same(o, g, keys, what)
+    assert gfc == ofc, (what, gfc, ofc)
+    assert np.array_equal(gfl[:gfc], ofl[:ofc]), what
+    assert host(stats_g).tolist() == ost.tolist(), (what, host(stats_g).tolist(), ost.tolist())
+    return o, ofl, ofc, ost
+
+
+# ------------------------------------------------------------------ marks
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_evict_marks_bit_exact(seed):
+    st, fl, fc = _state(seed, B=2, Hkv=4, max_blocks=10)
+    U, ms = 8, 160
+    r = rng(100 + seed)
+    vic = np.full((2, 4, ms), -1, np.int32)
+    nv = np.zeros((2, 4), np.int32)
+    for u in range(U):
+        b, h = divmod(u, 4)
+        cand = np.flatnonzero(st["live"][b, h])
+        m = int(r.integers(0, max(1, cand.size - 8)))
+        v = r.permutation(cand)[:m].tolist()
+        if u == 3:   # invalid victims: negative, past the length, already dead, a repeat
+            dead = np.flatnonzero(st["live"][b, h, :int(st["seq_len"][b, h])] == 0)
+            v += [-4, int(st["seq_len"][b, h]) + 1, ms + 7] + dead[:2].tolist()
+            if v[:1]:
+                v.append(v[0])
+        vic[b, h, :len(v)] = v
+        nv[b, h] = len(v)
+    _say(f"evict seed {seed}: {int(nv.sum())} victims")
+    d = Dev(st, fl, fc)
+    status = d.evict(vic, nv)
+    o, ostatus = oracle.vtok_evict(st, vic, nv)
+    torch.cuda.synchronize()
+    assert int(host(status)[0]) == ostatus
+    assert ostatus == 1
+    assert np.array_equal(host(d.live), o["live"])
+    assert np.array_equal(host(d.block_live), o["block_live"])
+    # a clean batch leaves the status at 0
+    nv2 = np.zeros_like(nv)
+    assert int(host(d.evict(vic, nv2))[0]) == 0
+
+
+# ------------------------------------------------------------ reclamation
+
+
+CASES = [
+    # dtype, D, B, Hkv, max_blocks, spare, free count cap, theta, max_sources, bad
+    ("bf16", 128, 2, 3, 12, 200, None, 0.25, 8, ()),                  # every plan fits
+    ("f32", 64, 2, 4, 20, 200, None, 0.10, 64, (("len", 5),)),
+    ("bf16", 64, 1, 8, 16, 6, 5, 0.0, 16, (("id", 2), ("count", 6))),  # first fit, deferrals
+    ("f32", 128, 3, 2, 9, 0, 0, 0.0, 4, ()),                          # no headroom at all
+    ("bf16", 128, 4, 8, 40, 300, None, 0.25, 2, ()),                  # the smallest batch
+    ("bf16", 128, 2, 2, 300, 5000, None, 0.25, 4096, ()),             # long heads, one batch
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-D{c[1]}-{c[2]}x{c[3]}-"
+                         f"mb{c[4]}-fc{c[6]}-th{c[7]}-ms{c[8]}")
+def test_reclaim_bit_exact(case):
+    dtype, D, B, Hkv, mb, spare, cap, theta, ms, bad = case
+    st, fl, fc = _state(7 + mb, dtype=dtype, D=D, B=B, Hkv=Hkv, max_blocks=mb, spare=spare,
+                        bad=bad)
+    if cap is not None:   # only the first `cap` entries of the list are free
+        fc = min(fc, cap)
+    _say(f"reclaim {case}: free {fc}")
+    d = Dev(st, fl, fc)
+    stats = d.reclaim(theta, ms)
+    o, ofl, ofc, ost = _compare_reclaim(st, fl, fc, d, theta, ms, stats, what=str(case))
+    _say(f"stats {ost.tolist()}")
+    if bad:
+        assert ost[9] != 0
+    if cap == 0:
+        assert ost[0] == 0 and ost[1] > 0
+    elif cap is not None:
+        assert ost[0] > 0 and ost[1] > 0
+    else:
+        assert ost[1] == 0 and ost[0] > 0
+
+
+def test_reclaim_without_score_row():
+    st, fl, fc = _state(3, B=2, Hkv=2, max_blocks=12, spare=100)
+    d = Dev(st, fl, fc)
+    stats = d.reclaim(0.1, 16, with_score=False)
+    _compare_reclaim(st, fl, fc, d, 0.1, 16, stats, with_score=False, what="no score")
+    assert np.array_equal(host(d.score), st["score"])
+
+
+def test_free_count_out_of_range_admits_nothing():
+    st, fl, fc = _state(4, B=1, Hkv=4, max_blocks=12, spare=100)
+    d = Dev(st, fl, fc)
+    d.fc.fill_(st["num_blocks"] + 1)     # more entries than blocks: refused on the device
+    stats = d.reclaim(0.0, 16)
+    torch.cuda.synchronize()
+    s = host(stats)
+    assert s[9] & 8 and s[0] == 0 and s[3] == 0
+    assert int(host(d.fc)[0]) == st["num_blocks"] + 1
+    assert np.array_equal(host(d.c.block_table), st["block_table"])
+
+
+def test_chain_of_marks_and_reclamations():
+    """Each side evolves by its own calls: marks, a reclamation, more marks,
+    another, with the free list carried over; identical at every stage."""
+    st, fl, fc = _state(21, B=2, Hkv=4, max_blocks=24, spare=60)
+    d = Dev(st, fl, fc)
+    r = rng(5)
+    for it in range(4):
+        U, ms = 8, 24 * 16
+        vic = np.full((2, 4, ms), -1, np.int32)
+        nv = np.zeros((2, 4), np.int32)
+        for u in range(U):
+            b, h = divmod(u, 4)
+            cand = np.flatnonzero(st["live"][b, h, :int(st["seq_len"][b, h])])
+            m = int(r.integers(0, cand.size // 3 + 1))
+            vic[b, h, :m] = r.permutation(cand)[:m]
+            nv[b, h] = m
+        st, _ = oracle.vtok_evict(st, vic, nv)
+        d.evict(vic, nv)
+        stats = d.reclaim(0.25, 6)
+        st, fl, fc, ost = _compare_reclaim(st, fl, fc, d, 0.25, 6, stats, what=f"iteration {it}")
+        _say(f"iteration {it}: stats {ost.tolist()}")
+
+
+def test_reclaim_on_a_relocation_stream():
+    """The copies run on a stream of their own; the next reader waits on an
+    event recorded after them (a GPU-side wait, no host synchronisation)."""
+    st, fl, fc = _state(30, B=2, Hkv=4, max_blocks=30, spare=200)
+    d = Dev(st, fl, fc)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    ready = torch.cuda.Event()
+    ready.record(main)                          # the state is written on the main stream
+    side.wait_event(ready)
+    stats = d.reclaim(0.25, 32, stream=side)
+    done = torch.cuda.Event()
+    done.record(side)
+    main.wait_event(done)
+    # a reader on the main stream: the block table and both pools, copied there
+    bt = d.c.block_table.clone()
+    kp = d.c.k_pool.clone()
+    vp = d.c.v_pool.clone()
+    st_h = stats.clone()
+    torch.cuda.synchronize()
+    o, ofl, ofc, ost = oracle.vtok_reclaim(st, 0.25, 32, fl, fc, with_score=True)
+    assert np.array_equal(host(bt), o["block_table"])
+    assert np.array_equal(host(kp), o["k_pool"]) and np.array_equal(host(vp), o["v_pool"])
+    assert host(st_h).tolist() == ost.tolist()
+    assert ost[0] > 0
+
+
+def test_full_size_random_eviction_layer():
+    """One layer of the block-aware workload (B16, 8 KV heads, D128, 64000
+    tokens: 4000 blocks a head, about 4.2 GB of K+V) with half of every head's
+    tokens marked dead by a uniform random policy (16 recent protected), then
+    one reclamation whose source batch covers the whole head (4096), in the
+    launch configuration of the benchmark.  Every output against the oracle."""
+    cfg = synth.CONFIGS["block_evict_64k"]
+    U = cfg.B * cfg.Hkv
+    case = synth.make_case(cfg, spare_blocks=U * 2048)
+    _say("full size: state built")
+    st = dict(case)
+    st["live"], st["block_live"] = oracle.vtok_liveness(case)
+    st["score"] = np.zeros((cfg.B, cfg.Hkv, case["max_blocks"] * 16), np.float32)
+    vic, nv = synth.random_victims(case, cfg.budget, cfg.recent)
+    used = set(case["block_table"][case["block_table"] >= 0].tolist())
+    free = np.array([x for x in range(case["num_blocks"]) if x not in used], np.int32)
+    fl = np.full(case["num_blocks"], -1, np.int32)
+    fl[:free.size] = free
+    d = Dev(st, fl, free.size)
+    d.evict(vic, nv)
+    stats = d.reclaim(0.25, 4096, with_score=False)
+    _say("full size: GPU done; oracle")
+    st2, _ = oracle.vtok_evict(st, vic, nv)
+    o, ofl, ofc, ost = oracle.vtok_reclaim(st2, 0.25, 4096, fl, free.size)
+    torch.cuda.synchronize()
+    _say(f"full size: stats {ost.tolist()}")
+    assert host(stats).tolist() == ost.tolist()
+    assert ost[0] == U and ost[1] == 0
+    for k, t in (("block_table", d.c.block_table), ("pos", d.c.pos), ("live", d.live),
+                 ("block_live", d.block_live)):
+        assert np.array_equal(host(t), o[k]), k
+    gfc = int(host(d.fc)[0])
+    assert gfc == ofc and np.array_equal(host(d.fl)[:gfc], ofl[:ofc])
+    # the pools: every destination block whole (the rows the copies wrote)
+    dest = np.setdiff1d(o["block_table"][o["block_table"] >= 0],
+                        st2["block_table"][st2["block_table"] >= 0])
+    kp, vp = host(d.c.k_pool), host(d.c.v_pool)
+    assert np.array_equal(kp[dest], o["k_pool"][dest]) and np.array_equal(vp[dest], o["v_pool"][dest])
+    assert np.array_equal(kp, o["k_pool"]) and np.array_equal(vp, o["v_pool"])
