@@ -5,7 +5,9 @@ eviction on one MI355X, on seeded synthetic inputs.
                     [--no-cpu-baseline]
 
 (--workload h2o_stream_870 times the H2O decode step instead: one
-kvev_h2o_step launch per decoded token of every sequence.)
+kvev_h2o_step launch per decoded token of every sequence.  --workload
+vtok_reclaim_64k times vToken's liveness marks and lazy reclamation of one
+64000-token layer.)
 
 A step is the whole eviction path for one layer's cache: scoring (SnapKV
 window sum + max-pool over the last W prompt queries), selection (budget,
@@ -95,6 +97,8 @@ def main():
     cfg = synth.CONFIGS[args.workload]
     if args.workload == "h2o_stream_870":
         return bench_h2o_stream(args, cfg)
+    if args.workload == "vtok_reclaim_64k":
+        return bench_vtok(args, cfg)
     if cfg.decode_steps:
         print(json.dumps({"error": f"{args.workload} is a decode schedule, not a one-shot pass"}))
         sys.exit(2)
@@ -468,6 +472,189 @@ def bench_h2o_stream(args, cfg):
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def _vtok_bytes(U, rows, nsrc, alloc_blocks, row_bytes):
+    """Algorithmic HBM bytes of one reclamation call.  Per moved row: K and V
+    read and written (4 x row_bytes), its position read, staged, read back and
+    written (16).  Per source block: its 16 liveness bytes read and written,
+    source and offset records written and read (16), block id read, rewritten
+    and pushed (12), live count written (4).  Per allocated block of a head:
+    block id and live count read by the plan (8)."""
+    return rows * (4 * row_bytes + 16) + nsrc * (32 + 16 + 12 + 4) + alloc_blocks * 8
+
+
+def bench_vtok(args, cfg):
+    """vToken on one 64000-token layer (B16, 8 KV heads, D128, bf16): a step
+    restores the layer's token table (block lists, positions, liveness, the
+    free list: device copies, about 50 MB), marks half of every head's tokens
+    dead (kvev_vtok_evict, the victims of a uniform random policy) and runs
+    one lazy reclamation whose source batch covers the head (kvev_vtok_reclaim,
+    theta_F = 0.25).  value = KV tokens covered per second (batch x heads x
+    context / step time)."""
+    import numpy as np
+    import torch
+
+    import kv_cache_eviction_qk_amd as K
+    import synth
+
+    B, Hkv, D = cfg.B, cfg.Hkv, cfg.D
+    U = B * Hkv
+    theta, max_sources = 0.25, 4096
+    steps, warm = args.steps, args.warmup
+    t0 = time.time()
+    spare = U * ((cfg.budget + 15) // 16 + 1)      # room for every head's destinations
+    case = synth.make_case(cfg, spare_blocks=spare)
+    vic, nv = synth.random_victims(case, cfg.budget, cfg.recent)
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    cache = K.Cache(dev(case["k_pool"]), dev(case["v_pool"]), dev(case["block_table"]),
+                    dev(case["seq_len"]), dev(case["pos"]))
+    ms = cache.max_slots
+    nblk = case["max_blocks"]
+    live0 = torch.zeros((B, Hkv, ms), dtype=torch.uint8, device="cuda")
+    live0[:, :, :cfg.L] = 1
+    bl0 = torch.zeros((B, Hkv, nblk), dtype=torch.int32, device="cuda")
+    bl0[:, :, :cfg.L // 16] = 16
+    used = np.zeros(case["num_blocks"], bool)
+    used[case["block_table"][case["block_table"] >= 0]] = True
+    free_ids = np.flatnonzero(~used).astype(np.int32)
+    fl0 = torch.full((case["num_blocks"],), -1, dtype=torch.int32, device="cuda")
+    fl0[:free_ids.size] = dev(free_ids)
+    fc0 = torch.tensor([free_ids.size], dtype=torch.int32, device="cuda")
+    bt0, pos0 = cache.block_table.clone(), cache.pos.clone()
+    live, bl = live0.clone(), bl0.clone()
+    fl, fc = fl0.clone(), fc0.clone()
+    vic_d, nv_d = dev(vic), dev(nv)
+    ws = K.new_vtok_workspace(cache, max_sources)
+    ews = K.new_vtok_evict_workspace(cache)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stats = torch.zeros(10, dtype=torch.int64, device="cuda")
+    evs = []
+
+    def step(timed):
+        for t, v in ((cache.block_table, bt0), (cache.pos, pos0), (live, live0), (bl, bl0),
+                     (fl, fl0), (fc, fc0)):
+            t.copy_(v)
+        K.vtok_evict(cache, live, bl, vic_d, nv_d, ews, status)
+        if timed:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+        K.vtok_reclaim(cache, live, bl, theta, max_sources, fl, fc, ws, stats=stats)
+        if timed:
+            b.record()
+            evs.append((a, b))
+
+    for _ in range(warm):
+        step(False)
+    torch.cuda.synchronize()
+    st = stats.cpu().numpy()
+    assert int(status.item()) == 0 and st[0] == U and st[1] == 0, st
+    w0 = time.perf_counter()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step(True)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = e0.elapsed_time(e1) / steps
+    ms_reclaim = sum(a.elapsed_time(b) for a, b in evs) / steps
+    if args.profile_steps:
+        log(f"profile run done: {ms_step:.4f} ms/step, reclaim {ms_reclaim:.4f} ms")
+        return
+    st = stats.cpu().numpy()
+    # the plan's sizes from the marks, on the host (accounting only), checked
+    # against the call's own statistics
+    nb_head = (cfg.L + 15) // 16
+    nsrc = rows = dests = 0
+    for u in range(U):
+        b, h = divmod(u, Hkv)
+        dead = np.bincount(vic[b, h, :nv[b, h]] // 16, minlength=nblk)[:nb_head]
+        cnt = 16 - dead
+        cand = np.flatnonzero(cnt[:nb_head - 1] < 16)[:max_sources]
+        t = int(cnt[cand].sum())
+        nsrc += cand.size
+        rows += t
+        dests += (t + 15) // 16
+    assert rows == int(st[4]) and nsrc - dests == int(st[3]), (rows, nsrc, dests, st)
+    row_bytes = D * (2 if cfg.dtype == "bf16" else 4)
+    call_bytes = _vtok_bytes(U, rows, nsrc, U * nb_head, row_bytes)
+    achieved = call_bytes / (ms_reclaim / 1e3) / 1e9
+    traffic = read_traffic(args.workload,
+                           os.path.join(ROOT, "kv_cache_eviction_qk_amd", "csrc", "vtoken.hip"),
+                           kernel="vtok_reclaim", sha_key="source_sha256_16")
+    cpu = None if args.no_cpu_baseline else cpu_baseline_vtok(cfg, theta, max_sources)
+    out = {
+        "metric": "vToken marks + lazy reclamation: KV tokens/sec covered (one 64000-token "
+                  "layer, half the tokens dead)",
+        "value": U * cfg.L / (ms_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic (seeded; uniform random victims, 16 recent protected)",
+        "config": {"workload": args.workload, "batch": B, "kv_heads": Hkv, "head_dim": D,
+                   "context": cfg.L, "victims_per_head": cfg.L - cfg.budget,
+                   "recent_window": cfg.recent, "theta_F": theta, "source_batch": max_sources,
+                   "block_size": 16},
+        "wall_s": wall,
+        "timing": "HIP events around the timed steps (table restore + marks + reclamation); "
+                  "the reclamation call alone between events of its own",
+        "reclaim_ms": ms_reclaim,
+        "blocks_freed": int(st[3]),
+        "rows_moved": int(st[4]),
+        "bytes_moved": int(st[5]),
+        "roofline": {"kernel": "kvev_vtok_reclaim (plan, admit, move, apply launches)",
+                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": call_bytes, "launch_ms": ms_reclaim},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_vtok(cfg, theta, max_sources):
+    """The oracle's marks and reclamation on the host (one thread), on a
+    bounded sample: a two-sequence slice (16 KV heads) of the same shape."""
+    import numpy as np
+
+    import oracle
+    import synth
+    sub = cfg.scaled(B=2)
+    U = sub.B * sub.Hkv
+    case = synth.make_case(sub, spare_blocks=U * ((sub.budget + 15) // 16 + 1))
+    vic, nv = synth.random_victims(case, sub.budget, sub.recent)
+    st = dict(case)
+    st["live"], st["block_live"] = oracle.vtok_liveness(case)
+    used = np.zeros(case["num_blocks"], bool)
+    used[case["block_table"][case["block_table"] >= 0]] = True
+    free_ids = np.flatnonzero(~used).astype(np.int32)
+    fl = np.full(case["num_blocks"], -1, np.int32)
+    fl[:free_ids.size] = free_ids
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        st2, _ = oracle.vtok_evict(st, vic, nv)
+        oracle.vtok_reclaim(st2, theta, max_sources, fl, free_ids.size)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt > 10.0 or reps >= 8:
+            break
+    return {"value": U * sub.L * reps / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} x marks + reclamation of {U} of {cfg.B * cfg.Hkv} KV heads "
+                      f"(a 2-sequence slice, {sub.L} tokens each); {dt:.1f} s"}
 
 
 def cpu_baseline_h2o(case, cfg, fill):

@@ -55,7 +55,7 @@ extern "C" {
 #endif
 
 #define KVEV_BLOCK_SIZE 16
-#define KVEV_ABI_VERSION 7
+#define KVEV_ABI_VERSION 8
 
 typedef enum {
   KVEV_OK = 0,
@@ -298,19 +298,28 @@ size_t kvev_h2o_workspace_bytes(const kvev_cache *cache, int32_t group, int32_t 
  * kvev_vtok_evict -- vToken's evict_token for a batch ([VTOK] section 3.2:
  * evicting a token only marks it dead in the token table; no KV memory moves
  * or is freed).  The token table of a head is its block list, pos, and
- * live: uint8 [batch][kv_heads][max_blocks*16] (1 live, 0 dead), with
+ * live: uint8 [batch][kv_heads][max_blocks*16] (nonzero live, 0 dead), with
  * block_live: int32 [batch][kv_heads][max_blocks] the live slots of each
  * logical block.  For every head u and i < n_victims[u], slot victims[u][i]
- * (int32 [batch][kv_heads][max_blocks*16], any order) is marked dead and its
- * block's count decremented.  A victim that is out of [0, seq_len), in a
- * block whose table entry is -1, or already dead (a repeat included) sets
- * *status (int32 on the device, written by the call: 0 or 1) and is skipped.
- * Device pointers; live must be 4-byte aligned.  Two kernels on `stream`.
- * Errors: KVEV_EINVAL for NULL pointers, a bad cache or a misaligned live.
+ * (int32 [batch][kv_heads][max_blocks*16], any order) is marked dead, and
+ * the live count of each block holding a victim is set to the number of its
+ * live slots afterwards.  A victim that is out of [0, seq_len), in a block
+ * whose table entry is -1, or already dead (a repeat within the call
+ * included), and a count n_victims[u] above max_blocks*16, set *status
+ * (int32 on the device, written by the call: 0 or 1); such victims are
+ * skipped.  Device pointers; live and the workspace 16-byte aligned; the
+ * workspace (kvev_vtok_evict_workspace_bytes, scratch only, no clearing
+ * needed) holds a claim word per slot.  Four kernels on `stream`, plain
+ * loads and stores (no atomics on the table).
+ * Errors: KVEV_EINVAL for NULL pointers, a bad cache or a misaligned live or
+ * workspace; KVEV_ENOSPACE for a missing or short workspace.
  */
 int kvev_vtok_evict(const kvev_cache *cache, uint8_t *live, int32_t *block_live,
                     const int32_t *victims, const int32_t *n_victims, int32_t *status,
-                    void *stream);
+                    void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes of kvev_vtok_evict (4 per slot); 0 for a bad cache. */
+size_t kvev_vtok_evict_workspace_bytes(const kvev_cache *cache);
 
 /*
  * kvev_vtok_reclaim -- vToken's lazy reclamation ([VTOK] section 3.3, stages
@@ -346,9 +355,10 @@ int kvev_vtok_evict(const kvev_cache *cache, uint8_t *live, int32_t *block_live,
  * [0, min(free_capacity, num_blocks)] -- nothing is admitted -- or a list
  * too small for the returned sources, whose excess is dropped)}.
  * Workspace: at least kvev_vtok_workspace_bytes(cache, max_sources) bytes
- * (scratch only).  live: 4-byte aligned.
- * Errors: KVEV_EINVAL for NULL pointers, a bad cache, theta_f outside
- * [0, 1) or max_sources outside [2, 4096]; KVEV_EUNSUPPORTED above 8192 KV
+ * (scratch only).  live, the cache's pos, score_or_null and the workspace:
+ * 16-byte aligned.
+ * Errors: KVEV_EINVAL for NULL pointers, a bad cache, a misaligned pointer,
+ * theta_f outside [0, 1) or max_sources outside [2, 4096]; KVEV_EUNSUPPORTED above 8192 KV
  * heads; KVEV_ENOSPACE when free_capacity < num_blocks or the workspace is
  * missing or short.
  */

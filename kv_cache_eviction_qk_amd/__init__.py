@@ -31,9 +31,10 @@ BLOCK_SIZE = 16
 # the functions include/kvev.h declares
 EXPORTS = ("kvev_score", "kvev_select", "kvev_compact", "kvev_evict", "kvev_measure",
            "kvev_h2o_step", "kvev_h2o_workspace_bytes", "kvev_vtok_evict",
-           "kvev_vtok_reclaim", "kvev_vtok_workspace_bytes", "kvev_window_attn",
+           "kvev_vtok_evict_workspace_bytes", "kvev_vtok_reclaim", "kvev_vtok_workspace_bytes",
+           "kvev_window_attn",
            "kvev_workspace_bytes", "kvev_strerror", "kvev_abi_version")
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 
 class KvevError(RuntimeError):
@@ -83,7 +84,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                 sz, P]
     L.kvev_h2o_workspace_bytes.argtypes = [P, i32, i32]
     L.kvev_h2o_workspace_bytes.restype = sz
-    L.kvev_vtok_evict.argtypes = [P, P, P, P, P, P, P]
+    L.kvev_vtok_evict.argtypes = [P, P, P, P, P, P, P, sz, P]
+    L.kvev_vtok_evict_workspace_bytes.argtypes = [P]
+    L.kvev_vtok_evict_workspace_bytes.restype = sz
     L.kvev_vtok_reclaim.argtypes = [P, P, P, P, ctypes.c_double, i32, P, P, i32, P, P, sz, P]
     L.kvev_vtok_workspace_bytes.argtypes = [P, i32]
     L.kvev_vtok_workspace_bytes.restype = sz
@@ -394,13 +397,22 @@ def h2o_step(cache: Cache, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Te
     return evicted
 
 
+def new_vtok_evict_workspace(cache: Cache) -> torch.Tensor:
+    """A workspace for kvev_vtok_evict on this cache shape (4 bytes a slot)."""
+    n = load_library().kvev_vtok_evict_workspace_bytes(ctypes.byref(cache.struct()))
+    if n == 0:
+        raise KvevError(EINVAL, "kvev_vtok_evict_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=cache.k_pool.device)
+
+
 def vtok_evict(cache: Cache, live: torch.Tensor, block_live: torch.Tensor,
-               victims: torch.Tensor, n_victims: torch.Tensor, status: Optional[torch.Tensor] = None,
-               stream=None) -> torch.Tensor:
+               victims: torch.Tensor, n_victims: torch.Tensor, workspace: torch.Tensor,
+               status: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """kvev_vtok_evict: mark the victim slots dead.  live uint8 [B, Hkv,
     max_slots], block_live int32 [B, Hkv, max_blocks] (both updated); victims
-    int32 [B, Hkv, max_slots], n_victims int32 [B, Hkv].  Returns status int32
-    [1] (1 when a victim was out of range or already dead)."""
+    int32 [B, Hkv, max_slots], n_victims int32 [B, Hkv]; workspace from
+    new_vtok_evict_workspace.  Returns status int32 [1] (1 when a victim was
+    out of range, already dead or repeated)."""
     L = load_library()
     c = cache.struct()
     B, Hkv = cache.batch, cache.kv_heads
@@ -408,11 +420,13 @@ def vtok_evict(cache: Cache, live: torch.Tensor, block_live: torch.Tensor,
     _need(block_live, "block_live", torch.int32, B * Hkv * cache.max_blocks)
     _need(victims, "victims", torch.int32, B * Hkv * cache.max_slots)
     _need(n_victims, "n_victims", torch.int32, B * Hkv)
+    _need(workspace, "workspace", torch.uint8)
     if status is None:
         status = torch.empty(1, dtype=torch.int32, device=live.device)
     _need(status, "status", torch.int32, 1)
     rc = L.kvev_vtok_evict(ctypes.byref(c), _ptr(live), _ptr(block_live), _ptr(victims),
-                           _ptr(n_victims), _ptr(status), _stream(stream))
+                           _ptr(n_victims), _ptr(status), _ptr(workspace), workspace.numel(),
+                           _stream(stream))
     _check(rc, "kvev_vtok_evict")
     return status
 

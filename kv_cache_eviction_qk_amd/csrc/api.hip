@@ -254,7 +254,7 @@ int kvev_h2o_step(const kvev_cache *cache, const void *q, const void *k_new, con
 
 // Workspace of kvev_vtok_reclaim (scratch only).
 struct VtokLayout {
-  size_t plan, src, srcoff, dst_off, push_off, dst_ids, tpos, tscore, misc, total;
+  size_t plan, src, srcoff, dstw, dst_off, push_off, tpos, tscore, misc, total;
 };
 
 VtokLayout vtok_layout(const kvev_cache *c, int32_t max_sources) {
@@ -264,15 +264,22 @@ VtokLayout vtok_layout(const kvev_cache *c, int32_t max_sources) {
   L.plan = off; off = a256(off + units * 8 * 4);
   L.src = off; off = a256(off + units * ms * 4);
   L.srcoff = off; off = a256(off + units * ms * 4);
+  L.dstw = off; off = a256(off + units * ms * 4);
   L.dst_off = off; off = a256(off + units * 4);
   L.push_off = off; off = a256(off + units * 4);
-  L.dst_ids = off; off = a256(off + (size_t)c->num_blocks * 4);
   L.tpos = off; off = a256(off + units * ms * KVEV_BLOCK_SIZE * 4);
   L.tscore = off; off = a256(off + units * ms * KVEV_BLOCK_SIZE * 4);
   L.misc = off; off = a256(off + 8 * 4);
   L.total = off;
   return L;
 }
+
+// Workspace of kvev_vtok_evict: a claim word per slot.
+size_t vtok_evict_ws(const kvev_cache *c) {
+  return a256((size_t)c->batch * c->kv_heads * c->max_blocks * KVEV_BLOCK_SIZE * 4);
+}
+
+bool misaligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
 
 kvev::VtokArgs vtok_args(const kvev_cache *cache, uint8_t *live, int32_t *block_live) {
   kvev::VtokArgs a{};
@@ -291,16 +298,23 @@ kvev::VtokArgs vtok_args(const kvev_cache *cache, uint8_t *live, int32_t *block_
   return a;
 }
 
+size_t kvev_vtok_evict_workspace_bytes(const kvev_cache *cache) {
+  return valid_cache(cache) ? vtok_evict_ws(cache) : 0;
+}
+
 int kvev_vtok_evict(const kvev_cache *cache, uint8_t *live, int32_t *block_live,
                     const int32_t *victims, const int32_t *n_victims, int32_t *status,
-                    void *stream) {
+                    void *workspace, size_t ws_bytes, void *stream) {
   if (!valid_cache(cache) || !live || !block_live || !victims || !n_victims || !status)
     return KVEV_EINVAL;
-  if (reinterpret_cast<uintptr_t>(live) & 3) return KVEV_EINVAL;
+  if (misaligned16(live)) return KVEV_EINVAL;
+  if (!workspace || ws_bytes < vtok_evict_ws(cache)) return KVEV_ENOSPACE;
+  if (misaligned16(workspace)) return KVEV_EINVAL;
   kvev::VtokArgs a = vtok_args(cache, live, block_live);
   a.victims = victims;
   a.n_victims = n_victims;
   a.status = status;
+  a.claim = static_cast<int32_t *>(workspace);
   return map_err(kvev::launch_vtok_evict(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -315,13 +329,15 @@ int kvev_vtok_reclaim(const kvev_cache *cache, uint8_t *live, int32_t *block_liv
                       int64_t *stats, void *workspace, size_t ws_bytes, void *stream) {
   if (!valid_cache(cache) || !live || !block_live || !free_list || !free_count || !stats)
     return KVEV_EINVAL;
-  if (reinterpret_cast<uintptr_t>(live) & 3) return KVEV_EINVAL;
+  if (misaligned16(live) || misaligned16(cache->pos) || misaligned16(score_or_null))
+    return KVEV_EINVAL;
   if (!(theta_f >= 0.0 && theta_f < 1.0)) return KVEV_EINVAL;  // NaN refused too
   if (max_sources < 2 || max_sources > kvev::kVtokMaxSources) return KVEV_EINVAL;
   if ((int64_t)cache->batch * cache->kv_heads > kvev::kVtokMaxUnits) return KVEV_EUNSUPPORTED;
   if (free_capacity < cache->num_blocks) return KVEV_ENOSPACE;
   const VtokLayout L = vtok_layout(cache, max_sources);
   if (!workspace || ws_bytes < L.total) return KVEV_ENOSPACE;
+  if (misaligned16(workspace)) return KVEV_EINVAL;
   uint8_t *ws = static_cast<uint8_t *>(workspace);
   kvev::VtokArgs a = vtok_args(cache, live, block_live);
   a.score = score_or_null;
@@ -334,9 +350,9 @@ int kvev_vtok_reclaim(const kvev_cache *cache, uint8_t *live, int32_t *block_liv
   a.plan = reinterpret_cast<int32_t *>(ws + L.plan);
   a.src = reinterpret_cast<int32_t *>(ws + L.src);
   a.srcoff = reinterpret_cast<int32_t *>(ws + L.srcoff);
+  a.dstw = reinterpret_cast<int32_t *>(ws + L.dstw);
   a.dst_off = reinterpret_cast<int32_t *>(ws + L.dst_off);
   a.push_off = reinterpret_cast<int32_t *>(ws + L.push_off);
-  a.dst_ids = reinterpret_cast<int32_t *>(ws + L.dst_ids);
   a.tpos = reinterpret_cast<int32_t *>(ws + L.tpos);
   a.tscore = reinterpret_cast<float *>(ws + L.tscore);
   a.misc = reinterpret_cast<int32_t *>(ws + L.misc);

@@ -117,10 +117,12 @@ struct VtokArgs {
   int32_t *status;                     // marks: bit 0, a victim that was not live
   int32_t *free_list, *free_count;
   int64_t *stats;                      // reclamation [10]
-  // workspace: plan records [units][8], sources and their live offsets
-  // [units][max_sources], destination / push offsets [units], destination ids
-  // [num_blocks], staged positions and scores [units][max_sources*16], misc [8]
-  int32_t *plan, *src, *srcoff, *dst_off, *push_off, *dst_ids, *tpos, *misc;
+  // workspace: plan records [units][8], sources, their live offsets and the
+  // destination ids of the first D source positions [units][max_sources],
+  // destination / push offsets [units], staged positions and scores
+  // [units][max_sources*16], misc [8]; for the marks, a claim word per slot
+  // [units][max_slots]
+  int32_t *plan, *src, *srcoff, *dstw, *dst_off, *push_off, *tpos, *misc, *claim;
   float *tscore;
   int32_t units, max_blocks, max_slots, num_blocks, row_bytes, max_sources, free_capacity;
   double theta_f;

@@ -36,7 +36,8 @@
 namespace kvev {
 
 namespace {
-constexpr int kPlanThreads = 256;
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanPer = 4;   // logical blocks per plan thread and pass
 constexpr int kAdmitThreads = 1024;
 constexpr int kMoveWaves = 4;  // source blocks per move workgroup (a wave each)
 constexpr size_t kNoRow = ~(size_t)0;
@@ -63,29 +64,67 @@ __device__ __forceinline__ int wg_excl_scan(int v, int *wave_tot) {
 
 __global__ void vtok_zero_kernel(int32_t *status) { *status = 0; }
 
-__global__ __launch_bounds__(256) void vtok_evict_kernel(const VtokArgs P) {
-  const int u = blockIdx.y;
-  const int i = blockIdx.x * 256 + threadIdx.x;
+// The checks every pass makes of victim i of head u: false for a victim out
+// of the head's length or in a block without an id.
+__device__ __forceinline__ bool victim_slot(const VtokArgs &P, int u, int i, int &v) {
+  v = P.victims[(size_t)u * P.max_slots + i];
+  const int n = P.seq_len[u];
+  return v >= 0 && v < n && v < P.max_slots &&
+         P.block_table[(size_t)u * P.max_blocks + v / kBlock] >= 0;
+}
+
+// Marks take three passes of plain loads and stores (no atomics on the table,
+// whose victims crowd into the same words and blocks):
+//   claim: a victim that is invalid or already dead sets the status; a live
+//          one writes its index into its slot's claim word;
+//   clear: the victim whose index the claim word holds clears the byte;
+//          another victim of the same slot is a repeat and sets the status;
+//   count: the live count of every block holding a victim is recounted from
+//          its 16 bytes (the same value from every such victim).
+__global__ __launch_bounds__(256) void vtok_claim_kernel(const VtokArgs P) {
+  const int u = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
   const int m = P.n_victims[u];
   if (i == 0 && m > P.max_slots) atomicOr(P.status, 1);  // the list holds max_slots entries
   if (i >= m || i >= P.max_slots) return;
-  const int n = P.seq_len[u];
-  const int v = P.victims[(size_t)u * P.max_slots + i];
-  if (v < 0 || v >= n || v >= P.max_slots || P.block_table[(size_t)u * P.max_blocks + v / kBlock] < 0) {
+  int v;
+  const size_t row = (size_t)u * P.max_slots;
+  if (!victim_slot(P, u, i, v) || P.live[row + v] == 0) {
     atomicOr(P.status, 1);
     return;
   }
-  // clear the byte with one atomic on its word: of two equal victims, one
-  // sees it set
+  P.claim[row + v] = i;
+}
+
+__global__ __launch_bounds__(256) void vtok_clear_kernel(const VtokArgs P) {
+  const int u = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= P.n_victims[u] || i >= P.max_slots) return;
+  int v;
+  if (!victim_slot(P, u, i, v)) return;
   const size_t at = (size_t)u * P.max_slots + v;
-  uint32_t *word = reinterpret_cast<uint32_t *>(P.live + (at & ~(size_t)3));
-  const int shift = (int)(at & 3) * 8;
-  const uint32_t old = atomicAnd(word, ~(0xffu << shift));
-  if (((old >> shift) & 0xffu) == 0) {
+  // a victim that was dead before the call was flagged by the claim pass and
+  // wrote no claim: whatever the word holds, clearing its byte changes nothing
+  if (P.claim[at] == i) {
+    P.live[at] = 0;
+  } else {
     atomicOr(P.status, 1);
-    return;
   }
-  atomicSub(P.block_live + (size_t)u * P.max_blocks + v / kBlock, 1);
+}
+
+__global__ __launch_bounds__(256) void vtok_count_kernel(const VtokArgs P) {
+  const int u = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= P.n_victims[u] || i >= P.max_slots) return;
+  int v;
+  if (!victim_slot(P, u, i, v)) return;
+  const int lb = v / kBlock;
+  const uint4 b = ld16(P.live + (size_t)u * P.max_slots + (size_t)lb * kBlock);
+  int c = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t x = w == 0 ? b.x : w == 1 ? b.y : w == 2 ? b.z : b.w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) c += ((x >> (8 * q)) & 0xffu) ? 1 : 0;
+  }
+  P.block_live[(size_t)u * P.max_blocks + lb] = c;
 }
 
 hipError_t launch_vtok_evict(const VtokArgs &a, hipStream_t s) {
@@ -93,18 +132,24 @@ hipError_t launch_vtok_evict(const VtokArgs &a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.units == 0) return hipSuccess;
-  hipLaunchKernelGGL(vtok_evict_kernel, dim3((unsigned)((a.max_slots + 255) / 256), (unsigned)a.units),
-                     dim3(256), 0, s, a);
+  const dim3 grid((unsigned)((a.max_slots + 255) / 256), (unsigned)a.units);
+  hipLaunchKernelGGL(vtok_claim_kernel, grid, dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(vtok_clear_kernel, grid, dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(vtok_count_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 // ----------------------------------------------------------- reclamation
 
-// plan record per head: {kind, nsrc, T, D, alloc, live, ...}; kind 0 skip
-// (bad head), 1 left as it is, 2 wants a plan
+// plan record per head: {kind, nsrc, T, D, alloc, live, status}; kind 0 skip
+// (bad head), 1 left as it is, 2 wants a plan.  Each thread takes kPlanPer
+// consecutive logical blocks per pass; one scan gives every thread the rank
+// and token offset of its first candidate.
 __global__ __launch_bounds__(kPlanThreads) void vtok_plan_kernel(const VtokArgs P) {
   __shared__ int wave_tot[kPlanThreads / kWave];
-  __shared__ int s_alloc, s_live, s_bad, s_k, s_T;
+  __shared__ int s_alloc, s_live, s_bad, s_tot;
   const int u = blockIdx.x, tid = threadIdx.x;
   const int n = P.seq_len[u];
   int32_t *plan = P.plan + (size_t)u * 8;
@@ -122,57 +167,65 @@ __global__ __launch_bounds__(kPlanThreads) void vtok_plan_kernel(const VtokArgs 
     s_alloc = 0;
     s_live = 0;
     s_bad = 0;
-    s_k = 0;
-    s_T = 0;
   }
-  __syncthreads();
-  // allocated blocks, live tokens, and the ordered selection of sources: the
-  // first max_sources allocated blocks that are not full, the tail excluded
+  // the ordered selection of sources: the first max_sources allocated blocks
+  // that are not full, the tail excluded
   int32_t *src = P.src + (size_t)u * P.max_sources;
   int32_t *srcoff = P.srcoff + (size_t)u * P.max_sources;
   int k_base = 0, t_base = 0;
   int my_alloc = 0, my_live = 0, my_bad = 0;
-  for (int lb0 = 0; lb0 < nb; lb0 += kPlanThreads) {
-    const int lb = lb0 + tid;
-    const int e = lb < nb ? bt[lb] : -1;
-    const int c = lb < nb ? bl[lb] : 0;
-    if (e >= 0) {
-      ++my_alloc;
-      my_live += c;
-      if (e >= P.num_blocks || c < 0 || c > kBlock) my_bad = 1;
+  for (int lb0 = 0; lb0 < nb; lb0 += kPlanThreads * kPlanPer) {
+    const int first = lb0 + tid * kPlanPer;
+    int e[kPlanPer], c[kPlanPer];
+    int nc = 0, nt = 0;
+#pragma unroll
+    for (int q = 0; q < kPlanPer; ++q) {
+      const int lb = first + q;
+      e[q] = lb < nb ? bt[lb] : -1;
+      c[q] = lb < nb ? bl[lb] : 0;
     }
-    const int cand = (lb < nb - 1 && e >= 0 && c < kBlock) ? 1 : 0;
-    const int rank = k_base + wg_excl_scan(cand, wave_tot);
-    const int toff = t_base + wg_excl_scan(cand ? c : 0, wave_tot);
-    if (cand && rank < P.max_sources) {
-      src[rank] = lb;
-      srcoff[rank] = toff;
+#pragma unroll
+    for (int q = 0; q < kPlanPer; ++q) {
+      const int lb = first + q;
+      if (e[q] >= 0) {
+        ++my_alloc;
+        my_live += c[q];
+        if (e[q] >= P.num_blocks || c[q] < 0 || c[q] > kBlock) my_bad = 1;
+      }
+      const bool cand = lb < nb - 1 && e[q] >= 0 && c[q] < kBlock;
+      nc += cand ? 1 : 0;
+      nt += cand ? max(c[q], 0) : 0;
     }
-    // the chunk's totals (the last thread's inclusive values)
-    if (tid == kPlanThreads - 1) {
-      s_k = rank + cand;
-      s_T = toff + (cand ? c : 0);
+    // candidates (< 2^13 per pass) and their tokens (< 2^16) in one scan
+    const int packed = wg_excl_scan((nc << 16) | nt, wave_tot);
+    int rank = k_base + (packed >> 16), toff = t_base + (packed & 0xffff);
+#pragma unroll
+    for (int q = 0; q < kPlanPer; ++q) {
+      const int lb = first + q;
+      const bool cand = lb < nb - 1 && e[q] >= 0 && c[q] < kBlock;
+      if (cand) {
+        if (rank < P.max_sources) {
+          src[rank] = lb;
+          srcoff[rank] = toff;
+        }
+        ++rank;
+        toff += max(c[q], 0);
+      }
     }
+    if (tid == kPlanThreads - 1) s_tot = packed + ((nc << 16) | nt);  // the pass's totals
     __syncthreads();
-    k_base = s_k;
-    t_base = s_T;
+    k_base += s_tot >> 16;
+    t_base += s_tot & 0xffff;
     __syncthreads();
   }
-  // T counts only the first max_sources candidates
   if (my_alloc) atomicAdd(&s_alloc, my_alloc);
   if (my_live) atomicAdd(&s_live, my_live);
   if (my_bad) atomicOr(&s_bad, 1);
   __syncthreads();
   if (tid != 0) return;
   const int k = min(k_base, P.max_sources);
-  int T = 0;
-  if (k_base > P.max_sources) {
-    // the live tokens of the first max_sources candidates: the offset of the
-    // next one, or (all of them) the chunk totals
-    T = srcoff[k - 1] + bl[src[k - 1]];
-  } else {
-    T = t_base;
-  }
+  // T counts the first max_sources candidates only
+  const int T = k_base > P.max_sources ? srcoff[k - 1] + bl[src[k - 1]] : t_base;
   const int D = (T + kBlock - 1) / kBlock;
   const int alloc = s_alloc, live = s_live;
   plan[4] = alloc;
@@ -244,8 +297,6 @@ __global__ __launch_bounds__(kAdmitThreads) void vtok_admit_kernel(const VtokArg
   }
   __syncthreads();
   const int taken = s_taken;
-  // the destination ids, before the pushes overwrite the list's top
-  for (int i = tid; i < taken; i += kAdmitThreads) P.dst_ids[i] = P.free_list[fc - 1 - i];
   // push offsets and statistics, heads in order
   long long st[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
   int status = fc_ok ? 0 : 8, pbase = 0;
@@ -319,33 +370,36 @@ __global__ __launch_bounds__(kAdmitThreads) void vtok_admit_kernel(const VtokArg
 }
 
 // A wave per source block: its live rows (K and V) go to consecutive rows of
-// the destinations; positions and scores are staged by their place among the
-// moved tokens.
+// the destinations, destination d of a head being free_list[top - 1 - off - d]
+// (nothing writes the list until the apply step); positions and scores are
+// staged by their place among the moved tokens, and the wave of source
+// position j < D records that position's destination id.
 __global__ __launch_bounds__(kMoveWaves * kWave) void vtok_move_kernel(const VtokArgs P) {
   const int u = blockIdx.y;
   const int off = P.dst_off[u];
   if (off < 0) return;  // not reclaimed
-  const int k = P.plan[(size_t)u * 8 + 1];
+  const int k = P.plan[(size_t)u * 8 + 1], T = P.plan[(size_t)u * 8 + 2];
+  const int D = P.plan[(size_t)u * 8 + 3];
   const int l = lane_id(), pieces = P.row_bytes / 16;
   const size_t urow = (size_t)u * P.max_slots;
   const size_t tbase = (size_t)u * P.max_sources * kBlock;
+  const int32_t *dst = P.free_list + (P.misc[0] - 1 - off);  // dst[-d]: destination d
   for (int j = blockIdx.x * kMoveWaves + (int)(threadIdx.x / kWave); j < k;
        j += (int)gridDim.x * kMoveWaves) {
     const int lb = P.src[(size_t)u * P.max_sources + j];
     const int i0 = P.srcoff[(size_t)u * P.max_sources + j];  // first moved index of this block
     const int from_blk = P.block_table[(size_t)u * P.max_blocks + lb];
+    if (l == 0 && j < D) P.dstw[(size_t)u * P.max_sources + j] = dst[-j];
     const bool mine = l < kBlock && P.live[urow + (size_t)lb * kBlock + l] != 0;
     const uint64_t mask = __ballot(mine);
     const int c = __popcll(mask);
     const int rank = __popcll(mask & ((1ull << l) - 1));
-    const int T = P.plan[(size_t)u * 8 + 2];
     if (mine && i0 + rank < T) {  // (always, when the live counts match the marks)
       P.tpos[tbase + i0 + rank] = P.pos[urow + (size_t)lb * kBlock + l];
       if (P.score) P.tscore[tbase + i0 + rank] = P.score[urow + (size_t)lb * kBlock + l];
     }
     // lane r < c learns the offset of the r-th live slot
-    const int o_of_rank =
-        __builtin_amdgcn_ds_permute((mine ? rank : (l | 32)) * 4, l);
+    const int o_of_rank = __builtin_amdgcn_ds_permute((mine ? rank : (l | 32)) * 4, l);
     const int n16 = c * pieces;  // 16-byte pieces per pool
     for (int t0 = 0; t0 < 2 * n16; t0 += 4 * kWave) {
       uint4 v[4];
@@ -362,21 +416,21 @@ __global__ __launch_bounds__(kMoveWaves * kWave) void vtok_move_kernel(const Vto
         to[q] = kNoRow;
         if (t < 2 * n16 && i0 + r < T) {
           const int i = i0 + r;
-          const int to_blk = P.dst_ids[off + i / kBlock];
+          const int to_blk = dst[-(i / kBlock)];
           to[q] = (((size_t)to_blk * kBlock + i % kBlock) * P.row_bytes) + (size_t)p * 16;
           v[q] = ld16(pool[q] + ((size_t)from_blk * kBlock + o) * P.row_bytes + (size_t)p * 16);
         }
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (t0 + q * kWave + l < 2 * n16 && to[q] != kNoRow) st16(pool[q] + to[q], v[q]);
+        if (to[q] != kNoRow) st16_nt(pool[q] + to[q], v[q]);
     }
   }
 }
 
 // The per-slot table and the block list of the source positions; the sources
 // go to the free list.  Runs after every copy, so no slot is read after it is
-// rewritten.
+// rewritten.  A thread takes four consecutive slots of one source position.
 __global__ __launch_bounds__(256) void vtok_apply_kernel(const VtokArgs P) {
   const int u = blockIdx.y;
   const int off = P.dst_off[u];
@@ -388,20 +442,31 @@ __global__ __launch_bounds__(256) void vtok_apply_kernel(const VtokArgs P) {
   int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
   const int32_t *src = P.src + (size_t)u * P.max_sources;
   const int base = P.misc[0] - P.misc[1] + P.push_off[u];  // where this head's sources go
-  for (int x = blockIdx.x * 256 + (int)threadIdx.x; x < k * kBlock; x += (int)gridDim.x * 256) {
-    const int j = x / kBlock, o = x % kBlock;
+  for (int x = blockIdx.x * 256 + (int)threadIdx.x; x < k * (kBlock / 4);
+       x += (int)gridDim.x * 256) {
+    const int j = x / (kBlock / 4), o4 = (x % (kBlock / 4)) * 4;
     const int lb = src[j];
     // the first D source positions take the moved tokens in order
     const int cnt = j < D ? min(kBlock, T - kBlock * j) : 0;
-    const size_t s = urow + (size_t)lb * kBlock + o;
-    P.live[s] = o < cnt ? 1 : 0;
-    if (o < cnt) {
-      P.pos[s] = P.tpos[tbase + (size_t)kBlock * j + o];
-      if (P.score) P.score[s] = P.tscore[tbase + (size_t)kBlock * j + o];
+    const size_t s = urow + (size_t)lb * kBlock + o4;
+    uint32_t lw = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lw |= (o4 + q < cnt ? 1u : 0u) << (8 * q);
+    *reinterpret_cast<uint32_t *>(P.live + s) = lw;
+    const size_t t = tbase + (size_t)kBlock * j + o4;
+    if (o4 + 4 <= cnt) {
+      *reinterpret_cast<int4 *>(P.pos + s) = *reinterpret_cast<const int4 *>(P.tpos + t);
+      if (P.score)
+        *reinterpret_cast<float4 *>(P.score + s) = *reinterpret_cast<const float4 *>(P.tscore + t);
+    } else {
+      for (int q = 0; q < 4 && o4 + q < cnt; ++q) {
+        P.pos[s + q] = P.tpos[t + q];
+        if (P.score) P.score[s + q] = P.tscore[t + q];
+      }
     }
-    if (o == 0) {
+    if (o4 == 0) {
       if (base + j < P.free_capacity) P.free_list[base + j] = bt[lb];
-      bt[lb] = j < D ? P.dst_ids[off + j] : -1;
+      bt[lb] = j < D ? P.dstw[(size_t)u * P.max_sources + j] : -1;
       P.block_live[(size_t)u * P.max_blocks + lb] = cnt;
     }
   }
@@ -429,7 +494,7 @@ hipError_t launch_vtok_reclaim(const VtokArgs &a, hipStream_t s) {
                      s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned apply_x = (unsigned)std::min((a.max_sources * kBlock + 255) / 256, 64);
+  const unsigned apply_x = (unsigned)std::min((a.max_sources * (kBlock / 4) + 255) / 256, 64);
   hipLaunchKernelGGL(vtok_apply_kernel, dim3(apply_x, (unsigned)a.units), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -205,6 +205,12 @@ CONFIGS = {
     "h2o_stream_870": Config("h2o_stream_870", B=8, Hkv=8, G=4, D=128, L=806, W=1, dtype="bf16",
                              recipe="heavy_hitters", flags=("sum",), decode_steps=256,
                              budget=870, recent=435, plant_frac=0.02, seed=1006),
+    # vToken lazy reclamation on one layer of the block-aware shape: half of
+    # every head's 64000 tokens marked dead by a uniform random policy (the 16
+    # most recent protected), then one reclamation over each head's blocks.
+    "vtok_reclaim_64k": Config("vtok_reclaim_64k", B=16, Hkv=8, G=8, D=128, L=64000, W=16,
+                               dtype="bf16", recipe="iid", flags=("sum",), budget=32000,
+                               recent=16, seed=1007),
 }
 
 

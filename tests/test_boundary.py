@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
     assert set(names) == set(K.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvev_abi_version() == K.ABI_VERSION == 7
+    assert L.kvev_abi_version() == K.ABI_VERSION == 8
     for code in (0, -1, -2, -3, -4):
         assert K.strerror(code)
 
@@ -282,17 +282,24 @@ def test_vtok_refusals():
     host, before a launch."""
     L = K.load_library()
 
-    def evict(c=None, ptrs=None):
+    def evict(c=None, ptrs=None, ws_bytes=1 << 30):
         c = cache(max_blocks=8) if c is None else c
-        p = dict(live=FAKE, bl=FAKE, vic=FAKE, nv=FAKE, st=FAKE)
+        p = dict(live=FAKE, bl=FAKE, vic=FAKE, nv=FAKE, st=FAKE, ws=FAKE)
         p.update(ptrs or {})
         return L.kvev_vtok_evict(ctypes.byref(c), p["live"], p["bl"], p["vic"], p["nv"], p["st"],
-                                 None)
+                                 p["ws"], ws_bytes, None)
 
     for name in ("live", "bl", "vic", "nv", "st"):
         assert evict(ptrs={name: None}) == K.EINVAL, name
-    assert evict(ptrs={"live": FAKE + 1}) == K.EINVAL      # live must be 4-byte aligned
+    assert evict(ptrs={"live": FAKE + 4}) == K.EINVAL      # live must be 16-byte aligned
+    assert evict(ptrs={"ws": FAKE + 8}) == K.EINVAL
     assert evict(c=cache(head_dim=96)) == K.EINVAL
+    c8 = cache(max_blocks=8)
+    need_e = L.kvev_vtok_evict_workspace_bytes(ctypes.byref(c8))
+    assert need_e >= 2 * 2 * 128 * 4                       # a claim word per slot
+    assert evict(ptrs={"ws": None}) == K.ENOSPACE
+    assert evict(ws_bytes=need_e - 1) == K.ENOSPACE
+    assert L.kvev_vtok_evict_workspace_bytes(None) == 0
 
     def reclaim(c=None, theta=0.25, max_sources=8, cap=None, ptrs=None, ws_bytes=1 << 30):
         c = cache(max_blocks=8) if c is None else c
@@ -304,7 +311,9 @@ def test_vtok_refusals():
 
     for name in ("live", "bl", "fl", "fc", "st"):
         assert reclaim(ptrs={name: None}) == K.EINVAL, name
-    assert reclaim(ptrs={"live": FAKE + 2}) == K.EINVAL
+    assert reclaim(ptrs={"live": FAKE + 4}) == K.EINVAL
+    assert reclaim(ptrs={"ws": FAKE + 8}) == K.EINVAL
+    assert reclaim(c=cache(pos=FAKE + 4)) == K.EINVAL
     for theta in (-0.1, 1.0, float("nan"), float("inf")):
         assert reclaim(theta=theta) == K.EINVAL, theta
     assert reclaim(max_sources=1) == K.EINVAL

@@ -114,7 +114,9 @@ class Dev:
                               stream=stream)
 
     def evict(self, vic, nv):
-        return K.vtok_evict(self.c, self.live, self.block_live, dev(vic), dev(nv))
+        if getattr(self, "ews", None) is None:
+            self.ews = K.new_vtok_evict_workspace(self.c)
+        return K.vtok_evict(self.c, self.live, self.block_live, dev(vic), dev(nv), self.ews)
 
     def state(self, like):
         out = dict(like)
