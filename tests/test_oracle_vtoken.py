@@ -203,3 +203,26 @@ def test_same_order_as_eager_compaction():
         ref.append((int(eager["pos"][0, 0, s]), eager["k_pool"][blk, s % 16].tobytes(),
                     eager["v_pool"][blk, s % 16].tobytes()))
     assert lazy == ref
+
+
+def test_inconsistent_heads_are_skipped():
+    """A head whose table holds a block id past the pool or a live count
+    outside [0, 16] is skipped with a status bit and left as it is; a victim
+    count above the list's capacity is flagged and clamped."""
+    st, fl, fc = _state([[3, 3, 3, 1], [4, 4, 4, 1], [2, 2, 2, 1]], spare=10)
+    st["block_live"][0, 1, 1] = 17
+    new, _, _, stats = oracle.vtok_reclaim(st, 0.0, 8, fl, fc)
+    assert stats[9] == 4 and stats[0] == 2
+    assert np.array_equal(new["block_table"][0, 1], st["block_table"][0, 1])
+    st["block_live"][0, 1, 1] = 4
+    st["block_table"][0, 2, 0] = st["num_blocks"] + 1
+    new, _, _, stats = oracle.vtok_reclaim(st, 0.0, 8, fl, fc)
+    assert stats[9] == 4 and stats[0] == 2 and stats[7] == 8   # the skipped head is not counted
+    st["seq_len"][0, 0] = st["max_blocks"] * 16 + 1
+    _, _, _, stats = oracle.vtok_reclaim(st, 0.0, 8, fl, fc)
+    assert stats[9] == 6 and stats[0] == 1
+    st2, _, _ = _state([[16, 16]])
+    vic = np.zeros((1, 1, 32), np.int32)
+    vic[0, 0] = np.arange(32)
+    new, status = oracle.vtok_evict(st2, vic, np.array([[40]], np.int32))
+    assert status == 1 and new["live"][0, 0].sum() == 0 and new["block_live"][0, 0].tolist() == [0, 0]
