@@ -81,7 +81,7 @@ def read_traffic(workload, kernel_src, kernel="score", sha_key="score_source_sha
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
     import numpy as np
     import torch
