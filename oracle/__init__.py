@@ -69,10 +69,15 @@ def lib():
         L.orc_h2o_step.argtypes = [P, P, i32, i32, P, P, P, P, i32, i32, i32, i32, i32, P, P, P,
                                    P, ctypes.c_double, i32, i32, P, P, P, P, P]
         L.orc_vtok_evict.argtypes = [P, P, P, P, i32, i32, P, P, P]
+        L.orc_fmix64.argtypes = [ctypes.c_uint64]
+        L.orc_fmix64.restype = ctypes.c_uint64
+        L.orc_vtok_digest.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, P]
+        L.orc_vtok_check.argtypes = [P, P, P, i32, i32, i32, P, i32, P]
         L.orc_vtok_reclaim.argtypes = [P, P, i32, i32, P, P, P, P, P, P, i32, i32, i32,
                                        ctypes.c_double, i32, P, P, i32, P]
         for f in (L.orc_lse_a, L.orc_score, L.orc_select, L.orc_compact, L.orc_measure,
-                  L.orc_h2o_step, L.orc_vtok_evict, L.orc_vtok_reclaim):
+                  L.orc_h2o_step, L.orc_vtok_evict, L.orc_vtok_reclaim, L.orc_vtok_digest,
+                  L.orc_vtok_check):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -288,3 +293,39 @@ def vtok_reclaim(state: dict, theta_f: float, max_sources: int, free_list: np.nd
         raise ValueError(f"oracle vtok_reclaim refused the arguments (rc={rc})")
     return new, fl, int(fc[0]), stats
 
+
+
+def fmix64(k: int) -> int:
+    """MurmurHash3's 64-bit finalizer, as the oracle's C code computes it."""
+    return int(lib().orc_fmix64(k & 0xFFFFFFFFFFFFFFFF))
+
+
+def vtok_digest(state: dict) -> np.ndarray:
+    """Per-head order-independent digest of the live tokens (I1's online
+    check): uint64 [B, Hkv]."""
+    U = state["B"] * state["Hkv"]
+    out = np.zeros((state["B"], state["Hkv"]), np.uint64)
+    row_bytes = state["D"] * (2 if state["dtype"] == "bf16" else 4)
+    rc = lib().orc_vtok_digest(_p(np.ascontiguousarray(state["k_pool"])),
+                               _p(np.ascontiguousarray(state["v_pool"])), row_bytes,
+                               _p(np.ascontiguousarray(state["block_table"], dtype=np.int32)),
+                               _p(np.ascontiguousarray(state["seq_len"], dtype=np.int32)),
+                               _p(np.ascontiguousarray(state["pos"], dtype=np.int32)),
+                               _p(np.ascontiguousarray(state["live"], dtype=np.uint8)), U,
+                               state["max_blocks"], state["num_blocks"], _p(out))
+    assert rc == 0
+    return out
+
+
+def vtok_check(state: dict, free_list: np.ndarray, free_count: int) -> np.ndarray:
+    """I2's online check: int64 [4] = {blocks held more than once, blocks held
+    by nobody, references out of range, live-count mismatches}."""
+    out = np.zeros(4, np.int64)
+    rc = lib().orc_vtok_check(_p(np.ascontiguousarray(state["block_table"], dtype=np.int32)),
+                              _p(np.ascontiguousarray(state["live"], dtype=np.uint8)),
+                              _p(np.ascontiguousarray(state["block_live"], dtype=np.int32)),
+                              state["B"] * state["Hkv"], state["max_blocks"], state["num_blocks"],
+                              _p(np.ascontiguousarray(free_list, dtype=np.int32)), int(free_count),
+                              _p(out))
+    assert rc == 0
+    return out

@@ -753,3 +753,89 @@ int orc_vtok_reclaim(void *k_pool, void *v_pool, int32_t elem_bytes, int32_t hea
   return 0;
 }
 
+
+
+/* ---- online checks of I1 and I2 ([VTOK] section 3.5) ---- */
+
+/* MurmurHash3's 64-bit finalizer (Appleby): xor-shift, multiply, twice. */
+uint64_t orc_fmix64(uint64_t k) {
+  k ^= k >> 33;
+  k *= 0xff51afd7ed558ccdULL;
+  k ^= k >> 33;
+  k *= 0xc4ceb9fe1a85ec53ULL;
+  k ^= k >> 33;
+  return k;
+}
+
+static uint64_t row_word(const void *pool, int64_t row, int32_t row_bytes, int64_t i) {
+  uint64_t w;
+  memcpy(&w, (const char *)pool + row * row_bytes + i * 8, 8);
+  return w;
+}
+
+int orc_vtok_digest(const void *k_pool, const void *v_pool, int32_t row_bytes,
+                    const int32_t *block_table, const int32_t *seq_len, const int32_t *pos,
+                    const uint8_t *live, int32_t units, int32_t max_blocks, int32_t num_blocks,
+                    uint64_t *digest) {
+  if (!k_pool || !v_pool || !block_table || !seq_len || !pos || !live || !digest ||
+      row_bytes <= 0 || row_bytes % 8)
+    return -1;
+  const uint64_t G = 0x9E3779B97F4A7C15ULL;
+  const int64_t max_slots = (int64_t)max_blocks * 16, nw = row_bytes / 8;
+  for (int64_t u = 0; u < units; ++u) {
+    int64_t n = seq_len[u];
+    if (n < 0) n = 0;
+    if (n > max_slots) n = max_slots;
+    uint64_t d = 0;
+    for (int64_t s = 0; s < n; ++s) {
+      const int64_t blk = block_table[u * max_blocks + s / 16];
+      if (blk < 0 || blk >= num_blocks || !live[u * max_slots + s]) continue;
+      const int64_t row = blk * 16 + s % 16;
+      uint64_t t = orc_fmix64((uint64_t)(uint32_t)pos[u * max_slots + s] ^ G);
+      for (int64_t i = 0; i < nw; ++i) {
+        t += orc_fmix64(row_word(k_pool, row, row_bytes, i) ^ ((uint64_t)(2 * i + 1) * G));
+        t += orc_fmix64(row_word(v_pool, row, row_bytes, i) ^ ((uint64_t)(2 * i + 2) * G));
+      }
+      d += orc_fmix64(t);
+    }
+    digest[u] = d;
+  }
+  return 0;
+}
+
+int orc_vtok_check(const int32_t *block_table, const uint8_t *live, const int32_t *block_live,
+                   int32_t units, int32_t max_blocks, int32_t num_blocks,
+                   const int32_t *free_list, int32_t free_count, int64_t *out) {
+  if (!block_table || !live || !block_live || !free_list || !out || num_blocks < 1 ||
+      free_count < 0)
+    return -1;
+  int32_t *held = (int32_t *)calloc((size_t)num_blocks, sizeof(int32_t));
+  out[0] = out[1] = out[2] = out[3] = 0;
+  for (int64_t u = 0; u < units; ++u)
+    for (int64_t lb = 0; lb < max_blocks; ++lb) {
+      const int64_t e = block_table[u * max_blocks + lb];
+      if (e < 0) continue;
+      if (e >= num_blocks) {
+        ++out[2];
+      } else {
+        ++held[e];
+      }
+      int64_t c = 0;
+      for (int64_t o = 0; o < 16; ++o) c += live[(u * max_blocks + lb) * 16 + o] != 0;
+      if (c != block_live[u * max_blocks + lb]) ++out[3];
+    }
+  for (int64_t i = 0; i < free_count; ++i) {
+    const int64_t e = free_list[i];
+    if (e < 0 || e >= num_blocks) {
+      ++out[2];
+    } else {
+      ++held[e];
+    }
+  }
+  for (int64_t b = 0; b < num_blocks; ++b) {
+    if (held[b] > 1) ++out[0];
+    if (held[b] == 0) ++out[1];
+  }
+  free(held);
+  return 0;
+}

@@ -151,6 +151,36 @@ int orc_vtok_reclaim(void *k_pool, void *v_pool, int32_t elem_bytes, int32_t hea
                      int32_t *free_list, int32_t *free_count, int32_t free_capacity,
                      int64_t *stats);
 
+/* The online checks of I1 and I2 ([VTOK] section 3.5: token conservation and
+ * unique mapping are verified at every relocation by hashing and comparing).
+ *
+ * orc_vtok_digest: per head, an order-independent digest of its live tokens:
+ * the sum (mod 2^64) over live slots s < seq_len (seq_len clamped to
+ * [0, max_blocks*16]) in blocks whose id lies in [0, num_blocks) of
+ * fmix64(t), where
+ *   t = fmix64(pos ^ G) + sum_i fmix64(k_i ^ (2i+1) G) + sum_i fmix64(v_i ^ (2i+2) G)
+ * (mod 2^64), pos zero-extended from 32 bits, k_i and v_i the row's
+ * little-endian 64-bit words, G = 0x9E3779B97F4A7C15, and fmix64 the
+ * 64-bit finalizer of Appleby's MurmurHash3.  A token keeps its digest
+ * wherever it is stored; any change of a live token's position, K or V
+ * changes the head's digest with overwhelming probability.
+ *
+ * orc_vtok_check: out[4] = {pool blocks held more than once, pool blocks held
+ * by nobody, references out of range, live-count mismatches}, counting as
+ * holders every table entry >= 0 of every head (all max_blocks entries) and
+ * free_list[0, *free_count).  A table entry >= num_blocks or a list entry
+ * outside [0, num_blocks) is out of range.  A mismatch is an entry >= 0 whose
+ * block_live differs from its number of nonzero live bytes.  I2 holds when
+ * the first three are 0.  Returns 0, or -1 for invalid arguments. */
+uint64_t orc_fmix64(uint64_t k);
+int orc_vtok_digest(const void *k_pool, const void *v_pool, int32_t row_bytes,
+                    const int32_t *block_table, const int32_t *seq_len, const int32_t *pos,
+                    const uint8_t *live, int32_t units, int32_t max_blocks, int32_t num_blocks,
+                    uint64_t *digest);
+int orc_vtok_check(const int32_t *block_table, const uint8_t *live, const int32_t *block_live,
+                   int32_t units, int32_t max_blocks, int32_t num_blocks,
+                   const int32_t *free_list, int32_t free_count, int64_t *out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -226,3 +226,105 @@ def test_inconsistent_heads_are_skipped():
     vic[0, 0] = np.arange(32)
     new, status = oracle.vtok_evict(st2, vic, np.array([[40]], np.int32))
     assert status == 1 and new["live"][0, 0].sum() == 0 and new["block_live"][0, 0].tolist() == [0, 0]
+
+
+# ------------------------------------------------ online checks of I1, I2
+
+M64 = (1 << 64) - 1
+
+
+def _unfmix64(h):
+    """The inverse of MurmurHash3's finalizer, from its published steps: undo
+    each xor-shift by 33 (two rounds suffice for 64 bits) and each multiply by
+    the odd constant's inverse mod 2^64."""
+    def unshift(x):
+        return x ^ (x >> 33) ^ (x >> 66)
+    h = unshift(h)
+    h = (h * pow(0xc4ceb9fe1a85ec53, -1, 1 << 64)) & M64
+    h = unshift(h)
+    h = (h * pow(0xff51afd7ed558ccd, -1, 1 << 64)) & M64
+    return unshift(h)
+
+
+def test_fmix64_is_murmur3_finalizer():
+    assert oracle.fmix64(0) == 0
+    r = rng(4)
+    for x in [1, 2, 3, M64, 1 << 63] + [int(v) for v in r.integers(0, 1 << 63, 50)]:
+        y = oracle.fmix64(x)
+        assert _unfmix64(y) == x, hex(x)
+        assert y != x
+
+
+def test_digest_follows_the_tokens_not_their_slots():
+    st, fl, fc = _state([[5, 7, 16, 9, 3], [2, 2, 2, 2, 11]], spare=10)
+    st["score"] = np.zeros_like(st["score"])
+    d0 = oracle.vtok_digest(st)
+    assert (d0 != 0).all()
+    new, fl2, fc2, stats = oracle.vtok_reclaim(st, 0.0, 8, fl, fc)
+    assert stats[0] == 2
+    assert np.array_equal(oracle.vtok_digest(new), d0)          # I1 across a relocation
+    # one token moved by hand to a free block: the same digest
+    m = dict(new)
+    m["k_pool"], m["v_pool"] = new["k_pool"].copy(), new["v_pool"].copy()
+    m["block_table"], m["live"] = new["block_table"].copy(), new["live"].copy()
+    m["pos"] = new["pos"].copy()
+    lb = 2                                   # the full block: not a source, still in place
+    old = m["block_table"][0, 0, lb]
+    assert old == st["block_table"][0, 0, lb] and m["live"][0, 0, 32:48].all()
+    dst = int(fl2[fc2 - 1])
+    m["k_pool"][dst] = m["k_pool"][old]
+    m["v_pool"][dst] = m["v_pool"][old]
+    m["block_table"][0, 0, lb] = dst
+    assert np.array_equal(oracle.vtok_digest(m), d0)
+
+
+def test_digest_sees_every_live_byte_and_ignores_dead_ones():
+    st, fl, fc = _state([[5, 7, 16, 9, 3], [2, 2, 2, 2, 11]], spare=4)
+    d0 = oracle.vtok_digest(st)
+    blk = st["block_table"][0, 0, 1]
+    for pool, o, j in (("k_pool", 0, 0), ("v_pool", 6, 7), ("k_pool", 3, 5)):
+        m = dict(st)
+        m[pool] = st[pool].copy()
+        m[pool].view(np.uint8).reshape(st["num_blocks"], 16, -1)[blk, o, j] ^= 1
+        d = oracle.vtok_digest(m)
+        assert d[0, 0] != d0[0, 0] and d[0, 1] == d0[0, 1], (pool, o, j)
+    m = dict(st)
+    m["pos"] = st["pos"].copy()
+    m["pos"][0, 0, 17] += 1
+    assert oracle.vtok_digest(m)[0, 0] != d0[0, 0]
+    # a dead slot (block 1 keeps 7 of 16) changes nothing
+    m = dict(st)
+    m["k_pool"] = st["k_pool"].copy()
+    m["k_pool"].view(np.uint8).reshape(st["num_blocks"], 16, -1)[blk, 12, :] ^= 0xff
+    assert np.array_equal(oracle.vtok_digest(m), d0)
+    # swapping the V rows of two live tokens (each keeps its own K and pos) changes it
+    m = dict(st)
+    m["v_pool"] = st["v_pool"].copy()
+    b0 = st["block_table"][0, 0, 0]
+    m["v_pool"][b0, [0, 1]] = st["v_pool"][b0, [1, 0]]
+    assert oracle.vtok_digest(m)[0, 0] != d0[0, 0]
+    # no live token: 0
+    m = dict(st)
+    m["live"] = np.zeros_like(st["live"])
+    assert (oracle.vtok_digest(m) == 0).all()
+
+
+def test_check_counts_every_kind_of_fault():
+    st, fl, fc = _state([[5, 7, 16, 9, 3], [2, 2, 2, 2, 11]], spare=6)
+    assert oracle.vtok_check(st, fl, fc).tolist() == [0, 0, 0, 0]
+    new, fl2, fc2, _ = oracle.vtok_reclaim(st, 0.0, 8, fl, fc)
+    assert oracle.vtok_check(new, fl2, fc2).tolist() == [0, 0, 0, 0]   # I2 after a relocation
+    m = dict(st)
+    m["block_table"] = st["block_table"].copy()
+    m["block_table"][0, 1, 0] = st["block_table"][0, 0, 0]           # two owners, one orphan
+    assert oracle.vtok_check(m, fl, fc).tolist() == [1, 1, 0, 0]
+    m["block_table"][0, 1, 0] = st["num_blocks"]                      # out of range
+    assert oracle.vtok_check(m, fl, fc).tolist() == [0, 1, 1, 0]
+    m = dict(st)
+    m["block_live"] = st["block_live"].copy()
+    m["block_live"][0, 0, 2] -= 1
+    assert oracle.vtok_check(m, fl, fc).tolist() == [0, 0, 0, 1]
+    fl_bad = fl.copy()
+    fl_bad[0] = -7
+    assert oracle.vtok_check(st, fl_bad, fc).tolist() == [0, 1, 1, 0]
+    assert oracle.vtok_check(st, fl, fc - 1).tolist() == [0, 1, 0, 0]
