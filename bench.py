@@ -569,6 +569,26 @@ def bench_vtok(args, cfg):
     if args.profile_steps:
         log(f"profile run done: {ms_step:.4f} ms/step, reclaim {ms_reclaim:.4f} ms")
         return
+    # the online checks of I1 and I2 around one more step, timed on their own
+    cws = K.new_vtok_check_workspace(cache)
+    for t, v in ((cache.block_table, bt0), (cache.pos, pos0), (live, live0), (bl, bl0),
+                 (fl, fl0), (fc, fc0)):
+        t.copy_(v)
+    K.vtok_evict(cache, live, bl, vic_d, nv_d, ews, status)
+    c0, c1, c2, c3 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    c0.record()
+    dig0 = K.vtok_digest(cache, live)
+    c1.record()
+    K.vtok_reclaim(cache, live, bl, theta, max_sources, fl, fc, ws, stats=stats)
+    dig1 = K.vtok_digest(cache, live).clone()
+    c2.record()
+    chk = K.vtok_check(cache, live, bl, fl, fc, cws)
+    c3.record()
+    torch.cuda.synchronize()
+    online = {"I1_digests_equal": bool(torch.equal(dig0, dig1)),
+              "I2_check": chk.cpu().tolist(), "digest_ms": c0.elapsed_time(c1),
+              "check_ms": c2.elapsed_time(c3)}
+    assert online["I1_digests_equal"] and online["I2_check"] == [0, 0, 0, 0], online
     st = stats.cpu().numpy()
     # the plan's sizes from the marks, on the host (accounting only), checked
     # against the call's own statistics
@@ -616,6 +636,7 @@ def bench_vtok(args, cfg):
         "blocks_freed": int(st[3]),
         "rows_moved": int(st[4]),
         "bytes_moved": int(st[5]),
+        "online_checks": online,
         "roofline": {"kernel": "kvev_vtok_reclaim (plan, admit, move, apply launches)",
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,

@@ -55,7 +55,7 @@ extern "C" {
 #endif
 
 #define KVEV_BLOCK_SIZE 16
-#define KVEV_ABI_VERSION 8
+#define KVEV_ABI_VERSION 9
 
 typedef enum {
   KVEV_OK = 0,
@@ -369,6 +369,48 @@ int kvev_vtok_reclaim(const kvev_cache *cache, uint8_t *live, int32_t *block_liv
 
 /* Workspace bytes of kvev_vtok_reclaim; 0 for a bad cache or max_sources. */
 size_t kvev_vtok_workspace_bytes(const kvev_cache *cache, int32_t max_sources);
+
+/*
+ * kvev_vtok_digest -- the online check of vToken's I1, token conservation
+ * ([VTOK] section 3.5: the set of live tokens and their K/V contents survive
+ * every relocation; checked by hashing and comparing).  For every head u,
+ * digest[u] (uint64 on the device, written by the call) is the sum mod 2^64,
+ * over the live slots s < seq_len (clamped to [0, max_blocks*16]) in blocks
+ * whose id lies in [0, num_blocks), of fmix64(t) with
+ *   t = fmix64(pos ^ G) + sum_i fmix64(k_i ^ (2i+1)*G) + sum_i fmix64(v_i ^ (2i+2)*G),
+ * pos zero-extended, k_i / v_i the little-endian 64-bit words of the token's
+ * K and V rows, G = 0x9E3779B97F4A7C15, fmix64 MurmurHash3's 64-bit
+ * finalizer.  A token's contribution does not depend on where it is stored,
+ * so equal digests before and after kvev_vtok_reclaim confirm I1 (with
+ * overwhelming probability).  live: 16-byte aligned.  Two kernels on
+ * `stream` (one reads every live K and V row once).
+ * Errors: KVEV_EINVAL for NULL pointers, a bad cache or misaligned pointers.
+ */
+int kvev_vtok_digest(const kvev_cache *cache, const uint8_t *live, uint64_t *digest,
+                     void *stream);
+
+/*
+ * kvev_vtok_check -- the online check of vToken's I2, unique mapping
+ * ([VTOK] section 3.5), and of the live counts of section 3.3 stage 1.
+ * out: int64[4] on the device = {pool blocks held more than once, pool
+ * blocks held by nobody, references out of range, live-count mismatches}.
+ * Holders are every table entry >= 0 of every head (all max_blocks entries)
+ * and free_list[0, *free_count); a table entry >= num_blocks, a list entry
+ * outside [0, num_blocks) and a free count outside [0, free_capacity] are out
+ * of range.  A mismatch is a table entry >= 0 whose block_live differs from
+ * the number of its nonzero live bytes.  I2 holds when the first three are
+ * 0.  Workspace: kvev_vtok_check_workspace_bytes (scratch, a holder count per
+ * pool block).  live and the workspace 16-byte aligned.  Five kernels on
+ * `stream`.
+ * Errors: KVEV_EINVAL for NULL pointers, a bad cache, misaligned pointers or
+ * a negative capacity; KVEV_ENOSPACE for a missing or short workspace.
+ */
+int kvev_vtok_check(const kvev_cache *cache, const uint8_t *live, const int32_t *block_live,
+                    const int32_t *free_list, const int32_t *free_count, int32_t free_capacity,
+                    int64_t *out, void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes of kvev_vtok_check; 0 for a bad cache. */
+size_t kvev_vtok_check_workspace_bytes(const kvev_cache *cache);
 
 /*
  * kvev_window_attn -- helper outside the eviction step: the log-sum-exp and

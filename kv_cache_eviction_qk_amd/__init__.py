@@ -32,9 +32,10 @@ BLOCK_SIZE = 16
 EXPORTS = ("kvev_score", "kvev_select", "kvev_compact", "kvev_evict", "kvev_measure",
            "kvev_h2o_step", "kvev_h2o_workspace_bytes", "kvev_vtok_evict",
            "kvev_vtok_evict_workspace_bytes", "kvev_vtok_reclaim", "kvev_vtok_workspace_bytes",
+           "kvev_vtok_digest", "kvev_vtok_check", "kvev_vtok_check_workspace_bytes",
            "kvev_window_attn",
            "kvev_workspace_bytes", "kvev_strerror", "kvev_abi_version")
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 
 class KvevError(RuntimeError):
@@ -89,6 +90,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kvev_vtok_evict_workspace_bytes.restype = sz
     L.kvev_vtok_reclaim.argtypes = [P, P, P, P, ctypes.c_double, i32, P, P, i32, P, P, sz, P]
     L.kvev_vtok_workspace_bytes.argtypes = [P, i32]
+    L.kvev_vtok_digest.argtypes = [P, P, P, P]
+    L.kvev_vtok_check.argtypes = [P, P, P, P, P, i32, P, P, sz, P]
+    L.kvev_vtok_check_workspace_bytes.argtypes = [P]
+    L.kvev_vtok_check_workspace_bytes.restype = sz
     L.kvev_vtok_workspace_bytes.restype = sz
     L.kvev_workspace_bytes.argtypes = [P, i32, i32]
     L.kvev_workspace_bytes.restype = sz
@@ -97,7 +102,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kvev_abi_version.argtypes = []
     for f in (L.kvev_score, L.kvev_select, L.kvev_compact, L.kvev_evict, L.kvev_window_attn,
               L.kvev_measure, L.kvev_h2o_step, L.kvev_vtok_evict, L.kvev_vtok_reclaim,
-              L.kvev_abi_version):
+              L.kvev_vtok_digest, L.kvev_vtok_check, L.kvev_abi_version):
         f.restype = ctypes.c_int
     if L.kvev_abi_version() != ABI_VERSION:
         raise ImportError(f"{path} has ABI version {L.kvev_abi_version()}, expected "
@@ -467,6 +472,52 @@ def vtok_reclaim(cache: Cache, live: torch.Tensor, block_live: torch.Tensor, the
                              _stream(stream))
     _check(rc, "kvev_vtok_reclaim")
     return stats
+
+
+def vtok_digest(cache: Cache, live: torch.Tensor, digest: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """kvev_vtok_digest: per-head digest of the live tokens (I1's online
+    check).  Returns int64 [B, Hkv] holding the uint64 digests' bits."""
+    L = load_library()
+    c = cache.struct()
+    B, Hkv = cache.batch, cache.kv_heads
+    _need(live, "live", torch.uint8, B * Hkv * cache.max_slots)
+    if digest is None:
+        digest = torch.empty((B, Hkv), dtype=torch.int64, device=live.device)
+    _need(digest, "digest", torch.int64, B * Hkv)
+    _check(L.kvev_vtok_digest(ctypes.byref(c), _ptr(live), _ptr(digest), _stream(stream)),
+           "kvev_vtok_digest")
+    return digest
+
+
+def new_vtok_check_workspace(cache: Cache) -> torch.Tensor:
+    n = load_library().kvev_vtok_check_workspace_bytes(ctypes.byref(cache.struct()))
+    if n == 0:
+        raise KvevError(EINVAL, "kvev_vtok_check_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=cache.k_pool.device)
+
+
+def vtok_check(cache: Cache, live: torch.Tensor, block_live: torch.Tensor,
+               free_list: torch.Tensor, free_count: torch.Tensor, workspace: torch.Tensor,
+               out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kvev_vtok_check: I2 and the live counts.  Returns int64 [4] = {blocks
+    held more than once, held by nobody, references out of range, live-count
+    mismatches}."""
+    L = load_library()
+    c = cache.struct()
+    B, Hkv = cache.batch, cache.kv_heads
+    _need(live, "live", torch.uint8, B * Hkv * cache.max_slots)
+    _need(block_live, "block_live", torch.int32, B * Hkv * cache.max_blocks)
+    _need(free_list, "free_list", torch.int32)
+    _need(free_count, "free_count", torch.int32, 1)
+    _need(workspace, "workspace", torch.uint8)
+    if out is None:
+        out = torch.empty(4, dtype=torch.int64, device=live.device)
+    _need(out, "out", torch.int64, 4)
+    _check(L.kvev_vtok_check(ctypes.byref(c), _ptr(live), _ptr(block_live), _ptr(free_list),
+                             _ptr(free_count), free_list.numel(), _ptr(out), _ptr(workspace),
+                             workspace.numel(), _stream(stream)), "kvev_vtok_check")
+    return out
 
 
 def window_attn(cache: Cache, q: torch.Tensor, q_pos: torch.Tensor, scale: float, group: int,

@@ -359,6 +359,36 @@ int kvev_vtok_reclaim(const kvev_cache *cache, uint8_t *live, int32_t *block_liv
   return map_err(kvev::launch_vtok_reclaim(a, static_cast<hipStream_t>(stream)));
 }
 
+int kvev_vtok_digest(const kvev_cache *cache, const uint8_t *live, uint64_t *digest,
+                     void *stream) {
+  if (!valid_cache(cache) || !live || !digest) return KVEV_EINVAL;
+  if (misaligned16(live) || (reinterpret_cast<uintptr_t>(digest) & 7)) return KVEV_EINVAL;
+  kvev::VtokArgs a = vtok_args(cache, const_cast<uint8_t *>(live), nullptr);
+  return map_err(kvev::launch_vtok_digest(a, digest, static_cast<hipStream_t>(stream)));
+}
+
+size_t kvev_vtok_check_workspace_bytes(const kvev_cache *cache) {
+  return valid_cache(cache) ? a256(((size_t)cache->num_blocks + 1) / 2 * 8) : 0;
+}
+
+int kvev_vtok_check(const kvev_cache *cache, const uint8_t *live, const int32_t *block_live,
+                    const int32_t *free_list, const int32_t *free_count, int32_t free_capacity,
+                    int64_t *out, void *workspace, size_t ws_bytes, void *stream) {
+  if (!valid_cache(cache) || !live || !block_live || !free_list || !free_count || !out)
+    return KVEV_EINVAL;
+  if (misaligned16(live) || (reinterpret_cast<uintptr_t>(out) & 7) || free_capacity < 0)
+    return KVEV_EINVAL;
+  if (!workspace || ws_bytes < kvev_vtok_check_workspace_bytes(cache)) return KVEV_ENOSPACE;
+  if (misaligned16(workspace)) return KVEV_EINVAL;
+  kvev::VtokArgs a = vtok_args(cache, const_cast<uint8_t *>(live),
+                               const_cast<int32_t *>(block_live));
+  a.free_list = const_cast<int32_t *>(free_list);
+  a.free_count = const_cast<int32_t *>(free_count);
+  a.free_capacity = free_capacity;
+  return map_err(kvev::launch_vtok_check(a, static_cast<int32_t *>(workspace), out,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 int kvev_abi_version(void) { return KVEV_ABI_VERSION; }
 
 const char *kvev_strerror(int status) {

@@ -129,6 +129,8 @@ struct VtokArgs {
 };
 hipError_t launch_vtok_evict(const VtokArgs &a, hipStream_t s);
 hipError_t launch_vtok_reclaim(const VtokArgs &a, hipStream_t s);
+hipError_t launch_vtok_digest(const VtokArgs &a, uint64_t *digest, hipStream_t s);
+hipError_t launch_vtok_check(const VtokArgs &a, int32_t *held, int64_t *out, hipStream_t s);
 
 struct WindowAttnArgs {
   const uint8_t *k_pool, *v_pool;

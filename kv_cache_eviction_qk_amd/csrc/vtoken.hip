@@ -499,4 +499,186 @@ hipError_t launch_vtok_reclaim(const VtokArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------- online checks (I1, I2)
+
+namespace {
+constexpr uint64_t kGold = 0x9E3779B97F4A7C15ull;
+
+// MurmurHash3's 64-bit finalizer (Appleby): xor-shift 33, multiply, twice.
+__device__ __forceinline__ uint64_t fmix64(uint64_t k) {
+  k ^= k >> 33;
+  k *= 0xff51afd7ed558ccdull;
+  k ^= k >> 33;
+  k *= 0xc4ceb9fe1a85ec53ull;
+  k ^= k >> 33;
+  return k;
+}
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) v += (uint64_t)__shfl_xor((unsigned long long)v, o);
+  return v;
+}
+}  // namespace
+
+// Waves stride over a head's logical blocks.  Per block: the live slots'
+// ranks by ballot, then four live tokens at a time, 16 lanes each; a lane
+// finalizes its share of the token's 64-bit words (K words keyed 2i+1, V
+// words 2i+2, times the golden-ratio constant), the 16 lanes sum, and the
+// token's finalized sum joins the head's digest, a commutative integer sum
+// (any order gives the same value).  One atomic per workgroup: a head's
+// workgroups are few, so its digest word sees few atomics.
+constexpr int kDigestWaves = 8;
+constexpr int kDigestParts = 64;  // workgroups per head at most
+__global__ __launch_bounds__(kDigestWaves * kWave) void vtok_digest_kernel(const VtokArgs P,
+                                                                         uint64_t *digest) {
+  __shared__ uint64_t part[kDigestWaves];
+  const int u = blockIdx.y, l = lane_id(), wv = (int)(threadIdx.x / kWave);
+  const int n = min(max(P.seq_len[u], 0), P.max_slots);
+  const int nb = (n + kBlock - 1) / kBlock;
+  const size_t urow = (size_t)u * P.max_slots;
+  const int nw = P.row_bytes / 8, g = l / 16, gl = l % 16;
+  uint64_t acc = 0;
+  for (int lb = blockIdx.x * kDigestWaves + wv; lb < nb; lb += (int)gridDim.x * kDigestWaves) {
+    const int e = P.block_table[(size_t)u * P.max_blocks + lb];
+    if (e < 0 || e >= P.num_blocks) continue;
+    const int slot = lb * kBlock + l;
+    const bool mine = l < kBlock && slot < n && P.live[urow + slot] != 0;
+    const uint64_t mask = __ballot(mine);
+    const int c = __popcll(mask);
+    const int rank = __popcll(mask & ((1ull << l) - 1));
+    const int o_of_rank = __builtin_amdgcn_ds_permute((mine ? rank : (l | 32)) * 4, l);
+    for (int r0 = 0; r0 < c; r0 += 4) {
+      const int r = r0 + g;
+      const int o = __shfl(o_of_rank, r < kBlock ? r : 0);
+      uint64_t t = 0;
+      if (r < c) {
+        const size_t row = ((size_t)e * kBlock + o) * P.row_bytes;
+        for (int w = gl; w < 2 * nw; w += 16) {
+          const bool is_k = w < nw;
+          const int i = is_k ? w : w - nw;
+          const uint64_t x =
+              *reinterpret_cast<const uint64_t *>((is_k ? P.k_pool : P.v_pool) + row + (size_t)i * 8);
+          t += fmix64(x ^ ((uint64_t)(is_k ? 2 * i + 1 : 2 * i + 2) * kGold));
+        }
+      }
+#pragma unroll
+      for (int x = 8; x >= 1; x >>= 1) t += (uint64_t)__shfl_xor((unsigned long long)t, x);
+      if (gl == 0 && r < c)
+        acc += fmix64(t + fmix64((uint64_t)(uint32_t)P.pos[urow + lb * kBlock + o] ^ kGold));
+    }
+  }
+  acc = wave_sum_u64(acc);
+  if (l == 0) part[wv] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t sum = 0;
+    for (int w = 0; w < kDigestWaves; ++w) sum += part[w];
+    if (sum != 0) atomicAdd((unsigned long long *)(digest + u), (unsigned long long)sum);
+  }
+}
+
+__global__ void vtok_fill_kernel(uint64_t *p, size_t n64) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n64;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+hipError_t launch_vtok_digest(const VtokArgs &a, uint64_t *digest, hipStream_t s) {
+  hipLaunchKernelGGL(vtok_fill_kernel, dim3((unsigned)std::min((a.units + 255) / 256, 1024)),
+                     dim3(256), 0, s, digest, (size_t)a.units);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.units == 0) return e;
+  const int parts = std::min((a.max_blocks + kDigestWaves - 1) / kDigestWaves, kDigestParts);
+  hipLaunchKernelGGL(vtok_digest_kernel, dim3((unsigned)parts, (unsigned)a.units),
+                     dim3(kDigestWaves * kWave), 0, s, a, digest);
+  return hipGetLastError();
+}
+
+// I2 and the live counts: every table entry and free-list entry adds one to
+// its block's holder count (integer atomics); then a pass over the pool.
+// out[4] = {held more than once, held by nobody, out of range, count
+// mismatches}.
+__global__ __launch_bounds__(256) void vtok_check_table_kernel(const VtokArgs P, int32_t *held,
+                                                               int64_t *out) {
+  const int u = blockIdx.y, lb = blockIdx.x * 256 + threadIdx.x;
+  int bad = 0, mis = 0;
+  if (lb < P.max_blocks) {
+    const int e = P.block_table[(size_t)u * P.max_blocks + lb];
+    if (e >= 0) {
+      if (e < P.num_blocks) {
+        atomicAdd(held + e, 1);
+      } else {
+        bad = 1;
+      }
+      const uint4 b = ld16(P.live + (size_t)u * P.max_slots + (size_t)lb * kBlock);
+      int c = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x = w == 0 ? b.x : w == 1 ? b.y : w == 2 ? b.z : b.w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) c += ((x >> (8 * q)) & 0xffu) ? 1 : 0;
+      }
+      mis = c != P.block_live[(size_t)u * P.max_blocks + lb] ? 1 : 0;
+    }
+  }
+  const uint64_t bb = __ballot(bad), mm = __ballot(mis);
+  if (lane_id() == 0) {
+    if (bb) atomicAdd((unsigned long long *)(out + 2), (unsigned long long)__popcll(bb));
+    if (mm) atomicAdd((unsigned long long *)(out + 3), (unsigned long long)__popcll(mm));
+  }
+}
+
+__global__ __launch_bounds__(256) void vtok_check_list_kernel(const VtokArgs P, int32_t *held,
+                                                              int64_t *out) {
+  const int fc_raw = *P.free_count;
+  const int fc = min(max(fc_raw, 0), P.free_capacity);
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  int bad = 0;
+  if (i < fc) {
+    const int e = P.free_list[i];
+    if (e >= 0 && e < P.num_blocks) {
+      atomicAdd(held + e, 1);
+    } else {
+      bad = 1;
+    }
+  }
+  if (i == 0 && fc != fc_raw) bad = 1;  // a count outside [0, capacity]
+  const uint64_t bb = __ballot(bad);
+  if (lane_id() == 0 && bb)
+    atomicAdd((unsigned long long *)(out + 2), (unsigned long long)__popcll(bb));
+}
+
+__global__ __launch_bounds__(256) void vtok_check_pool_kernel(const VtokArgs P,
+                                                              const int32_t *held, int64_t *out) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  const int h = b < P.num_blocks ? held[b] : 1;
+  const uint64_t twice = __ballot(h > 1), none = __ballot(h == 0);
+  if (lane_id() == 0) {
+    if (twice) atomicAdd((unsigned long long *)(out + 0), (unsigned long long)__popcll(twice));
+    if (none) atomicAdd((unsigned long long *)(out + 1), (unsigned long long)__popcll(none));
+  }
+}
+
+hipError_t launch_vtok_check(const VtokArgs &a, int32_t *held, int64_t *out, hipStream_t s) {
+  hipLaunchKernelGGL(vtok_fill_kernel, dim3(1), dim3(64), 0, s, reinterpret_cast<uint64_t *>(out),
+                     (size_t)4);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t n64 = ((size_t)a.num_blocks + 1) / 2;  // the holder counts, as 64-bit words
+  hipLaunchKernelGGL(vtok_fill_kernel, dim3((unsigned)std::min<size_t>((n64 + 255) / 256, 4096)),
+                     dim3(256), 0, s, reinterpret_cast<uint64_t *>(held), n64);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(vtok_check_table_kernel,
+                     dim3((unsigned)((a.max_blocks + 255) / 256), (unsigned)a.units), dim3(256), 0,
+                     s, a, held, out);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(vtok_check_list_kernel, dim3((unsigned)((a.free_capacity + 255) / 256)),
+                     dim3(256), 0, s, a, held, out);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(vtok_check_pool_kernel, dim3((unsigned)((a.num_blocks + 255) / 256)),
+                     dim3(256), 0, s, a, held, out);
+  return hipGetLastError();
+}
+
 }  // namespace kvev

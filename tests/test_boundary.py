@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
     assert set(names) == set(K.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvev_abi_version() == K.ABI_VERSION == 8
+    assert L.kvev_abi_version() == K.ABI_VERSION == 9
     for code in (0, -1, -2, -3, -4):
         assert K.strerror(code)
 
@@ -331,3 +331,30 @@ def test_vtok_refusals():
     assert L.kvev_vtok_workspace_bytes(None, 8) == 0
     # it grows with max_sources (staged rows of every source)
     assert L.kvev_vtok_workspace_bytes(ctypes.byref(c), 64) > need
+
+
+def test_vtok_check_refusals():
+    L = K.load_library()
+    c = cache(max_blocks=8)
+    assert L.kvev_vtok_digest(ctypes.byref(c), None, FAKE, None) == K.EINVAL
+    assert L.kvev_vtok_digest(ctypes.byref(c), FAKE, None, None) == K.EINVAL
+    assert L.kvev_vtok_digest(ctypes.byref(c), FAKE + 4, FAKE, None) == K.EINVAL
+    assert L.kvev_vtok_digest(ctypes.byref(c), FAKE, FAKE + 4, None) == K.EINVAL
+    assert L.kvev_vtok_digest(ctypes.byref(cache(head_dim=96)), FAKE, FAKE, None) == K.EINVAL
+    need = L.kvev_vtok_check_workspace_bytes(ctypes.byref(c))
+    assert need >= c.num_blocks * 4
+    assert L.kvev_vtok_check_workspace_bytes(None) == 0
+
+    def check(ptrs=None, cap=64, ws_bytes=1 << 20):
+        p = dict(live=FAKE, bl=FAKE, fl=FAKE, fc=FAKE, out=FAKE, ws=FAKE)
+        p.update(ptrs or {})
+        return L.kvev_vtok_check(ctypes.byref(c), p["live"], p["bl"], p["fl"], p["fc"], cap,
+                                 p["out"], p["ws"], ws_bytes, None)
+
+    for name in ("live", "bl", "fl", "fc", "out"):
+        assert check(ptrs={name: None}) == K.EINVAL, name
+    assert check(ptrs={"live": FAKE + 4}) == K.EINVAL
+    assert check(ptrs={"out": FAKE + 4}) == K.EINVAL
+    assert check(cap=-1) == K.EINVAL
+    assert check(ptrs={"ws": None}) == K.ENOSPACE
+    assert check(ws_bytes=need - 1) == K.ENOSPACE

@@ -294,6 +294,56 @@ def test_reclaim_on_a_relocation_stream():
     assert ost[0] > 0
 
 
+# ---------------------------------------------- online checks of I1, I2
+
+
+def _digest(d):
+    return host(K.vtok_digest(d.c, d.live)).view(np.uint64)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64), ("bf16", 64), ("f32", 128)])
+def test_digest_and_check_match_the_oracle(dtype, D):
+    st, fl, fc = _state(50 + D, dtype=dtype, D=D, B=2, Hkv=4, max_blocks=20, spare=80,
+                        bad=(("len", 5),))
+    d = Dev(st, fl, fc)
+    g = _digest(d)
+    o = oracle.vtok_digest(st)
+    assert np.array_equal(g, o)
+    cws = K.new_vtok_check_workspace(d.c)
+    assert host(K.vtok_check(d.c, d.live, d.block_live, d.fl, d.fc, cws)).tolist() == \
+        oracle.vtok_check(st, fl, fc).tolist()
+    # planted faults, each against the oracle
+    bt = st["block_table"].copy()
+    bt[1, 2, 0] = bt[0, 0][bt[0, 0] >= 0][0]       # a second owner of a held block
+    bt[1, 3, 1] = st["num_blocks"] + 2             # out of range
+    bl = st["block_live"].copy()
+    lb = int(np.flatnonzero(bt[0, 0] >= 0)[-1])
+    bl[0, 0, lb] += 1                              # a count off by one
+    m = dict(st, block_table=bt, block_live=bl)
+    d2 = Dev(m, fl, fc)
+    want = oracle.vtok_check(m, fl, fc)
+    assert want[0] >= 1 and want[2] >= 1 and want[3] >= 1
+    assert host(K.vtok_check(d2.c, d2.live, d2.block_live, d2.fl, d2.fc, cws)).tolist() == \
+        want.tolist()
+    assert np.array_equal(_digest(d2), oracle.vtok_digest(m))
+
+
+def test_online_checks_around_reclamation():
+    """I1: every head's digest is the same before and after the relocation;
+    I2: every block held once, every live count right, after it."""
+    st, fl, fc = _state(61, B=2, Hkv=4, max_blocks=40, spare=200)
+    d = Dev(st, fl, fc)
+    before = _digest(d)
+    stats = d.reclaim(0.1, 64)
+    after = _digest(d)
+    cws = K.new_vtok_check_workspace(d.c)
+    chk = host(K.vtok_check(d.c, d.live, d.block_live, d.fl, d.fc, cws))
+    torch.cuda.synchronize()
+    assert host(stats)[0] > 0
+    assert np.array_equal(before, after) and np.array_equal(before, oracle.vtok_digest(st))
+    assert chk.tolist() == [0, 0, 0, 0]
+
+
 def test_full_size_random_eviction_layer():
     """One layer of the block-aware workload (B16, 8 KV heads, D128, 64000
     tokens: 4000 blocks a head, about 4.2 GB of K+V) with half of every head's
@@ -314,7 +364,12 @@ def test_full_size_random_eviction_layer():
     fl[:free.size] = free
     d = Dev(st, fl, free.size)
     d.evict(vic, nv)
+    before = _digest(d)
     stats = d.reclaim(0.25, 4096, with_score=False)
+    after = _digest(d)
+    cws = K.new_vtok_check_workspace(d.c)
+    chk = host(K.vtok_check(d.c, d.live, d.block_live, d.fl, d.fc, cws))
+    assert np.array_equal(before, after) and chk.tolist() == [0, 0, 0, 0]   # I1, I2 online
     _say("full size: GPU done; oracle")
     st2, _ = oracle.vtok_evict(st, vic, nv)
     o, ofl, ofc, ost = oracle.vtok_reclaim(st2, 0.25, 4096, fl, free.size)
@@ -333,3 +388,4 @@ def test_full_size_random_eviction_layer():
     kp, vp = host(d.c.k_pool), host(d.c.v_pool)
     assert np.array_equal(kp[dest], o["k_pool"][dest]) and np.array_equal(vp[dest], o["v_pool"][dest])
     assert np.array_equal(kp, o["k_pool"]) and np.array_equal(vp, o["v_pool"])
+    assert np.array_equal(after, oracle.vtok_digest(o))
