@@ -55,7 +55,7 @@ extern "C" {
 #endif
 
 #define KVEV_BLOCK_SIZE 16
-#define KVEV_ABI_VERSION 9
+#define KVEV_ABI_VERSION 10
 
 typedef enum {
   KVEV_OK = 0,
@@ -153,6 +153,35 @@ int kvev_score(const kvev_cache *cache, const kvev_window *win, int32_t flags,
 int kvev_select(const kvev_cache *cache, const float *score, int32_t budget,
                 int32_t recent_window, int32_t *victims, int32_t *n_victims, void *workspace,
                 size_t ws_bytes, void *stream);
+
+/*
+ * kvev_select_shared -- victim selection with one score shared by all KV
+ * heads of a sequence ([H2O] "Formulating Cumulative Attention Scores": a
+ * token's cumulative score sums the attention of every head of the layer;
+ * the page's cache class keeps one score per token for the batch row).
+ * score: fp32 [batch][kv_heads][max_blocks*16] per-head scores (each
+ * already summed over its GQA group, e.g. from kvev_score), 16-byte
+ * aligned.  For every sequence b the shared row is
+ *   S_b[s] = score[b][0][s] + score[b][1][s] + ... + score[b][kv_heads-1][s]
+ * in fp32, heads in ascending order, and kvev_select's rule runs on it once
+ * (m = max(0, n - budget) victims among the slots [0, n - recent_window), the
+ * m smallest (S, slot) pairs, ascending).  Every head of the sequence
+ * receives the same victims: victims int32 [batch][kv_heads][max_blocks*16]
+ * and n_victims int32 [batch][kv_heads], ready for kvev_compact.  The heads
+ * of a sequence must hold the same tokens in the same slots: when their
+ * seq_len differ, or their pos differ at any slot below it, n_victims is -1
+ * on every head of the sequence.  Workspace: kvev_select_shared_workspace_bytes
+ * (scratch only; no clearing needed), 16-byte aligned.  Six kernels on
+ * `stream`.
+ * Errors: as kvev_select (KVEV_EINVAL, KVEV_EUNSUPPORTED above 1M slots per
+ * head, KVEV_ENOSPACE).
+ */
+int kvev_select_shared(const kvev_cache *cache, const float *score, int32_t budget,
+                       int32_t recent_window, int32_t *victims, int32_t *n_victims,
+                       void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes of kvev_select_shared; 0 for a bad cache. */
+size_t kvev_select_shared_workspace_bytes(const kvev_cache *cache);
 
 /*
  * kvev_compact -- remove the victims and repack each KV head in place.

@@ -33,9 +33,10 @@ EXPORTS = ("kvev_score", "kvev_select", "kvev_compact", "kvev_evict", "kvev_meas
            "kvev_h2o_step", "kvev_h2o_workspace_bytes", "kvev_vtok_evict",
            "kvev_vtok_evict_workspace_bytes", "kvev_vtok_reclaim", "kvev_vtok_workspace_bytes",
            "kvev_vtok_digest", "kvev_vtok_check", "kvev_vtok_check_workspace_bytes",
+           "kvev_select_shared", "kvev_select_shared_workspace_bytes",
            "kvev_window_attn",
            "kvev_workspace_bytes", "kvev_strerror", "kvev_abi_version")
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 
 class KvevError(RuntimeError):
@@ -91,6 +92,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kvev_vtok_reclaim.argtypes = [P, P, P, P, ctypes.c_double, i32, P, P, i32, P, P, sz, P]
     L.kvev_vtok_workspace_bytes.argtypes = [P, i32]
     L.kvev_vtok_digest.argtypes = [P, P, P, P]
+    L.kvev_select_shared.argtypes = [P, P, i32, i32, P, P, P, sz, P]
+    L.kvev_select_shared_workspace_bytes.argtypes = [P]
+    L.kvev_select_shared_workspace_bytes.restype = sz
     L.kvev_vtok_check.argtypes = [P, P, P, P, P, i32, P, P, sz, P]
     L.kvev_vtok_check_workspace_bytes.argtypes = [P]
     L.kvev_vtok_check_workspace_bytes.restype = sz
@@ -102,7 +106,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kvev_abi_version.argtypes = []
     for f in (L.kvev_score, L.kvev_select, L.kvev_compact, L.kvev_evict, L.kvev_window_attn,
               L.kvev_measure, L.kvev_h2o_step, L.kvev_vtok_evict, L.kvev_vtok_reclaim,
-              L.kvev_vtok_digest, L.kvev_vtok_check, L.kvev_abi_version):
+              L.kvev_vtok_digest, L.kvev_vtok_check, L.kvev_select_shared,
+              L.kvev_abi_version):
         f.restype = ctypes.c_int
     if L.kvev_abi_version() != ABI_VERSION:
         raise ImportError(f"{path} has ABI version {L.kvev_abi_version()}, expected "
@@ -273,6 +278,35 @@ def select(cache: Cache, score_row: torch.Tensor, budget: int, recent_window: in
     rc = L.kvev_select(ctypes.byref(c), _ptr(score_row), budget, recent_window, _ptr(victims),
                        _ptr(n_victims), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(rc, "kvev_select")
+    return victims, n_victims
+
+
+def new_select_shared_workspace(cache: Cache) -> torch.Tensor:
+    n = load_library().kvev_select_shared_workspace_bytes(ctypes.byref(cache.struct()))
+    if n == 0:
+        raise KvevError(EINVAL, "kvev_select_shared_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=cache.k_pool.device)
+
+
+def select_shared(cache: Cache, score_row: torch.Tensor, budget: int, recent_window: int,
+                  workspace: torch.Tensor, victims: Optional[torch.Tensor] = None,
+                  n_victims: Optional[torch.Tensor] = None, stream=None):
+    """kvev_select_shared: one victim set per sequence from the per-head scores
+    summed over its KV heads, given to every head -> (victims, n_victims)."""
+    L = load_library()
+    c = cache.struct()
+    B, Hkv = cache.batch, cache.kv_heads
+    _need(score_row, "score_row", torch.float32, B * Hkv * cache.max_slots)
+    _need(workspace, "workspace", torch.uint8)
+    if victims is None:
+        victims = torch.empty((B, Hkv, cache.max_slots), dtype=torch.int32, device=score_row.device)
+    if n_victims is None:
+        n_victims = torch.empty((B, Hkv), dtype=torch.int32, device=score_row.device)
+    _need(victims, "victims", torch.int32, B * Hkv * cache.max_slots)
+    _need(n_victims, "n_victims", torch.int32, B * Hkv)
+    _check(L.kvev_select_shared(ctypes.byref(c), _ptr(score_row), budget, recent_window,
+                                _ptr(victims), _ptr(n_victims), _ptr(workspace),
+                                workspace.numel(), _stream(stream)), "kvev_select_shared")
     return victims, n_victims
 
 

@@ -143,28 +143,6 @@ int check_window(const kvev_cache *c, const kvev_window *w) {
   return KVEV_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int kvev_measure(const int32_t *seq_len_before, const int32_t *victims,
-                 const int32_t *n_victims, int32_t units, int32_t max_slots, int64_t *out,
-                 void *stream) {
-  if (!seq_len_before || !victims || !n_victims || !out || units < 0 || max_slots <= 0 ||
-      max_slots % KVEV_BLOCK_SIZE != 0)
-    return KVEV_EINVAL;
-  if ((int64_t)max_slots / KVEV_BLOCK_SIZE > (int64_t)65535 * 256 || units > 65535)
-    return KVEV_EUNSUPPORTED;
-  kvev::MeasureArgs a{};
-  a.seq_len_before = seq_len_before;
-  a.victims = victims;
-  a.n_victims = n_victims;
-  a.out = out;
-  a.units = units;
-  a.max_slots = max_slots;
-  return map_err(kvev::launch_measure(a, static_cast<hipStream_t>(stream)));
-}
-
 // Workspace of kvev_h2o_step: [arrival counters | error flags] (state, zero
 // between calls) then the parts' e values and (max, sum) per row.
 struct H2oLayout {
@@ -185,6 +163,28 @@ H2oLayout h2o_layout(const kvev_cache *c, int32_t group, int32_t budget) {
   L.o = off; off = a256(off + units * (size_t)kvev::kH2oMaxSplit * group * c->head_dim * 4);
   L.total = off;
   return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvev_measure(const int32_t *seq_len_before, const int32_t *victims,
+                 const int32_t *n_victims, int32_t units, int32_t max_slots, int64_t *out,
+                 void *stream) {
+  if (!seq_len_before || !victims || !n_victims || !out || units < 0 || max_slots <= 0 ||
+      max_slots % KVEV_BLOCK_SIZE != 0)
+    return KVEV_EINVAL;
+  if ((int64_t)max_slots / KVEV_BLOCK_SIZE > (int64_t)65535 * 256 || units > 65535)
+    return KVEV_EUNSUPPORTED;
+  kvev::MeasureArgs a{};
+  a.seq_len_before = seq_len_before;
+  a.victims = victims;
+  a.n_victims = n_victims;
+  a.out = out;
+  a.units = units;
+  a.max_slots = max_slots;
+  return map_err(kvev::launch_measure(a, static_cast<hipStream_t>(stream)));
 }
 
 size_t kvev_h2o_workspace_bytes(const kvev_cache *cache, int32_t group, int32_t budget) {
@@ -250,143 +250,6 @@ int kvev_h2o_step(const kvev_cache *cache, const void *q, const void *k_new, con
   if (kvev::h2o_lds_bytes(a, cache->head_dim) > kMaxLds - 4096) return KVEV_EUNSUPPORTED;
   return map_err(kvev::launch_h2o_step(a, cache->dtype == KVEV_BF16, cache->head_dim,
                                        static_cast<hipStream_t>(stream)));
-}
-
-// Workspace of kvev_vtok_reclaim (scratch only).
-struct VtokLayout {
-  size_t plan, src, srcoff, dstw, dst_off, push_off, tpos, tscore, misc, total;
-};
-
-VtokLayout vtok_layout(const kvev_cache *c, int32_t max_sources) {
-  VtokLayout L{};
-  const size_t units = (size_t)c->batch * c->kv_heads, ms = (size_t)max_sources;
-  size_t off = 0;
-  L.plan = off; off = a256(off + units * 8 * 4);
-  L.src = off; off = a256(off + units * ms * 4);
-  L.srcoff = off; off = a256(off + units * ms * 4);
-  L.dstw = off; off = a256(off + units * ms * 4);
-  L.dst_off = off; off = a256(off + units * 4);
-  L.push_off = off; off = a256(off + units * 4);
-  L.tpos = off; off = a256(off + units * ms * KVEV_BLOCK_SIZE * 4);
-  L.tscore = off; off = a256(off + units * ms * KVEV_BLOCK_SIZE * 4);
-  L.misc = off; off = a256(off + 8 * 4);
-  L.total = off;
-  return L;
-}
-
-// Workspace of kvev_vtok_evict: a claim word per slot.
-size_t vtok_evict_ws(const kvev_cache *c) {
-  return a256((size_t)c->batch * c->kv_heads * c->max_blocks * KVEV_BLOCK_SIZE * 4);
-}
-
-bool misaligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
-
-kvev::VtokArgs vtok_args(const kvev_cache *cache, uint8_t *live, int32_t *block_live) {
-  kvev::VtokArgs a{};
-  a.k_pool = static_cast<uint8_t *>(cache->k_pool);
-  a.v_pool = static_cast<uint8_t *>(cache->v_pool);
-  a.block_table = cache->block_table;
-  a.seq_len = cache->seq_len;
-  a.pos = cache->pos;
-  a.live = live;
-  a.block_live = block_live;
-  a.units = cache->batch * cache->kv_heads;
-  a.max_blocks = cache->max_blocks;
-  a.max_slots = cache->max_blocks * KVEV_BLOCK_SIZE;
-  a.num_blocks = cache->num_blocks;
-  a.row_bytes = cache->head_dim * elem_bytes(cache);
-  return a;
-}
-
-size_t kvev_vtok_evict_workspace_bytes(const kvev_cache *cache) {
-  return valid_cache(cache) ? vtok_evict_ws(cache) : 0;
-}
-
-int kvev_vtok_evict(const kvev_cache *cache, uint8_t *live, int32_t *block_live,
-                    const int32_t *victims, const int32_t *n_victims, int32_t *status,
-                    void *workspace, size_t ws_bytes, void *stream) {
-  if (!valid_cache(cache) || !live || !block_live || !victims || !n_victims || !status)
-    return KVEV_EINVAL;
-  if (misaligned16(live)) return KVEV_EINVAL;
-  if (!workspace || ws_bytes < vtok_evict_ws(cache)) return KVEV_ENOSPACE;
-  if (misaligned16(workspace)) return KVEV_EINVAL;
-  kvev::VtokArgs a = vtok_args(cache, live, block_live);
-  a.victims = victims;
-  a.n_victims = n_victims;
-  a.status = status;
-  a.claim = static_cast<int32_t *>(workspace);
-  return map_err(kvev::launch_vtok_evict(a, static_cast<hipStream_t>(stream)));
-}
-
-size_t kvev_vtok_workspace_bytes(const kvev_cache *cache, int32_t max_sources) {
-  if (!valid_cache(cache) || max_sources < 2 || max_sources > kvev::kVtokMaxSources) return 0;
-  return vtok_layout(cache, max_sources).total;
-}
-
-int kvev_vtok_reclaim(const kvev_cache *cache, uint8_t *live, int32_t *block_live,
-                      float *score_or_null, double theta_f, int32_t max_sources,
-                      int32_t *free_list, int32_t *free_count, int32_t free_capacity,
-                      int64_t *stats, void *workspace, size_t ws_bytes, void *stream) {
-  if (!valid_cache(cache) || !live || !block_live || !free_list || !free_count || !stats)
-    return KVEV_EINVAL;
-  if (misaligned16(live) || misaligned16(cache->pos) || misaligned16(score_or_null))
-    return KVEV_EINVAL;
-  if (!(theta_f >= 0.0 && theta_f < 1.0)) return KVEV_EINVAL;  // NaN refused too
-  if (max_sources < 2 || max_sources > kvev::kVtokMaxSources) return KVEV_EINVAL;
-  if ((int64_t)cache->batch * cache->kv_heads > kvev::kVtokMaxUnits) return KVEV_EUNSUPPORTED;
-  if (free_capacity < cache->num_blocks) return KVEV_ENOSPACE;
-  const VtokLayout L = vtok_layout(cache, max_sources);
-  if (!workspace || ws_bytes < L.total) return KVEV_ENOSPACE;
-  if (misaligned16(workspace)) return KVEV_EINVAL;
-  uint8_t *ws = static_cast<uint8_t *>(workspace);
-  kvev::VtokArgs a = vtok_args(cache, live, block_live);
-  a.score = score_or_null;
-  a.free_list = free_list;
-  a.free_count = free_count;
-  a.stats = stats;
-  a.max_sources = max_sources;
-  a.free_capacity = free_capacity;
-  a.theta_f = theta_f;
-  a.plan = reinterpret_cast<int32_t *>(ws + L.plan);
-  a.src = reinterpret_cast<int32_t *>(ws + L.src);
-  a.srcoff = reinterpret_cast<int32_t *>(ws + L.srcoff);
-  a.dstw = reinterpret_cast<int32_t *>(ws + L.dstw);
-  a.dst_off = reinterpret_cast<int32_t *>(ws + L.dst_off);
-  a.push_off = reinterpret_cast<int32_t *>(ws + L.push_off);
-  a.tpos = reinterpret_cast<int32_t *>(ws + L.tpos);
-  a.tscore = reinterpret_cast<float *>(ws + L.tscore);
-  a.misc = reinterpret_cast<int32_t *>(ws + L.misc);
-  return map_err(kvev::launch_vtok_reclaim(a, static_cast<hipStream_t>(stream)));
-}
-
-int kvev_vtok_digest(const kvev_cache *cache, const uint8_t *live, uint64_t *digest,
-                     void *stream) {
-  if (!valid_cache(cache) || !live || !digest) return KVEV_EINVAL;
-  if (misaligned16(live) || (reinterpret_cast<uintptr_t>(digest) & 7)) return KVEV_EINVAL;
-  kvev::VtokArgs a = vtok_args(cache, const_cast<uint8_t *>(live), nullptr);
-  return map_err(kvev::launch_vtok_digest(a, digest, static_cast<hipStream_t>(stream)));
-}
-
-size_t kvev_vtok_check_workspace_bytes(const kvev_cache *cache) {
-  return valid_cache(cache) ? a256(((size_t)cache->num_blocks + 1) / 2 * 8) : 0;
-}
-
-int kvev_vtok_check(const kvev_cache *cache, const uint8_t *live, const int32_t *block_live,
-                    const int32_t *free_list, const int32_t *free_count, int32_t free_capacity,
-                    int64_t *out, void *workspace, size_t ws_bytes, void *stream) {
-  if (!valid_cache(cache) || !live || !block_live || !free_list || !free_count || !out)
-    return KVEV_EINVAL;
-  if (misaligned16(live) || (reinterpret_cast<uintptr_t>(out) & 7) || free_capacity < 0)
-    return KVEV_EINVAL;
-  if (!workspace || ws_bytes < kvev_vtok_check_workspace_bytes(cache)) return KVEV_ENOSPACE;
-  if (misaligned16(workspace)) return KVEV_EINVAL;
-  kvev::VtokArgs a = vtok_args(cache, const_cast<uint8_t *>(live),
-                               const_cast<int32_t *>(block_live));
-  a.free_list = const_cast<int32_t *>(free_list);
-  a.free_count = const_cast<int32_t *>(free_count);
-  a.free_capacity = free_capacity;
-  return map_err(kvev::launch_vtok_check(a, static_cast<int32_t *>(workspace), out,
-                                         static_cast<hipStream_t>(stream)));
 }
 
 int kvev_abi_version(void) { return KVEV_ABI_VERSION; }
@@ -544,7 +407,176 @@ kvev::SelHead sel_head(const kvev_cache *cache, int32_t *n_victims, int32_t budg
 
 }  // namespace
 
+namespace {
+
+// Workspace of kvev_vtok_reclaim (scratch only).
+struct VtokLayout {
+  size_t plan, src, srcoff, dstw, dst_off, push_off, tpos, tscore, misc, total;
+};
+
+VtokLayout vtok_layout(const kvev_cache *c, int32_t max_sources) {
+  VtokLayout L{};
+  const size_t units = (size_t)c->batch * c->kv_heads, ms = (size_t)max_sources;
+  size_t off = 0;
+  L.plan = off; off = a256(off + units * 8 * 4);
+  L.src = off; off = a256(off + units * ms * 4);
+  L.srcoff = off; off = a256(off + units * ms * 4);
+  L.dstw = off; off = a256(off + units * ms * 4);
+  L.dst_off = off; off = a256(off + units * 4);
+  L.push_off = off; off = a256(off + units * 4);
+  L.tpos = off; off = a256(off + units * ms * KVEV_BLOCK_SIZE * 4);
+  L.tscore = off; off = a256(off + units * ms * KVEV_BLOCK_SIZE * 4);
+  L.misc = off; off = a256(off + 8 * 4);
+  L.total = off;
+  return L;
+}
+
+// Workspace of kvev_vtok_evict: a claim word per slot.
+size_t vtok_evict_ws(const kvev_cache *c) {
+  return a256((size_t)c->batch * c->kv_heads * c->max_blocks * KVEV_BLOCK_SIZE * 4);
+}
+
+bool misaligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
+
+kvev::VtokArgs vtok_args(const kvev_cache *cache, uint8_t *live, int32_t *block_live) {
+  kvev::VtokArgs a{};
+  a.k_pool = static_cast<uint8_t *>(cache->k_pool);
+  a.v_pool = static_cast<uint8_t *>(cache->v_pool);
+  a.block_table = cache->block_table;
+  a.seq_len = cache->seq_len;
+  a.pos = cache->pos;
+  a.live = live;
+  a.block_live = block_live;
+  a.units = cache->batch * cache->kv_heads;
+  a.max_blocks = cache->max_blocks;
+  a.max_slots = cache->max_blocks * KVEV_BLOCK_SIZE;
+  a.num_blocks = cache->num_blocks;
+  a.row_bytes = cache->head_dim * elem_bytes(cache);
+  return a;
+}
+
+// Workspace of kvev_select_shared: the selection's regions for a view of
+// the cache with one head per sequence, then the shared rows and victims.
+struct SharedLayout {
+  StateLayout S;
+  SelectLayout L;
+  size_t row, vvict, vnv, total;
+};
+
+kvev_cache shared_view(const kvev_cache *c) {
+  kvev_cache v = *c;
+  v.kv_heads = 1;
+  return v;
+}
+
+SharedLayout shared_layout(const kvev_cache *c) {
+  const kvev_cache v = shared_view(c);
+  SharedLayout X{};
+  X.S = state_layout(&v);
+  X.L = select_layout(&v);
+  const size_t ms = (size_t)c->max_blocks * KVEV_BLOCK_SIZE, B = (size_t)c->batch;
+  size_t off = X.L.total;
+  X.row = off; off = a256(off + B * ms * 4);
+  X.vvict = off; off = a256(off + B * ms * 4);
+  X.vnv = off; off = a256(off + B * 4);
+  X.total = off;
+  return X;
+}
+
+}  // namespace
+
 extern "C" {
+
+size_t kvev_vtok_evict_workspace_bytes(const kvev_cache *cache) {
+  return valid_cache(cache) ? vtok_evict_ws(cache) : 0;
+}
+
+int kvev_vtok_evict(const kvev_cache *cache, uint8_t *live, int32_t *block_live,
+                    const int32_t *victims, const int32_t *n_victims, int32_t *status,
+                    void *workspace, size_t ws_bytes, void *stream) {
+  if (!valid_cache(cache) || !live || !block_live || !victims || !n_victims || !status)
+    return KVEV_EINVAL;
+  if (misaligned16(live)) return KVEV_EINVAL;
+  if (!workspace || ws_bytes < vtok_evict_ws(cache)) return KVEV_ENOSPACE;
+  if (misaligned16(workspace)) return KVEV_EINVAL;
+  kvev::VtokArgs a = vtok_args(cache, live, block_live);
+  a.victims = victims;
+  a.n_victims = n_victims;
+  a.status = status;
+  a.claim = static_cast<int32_t *>(workspace);
+  return map_err(kvev::launch_vtok_evict(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t kvev_vtok_workspace_bytes(const kvev_cache *cache, int32_t max_sources) {
+  if (!valid_cache(cache) || max_sources < 2 || max_sources > kvev::kVtokMaxSources) return 0;
+  return vtok_layout(cache, max_sources).total;
+}
+
+int kvev_vtok_reclaim(const kvev_cache *cache, uint8_t *live, int32_t *block_live,
+                      float *score_or_null, double theta_f, int32_t max_sources,
+                      int32_t *free_list, int32_t *free_count, int32_t free_capacity,
+                      int64_t *stats, void *workspace, size_t ws_bytes, void *stream) {
+  if (!valid_cache(cache) || !live || !block_live || !free_list || !free_count || !stats)
+    return KVEV_EINVAL;
+  if (misaligned16(live) || misaligned16(cache->pos) || misaligned16(score_or_null))
+    return KVEV_EINVAL;
+  if (!(theta_f >= 0.0 && theta_f < 1.0)) return KVEV_EINVAL;  // NaN refused too
+  if (max_sources < 2 || max_sources > kvev::kVtokMaxSources) return KVEV_EINVAL;
+  if ((int64_t)cache->batch * cache->kv_heads > kvev::kVtokMaxUnits) return KVEV_EUNSUPPORTED;
+  if (free_capacity < cache->num_blocks) return KVEV_ENOSPACE;
+  const VtokLayout L = vtok_layout(cache, max_sources);
+  if (!workspace || ws_bytes < L.total) return KVEV_ENOSPACE;
+  if (misaligned16(workspace)) return KVEV_EINVAL;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  kvev::VtokArgs a = vtok_args(cache, live, block_live);
+  a.score = score_or_null;
+  a.free_list = free_list;
+  a.free_count = free_count;
+  a.stats = stats;
+  a.max_sources = max_sources;
+  a.free_capacity = free_capacity;
+  a.theta_f = theta_f;
+  a.plan = reinterpret_cast<int32_t *>(ws + L.plan);
+  a.src = reinterpret_cast<int32_t *>(ws + L.src);
+  a.srcoff = reinterpret_cast<int32_t *>(ws + L.srcoff);
+  a.dstw = reinterpret_cast<int32_t *>(ws + L.dstw);
+  a.dst_off = reinterpret_cast<int32_t *>(ws + L.dst_off);
+  a.push_off = reinterpret_cast<int32_t *>(ws + L.push_off);
+  a.tpos = reinterpret_cast<int32_t *>(ws + L.tpos);
+  a.tscore = reinterpret_cast<float *>(ws + L.tscore);
+  a.misc = reinterpret_cast<int32_t *>(ws + L.misc);
+  return map_err(kvev::launch_vtok_reclaim(a, static_cast<hipStream_t>(stream)));
+}
+
+int kvev_vtok_digest(const kvev_cache *cache, const uint8_t *live, uint64_t *digest,
+                     void *stream) {
+  if (!valid_cache(cache) || !live || !digest) return KVEV_EINVAL;
+  if (misaligned16(live) || (reinterpret_cast<uintptr_t>(digest) & 7)) return KVEV_EINVAL;
+  kvev::VtokArgs a = vtok_args(cache, const_cast<uint8_t *>(live), nullptr);
+  return map_err(kvev::launch_vtok_digest(a, digest, static_cast<hipStream_t>(stream)));
+}
+
+size_t kvev_vtok_check_workspace_bytes(const kvev_cache *cache) {
+  return valid_cache(cache) ? a256(((size_t)cache->num_blocks + 1) / 2 * 8) : 0;
+}
+
+int kvev_vtok_check(const kvev_cache *cache, const uint8_t *live, const int32_t *block_live,
+                    const int32_t *free_list, const int32_t *free_count, int32_t free_capacity,
+                    int64_t *out, void *workspace, size_t ws_bytes, void *stream) {
+  if (!valid_cache(cache) || !live || !block_live || !free_list || !free_count || !out)
+    return KVEV_EINVAL;
+  if (misaligned16(live) || (reinterpret_cast<uintptr_t>(out) & 7) || free_capacity < 0)
+    return KVEV_EINVAL;
+  if (!workspace || ws_bytes < kvev_vtok_check_workspace_bytes(cache)) return KVEV_ENOSPACE;
+  if (misaligned16(workspace)) return KVEV_EINVAL;
+  kvev::VtokArgs a = vtok_args(cache, const_cast<uint8_t *>(live),
+                               const_cast<int32_t *>(block_live));
+  a.free_list = const_cast<int32_t *>(free_list);
+  a.free_count = const_cast<int32_t *>(free_count);
+  a.free_capacity = free_capacity;
+  return map_err(kvev::launch_vtok_check(a, static_cast<int32_t *>(workspace), out,
+                                         static_cast<hipStream_t>(stream)));
+}
 
 int kvev_score(const kvev_cache *cache, const kvev_window *win, int32_t flags,
                int32_t pool_kernel, float *sum, float *pooled, float *drop, void *workspace,
@@ -682,6 +714,46 @@ int kvev_window_attn(const kvev_cache *cache, const kvev_window *win, float *lse
   a.scale = win->scale;
   return map_err(kvev::launch_window_attn(a, cache->dtype == KVEV_BF16, cache->head_dim,
                                           static_cast<hipStream_t>(stream)));
+}
+
+
+size_t kvev_select_shared_workspace_bytes(const kvev_cache *cache) {
+  return valid_cache(cache) ? shared_layout(cache).total : 0;
+}
+
+int kvev_select_shared(const kvev_cache *cache, const float *score, int32_t budget,
+                       int32_t recent_window, int32_t *victims, int32_t *n_victims,
+                       void *workspace, size_t ws_bytes, void *stream) {
+  if (!valid_cache(cache) || !score || !victims || !n_victims) return KVEV_EINVAL;
+  if (misaligned16(score) || misaligned16(workspace)) return KVEV_EINVAL;
+  if (budget <= 0 || recent_window < 0 || recent_window >= budget) return KVEV_EINVAL;
+  const SharedLayout X = shared_layout(cache);
+  if (X.L.chunks > kvev::kSelectMaxChunks) return KVEV_EUNSUPPORTED;
+  if (!workspace || ws_bytes < X.total) return KVEV_ENOSPACE;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  const kvev_cache v = shared_view(cache);
+  kvev::SharedArgs a{};
+  a.score = score;
+  a.seq_len = cache->seq_len;
+  a.pos = cache->pos;
+  a.row = reinterpret_cast<float *>(ws + X.row);
+  a.vseq = reinterpret_cast<int32_t *>(ws + X.S.head_acc);  // unused by a selection
+  a.vvict = reinterpret_cast<int32_t *>(ws + X.vvict);
+  a.vnv = reinterpret_cast<int32_t *>(ws + X.vnv);
+  a.victims = victims;
+  a.n_victims = n_victims;
+  a.zero = reinterpret_cast<uint32_t *>(ws);  // histograms and lengths
+  a.zero_words = X.S.total / 4;
+  a.B = cache->batch;
+  a.Hkv = cache->kv_heads;
+  a.max_slots = cache->max_blocks * KVEV_BLOCK_SIZE;
+  a.sel.score = a.row;
+  a.sel.seq_len = a.vseq;
+  a.sel.victims = a.vvict;
+  a.sel.sel = sel_head(&v, a.vnv, budget, recent_window, workspace);
+  a.sel.units = cache->batch;
+  a.sel.max_slots = a.max_slots;
+  return map_err(kvev::launch_select_shared(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

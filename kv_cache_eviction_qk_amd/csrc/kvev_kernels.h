@@ -132,6 +132,21 @@ hipError_t launch_vtok_reclaim(const VtokArgs &a, hipStream_t s);
 hipError_t launch_vtok_digest(const VtokArgs &a, uint64_t *digest, hipStream_t s);
 hipError_t launch_vtok_check(const VtokArgs &a, int32_t *held, int64_t *out, hipStream_t s);
 
+// Shared scores across the KV heads of a sequence (policy.hip).
+struct SharedArgs {
+  const float *score;          // [B][Hkv][max_slots] per-head scores
+  const int32_t *seq_len, *pos;
+  float *row;                  // workspace [B][max_slots]: the shared rows
+  int32_t *vseq;               // workspace [B]: the shared rows' lengths (zeroed first)
+  int32_t *vvict, *vnv;        // workspace: the selection's victims [B][max_slots], counts [B]
+  int32_t *victims, *n_victims;  // outputs [B][Hkv][max_slots], [B][Hkv]
+  uint32_t *zero;              // the words cleared first: vseq and the selection histograms
+  size_t zero_words;
+  SelectArgs sel;              // the selection over the B shared rows
+  int32_t B, Hkv, max_slots;
+};
+hipError_t launch_select_shared(const SharedArgs &a, hipStream_t s);
+
 struct WindowAttnArgs {
   const uint8_t *k_pool, *v_pool;
   const int32_t *block_table, *seq_len, *pos;

@@ -70,6 +70,7 @@ def lib():
                                    P, ctypes.c_double, i32, i32, P, P, P, P, P]
         L.orc_vtok_evict.argtypes = [P, P, P, P, i32, i32, P, P, P]
         L.orc_fmix64.argtypes = [ctypes.c_uint64]
+        L.orc_select_shared.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P]
         L.orc_fmix64.restype = ctypes.c_uint64
         L.orc_vtok_digest.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, P]
         L.orc_vtok_check.argtypes = [P, P, P, i32, i32, i32, P, i32, P]
@@ -77,7 +78,7 @@ def lib():
                                        ctypes.c_double, i32, P, P, i32, P]
         for f in (L.orc_lse_a, L.orc_score, L.orc_select, L.orc_compact, L.orc_measure,
                   L.orc_h2o_step, L.orc_vtok_evict, L.orc_vtok_reclaim, L.orc_vtok_digest,
-                  L.orc_vtok_check):
+                  L.orc_vtok_check, L.orc_select_shared):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -329,3 +330,20 @@ def vtok_check(state: dict, free_list: np.ndarray, free_count: int) -> np.ndarra
                               _p(out))
     assert rc == 0
     return out
+
+
+def select_shared(scores32: np.ndarray, seq_len: np.ndarray, pos: np.ndarray, budget: int,
+                  recent: int):
+    """Victims [B, Hkv, max_slots] and n_victims [B, Hkv] of the selection on
+    each sequence's scores summed over its KV heads (fp32, heads ascending)."""
+    scores32 = np.ascontiguousarray(scores32, dtype=np.float32)
+    B, Hkv = seq_len.shape
+    ms = scores32.size // (B * Hkv)
+    vic = np.full((B, Hkv, ms), -1, np.int32)
+    nv = np.zeros((B, Hkv), np.int32)
+    rc = lib().orc_select_shared(_p(scores32), _p(np.ascontiguousarray(seq_len, dtype=np.int32)),
+                                 _p(np.ascontiguousarray(pos, dtype=np.int32)), B, Hkv, ms,
+                                 budget, recent, _p(vic), _p(nv))
+    if rc != 0:
+        raise ValueError(f"oracle select_shared refused the arguments (rc={rc})")
+    return vic, nv

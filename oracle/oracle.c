@@ -839,3 +839,40 @@ int orc_vtok_check(const int32_t *block_table, const uint8_t *live, const int32_
   free(held);
   return 0;
 }
+
+
+/* ---- shared scores across the KV heads of a sequence ([H2O] Eq. for S_j) ---- */
+
+int orc_select_shared(const float *scores, const int32_t *seq_len, const int32_t *pos, int32_t B,
+                      int32_t Hkv, int32_t max_slots, int32_t budget, int32_t recent_window,
+                      int32_t *victims, int32_t *n_victims) {
+  if (!scores || !seq_len || !pos || !victims || !n_victims || B < 0 || Hkv < 1 ||
+      max_slots < 1)
+    return -1;
+  if (budget <= 0 || recent_window < 0 || recent_window >= budget) return -1;
+  float *row = (float *)malloc(sizeof(float) * (size_t)max_slots);
+  int32_t *vic = (int32_t *)malloc(sizeof(int32_t) * (size_t)max_slots);
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t u0 = b * Hkv;
+    const int32_t n = seq_len[u0];
+    int ok = n >= 0 && n <= max_slots;
+    for (int64_t h = 1; h < Hkv; ++h) ok = ok && seq_len[u0 + h] == n;
+    for (int64_t s = 0; ok && s < n; ++s) {
+      float acc = scores[u0 * max_slots + s];
+      for (int64_t h = 1; h < Hkv; ++h) {
+        acc = acc + scores[(u0 + h) * max_slots + s];
+        if (pos[(u0 + h) * max_slots + s] != pos[u0 * max_slots + s]) ok = 0;
+      }
+      row[s] = acc;
+    }
+    int32_t m = -1;
+    if (ok) orc_select(row, &n, 1, max_slots, budget, recent_window, vic, &m);
+    for (int64_t h = 0; h < Hkv; ++h) {
+      n_victims[u0 + h] = m;
+      for (int64_t i = 0; i < m; ++i) victims[(u0 + h) * max_slots + i] = vic[i];
+    }
+  }
+  free(row);
+  free(vic);
+  return 0;
+}

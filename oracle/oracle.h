@@ -67,6 +67,19 @@ int orc_score(const orc_cache *c, const orc_window *w, int flags, int pool_kerne
 int orc_select(const float *scores, const int32_t *seq_len, int32_t units, int32_t max_slots,
                int32_t budget, int32_t recent_window, int32_t *victims, int32_t *n_victims);
 
+/* Selection with one score per token shared by all KV heads of a sequence
+ * ([H2O] "Formulating Cumulative Attention Scores": S_j sums the attention
+ * of every head of the layer).  scores: fp32 [B][Hkv][max_slots] per-head
+ * rows.  The shared row of sequence b adds its heads' rows in fp32, heads in
+ * ascending order (the precision and order in which the library takes the
+ * same decision), then orc_select runs on it; every head of the sequence gets
+ * its victims.  Heads of a sequence whose seq_len differ, or whose pos differ
+ * at a slot below it, or a length outside [0, max_slots]: n_victims = -1 on
+ * every head of the sequence.  Returns 0 or -1 (invalid arguments). */
+int orc_select_shared(const float *scores, const int32_t *seq_len, const int32_t *pos, int32_t B,
+                      int32_t Hkv, int32_t max_slots, int32_t budget, int32_t recent_window,
+                      int32_t *victims, int32_t *n_victims);
+
 /* In-place, order-preserving compaction of every KV head; frees emptied tail
  * blocks to the free list.  elem_bytes is 4 (fp32) or 2 (bf16).  score may be
  * NULL.  stats[5] = {blocks_freed, rows_moved, bytes_moved, at_risk_rows, status}.

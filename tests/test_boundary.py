@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
     assert set(names) == set(K.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvev_abi_version() == K.ABI_VERSION == 9
+    assert L.kvev_abi_version() == K.ABI_VERSION == 10
     for code in (0, -1, -2, -3, -4):
         assert K.strerror(code)
 
@@ -358,3 +358,25 @@ def test_vtok_check_refusals():
     assert check(cap=-1) == K.EINVAL
     assert check(ptrs={"ws": None}) == K.ENOSPACE
     assert check(ws_bytes=need - 1) == K.ENOSPACE
+
+
+def test_select_shared_refusals():
+    L = K.load_library()
+    c = cache(max_blocks=8)
+    need = L.kvev_select_shared_workspace_bytes(ctypes.byref(c))
+    assert need > 0 and L.kvev_select_shared_workspace_bytes(None) == 0
+
+    def call(budget=64, recent=8, ptrs=None, ws_bytes=1 << 30):
+        p = dict(s=FAKE, v=FAKE, n=FAKE, ws=FAKE)
+        p.update(ptrs or {})
+        return L.kvev_select_shared(ctypes.byref(c), p["s"], budget, recent, p["v"], p["n"],
+                                    p["ws"], ws_bytes, None)
+
+    for name in ("s", "v", "n"):
+        assert call(ptrs={name: None}) == K.EINVAL, name
+    assert call(ptrs={"s": FAKE + 4}) == K.EINVAL
+    assert call(budget=0) == K.EINVAL
+    assert call(recent=64) == K.EINVAL
+    assert call(recent=-1) == K.EINVAL
+    assert call(ptrs={"ws": None}) == K.ENOSPACE
+    assert call(ws_bytes=need - 1) == K.ENOSPACE
