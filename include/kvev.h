@@ -55,7 +55,7 @@ extern "C" {
 #endif
 
 #define KVEV_BLOCK_SIZE 16
-#define KVEV_ABI_VERSION 10
+#define KVEV_ABI_VERSION 11
 
 typedef enum {
   KVEV_OK = 0,
@@ -153,6 +153,23 @@ int kvev_score(const kvev_cache *cache, const kvev_window *win, int32_t flags,
 int kvev_select(const kvev_cache *cache, const float *score, int32_t budget,
                 int32_t recent_window, int32_t *victims, int32_t *n_victims, void *workspace,
                 size_t ws_bytes, void *stream);
+
+/*
+ * kvev_select_budgets -- kvev_select with a budget and a recent window per
+ * KV head: budget and recent_window are int32 [batch][kv_heads] on the
+ * device.  For asymmetric allocations across layers ([H2O] "Asymmetric
+ * Layer Allocation": larger recent windows in early layers, larger heavy
+ * hitter pools in deep ones), the layers of a model can be stacked along the
+ * batch axis of one cache so that a single call serves them all, each with
+ * its own pair.  A head whose pair is invalid (budget <= 0, recent_window < 0
+ * or recent_window >= budget) gets n_victims -1, as does an inconsistent
+ * seq_len.  Same workspace as kvev_select (kvev_workspace_bytes).
+ * Errors: KVEV_EINVAL for NULL pointers, a bad cache or a misaligned score;
+ * KVEV_EUNSUPPORTED above 1M slots per head; KVEV_ENOSPACE.
+ */
+int kvev_select_budgets(const kvev_cache *cache, const float *score, const int32_t *budget,
+                        const int32_t *recent_window, int32_t *victims, int32_t *n_victims,
+                        void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * kvev_select_shared -- victim selection with one score shared by all KV

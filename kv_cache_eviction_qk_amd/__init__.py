@@ -33,10 +33,10 @@ EXPORTS = ("kvev_score", "kvev_select", "kvev_compact", "kvev_evict", "kvev_meas
            "kvev_h2o_step", "kvev_h2o_workspace_bytes", "kvev_vtok_evict",
            "kvev_vtok_evict_workspace_bytes", "kvev_vtok_reclaim", "kvev_vtok_workspace_bytes",
            "kvev_vtok_digest", "kvev_vtok_check", "kvev_vtok_check_workspace_bytes",
-           "kvev_select_shared", "kvev_select_shared_workspace_bytes",
+           "kvev_select_shared", "kvev_select_shared_workspace_bytes", "kvev_select_budgets",
            "kvev_window_attn",
            "kvev_workspace_bytes", "kvev_strerror", "kvev_abi_version")
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 
 class KvevError(RuntimeError):
@@ -93,6 +93,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kvev_vtok_workspace_bytes.argtypes = [P, i32]
     L.kvev_vtok_digest.argtypes = [P, P, P, P]
     L.kvev_select_shared.argtypes = [P, P, i32, i32, P, P, P, sz, P]
+    L.kvev_select_budgets.argtypes = [P, P, P, P, P, P, P, sz, P]
     L.kvev_select_shared_workspace_bytes.argtypes = [P]
     L.kvev_select_shared_workspace_bytes.restype = sz
     L.kvev_vtok_check.argtypes = [P, P, P, P, P, i32, P, P, sz, P]
@@ -107,7 +108,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for f in (L.kvev_score, L.kvev_select, L.kvev_compact, L.kvev_evict, L.kvev_window_attn,
               L.kvev_measure, L.kvev_h2o_step, L.kvev_vtok_evict, L.kvev_vtok_reclaim,
               L.kvev_vtok_digest, L.kvev_vtok_check, L.kvev_select_shared,
-              L.kvev_abi_version):
+              L.kvev_select_budgets, L.kvev_abi_version):
         f.restype = ctypes.c_int
     if L.kvev_abi_version() != ABI_VERSION:
         raise ImportError(f"{path} has ABI version {L.kvev_abi_version()}, expected "
@@ -278,6 +279,32 @@ def select(cache: Cache, score_row: torch.Tensor, budget: int, recent_window: in
     rc = L.kvev_select(ctypes.byref(c), _ptr(score_row), budget, recent_window, _ptr(victims),
                        _ptr(n_victims), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(rc, "kvev_select")
+    return victims, n_victims
+
+
+def select_budgets(cache: Cache, score_row: torch.Tensor, budget: torch.Tensor,
+                   recent_window: torch.Tensor, workspace: torch.Tensor,
+                   victims: Optional[torch.Tensor] = None, n_victims: Optional[torch.Tensor] = None,
+                   stream=None):
+    """kvev_select_budgets: kvev_select with int32 [B, Hkv] budgets and recent
+    windows on the GPU -> (victims, n_victims)."""
+    L = load_library()
+    c = cache.struct()
+    B, Hkv = cache.batch, cache.kv_heads
+    _need(score_row, "score_row", torch.float32, B * Hkv * cache.max_slots)
+    _need(budget, "budget", torch.int32, B * Hkv)
+    _need(recent_window, "recent_window", torch.int32, B * Hkv)
+    _need(workspace, "workspace", torch.uint8)
+    if victims is None:
+        victims = torch.empty((B, Hkv, cache.max_slots), dtype=torch.int32, device=score_row.device)
+    if n_victims is None:
+        n_victims = torch.empty((B, Hkv), dtype=torch.int32, device=score_row.device)
+    _need(victims, "victims", torch.int32, B * Hkv * cache.max_slots)
+    _need(n_victims, "n_victims", torch.int32, B * Hkv)
+    _check(L.kvev_select_budgets(ctypes.byref(c), _ptr(score_row), _ptr(budget),
+                                 _ptr(recent_window), _ptr(victims), _ptr(n_victims),
+                                 _ptr(workspace), workspace.numel(), _stream(stream)),
+           "kvev_select_budgets")
     return victims, n_victims
 
 

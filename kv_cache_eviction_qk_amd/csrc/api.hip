@@ -756,4 +756,26 @@ int kvev_select_shared(const kvev_cache *cache, const float *score, int32_t budg
   return map_err(kvev::launch_select_shared(a, static_cast<hipStream_t>(stream)));
 }
 
+
+int kvev_select_budgets(const kvev_cache *cache, const float *score, const int32_t *budget,
+                        const int32_t *recent_window, int32_t *victims, int32_t *n_victims,
+                        void *workspace, size_t ws_bytes, void *stream) {
+  if (!valid_cache(cache) || !score || !budget || !recent_window || !victims || !n_victims)
+    return KVEV_EINVAL;
+  if (misaligned16(score)) return KVEV_EINVAL;
+  const SelectLayout L = select_layout(cache);
+  if (L.chunks > kvev::kSelectMaxChunks) return KVEV_EUNSUPPORTED;
+  if (!workspace || ws_bytes < L.total) return KVEV_ENOSPACE;
+  kvev::SelectArgs a{};
+  a.score = score;
+  a.seq_len = cache->seq_len;
+  a.victims = victims;
+  a.sel = sel_head(cache, n_victims, 1, 0, workspace);
+  a.sel.budget_u = budget;
+  a.sel.recent_u = recent_window;
+  a.units = cache->batch * cache->kv_heads;
+  a.max_slots = cache->max_blocks * KVEV_BLOCK_SIZE;
+  return map_err(kvev::launch_select(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

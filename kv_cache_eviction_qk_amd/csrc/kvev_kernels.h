@@ -20,7 +20,16 @@ struct SelHead {
   uint2 *cand;            // scratch [units][nwg][4096]: (key, slot) pairs of the bucket
   uint32_t *ccount;       // scratch [units][nwg]: pairs in each collect region
   int32_t budget, recent, chunks, nwg;  // chunks: 1024-slot chunks; nwg: 4096-slot regions
+  const int32_t *budget_u, *recent_u;  // per-unit budgets and recent windows, or null
 };
+
+// The budget and recent window of unit u; false when the pair is invalid
+// (the unit is then treated as an inconsistent head: n_victims -1).
+__device__ __forceinline__ bool unit_budget(const SelHead &S, int u, int &budget, int &recent) {
+  budget = S.budget_u ? S.budget_u[u] : S.budget;
+  recent = S.recent_u ? S.recent_u[u] : S.recent;
+  return budget > 0 && recent >= 0 && recent < budget;
+}
 
 struct ScoreArgs {
   const uint8_t *k_pool, *v_pool;

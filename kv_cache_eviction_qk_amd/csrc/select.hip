@@ -32,9 +32,11 @@ __global__ __launch_bounds__(kHistThreads) void select_hist_kernel(const SelectA
   __shared__ uint32_t hl[kSelectBins];
   const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
   const int n = P.seq_len[u];
+  int budget, recent;
+  if (!unit_budget(P.sel, u, budget, recent)) return;   // the head step flags it
   if (n < 0 || n > P.max_slots) return;  // inconsistent head: the head step flags it
-  const int m = max(0, n - P.sel.budget);
-  const int nc = max(0, n - P.sel.recent);  // > m whenever m > 0
+  const int m = max(0, n - budget);
+  const int nc = max(0, n - recent);  // > m whenever m > 0
   if (m == 0) return;
   const int s0 = c * kHistChunk;
   if (s0 >= nc) return;
@@ -63,9 +65,11 @@ __global__ __launch_bounds__(kSelThreads) void select_collect_kernel(const Selec
   __shared__ CollectLds L;
   const int c = blockIdx.x, u = blockIdx.y;
   const int n = P.seq_len[u];
+  int budget, recent;
+  if (!unit_budget(P.sel, u, budget, recent)) return;
   if (n < 0 || n > P.max_slots) return;
-  const int m = max(0, n - P.sel.budget);
-  const int nc = max(0, n - P.sel.recent);
+  const int m = max(0, n - budget);
+  const int nc = max(0, n - recent);
   if (m == 0 || c * kHistChunk >= nc) return;
   collect_chunk(P.sel, P.score + (size_t)u * P.max_slots, P.sel.hist + (size_t)u * kSelectBins, u,
                 c, m, nc, P.max_slots, L);
@@ -77,12 +81,14 @@ __global__ __launch_bounds__(kSelThreads) void select_refine_kernel(const Select
   RefineLds &L = *reinterpret_cast<RefineLds *>(smem);
   const int u = blockIdx.x, tid = threadIdx.x;
   const int n = P.seq_len[u];
-  if (n < 0 || n > P.max_slots) {  // inconsistent head
+  int budget, recent;
+  const bool ok = unit_budget(P.sel, u, budget, recent);
+  if (!ok || n < 0 || n > P.max_slots) {  // inconsistent head
     if (tid == 0) P.sel.n_victims[u] = -1;
     return;
   }
-  const int m = max(0, n - P.sel.budget);
-  const int nc = max(0, n - P.sel.recent);
+  const int m = max(0, n - budget);
+  const int nc = max(0, n - recent);
   if (m == 0) {
     if (tid == 0) P.sel.n_victims[u] = 0;
     return;
@@ -94,9 +100,11 @@ __global__ __launch_bounds__(kEmitThreads) void select_emit_kernel(const SelectA
   __shared__ int wave_tot[kEmitThreads / kWave];
   const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
   const int n = P.seq_len[u];
+  int budget, recent;
+  if (!unit_budget(P.sel, u, budget, recent)) return;
   if (n < 0 || n > P.max_slots) return;
-  const int m = max(0, n - P.sel.budget);
-  const int nc = max(0, n - P.sel.recent);
+  const int m = max(0, n - budget);
+  const int nc = max(0, n - recent);
   if (m == 0) return;
   const int s0 = c * kSelectChunk;
   if (s0 >= nc) return;

@@ -71,6 +71,7 @@ def lib():
         L.orc_vtok_evict.argtypes = [P, P, P, P, i32, i32, P, P, P]
         L.orc_fmix64.argtypes = [ctypes.c_uint64]
         L.orc_select_shared.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P]
+        L.orc_select_budgets.argtypes = [P, P, i32, i32, P, P, P, P]
         L.orc_fmix64.restype = ctypes.c_uint64
         L.orc_vtok_digest.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, P]
         L.orc_vtok_check.argtypes = [P, P, P, i32, i32, i32, P, i32, P]
@@ -78,7 +79,7 @@ def lib():
                                        ctypes.c_double, i32, P, P, i32, P]
         for f in (L.orc_lse_a, L.orc_score, L.orc_select, L.orc_compact, L.orc_measure,
                   L.orc_h2o_step, L.orc_vtok_evict, L.orc_vtok_reclaim, L.orc_vtok_digest,
-                  L.orc_vtok_check, L.orc_select_shared):
+                  L.orc_vtok_check, L.orc_select_shared, L.orc_select_budgets):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -346,4 +347,20 @@ def select_shared(scores32: np.ndarray, seq_len: np.ndarray, pos: np.ndarray, bu
                                  budget, recent, _p(vic), _p(nv))
     if rc != 0:
         raise ValueError(f"oracle select_shared refused the arguments (rc={rc})")
+    return vic, nv
+
+
+def select_budgets(scores32: np.ndarray, seq_len: np.ndarray, budget: np.ndarray,
+                   recent: np.ndarray):
+    """Victims [U, max_slots] and n_victims [U] with a (budget, recent) pair
+    per unit."""
+    scores32 = np.ascontiguousarray(scores32, dtype=np.float32)
+    U = int(np.prod(seq_len.shape))
+    ms = scores32.size // U
+    vic = np.full((U, ms), -1, np.int32)
+    nv = np.zeros(U, np.int32)
+    rc = lib().orc_select_budgets(_p(scores32), _p(np.ascontiguousarray(seq_len, dtype=np.int32)),
+                                  U, ms, _p(np.ascontiguousarray(budget, dtype=np.int32)),
+                                  _p(np.ascontiguousarray(recent, dtype=np.int32)), _p(vic), _p(nv))
+    assert rc == 0
     return vic, nv

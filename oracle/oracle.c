@@ -876,3 +876,22 @@ int orc_select_shared(const float *scores, const int32_t *seq_len, const int32_t
   free(vic);
   return 0;
 }
+
+
+/* ---- per-unit budgets ([H2O] asymmetric layer allocation) ---- */
+
+int orc_select_budgets(const float *scores, const int32_t *seq_len, int32_t units,
+                       int32_t max_slots, const int32_t *budget, const int32_t *recent_window,
+                       int32_t *victims, int32_t *n_victims) {
+  if (!scores || !seq_len || !budget || !recent_window || !victims || !n_victims) return -1;
+  for (int64_t u = 0; u < units; ++u) {
+    const int32_t b = budget[u], r = recent_window[u], n = seq_len[u];
+    if (b <= 0 || r < 0 || r >= b || n < 0 || n > max_slots) {
+      n_victims[u] = -1;
+      continue;
+    }
+    orc_select(scores + u * (int64_t)max_slots, seq_len + u, 1, max_slots, b, r,
+               victims + u * (int64_t)max_slots, n_victims + u);
+  }
+  return 0;
+}

@@ -80,6 +80,13 @@ int orc_select_shared(const float *scores, const int32_t *seq_len, const int32_t
                       int32_t Hkv, int32_t max_slots, int32_t budget, int32_t recent_window,
                       int32_t *victims, int32_t *n_victims);
 
+/* orc_select with a (budget, recent_window) pair per unit; a unit whose pair
+ * is invalid (budget <= 0, recent < 0, recent >= budget) or whose seq_len is
+ * outside [0, max_slots] gets n_victims = -1.  Returns 0 or -1. */
+int orc_select_budgets(const float *scores, const int32_t *seq_len, int32_t units,
+                       int32_t max_slots, const int32_t *budget, const int32_t *recent_window,
+                       int32_t *victims, int32_t *n_victims);
+
 /* In-place, order-preserving compaction of every KV head; frees emptied tail
  * blocks to the free list.  elem_bytes is 4 (fp32) or 2 (bf16).  score may be
  * NULL.  stats[5] = {blocks_freed, rows_moved, bytes_moved, at_risk_rows, status}.

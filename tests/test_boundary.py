@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
     assert set(names) == set(K.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvev_abi_version() == K.ABI_VERSION == 10
+    assert L.kvev_abi_version() == K.ABI_VERSION == 11
     for code in (0, -1, -2, -3, -4):
         assert K.strerror(code)
 
@@ -380,3 +380,22 @@ def test_select_shared_refusals():
     assert call(recent=-1) == K.EINVAL
     assert call(ptrs={"ws": None}) == K.ENOSPACE
     assert call(ws_bytes=need - 1) == K.ENOSPACE
+
+
+def test_select_budgets_refusals():
+    L = K.load_library()
+    c = cache(max_blocks=8)
+    need = L.kvev_workspace_bytes(ctypes.byref(c), 0, 0)
+
+    def call(ptrs=None, ws_bytes=1 << 30):
+        p = dict(s=FAKE, b=FAKE, r=FAKE, v=FAKE, n=FAKE, ws=FAKE)
+        p.update(ptrs or {})
+        return L.kvev_select_budgets(ctypes.byref(c), p["s"], p["b"], p["r"], p["v"], p["n"],
+                                     p["ws"], ws_bytes, None)
+
+    for name in ("s", "b", "r", "v", "n"):
+        assert call(ptrs={name: None}) == K.EINVAL, name
+    assert call(ptrs={"s": FAKE + 8}) == K.EINVAL
+    assert call(ptrs={"ws": None}) == K.ENOSPACE
+    assert call(ws_bytes=64) == K.ENOSPACE        # far below the selection's regions
+    assert need > 64

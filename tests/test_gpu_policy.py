@@ -135,3 +135,48 @@ def test_shared_selection_full_layer():
     ov, on = oracle.select_shared(scores, seq, pos, 32000, 16)
     assert np.array_equal(host(n), on) and (on == 32000).all()
     assert np.array_equal(host(v)[:, :, :32000], ov[:, :, :32000])
+
+
+def test_per_head_budgets_bit_exact():
+    """kvev_select_budgets against oracle.select_budgets: four layers stacked
+    along the batch axis with an asymmetric schedule (early layers: long
+    recent windows and few heavy hitters; deep layers: the reverse), plus
+    invalid pairs and lengths that give -1."""
+    r = rng(21)
+    layers, B, Hkv, ms = 4, 3, 4, 4096
+    U = layers * B * Hkv
+    scores = r.integers(0, 50, (layers * B, Hkv, ms)).astype(np.float32)
+    seq = r.integers(ms // 2, ms + 1, (layers * B, Hkv)).astype(np.int32)
+    heavy = np.array([256, 512, 768, 1024], np.int32)      # per layer
+    recent = np.array([768, 512, 256, 64], np.int32)
+    bud = np.repeat(heavy + recent, B * Hkv).reshape(layers * B, Hkv).copy()
+    rec = np.repeat(recent, B * Hkv).reshape(layers * B, Hkv).copy()
+    bud[1, 2], rec[1, 2] = 100, 100        # recent >= budget: -1
+    bud[5, 0] = 0                          # no budget: -1
+    seq[7, 3] = ms + 5                     # past the capacity: -1
+    c = _Cache(layers * B, Hkv, ms, seq, np.zeros((layers * B, Hkv, ms), np.int32))
+    ws = K.new_workspace(c.c)
+    v, n = K.select_budgets(c.c, dev(scores), dev(bud), dev(rec), ws)
+    ov, on = oracle.select_budgets(scores.reshape(U, ms), seq.reshape(U), bud.reshape(U),
+                                   rec.reshape(U))
+    gv, gn = host(v).reshape(U, ms), host(n).reshape(U)
+    assert np.array_equal(gn, on)
+    assert (on == -1).sum() == 3
+    for u in range(U):
+        m = max(0, int(on[u]))
+        assert np.array_equal(gv[u, :m], ov[u, :m]), u
+    # the scalar entry point gives the same victims on a uniform schedule
+    bu = np.full((layers * B, Hkv), 900, np.int32)
+    ru = np.full((layers * B, Hkv), 50, np.int32)
+    seq[7, 3] = ms
+    c2 = _Cache(layers * B, Hkv, ms, seq, np.zeros((layers * B, Hkv, ms), np.int32))
+    v1, n1 = K.select_budgets(c2.c, dev(scores), dev(bu), dev(ru), ws)
+    vic = dev(np.full((layers * B, Hkv, ms), -1, np.int32))
+    nv = dev(np.zeros((layers * B, Hkv), np.int32))
+    K.select(c2.c, dev(scores), 900, 50, vic, nv, ws)
+    assert np.array_equal(host(n1), host(nv))
+    h1, h2, hn = host(v1), host(vic), host(nv)
+    for b in range(layers * B):
+        for h in range(Hkv):
+            m = int(hn[b, h])
+            assert np.array_equal(h1[b, h, :m], h2[b, h, :m])

@@ -89,3 +89,28 @@ def test_misaligned_heads_are_refused_per_sequence():
     pos[2, 1, 45] = 99                 # past the length: not a token
     _, nv2 = oracle.select_shared(scores, seq, pos, 20, 4)
     assert nv2[2].tolist() == [20, 20]
+
+
+def test_per_unit_budgets_brute_force():
+    """Each unit's victims are the m = n - budget smallest (score, slot) pairs
+    among its first n - recent slots (full sort), with its own pair; invalid
+    pairs and lengths give -1."""
+    r = rng(9)
+    U, ms = 8, 96
+    scores = r.integers(0, 6, (U, ms)).astype(np.float32)
+    seq = r.integers(0, ms + 1, U).astype(np.int32)
+    budget = r.integers(1, 60, U).astype(np.int32)
+    recent = np.minimum(r.integers(0, 20, U), budget - 1).astype(np.int32)
+    budget[5], recent[5] = 10, 10          # recent >= budget: refused
+    seq[6] = ms + 1                        # past the capacity: refused
+    vic, nv = oracle.select_budgets(scores, seq, budget, recent)
+    for u in range(U):
+        if u in (5, 6):
+            assert nv[u] == -1
+            continue
+        n = int(seq[u])
+        m = max(0, n - int(budget[u]))
+        nc = max(0, n - int(recent[u]))
+        order = np.lexsort((np.arange(nc), scores[u, :nc]))
+        assert nv[u] == m
+        assert np.array_equal(vic[u, :m], np.sort(order[:m]))
