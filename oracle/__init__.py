@@ -72,6 +72,8 @@ def lib():
         L.orc_fmix64.argtypes = [ctypes.c_uint64]
         L.orc_select_shared.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P]
         L.orc_select_budgets.argtypes = [P, P, i32, i32, P, P, P, P]
+        L.orc_ring_step.argtypes = [P, P, i32, i32, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                    P, P, P, P, P, ctypes.c_double, i32, i32, i32, i32, P, P, P]
         L.orc_fmix64.restype = ctypes.c_uint64
         L.orc_vtok_digest.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, P]
         L.orc_vtok_check.argtypes = [P, P, P, i32, i32, i32, P, i32, P]
@@ -79,7 +81,8 @@ def lib():
                                        ctypes.c_double, i32, P, P, i32, P]
         for f in (L.orc_lse_a, L.orc_score, L.orc_select, L.orc_compact, L.orc_measure,
                   L.orc_h2o_step, L.orc_vtok_evict, L.orc_vtok_reclaim, L.orc_vtok_digest,
-                  L.orc_vtok_check, L.orc_select_shared, L.orc_select_budgets):
+                  L.orc_vtok_check, L.orc_select_shared, L.orc_select_budgets,
+                  L.orc_ring_step):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -364,3 +367,53 @@ def select_budgets(scores32: np.ndarray, seq_len: np.ndarray, budget: np.ndarray
                                   _p(np.ascontiguousarray(recent, dtype=np.int32)), _p(vic), _p(nv))
     assert rc == 0
     return vic, nv
+
+
+def ring_state(state: dict, obs_window: int):
+    """Adds the ring-buffer adaptation's state to a COPY of a stream state:
+    hist fp32 [B,Hkv,max_slots,obs_window] (zeros), ring int32 [B,Hkv] (0)
+    and rank int32 [B,Hkv,max_slots] (each slot's index in position order)."""
+    new = dict(state)
+    B, Hkv, mb = state["B"], state["Hkv"], state["max_blocks"]
+    new["hist"] = np.zeros((B, Hkv, mb * 16, obs_window), np.float32)
+    new["ring"] = np.zeros((B, Hkv), np.int32)
+    rank = np.zeros((B, Hkv, mb * 16), np.int32)
+    for b in range(B):
+        for h in range(Hkv):
+            n = int(state["seq_len"][b, h])
+            p = state["pos"][b, h, :n]
+            rank[b, h, :n] = np.argsort(np.argsort(p, kind="stable"), kind="stable")
+    new["rank"] = rank
+    return new
+
+
+def ring_step(state: dict, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+              t_pos: np.ndarray, observe: np.ndarray, budget: int, recent: int,
+              pool_kernel: int, free_list: Optional[np.ndarray] = None, free_count: int = 0):
+    """One decode step of the SnapKV ring-buffer adaptation on a COPY of a
+    ring state (see ring_state).  Returns (new_state, evicted_pos [B,Hkv],
+    free_list, free_count)."""
+    new = dict(state)
+    for k in ("k_pool", "v_pool", "block_table", "seq_len", "pos", "hist", "ring", "rank"):
+        new[k] = np.ascontiguousarray(state[k]).copy()
+    B, Hkv = state["B"], state["Hkv"]
+    W = state["hist"].shape[-1]
+    is_bf16 = 1 if state["dtype"] == "bf16" else 0
+    if free_list is None:
+        free_list = np.full(state["num_blocks"], -1, np.int32)
+    fl = np.ascontiguousarray(free_list, dtype=np.int32).copy()
+    fc = np.array([free_count], np.int32)
+    ev = np.zeros((B, Hkv), np.int32)
+    rc = lib().orc_ring_step(_p(new["k_pool"]), _p(new["v_pool"]), is_bf16, state["D"],
+                             _p(new["block_table"]), _p(new["seq_len"]), _p(new["pos"]),
+                             _p(new["hist"]), _p(new["ring"]), _p(new["rank"]), B, Hkv,
+                             state["max_blocks"], state["num_blocks"], state["G"],
+                             _p(np.ascontiguousarray(q)), _p(np.ascontiguousarray(k_new)),
+                             _p(np.ascontiguousarray(v_new)),
+                             _p(np.ascontiguousarray(t_pos, dtype=np.int32)),
+                             _p(np.ascontiguousarray(observe, dtype=np.int32)),
+                             float(state["scale"]), budget, recent, W, pool_kernel, _p(fl),
+                             _p(fc), _p(ev))
+    if rc != 0:
+        raise ValueError(f"oracle ring_step refused the arguments (rc={rc})")
+    return new, ev, fl, int(fc[0])

@@ -895,3 +895,178 @@ int orc_select_budgets(const float *scores, const int32_t *seq_len, int32_t unit
   }
   return 0;
 }
+
+
+/* ---- SnapKV's decode-time ring buffer ([SNAP] "How it works") ---- */
+
+typedef struct {
+  int32_t pos;
+  int64_t idx; /* slot, or -1 for the new token */
+} by_pos;
+
+static int by_pos_cmp(const void *a, const void *b) {
+  const by_pos *x = (const by_pos *)a, *y = (const by_pos *)b;
+  return (x->pos > y->pos) - (x->pos < y->pos);
+}
+
+int orc_ring_step(void *k_pool, void *v_pool, int32_t is_bf16, int32_t head_dim,
+                  int32_t *block_table, int32_t *seq_len, int32_t *pos, float *hist,
+                  int32_t *ring, int32_t *rank, int32_t batch, int32_t kv_heads,
+                  int32_t max_blocks, int32_t num_blocks, int32_t group, const void *q,
+                  const void *k_new, const void *v_new, const int32_t *t_pos,
+                  const int32_t *observe, double scale, int32_t budget, int32_t recent,
+                  int32_t obs_window, int32_t pool_kernel, int32_t *free_list,
+                  int32_t *free_count, int32_t *evicted_pos) {
+  if (!k_pool || !v_pool || !block_table || !seq_len || !pos || !hist || !ring || !rank || !q ||
+      !k_new || !v_new || !t_pos || !observe || !free_list || !free_count || !evicted_pos)
+    return -1;
+  if (group < 1 || budget <= 0 || recent < 0 || recent >= budget || obs_window < 1) return -1;
+  if (pool_kernel < 1 || pool_kernel % 2 == 0 || budget > max_blocks * 16) return -1;
+  const int64_t D = head_dim, G = group, W = obs_window, max_slots = (int64_t)max_blocks * 16;
+  const int64_t row_bytes = D * (is_bf16 ? 2 : 4), r = (pool_kernel - 1) / 2;
+  double *s = (double *)malloc(sizeof(double) * (size_t)(G * (budget + 1)));
+  double *lse = (double *)malloc(sizeof(double) * (size_t)G);
+  float *S = (float *)malloc(sizeof(float) * (size_t)(budget + 1));
+  float *pooled = (float *)malloc(sizeof(float) * (size_t)(budget + 1));
+  by_pos *order = (by_pos *)malloc(sizeof(by_pos) * (size_t)(budget + 1));
+  for (int64_t u = 0; u < (int64_t)batch * kv_heads; ++u) {
+    const int64_t b = u / kv_heads, h = u % kv_heads;
+    const int64_t n = seq_len[u], t = t_pos[b];
+    int32_t *bt = block_table + u * max_blocks;
+    int32_t *ps = pos + u * max_slots;
+    float *hs = hist + u * max_slots * W;
+    if (n < 0 || n > budget || ring[u] < 0 || ring[u] >= W) {
+      evicted_pos[u] = -2;
+      continue;
+    }
+    int bad = 0;
+    for (int64_t lb = 0; lb < (n + 15) / 16; ++lb)
+      if (bt[lb] < 0 || bt[lb] >= num_blocks) bad = 1;
+    const int need_block = n < budget && n % 16 == 0 && bt[n / 16] < 0;
+    if (!need_block && n < budget && bt[n / 16] >= num_blocks) bad = 1;
+    if (bad) {
+      evicted_pos[u] = -4;
+      continue;
+    }
+    if (need_block) {
+      if (*free_count <= 0) {
+        evicted_pos[u] = -3;
+        continue;
+      }
+      const int32_t blk = free_list[--*free_count];
+      if (blk < 0 || blk >= num_blocks) {
+        evicted_pos[u] = -4;
+        continue;
+      }
+      bt[n / 16] = blk;
+    }
+    /* the step's softmax over the cached tokens (pos <= t) and the new token */
+    const char *knew = (const char *)k_new + u * row_bytes;
+    for (int64_t g = 0; g < G; ++g) {
+      const int64_t qrow = (b * kv_heads + h) * G + g;
+      double mx = -INFINITY;
+      for (int64_t j = 0; j <= n; ++j) {
+        if (j < n && ps[j] > t) {
+          s[g * (budget + 1) + j] = -INFINITY;
+          continue;
+        }
+        const int64_t prow = j < n ? (int64_t)bt[j / 16] * 16 + j % 16 : -1;
+        double acc = 0.0;
+        for (int64_t d = 0; d < D; ++d) {
+          const double kd = j < n ? widen(k_pool, is_bf16, prow * D + d) : widen(knew, is_bf16, d);
+          acc += widen(q, is_bf16, qrow * D + d) * kd;
+        }
+        s[g * (budget + 1) + j] = scale * acc;
+        if (s[g * (budget + 1) + j] > mx) mx = s[g * (budget + 1) + j];
+      }
+      double z = 0.0;
+      for (int64_t j = 0; j <= n; ++j) z += exp(s[g * (budget + 1) + j] - mx);
+      lse[g] = mx + log(z);
+    }
+    /* on_decode_step: the cached slots' weights into the ring, then advance */
+    if (observe[b]) {
+      for (int64_t j = 0; j < n; ++j) {
+        double pj = 0.0;
+        for (int64_t g = 0; g < G; ++g) pj += exp(s[g * (budget + 1) + j] - lse[g]);
+        hs[j * W + ring[u]] = (float)pj;
+      }
+      ring[u] = (int32_t)((ring[u] + 1) % W);
+    }
+    /* admit the new token with a zero ring; evict when over the budget */
+    int64_t dst;
+    int64_t kept_new = 1;
+    if (n < budget) {
+      dst = n;
+      seq_len[u] = (int32_t)(n + 1);
+      evicted_pos[u] = -1;
+    } else {
+      for (int64_t j = 0; j <= n; ++j) {
+        float acc = 0.f;
+        if (j < n)
+          for (int64_t w = 0; w < W; ++w) acc = acc + hs[j * W + w];
+        S[j] = acc;
+        order[j].pos = j < n ? ps[j] : (int32_t)t;
+        order[j].idx = j < n ? j : -1;
+      }
+      qsort(order, (size_t)(n + 1), sizeof(by_pos), by_pos_cmp);
+      /* max-pool over the neighbours in position order, clamped at both ends */
+      for (int64_t k = 0; k <= n; ++k) {
+        const int64_t lo = k - r > 0 ? k - r : 0, hi = k + r < n ? k + r : n;
+        float m = S[order[lo].idx < 0 ? n : order[lo].idx];
+        for (int64_t k2 = lo + 1; k2 <= hi; ++k2) {
+          const float v = S[order[k2].idx < 0 ? n : order[k2].idx];
+          if (v > m) m = v;
+        }
+        pooled[order[k].idx < 0 ? n : order[k].idx] = m;
+      }
+      int64_t best = -2;
+      float bv = 0.f;
+      int64_t bp = 0;
+      for (int64_t j = 0; j <= n; ++j) {
+        const int64_t pj = j < n ? ps[j] : t;
+        if (t - pj < recent) continue;
+        const cand a = {pooled[j], 0}, c = {bv, 0};
+        int less;
+        if (best == -2) {
+          less = 1;
+        } else {
+          const int cmp = cand_cmp(&a, &c);
+          less = cmp < 0 || (cmp == 0 && pj < bp);
+        }
+        if (less) {
+          best = j < n ? j : -1;
+          bv = pooled[j];
+          bp = pj;
+        }
+      }
+      if (best < 0) {
+        evicted_pos[u] = (int32_t)t;
+        kept_new = 0;
+        dst = -1;
+      } else {
+        dst = best;
+        evicted_pos[u] = ps[dst];
+      }
+    }
+    if (kept_new) {
+      const int64_t row = (int64_t)bt[dst / 16] * 16 + dst % 16;
+      copy_row(k_pool, row, knew, row_bytes);
+      copy_row(v_pool, row, (const char *)v_new + u * row_bytes, row_bytes);
+      ps[dst] = (int32_t)t;
+      for (int64_t w = 0; w < W; ++w) hs[dst * W + w] = 0.f;
+    }
+    /* each slot's index in position order */
+    const int64_t n2 = seq_len[u];
+    for (int64_t j = 0; j < n2; ++j) {
+      int32_t c = 0;
+      for (int64_t i = 0; i < n2; ++i) c += ps[i] < ps[j];
+      rank[u * max_slots + j] = c;
+    }
+  }
+  free(order);
+  free(pooled);
+  free(S);
+  free(lse);
+  free(s);
+  return 0;
+}

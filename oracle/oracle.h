@@ -87,6 +87,40 @@ int orc_select_budgets(const float *scores, const int32_t *seq_len, int32_t unit
                        int32_t max_slots, const int32_t *budget, const int32_t *recent_window,
                        int32_t *victims, int32_t *n_victims);
 
+/* One decode step of SnapKV's ring-buffer adaptation for every KV head
+ * ([SNAP] "How it works", "On the adaptation", "Parameters").  Per slot the
+ * cache keeps a ring of the last obs_window observed attention weights,
+ * hist [batch][kv_heads][max_blocks*16][obs_window] fp32, and ring
+ * [batch][kv_heads] the ring index written next.  The new token of sequence
+ * b (position t_pos[b]; k_new, v_new, q as in orc_h2o_step) attends to the
+ * cached tokens with pos <= t and to itself; the weight of cached token j is
+ * the group sum of its softmax probabilities, rounded to fp32.  When
+ * observe[b] is nonzero, every cached slot's weight goes to its ring at
+ * index ring[u] and the index advances modulo obs_window; a null step
+ * (observe[b] == 0) writes nothing and leaves the index.  The new token is
+ * then admitted with an all-zero ring.  Below the budget it is appended (a
+ * block popped from the free list when needed).  At the budget one of the
+ * n + 1 tokens is dropped: with sums S = the fp32 sum of each ring, index 0
+ * upward (0 for the new token), and the tokens taken in position order,
+ * pooled = the max of S over the poolKernel tokens centred on each (clamped
+ * at both ends); the victim is the smallest (pooled, position) among the
+ * tokens at least `recent` positions older than t (the new token included
+ * when recent == 0).  A cached victim's slot receives the new token (K, V,
+ * pos, a zero ring); a dropped new token leaves the cache as it was.
+ * rank [batch][kv_heads][max_blocks*16] is written for the slots below the
+ * new length: each slot's index in position order.  evicted_pos as in
+ * orc_h2o_step (-1 appended, the dropped position, or -2 / -3 / -4 with the
+ * head unchanged, rings included).  Returns 0, or -1 on invalid arguments
+ * (recent >= budget, obs_window < 1, an even or non-positive pool_kernel). */
+int orc_ring_step(void *k_pool, void *v_pool, int32_t is_bf16, int32_t head_dim,
+                  int32_t *block_table, int32_t *seq_len, int32_t *pos, float *hist,
+                  int32_t *ring, int32_t *rank, int32_t batch, int32_t kv_heads,
+                  int32_t max_blocks, int32_t num_blocks, int32_t group, const void *q,
+                  const void *k_new, const void *v_new, const int32_t *t_pos,
+                  const int32_t *observe, double scale, int32_t budget, int32_t recent,
+                  int32_t obs_window, int32_t pool_kernel, int32_t *free_list,
+                  int32_t *free_count, int32_t *evicted_pos);
+
 /* In-place, order-preserving compaction of every KV head; frees emptied tail
  * blocks to the free list.  elem_bytes is 4 (fp32) or 2 (bf16).  score may be
  * NULL.  stats[5] = {blocks_freed, rows_moved, bytes_moved, at_risk_rows, status}.
