@@ -371,11 +371,11 @@ def select_budgets(scores32: np.ndarray, seq_len: np.ndarray, budget: np.ndarray
 
 def ring_state(state: dict, obs_window: int):
     """Adds the ring-buffer adaptation's state to a COPY of a stream state:
-    hist fp32 [B,Hkv,max_slots,obs_window] (zeros), ring int32 [B,Hkv] (0)
+    hist fp32 [B,Hkv,obs_window,max_slots] (zeros), ring int32 [B,Hkv] (0)
     and rank int32 [B,Hkv,max_slots] (each slot's index in position order)."""
     new = dict(state)
     B, Hkv, mb = state["B"], state["Hkv"], state["max_blocks"]
-    new["hist"] = np.zeros((B, Hkv, mb * 16, obs_window), np.float32)
+    new["hist"] = np.zeros((B, Hkv, obs_window, mb * 16), np.float32)
     new["ring"] = np.zeros((B, Hkv), np.int32)
     rank = np.zeros((B, Hkv, mb * 16), np.int32)
     for b in range(B):
@@ -397,7 +397,7 @@ def ring_step(state: dict, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
     for k in ("k_pool", "v_pool", "block_table", "seq_len", "pos", "hist", "ring", "rank"):
         new[k] = np.ascontiguousarray(state[k]).copy()
     B, Hkv = state["B"], state["Hkv"]
-    W = state["hist"].shape[-1]
+    W = state["hist"].shape[2]
     is_bf16 = 1 if state["dtype"] == "bf16" else 0
     if free_list is None:
         free_list = np.full(state["num_blocks"], -1, np.int32)

@@ -934,7 +934,7 @@ int orc_ring_step(void *k_pool, void *v_pool, int32_t is_bf16, int32_t head_dim,
     const int64_t n = seq_len[u], t = t_pos[b];
     int32_t *bt = block_table + u * max_blocks;
     int32_t *ps = pos + u * max_slots;
-    float *hs = hist + u * max_slots * W;
+    float *hs = hist + u * W * max_slots; /* [W][max_slots] per head */
     if (n < 0 || n > budget || ring[u] < 0 || ring[u] >= W) {
       evicted_pos[u] = -2;
       continue;
@@ -988,7 +988,7 @@ int orc_ring_step(void *k_pool, void *v_pool, int32_t is_bf16, int32_t head_dim,
       for (int64_t j = 0; j < n; ++j) {
         double pj = 0.0;
         for (int64_t g = 0; g < G; ++g) pj += exp(s[g * (budget + 1) + j] - lse[g]);
-        hs[j * W + ring[u]] = (float)pj;
+        hs[(int64_t)ring[u] * max_slots + j] = (float)pj;
       }
       ring[u] = (int32_t)((ring[u] + 1) % W);
     }
@@ -1003,7 +1003,7 @@ int orc_ring_step(void *k_pool, void *v_pool, int32_t is_bf16, int32_t head_dim,
       for (int64_t j = 0; j <= n; ++j) {
         float acc = 0.f;
         if (j < n)
-          for (int64_t w = 0; w < W; ++w) acc = acc + hs[j * W + w];
+          for (int64_t w = 0; w < W; ++w) acc = acc + hs[w * max_slots + j];
         S[j] = acc;
         order[j].pos = j < n ? ps[j] : (int32_t)t;
         order[j].idx = j < n ? j : -1;
@@ -1053,7 +1053,7 @@ int orc_ring_step(void *k_pool, void *v_pool, int32_t is_bf16, int32_t head_dim,
       copy_row(k_pool, row, knew, row_bytes);
       copy_row(v_pool, row, (const char *)v_new + u * row_bytes, row_bytes);
       ps[dst] = (int32_t)t;
-      for (int64_t w = 0; w < W; ++w) hs[dst * W + w] = 0.f;
+      for (int64_t w = 0; w < W; ++w) hs[w * max_slots + dst] = 0.f;
     }
     /* each slot's index in position order */
     const int64_t n2 = seq_len[u];

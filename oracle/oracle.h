@@ -90,7 +90,8 @@ int orc_select_budgets(const float *scores, const int32_t *seq_len, int32_t unit
 /* One decode step of SnapKV's ring-buffer adaptation for every KV head
  * ([SNAP] "How it works", "On the adaptation", "Parameters").  Per slot the
  * cache keeps a ring of the last obs_window observed attention weights,
- * hist [batch][kv_heads][max_blocks*16][obs_window] fp32, and ring
+ * hist [batch][kv_heads][obs_window][max_blocks*16] fp32 (ring index major,
+ * so one index of every slot is contiguous), and ring
  * [batch][kv_heads] the ring index written next.  The new token of sequence
  * b (position t_pos[b]; k_new, v_new, q as in orc_h2o_step) attends to the
  * cached tokens with pos <= t and to itself; the weight of cached token j is

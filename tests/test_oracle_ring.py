@@ -61,9 +61,9 @@ def test_ring_weights_are_the_single_query_sum_scores():
         lse64, _ = oracle.lse_a(ch)
         lse32, _ = rounded_window_inputs(ch, lse64)
         want = oracle.score(ch, lse32, oracle.SUM)["sum"]
-        got = st["hist"][:, :, :t, idx]
+        got = st["hist"][:, :, idx, :t]
         assert np.allclose(got, want[:, :, :t], rtol=2e-6, atol=1e-30), t
-        assert (st["hist"][:, :, t] == 0).all()      # the new token: a zero ring
+        assert (st["hist"][:, :, :, t] == 0).all()   # the new token: a zero ring
         assert (st["pos"][:, :, t] == t).all()
 
 
@@ -82,10 +82,10 @@ def test_ring_wraps_and_null_steps_are_inert():
             written[t] = idx
             # only the index written changed in the cached rows
             other = [w for w in range(W) if w != idx]
-            assert np.array_equal(st["hist"][:, :, :t][..., other], before["hist"][:, :, :t][..., other])
+            assert np.array_equal(st["hist"][:, :, other, :t], before["hist"][:, :, other, :t])
         else:
             assert np.array_equal(st["ring"], before["ring"])
-            assert np.array_equal(st["hist"][:, :, :t], before["hist"][:, :, :t])
+            assert np.array_equal(st["hist"][:, :, :, :t], before["hist"][:, :, :, :t])
     # the observed steps cycle through the indices, skipping the null steps
     obs = [t for t in range(2, T) if t not in (5, 6)]
     assert [written[t] for t in obs] == [i % W for i in range(len(obs))]
@@ -96,12 +96,12 @@ def _brute_victim(st, u, t, recent, pool):
     B, Hkv = st["B"], st["Hkv"]
     b, h = divmod(u, Hkv)
     n = int(st["seq_len"][b, h])
-    W = st["hist"].shape[-1]
+    W = st["hist"].shape[2]
     S = []
     for j in range(n):
         acc = np.float32(0)
         for w in range(W):
-            acc = np.float32(acc + st["hist"][b, h, j, w])
+            acc = np.float32(acc + st["hist"][b, h, w, j])
         S.append(acc)
     S.append(np.float32(0))
     P = list(st["pos"][b, h, :n]) + [t]
@@ -128,7 +128,7 @@ def test_eviction_by_brute_force(seed, pool, recent, W):
         for h in range(Hkv):
             st["pos"][b, h, :n] = r.permutation(np.arange(40))[:n]
     st = _ring(st, W)
-    st["hist"][:, :, :n] = (r.integers(0, 5, (B, Hkv, n, W)) / 8).astype(np.float32)
+    st["hist"][:, :, :, :n] = (r.integers(0, 5, (B, Hkv, W, n)) / 8).astype(np.float32)
     t = 50
     want = [_brute_victim(st, u, t, recent, pool) for u in range(B * Hkv)]
     new, ev, _, _ = oracle.ring_step(st, _enc(qs[0], st), _enc(keys[:, :, 0], st),
@@ -141,7 +141,7 @@ def test_eviction_by_brute_force(seed, pool, recent, W):
             assert np.array_equal(new["pos"][b, h], st["pos"][b, h])
             continue
         slot = int(np.flatnonzero(st["pos"][b, h, :n] == want[u])[0])
-        assert new["pos"][b, h, slot] == t and (new["hist"][b, h, slot] == 0).all()
+        assert new["pos"][b, h, slot] == t and (new["hist"][b, h, :, slot] == 0).all()
         p = new["pos"][b, h, :n]
         assert np.array_equal(new["rank"][b, h, :n], np.argsort(np.argsort(p)))
 
@@ -150,7 +150,7 @@ def test_new_token_dropped_and_ties_drop_the_lower_position():
     B, Hkv, G, D, n, W = 1, 1, 1, 16, 8, 2
     keys, vals, qs = _stream_inputs(7, B, Hkv, G, D, 16)
     st = _ring(_state(keys, vals, n, n, G), W)
-    st["hist"][:, :, :n] = 1.0
+    st["hist"][:, :, :, :n] = 1.0
     new, ev, _, _ = oracle.ring_step(st, _enc(qs[0], st), _enc(keys[:, :, 0], st),
                                      _enc(vals[:, :, 0], st), np.full(B, 20, np.int32),
                                      np.zeros(B, np.int32), n, 0, 1)
@@ -187,7 +187,7 @@ def test_refusals():
             oracle.ring_step(st, _enc(qs[2], st), _enc(keys[:, :, 2], st), _enc(vals[:, :, 2], st),
                              np.full(B, 2, np.int32), np.ones(B, np.int32), budget, recent, pool)
     st0 = dict(st)
-    st0["hist"] = np.zeros(st["hist"].shape[:-1] + (0,), np.float32)
+    st0["hist"] = np.zeros(st["hist"].shape[:2] + (0,) + st["hist"].shape[3:], np.float32)
     with pytest.raises(ValueError):
         oracle.ring_step(st0, _enc(qs[2], st), _enc(keys[:, :, 2], st), _enc(vals[:, :, 2], st),
                          np.full(B, 2, np.int32), np.ones(B, np.int32), 8, 2, 1)
