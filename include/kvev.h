@@ -55,7 +55,7 @@ extern "C" {
 #endif
 
 #define KVEV_BLOCK_SIZE 16
-#define KVEV_ABI_VERSION 11
+#define KVEV_ABI_VERSION 12
 
 typedef enum {
   KVEV_OK = 0,
@@ -339,6 +339,58 @@ int kvev_h2o_step(const kvev_cache *cache, const void *q, const void *k_new, con
 /* Workspace bytes kvev_h2o_step needs for this cache, group and budget; 0
  * for a bad cache or a group / budget it refuses. */
 size_t kvev_h2o_workspace_bytes(const kvev_cache *cache, int32_t group, int32_t budget);
+
+/*
+ * kvev_ring_step -- one decode step of SnapKV's ring-buffer adaptation for
+ * every KV head ([SNAP] "How it works", "On the adaptation", "Parameters",
+ * "Tie-breaking").  State beside the cache (device, caller-owned):
+ *   hist: fp32 [batch][kv_heads][obs_window][max_blocks*16], each slot's
+ *         ring of its last obs_window observed weights (ring index major);
+ *   ring: int32 [batch][kv_heads], the ring index written next;
+ *   rank: int32 [batch][kv_heads][max_blocks*16], each slot's index in
+ *         position order (below seq_len); kvev_ring_init sets all three.
+ * The new token of sequence b sits at position t_pos[b]; k_new, v_new are
+ * [batch][kv_heads][head_dim] and q [batch][kv_heads*group][head_dim] in the
+ * cache dtype.  Its query rows attend to the cached tokens with pos <= t and
+ * to itself; a cached token's weight is the sum over the group of its
+ * softmax probabilities (fp32).  observe: int32 [batch]; nonzero writes every
+ * cached slot's weight at its ring index and advances the index modulo
+ * obs_window; 0 (a null attention vector) writes nothing and leaves it.  The
+ * new token enters with a zero ring.  Below the budget it is appended (a
+ * block popped from the free list when its logical block has none; heads
+ * appending in the same step may take the blocks in any order).  At the
+ * budget one token is dropped: ring sums S (index 0 upward, fp32; 0 for the
+ * new token), max-pooled over the pool_kernel tokens centred on each in
+ * position order (clamped at both ends); the smallest (pooled, position)
+ * among the tokens at least recent_window positions older than t (the new
+ * token included when recent_window == 0) is dropped, and the new token
+ * overwrites a dropped cached token's slot (K, V, pos, a zero ring).
+ * evicted_pos: int32 [batch][kv_heads], -1 appended, else the dropped
+ * position; -2 (seq_len outside [0, budget], ring index or a rank out of
+ * range), -3 (no free block), -4 (a block id out of range) leave the head
+ * unchanged.  Positions of a head must be distinct.  One 1024-thread
+ * workgroup per head on `stream`.
+ * Errors: KVEV_EINVAL for NULL pointers, a bad cache, group < 1,
+ * recent_window outside [0, budget), obs_window < 1, an even or
+ * non-positive pool_kernel, budget above the capacity; KVEV_EUNSUPPORTED
+ * for group > 8, budget > 4096, group * (budget + 1) > 16384 or pool_kernel
+ * > 2 * budget + 1.
+ */
+int kvev_ring_step(const kvev_cache *cache, float *hist, int32_t *ring, int32_t *rank,
+                   const void *q, const void *k_new, const void *v_new, const int32_t *t_pos,
+                   const int32_t *observe, int32_t group, float scale, int32_t budget,
+                   int32_t recent_window, int32_t obs_window, int32_t pool_kernel,
+                   int32_t *free_list, int32_t *free_count, int32_t *evicted_pos, void *stream);
+
+/*
+ * kvev_ring_init -- the ring state of a cache for kvev_ring_step: every
+ * ring zero, every ring index 0, and each slot's rank (its index in position
+ * order among the head's seq_len slots; heads longer than 4096 are left
+ * without ranks, which the step refuses anyway).  One workgroup per head.
+ * Errors: KVEV_EINVAL for NULL pointers, a bad cache or obs_window < 1.
+ */
+int kvev_ring_init(const kvev_cache *cache, float *hist, int32_t *ring, int32_t *rank,
+                   int32_t obs_window, void *stream);
 
 /*
  * kvev_vtok_evict -- vToken's evict_token for a batch ([VTOK] section 3.2:

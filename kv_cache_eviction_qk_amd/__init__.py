@@ -34,9 +34,10 @@ EXPORTS = ("kvev_score", "kvev_select", "kvev_compact", "kvev_evict", "kvev_meas
            "kvev_vtok_evict_workspace_bytes", "kvev_vtok_reclaim", "kvev_vtok_workspace_bytes",
            "kvev_vtok_digest", "kvev_vtok_check", "kvev_vtok_check_workspace_bytes",
            "kvev_select_shared", "kvev_select_shared_workspace_bytes", "kvev_select_budgets",
+           "kvev_ring_step", "kvev_ring_init",
            "kvev_window_attn",
            "kvev_workspace_bytes", "kvev_strerror", "kvev_abi_version")
-ABI_VERSION = 11
+ABI_VERSION = 12
 
 
 class KvevError(RuntimeError):
@@ -94,6 +95,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kvev_vtok_digest.argtypes = [P, P, P, P]
     L.kvev_select_shared.argtypes = [P, P, i32, i32, P, P, P, sz, P]
     L.kvev_select_budgets.argtypes = [P, P, P, P, P, P, P, sz, P]
+    L.kvev_ring_step.argtypes = [P, P, P, P, P, P, P, P, P, i32, ctypes.c_float, i32, i32, i32,
+                                 i32, P, P, P, P]
+    L.kvev_ring_init.argtypes = [P, P, P, P, i32, P]
     L.kvev_select_shared_workspace_bytes.argtypes = [P]
     L.kvev_select_shared_workspace_bytes.restype = sz
     L.kvev_vtok_check.argtypes = [P, P, P, P, P, i32, P, P, sz, P]
@@ -108,7 +112,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for f in (L.kvev_score, L.kvev_select, L.kvev_compact, L.kvev_evict, L.kvev_window_attn,
               L.kvev_measure, L.kvev_h2o_step, L.kvev_vtok_evict, L.kvev_vtok_reclaim,
               L.kvev_vtok_digest, L.kvev_vtok_check, L.kvev_select_shared,
-              L.kvev_select_budgets, L.kvev_abi_version):
+              L.kvev_select_budgets, L.kvev_ring_step, L.kvev_ring_init, L.kvev_abi_version):
         f.restype = ctypes.c_int
     if L.kvev_abi_version() != ABI_VERSION:
         raise ImportError(f"{path} has ABI version {L.kvev_abi_version()}, expected "
@@ -579,6 +583,50 @@ def vtok_check(cache: Cache, live: torch.Tensor, block_live: torch.Tensor,
                              _ptr(free_count), free_list.numel(), _ptr(out), _ptr(workspace),
                              workspace.numel(), _stream(stream)), "kvev_vtok_check")
     return out
+
+
+class RingState:
+    """The SnapKV ring-buffer state of a cache: hist fp32 [B, Hkv, W,
+    max_slots], ring int32 [B, Hkv], rank int32 [B, Hkv, max_slots]."""
+
+    def __init__(self, cache: Cache, obs_window: int, stream=None):
+        B, Hkv, dev_ = cache.batch, cache.kv_heads, cache.k_pool.device
+        self.W = obs_window
+        self.hist = torch.empty((B, Hkv, obs_window, cache.max_slots), dtype=torch.float32,
+                                device=dev_)
+        self.ring = torch.empty((B, Hkv), dtype=torch.int32, device=dev_)
+        self.rank = torch.zeros((B, Hkv, cache.max_slots), dtype=torch.int32, device=dev_)
+        _check(load_library().kvev_ring_init(ctypes.byref(cache.struct()), _ptr(self.hist),
+                                             _ptr(self.ring), _ptr(self.rank), obs_window,
+                                             _stream(stream)), "kvev_ring_init")
+
+
+def ring_step(cache: Cache, state: RingState, q: torch.Tensor, k_new: torch.Tensor,
+              v_new: torch.Tensor, t_pos: torch.Tensor, observe: torch.Tensor, group: int,
+              scale: float, budget: int, recent: int, pool_kernel: int, free_list: torch.Tensor,
+              free_count: torch.Tensor, evicted: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """kvev_ring_step: one SnapKV ring-buffer decode step of every KV head.
+    observe int32 [B] (0: a null step).  Returns evicted int32 [B, Hkv]."""
+    L = load_library()
+    c = cache.struct()
+    B, Hkv, D = cache.batch, cache.kv_heads, cache.head_dim
+    _need(q, "q", cache.k_pool.dtype, B * Hkv * group * D)
+    _need(k_new, "k_new", cache.k_pool.dtype, B * Hkv * D)
+    _need(v_new, "v_new", cache.k_pool.dtype, B * Hkv * D)
+    _need(t_pos, "t_pos", torch.int32, B)
+    _need(observe, "observe", torch.int32, B)
+    _need(state.hist, "hist", torch.float32, B * Hkv * state.W * cache.max_slots)
+    _need(free_list, "free_list", torch.int32)
+    _need(free_count, "free_count", torch.int32, 1)
+    if evicted is None:
+        evicted = torch.empty((B, Hkv), dtype=torch.int32, device=q.device)
+    _need(evicted, "evicted", torch.int32, B * Hkv)
+    _check(L.kvev_ring_step(ctypes.byref(c), _ptr(state.hist), _ptr(state.ring), _ptr(state.rank),
+                            _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(t_pos), _ptr(observe), group,
+                            scale, budget, recent, state.W, pool_kernel, _ptr(free_list),
+                            _ptr(free_count), _ptr(evicted), _stream(stream)), "kvev_ring_step")
+    return evicted
 
 
 def window_attn(cache: Cache, q: torch.Tensor, q_pos: torch.Tensor, scale: float, group: int,

@@ -778,4 +778,67 @@ int kvev_select_budgets(const kvev_cache *cache, const float *score, const int32
   return map_err(kvev::launch_select(a, static_cast<hipStream_t>(stream)));
 }
 
+
+int kvev_ring_init(const kvev_cache *cache, float *hist, int32_t *ring, int32_t *rank,
+                   int32_t obs_window, void *stream) {
+  if (!valid_cache(cache) || !hist || !ring || !rank || obs_window < 1) return KVEV_EINVAL;
+  kvev::RingArgs a{};
+  a.seq_len = cache->seq_len;
+  a.pos = cache->pos;
+  a.hist = hist;
+  a.ring = ring;
+  a.rank = rank;
+  a.units = cache->batch * cache->kv_heads;
+  a.W = obs_window;
+  a.max_slots = cache->max_blocks * KVEV_BLOCK_SIZE;
+  return map_err(kvev::launch_ring_init(a, static_cast<hipStream_t>(stream)));
+}
+
+int kvev_ring_step(const kvev_cache *cache, float *hist, int32_t *ring, int32_t *rank,
+                   const void *q, const void *k_new, const void *v_new, const int32_t *t_pos,
+                   const int32_t *observe, int32_t group, float scale, int32_t budget,
+                   int32_t recent_window, int32_t obs_window, int32_t pool_kernel,
+                   int32_t *free_list, int32_t *free_count, int32_t *evicted_pos, void *stream) {
+  if (!valid_cache(cache) || !hist || !ring || !rank || !q || !k_new || !v_new || !t_pos ||
+      !observe || !free_list || !free_count || !evicted_pos)
+    return KVEV_EINVAL;
+  if (group < 1 || budget < 1 || recent_window < 0 || recent_window >= budget ||
+      obs_window < 1 || pool_kernel < 1 || pool_kernel % 2 == 0 ||
+      budget > cache->max_blocks * KVEV_BLOCK_SIZE)
+    return KVEV_EINVAL;
+  if (group > kvev::kRingMaxGroup || budget > kvev::kRingMaxBudget ||
+      (int64_t)group * (budget + 1) > 16384 || pool_kernel > 2 * budget + 1)
+    return KVEV_EUNSUPPORTED;
+  kvev::RingArgs a{};
+  a.k_pool = static_cast<uint8_t *>(cache->k_pool);
+  a.v_pool = static_cast<uint8_t *>(cache->v_pool);
+  a.block_table = cache->block_table;
+  a.seq_len = cache->seq_len;
+  a.pos = cache->pos;
+  a.hist = hist;
+  a.ring = ring;
+  a.rank = rank;
+  a.q = static_cast<const uint8_t *>(q);
+  a.k_new = static_cast<const uint8_t *>(k_new);
+  a.v_new = static_cast<const uint8_t *>(v_new);
+  a.t_pos = t_pos;
+  a.observe = observe;
+  a.free_list = free_list;
+  a.free_count = free_count;
+  a.evicted = evicted_pos;
+  a.units = cache->batch * cache->kv_heads;
+  a.Hkv = cache->kv_heads;
+  a.G = group;
+  a.W = obs_window;
+  a.max_blocks = cache->max_blocks;
+  a.max_slots = cache->max_blocks * KVEV_BLOCK_SIZE;
+  a.num_blocks = cache->num_blocks;
+  a.budget = budget;
+  a.recent = recent_window;
+  a.pool_kernel = pool_kernel;
+  a.c1 = scale * 1.4426950408889634f;
+  return map_err(kvev::launch_ring_step(a, cache->dtype == KVEV_BF16, cache->head_dim,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

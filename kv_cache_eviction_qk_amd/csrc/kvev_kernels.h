@@ -156,6 +156,26 @@ struct SharedArgs {
 };
 hipError_t launch_select_shared(const SharedArgs &a, hipStream_t s);
 
+// SnapKV's decode-time ring buffer (ring_step.hip).
+constexpr int kRingMaxGroup = 8;
+constexpr int kRingMaxBudget = 4096;
+constexpr int kRingMaxBlocks = kRingMaxBudget / 16 + 1;
+struct RingArgs {
+  uint8_t *k_pool, *v_pool;
+  int32_t *block_table, *seq_len, *pos;
+  float *hist;                         // [units][W][max_slots] rings
+  int32_t *ring, *rank;                // [units] next ring index; [units][max_slots] position order
+  const uint8_t *q, *k_new, *v_new;    // [B][Hq][D], [B][Hkv][D], [B][Hkv][D]
+  const int32_t *t_pos, *observe;      // [B]
+  int32_t *free_list, *free_count;
+  int32_t *evicted;                    // [units]
+  int32_t units, Hkv, G, W, max_blocks, max_slots, num_blocks, budget, recent, pool_kernel;
+  float c1;                            // softmax scale * log2(e)
+};
+hipError_t launch_ring_step(const RingArgs &a, int bf16, int head_dim, hipStream_t s);
+hipError_t launch_ring_init(const RingArgs &a, hipStream_t s);
+size_t ring_lds_bytes(const RingArgs &a);
+
 struct WindowAttnArgs {
   const uint8_t *k_pool, *v_pool;
   const int32_t *block_table, *seq_len, *pos;

@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
     assert set(names) == set(K.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvev_abi_version() == K.ABI_VERSION == 11
+    assert L.kvev_abi_version() == K.ABI_VERSION == 12
     for code in (0, -1, -2, -3, -4):
         assert K.strerror(code)
 
@@ -399,3 +399,33 @@ def test_select_budgets_refusals():
     assert call(ptrs={"ws": None}) == K.ENOSPACE
     assert call(ws_bytes=64) == K.ENOSPACE        # far below the selection's regions
     assert need > 64
+
+
+def test_ring_step_refusals():
+    L = K.load_library()
+    c = cache(max_blocks=8)
+
+    def call(group=4, budget=64, recent=8, W=4, pool=3, ptrs=None, cc=None):
+        p = dict(h=FAKE, r=FAKE, k=FAKE, q=FAKE, kn=FAKE, vn=FAKE, t=FAKE, o=FAKE, fl=FAKE,
+                 fc=FAKE, ev=FAKE)
+        p.update(ptrs or {})
+        return L.kvev_ring_step(ctypes.byref(cc or c), p["h"], p["r"], p["k"], p["q"], p["kn"],
+                                p["vn"], p["t"], p["o"], group, 0.1, budget, recent, W, pool,
+                                p["fl"], p["fc"], p["ev"], None)
+
+    for name in ("h", "r", "k", "q", "kn", "vn", "t", "o", "fl", "fc", "ev"):
+        assert call(ptrs={name: None}) == K.EINVAL, name
+    assert call(group=0) == K.EINVAL
+    assert call(recent=64) == K.EINVAL               # recentWindow >= budget
+    assert call(W=0) == K.EINVAL                     # obsWindow of zero
+    assert call(pool=2) == K.EINVAL                  # an even poolKernel
+    assert call(pool=0) == K.EINVAL
+    assert call(budget=129) == K.EINVAL              # above the capacity
+    assert call(cc=cache(head_dim=96)) == K.EINVAL
+    assert call(group=9) == K.EUNSUPPORTED
+    big = cache(max_blocks=300)
+    assert call(cc=big, group=1, budget=4097) == K.EUNSUPPORTED
+    assert call(cc=big, group=8, budget=2048) == K.EUNSUPPORTED   # 8 * 2049 > 16384
+    assert call(pool=131) == K.EUNSUPPORTED
+    assert L.kvev_ring_init(ctypes.byref(c), None, FAKE, FAKE, 4, None) == K.EINVAL
+    assert L.kvev_ring_init(ctypes.byref(c), FAKE, FAKE, FAKE, 0, None) == K.EINVAL
