@@ -7,7 +7,8 @@ eviction on one MI355X, on seeded synthetic inputs.
 (--workload h2o_stream_870 times the H2O decode step instead: one
 kvev_h2o_step launch per decoded token of every sequence.  --workload
 vtok_reclaim_64k times vToken's liveness marks and lazy reclamation of one
-64000-token layer.)
+64000-token layer; --workload snap_ring_870 times SnapKV's decode-time ring
+buffer step.)
 
 A step is the whole eviction path for one layer's cache: scoring (SnapKV
 window sum + max-pool over the last W prompt queries), selection (budget,
@@ -99,6 +100,8 @@ def main():
         return bench_h2o_stream(args, cfg)
     if args.workload == "vtok_reclaim_64k":
         return bench_vtok(args, cfg)
+    if args.workload == "snap_ring_870":
+        return bench_ring_stream(args, cfg)
     if cfg.decode_steps:
         print(json.dumps({"error": f"{args.workload} is a decode schedule, not a one-shot pass"}))
         sys.exit(2)
@@ -472,6 +475,166 @@ def bench_h2o_stream(args, cfg):
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_ring_stream(args, cfg):
+    """SnapKV's decode-time ring buffer, one kvev_ring_step launch per step
+    over every KV head (softmax weights into the rings, pooled ring sums,
+    one token dropped per head at the budget).  The first budget - L steps
+    fill the cache (untimed, with the warmup steps); every timed step drops
+    one token per head.  Every seventh step of a sequence is a null step.
+    value = decoded tokens (one per sequence) per second."""
+    import numpy as np
+    import torch
+
+    import kv_cache_eviction_qk_amd as K
+    import synth
+
+    B, Hkv, G, D, W = cfg.B, cfg.Hkv, cfg.G, cfg.D, cfg.W
+    fill = cfg.budget - cfg.L
+    warm = args.warmup
+    steps = min(args.steps, cfg.decode_steps - fill - warm)
+    if steps < 1:
+        print(json.dumps({"error": f"{cfg.decode_steps} steps in the stream: lower --warmup"}))
+        sys.exit(2)
+    case = synth.make_case(cfg)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    cache = K.Cache(dev(case["k_pool"]), dev(case["v_pool"]), dev(case["block_table"]),
+                    dev(case["seq_len"]), dev(case["pos"]))
+    rs = K.RingState(cache, W)
+    free_list = torch.full((case["num_blocks"],), -1, dtype=torch.int32, device="cuda")
+    free_count = torch.zeros(1, dtype=torch.int32, device="cuda")
+    total = fill + warm + steps
+    qs, ks, vs, obs = [], [], [], []
+    for i in range(total):  # every step's inputs resident before the timed region
+        q, _ = synth.make_queries(cfg, 0, 1, case["dirs"], step=i)
+        k, v = synth.decode_token_kv(case, i)
+        qs.append(dev(q.reshape(B, cfg.Hq, D)))
+        ks.append(dev(k))
+        vs.append(dev(v))
+        obs.append(dev(np.array([int((i + b) % 7 != 3) for b in range(B)], np.int32)))
+    tpos = [torch.full((B,), cfg.L + i, dtype=torch.int32, device="cuda") for i in range(total)]
+    evicted = torch.empty((B, Hkv), dtype=torch.int32, device="cuda")
+
+    def step(i):
+        K.ring_step(cache, rs, qs[i], ks[i], vs[i], tpos[i], obs[i], G, cfg.softmax_scale,
+                    cfg.budget, cfg.recent, cfg.pool_kernel, free_list, free_count, evicted)
+
+    for i in range(fill + warm):
+        step(i)
+    torch.cuda.synchronize()
+    assert int(cache.seq_len.min()) == cfg.budget
+    log(f"stream filled to {cfg.budget} tokens per head; {warm} warmup steps")
+    state = (cache.k_pool, cache.v_pool, cache.block_table, cache.seq_len, cache.pos, rs.hist,
+             rs.ring, rs.rank)
+    snap = [t.clone() for t in state]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(fill + warm, total):
+            step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = e0.elapsed_time(e1) / steps
+    if args.profile_steps:
+        log(f"profile run done: {ms_step:.4f} ms/step")
+        return
+    ev = evicted.cpu().numpy()
+    assert (ev >= 0).all(), "a timed step did not drop a token"
+    after = [t.clone() for t in state]
+    for t, v in zip(state, snap):
+        t.copy_(v)
+    torch.cuda.synchronize()
+    x0, x1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    x0.record()
+    for i in range(fill + warm, total):
+        step(i)
+    x1.record()
+    torch.cuda.synchronize()
+    ms_eager = x0.elapsed_time(x1) / steps
+    assert all(bool(torch.equal(a, b)) for a, b in zip(after, state)), \
+        "graph replay and eager steps differ"
+    # algorithmic bytes of one step: per cached token its key row, position,
+    # rank (read and written) and ring (obsWindow entries read, one written);
+    # per head the query rows and the new token's key and value rows
+    eb = 2 if cfg.dtype == "bf16" else 4
+    units, n = B * Hkv, cfg.budget
+    step_bytes = (units * n * (D * eb + 4 + 8 + 4 * W + 4)
+                  + units * math.ceil(n / 16) * 4
+                  + B * cfg.Hq * D * eb
+                  + units * 3 * D * eb)
+    achieved = step_bytes / (ms_step / 1e3) / 1e9
+    traffic = read_traffic(args.workload,
+                           os.path.join(ROOT, "kv_cache_eviction_qk_amd", "csrc", "ring_step.hip"),
+                           kernel="ring_step", sha_key="source_sha256_16")
+    cpu = None if args.no_cpu_baseline else cpu_baseline_ring(case, cfg, fill)
+    out = {
+        "metric": "SnapKV ring-buffer decode steps: tokens/sec (ring weights + pooled ring sums "
+                  "+ drop + in-place overwrite per step)",
+        "value": B / (ms_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; 2% heavy hitters planted on the query direction)",
+        "config": {"workload": args.workload, "batch": B, "kv_heads": Hkv, "group": G,
+                   "head_dim": D, "budget": cfg.budget, "recent_window": cfg.recent,
+                   "obs_window": W, "pool_kernel": cfg.pool_kernel, "start_tokens": cfg.L,
+                   "null_steps": "every seventh step of a sequence", "block_size": 16},
+        "wall_s": wall,
+        "timing": "one HIP graph of the timed steps, replayed once",
+        "eager_ms_per_step": ms_eager,
+        "roofline": {"kernel": "ring_step_kernel (kvev_ring_step)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": step_bytes, "launch_ms": ms_step},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_ring(case, cfg, fill):
+    """The oracle's ring step on the host (one thread), for a bounded sample:
+    the fill steps untimed, then 12 dropping steps timed."""
+    import numpy as np
+
+    import oracle
+    import synth
+    st = oracle.ring_state(dict(case), cfg.W)
+
+    def one(i):
+        q, _ = synth.make_queries(cfg, 0, 1, case["dirs"], step=i)
+        k, v = synth.decode_token_kv(case, i)
+        obs = np.array([int((i + b) % 7 != 3) for b in range(cfg.B)], np.int32)
+        return oracle.ring_step(st, q.reshape(cfg.B, cfg.Hq, cfg.D), k, v,
+                                np.full(cfg.B, cfg.L + i, np.int32), obs, cfg.budget, cfg.recent,
+                                cfg.pool_kernel)[0]
+    for i in range(fill):
+        st = one(i)
+    n = 12
+    t0 = time.perf_counter()
+    for i in range(fill, fill + n):
+        st = one(i)
+    dt = time.perf_counter() - t0
+    return {"value": cfg.B * n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} dropping steps of all {cfg.B * cfg.Hkv} KV heads at {cfg.budget} "
+                      f"tokens; {dt:.1f} s"}
 
 
 def _vtok_bytes(U, rows, nsrc, alloc_blocks, row_bytes):

@@ -205,6 +205,11 @@ CONFIGS = {
     "h2o_stream_870": Config("h2o_stream_870", B=8, Hkv=8, G=4, D=128, L=806, W=1, dtype="bf16",
                              recipe="heavy_hitters", flags=("sum",), decode_steps=256,
                              budget=870, recent=435, plant_frac=0.02, seed=1006),
+    # SnapKV's decode-time ring buffer on the H2O decode lifecycle's shape:
+    # obsWindow 32 (the field W), poolKernel 7, recent window 32, budget 870.
+    "snap_ring_870": Config("snap_ring_870", B=8, Hkv=8, G=4, D=128, L=806, W=32, dtype="bf16",
+                            recipe="heavy_hitters", flags=("pool",), pool_kernel=7,
+                            decode_steps=256, budget=870, recent=32, plant_frac=0.02, seed=1008),
     # vToken lazy reclamation on one layer of the block-aware shape: half of
     # every head's 64000 tokens marked dead by a uniform random policy (the 16
     # most recent protected), then one reclamation over each head's blocks.
