@@ -72,6 +72,8 @@ def lib():
         L.orc_fmix64.argtypes = [ctypes.c_uint64]
         L.orc_select_shared.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P]
         L.orc_select_budgets.argtypes = [P, P, i32, i32, P, P, P, P]
+        L.orc_vtok_sync.argtypes = [P, P, P, P, P, i32, i32, i32, i32, P, P, P]
+        L.orc_vtok_slot_mapping.argtypes = [P, P, P, P, i32, i32, i32, P, P, P]
         L.orc_ring_step.argtypes = [P, P, i32, i32, P, P, P, P, P, P, i32, i32, i32, i32, i32,
                                     P, P, P, P, P, ctypes.c_double, i32, i32, i32, i32, P, P, P]
         L.orc_fmix64.restype = ctypes.c_uint64
@@ -82,7 +84,7 @@ def lib():
         for f in (L.orc_lse_a, L.orc_score, L.orc_select, L.orc_compact, L.orc_measure,
                   L.orc_h2o_step, L.orc_vtok_evict, L.orc_vtok_reclaim, L.orc_vtok_digest,
                   L.orc_vtok_check, L.orc_select_shared, L.orc_select_budgets,
-                  L.orc_ring_step):
+                  L.orc_ring_step, L.orc_vtok_sync, L.orc_vtok_slot_mapping):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -417,3 +419,37 @@ def ring_step(state: dict, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
     if rc != 0:
         raise ValueError(f"oracle ring_step refused the arguments (rc={rc})")
     return new, ev, fl, int(fc[0])
+
+
+def vtok_sync(state: dict, new_len: np.ndarray, pos0: np.ndarray):
+    """sync_new_tokens on a COPY of a vToken state: slots [seq_len, new_len)
+    become live at positions pos0[b] + k.  Returns (new_state, status [B,Hkv])."""
+    new = dict(state)
+    for k in ("seq_len", "pos", "live", "block_live"):
+        new[k] = np.ascontiguousarray(state[k]).copy()
+    B, Hkv = state["B"], state["Hkv"]
+    stat = np.zeros((B, Hkv), np.int32)
+    rc = lib().orc_vtok_sync(_p(np.ascontiguousarray(state["block_table"], dtype=np.int32)),
+                             _p(new["seq_len"]), _p(new["pos"]), _p(new["live"]),
+                             _p(new["block_live"]), B, Hkv, state["max_blocks"],
+                             state["num_blocks"], _p(np.ascontiguousarray(new_len, dtype=np.int32)),
+                             _p(np.ascontiguousarray(pos0, dtype=np.int32)), _p(stat))
+    assert rc == 0
+    return new, stat
+
+
+def vtok_slot_mapping(state: dict):
+    """Eq. 2 for every live token, in logical order: (slots [B,Hkv,max_slots],
+    positions [B,Hkv,max_slots], count [B,Hkv])."""
+    B, Hkv, mb = state["B"], state["Hkv"], state["max_blocks"]
+    slots = np.full((B, Hkv, mb * 16), -1, np.int32)
+    positions = np.full((B, Hkv, mb * 16), -1, np.int32)
+    count = np.zeros((B, Hkv), np.int32)
+    rc = lib().orc_vtok_slot_mapping(_p(np.ascontiguousarray(state["block_table"], dtype=np.int32)),
+                                     _p(np.ascontiguousarray(state["seq_len"], dtype=np.int32)),
+                                     _p(np.ascontiguousarray(state["pos"], dtype=np.int32)),
+                                     _p(np.ascontiguousarray(state["live"], dtype=np.uint8)),
+                                     B * Hkv, mb, state["num_blocks"], _p(slots), _p(positions),
+                                     _p(count))
+    assert rc == 0
+    return slots, positions, count

@@ -1070,3 +1070,63 @@ int orc_ring_step(void *k_pool, void *v_pool, int32_t is_bf16, int32_t head_dim,
   free(s);
   return 0;
 }
+
+
+/* ---- vToken's sync_new_tokens and slot mapping ([VTOK] section 3.2, Eq. 2) ---- */
+
+int orc_vtok_sync(const int32_t *block_table, int32_t *seq_len, int32_t *pos, uint8_t *live,
+                  int32_t *block_live, int32_t batch, int32_t kv_heads, int32_t max_blocks,
+                  int32_t num_blocks, const int32_t *new_len, const int32_t *pos0,
+                  int32_t *status) {
+  if (!block_table || !seq_len || !pos || !live || !block_live || !new_len || !pos0 || !status)
+    return -1;
+  const int64_t max_slots = (int64_t)max_blocks * 16;
+  for (int64_t u = 0; u < (int64_t)batch * kv_heads; ++u) {
+    const int64_t b = u / kv_heads, n = seq_len[u], m = new_len[u];
+    const int32_t *bt = block_table + u * max_blocks;
+    if (n < 0 || m < n || m > max_slots) {
+      status[u] = -2;
+      continue;
+    }
+    int bad = 0;
+    for (int64_t s = n; s < m; ++s)
+      if (bt[s / 16] < 0 || bt[s / 16] >= num_blocks) bad = 1;
+    if (bad) {
+      status[u] = -4;
+      continue;
+    }
+    for (int64_t s = n; s < m; ++s) {
+      live[u * max_slots + s] = 1;
+      pos[u * max_slots + s] = (int32_t)(pos0[b] + (s - n));
+      block_live[u * max_blocks + s / 16] += 1;
+    }
+    seq_len[u] = (int32_t)m;
+    status[u] = 0;
+  }
+  return 0;
+}
+
+int orc_vtok_slot_mapping(const int32_t *block_table, const int32_t *seq_len, const int32_t *pos,
+                          const uint8_t *live, int32_t units, int32_t max_blocks,
+                          int32_t num_blocks, int32_t *slots, int32_t *positions,
+                          int32_t *count) {
+  if (!block_table || !seq_len || !pos || !live || !slots || !positions || !count) return -1;
+  const int64_t max_slots = (int64_t)max_blocks * 16;
+  for (int64_t u = 0; u < units; ++u) {
+    const int64_t n = seq_len[u];
+    if (n < 0 || n > max_slots) {
+      count[u] = -1;
+      continue;
+    }
+    int64_t k = 0;
+    for (int64_t s = 0; s < n; ++s) {
+      const int64_t blk = block_table[u * max_blocks + s / 16];
+      if (blk < 0 || blk >= num_blocks || !live[u * max_slots + s]) continue;
+      slots[u * max_slots + k] = (int32_t)(blk * 16 + s % 16); /* Eq. 2 */
+      positions[u * max_slots + k] = pos[u * max_slots + s];
+      ++k;
+    }
+    count[u] = (int32_t)k;
+  }
+  return 0;
+}

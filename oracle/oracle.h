@@ -206,6 +206,30 @@ int orc_vtok_reclaim(void *k_pool, void *v_pool, int32_t elem_bytes, int32_t hea
                      int32_t *free_list, int32_t *free_count, int32_t free_capacity,
                      int64_t *stats);
 
+/* vToken's sync_new_tokens ([VTOK] section 3.2: the scheduler passes the
+ * current block list and length; the table gives the new tokens sequential
+ * logical IDs at their physical positions).  For every head u with
+ * n = seq_len[u] and m = new_len[u]: the slots [n, m) become live, slot s
+ * takes position pos0[b] + (s - n), each block's live count grows by its new
+ * slots, and seq_len[u] = m.  status[u] = 0, or -2 (m < n or m above the
+ * capacity), -4 (a block of [n, m) without an id in [0, num_blocks)); a head
+ * with a nonzero status is left unchanged.  Returns 0 or -1. */
+int orc_vtok_sync(const int32_t *block_table, int32_t *seq_len, int32_t *pos, uint8_t *live,
+                  int32_t *block_live, int32_t batch, int32_t kv_heads, int32_t max_blocks,
+                  int32_t num_blocks, const int32_t *new_len, const int32_t *pos0,
+                  int32_t *status);
+
+/* vToken's BuildSlotMapping ([VTOK] Eq. 2 and Algorithm 1, step 4): for every
+ * head, the live tokens below seq_len in logical order, each as its physical
+ * slot block_id * 16 + offset (slots [units][max_slots]) and its position
+ * (positions [units][max_slots]); count[u] of them.  Slots in blocks without
+ * an id in [0, num_blocks) are skipped; a seq_len outside [0, max_slots]
+ * gives count -1.  Returns 0 or -1. */
+int orc_vtok_slot_mapping(const int32_t *block_table, const int32_t *seq_len, const int32_t *pos,
+                          const uint8_t *live, int32_t units, int32_t max_blocks,
+                          int32_t num_blocks, int32_t *slots, int32_t *positions,
+                          int32_t *count);
+
 /* The online checks of I1 and I2 ([VTOK] section 3.5: token conservation and
  * unique mapping are verified at every relocation by hashing and comparing).
  *

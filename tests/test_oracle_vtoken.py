@@ -328,3 +328,62 @@ def test_check_counts_every_kind_of_fault():
     fl_bad[0] = -7
     assert oracle.vtok_check(st, fl_bad, fc).tolist() == [0, 1, 1, 0]
     assert oracle.vtok_check(st, fl, fc - 1).tolist() == [0, 1, 0, 0]
+
+
+# --------------------------------------- sync_new_tokens and slot mapping
+
+
+def test_slot_mapping_is_eq2_on_a_dense_head_and_skips_dead_slots():
+    st, fl, fc = _state([[16, 16, 9]])
+    st["seq_len"][0, 0] = 41
+    st["live"][0, 0, 32:41] = 1
+    st["block_live"][0, 0, 2] = 9
+    slots, positions, count = oracle.vtok_slot_mapping(st)
+    bt = st["block_table"][0, 0]
+    want = [int(bt[s // 16]) * 16 + s % 16 for s in range(41)]   # Eq. 2
+    assert count[0, 0] == 41 and slots[0, 0, :41].tolist() == want
+    assert positions[0, 0, :41].tolist() == st["pos"][0, 0, :41].tolist()
+    vic = np.full((1, 1, 48), -1, np.int32)
+    vic[0, 0, :3] = [0, 17, 40]
+    new, _ = oracle.vtok_evict(st, vic, np.array([[3]], np.int32))
+    s2, p2, c2 = oracle.vtok_slot_mapping(new)
+    keep = [s for s in range(41) if s not in (0, 17, 40)]
+    assert c2[0, 0] == 38 and s2[0, 0, :38].tolist() == [want[s] for s in keep]
+
+
+def test_slot_mapping_reads_the_live_tokens_after_reclamation():
+    r = rng(12)
+    fills = [list(r.integers(0, 17, size=7)) for _ in range(3)]
+    st, fl, fc = _state(fills, spare=30)
+    new, _, _, stats = oracle.vtok_reclaim(st, 0.0, 8, fl, fc)
+    assert stats[0] > 0
+    slots, positions, count = oracle.vtok_slot_mapping(new)
+    for h in range(3):
+        got = [(int(positions[0, h, k]),
+                new["k_pool"].reshape(-1, new["D"])[slots[0, h, k]].tobytes(),
+                new["v_pool"].reshape(-1, new["D"])[slots[0, h, k]].tobytes())
+               for k in range(count[0, h])]
+        assert got == _live_tokens(new, h)                  # logical order, through Eq. 2
+        assert sorted(got) == sorted(_live_tokens(st, h))   # and the same tokens as before
+
+
+def test_sync_registers_new_tokens():
+    st, fl, fc = _state([[16, 5], [16, 16, 16]])
+    st["seq_len"][0] = [21, 48]
+    new, status = oracle.vtok_sync(st, np.array([[30, 48]], np.int32), np.array([100], np.int32))
+    assert status.tolist() == [[0, 0]]
+    assert new["seq_len"][0].tolist() == [30, 48]
+    assert new["live"][0, 0, 21:30].all() and new["block_live"][0, 0, 1] == 5 + 9
+    assert new["pos"][0, 0, 21:30].tolist() == list(range(100, 109))
+    assert np.array_equal(new["pos"][0, 1], st["pos"][0, 1])        # nothing new
+    # then marked dead, the counts return: sync and evict are inverse on counts
+    vic = np.full((1, 2, 48), -1, np.int32)
+    vic[0, 0, :9] = np.arange(21, 30)
+    back, s2 = oracle.vtok_evict(new, vic, np.array([[9, 0]], np.int32))
+    assert s2 == 0 and np.array_equal(back["block_live"], st["block_live"])
+    # a shrinking length, one past the capacity, a block without an id
+    bad, status = oracle.vtok_sync(st, np.array([[20, 49]], np.int32), np.array([0], np.int32))
+    assert status.tolist() == [[-2, -2]] and np.array_equal(bad["live"], st["live"])
+    st["block_table"][0, 0, 1] = -1
+    bad, status = oracle.vtok_sync(st, np.array([[25, 48]], np.int32), np.array([0], np.int32))
+    assert status.tolist() == [[-4, 0]]
