@@ -747,10 +747,16 @@ def bench_vtok(args, cfg):
     c2.record()
     chk = K.vtok_check(cache, live, bl, fl, fc, cws)
     c3.record()
+    m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    m0.record()
+    _, _, mcount = K.vtok_slot_mapping(cache, live)
+    m1.record()
     torch.cuda.synchronize()
     online = {"I1_digests_equal": bool(torch.equal(dig0, dig1)),
               "I2_check": chk.cpu().tolist(), "digest_ms": c0.elapsed_time(c1),
-              "check_ms": c2.elapsed_time(c3)}
+              "check_ms": c2.elapsed_time(c3), "slot_mapping_ms": m0.elapsed_time(m1),
+              "mapped_tokens": int(mcount.sum().item())}
+    assert online["mapped_tokens"] == U * cfg.budget, online
     assert online["I1_digests_equal"] and online["I2_check"] == [0, 0, 0, 0], online
     st = stats.cpu().numpy()
     # the plan's sizes from the marks, on the host (accounting only), checked

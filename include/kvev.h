@@ -55,7 +55,7 @@ extern "C" {
 #endif
 
 #define KVEV_BLOCK_SIZE 16
-#define KVEV_ABI_VERSION 12
+#define KVEV_ABI_VERSION 13
 
 typedef enum {
   KVEV_OK = 0,
@@ -467,6 +467,39 @@ int kvev_vtok_reclaim(const kvev_cache *cache, uint8_t *live, int32_t *block_liv
 
 /* Workspace bytes of kvev_vtok_reclaim; 0 for a bad cache or max_sources. */
 size_t kvev_vtok_workspace_bytes(const kvev_cache *cache, int32_t max_sources);
+
+/*
+ * kvev_vtok_sync -- vToken's sync_new_tokens ([VTOK] section 3.2: the
+ * scheduler passes the current block list and length; the table registers
+ * the new tokens at their physical positions with sequential logical IDs).
+ * For every head u with n = seq_len[u] and m = new_len[u] (int32
+ * [batch][kv_heads], device): the slots [n, m) become live, slot s takes
+ * position pos0[b] + (s - n) (pos0: int32 [batch], device), each block's
+ * live count grows by its new slots, and seq_len[u] = m.  The caller has
+ * already written the new K/V rows and the block ids of [n, m) (from its
+ * allocator).  status[u] (int32 [batch][kv_heads], device) = 0, -2 (m < n
+ * or m above the capacity) or -4 (a block of [n, m) without an id in
+ * [0, num_blocks)); a head with a nonzero status is left unchanged.  One
+ * workgroup per head on `stream`.
+ * Errors: KVEV_EINVAL for NULL pointers or a bad cache.
+ */
+int kvev_vtok_sync(const kvev_cache *cache, uint8_t *live, int32_t *block_live,
+                   const int32_t *new_len, const int32_t *pos0, int32_t *status, void *stream);
+
+/*
+ * kvev_vtok_slot_mapping -- vToken's BuildSlotMapping ([VTOK] Algorithm 1,
+ * step 4, and Eq. 2: slot = block_id * block_size + offset for every live
+ * token).  For every head, the live slots below seq_len in logical order go
+ * to slots (int32 [batch][kv_heads][max_blocks*16], the physical row of the
+ * pools) with their positions (same shape); count[u] (int32
+ * [batch][kv_heads]) of them, or -1 for a seq_len outside [0, max_blocks*16].
+ * Slots in blocks without an id in [0, num_blocks) are skipped.  An attention
+ * kernel reads a reclaimed head through this mapping.  One workgroup per head
+ * on `stream`.
+ * Errors: KVEV_EINVAL for NULL pointers or a bad cache.
+ */
+int kvev_vtok_slot_mapping(const kvev_cache *cache, const uint8_t *live, int32_t *slots,
+                           int32_t *positions, int32_t *count, void *stream);
 
 /*
  * kvev_vtok_digest -- the online check of vToken's I1, token conservation

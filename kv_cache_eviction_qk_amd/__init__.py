@@ -34,10 +34,10 @@ EXPORTS = ("kvev_score", "kvev_select", "kvev_compact", "kvev_evict", "kvev_meas
            "kvev_vtok_evict_workspace_bytes", "kvev_vtok_reclaim", "kvev_vtok_workspace_bytes",
            "kvev_vtok_digest", "kvev_vtok_check", "kvev_vtok_check_workspace_bytes",
            "kvev_select_shared", "kvev_select_shared_workspace_bytes", "kvev_select_budgets",
-           "kvev_ring_step", "kvev_ring_init",
+           "kvev_ring_step", "kvev_ring_init", "kvev_vtok_sync", "kvev_vtok_slot_mapping",
            "kvev_window_attn",
            "kvev_workspace_bytes", "kvev_strerror", "kvev_abi_version")
-ABI_VERSION = 12
+ABI_VERSION = 13
 
 
 class KvevError(RuntimeError):
@@ -98,6 +98,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kvev_ring_step.argtypes = [P, P, P, P, P, P, P, P, P, i32, ctypes.c_float, i32, i32, i32,
                                  i32, P, P, P, P]
     L.kvev_ring_init.argtypes = [P, P, P, P, i32, P]
+    L.kvev_vtok_sync.argtypes = [P, P, P, P, P, P, P]
+    L.kvev_vtok_slot_mapping.argtypes = [P, P, P, P, P, P]
     L.kvev_select_shared_workspace_bytes.argtypes = [P]
     L.kvev_select_shared_workspace_bytes.restype = sz
     L.kvev_vtok_check.argtypes = [P, P, P, P, P, i32, P, P, sz, P]
@@ -112,7 +114,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for f in (L.kvev_score, L.kvev_select, L.kvev_compact, L.kvev_evict, L.kvev_window_attn,
               L.kvev_measure, L.kvev_h2o_step, L.kvev_vtok_evict, L.kvev_vtok_reclaim,
               L.kvev_vtok_digest, L.kvev_vtok_check, L.kvev_select_shared,
-              L.kvev_select_budgets, L.kvev_ring_step, L.kvev_ring_init, L.kvev_abi_version):
+              L.kvev_select_budgets, L.kvev_ring_step, L.kvev_ring_init, L.kvev_vtok_sync,
+              L.kvev_vtok_slot_mapping, L.kvev_abi_version):
         f.restype = ctypes.c_int
     if L.kvev_abi_version() != ABI_VERSION:
         raise ImportError(f"{path} has ABI version {L.kvev_abi_version()}, expected "
@@ -553,6 +556,40 @@ def vtok_digest(cache: Cache, live: torch.Tensor, digest: Optional[torch.Tensor]
     _check(L.kvev_vtok_digest(ctypes.byref(c), _ptr(live), _ptr(digest), _stream(stream)),
            "kvev_vtok_digest")
     return digest
+
+
+def vtok_sync(cache: Cache, live: torch.Tensor, block_live: torch.Tensor, new_len: torch.Tensor,
+              pos0: torch.Tensor, status: Optional[torch.Tensor] = None, stream=None):
+    """kvev_vtok_sync: register the slots [seq_len, new_len) as live tokens at
+    positions pos0[b] + k.  Returns status int32 [B, Hkv]."""
+    L = load_library()
+    c = cache.struct()
+    B, Hkv = cache.batch, cache.kv_heads
+    _need(live, "live", torch.uint8, B * Hkv * cache.max_slots)
+    _need(block_live, "block_live", torch.int32, B * Hkv * cache.max_blocks)
+    _need(new_len, "new_len", torch.int32, B * Hkv)
+    _need(pos0, "pos0", torch.int32, B)
+    if status is None:
+        status = torch.empty((B, Hkv), dtype=torch.int32, device=live.device)
+    _need(status, "status", torch.int32, B * Hkv)
+    _check(L.kvev_vtok_sync(ctypes.byref(c), _ptr(live), _ptr(block_live), _ptr(new_len),
+                            _ptr(pos0), _ptr(status), _stream(stream)), "kvev_vtok_sync")
+    return status
+
+
+def vtok_slot_mapping(cache: Cache, live: torch.Tensor, stream=None):
+    """kvev_vtok_slot_mapping -> (slots, positions int32 [B, Hkv, max_slots],
+    count int32 [B, Hkv]): every live token's physical row by Eq. 2."""
+    L = load_library()
+    c = cache.struct()
+    B, Hkv = cache.batch, cache.kv_heads
+    _need(live, "live", torch.uint8, B * Hkv * cache.max_slots)
+    slots = torch.empty((B, Hkv, cache.max_slots), dtype=torch.int32, device=live.device)
+    positions = torch.empty_like(slots)
+    count = torch.empty((B, Hkv), dtype=torch.int32, device=live.device)
+    _check(L.kvev_vtok_slot_mapping(ctypes.byref(c), _ptr(live), _ptr(slots), _ptr(positions),
+                                    _ptr(count), _stream(stream)), "kvev_vtok_slot_mapping")
+    return slots, positions, count
 
 
 def new_vtok_check_workspace(cache: Cache) -> torch.Tensor:

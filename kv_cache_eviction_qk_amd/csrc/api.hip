@@ -448,6 +448,7 @@ kvev::VtokArgs vtok_args(const kvev_cache *cache, uint8_t *live, int32_t *block_
   a.live = live;
   a.block_live = block_live;
   a.units = cache->batch * cache->kv_heads;
+  a.Hkv = cache->kv_heads;
   a.max_blocks = cache->max_blocks;
   a.max_slots = cache->max_blocks * KVEV_BLOCK_SIZE;
   a.num_blocks = cache->num_blocks;
@@ -839,6 +840,28 @@ int kvev_ring_step(const kvev_cache *cache, float *hist, int32_t *ring, int32_t 
   a.c1 = scale * 1.4426950408889634f;
   return map_err(kvev::launch_ring_step(a, cache->dtype == KVEV_BF16, cache->head_dim,
                                         static_cast<hipStream_t>(stream)));
+}
+
+
+int kvev_vtok_sync(const kvev_cache *cache, uint8_t *live, int32_t *block_live,
+                   const int32_t *new_len, const int32_t *pos0, int32_t *status, void *stream) {
+  if (!valid_cache(cache) || !live || !block_live || !new_len || !pos0 || !status)
+    return KVEV_EINVAL;
+  kvev::VtokArgs a = vtok_args(cache, live, block_live);
+  a.new_len = new_len;
+  a.pos0 = pos0;
+  a.status = status;
+  return map_err(kvev::launch_vtok_sync(a, static_cast<hipStream_t>(stream)));
+}
+
+int kvev_vtok_slot_mapping(const kvev_cache *cache, const uint8_t *live, int32_t *slots,
+                           int32_t *positions, int32_t *count, void *stream) {
+  if (!valid_cache(cache) || !live || !slots || !positions || !count) return KVEV_EINVAL;
+  kvev::VtokArgs a = vtok_args(cache, const_cast<uint8_t *>(live), nullptr);
+  a.map_slots = slots;
+  a.map_pos = positions;
+  a.map_count = count;
+  return map_err(kvev::launch_vtok_slot_mapping(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

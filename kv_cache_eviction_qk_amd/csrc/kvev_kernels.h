@@ -117,7 +117,7 @@ size_t h2o_lds_bytes(const H2oArgs &a, int head_dim);  // dynamic LDS of one wor
 struct VtokArgs {
   uint8_t *k_pool, *v_pool;
   int32_t *block_table;
-  const int32_t *seq_len;
+  int32_t *seq_len;                    // written by sync_new_tokens only
   int32_t *pos;
   float *score;                        // optional score row moved with the tokens
   uint8_t *live;                       // [units][max_slots] liveness bytes
@@ -133,12 +133,18 @@ struct VtokArgs {
   // [units][max_slots]
   int32_t *plan, *src, *srcoff, *dstw, *dst_off, *push_off, *tpos, *misc, *claim;
   float *tscore;
-  int32_t units, max_blocks, max_slots, num_blocks, row_bytes, max_sources, free_capacity;
+  // sync_new_tokens: new lengths [units], first positions [B]; slot mapping
+  // outputs: slots and positions [units][max_slots], counts [units]
+  const int32_t *new_len, *pos0;
+  int32_t *map_slots, *map_pos, *map_count;
+  int32_t units, Hkv, max_blocks, max_slots, num_blocks, row_bytes, max_sources, free_capacity;
   double theta_f;
 };
 hipError_t launch_vtok_evict(const VtokArgs &a, hipStream_t s);
 hipError_t launch_vtok_reclaim(const VtokArgs &a, hipStream_t s);
 hipError_t launch_vtok_digest(const VtokArgs &a, uint64_t *digest, hipStream_t s);
+hipError_t launch_vtok_sync(const VtokArgs &a, hipStream_t s);
+hipError_t launch_vtok_slot_mapping(const VtokArgs &a, hipStream_t s);
 hipError_t launch_vtok_check(const VtokArgs &a, int32_t *held, int64_t *out, hipStream_t s);
 
 // Shared scores across the KV heads of a sequence (policy.hip).

@@ -499,6 +499,95 @@ hipError_t launch_vtok_reclaim(const VtokArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------- sync_new_tokens and slot mapping
+
+// [VTOK] section 3.2, sync_new_tokens: the slots [seq_len, new_len) of a head
+// become live at sequential positions; each block's live count grows by its
+// new slots.  One workgroup per head.
+__global__ __launch_bounds__(256) void vtok_sync_kernel(const VtokArgs P) {
+  __shared__ int s_bad;
+  const int u = blockIdx.x, b = u / P.Hkv, tid = threadIdx.x;
+  const int n = P.seq_len[u], m = P.new_len[u];
+  if (n < 0 || m < n || m > P.max_slots) {
+    if (tid == 0) P.status[u] = -2;
+    return;
+  }
+  const int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  const int lb0 = n / kBlock, lb1 = (m + kBlock - 1) / kBlock;  // blocks touched
+  for (int lb = lb0 + tid; lb < lb1; lb += 256) {
+    const int e = bt[lb];
+    if (e < 0 || e >= P.num_blocks) s_bad = 1;
+  }
+  __syncthreads();
+  if (s_bad) {
+    if (tid == 0) P.status[u] = -4;
+    return;
+  }
+  const size_t urow = (size_t)u * P.max_slots;
+  const int p0 = P.pos0[b];
+  for (int s = n + tid; s < m; s += 256) {
+    P.live[urow + s] = 1;
+    P.pos[urow + s] = p0 + (s - n);
+  }
+  for (int lb = lb0 + tid; lb < lb1; lb += 256)
+    P.block_live[(size_t)u * P.max_blocks + lb] += min(m, (lb + 1) * kBlock) - max(n, lb * kBlock);
+  if (tid == 0) {
+    P.seq_len[u] = m;
+    P.status[u] = 0;
+  }
+}
+
+hipError_t launch_vtok_sync(const VtokArgs &a, hipStream_t s) {
+  if (a.units == 0) return hipSuccess;
+  hipLaunchKernelGGL(vtok_sync_kernel, dim3((unsigned)a.units), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// [VTOK] Algorithm 1, step 4, and Eq. 2: every live token's physical slot
+// (block id * 16 + offset) and position, in logical order.  One workgroup
+// per head; a block-wide scan ranks the live slots of each 1024-slot chunk.
+constexpr int kMapThreads = 1024;
+__global__ __launch_bounds__(kMapThreads) void vtok_map_kernel(const VtokArgs P) {
+  __shared__ int wave_tot[kMapThreads / kWave];
+  __shared__ int s_tot;
+  const int u = blockIdx.x, tid = threadIdx.x;
+  const int n = P.seq_len[u];
+  if (n < 0 || n > P.max_slots) {
+    if (tid == 0) P.map_count[u] = -1;
+    return;
+  }
+  const int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
+  const size_t urow = (size_t)u * P.max_slots;
+  int base = 0;
+  for (int s0 = 0; s0 < n; s0 += kMapThreads) {
+    const int s = s0 + tid;
+    int e = -1;
+    bool ok = false;
+    if (s < n) {
+      e = bt[s / kBlock];
+      ok = e >= 0 && e < P.num_blocks && P.live[urow + s] != 0;
+    }
+    const int rank = wg_excl_scan(ok ? 1 : 0, wave_tot);
+    if (ok) {
+      P.map_slots[urow + base + rank] = e * kBlock + s % kBlock;  // Eq. 2
+      P.map_pos[urow + base + rank] = P.pos[urow + s];
+    }
+    if (tid == kMapThreads - 1) s_tot = base + rank + (ok ? 1 : 0);
+    __syncthreads();
+    base = s_tot;
+    __syncthreads();
+  }
+  if (tid == 0) P.map_count[u] = base;
+}
+
+hipError_t launch_vtok_slot_mapping(const VtokArgs &a, hipStream_t s) {
+  if (a.units == 0) return hipSuccess;
+  hipLaunchKernelGGL(vtok_map_kernel, dim3((unsigned)a.units), dim3(kMapThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------- online checks (I1, I2)
 
 namespace {

@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
     assert set(names) == set(K.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvev_abi_version() == K.ABI_VERSION == 12
+    assert L.kvev_abi_version() == K.ABI_VERSION == 13
     for code in (0, -1, -2, -3, -4):
         assert K.strerror(code)
 
@@ -429,3 +429,19 @@ def test_ring_step_refusals():
     assert call(pool=131) == K.EUNSUPPORTED
     assert L.kvev_ring_init(ctypes.byref(c), None, FAKE, FAKE, 4, None) == K.EINVAL
     assert L.kvev_ring_init(ctypes.byref(c), FAKE, FAKE, FAKE, 0, None) == K.EINVAL
+
+
+def test_vtok_sync_and_mapping_refusals():
+    L = K.load_library()
+    c = cache(max_blocks=8)
+    for i in range(5):
+        p = [FAKE] * 5
+        p[i] = None
+        assert L.kvev_vtok_sync(ctypes.byref(c), *p, None) == K.EINVAL, i
+    for i in range(4):
+        p = [FAKE] * 4
+        p[i] = None
+        assert L.kvev_vtok_slot_mapping(ctypes.byref(c), *p, None) == K.EINVAL, i
+    bad = cache(head_dim=96)
+    assert L.kvev_vtok_sync(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, None) == K.EINVAL
+    assert L.kvev_vtok_slot_mapping(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None) == K.EINVAL

@@ -294,6 +294,59 @@ def test_reclaim_on_a_relocation_stream():
     assert ost[0] > 0
 
 
+# ------------------------------------- sync_new_tokens and slot mapping
+
+
+def test_sync_bit_exact():
+    st, fl, fc = _state(71, B=2, Hkv=4, max_blocks=20, spare=200, holes=False)
+    r = rng(72)
+    U, ms = 8, 20 * 16
+    new_len = st["seq_len"].copy()
+    free = list(fl[:fc])
+    for u in range(U):
+        b, h = divmod(u, 4)
+        n = int(st["seq_len"][b, h])
+        m = min(ms, n + int(r.integers(0, 60)))
+        for lb in range((n + 15) // 16, (m + 15) // 16):   # the caller's allocator
+            st["block_table"][b, h, lb] = free.pop()
+        new_len[b, h] = m
+    new_len[0, 1] = int(st["seq_len"][0, 1]) - 1 if st["seq_len"][0, 1] > 0 else ms + 1  # -2
+    n6 = int(st["seq_len"][1, 2])
+    if n6 + 20 <= ms:                                   # a block without an id: -4
+        new_len[1, 2] = n6 + 20
+        st["block_table"][1, 2, (n6 + 19) // 16] = -1
+    pos0 = np.array([1000, 5000], np.int32)
+    d = Dev(st, fl, fc)
+    status = K.vtok_sync(d.c, d.live, d.block_live, dev(new_len), dev(pos0))
+    o, ostat = oracle.vtok_sync(st, new_len, pos0)
+    torch.cuda.synchronize()
+    assert host(status).tolist() == ostat.tolist()
+    assert (ostat == 0).sum() >= 5 and (ostat == -2).sum() >= 1
+    assert np.array_equal(host(d.c.seq_len), o["seq_len"])
+    assert np.array_equal(host(d.c.pos), o["pos"])
+    assert np.array_equal(host(d.live), o["live"])
+    assert np.array_equal(host(d.block_live), o["block_live"])
+
+
+@pytest.mark.parametrize("seed", [80, 81])
+def test_slot_mapping_bit_exact_after_reclamation(seed):
+    st, fl, fc = _state(seed, B=2, Hkv=4, max_blocks=30, spare=150, bad=(("len", 6),))
+    d = Dev(st, fl, fc)
+    d.reclaim(0.1, 16)
+    g_slots, g_pos, g_cnt = K.vtok_slot_mapping(d.c, d.live)
+    o, _, _, _ = oracle.vtok_reclaim(st, 0.1, 16, fl, fc, with_score=True)
+    slots, positions, count = oracle.vtok_slot_mapping(o)
+    torch.cuda.synchronize()
+    gc = host(g_cnt)
+    assert np.array_equal(gc, count) and count[1, 2] == -1
+    gs, gp = host(g_slots), host(g_pos)
+    for b in range(2):
+        for h in range(4):
+            k = max(0, int(count[b, h]))
+            assert np.array_equal(gs[b, h, :k], slots[b, h, :k]), (b, h)
+            assert np.array_equal(gp[b, h, :k], positions[b, h, :k]), (b, h)
+
+
 # ---------------------------------------------- online checks of I1, I2
 
 
