@@ -186,6 +186,10 @@ class Cache:
         return self.k_pool.shape[-1]
 
     @property
+    def num_blocks(self) -> int:
+        return self.k_pool.shape[0]
+
+    @property
     def units(self) -> int:
         return self.batch * self.kv_heads
 
