@@ -8,7 +8,9 @@ eviction on one MI355X, on seeded synthetic inputs.
 kvev_h2o_step launch per decoded token of every sequence.  --workload
 vtok_reclaim_64k times vToken's liveness marks and lazy reclamation of one
 64000-token layer; --workload snap_ring_870 times SnapKV's decode-time ring
-buffer step.)
+buffer step; --workload h2o_decode_4k times H2O's decode-time accumulation:
+256 steps of accumulated scoring over a growing 4096-token cache, then one
+selection and compaction to the budget.)
 
 A step is the whole eviction path for one layer's cache: scoring (SnapKV
 window sum + max-pool over the last W prompt queries), selection (budget,
@@ -102,6 +104,8 @@ def main():
         return bench_vtok(args, cfg)
     if args.workload == "snap_ring_870":
         return bench_ring_stream(args, cfg)
+    if args.workload == "h2o_decode_4k":
+        return bench_decode_accumulate(args, cfg)
     if cfg.decode_steps:
         print(json.dumps({"error": f"{args.workload} is a decode schedule, not a one-shot pass"}))
         sys.exit(2)
@@ -475,6 +479,192 @@ def bench_h2o_stream(args, cfg):
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_decode_accumulate(args, cfg):
+    """H2O decode-time accumulation on the 4096-token decode shape (B8, 8 KV
+    heads x 4, D128, bf16): one schedule is 256 decode steps, each one
+    kvev_score launch (SUM | ACCUMULATE, one query row per head) over the
+    grown cache, then kvev_select and kvev_compact to the budget (870 tokens,
+    435 recent).  The step's LSE is the attention forward's output in a
+    model; here kvev_window_attn computes every step's LSE before the timed
+    region.  The cache holds every decoded token's row from the start; a
+    step's token joins by its length.  value = scored KV tokens (batch x
+    cached tokens, summed over the steps) per second."""
+    import numpy as np
+    import torch
+
+    import kv_cache_eviction_qk_amd as K
+    import synth
+
+    B, Hkv, G, D = cfg.B, cfg.Hkv, cfg.G, cfg.D
+    T = cfg.decode_steps
+    case = synth.make_case(cfg)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    cache = K.Cache(dev(case["k_pool"]), dev(case["v_pool"]), dev(case["block_table"]),
+                    dev(case["seq_len"]), dev(case["pos"]))
+    ws = K.new_workspace(cache, G, 1)
+    # one cache view per step (its own length tensor), so the steps need no
+    # copies between launches and the schedule can be captured as a graph
+    qs, qps, lses, views = [], [], [], []
+    for t in range(T):  # every step's query and LSE resident before the timed region
+        q, qp = synth.make_queries(cfg, 0, 1, case["dirs"], step=t)
+        qs.append(dev(q))
+        qps.append(dev(qp))
+        n_t = torch.full((B, Hkv), cfg.L + t + 1, dtype=torch.int32, device="cuda")
+        views.append(K.Cache(cache.k_pool, cache.v_pool, cache.block_table, n_t, cache.pos))
+        lse, _ = K.window_attn(views[-1], qs[-1], qps[-1], cfg.softmax_scale, G, ws)
+        lses.append(lse.clone())
+    final_len = torch.full((B, Hkv), cfg.L_final, dtype=torch.int32, device="cuda")
+    final = K.Cache(cache.k_pool, cache.v_pool, cache.block_table, final_len, cache.pos)
+    torch.cuda.synchronize()
+    score = cache.score_buffer()
+    state = (cache.k_pool, cache.v_pool, cache.block_table, cache.pos, final_len)
+    snap = [t.clone() for t in state]
+    free_list = torch.full((case["num_blocks"] + 8,), -1, dtype=torch.int32, device="cuda")
+    free_count = torch.zeros(1, dtype=torch.int32, device="cuda")
+    vic = torch.empty((B, Hkv, cache.max_slots), dtype=torch.int32, device="cuda")
+    nv = torch.empty((B, Hkv), dtype=torch.int32, device="cuda")
+    stats = torch.zeros(5, dtype=torch.int64, device="cuda")
+
+    def scoring():
+        score.zero_()
+        for t in range(T):
+            K.score(views[t], qs[t], lses[t], qps[t], cfg.softmax_scale, G, K.SUM | K.ACCUMULATE,
+                    1, sum=score)
+
+    def schedule():
+        scoring()
+        K.select(final, score, cfg.budget, cfg.recent, vic, nv, ws)
+        K.compact(final, vic, nv, free_list, free_count, ws, stats=stats, score_row=score)
+
+    def restore():
+        for t, v in zip(state, snap):
+            t.copy_(v)
+        free_count.zero_()
+
+    schedule()          # warm, and the selection's persistent state exercised once
+    restore()
+    torch.cuda.synchronize()
+    g_sched, g_score = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_sched):
+        schedule()
+    with torch.cuda.graph(g_score):
+        scoring()
+    torch.cuda.synchronize()
+    reps = max(1, min(args.steps, 5))
+    total_ms = wall = score_ms = 0.0
+    for _ in range(reps):
+        restore()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record()
+        g_sched.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        wall += time.perf_counter() - w0
+        total_ms += e0.elapsed_time(e1)
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        g_score.replay()
+        s1.record()
+        torch.cuda.synchronize()
+        score_ms += s0.elapsed_time(s1)
+    ms_sched = total_ms / reps
+    ms_score = score_ms / reps / T   # a score launch (plus the zero fill spread over the steps)
+    # the graph-replayed schedule matches an eager one
+    restore()
+    schedule()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (score, vic, nv, cache.k_pool, cache.pos)]
+    restore()
+    g_sched.replay()
+    torch.cuda.synchronize()
+    assert all(bool(torch.equal(a, b)) for a, b in zip(eager, (score, vic, nv, cache.k_pool,
+                                                              cache.pos))), "graph != eager"
+    st = stats.cpu().numpy()
+    assert int(st[4]) == 0 and int(nv.min()) == cfg.L_final - cfg.budget, (st, nv.min())
+    if args.profile_steps:
+        log(f"profile run done: {ms_sched:.3f} ms/schedule, score {ms_score * 1e3:.2f} us")
+        return
+    eb = 2 if cfg.dtype == "bf16" else 4
+    units = B * Hkv
+    scored = B * sum(cfg.L + t + 1 for t in range(T))
+    # one score launch at the mean length: K rows, positions, block ids, the
+    # score read and written (ACCUMULATE), the query rows and LSE
+    n_mean = sum(cfg.L + t + 1 for t in range(T)) / T
+    launch_bytes = (units * n_mean * (D * eb + 4 + 8) + units * math.ceil(n_mean / 16) * 4
+                    + B * cfg.Hq * D * eb + B * cfg.Hq * 4)
+    achieved = launch_bytes / (ms_score / 1e3) / 1e9
+    out = {
+        "metric": "H2O decode-time accumulation: scored KV tokens/sec (256 accumulated scoring "
+                  "steps + select + compact per schedule)",
+        "value": scored / (ms_sched / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": reps,
+        "warmup": max(1, args.warmup),
+        "ms_per_step": ms_sched,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; 2% heavy hitters planted on the query direction)",
+        "config": {"workload": args.workload, "batch": B, "kv_heads": Hkv, "group": G,
+                   "head_dim": D, "context": f"{cfg.L} -> {cfg.L_final}", "decode_steps": T,
+                   "budget": cfg.budget, "recent_window": cfg.recent, "score": "sum+accumulate",
+                   "block_size": 16},
+        "wall_s": wall,
+        "timing": "a step is one whole schedule (256 score launches, then select and compact) "
+                  "captured as one HIP graph and replayed between HIP events; the 256 score "
+                  "launches alone as a second graph for the per-launch time",
+        "score_launch_us": ms_score * 1e3,
+        "blocks_freed": int(st[0]),
+        "roofline": {"kernel": "score_kernel (kvev_score, SUM | ACCUMULATE, one query row)",
+                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": read_traffic(args.workload, os.path.join(
+                         ROOT, "kv_cache_eviction_qk_amd", "csrc", "score.hip"),
+                         kernel="score", sha_key="source_sha256_16"),
+                     "algorithmic_bytes": launch_bytes, "launch_ms": ms_score},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_decode(case, cfg),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_decode(case, cfg):
+    """The oracle's accumulated scoring on the host cores for a bounded
+    sample: the first 8 decode steps of the schedule (its own LSE per step,
+    excluded from the timing), every head."""
+    import numpy as np
+
+    import oracle
+    import synth
+    threads = oracle.default_threads()
+    B, Hkv = cfg.B, cfg.Hkv
+    acc = np.zeros((B, Hkv, case["max_blocks"] * 16), np.float32)
+    steps, scored, dt = 8, 0, 0.0
+    for t in range(steps):
+        n = cfg.L + t + 1
+        q, q_pos = synth.make_queries(cfg, 0, 1, case["dirs"], step=t)
+        st = dict(case, seq_len=np.full((B, Hkv), n, np.int32), q=q, q_pos=q_pos, W=1)
+        lse64, _ = oracle.lse_a(st, nthreads=threads)
+        t0 = time.perf_counter()
+        o = oracle.score(st, lse64.astype(np.float32), oracle.SUM | oracle.ACCUMULATE, 1,
+                         prev_sum=acc, nthreads=threads)["sum"]
+        dt += time.perf_counter() - t0
+        acc = np.nan_to_num(o, nan=0.0).astype(np.float32)
+        scored += B * n
+    return {"value": scored / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the first {steps} accumulated scoring steps of all {B * Hkv} KV heads; "
+                      f"{dt:.1f} s (select and compact not included)"}
 
 
 def bench_ring_stream(args, cfg):
