@@ -292,7 +292,10 @@ def main():
         cpu = cpu_baseline(case, cfg, kind)
 
     out = {
-        "metric": "scored KV tokens/sec (score+select+compact) at 32K ctx; % of peak HBM GB/s",
+        "metric": ("scored KV tokens/sec (score+select+compact) at 32K ctx; % of peak HBM GB/s"
+                   if args.workload == "snapkv_prefill_32k" else
+                   f"scored KV tokens/sec (score+select+compact) at {cfg.L} tokens; "
+                   "% of peak HBM GB/s"),
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -303,7 +306,11 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.dtype,
-        "data": "synthetic (seeded; spans planted on window-query directions)",
+        "data": {"spans": "synthetic (seeded; spans planted on window-query directions)",
+                 "heavy_hitters": "synthetic (seeded; 2% heavy hitters planted on the query "
+                                  "direction)",
+                 "near_mean": "synthetic (seeded; 10% near-mean value rows)",
+                 "iid": "synthetic (seeded; iid normal rows)"}[cfg.recipe],
         "config": {"workload": args.workload, "path": args.path, "batch": B, "kv_heads": Hkv,
                    "group": G,
                    "head_dim": D, "context": n, "obs_window": W, "pool_kernel": cfg.pool_kernel,
