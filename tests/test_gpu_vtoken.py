@@ -442,3 +442,90 @@ def test_full_size_random_eviction_layer():
     assert np.array_equal(kp[dest], o["k_pool"][dest]) and np.array_equal(vp[dest], o["v_pool"][dest])
     assert np.array_equal(kp, o["k_pool"]) and np.array_equal(vp, o["v_pool"])
     assert np.array_equal(after, oracle.vtok_digest(o))
+
+
+def test_algorithm1_runtime_loop():
+    """The review's Algorithm 1 as a loop of decode steps, GPU beside the
+    oracle: SyncNewTokens (one token a step), SelectVictims (a seeded random
+    policy over the live tokens outside a recent window of 8), EvictToken,
+    BuildSlotMapping, and every eighth step ReclaimAsync on a relocation stream
+    that the next step waits for through an event.  Every table, pool and
+    mapping is compared bit for bit at every step, and the online checks
+    (digests equal across each reclamation, the block check clean) hold."""
+    B, Hkv, D, mb = 2, 2, 64, 24
+    st, fl, fc = _state(90, D=D, B=B, Hkv=Hkv, max_blocks=mb, spare=40, holes=False)
+    # every block of the capacity allocated up front (the allocator's job);
+    # the heads start at 100 live tokens
+    used = set(st["block_table"][st["block_table"] >= 0].tolist())
+    spare = [x for x in range(st["num_blocks"]) if x not in used]
+    for b in range(B):
+        for h in range(Hkv):
+            for lb in range(mb):
+                if st["block_table"][b, h, lb] < 0:
+                    st["block_table"][b, h, lb] = spare.pop()
+    st["seq_len"][:] = 0
+    st["live"][:] = 0
+    st["block_live"][:] = 0
+    st, s0 = oracle.vtok_sync(st, np.full((B, Hkv), 100, np.int32), np.zeros(B, np.int32))
+    assert (s0 == 0).all()
+    fl = np.full(st["num_blocks"], -1, np.int32)
+    fl[:len(spare)] = spare
+    fc = len(spare)
+    d = Dev(st, fl, fc)
+    ws = K.new_vtok_workspace(d.c, 8)
+    cws = K.new_vtok_check_workspace(d.c)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    r = rng(91)
+    for step in range(40):
+        t = 100 + step
+        n = st["seq_len"].copy()
+        # 1. SyncNewTokens
+        K.vtok_sync(d.c, d.live, d.block_live, dev(n + 1), dev(np.full(B, t, np.int32)))
+        st, ss = oracle.vtok_sync(st, n + 1, np.full(B, t, np.int32))
+        assert (ss == 0).all()
+        # 2-3. SelectVictims (random policy) and EvictToken
+        vic = np.full((B, Hkv, mb * 16), -1, np.int32)
+        nv = np.zeros((B, Hkv), np.int32)
+        for b in range(B):
+            for h in range(Hkv):
+                m = int(st["seq_len"][b, h])
+                ok = np.flatnonzero((st["live"][b, h, :m] != 0) & (st["pos"][b, h, :m] <= t - 8)
+                                    & (st["block_table"][b, h, np.arange(m) // 16] >= 0))
+                k = int(r.integers(0, 3))
+                pick = r.choice(ok, size=min(k, ok.size), replace=False) if ok.size else []
+                vic[b, h, :len(pick)] = pick
+                nv[b, h] = len(pick)
+        d.evict(vic, nv)
+        st, es = oracle.vtok_evict(st, vic, nv)
+        assert es == 0
+        # 4. BuildSlotMapping
+        gs, gp, gc = K.vtok_slot_mapping(d.c, d.live)
+        os_, op, oc = oracle.vtok_slot_mapping(st)
+        assert np.array_equal(host(gc), oc)
+        for b in range(B):
+            for h in range(Hkv):
+                k = int(oc[b, h])
+                assert np.array_equal(host(gs)[b, h, :k], os_[b, h, :k])
+                assert np.array_equal(host(gp)[b, h, :k], op[b, h, :k])
+        # 5. ReclaimAsync on the relocation stream, after this step's work
+        if step % 8 == 7:
+            before = _digest(d)
+            ready = torch.cuda.Event()
+            ready.record(main)
+            side.wait_event(ready)
+            K.vtok_reclaim(d.c, d.live, d.block_live, 0.25, 8, d.fl, d.fc, ws, stream=side)
+            done = torch.cuda.Event()
+            done.record(side)
+            main.wait_event(done)   # the next step's reads wait on the GPU side only
+            st, fl, fc, ost = oracle.vtok_reclaim(st, 0.25, 8, fl, fc)
+            after = _digest(d)
+            chk = host(K.vtok_check(d.c, d.live, d.block_live, d.fl, d.fc, cws))
+            assert np.array_equal(before, after) and chk.tolist() == [0, 0, 0, 0]
+            _say(f"step {step}: reclaimed {ost[0]} heads, {ost[3]} blocks freed")
+        torch.cuda.synchronize()
+        g, gfl, gfc = d.state(st)
+        for key in ("block_table", "pos", "live", "block_live", "k_pool", "v_pool"):
+            assert np.array_equal(g[key], st[key]), (step, key)
+        assert np.array_equal(host(d.c.seq_len), st["seq_len"])
+        assert gfc == fc and np.array_equal(gfl[:gfc], fl[:fc]), step
