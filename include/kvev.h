@@ -55,7 +55,7 @@ extern "C" {
 #endif
 
 #define KVEV_BLOCK_SIZE 16
-#define KVEV_ABI_VERSION 13
+#define KVEV_ABI_VERSION 14
 
 typedef enum {
   KVEV_OK = 0,
@@ -494,12 +494,18 @@ int kvev_vtok_sync(const kvev_cache *cache, uint8_t *live, int32_t *block_live,
  * pools) with their positions (same shape); count[u] (int32
  * [batch][kv_heads]) of them, or -1 for a seq_len outside [0, max_blocks*16].
  * Slots in blocks without an id in [0, num_blocks) are skipped.  An attention
- * kernel reads a reclaimed head through this mapping.  One workgroup per head
- * on `stream`.
- * Errors: KVEV_EINVAL for NULL pointers or a bad cache.
+ * kernel reads a reclaimed head through this mapping.  Workspace:
+ * kvev_vtok_map_workspace_bytes (scratch: live slots per 4096-slot chunk).
+ * Two launches over 4096-slot chunks of every head on `stream`.
+ * Errors: KVEV_EINVAL for NULL pointers or a bad cache; KVEV_ENOSPACE for a
+ * missing or short workspace.
  */
 int kvev_vtok_slot_mapping(const kvev_cache *cache, const uint8_t *live, int32_t *slots,
-                           int32_t *positions, int32_t *count, void *stream);
+                           int32_t *positions, int32_t *count, void *workspace, size_t ws_bytes,
+                           void *stream);
+
+/* Workspace bytes of kvev_vtok_slot_mapping; 0 for a bad cache. */
+size_t kvev_vtok_map_workspace_bytes(const kvev_cache *cache);
 
 /*
  * kvev_vtok_digest -- the online check of vToken's I1, token conservation

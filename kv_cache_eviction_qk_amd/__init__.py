@@ -35,9 +35,10 @@ EXPORTS = ("kvev_score", "kvev_select", "kvev_compact", "kvev_evict", "kvev_meas
            "kvev_vtok_digest", "kvev_vtok_check", "kvev_vtok_check_workspace_bytes",
            "kvev_select_shared", "kvev_select_shared_workspace_bytes", "kvev_select_budgets",
            "kvev_ring_step", "kvev_ring_init", "kvev_vtok_sync", "kvev_vtok_slot_mapping",
+           "kvev_vtok_map_workspace_bytes",
            "kvev_window_attn",
            "kvev_workspace_bytes", "kvev_strerror", "kvev_abi_version")
-ABI_VERSION = 13
+ABI_VERSION = 14
 
 
 class KvevError(RuntimeError):
@@ -99,7 +100,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                  i32, P, P, P, P]
     L.kvev_ring_init.argtypes = [P, P, P, P, i32, P]
     L.kvev_vtok_sync.argtypes = [P, P, P, P, P, P, P]
-    L.kvev_vtok_slot_mapping.argtypes = [P, P, P, P, P, P]
+    L.kvev_vtok_slot_mapping.argtypes = [P, P, P, P, P, P, sz, P]
+    L.kvev_vtok_map_workspace_bytes.argtypes = [P]
+    L.kvev_vtok_map_workspace_bytes.restype = sz
     L.kvev_select_shared_workspace_bytes.argtypes = [P]
     L.kvev_select_shared_workspace_bytes.restype = sz
     L.kvev_vtok_check.argtypes = [P, P, P, P, P, i32, P, P, sz, P]
@@ -581,18 +584,24 @@ def vtok_sync(cache: Cache, live: torch.Tensor, block_live: torch.Tensor, new_le
     return status
 
 
-def vtok_slot_mapping(cache: Cache, live: torch.Tensor, stream=None):
+def vtok_slot_mapping(cache: Cache, live: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                      stream=None):
     """kvev_vtok_slot_mapping -> (slots, positions int32 [B, Hkv, max_slots],
     count int32 [B, Hkv]): every live token's physical row by Eq. 2."""
     L = load_library()
     c = cache.struct()
     B, Hkv = cache.batch, cache.kv_heads
     _need(live, "live", torch.uint8, B * Hkv * cache.max_slots)
+    if workspace is None:
+        workspace = torch.empty(L.kvev_vtok_map_workspace_bytes(ctypes.byref(c)),
+                                dtype=torch.uint8, device=live.device)
+    _need(workspace, "workspace", torch.uint8)
     slots = torch.empty((B, Hkv, cache.max_slots), dtype=torch.int32, device=live.device)
     positions = torch.empty_like(slots)
     count = torch.empty((B, Hkv), dtype=torch.int32, device=live.device)
     _check(L.kvev_vtok_slot_mapping(ctypes.byref(c), _ptr(live), _ptr(slots), _ptr(positions),
-                                    _ptr(count), _stream(stream)), "kvev_vtok_slot_mapping")
+                                    _ptr(count), _ptr(workspace), workspace.numel(),
+                                    _stream(stream)), "kvev_vtok_slot_mapping")
     return slots, positions, count
 
 

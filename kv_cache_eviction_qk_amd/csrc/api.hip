@@ -854,13 +854,23 @@ int kvev_vtok_sync(const kvev_cache *cache, uint8_t *live, int32_t *block_live,
   return map_err(kvev::launch_vtok_sync(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t kvev_vtok_map_workspace_bytes(const kvev_cache *cache) {
+  if (!valid_cache(cache)) return 0;
+  const size_t chunks = ((size_t)cache->max_blocks * KVEV_BLOCK_SIZE + 4095) / 4096;
+  return a256((size_t)cache->batch * cache->kv_heads * chunks * 4);
+}
+
 int kvev_vtok_slot_mapping(const kvev_cache *cache, const uint8_t *live, int32_t *slots,
-                           int32_t *positions, int32_t *count, void *stream) {
+                           int32_t *positions, int32_t *count, void *workspace, size_t ws_bytes,
+                           void *stream) {
   if (!valid_cache(cache) || !live || !slots || !positions || !count) return KVEV_EINVAL;
+  if (!workspace || ws_bytes < kvev_vtok_map_workspace_bytes(cache)) return KVEV_ENOSPACE;
   kvev::VtokArgs a = vtok_args(cache, const_cast<uint8_t *>(live), nullptr);
   a.map_slots = slots;
   a.map_pos = positions;
   a.map_count = count;
+  a.map_chunk = static_cast<int32_t *>(workspace);
+  a.map_chunks = (a.max_slots + 4095) / 4096;
   return map_err(kvev::launch_vtok_slot_mapping(a, static_cast<hipStream_t>(stream)));
 }
 

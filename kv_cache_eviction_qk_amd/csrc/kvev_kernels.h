@@ -137,6 +137,7 @@ struct VtokArgs {
   // outputs: slots and positions [units][max_slots], counts [units]
   const int32_t *new_len, *pos0;
   int32_t *map_slots, *map_pos, *map_count;
+  int32_t *map_chunk, map_chunks;      // workspace: live slots per 1024-slot chunk [units][chunks]
   int32_t units, Hkv, max_blocks, max_slots, num_blocks, row_bytes, max_sources, free_capacity;
   double theta_f;
 };

@@ -546,29 +546,69 @@ hipError_t launch_vtok_sync(const VtokArgs &a, hipStream_t s) {
 }
 
 // [VTOK] Algorithm 1, step 4, and Eq. 2: every live token's physical slot
-// (block id * 16 + offset) and position, in logical order.  One workgroup
-// per head; a block-wide scan ranks the live slots of each 1024-slot chunk.
+// (block id * 16 + offset) and position, in logical order.  Two launches over
+// chunks of kMapChunk slots of every head: the live count of each chunk, then
+// each chunk's offset (the counts before it) and block-wide scans that rank
+// its live slots, 1024 at a time.
 constexpr int kMapThreads = 1024;
-__global__ __launch_bounds__(kMapThreads) void vtok_map_kernel(const VtokArgs P) {
+constexpr int kMapChunk = 4 * kMapThreads;
+
+__device__ __forceinline__ bool map_live(const VtokArgs &P, int u, int s, int n, int &e) {
+  e = -1;
+  if (s >= n) return false;
+  e = P.block_table[(size_t)u * P.max_blocks + s / kBlock];
+  return e >= 0 && e < P.num_blocks && P.live[(size_t)u * P.max_slots + s] != 0;
+}
+
+__global__ __launch_bounds__(kMapThreads) void vtok_map_count_kernel(const VtokArgs P) {
+  __shared__ int s_cnt[kMapThreads / kWave];
+  const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
+  const int n = P.seq_len[u];
+  if (n < 0 || n > P.max_slots || c * kMapChunk >= n) return;
+  int w = 0;
+#pragma unroll
+  for (int q = 0; q < kMapChunk / kMapThreads; ++q) {
+    int e;
+    w += __popcll(__ballot(map_live(P, u, c * kMapChunk + q * kMapThreads + tid, n, e)));
+  }
+  if (lane_id() == 0) s_cnt[tid / kWave] = w;
+  __syncthreads();
+  if (tid == 0) {
+    int t = 0;
+    for (int q = 0; q < kMapThreads / kWave; ++q) t += s_cnt[q];
+    P.map_chunk[(size_t)u * P.map_chunks + c] = t;
+  }
+}
+
+__global__ __launch_bounds__(kMapThreads) void vtok_map_write_kernel(const VtokArgs P) {
   __shared__ int wave_tot[kMapThreads / kWave];
   __shared__ int s_tot;
-  const int u = blockIdx.x, tid = threadIdx.x;
+  const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
   const int n = P.seq_len[u];
   if (n < 0 || n > P.max_slots) {
-    if (tid == 0) P.map_count[u] = -1;
+    if (c == 0 && tid == 0) P.map_count[u] = -1;
     return;
   }
-  const int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
-  const size_t urow = (size_t)u * P.max_slots;
+  const int chunks = (n + kMapChunk - 1) / kMapChunk;
+  if (n == 0 && c == 0 && tid == 0) P.map_count[u] = 0;
+  if (c >= chunks) return;
+  // the live slots of the chunks before this one: a strided sum, reduced
+  // over the workgroup
+  const int32_t *cnt = P.map_chunk + (size_t)u * P.map_chunks;
+  int own = 0;
+  for (int q = tid; q < c; q += kMapThreads) own += cnt[q];
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) own += __shfl_xor(own, o);
+  if (lane_id() == 0) wave_tot[tid / kWave] = own;
+  __syncthreads();
   int base = 0;
-  for (int s0 = 0; s0 < n; s0 += kMapThreads) {
-    const int s = s0 + tid;
-    int e = -1;
-    bool ok = false;
-    if (s < n) {
-      e = bt[s / kBlock];
-      ok = e >= 0 && e < P.num_blocks && P.live[urow + s] != 0;
-    }
+  for (int w = 0; w < kMapThreads / kWave; ++w) base += wave_tot[w];
+  __syncthreads();  // wave_tot is the scans' next
+  const size_t urow = (size_t)u * P.max_slots;
+  for (int q = 0; q < kMapChunk / kMapThreads; ++q) {
+    int e;
+    const int s = c * kMapChunk + q * kMapThreads + tid;
+    const bool ok = map_live(P, u, s, n, e);
     const int rank = wg_excl_scan(ok ? 1 : 0, wave_tot);
     if (ok) {
       P.map_slots[urow + base + rank] = e * kBlock + s % kBlock;  // Eq. 2
@@ -579,12 +619,16 @@ __global__ __launch_bounds__(kMapThreads) void vtok_map_kernel(const VtokArgs P)
     base = s_tot;
     __syncthreads();
   }
-  if (tid == 0) P.map_count[u] = base;
+  if (c == chunks - 1 && tid == 0) P.map_count[u] = base;
 }
 
 hipError_t launch_vtok_slot_mapping(const VtokArgs &a, hipStream_t s) {
   if (a.units == 0) return hipSuccess;
-  hipLaunchKernelGGL(vtok_map_kernel, dim3((unsigned)a.units), dim3(kMapThreads), 0, s, a);
+  const dim3 grid((unsigned)a.map_chunks, (unsigned)a.units);
+  hipLaunchKernelGGL(vtok_map_count_kernel, grid, dim3(kMapThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(vtok_map_write_kernel, grid, dim3(kMapThreads), 0, s, a);
   return hipGetLastError();
 }
 

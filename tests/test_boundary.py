@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
     assert set(names) == set(K.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvev_abi_version() == K.ABI_VERSION == 13
+    assert L.kvev_abi_version() == K.ABI_VERSION == 14
     for code in (0, -1, -2, -3, -4):
         assert K.strerror(code)
 
@@ -441,7 +441,14 @@ def test_vtok_sync_and_mapping_refusals():
     for i in range(4):
         p = [FAKE] * 4
         p[i] = None
-        assert L.kvev_vtok_slot_mapping(ctypes.byref(c), *p, None) == K.EINVAL, i
+        assert L.kvev_vtok_slot_mapping(ctypes.byref(c), *p, FAKE, 1 << 20, None) == K.EINVAL, i
+    need = L.kvev_vtok_map_workspace_bytes(ctypes.byref(c))
+    assert need >= 2 * 2 * 4
+    assert L.kvev_vtok_slot_mapping(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, None, 1 << 20,
+                                    None) == K.ENOSPACE
+    assert L.kvev_vtok_slot_mapping(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
+                                    None) == K.ENOSPACE
     bad = cache(head_dim=96)
     assert L.kvev_vtok_sync(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, None) == K.EINVAL
-    assert L.kvev_vtok_slot_mapping(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None) == K.EINVAL
+    assert L.kvev_vtok_slot_mapping(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                                    None) == K.EINVAL
