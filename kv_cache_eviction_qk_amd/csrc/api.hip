@@ -324,7 +324,12 @@ int build_score_args(const kvev_cache *cache, const kvev_window *win, int32_t fl
   a.halo_blocks = (a.pool_r + KVEV_BLOCK_SIZE - 1) / KVEV_BLOCK_SIZE;
   // Up to 8 waves (512 threads) share one staging of the window rows and
   // split a tile of up to 256 blocks; smaller tiles when the tiles would not
-  // cover the 256 CUs or when the staged window rows plus the tile's score
+  // cover the 256 CUs, and down to two tiles per CU while what each tile
+  // stages besides its own keys (the window rows, with the attention output
+  // for DropKV, and the halo blocks) stays within a sixteenth of its key
+  // bytes (one CU pulls more bytes at once with two workgroups; a
+  // single-query decode window tiles finer, a 32-query prefill window does
+  // not); smaller again when the staged window rows plus the tile's score
   // rows exceed a workgroup's LDS (large G*W windows); fewer waves for small
   // tiles.
   const int bf16 = cache->dtype == KVEV_BF16;
@@ -334,7 +339,13 @@ int build_score_args(const kvev_cache *cache, const kvev_window *win, int32_t fl
                                  fused);
   };
   int tb = KV_TILE_MAX, threads = KV_THREADS_MAX;
-  while (tb > 16 && (int64_t)a.units * ((cache->max_blocks + tb - 1) / tb) < 256) tb /= 2;
+  auto tiles_of = [&](int t) { return (int64_t)a.units * ((cache->max_blocks + t - 1) / t); };
+  while (tb > 16 && tiles_of(tb) < 256) tb /= 2;
+  const int64_t row_bytes = (int64_t)cache->head_dim * (bf16 ? 2 : 4);
+  const int64_t block_bytes = (int64_t)KVEV_BLOCK_SIZE * row_bytes * (is_drop ? 2 : 1);
+  const int64_t staged = (int64_t)a.row_tiles * 16 * row_bytes * (is_drop ? 2 : 1) +
+                         2 * (int64_t)a.halo_blocks * block_bytes;
+  while (tb > 16 && tiles_of(tb) < 512 && staged * 16 <= (int64_t)(tb / 2) * block_bytes) tb /= 2;
   while (tb > 1 && lds_of(tb) > kMaxLds - 1024) tb /= 2;
   if (lds_of(tb) > kMaxLds - 1024) return KVEV_EUNSUPPORTED;
   while (threads > 256 && tb < 16 * (threads / 64)) threads /= 2;
