@@ -207,6 +207,10 @@ constexpr int kSelectMaxChunks = 1024;  // chunks per head: up to 1M slots
 constexpr int kHistChunk = 4096;        // slots per select histogram workgroup
 constexpr int kCompactMaxUnits = 4096;  // compact.hip gather limit
 constexpr int kCompactChunk = 1024;     // compact.hip prep chunk (slots)
+// The fused pass's prep reads the selection's per-chunk victim offsets by its
+// own chunk index, and packs a head's chunk arrivals into 11 bits.
+static_assert(kCompactChunk == kSelectChunk, "prep chunks must be the selection's chunks");
+static_assert(kSelectMaxChunks < 2048, "chunk arrivals are counted in 11 bits");
 constexpr int kH2oMaxBudget = 4096;    // h2o_step.hip: tokens per head
 constexpr int kH2oMaxLogits = 16384;   // h2o_step.hip: G * budget (64 KB of LDS)
 constexpr int kH2oMaxSplit = 8;        // h2o_step.hip: workgroups per head
