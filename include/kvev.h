@@ -235,18 +235,23 @@ int kvev_compact(const kvev_cache *cache, const int32_t *victims, const int32_t 
  * kvev_select on that score, then kvev_compact with the score as
  * score_or_null, with the same results as those three calls ([SNAP] "How it
  * works": score the window, keep the top budget, drop the rest; [VTOK]
- * section 3.3 for the repack).  Fused: the scoring pass also builds the
- * selection histogram and the last tile of each head finds the threshold,
- * and the compaction's first step marks the victims against it, so the
- * scores are not re-read to select them.
+ * section 3.3 for the repack).  Two launches: the scoring pass (which also
+ * builds each head's selection histogram), then one launch that finds each
+ * head's exact threshold, writes the victims and compacts the head in place
+ * without staging any row.
  * flags: exactly one of KVEV_SUM, KVEV_POOL, KVEV_DROP (KVEV_ACCUMULATE with
- * KVEV_SUM); score: fp32 [batch][kv_heads][max_blocks*16], 16-byte aligned, receives that kind
- * (with ACCUMULATE it holds the running sums on entry) and is compacted with
- * the tokens, so after the call its slots [0, n') hold the kept tokens'
- * scores.  victims, n_victims, free_list, free_count, stats: as written by
- * kvev_select and kvev_compact.  Errors: the union of those three calls'
- * (KVEV_EINVAL also for several score kinds in flags); workspace as for
- * kvev_compact.
+ * KVEV_SUM); score: fp32 [batch][kv_heads][max_blocks*16], 16-byte aligned.
+ * On entry it matters only with ACCUMULATE (the running sums).  On return its
+ * slots [0, n') hold the kept tokens' scores in their compacted order; its
+ * slots from n' on are unspecified.  victims, n_victims, free_list,
+ * free_count, stats: as written by kvev_select and kvev_compact (stats[3]
+ * counts the kept rows below n' that move, as kvev_compact does, though
+ * none is staged), plus status bit 8 if a wait between workgroups reached
+ * its spin limit (never expected).  Errors: the union of those three calls'
+ * (KVEV_EINVAL also for several score kinds in flags or a workspace off 16
+ * bytes); workspace: kvev_workspace_bytes(cache, 0, 0) bytes, as for
+ * kvev_compact.  The workspace's state part also holds the pass's ticket and
+ * arrival counters: after a KVEV_EDEVICE return, zero it again.
  */
 int kvev_evict(const kvev_cache *cache, const kvev_window *win, int32_t flags,
                int32_t pool_kernel, int32_t budget, int32_t recent_window, float *score,

@@ -22,7 +22,7 @@ OUT = os.path.join(HERE, "libkvev.so")
 BUILD_DIR = os.path.join(ROOT, "_build", "kvev")
 ARCH = os.environ.get("KVEV_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.hip", "score.hip", "select.hip", "compact.hip", "measure.hip", "window_attn.hip", "h2o_step.hip", "vtoken.hip", "policy.hip", "ring_step.hip"]
+SOURCES = ["api.hip", "score.hip", "select.hip", "compact.hip", "finish.hip", "measure.hip", "window_attn.hip", "h2o_step.hip", "vtoken.hip", "policy.hip", "ring_step.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -50,18 +50,61 @@ size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 // all entry points; selection and compaction use disjoint parts of it, so
 // the fused call can pass the threshold from one to the other.
 struct StateLayout {
-  size_t hist, hist2, head_acc, total;
+  size_t hist, hist2, head_acc, fin_err, fin_nmem, fin_arrive, fin_marks, fin_done, fin_ctr,
+      fin_acc, total;
+  int marks_per_head;
 };
 
 StateLayout state_layout(const kvev_cache *c) {
   StateLayout L{};
   const size_t units = (size_t)c->batch * c->kv_heads;
+  const size_t max_slots = (size_t)c->max_blocks * KVEV_BLOCK_SIZE;
+  L.marks_per_head = (int)((max_slots + 255) / 256);
   size_t off = 0;
   L.hist = off; off = a256(off + units * kvev::kSelectBins * 4);
   L.hist2 = off; off = a256(off + units * kvev::kSelectBins * 4);
   L.head_acc = off; off = a256(off + units * 8);
+  // kvev_evict's pass after scoring (it also uses hist and hist2): bad-block
+  // flags, bucket member counts, arrivals, batch marks, heads' workgroups
+  // done, ticket and done counters, stat accumulators
+  L.fin_err = off; off = a256(off + units * 4);
+  L.fin_nmem = off; off = a256(off + units * 4);
+  L.fin_arrive = off; off = a256(off + units * 4);
+  L.fin_marks = off; off = a256(off + units * (size_t)L.marks_per_head * 4);
+  L.fin_done = off; off = a256(off + units * 4);
+  L.fin_ctr = off; off = a256(off + 4 * 4);
+  L.fin_acc = off; off = a256(off + 4 * 8);
   L.total = off;
   return L;
+}
+
+// kvev_evict's scratch after the state: the scores of the pass, the bucket
+// members and the keys below the bucket per 1024-slot chunk, per head.
+struct EvictLayout {
+  size_t sc, mem, gbelow, total;
+  int chunks;
+};
+
+EvictLayout evict_layout(const kvev_cache *c) {
+  EvictLayout L{};
+  const size_t units = (size_t)c->batch * c->kv_heads;
+  const size_t max_slots = (size_t)c->max_blocks * KVEV_BLOCK_SIZE;
+  L.chunks = (int)((max_slots + 1023) / 1024);
+  size_t off = state_layout(c).total;
+  L.sc = off; off = a256(off + units * max_slots * 4);
+  L.mem = off; off = a256(off + units * max_slots * 8);
+  L.gbelow = off; off = a256(off + units * (size_t)L.chunks * 4);
+  L.total = off;
+  return L;
+}
+
+size_t evict_layout_total(const kvev_cache *c) { return evict_layout(c).total; }
+
+size_t compact_layout_total(const kvev_cache *c);
+
+// The workspace kvev_select, kvev_compact and kvev_evict share.
+size_t main_layout_total(const kvev_cache *c) {
+  return std::max(compact_layout_total(c), evict_layout_total(c));
 }
 
 struct SelectLayout {
@@ -110,6 +153,8 @@ CompactLayout compact_layout(const kvev_cache *c) {
   L.total = off;
   return L;
 }
+
+size_t compact_layout_total(const kvev_cache *c) { return compact_layout(c).total; }
 
 struct WaLayout {
   size_t part_m, part_l, part_acc, total;
@@ -267,7 +312,7 @@ const char *kvev_strerror(int status) {
 
 size_t kvev_workspace_bytes(const kvev_cache *cache, int32_t group, int32_t obs_window) {
   if (!valid_cache(cache)) return 0;
-  size_t need = compact_layout(cache).total;  // includes the selection scratch
+  size_t need = main_layout_total(cache);
   if (group >= 1 && obs_window >= 1) {
     const size_t wa = wa_layout(cache, group, obs_window).total;
     if (wa > need) need = wa;
@@ -282,7 +327,7 @@ namespace {
 // Validates the score arguments and fills the kernel's argument block and
 // its LDS size.  Nothing is enqueued.
 int build_score_args(const kvev_cache *cache, const kvev_window *win, int32_t flags,
-                     int32_t pool_kernel, float *sum, float *pooled, float *drop, int fused,
+                     int32_t pool_kernel, float *sum, float *pooled, float *drop, int hist,
                      kvev::ScoreArgs &a) {
   if (!valid_cache(cache)) return KVEV_EINVAL;
   int rc = check_window(cache, win);
@@ -311,6 +356,8 @@ int build_score_args(const kvev_cache *cache, const kvev_window *win, int32_t fl
   a.sum = sum;
   a.pooled = pooled;
   a.drop = drop;
+  a.prev = sum;
+  a.head_err = nullptr;
   a.units = cache->batch * cache->kv_heads;
   a.Hkv = cache->kv_heads;
   a.G = win->group;
@@ -336,7 +383,7 @@ int build_score_args(const kvev_cache *cache, const kvev_window *win, int32_t fl
   const int is_drop = (flags & KVEV_DROP) ? 1 : 0;
   auto lds_of = [&](int t) {
     return kvev::score_lds_bytes(bf16, cache->head_dim, is_drop, a.row_tiles, t, a.halo_blocks,
-                                 fused);
+                                 hist);
   };
   int tb = KV_TILE_MAX, threads = KV_THREADS_MAX;
   auto tiles_of = [&](int t) { return (int64_t)a.units * ((cache->max_blocks + t - 1) / t); };
@@ -652,43 +699,70 @@ int kvev_evict(const kvev_cache *cache, const kvev_window *win, int32_t flags,
   const int kind = flags & (KVEV_SUM | KVEV_POOL | KVEV_DROP);
   if (kind != KVEV_SUM && kind != KVEV_POOL && kind != KVEV_DROP) return KVEV_EINVAL;
   if (budget <= 0 || recent_window < 0 || recent_window >= budget) return KVEV_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) & 15) return KVEV_EINVAL;
+  const StateLayout S = state_layout(cache);
+  const EvictLayout E = evict_layout(cache);
+  // this pass's scores go to the workspace row; the output row receives them
+  // compacted (the address is formed before the workspace is checked, and
+  // used only after)
+  float *sc = reinterpret_cast<float *>(reinterpret_cast<uintptr_t>(workspace) + E.sc);
   kvev::ScoreArgs a;
-  int rc = build_score_args(cache, win, flags, pool_kernel, kind == KVEV_SUM ? score : nullptr,
-                            kind == KVEV_POOL ? score : nullptr, kind == KVEV_DROP ? score : nullptr,
-                            1, a);
+  int rc = build_score_args(cache, win, flags, pool_kernel, kind == KVEV_SUM ? sc : nullptr,
+                            kind == KVEV_POOL ? sc : nullptr, kind == KVEV_DROP ? sc : nullptr, 1,
+                            a);
   if (rc) return rc;
   if (free_capacity < cache->num_blocks) return KVEV_ENOSPACE;
-  if (cache->batch * cache->kv_heads > kvev::kCompactMaxUnits) return KVEV_EUNSUPPORTED;
-  const CompactLayout L = compact_layout(cache);
-  if (L.chunks > kvev::kSelectMaxChunks) return KVEV_EUNSUPPORTED;
-  if (!workspace || ws_bytes < L.total) return KVEV_ENOSPACE;
-  a.sel = sel_head(cache, n_victims, budget, recent_window, workspace);
-  a.sel_kind = kind;
-  kvev::CompactArgs c{};
-  fill_compact_args(const_cast<kvev_cache *>(cache), score, free_list, free_count, free_capacity,
-                    stats, workspace, c);
-  c.victims = victims;
-  c.n_victims = n_victims;
-  c.victims_out = victims;
-  c.head_sel = a.sel.head_sel;
-  c.chunk_off = a.sel.chunk_off;
-  c.sel_score = score;
-  c.recent = recent_window;
-  c.rows_cap = std::min(budget, c.max_slots);  // n' = min(n, budget)
+  if ((size_t)cache->max_blocks * KVEV_BLOCK_SIZE >
+      (size_t)kvev::kSelectMaxChunks * kvev::kSelectChunk)
+    return KVEV_EUNSUPPORTED;  // 1M slots per head
+  if (!workspace || ws_bytes < main_layout_total(cache)) return KVEV_ENOSPACE;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  a.prev = score;  // ACCUMULATE: the running sums are in the output row
+  a.head_err = reinterpret_cast<uint32_t *>(ws + S.fin_err);
+  a.hist = reinterpret_cast<uint32_t *>(ws + S.hist);
+  a.sel_budget = budget;
+  a.sel_recent = recent_window;
+  kvev::FinishArgs f{};
+  f.k_pool = static_cast<uint8_t *>(cache->k_pool);
+  f.v_pool = static_cast<uint8_t *>(cache->v_pool);
+  f.block_table = cache->block_table;
+  f.seq_len = cache->seq_len;
+  f.pos = cache->pos;
+  f.sc = sc;
+  f.score_out = score;
+  f.victims = victims;
+  f.n_victims = n_victims;
+  f.free_list = free_list;
+  f.free_count = free_count;
+  f.stats = stats;
+  f.head_err = a.head_err;
+  f.hist = a.hist;
+  f.hist2 = reinterpret_cast<uint32_t *>(ws + S.hist2);
+  f.nmem = reinterpret_cast<uint32_t *>(ws + S.fin_nmem);
+  f.arrive = reinterpret_cast<uint32_t *>(ws + S.fin_arrive);
+  f.mem = reinterpret_cast<uint2 *>(ws + E.mem);
+  f.gbelow = reinterpret_cast<uint32_t *>(ws + E.gbelow);
+  f.chunks = E.chunks;
+  f.marks = reinterpret_cast<uint32_t *>(ws + S.fin_marks);
+  f.head_done = reinterpret_cast<uint32_t *>(ws + S.fin_done);
+  f.ctr = reinterpret_cast<uint32_t *>(ws + S.fin_ctr);
+  f.acc = reinterpret_cast<unsigned long long *>(ws + S.fin_acc);
+  f.units = cache->batch * cache->kv_heads;
+  f.max_blocks = cache->max_blocks;
+  f.max_slots = cache->max_blocks * KVEV_BLOCK_SIZE;
+  f.num_blocks = cache->num_blocks;
+  f.row_bytes = cache->head_dim * elem_bytes(cache);
+  f.budget = budget;
+  f.recent = recent_window;
+  f.kh = kvev::finish_parts(f.units, std::min(budget, f.max_slots));
+  f.marks_per_head = S.marks_per_head;
+  f.free_capacity = free_capacity;
+  if ((int64_t)f.units * f.kh > INT32_MAX) return KVEV_EUNSUPPORTED;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  kvev::SelectArgs sa{};
-  sa.score = score;
-  sa.seq_len = cache->seq_len;
-  sa.victims = victims;
-  sa.sel = a.sel;
-  sa.units = cache->batch * cache->kv_heads;
-  sa.max_slots = cache->max_blocks * KVEV_BLOCK_SIZE;
   rc = map_err(kvev::launch_score(a, cache->dtype == KVEV_BF16, cache->head_dim,
                                   kind == KVEV_DROP, st));
   if (rc) return rc;
-  rc = map_err(kvev::launch_select_threshold(sa, st));
-  if (rc) return rc;
-  return map_err(kvev::launch_evict_compact(c, st));
+  return map_err(kvev::launch_finish(f, st));
 }
 
 int kvev_window_attn(const kvev_cache *cache, const kvev_window *win, float *lse_out,

@@ -12,10 +12,9 @@
 //           word of the head (arrivals, chunks with errors, rows moved, rows
 //           staged) with a single atomic; the chunk that arrives last records
 //           the head's totals, so no chunk reads another's memory.
-//           Two forms: from a caller's ascending victim list (256 evenly
-//           spaced samples bracket the chunk's victims, one range load
-//           fetches them), or from the threshold the selection left in the
-//           workspace, which then also writes the victim list.
+//           The chunk's victims come from the caller's ascending victim list
+//           (256 evenly spaced samples bracket them, one range load fetches
+//           them).
 //   gather  (persistent grid over (head, rank range) items): each thread
 //           issues all of its 16-byte K and V loads before any store; the
 //           moved rows are stored with the nontemporal hint, so they reach
@@ -393,76 +392,6 @@ __global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArg
   prep_finish(P, u, n, m, moved, staged, S);
 }
 
-// Prep from the selection's threshold: slot s < nc is a victim iff its key
-// is below T, or equal to T with s <= cut; the chunk's first victim index
-// comes from the selection's per-chunk offsets.
-__global__ __launch_bounds__(kThreads) void evict_prep_kernel(const CompactArgs P) {
-  __shared__ PrepLds S;
-  const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
-  prep_common_start(P, u, c);
-  // one round of loads: the head's length and victim count, threshold and
-  // chunk offset, and the chunk's pos, scores and block ids (indices clamped
-  // inside the rows, so none waits on another)
-  const size_t urow = (size_t)u * P.max_slots;
-  const int s0 = c * kChunk;
-  const int n = P.seq_len[u];
-  const int m = P.n_victims[u];
-  const uint32_t T = P.head_sel[u * 4 + 0];
-  const int cut = (int)P.head_sel[u * 4 + 1];
-  const uint32_t coff = P.chunk_off[(size_t)u * P.chunks + c];
-  int posv[kPerThread];
-  float scv[kPerThread], sel[kPerThread];
-#pragma unroll
-  for (int q = 0; q < kPerThread; ++q) {
-    const size_t i = urow + min(s0 + tid * kPerThread + q, P.max_slots - 1);
-    posv[q] = P.pos[i];
-    sel[q] = P.sel_score[i];
-  }
-  if (P.score) {
-#pragma unroll
-    for (int q = 0; q < kPerThread; ++q)
-      scv[q] = P.score[urow + min(s0 + tid * kPerThread + q, P.max_slots - 1)];
-  } else {
-#pragma unroll
-    for (int q = 0; q < kPerThread; ++q) scv[q] = 0.f;
-  }
-  const int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
-  const int blk_raw = tid < kChunk / kBlock ? bt[min(s0 / kBlock + tid, P.max_blocks - 1)] : 0;
-
-  if (settle_trivial(P, u, c, n, m)) return;
-  if (c == 0 && tid == 0) {
-    P.head_info[(size_t)u * 8 + 0] = n;
-    P.head_info[(size_t)u * 8 + 1] = m;
-  }
-  if (tid == 0) {
-    S.s_err = 0;
-    S.s_nstage = 0;
-  }
-  const int nc = max(0, n - P.recent);
-  int moved = 0, staged = 0;
-  if (s0 < n) {
-    const int s1 = min(s0 + kChunk, n);
-    const int j0 = s0 < nc ? (int)coff : m;
-    int bad = 0;
-    if (tid < kChunk / kBlock) {
-      const int blk = s0 / kBlock + tid < blocks_of(s1) ? blk_raw : 0;
-      if (blk < 0 || blk >= P.num_blocks) bad = 1;
-      S.blk_l[tid] = blk;
-    }
-    bool vf[kPerThread];
-#pragma unroll
-    for (int q = 0; q < kPerThread; ++q) {
-      const int s = s0 + tid * kPerThread + q;
-      const uint32_t k = score_key(sel[q]);
-      vf[q] = s < s1 && s < nc && (k < T || (k == T && s <= cut));
-    }
-    __syncthreads();  // block ids, s_err and s_nstage initialised
-    if (bad) atomicOr(&S.s_err, 1);
-    rank_and_stage(P, u, s0, s1, n - m, m, j0, vf, posv, scv, P.victims_out, S, moved, staged);
-  }
-  prep_finish(P, u, n, m, moved, staged, S);
-}
-
 // Persistent grid over (head, row range) items.  A prefix pass reads each
 // head's record once and keeps in LDS the item and free-list offsets of every
 // head.  Item 0 of a head records its stats and seq_len; every item appends
@@ -659,13 +588,6 @@ static hipError_t launch_gather(const CompactArgs &a, hipStream_t s) {
 
 hipError_t launch_compact(const CompactArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(compact_prep_kernel, dim3(a.chunks, a.units), dim3(kThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_gather(a, s);
-}
-
-hipError_t launch_evict_compact(const CompactArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(evict_prep_kernel, dim3(a.chunks, a.units), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_gather(a, s);

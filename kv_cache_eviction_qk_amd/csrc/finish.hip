@@ -1,0 +1,745 @@
+// finish.hip -- selection and in-place compaction of the fused eviction pass,
+// in one launch after the scoring pass (gfx950).
+//
+// The scoring pass has written every live slot's eviction score to a
+// workspace row and added the top 11 bits of each candidate's order key to
+// its head's histogram.  Each KV head then gets kh workgroups of 1024
+// threads.  A workgroup takes its (head, part k) from a ticket counter, so
+// every workgroup with a lower ticket is already resident or done.
+//
+//  1. Threshold.  From the histogram every workgroup of the head knows the
+//     bucket b holding the m-th smallest key.  Each collects, over its own
+//     share of the candidate slots, the keys below b per 1024-slot chunk and
+//     the bucket's (key, slot) members with the histogram of their key bits
+//     20..10, and publishes them; after the head's workgroups have all
+//     arrived, each reads what all published and finds, in LDS, the key T
+//     and the cut slot of the m-th smallest (key, slot) pair (sub-bucket from
+//     the second histogram, a radix pass over the last 10 bits, rank counting
+//     among equal keys).  Victims are the candidates with key < T, or key ==
+//     T and slot <= cut: equal scores evict the lower position ([SNAP]
+//     "Tie-breaking").
+//  2. Victim list.  Each workgroup writes the victims of its share's groups
+//     at their offsets, in ascending slot order.
+//  3. Compaction ([H2O] "PagedAttention Memory Integration"; [VTOK] section
+//     3.3 stage 3: destinations filled in logical order).  Batches k, k + kh,
+//     ... of 256 destination ranks.  A batch finds the kept slots of its
+//     ranks, loads their K, V and pos, and then marks itself "read"; before
+//     storing into its destination slots it waits for the marks of the
+//     batches that read those slots.  A kept row only moves down (rank <=
+//     slot), so those are this batch or lower ones.  Nothing is staged: only
+//     the moved rows are read and written.
+//  4. The last workgroup of a head appends its emptied tail blocks
+//     [ceil(n'/16), ceil(n/16)) to the free list in (b, h, block) order and
+//     clears their table entries ([VTOK] section 3.5, I2 and I4).  The last
+//     workgroup of the launch sets seq_len, the free count and the stats,
+//     and leaves the state words zero for the next call.
+//
+// Waits and hand-offs.  A workgroup waits only for workgroups of its own
+// head: at the head's arrival counter, and for the marks of lower batches.
+// Tickets are taken in dispatch order, so when a workgroup of a later head is
+// resident every workgroup of this head has been dispatched, and a head
+// needs only kh workgroups at once: every wait ends (each also has a spin
+// limit, status bit 8, so no wave can loop forever).  Published values are
+// written with agent-scope atomic stores and read with agent-scope atomic
+// loads (both bypass the per-XCD L2, which is not coherent across XCDs), and
+// the arrival add is issued after s_waitcnt has seen every one of those
+// stores complete; the reader issues its loads only after its poll of the
+// counter has returned.  A release / acquire pair would order the same
+// accesses through the memory model, but on gfx950 an agent-scope release
+// writes back the whole L2: one per workgroup over 256 workgroups cost
+// 9 us.  A batch's "read" mark carries no data: it is stored after the
+// batch's loads have returned (s_waitcnt), so no store can reach a row
+// before its reader holds it.
+//
+// A head whose length is out of range gets n_victims = -1 and is left alone
+// (status bit 2).  A head where the scoring pass met a block id outside the
+// pool gets its victim list but no compaction (status bit 1).  A head that
+// loses nothing keeps its tokens.  The output score row receives the
+// compacted scores [0, n') of every head that was scored.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "kvev_device.h"
+#include "kvev_kernels.h"
+#include "kvev_select_head.h"
+
+namespace kvev {
+
+namespace {
+
+constexpr int kFT = 1024;               // threads per workgroup
+constexpr int kFW = kFT / kWave;        // waves
+constexpr int kGrp = 4 * kFT;           // slots per group: 4 consecutive slots per thread
+constexpr int kRes = 8;                 // groups of a share whose keys stay in registers
+constexpr int kBatchRanks = 256;        // destination ranks per batch
+constexpr int kMem = 4096;              // sub-bucket members kept in LDS
+constexpr int kTie = 2048;              // keys equal to T ranked by counting
+constexpr int kPreBlk = 1024;           // source block ids prefetched per batch (4 groups)
+constexpr unsigned kSpinLimit = 1u << 20;  // polls of a wait before it gives up (status bit 8)
+
+constexpr int kChunk = kSelectChunk;    // victim offsets are kept per 1024-slot chunk
+constexpr int kMaxChunks = kSelectMaxChunks;
+
+struct FinLds {
+  uint32_t h[kSelectBins];           // key histogram (top bits, then reused)
+  uint32_t h2[kSelectBins];          // key bits 20..10 of the bucket's members
+  uint32_t cv[kMaxChunks + 1];       // victims per chunk, then victims before each chunk
+  uint2 sub[kMem];                   // the sub-bucket's members
+  int32_t blk[kPreBlk];              // block ids of the batch's first source groups
+  int32_t src[kBatchRanks];          // source slot of each rank of a batch
+  int32_t sblk[kBatchRanks];         // source block id of each rank (-1: stays)
+  int32_t dblk[kBatchRanks / kBlock];  // destination block ids of the batch
+  int32_t wtot[kFW];                 // scan scratch
+  RankOut r;
+  uint32_t ticket, nsub, nt, cut, nown, mbase;
+  int32_t moved, at_risk, last;
+  unsigned long long pre_tot[2];
+};
+
+__device__ __forceinline__ int blocks_of(int n) { return (n + kBlock - 1) / kBlock; }
+
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint2 ld_agent2(const uint2 *p) {
+  const unsigned long long v =
+      __hip_atomic_load(reinterpret_cast<const unsigned long long *>(p), __ATOMIC_RELAXED,
+                        __HIP_MEMORY_SCOPE_AGENT);
+  return make_uint2((uint32_t)v, (uint32_t)(v >> 32));
+}
+__device__ __forceinline__ void st_agent2(uint2 *p, uint2 v) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long *>(p),
+                     (unsigned long long)v.x | ((unsigned long long)v.y << 32), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+// Every earlier memory access of this thread has completed.
+__device__ __forceinline__ void wait_mem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Exclusive prefix sum of v over the 1024 threads (every thread must call);
+// *total receives the sum.
+__device__ int block_scan(int v, int *wtot, int *total) {
+  const int lane = lane_id(), wv = threadIdx.x / kWave;
+  const int incl = (int)wave_incl_scan((uint32_t)v);
+  __syncthreads();
+  if (lane == kWave - 1) wtot[wv] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kFW; ++w) {
+    const int t = wtot[w];
+    before += w < wv ? t : 0;
+    all += t;
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+// Wave 0 polls *p until it reads at least `want` (the caller then barriers).
+__device__ void wait_count(const uint32_t *p, uint32_t want, unsigned long long *acc) {
+  if (threadIdx.x >= kWave) return;
+  unsigned spins = 0;
+  while (ld_agent(p) < want) {
+    if (++spins > kSpinLimit) {
+      if (threadIdx.x == 0) atomicOr(&acc[3], 8ull);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// The free-list offset of head u (blocks freed by the heads before it) and
+// the total over all heads; a head frees blocks when its length is in range,
+// it loses tokens and the scoring pass met no bad block id.  The loads are
+// issued by freed_prefix_load; every thread calls both.
+struct Prefix {
+  long long b, t;
+};
+__device__ Prefix freed_prefix_load(const FinishArgs &P, int u) {
+  Prefix x{0, 0};
+  for (int i = threadIdx.x; i < P.units; i += kFT) {
+    const int n = P.seq_len[i];
+    int fr = 0;
+    if (n >= 0 && n <= P.max_slots && P.head_err[i] == 0) {
+      const int m = max(0, n - P.budget);
+      if (m > 0) fr = blocks_of(n) - blocks_of(n - m);
+    }
+    x.t += fr;
+    x.b += i < u ? fr : 0;
+  }
+  return x;
+}
+__device__ void freed_prefix(Prefix x, FinLds &L, int &before, int &total) {
+  long long b = x.b, t = x.t;
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) {
+    b += __shfl_xor(b, o);
+    t += __shfl_xor(t, o);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) L.pre_tot[0] = L.pre_tot[1] = 0;
+  __syncthreads();
+  if (lane_id() == 0) {
+    atomicAdd(&L.pre_tot[0], (unsigned long long)b);
+    atomicAdd(&L.pre_tot[1], (unsigned long long)t);
+  }
+  __syncthreads();
+  before = (int)L.pre_tot[0];
+  total = (int)L.pre_tot[1];
+}
+
+template <int PR>  // 16-byte pieces of one K (or V) row: 8, 16 or 32
+__global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  FinLds &L = *reinterpret_cast<FinLds *>(smem);
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
+
+  if (tid == 0) L.ticket = atomicAdd(&P.ctr[0], 1u);
+  __syncthreads();
+  const int ticket = (int)L.ticket;
+  const int u = ticket / P.kh, k = ticket % P.kh;
+  const size_t urow = (size_t)u * P.max_slots;
+  const int n = P.seq_len[u];
+  const bool consistent = n >= 0 && n <= P.max_slots;
+  const int m = consistent ? max(0, n - P.budget) : 0;
+  const int nc = consistent ? max(0, n - P.recent) : 0;
+  const int n2 = n - m;
+  const bool bad = consistent && P.head_err[u] != 0;
+  const float *sc = P.sc + urow;
+  float *so = P.score_out + urow;
+  unsigned long long *acc = P.acc;
+  // the head's free-list offset and the total, for the head's last workgroup
+  const Prefix pfx = freed_prefix_load(P, u);
+
+  if (!consistent) {
+    if (k == 0 && tid == 0) {
+      P.n_victims[u] = -1;
+      atomicOr(&acc[3], 2ull);
+    }
+  } else if (m == 0) {
+    // nothing to evict: the scores of [0, n) go to the output row as they are
+    if (k == 0 && tid == 0) P.n_victims[u] = 0;
+    const int share = ((n + P.kh - 1) / P.kh + 3) & ~3;
+    const int s0 = k * share, s1 = min(n, s0 + share);
+    for (int s = s0 + tid; s < s1; s += kFT) so[s] = sc[s];
+  } else {
+    // ------------------------------------------------------------ threshold
+    const int ngrp = (nc + kGrp - 1) / kGrp;      // groups with candidates
+    const int ngrp_all = (n + kGrp - 1) / kGrp;   // groups with live slots
+    const int nch = (nc + kChunk - 1) / kChunk;   // chunks with candidates
+    const int nch_all = (n + kChunk - 1) / kChunk;
+    const int gpp = (ngrp + P.kh - 1) / P.kh;     // groups per share
+    const int g_lo = min(k * gpp, ngrp), g_hi = min(g_lo + gpp, ngrp);
+    // keys of the share held in registers (not beside the widest rows' pieces)
+    const bool res = PR <= 16 && g_hi - g_lo <= kRes;
+    uint32_t kr[kRes][4];
+    // this thread's 4 keys of group g (slots g*4096 + 4*tid + e)
+    auto load4 = [&](int g, uint32_t (&o)[4]) {
+      const int s = min(g * kGrp + 4 * tid, P.max_slots - 4);
+      const float4 v = *reinterpret_cast<const float4 *>(sc + s);
+      o[0] = score_key(v.x);
+      o[1] = score_key(v.y);
+      o[2] = score_key(v.z);
+      o[3] = score_key(v.w);
+    };
+    auto keys_of = [&](int g, uint32_t (&o)[4]) {
+      if (res && g >= g_lo && g < g_hi) {
+#pragma unroll
+        for (int q = 0; q < kRes; ++q)
+          if (q == g - g_lo) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = kr[q][e];
+          }
+      } else {
+        load4(g, o);
+      }
+    };
+    const uint32_t *hg = P.hist + (size_t)u * kSelectBins;
+    uint32_t hv[kSelectBins / kFT];
+#pragma unroll
+    for (int q = 0; q < kSelectBins / kFT; ++q) hv[q] = hg[tid + q * kFT];
+    if (res) {
+#pragma unroll
+      for (int q = 0; q < kRes; ++q)
+        if (q < g_hi - g_lo) load4(g_lo + q, kr[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < kSelectBins / kFT; ++q) {
+      L.h[tid + q * kFT] = hv[q];
+      L.h2[tid + q * kFT] = 0;
+    }
+    for (int i = tid; i <= kMaxChunks; i += kFT) L.cv[i] = 0;
+    if (tid == 0) {
+      L.nsub = 0;
+      L.nown = 0;
+      L.moved = 0;
+      L.at_risk = 0;
+    }
+    __syncthreads();
+    wg_rank_bin<kSelectBins>(L.h, (uint32_t)m, &L.r);
+    const uint32_t bkt = L.r.bin;
+    const uint32_t need = (uint32_t)m - L.r.below;  // rank inside the bucket
+    // ---- own share: keys below the bucket per chunk (a wave covers 256
+    // slots of a group: chunk = 4 g + wave / 4), the bucket's members (counted
+    // first, so one atomic per workgroup reserves their place), and the
+    // histogram of their key bits 20..10
+    uint2 *gmem = P.mem + urow;
+    uint32_t *gbel = P.gbelow + (size_t)u * P.chunks;
+    for (int g = g_lo; g < g_hi; ++g) {
+      uint32_t kk[4];
+      keys_of(g, kk);
+      uint32_t below = 0, mine = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = g * kGrp + 4 * tid + e;
+        const bool in = s < nc;
+        const uint32_t top = kk[e] >> 21;
+        below += (uint32_t)__popcll(__ballot(in && top < bkt));
+        const bool mb = in && top == bkt;
+        if (mb) atomicAdd(&L.h2[(kk[e] >> 10) & 2047u], 1u);
+        mine += (uint32_t)__popcll(__ballot(mb));
+      }
+      if (lane == 0) {
+        if (below) atomicAdd(&L.cv[4 * g + wv / 4], below);
+        if (mine) atomicAdd(&L.nown, mine);
+      }
+    }
+    __syncthreads();
+    if (tid == 0) L.mbase = L.nown ? atomicAdd(&P.nmem[u], L.nown) : 0u;
+    if (tid == 0) L.nown = 0;
+    for (int c = 4 * g_lo + tid; c < min(4 * g_hi, nch); c += kFT) st_agent(gbel + c, L.cv[c]);
+    uint32_t *h2g = P.hist2 + (size_t)u * kSelectBins;
+#pragma unroll
+    for (int q = 0; q < kSelectBins / kFT; ++q)
+      if (L.h2[tid + q * kFT]) atomicAdd(&h2g[tid + q * kFT], L.h2[tid + q * kFT]);
+    __syncthreads();
+    const uint32_t mbase = L.mbase;
+    for (int g = g_lo; g < g_hi; ++g) {
+      uint32_t kk[4];
+      keys_of(g, kk);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = g * kGrp + 4 * tid + e;
+        const bool mb = s < nc && (kk[e] >> 21) == bkt;
+        const uint64_t mm = __ballot(mb);
+        if (mm) {
+          uint32_t base = 0;
+          if (lane == 0) base = atomicAdd(&L.nown, (uint32_t)__popcll(mm));
+          base = __shfl(base, 0);
+          if (mb) st_agent2(gmem + mbase + base + (uint32_t)ballot_prefix(mm),
+                            make_uint2(kk[e], (uint32_t)s));
+        }
+      }
+    }
+    // ---- arrive, then wait for every workgroup of the head
+    wait_mem();
+    __syncthreads();
+    if (tid == 0) atomicAdd(&P.arrive[u], 1u);
+    wait_count(&P.arrive[u], (uint32_t)P.kh, acc);
+    __syncthreads();
+    // ---- what the head's workgroups published: one round of loads
+    const int nmem = (int)ld_agent(&P.nmem[u]);
+#pragma unroll
+    for (int q = 0; q < kSelectBins / kFT; ++q) hv[q] = ld_agent(&h2g[tid + q * kFT]);
+    uint32_t cb = tid < nch ? ld_agent(gbel + tid) : 0u;
+    uint2 pr[4];  // the first members, read before their count is known
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      pr[q] = q * kFT + tid < P.max_slots ? ld_agent2(gmem + q * kFT + tid) : make_uint2(0u, 0u);
+    for (int c = tid + kFT; c < nch; c += kFT) L.cv[c] = ld_agent(gbel + c);
+    if (tid < nch) L.cv[tid] = cb;
+#pragma unroll
+    for (int q = 0; q < kSelectBins / kFT; ++q) L.h2[tid + q * kFT] = hv[q];
+    for (int i = tid; i < 1024; i += kFT) L.h[i] = 0;
+    __syncthreads();
+    wg_rank_bin<kSelectBins>(L.h2, need, &L.r);
+    const uint32_t pre = (bkt << 11) | L.r.bin;  // key >> 10 of T
+    const uint32_t need2 = need - L.r.below;
+    // every member: those below the sub-bucket are victims (per chunk); the
+    // sub-bucket's keys get the histogram of their last 10 bits and go to LDS
+    // (the first kMem of them)
+    for (int i0 = 0; i0 < nmem; i0 += 4 * kFT) {
+      if (i0 > 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = i0 + q * kFT + tid;
+          pr[q] = i < nmem ? ld_agent2(gmem + i) : make_uint2(0u, 0u);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool v = i0 + q * kFT + tid < nmem;
+        const uint32_t p = pr[q].x >> 10;
+        wave_count_add(L.cv, (int)pr[q].y / kChunk, v && p < pre);
+        const bool sb = v && p == pre;
+        if (sb) atomicAdd(&L.h[pr[q].x & 1023u], 1u);
+        const uint64_t sm = __ballot(sb);
+        if (sm) {
+          uint32_t base = 0;
+          if (lane == 0) base = atomicAdd(&L.nsub, (uint32_t)__popcll(sm));
+          base = __shfl(base, 0);
+          const uint32_t j = base + (uint32_t)ballot_prefix(sm);
+          if (sb && j < (uint32_t)kMem) L.sub[j] = pr[q];
+        }
+      }
+    }
+    __syncthreads();
+    const int nsub = (int)L.nsub;
+    const bool sub_lds = nsub <= kMem;
+    // every key of the sub-bucket: from LDS, or (too many) streamed again
+    auto for_sub = [&](auto &&f) {
+      if (sub_lds) {
+        for (int i = tid; i < nsub; i += kFT) f(L.sub[i].x, (int)L.sub[i].y);
+      } else {
+        for (int i = tid; i < nmem; i += kFT) {
+          const uint2 p = ld_agent2(gmem + i);
+          if ((p.x >> 10) == pre) f(p.x, (int)p.y);
+        }
+      }
+    };
+    wg_rank_bin<1024>(L.h, need2, &L.r);
+    const uint32_t T = (pre << 10) | L.r.bin;
+    const uint32_t eT = need2 - L.r.below;  // keys equal to T that are victims
+    const uint32_t cnt_t = L.h[L.r.bin];
+    __syncthreads();
+    // the cut: the eT-th smallest slot among the keys equal to T
+    int cut = INT_MAX;
+    if (eT < cnt_t) {
+      if (cnt_t <= (uint32_t)kTie) {
+        int *tie = reinterpret_cast<int *>(L.h2);
+        if (tid == 0) L.nt = 0;
+        __syncthreads();
+        for_sub([&](uint32_t key, int s) {
+          if (key == T) tie[atomicAdd(&L.nt, 1u)] = s;
+        });
+        __syncthreads();
+        for (int i = tid; i < (int)cnt_t; i += kFT) {
+          const int si = tie[i];
+          uint32_t r = 0;
+          for (int j = 0; j < (int)cnt_t; ++j) r += tie[j] < si ? 1u : 0u;
+          if (r == eT - 1) L.cut = (uint32_t)si;
+        }
+        __syncthreads();
+        cut = (int)L.cut;
+      } else {
+        // many equal keys: radix over the slot bits (4 x 8)
+        uint32_t sp = 0, smask = 0, rank = eT;
+        for (int pass = 0; pass < 4; ++pass) {
+          const int shift = 24 - 8 * pass;
+          for (int i = tid; i < 256; i += kFT) L.h[i] = 0;
+          __syncthreads();
+          for_sub([&](uint32_t key, int s) {
+            if (key == T && ((uint32_t)s & smask) == sp)
+              atomicAdd(&L.h[((uint32_t)s >> shift) & 255u], 1u);
+          });
+          __syncthreads();
+          wg_rank_bin<256>(L.h, rank, &L.r);
+          sp |= L.r.bin << shift;
+          smask |= 255u << shift;
+          rank -= L.r.below;
+          __syncthreads();
+        }
+        cut = (int)sp;
+      }
+    }
+    // the sub-bucket's victims per chunk, then the chunks' offsets
+    if (sub_lds) {
+      for (int i0 = 0; i0 < nsub; i0 += kFT) {  // wave-uniform
+        const int i = i0 + tid;
+        const uint2 p = i < nsub ? L.sub[i] : make_uint2(0u, 0u);
+        wave_count_add(L.cv, (int)p.y / kChunk,
+                       i < nsub && (p.x < T || (p.x == T && (int)p.y <= cut)));
+      }
+    } else {
+      for_sub([&](uint32_t key, int s) {
+        if (key < T || (key == T && s <= cut)) atomicAdd(&L.cv[s / kChunk], 1u);
+      });
+    }
+    __syncthreads();
+    if (wv == 0) {  // exclusive scan of the chunk counts (at most 1024: 16 per lane)
+      const int per = (nch_all + kWave - 1) / kWave;
+      const int c0 = min(lane * per, nch_all), c1 = min(c0 + per, nch_all);
+      uint32_t mine = 0;
+      for (int c = c0; c < c1; ++c) mine += L.cv[c];
+      uint32_t e = wave_incl_scan(mine) - mine;
+      for (int c = c0; c < c1; ++c) {
+        const uint32_t x = L.cv[c];
+        L.cv[c] = e;
+        e += x;
+      }
+      if (lane == kWave - 1) L.cv[nch_all] = e;  // == m
+    }
+    __syncthreads();
+
+    // victim flags of a group's slots for this thread
+    auto vic4 = [&](int g, const uint32_t (&kk)[4], bool (&v)[4]) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = g * kGrp + 4 * tid + e;
+        v[e] = s < nc && (kk[e] < T || (kk[e] == T && s <= cut));
+      }
+    };
+
+    // ------------------------------------------------------------ victim list
+    if (k == 0 && tid == 0) P.n_victims[u] = m;
+    int32_t *vout = P.victims + urow;
+    for (int g = g_lo; g < g_hi; ++g) {
+      uint32_t kk[4];
+      keys_of(g, kk);
+      bool v[4];
+      vic4(g, kk, v);
+      const int cnt = (int)v[0] + (int)v[1] + (int)v[2] + (int)v[3];
+      int tot;
+      int o = (int)L.cv[4 * g] + block_scan(cnt, L.wtot, &tot);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (v[e]) {
+          if (o < m) vout[o] = g * kGrp + 4 * tid + e;
+          ++o;
+        }
+    }
+
+    // ------------------------------------------------------------ compaction
+    if (bad) {
+      // no compaction: the scores of [0, n) go to the output row as they are
+      const int share = ((n + P.kh - 1) / P.kh + 3) & ~3;
+      const int s0 = k * share, s1 = min(n, s0 + share);
+      for (int s = s0 + tid; s < s1; s += kFT) so[s] = sc[s];
+    } else {
+      const int nbatch = (n2 + kBatchRanks - 1) / kBatchRanks;
+      const int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
+      const int32_t *pos = P.pos + urow;
+      uint32_t *marks = P.marks + (size_t)u * P.marks_per_head;
+      constexpr int kRowPieces = kBatchRanks * PR;   // 16-byte pieces of K (or V) per batch
+      constexpr int kPer = kRowPieces / kFT;         // per thread, per tensor
+      const int row_bytes = PR * 16;
+      // kept slots before chunk c: the chunk's start minus the victims before it
+      auto kbc = [&](int c) { return c * kChunk - (int)L.cv[min(c, nch_all)]; };
+      // the last chunk c with kbc(c) <= r (kbc does not decrease)
+      auto chunk_of_rank = [&](int r) {
+        int lo = 0, hi = nch_all - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (kbc(mid) <= r) lo = mid; else hi = mid - 1;
+        }
+        return lo;
+      };
+      for (int rho = k; rho < nbatch; rho += P.kh) {
+        const int R0 = rho * kBatchRanks, R1 = min(R0 + kBatchRanks, n2);
+        const int gs = chunk_of_rank(R0) / 4;  // group of the first source
+        // block ids: the destinations', and the first source groups' (one
+        // round of loads, in flight while the groups are ranked)
+        const int b0 = gs * (kGrp / kBlock);
+        const int bid = b0 + tid < blocks_of(n) ? bt[b0 + tid] : 0;
+        const int did = tid < kBatchRanks / kBlock && R0 / kBlock + tid < blocks_of(n2)
+                            ? bt[R0 / kBlock + tid] : 0;
+        // rank each kept slot of group g; record the sources of [R0, R1)
+        for (int g = gs; g < ngrp_all && kbc(4 * g) < R1; ++g) {
+          uint32_t kk[4];
+          keys_of(g, kk);
+          bool v[4];
+          vic4(g, kk, v);
+          int kc = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int s = g * kGrp + 4 * tid + e;
+            kc += (s < n && !v[e]) ? 1 : 0;
+          }
+          int tot;
+          int r = kbc(4 * g) + block_scan(kc, L.wtot, &tot);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int s = g * kGrp + 4 * tid + e;
+            if (s < n && !v[e]) {
+              if (r >= R0 && r < R1) L.src[r - R0] = s;
+              ++r;
+            }
+          }
+        }
+        L.blk[tid] = bid;
+        if (tid < kBatchRanks / kBlock) L.dblk[tid] = did;
+        __syncthreads();
+        // ---- loads: source block ids (prefetched, else loaded), K / V
+        // pieces, pos and score
+        const int nr = R1 - R0;
+        if (tid < nr) {
+          const int s = L.src[tid];
+          const int lb = s / kBlock - b0;
+          L.sblk[tid] = s == R0 + tid ? -1 : (lb < kPreBlk ? L.blk[lb] : bt[s / kBlock]);
+        }
+        __syncthreads();
+        uint4 kv[kPer], vv[kPer];
+        bool mv[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          const int idx = tid + j * kFT;
+          const int r = idx / PR, part = idx % PR;
+          const int blk = r < nr ? L.sblk[r] : -1;
+          mv[j] = blk >= 0;
+          const int s = mv[j] ? L.src[r] : 0;
+          const size_t off =
+              ((size_t)max(blk, 0) * kBlock + s % kBlock) * row_bytes + (size_t)part * 16;
+          kv[j] = mv[j] ? ld16(P.k_pool + off) : make_uint4(0, 0, 0, 0);
+          vv[j] = mv[j] ? ld16(P.v_pool + off) : make_uint4(0, 0, 0, 0);
+        }
+        int my_pos = 0;
+        float my_sc = 0.f;
+        if (tid < nr) {
+          const int s = L.src[tid];
+          my_pos = pos[s];
+          my_sc = sc[s];
+        }
+        // every load of the batch has returned its data before the mark
+        wait_mem();
+        __syncthreads();
+        if (tid == 0) st_agent(&marks[rho], 1u);
+        // ---- wait for the batches that read this batch's destination
+        // slots: they lie in chunk R0 / 1024, whose kept slots have the ranks
+        // [kbc(c), kbc(c + 1)); only batches below this one need waiting for
+        const int cd = R0 / kChunk;
+        const int klo = kbc(cd), khi = kbc(cd + 1);
+        const int lo = klo / kBatchRanks, hi = min((khi - 1) / kBatchRanks, rho - 1);
+        if (wv == 0 && khi > klo && lo <= hi) {
+          unsigned spins = 0;
+          for (int c0 = lo; c0 <= hi; c0 += kWave) {
+            const int bi = c0 + lane;
+            bool done = bi > hi;
+            for (;;) {
+              if (!done) done = ld_agent(&marks[bi]) != 0;
+              if (__all(done)) break;
+              if (++spins > kSpinLimit) {
+                if (lane == 0) atomicOr(&acc[3], 8ull);
+                break;
+              }
+              __builtin_amdgcn_s_sleep(1);
+            }
+          }
+        }
+        __syncthreads();
+        // ---- stores: K / V rows (nontemporal), pos, score
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          const int idx = tid + j * kFT;
+          const int r = idx / PR, part = idx % PR;
+          if (mv[j]) {
+            const int d = R0 + r;
+            const size_t off = ((size_t)L.dblk[r / kBlock] * kBlock + d % kBlock) * row_bytes +
+                               (size_t)part * 16;
+            st16_nt(P.k_pool + off, kv[j]);
+            st16_nt(P.v_pool + off, vv[j]);
+          }
+        }
+        if (tid < nr) {
+          const int d = R0 + tid, s = L.src[tid];
+          if (s != d) P.pos[urow + d] = my_pos;
+          so[d] = my_sc;
+          const bool moves = s != d;
+          const uint64_t mb = __ballot(moves), rb = __ballot(moves && s < n2);
+          if (lane == 0) {
+            atomicAdd(&L.moved, __popcll(mb));
+            atomicAdd(&L.at_risk, __popcll(rb));
+          }
+        }
+        __syncthreads();
+      }
+      if (tid == 0 && L.moved) {
+        atomicAdd(&acc[1], (unsigned long long)L.moved);
+        atomicAdd(&acc[2], (unsigned long long)L.at_risk);
+      }
+    }
+  }
+
+  // ------------------------------------------------------------ arrivals
+  __syncthreads();
+  if (tid == 0) L.last = atomicAdd(&P.head_done[u], 1u) == (uint32_t)(P.kh - 1) ? 1 : 0;
+  __syncthreads();
+  int before, total;
+  freed_prefix(pfx, L, before, total);
+  const int fc0 = *P.free_count;
+  const bool room = fc0 >= 0 && (long long)fc0 + total <= (long long)P.free_capacity;
+  if (L.last) {
+    if (consistent && m > 0) {
+      if (bad) {
+        if (tid == 0) atomicOr(&acc[3], 1ull);
+      } else {
+        const int lb0 = blocks_of(n2), lb1 = blocks_of(n);
+        int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
+        if (room) {
+          int32_t *fl = P.free_list + fc0 + before;
+          for (int i = tid; i < lb1 - lb0; i += kFT) {
+            fl[i] = bt[lb0 + i];
+            bt[lb0 + i] = -1;
+          }
+          if (tid == 0) atomicAdd(&acc[0], (unsigned long long)(lb1 - lb0));
+        }
+        const int nbatch = (n2 + kBatchRanks - 1) / kBatchRanks;
+        uint32_t *marks = P.marks + (size_t)u * P.marks_per_head;
+        for (int i = tid; i < nbatch; i += kFT) st_agent(&marks[i], 0u);
+      }
+      // the head's selection state for the next call
+      for (int i = tid; i < kSelectBins; i += kFT) {
+        st_agent(&P.hist[(size_t)u * kSelectBins + i], 0u);
+        st_agent(&P.hist2[(size_t)u * kSelectBins + i], 0u);
+      }
+      if (tid == 0) {
+        st_agent(&P.nmem[u], 0u);
+        st_agent(&P.arrive[u], 0u);
+      }
+    }
+    if (tid == 0) st_agent(&P.head_done[u], 0u);
+  }
+  __syncthreads();
+  if (tid == 0)
+    L.last = atomicAdd(&P.ctr[1], 1u) == (uint32_t)(P.units * P.kh - 1) ? 1 : 0;
+  __syncthreads();
+  if (!L.last) return;
+  // ---- the last workgroup of the launch: lengths, free count, stats, state
+  for (int i = tid; i < P.units; i += kFT) {
+    const int ni = P.seq_len[i];
+    if (ni >= 0 && ni <= P.max_slots && P.head_err[i] == 0) P.seq_len[i] = min(ni, P.budget);
+    st_agent(&P.head_err[i], 0u);
+  }
+  if (tid == 0) {
+    const unsigned long long freed = atomicExch(&acc[0], 0ull);
+    const unsigned long long moved = atomicExch(&acc[1], 0ull);
+    const unsigned long long risk = atomicExch(&acc[2], 0ull);
+    unsigned long long status = atomicExch(&acc[3], 0ull);
+    if (room) *P.free_count = fc0 + total;
+    else status |= 4ull;
+    P.stats[0] = (int64_t)freed;
+    P.stats[1] = (int64_t)moved;
+    P.stats[2] = (int64_t)(moved * 4ull * (unsigned long long)P.row_bytes);
+    P.stats[3] = (int64_t)risk;
+    P.stats[4] = (int64_t)status;
+    st_agent(&P.ctr[0], 0u);
+    st_agent(&P.ctr[1], 0u);
+  }
+}
+
+}  // namespace
+
+size_t finish_lds_bytes() { return sizeof(FinLds); }
+
+int finish_parts(int units, int rows_cap) {
+  // enough workgroups to cover the CUs twice, at most one per batch of ranks
+  const int batches = std::max(1, (rows_cap + kBatchRanks - 1) / kBatchRanks);
+  const int want = std::max(1, (512 + units - 1) / units);
+  return std::min(batches, want);
+}
+
+hipError_t launch_finish(const FinishArgs &a, hipStream_t s) {
+  const size_t lds = sizeof(FinLds);
+  const dim3 grid((unsigned)(a.units * a.kh));
+  switch (a.row_bytes / 16) {
+    case 8: hipLaunchKernelGGL(evict_finish_kernel<8>, grid, dim3(kFT), lds, s, a); break;
+    case 16: hipLaunchKernelGGL(evict_finish_kernel<16>, grid, dim3(kFT), lds, s, a); break;
+    case 32: hipLaunchKernelGGL(evict_finish_kernel<32>, grid, dim3(kFT), lds, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvev

@@ -8,8 +8,8 @@
 
 namespace kvev {
 
-// Per-head selection state and outputs, shared by the select kernels and the
-// fused score path (kvev_select_head.h).
+// Per-head selection state and outputs of the select kernels
+// (kvev_select_head.h).
 struct SelHead {
   int32_t *n_victims;
   uint32_t *hist;         // state [units][2048]: top 11 key bits (zero between calls)
@@ -38,14 +38,16 @@ struct ScoreArgs {
   const float *lse;
   const int32_t *q_pos;
   float *sum, *pooled, *drop;
+  const float *prev;             // ACCUMULATE: the running sums added to (normally `sum`)
+  uint32_t *head_err;            // optional [units]: set to 1 when a block id is outside the pool
+  // optional [units][2048]: the top 11 key bits of the written score over each
+  // head's candidate slots [0, n - sel_recent), for heads with n > sel_budget
+  uint32_t *hist;
+  int32_t sel_budget, sel_recent;
   int32_t units, Hkv, G, W, max_blocks, num_blocks;
   int32_t rows, row_tiles;       // G*W and ceil(rows / 16)
   int32_t flags, pool_r, halo_blocks, tile_blocks, tiles_per_head, threads;
   float c1;                      // scale * log2(e)
-  // fused selection (sel.hist != nullptr): the score kind sel_kind (1 sum,
-  // 2 pooled, 4 drop) is histogrammed into sel.hist as it is written
-  SelHead sel;
-  int32_t sel_kind;
 };
 
 struct SelectArgs {
@@ -56,19 +58,11 @@ struct SelectArgs {
   int32_t units, max_slots;
 };
 
-// The threshold steps after the histogram (collect, refine); the fused
-// path runs them after the score kernel built the histogram.
-hipError_t launch_select_threshold(const SelectArgs &a, hipStream_t s);
-
 struct CompactArgs {
   uint8_t *k_pool, *v_pool;
   int32_t *block_table, *seq_len, *pos;
   float *score;                 // optional score row moved with the tokens
   const int32_t *victims, *n_victims;
-  int32_t *victims_out;         // fused path: victims written by the prep step
-  const uint32_t *head_sel, *chunk_off;  // fused path: threshold and chunk offsets
-  const float *sel_score;       // fused path: the score row the threshold applies to
-  int32_t recent;               // fused path: protected recent window
   int32_t *free_list, *free_count;
   int64_t *stats;
   // workspace regions
@@ -84,6 +78,36 @@ struct CompactArgs {
       free_capacity, rows_per_item;
   int32_t rows_cap;             // kept rows per head are at most this (sizes the gather grid)
 };
+
+// The fused eviction pass after scoring (finish.hip): exact threshold,
+// victims and in-place compaction of every head in one launch.
+struct FinishArgs {
+  uint8_t *k_pool, *v_pool;
+  int32_t *block_table, *seq_len, *pos;
+  const float *sc;              // [units][max_slots] this pass's scores (workspace)
+  float *score_out;             // [units][max_slots] receives the compacted scores
+  int32_t *victims, *n_victims;
+  int32_t *free_list, *free_count;
+  int64_t *stats;
+  // state (zero between calls): bad-block flags and key histograms the
+  // scoring pass set, the bucket's second-level histograms, member counts
+  // and arrivals per head, per-batch "sources read" marks, workgroups done
+  // per head, the ticket and done counters, and the stat accumulators
+  uint32_t *head_err, *hist, *hist2, *nmem, *arrive, *marks, *head_done, *ctr;
+  unsigned long long *acc;      // [4]: blocks freed, rows moved, at-risk rows, status bits
+  // scratch: the bucket's (key, slot) members [units][max_slots], keys below
+  // the bucket per 1024-slot chunk [units][chunks]
+  uint2 *mem;
+  uint32_t *gbelow;
+  int32_t chunks;               // 1024-slot chunks per head
+  int32_t units, max_blocks, max_slots, num_blocks, row_bytes, budget, recent;
+  int32_t kh;                   // workgroups per head
+  int32_t marks_per_head;       // batches of 256 ranks a head can have
+  int32_t free_capacity;
+};
+hipError_t launch_finish(const FinishArgs &a, hipStream_t s);
+size_t finish_lds_bytes();
+int finish_parts(int units, int rows_cap);  // workgroups per head
 
 struct MeasureArgs {
   const int32_t *seq_len_before, *victims, *n_victims;
@@ -198,7 +222,6 @@ struct WindowAttnArgs {
 hipError_t launch_score(const ScoreArgs &a, int bf16, int head_dim, int drop, hipStream_t s);
 hipError_t launch_select(const SelectArgs &a, hipStream_t s);
 hipError_t launch_compact(const CompactArgs &a, hipStream_t s);
-hipError_t launch_evict_compact(const CompactArgs &a, hipStream_t s);
 hipError_t launch_window_attn(const WindowAttnArgs &a, int bf16, int head_dim, hipStream_t s);
 
 constexpr int kSelectChunk = 1024;      // victim offsets are kept per chunk of slots
@@ -207,19 +230,17 @@ constexpr int kSelectMaxChunks = 1024;  // chunks per head: up to 1M slots
 constexpr int kHistChunk = 4096;        // slots per select histogram workgroup
 constexpr int kCompactMaxUnits = 4096;  // compact.hip gather limit
 constexpr int kCompactChunk = 1024;     // compact.hip prep chunk (slots)
-// The fused pass's prep reads the selection's per-chunk victim offsets by its
-// own chunk index, and packs a head's chunk arrivals into 11 bits.
-static_assert(kCompactChunk == kSelectChunk, "prep chunks must be the selection's chunks");
-static_assert(kSelectMaxChunks < 2048, "chunk arrivals are counted in 11 bits");
+// Prep packs a head's chunk arrivals into 11 bits.
+static_assert(kSelectMaxChunks * kSelectChunk / kCompactChunk < 2048,
+              "chunk arrivals are counted in 11 bits");
 constexpr int kH2oMaxBudget = 4096;    // h2o_step.hip: tokens per head
 constexpr int kH2oMaxLogits = 16384;   // h2o_step.hip: G * budget (64 KB of LDS)
 constexpr int kH2oMaxSplit = 8;        // h2o_step.hip: workgroups per head
 constexpr int kVtokMaxUnits = 8192;    // vtoken.hip: heads per reclamation call (admission in LDS)
 constexpr int kVtokMaxSources = 4096;  // vtoken.hip: sources per head and call
 
-// LDS bytes of one score workgroup (fused: room for the tile histogram and
-// the head selection).
+// LDS bytes of one score workgroup (hist: with the tile's key histogram).
 __host__ __device__ size_t score_lds_bytes(int bf16, int head_dim, int drop, int row_tiles,
-                                            int tile_blocks, int halo_blocks, int fused);
+                                            int tile_blocks, int halo_blocks, int hist);
 
 }  // namespace kvev

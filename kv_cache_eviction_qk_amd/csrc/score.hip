@@ -20,10 +20,13 @@
 // LDS without any exchange between workgroups ([SNAP] "How it works").
 // No float atomics: results are bitwise reproducible.
 //
-// Fused with selection (kvev_evict), the tile also adds the top 11 key bits
-// of the score kind that drives eviction, over its candidate slots, into the
-// head's selection histogram (integer atomics), so no separate pass re-reads
-// the scores to build it.
+// For the fused eviction pass the scores go to a workspace row (the output
+// row is then written compacted), ACCUMULATE reads the running sums from
+// their own pointer, a tile that meets a block id outside the pool flags its
+// head (so that the pass leaves such a head's cache alone), and each tile
+// adds the top 11 key bits of its candidate slots' scores to its head's
+// histogram (LDS, then integer atomics), so the selection needs no pass of
+// its own over the scores.
 #include <hip/hip_runtime.h>
 
 #include "kvev_device.h"
@@ -52,7 +55,7 @@ __device__ __forceinline__ int remap_xcd(int id, int n) {
 
 }  // namespace
 
-template <bool BF16, int D, bool DROP, int kThreads, bool FUSED>
+template <bool BF16, int D, bool DROP, int kThreads>
 __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
   constexpr int kWaves = kThreads / kWave;
   using G_ = Geo<BF16, D>;
@@ -70,10 +73,9 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
   float *S_lds = an2 + (DROP ? RT * 16 : 0);
   const int span_blocks = P.tile_blocks + 2 * P.halo_blocks;
   float *D_lds = S_lds + span_blocks * 16;
-  // fused selection: the tile's histogram after the score layout
   uint32_t *hl = reinterpret_cast<uint32_t *>(
-      smem + ((score_lds_bytes(BF16, D, DROP, RT, P.tile_blocks, P.halo_blocks, 0) + 15) & ~size_t(15)));
-  constexpr bool fused = FUSED;
+      smem + ((score_lds_bytes(BF16, D, DROP, RT, P.tile_blocks, P.halo_blocks, 0) + 15) &
+              ~size_t(15)));  // tile histogram (with P.hist)
 
   const int wg = remap_xcd(blockIdx.x, gridDim.x);
   const int u = wg / P.tiles_per_head;
@@ -125,8 +127,8 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
   if (n <= 0 || n > max_slots) return;  // empty or inconsistent head: nothing to score
   const int nb = (n + kBlock - 1) / kBlock;
   if (tb0 >= nb) return;
-  const int sel_m = fused ? max(0, n - P.sel.budget) : 0;  // victims of the head
-  const int sel_nc = max(0, n - P.sel.recent);             // candidate slots
+  const bool want_hist = P.hist != nullptr && n > P.sel_budget;
+  const int sel_nc = n - P.sel_recent;  // candidate slots
   const int tb1 = min(tb0 + P.tile_blocks, nb);
   const int cb1 = min(nb, tb1 + P.halo_blocks);
   const int wb1 = min(wb1s, cb1);  // this wave's live blocks: [wb0, wb1)
@@ -134,6 +136,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
   const bool my_bad = (l < nwb) && (my_id < 0 || my_id >= P.num_blocks);
   const uint64_t bad_mask = __ballot(my_bad);
   if (my_bad) my_id = 0;  // a bad id loads block 0 and yields NaN scores
+  if (bad_mask && P.head_err && l == 0) atomicOr(&P.head_err[u], 1u);
 
   struct Frag {
     uint4 k[NB][U];
@@ -194,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
       an2[r] = r < rows ? ss : 0.f;
     }
   }
-  if (sel_m > 0)
+  if (want_hist)
     for (int i = threadIdx.x; i < kSelectBins; i += kThreads) hl[i] = 0;
   // earliest window query: keys at or before it are never masked
   int minq = qpw;
@@ -344,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         v[e] = S8[e];
-        if (P.flags & 8) v[e] += g0 + e < s1 ? P.sum[orow + g0 + e] : 0.f;
+        if (P.flags & 8) v[e] += g0 + e < s1 ? P.prev[orow + g0 + e] : 0.f;
         selv[e] = v[e];
       }
       put8(P.sum, v);
@@ -379,50 +382,46 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
         }
       }
       put8(P.pooled, v);
-      if (P.sel_kind == 2)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) selv[e] = v[e];
+      for (int e = 0; e < 8; ++e) selv[e] = v[e];
     }
     if constexpr (DROP) {
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = D_lds[min(g0 + e, span_end - 1) - base];
       put8(P.drop, v);
-      if (P.sel_kind == 4)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) selv[e] = v[e];
+      for (int e = 0; e < 8; ++e) selv[e] = v[e];
     }
-    if (sel_m > 0) {
+    if (want_hist) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (g0 + e < s1 && g0 + e < sel_nc) atomicAdd(&hl[score_key(selv[e]) >> 21], 1u);
     }
   }
-  if (sel_m == 0) return;
-
-  // ---- fused selection: add the tile histogram to the head's
+  if (!want_hist) return;
   __syncthreads();
-  uint32_t *hg = P.sel.hist + (size_t)u * kSelectBins;
+  uint32_t *hg = P.hist + (size_t)u * kSelectBins;
   for (int i = threadIdx.x; i < kSelectBins; i += kThreads)
     if (hl[i]) atomicAdd(&hg[i], hl[i]);
 }
 
 __host__ __device__ size_t score_lds_bytes(int bf16, int head_dim, int drop, int row_tiles,
-                                            int tile_blocks, int halo_blocks, int fused) {
+                                            int tile_blocks, int halo_blocks, int hist) {
   const size_t rowb = (size_t)head_dim * (bf16 ? 2 : 4);
   const size_t frag = (size_t)row_tiles * 16 * rowb;  // bytes of one staged row set
   size_t bytes = frag * (drop ? 2 : 1);
   bytes += (size_t)row_tiles * 16 * 4 * (drop ? 3 : 2);
   bytes += (size_t)(tile_blocks + 2 * halo_blocks) * 16 * 4 * (drop ? 2 : 1);
-  if (fused) bytes = ((bytes + 15) & ~size_t(15)) + kSelectBins * 4;  // tile histogram
+  if (hist) bytes = ((bytes + 15) & ~size_t(15)) + kSelectBins * 4;  // tile histogram
   return bytes;
 }
 
-template <bool BF16, int D, bool DROP, int T, bool FUSED>
+template <bool BF16, int D, bool DROP, int T>
 static hipError_t launch_t(const ScoreArgs &a, hipStream_t s) {
   const size_t lds = score_lds_bytes(BF16, D, DROP, a.row_tiles, a.tile_blocks, a.halo_blocks,
-                                     FUSED);
-  auto fn = score_kernel<BF16, D, DROP, T, FUSED>;
+                                     a.hist != nullptr);
+  auto fn = score_kernel<BF16, D, DROP, T>;
   static size_t lds_set = 0;  // largest dynamic LDS size enabled for this variant
   if (lds > 65536 && lds > lds_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
@@ -437,10 +436,8 @@ static hipError_t launch_t(const ScoreArgs &a, hipStream_t s) {
 
 template <bool BF16, int D, bool DROP>
 static hipError_t launch_threads(const ScoreArgs &a, hipStream_t s) {
-  const bool fused = a.sel.hist != nullptr;
-  if (a.threads == 512)
-    return fused ? launch_t<BF16, D, DROP, 512, true>(a, s) : launch_t<BF16, D, DROP, 512, false>(a, s);
-  return fused ? launch_t<BF16, D, DROP, 256, true>(a, s) : launch_t<BF16, D, DROP, 256, false>(a, s);
+  if (a.threads == 512) return launch_t<BF16, D, DROP, 512>(a, s);
+  return launch_t<BF16, D, DROP, 256>(a, s);
 }
 
 hipError_t launch_score(const ScoreArgs &a, int bf16, int head_dim, int drop, hipStream_t s) {

@@ -144,21 +144,15 @@ __global__ __launch_bounds__(kEmitThreads) void select_emit_kernel(const SelectA
     }
 }
 
-hipError_t launch_select_threshold(const SelectArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(select_collect_kernel, dim3(a.sel.nwg, a.units), dim3(kSelThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(select_refine_kernel, dim3(a.units), dim3(kSelThreads), sizeof(RefineLds), s,
-                     a);
-  return hipGetLastError();
-}
-
 hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(select_hist_kernel, dim3(a.sel.nwg, a.units), dim3(kHistThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_select_threshold(a, s);
-  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(select_collect_kernel, dim3(a.sel.nwg, a.units), dim3(kSelThreads), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(select_refine_kernel, dim3(a.units), dim3(kSelThreads), sizeof(RefineLds), s,
+                     a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(select_emit_kernel, dim3(a.sel.chunks, a.units), dim3(kEmitThreads), 0, s, a);
   return hipGetLastError();
 }
