@@ -261,6 +261,15 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
     uint32_t hv[kSelectBins / kFT];
 #pragma unroll
     for (int q = 0; q < kSelectBins / kFT; ++q) hv[q] = hg[tid + q * kFT];
+    // block ids of the share's first groups, where a batch's sources mostly
+    // lie (batch k of a head usually draws on group k)
+    const int32_t *btu = P.block_table + (size_t)u * P.max_blocks;
+    const int pb0 = g_lo * (kGrp / kBlock);
+    const int pbid = !bad && pb0 + tid < blocks_of(n) ? btu[pb0 + tid] : 0;
+    // and the destination block ids of this workgroup's first batch
+    const int pdid = !bad && tid < kBatchRanks / kBlock &&
+                             k * (kBatchRanks / kBlock) + tid < blocks_of(n - m)
+                         ? btu[k * (kBatchRanks / kBlock) + tid] : 0;
     if (res) {
 #pragma unroll
       for (int q = 0; q < kRes; ++q)
@@ -373,7 +382,7 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
       for (int q = 0; q < 4; ++q) {
         const bool v = i0 + q * kFT + tid < nmem;
         const uint32_t p = pr[q].x >> 10;
-        wave_count_add(L.cv, (int)pr[q].y / kChunk, v && p < pre);
+        if (v && p < pre) atomicAdd(&L.cv[pr[q].y / kChunk], 1u);
         const bool sb = v && p == pre;
         if (sb) atomicAdd(&L.h[pr[q].x & 1023u], 1u);
         const uint64_t sm = __ballot(sb);
@@ -447,11 +456,9 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
     }
     // the sub-bucket's victims per chunk, then the chunks' offsets
     if (sub_lds) {
-      for (int i0 = 0; i0 < nsub; i0 += kFT) {  // wave-uniform
-        const int i = i0 + tid;
-        const uint2 p = i < nsub ? L.sub[i] : make_uint2(0u, 0u);
-        wave_count_add(L.cv, (int)p.y / kChunk,
-                       i < nsub && (p.x < T || (p.x == T && (int)p.y <= cut)));
+      for (int i = tid; i < nsub; i += kFT) {
+        const uint2 p = L.sub[i];
+        if (p.x < T || (p.x == T && (int)p.y <= cut)) atomicAdd(&L.cv[p.y / kChunk], 1u);
       }
     } else {
       for_sub([&](uint32_t key, int s) {
@@ -527,14 +534,19 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
         }
         return lo;
       };
+      int b0 = pb0;  // first block whose id L.blk holds
+      L.blk[tid] = pbid;
       for (int rho = k; rho < nbatch; rho += P.kh) {
         const int R0 = rho * kBatchRanks, R1 = min(R0 + kBatchRanks, n2);
         const int gs = chunk_of_rank(R0) / 4;  // group of the first source
-        // block ids: the destinations', and the first source groups' (one
-        // round of loads, in flight while the groups are ranked)
-        const int b0 = gs * (kGrp / kBlock);
-        const int bid = b0 + tid < blocks_of(n) ? bt[b0 + tid] : 0;
-        const int did = tid < kBatchRanks / kBlock && R0 / kBlock + tid < blocks_of(n2)
+        // block ids: the destinations', and the first source groups' unless
+        // the prefetched ones cover them (loads in flight while the groups
+        // are ranked)
+        const bool fresh = gs * (kGrp / kBlock) < b0 || gs * (kGrp / kBlock) >= b0 + kPreBlk;
+        const int bid = fresh && gs * (kGrp / kBlock) + tid < blocks_of(n)
+                            ? bt[gs * (kGrp / kBlock) + tid] : 0;
+        const int did = rho == k ? pdid
+                        : tid < kBatchRanks / kBlock && R0 / kBlock + tid < blocks_of(n2)
                             ? bt[R0 / kBlock + tid] : 0;
         // rank each kept slot of group g; record the sources of [R0, R1)
         for (int g = gs; g < ngrp_all && kbc(4 * g) < R1; ++g) {
@@ -559,7 +571,11 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
             }
           }
         }
-        L.blk[tid] = bid;
+        if (fresh) {
+          __syncthreads();  // the previous batch's readers of blk are done
+          L.blk[tid] = bid;
+          b0 = gs * (kGrp / kBlock);
+        }
         if (tid < kBatchRanks / kBlock) L.dblk[tid] = did;
         __syncthreads();
         // ---- loads: source block ids (prefetched, else loaded), K / V
