@@ -145,7 +145,7 @@ def main():
     nb = case["num_blocks"]
     free_lists = [torch.full((nb,), -1, dtype=torch.int32, device="cuda") for _ in range(copies)]
     free_counts = [torch.zeros(1, dtype=torch.int32, device="cuda") for _ in range(copies)]
-    ws = K.new_workspace(pristine)
+    ws = K.new_workspace(pristine, G, W)  # room for split windows
     score_out = pristine.score_buffer()
     victims = torch.empty((B, Hkv, pristine.max_slots), dtype=torch.int32, device="cuda")
     n_victims = torch.empty((B, Hkv), dtype=torch.int32, device="cuda")
@@ -183,7 +183,7 @@ def main():
         if ev is not None:
             ev[0].record()
         K.score(c, q, lse, q_pos, cfg.softmax_scale, G, flag, cfg.pool_kernel, sum=outs["sum"],
-                pooled=outs["pooled"], drop=outs["drop"], a=a)
+                pooled=outs["pooled"], drop=outs["drop"], a=a, workspace=ws)
         if ev is not None:
             ev[1].record()
         K.select(c, score_out, cfg.budget, cfg.recent, victims, n_victims, ws)
@@ -249,7 +249,7 @@ def main():
     s0.record()
     for i in range(steps):
         K.score(caches[i], q, lse, q_pos, cfg.softmax_scale, G, flag, cfg.pool_kernel,
-                sum=outs["sum"], pooled=outs["pooled"], drop=outs["drop"], a=a)
+                sum=outs["sum"], pooled=outs["pooled"], drop=outs["drop"], a=a, workspace=ws)
     s1.record()
     torch.cuda.synchronize()
     t_score_alone = s0.elapsed_time(s1) / steps
@@ -552,7 +552,7 @@ def bench_decode_accumulate(args, cfg):
         score.zero_()
         for t in range(T):
             K.score(views[t], qs[t], lses[t], qps[t], cfg.softmax_scale, G, K.SUM | K.ACCUMULATE,
-                    1, sum=score)
+                    1, sum=score, workspace=ws)
 
     def schedule():
         scoring()
@@ -1099,10 +1099,10 @@ def cpu_baseline(case, cfg, kind):
     lse64, a64 = oracle.lse_a(case, want_a=(kind == "drop"), units=sample, nthreads=threads)
     import synth
     lse32 = lse64.astype(np.float32)
-    a_enc = synth.encode(a64, cfg.dtype) if a64 is not None else None
+    a32 = a64.astype(np.float32) if a64 is not None else None
     flag = {"sum": oracle.SUM, "pool": oracle.POOL, "drop": oracle.DROP}[kind]
     t0 = time.perf_counter()
-    out = oracle.score(case, lse32, flag, cfg.pool_kernel, a_enc=a_enc, units=sample,
+    out = oracle.score(case, lse32, flag, cfg.pool_kernel, a32=a32, units=sample,
                        nthreads=threads)
     key = {"sum": "sum", "pool": "pooled", "drop": "drop"}[kind]
     s32 = np.nan_to_num(out[key], nan=0.0).astype(np.float32)

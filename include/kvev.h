@@ -55,7 +55,7 @@ extern "C" {
 #endif
 
 #define KVEV_BLOCK_SIZE 16
-#define KVEV_ABI_VERSION 14
+#define KVEV_ABI_VERSION 15
 
 typedef enum {
   KVEV_OK = 0,
@@ -95,7 +95,8 @@ typedef struct kvev_window {
   int32_t obs_window;   /* W window queries per query head, >= 1 */
   const void *q;        /* [batch][kv_heads*group][W][head_dim], cache dtype */
   const float *lse;     /* [batch][kv_heads*group][W]: log-sum-exp of scale*q.k */
-  const void *a;        /* [batch][kv_heads*group][W][head_dim], cache dtype; DROP only */
+  const float *a;       /* [batch][kv_heads*group][W][head_dim], fp32 (the forward
+                           pass's attention output, whatever the cache dtype); DROP only */
   const int32_t *q_pos; /* [batch][W] positions of the window queries (causal mask) */
   float scale;          /* softmax scale applied to q.k, usually 1/sqrt(head_dim) */
 } kvev_window;
@@ -115,7 +116,10 @@ typedef struct kvev_window {
  *   KVEV_POOL: pooled[j] = max over i in [j-r, j+r] clamped to [0, n-1] of
  *              sum_{w,g} p at i, r = (pool_kernel-1)/2 ([SNAP] "How it works").
  *   KVEV_DROP: drop[j] = sum_{w,g} p/(1-p) * ||a_{g,w} - v_j|| ([DROP] Lemma 1
- *              and the window sum), +inf for a term with p >= 1.
+ *              and the window sum), +inf for a term with p >= 1.  Terms
+ *              with p >= 1/4 are computed in double from the rows (the
+ *              term's rounding error grows as 1/(1-p)); the others in fp32,
+ *              a.v from a's bf16 high and low parts on bf16 caches.
  * Outputs are fp32 [batch][kv_heads][max_blocks*16]; only slots [0, n) are
  * written.  Pass NULL for kinds not requested.  Reductions use a fixed order:
  * results are bitwise reproducible run to run.
@@ -124,9 +128,13 @@ typedef struct kvev_window {
  * window is refused); flags empty or unknown; POOL without `pooled`, or
  * pool_kernel < 1 or even ([SNAP] Parameters); DROP without `a` or `drop`;
  * SUM without `sum`; ACCUMULATE without SUM or combined with POOL or DROP.
- * KVEV_EUNSUPPORTED: group*obs_window above 4096, or window rows that do not
- * fit a workgroup's 160 KB of LDS with the tile (bf16, head_dim 128: about
- * 540 rows, 270 with DROP).  No workspace is used; `workspace` may be NULL.
+ * KVEV_EUNSUPPORTED: group*obs_window above 4096.  Window rows that do not
+ * fit a workgroup's 160 KB of LDS beside a 16-block tile (bf16, head_dim
+ * 128: about 540 rows, 180 with DROP) are split over several workgroups per
+ * tile; their raw sums then go to `workspace` past the part the other entry
+ * points use (16-byte aligned, kvev_workspace_bytes(cache, group,
+ * obs_window) bytes, else KVEV_ENOSPACE).  Windows that fit use no
+ * workspace; `workspace` may then be NULL.
  */
 int kvev_score(const kvev_cache *cache, const kvev_window *win, int32_t flags,
                int32_t pool_kernel, float *sum, float *pooled, float *drop, void *workspace,
@@ -560,17 +568,19 @@ size_t kvev_vtok_check_workspace_bytes(const kvev_cache *cache);
  * FlashAttention-style forward pass would produce ([DROP] Jargon,
  * "Log-sum-exp"; "Why does the Triton kernel matter").
  *     lse_out[b][hq][w] = log sum_{pos_j <= q_pos[w]} exp(scale * q.k_j)   (fp32)
- *     a_out[b][hq][w][:] = sum_j exp(scale * q.k_j - lse) v_j           (cache dtype, may be NULL)
+ *     a_out[b][hq][w][:] = sum_j exp(scale * q.k_j - lse) v_j           (fp32, may be NULL)
  * fp32 arithmetic throughout.  A query that attends no key gets lse = -inf
  * and a = 0.  Workspace: at least kvev_workspace_bytes(cache, group, W).
  * Errors as for kvev_score; KVEV_ENOSPACE for a short workspace.
  */
 int kvev_window_attn(const kvev_cache *cache, const kvev_window *win, float *lse_out,
-                     void *a_out, void *workspace, size_t ws_bytes, void *stream);
+                     float *a_out, void *workspace, size_t ws_bytes, void *stream);
 
-/* Workspace bytes needed by kvev_select, kvev_compact, kvev_evict and (for this window
- * shape; pass 1, 1 when unused) kvev_window_attn on this cache shape.
- * 0 for a bad cache. */
+/* Workspace bytes needed by kvev_select, kvev_compact, kvev_evict, kvev_score
+ * and kvev_window_attn on this cache shape with this window shape (group,
+ * obs_window); pass 0, 0 for calls without a window (kvev_select,
+ * kvev_compact).  Windows too large for one workgroup's LDS add room for
+ * their split rows' raw sums.  0 for a bad cache. */
 size_t kvev_workspace_bytes(const kvev_cache *cache, int32_t group, int32_t obs_window);
 
 /* Static description of a status code. */

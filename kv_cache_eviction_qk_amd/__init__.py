@@ -38,7 +38,7 @@ EXPORTS = ("kvev_score", "kvev_select", "kvev_compact", "kvev_evict", "kvev_meas
            "kvev_vtok_map_workspace_bytes",
            "kvev_window_attn",
            "kvev_workspace_bytes", "kvev_strerror", "kvev_abi_version")
-ABI_VERSION = 14
+ABI_VERSION = 15
 
 
 class KvevError(RuntimeError):
@@ -231,7 +231,7 @@ def _window(cache: Cache, q, lse, q_pos, scale, group, a=None) -> WindowStruct:
     if lse is not None:
         _need(lse, "lse", torch.float32, B * Hkv * group * W)
     if a is not None:
-        _need(a, "a", cache.k_pool.dtype, q.numel())
+        _need(a, "a", torch.float32, q.numel())  # the forward pass's output, fp32
     _need(q_pos, "q_pos", torch.int32, B * W)
     return WindowStruct(group, W, _ptr(q), _ptr(lse), _ptr(a), _ptr(q_pos), float(scale))
 
@@ -251,11 +251,16 @@ def new_workspace(cache: Cache, group: int = 1, obs_window: int = 1) -> torch.Te
 def score(cache: Cache, q: torch.Tensor, lse: torch.Tensor, q_pos: torch.Tensor, scale: float,
           group: int, flags: int, pool_kernel: int = 1, sum: Optional[torch.Tensor] = None,
           pooled: Optional[torch.Tensor] = None, drop: Optional[torch.Tensor] = None,
-          a: Optional[torch.Tensor] = None, stream=None) -> dict:
-    """kvev_score.  Output buffers are allocated (filled with 0) when not given."""
+          a: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+          stream=None) -> dict:
+    """kvev_score.  Output buffers are allocated (filled with 0) when not given;
+    so is the workspace, which only windows too large for one workgroup use."""
     L = load_library()
     c = cache.struct()
     w = _window(cache, q, lse, q_pos, scale, group, a)
+    if workspace is None:
+        workspace = new_workspace(cache, group, q.shape[2])
+    _need(workspace, "workspace", torch.uint8)
     if flags & SUM and sum is None:
         sum = cache.score_buffer()
     if flags & POOL and pooled is None:
@@ -266,7 +271,8 @@ def score(cache: Cache, q: torch.Tensor, lse: torch.Tensor, q_pos: torch.Tensor,
         if t is not None:
             _need(t, nm, torch.float32, cache.units * cache.max_slots)
     rc = L.kvev_score(ctypes.byref(c), ctypes.byref(w), flags, pool_kernel, _ptr(sum),
-                      _ptr(pooled), _ptr(drop), None, 0, _stream(stream))
+                      _ptr(pooled), _ptr(drop), _ptr(workspace), workspace.numel(),
+                      _stream(stream))
     _check(rc, "kvev_score")
     return {"sum": sum, "pooled": pooled, "drop": drop}
 
@@ -682,7 +688,7 @@ def ring_step(cache: Cache, state: RingState, q: torch.Tensor, k_new: torch.Tens
 def window_attn(cache: Cache, q: torch.Tensor, q_pos: torch.Tensor, scale: float, group: int,
                 workspace: torch.Tensor, want_a: bool = False, lse_out=None, a_out=None,
                 stream=None):
-    """kvev_window_attn -> (lse fp32 [B, Hq, W], a [B, Hq, W, D] in the cache dtype or None)."""
+    """kvev_window_attn -> (lse fp32 [B, Hq, W], a fp32 [B, Hq, W, D] or None)."""
     L = load_library()
     c = cache.struct()
     w = _window(cache, q, None, q_pos, scale, group)
@@ -690,9 +696,9 @@ def window_attn(cache: Cache, q: torch.Tensor, q_pos: torch.Tensor, scale: float
         lse_out = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     _need(lse_out, "lse_out", torch.float32, q.shape[0] * q.shape[1] * q.shape[2])
     if want_a and a_out is None:
-        a_out = torch.empty_like(q)
+        a_out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     if a_out is not None:
-        _need(a_out, "a_out", q.dtype, q.numel())
+        _need(a_out, "a_out", torch.float32, q.numel())
     _need(workspace, "workspace", torch.uint8)
     rc = L.kvev_window_attn(ctypes.byref(c), ctypes.byref(w), _ptr(lse_out), _ptr(a_out),
                             _ptr(workspace), workspace.numel(), _stream(stream))

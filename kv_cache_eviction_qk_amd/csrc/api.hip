@@ -179,6 +179,33 @@ WaLayout wa_layout(const kvev_cache *c, int group, int obs_window) {
 
 int map_err(hipError_t e) { return e == hipSuccess ? KVEV_OK : KVEV_EDEVICE; }
 
+// Window rows a score workgroup stages: split over several workgroups per
+// tile when they do not fit in LDS beside a 16-block tile (DropKV stages a
+// second and, for bf16, a third copy of each row).  Returns the parts;
+// *rt_part receives the row tiles of each.
+int score_row_parts(int bf16, int head_dim, int drop, int row_tiles, int *rt_part) {
+  int parts = 1, rtp = row_tiles;
+  while (rtp > 1 &&
+         kvev::score_lds_bytes(bf16, head_dim, drop, rtp, 16, 0, 1) > kMaxLds - 1024) {
+    ++parts;
+    rtp = (row_tiles + parts - 1) / parts;
+  }
+  *rt_part = rtp;
+  return (row_tiles + rtp - 1) / rtp;
+}
+
+// Workspace bytes of the split windows' raw sums (0 when the rows fit).
+size_t score_parts_bytes(const kvev_cache *c, int32_t group, int32_t obs_window, int drop,
+                         int want_sum) {
+  if (group < 1 || obs_window < 1) return 0;
+  int rtp;
+  const int parts = score_row_parts(c->dtype == KVEV_BF16, c->head_dim, drop,
+                                    (group * obs_window + 15) / 16, &rtp);
+  if (parts == 1) return 0;
+  const size_t row = (size_t)c->batch * c->kv_heads * c->max_blocks * KVEV_BLOCK_SIZE * 4;
+  return a256((size_t)parts * row * ((want_sum ? 1 : 0) + (drop ? 1 : 0)));
+}
+
 int check_window(const kvev_cache *c, const kvev_window *w) {
   if (!w || !w->q || !w->lse || !w->q_pos) return KVEV_EINVAL;
   if (w->group < 1 || w->obs_window < 1) return KVEV_EINVAL;
@@ -312,7 +339,8 @@ const char *kvev_strerror(int status) {
 
 size_t kvev_workspace_bytes(const kvev_cache *cache, int32_t group, int32_t obs_window) {
   if (!valid_cache(cache)) return 0;
-  size_t need = main_layout_total(cache);
+  // the main workspace, then (large windows) the split rows' raw sums
+  size_t need = main_layout_total(cache) + score_parts_bytes(cache, group, obs_window, 1, 1);
   if (group >= 1 && obs_window >= 1) {
     const size_t wa = wa_layout(cache, group, obs_window).total;
     if (wa > need) need = wa;
@@ -329,6 +357,7 @@ namespace {
 int build_score_args(const kvev_cache *cache, const kvev_window *win, int32_t flags,
                      int32_t pool_kernel, float *sum, float *pooled, float *drop, int hist,
                      kvev::ScoreArgs &a) {
+  // (split windows: the caller points part_sum / part_drop at its workspace)
   if (!valid_cache(cache)) return KVEV_EINVAL;
   int rc = check_window(cache, win);
   if (rc) return rc;
@@ -350,7 +379,7 @@ int build_score_args(const kvev_cache *cache, const kvev_window *win, int32_t fl
   a.seq_len = cache->seq_len;
   a.pos = cache->pos;
   a.q = static_cast<const uint8_t *>(win->q);
-  a.a = static_cast<const uint8_t *>(win->a);
+  a.a = win->a;
   a.lse = win->lse;
   a.q_pos = win->q_pos;
   a.sum = sum;
@@ -368,7 +397,13 @@ int build_score_args(const kvev_cache *cache, const kvev_window *win, int32_t fl
   a.row_tiles = (a.rows + 15) / 16;
   a.flags = flags & (KVEV_SUM | KVEV_POOL | KVEV_ACCUMULATE);
   a.pool_r = (flags & KVEV_POOL) ? (pool_kernel - 1) / 2 : 0;
-  a.halo_blocks = (a.pool_r + KVEV_BLOCK_SIZE - 1) / KVEV_BLOCK_SIZE;
+  const int bf16 = cache->dtype == KVEV_BF16;
+  const int is_drop = (flags & KVEV_DROP) ? 1 : 0;
+  a.row_parts = score_row_parts(bf16, cache->head_dim, is_drop, a.row_tiles, &a.rt_part);
+  if (a.row_parts > 1) hist = 0;  // the combine pass builds the histogram
+  // split windows pool in the combine pass: no halo blocks
+  a.halo_blocks =
+      a.row_parts > 1 ? 0 : (a.pool_r + KVEV_BLOCK_SIZE - 1) / KVEV_BLOCK_SIZE;
   // Up to 8 waves (512 threads) share one staging of the window rows and
   // split a tile of up to 256 blocks; smaller tiles when the tiles would not
   // cover the 256 CUs, and down to two tiles per CU while what each tile
@@ -379,18 +414,21 @@ int build_score_args(const kvev_cache *cache, const kvev_window *win, int32_t fl
   // not); smaller again when the staged window rows plus the tile's score
   // rows exceed a workgroup's LDS (large G*W windows); fewer waves for small
   // tiles.
-  const int bf16 = cache->dtype == KVEV_BF16;
-  const int is_drop = (flags & KVEV_DROP) ? 1 : 0;
   auto lds_of = [&](int t) {
-    return kvev::score_lds_bytes(bf16, cache->head_dim, is_drop, a.row_tiles, t, a.halo_blocks,
+    return kvev::score_lds_bytes(bf16, cache->head_dim, is_drop, a.rt_part, t, a.halo_blocks,
                                  hist);
   };
-  int tb = KV_TILE_MAX, threads = KV_THREADS_MAX;
-  auto tiles_of = [&](int t) { return (int64_t)a.units * ((cache->max_blocks + t - 1) / t); };
+  // fp32 DropKV at head_dim 128: two stages of key and value fragments fill
+  // 256 registers, so one wave per SIMD (4 waves, 512 registers each)
+  const int max_threads = (!bf16 && cache->head_dim == 128 && is_drop) ? 256 : KV_THREADS_MAX;
+  int tb = KV_TILE_MAX, threads = max_threads;
+  auto tiles_of = [&](int t) {
+    return (int64_t)a.units * ((cache->max_blocks + t - 1) / t) * a.row_parts;
+  };
   while (tb > 16 && tiles_of(tb) < 256) tb /= 2;
   const int64_t row_bytes = (int64_t)cache->head_dim * (bf16 ? 2 : 4);
   const int64_t block_bytes = (int64_t)KVEV_BLOCK_SIZE * row_bytes * (is_drop ? 2 : 1);
-  const int64_t staged = (int64_t)a.row_tiles * 16 * row_bytes * (is_drop ? 2 : 1) +
+  const int64_t staged = (int64_t)a.rt_part * 16 * row_bytes * (is_drop ? (bf16 ? 3 : 2) : 1) +
                          2 * (int64_t)a.halo_blocks * block_bytes;
   while (tb > 16 && tiles_of(tb) < 512 && staged * 16 <= (int64_t)(tb / 2) * block_bytes) tb /= 2;
   while (tb > 1 && lds_of(tb) > kMaxLds - 1024) tb /= 2;
@@ -402,8 +440,19 @@ int build_score_args(const kvev_cache *cache, const kvev_window *win, int32_t fl
   a.threads = threads;
   a.tiles_per_head = (cache->max_blocks + tb - 1) / tb;
   a.c1 = win->scale * 1.4426950408889634f;
-  if ((int64_t)a.units * a.tiles_per_head > INT32_MAX) return KVEV_EUNSUPPORTED;
+  a.scale = win->scale;
+  if ((int64_t)a.units * a.tiles_per_head * a.row_parts > INT32_MAX) return KVEV_EUNSUPPORTED;
   return KVEV_OK;
+}
+
+// Points a split window's raw sums at `ws` (the caller checked its size).
+void set_score_parts(kvev::ScoreArgs &a, const kvev_cache *c, uint8_t *ws) {
+  if (a.row_parts == 1) return;
+  const size_t row = (size_t)a.units * c->max_blocks * KVEV_BLOCK_SIZE;
+  float *p = reinterpret_cast<float *>(ws);
+  const bool want_sum = (a.flags & (KVEV_SUM | KVEV_POOL)) != 0;
+  a.part_sum = want_sum ? p : nullptr;
+  a.part_drop = a.drop ? p + (want_sum ? (size_t)a.row_parts * row : 0) : nullptr;
 }
 
 // Fills the compaction argument block (workspace pointers included).
@@ -640,11 +689,19 @@ int kvev_vtok_check(const kvev_cache *cache, const uint8_t *live, const int32_t 
 int kvev_score(const kvev_cache *cache, const kvev_window *win, int32_t flags,
                int32_t pool_kernel, float *sum, float *pooled, float *drop, void *workspace,
                size_t ws_bytes, void *stream) {
-  (void)workspace;
-  (void)ws_bytes;
   kvev::ScoreArgs a;
   const int rc = build_score_args(cache, win, flags, pool_kernel, sum, pooled, drop, 0, a);
   if (rc) return rc;
+  if (a.row_parts > 1) {
+    // the split rows' raw sums go to the workspace past its main part (whose
+    // state the other entry points keep)
+    const size_t need = main_layout_total(cache) +
+                        score_parts_bytes(cache, win->group, win->obs_window, a.drop != nullptr,
+                                          (a.flags & (KVEV_SUM | KVEV_POOL)) != 0);
+    if (!workspace || ws_bytes < need) return KVEV_ENOSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 15) return KVEV_EINVAL;
+    set_score_parts(a, cache, static_cast<uint8_t *>(workspace) + main_layout_total(cache));
+  }
   return map_err(kvev::launch_score(a, cache->dtype == KVEV_BF16, cache->head_dim,
                                     (flags & KVEV_DROP) ? 1 : 0, static_cast<hipStream_t>(stream)));
 }
@@ -715,8 +772,11 @@ int kvev_evict(const kvev_cache *cache, const kvev_window *win, int32_t flags,
   if ((size_t)cache->max_blocks * KVEV_BLOCK_SIZE >
       (size_t)kvev::kSelectMaxChunks * kvev::kSelectChunk)
     return KVEV_EUNSUPPORTED;  // 1M slots per head
-  if (!workspace || ws_bytes < main_layout_total(cache)) return KVEV_ENOSPACE;
+  const size_t parts_bytes = score_parts_bytes(cache, win->group, win->obs_window,
+                                               kind == KVEV_DROP, kind != KVEV_DROP);
+  if (!workspace || ws_bytes < main_layout_total(cache) + parts_bytes) return KVEV_ENOSPACE;
   uint8_t *ws = static_cast<uint8_t *>(workspace);
+  set_score_parts(a, cache, ws + main_layout_total(cache));
   a.prev = score;  // ACCUMULATE: the running sums are in the output row
   a.head_err = reinterpret_cast<uint32_t *>(ws + S.fin_err);
   a.hist = reinterpret_cast<uint32_t *>(ws + S.hist);
@@ -766,7 +826,7 @@ int kvev_evict(const kvev_cache *cache, const kvev_window *win, int32_t flags,
 }
 
 int kvev_window_attn(const kvev_cache *cache, const kvev_window *win, float *lse_out,
-                     void *a_out, void *workspace, size_t ws_bytes, void *stream) {
+                     float *a_out, void *workspace, size_t ws_bytes, void *stream) {
   if (!valid_cache(cache) || !win || !win->q || !win->q_pos || !lse_out) return KVEV_EINVAL;
   if (win->group < 1 || win->obs_window < 1) return KVEV_EINVAL;
   if ((int64_t)win->group * win->obs_window > 4096) return KVEV_EUNSUPPORTED;
@@ -783,7 +843,7 @@ int kvev_window_attn(const kvev_cache *cache, const kvev_window *win, float *lse
   a.q = static_cast<const uint8_t *>(win->q);
   a.q_pos = win->q_pos;
   a.lse_out = lse_out;
-  a.a_out = static_cast<uint8_t *>(a_out);
+  a.a_out = a_out;
   a.part_m = reinterpret_cast<float *>(ws + L.part_m);
   a.part_l = reinterpret_cast<float *>(ws + L.part_l);
   a.part_acc = reinterpret_cast<float *>(ws + L.part_acc);

@@ -34,7 +34,8 @@ __device__ __forceinline__ bool unit_budget(const SelHead &S, int u, int &budget
 struct ScoreArgs {
   const uint8_t *k_pool, *v_pool;
   const int32_t *block_table, *seq_len, *pos;
-  const uint8_t *q, *a;
+  const uint8_t *q;
+  const float *a;                // DROP: fp32 [B][Hq][W][D]
   const float *lse;
   const int32_t *q_pos;
   float *sum, *pooled, *drop;
@@ -48,6 +49,12 @@ struct ScoreArgs {
   int32_t rows, row_tiles;       // G*W and ceil(rows / 16)
   int32_t flags, pool_r, halo_blocks, tile_blocks, tiles_per_head, threads;
   float c1;                      // scale * log2(e)
+  float scale;                   // the softmax scale itself (exact DropKV terms)
+  // rows split over row_parts workgroups per tile, rt_part row tiles each;
+  // with row_parts > 1 the parts' raw sums go to part_sum / part_drop
+  // [row_parts][units][max_slots] (workspace) and a combine pass finishes
+  int32_t row_parts, rt_part;
+  float *part_sum, *part_drop;
 };
 
 struct SelectArgs {
@@ -213,7 +220,7 @@ struct WindowAttnArgs {
   const uint8_t *q;
   const int32_t *q_pos;
   float *lse_out;
-  uint8_t *a_out;
+  float *a_out;                        // fp32 [B][Hq][W][D]
   float *part_m, *part_l, *part_acc;   // workspace partials
   int32_t units, Hkv, G, W, max_blocks, num_blocks, rows, chunk_slots, chunks, want_a;
   float scale;
@@ -238,6 +245,9 @@ constexpr int kH2oMaxLogits = 16384;   // h2o_step.hip: G * budget (64 KB of LDS
 constexpr int kH2oMaxSplit = 8;        // h2o_step.hip: workgroups per head
 constexpr int kVtokMaxUnits = 8192;    // vtoken.hip: heads per reclamation call (admission in LDS)
 constexpr int kVtokMaxSources = 4096;  // vtoken.hip: sources per head and call
+// score.hip: DropKV terms with p >= 1/4 queued for the exact pass, per staged
+// window row (weights of one row sum to 1: at most four reach 1/4)
+constexpr int kExactPerRow = 4;
 
 // LDS bytes of one score workgroup (hist: with the tile's key histogram).
 __host__ __device__ size_t score_lds_bytes(int bf16, int head_dim, int drop, int row_tiles,

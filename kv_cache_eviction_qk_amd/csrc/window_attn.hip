@@ -32,12 +32,6 @@ __device__ __forceinline__ float load_elem(const uint8_t *base, size_t idx) {
   }
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
 }  // namespace
 
 template <bool BF16, int D>
@@ -161,11 +155,7 @@ __global__ __launch_bounds__(D) void window_attn_combine_kernel(const WindowAttn
   const size_t orow = ((size_t)b * Hq + (size_t)h * P.G) * P.W + row;
   if (d == 0) P.lse_out[orow] = (L > 0.f) ? M + logf(L) : -__builtin_inff();
   if (P.want_a) {
-    const float a = (L > 0.f) ? A / L : 0.f;
-    if constexpr (BF16)
-      reinterpret_cast<uint16_t *>(P.a_out)[orow * D + d] = f32_to_bf16_rne(a);
-    else
-      reinterpret_cast<float *>(P.a_out)[orow * D + d] = a;
+    P.a_out[orow * D + d] = (L > 0.f) ? A / L : 0.f;  // fp32 whatever the cache dtype
   }
 }
 

@@ -108,8 +108,11 @@ def _cache(case: dict) -> Cache:
 
 
 def _window(case: dict, lse=None, a=None) -> Window:
+    # the softmax scale as the library receives it (fp32); `a` as fp32
+    if a is not None:
+        assert a.dtype == np.float32, "the window output a is fp32"
     return Window(case["G"], case["W"], _p(case["q"]), _p(lse), _p(a), _p(case["q_pos"]),
-                  float(case["scale"]))
+                  float(np.float32(case["scale"])))
 
 
 def _mask(case: dict, units) -> Optional[np.ndarray]:
@@ -132,7 +135,7 @@ def lse_a(case: dict, want_a: bool = False, units=None, nthreads: int = 0):
     return lse, a
 
 
-def score(case: dict, lse32: np.ndarray, flags: int, pool_kernel: int = 1, a_enc=None,
+def score(case: dict, lse32: np.ndarray, flags: int, pool_kernel: int = 1, a32=None,
           prev_sum: Optional[np.ndarray] = None, units=None, nthreads: int = 0):
     """Scores in double: dict with 'sum', 'pooled', 'drop' arrays [B,Hkv,max_slots]
     (slots >= seq_len are NaN).  Returns None for the kinds not requested."""
@@ -144,7 +147,7 @@ def score(case: dict, lse32: np.ndarray, flags: int, pool_kernel: int = 1, a_enc
     dr = np.full(shape, np.nan) if flags & DROP else None
     lse32 = np.ascontiguousarray(lse32, dtype=np.float32)
     prev = None if prev_sum is None else np.ascontiguousarray(prev_sum, dtype=np.float32)
-    c, w = _cache(case), _window(case, lse32, a_enc)
+    c, w = _cache(case), _window(case, lse32, a32)
     rc = lib().orc_score(ctypes.byref(c), ctypes.byref(w), flags, pool_kernel, _p(prev), _p(s),
                          _p(pl), _p(dr), _p(_mask(case, units)), nthreads or default_threads())
     if rc != 0:
@@ -235,7 +238,7 @@ def h2o_step(state: dict, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
                             state["G"], _p(np.ascontiguousarray(q, dtype=edt)),
                             _p(np.ascontiguousarray(k_new, dtype=edt)),
                             _p(np.ascontiguousarray(v_new, dtype=edt)),
-                            _p(np.ascontiguousarray(t_pos, dtype=np.int32)), float(state["scale"]),
+                            _p(np.ascontiguousarray(t_pos, dtype=np.int32)), float(np.float32(state["scale"])),
                             budget, recent, _p(free_list), _p(fc), _p(ev), _p(attn), _p(aabs))
     if rc != 0:
         raise ValueError(f"oracle h2o_step refused the arguments (rc={rc})")
@@ -414,7 +417,7 @@ def ring_step(state: dict, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
                              _p(np.ascontiguousarray(v_new)),
                              _p(np.ascontiguousarray(t_pos, dtype=np.int32)),
                              _p(np.ascontiguousarray(observe, dtype=np.int32)),
-                             float(state["scale"]), budget, recent, W, pool_kernel, _p(fl),
+                             float(np.float32(state["scale"])), budget, recent, W, pool_kernel, _p(fl),
                              _p(fc), _p(ev))
     if rc != 0:
         raise ValueError(f"oracle ring_step refused the arguments (rc={rc})")

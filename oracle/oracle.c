@@ -187,7 +187,7 @@ static void score_unit(void *vctx, int64_t u) {
           int64_t prow = phys_row(c, u, j);
           double r2 = 0.0;
           for (int64_t d = 0; d < D; ++d) {
-            double diff = widen(w->a, c->is_bf16, qrow * D + d) -
+            double diff = (double)w->a[qrow * D + d] -
                           widen(c->v_pool, c->is_bf16, prow * D + d);
             r2 += diff * diff;
           }

@@ -44,9 +44,11 @@ typedef struct {
   int32_t group, obs_window;     /* G query heads per KV head, W window queries */
   const void *q;                 /* [batch][kv_heads*group][W][head_dim], cache dtype */
   const float *lse;              /* [batch][kv_heads*group][W] */
-  const void *a;                 /* [batch][kv_heads*group][W][head_dim], cache dtype */
+  const float *a;                /* [batch][kv_heads*group][W][head_dim], fp32 (the
+                                    forward pass's output, whatever the cache dtype) */
   const int32_t *q_pos;          /* [batch][W] */
-  double scale;                  /* multiplies q.k before the LSE is subtracted */
+  double scale;                  /* multiplies q.k before the LSE is subtracted (the
+                                    callers pass the fp32 value the library gets) */
 } orc_window;
 
 /* Input builder (not the method): LSE and attention output of each window

@@ -225,7 +225,7 @@ class Run:
         self.dc = device_cache(case)
         self.q, self.qp = device_window(case)
         B, H, ms = case["B"], case["Hkv"], case["max_blocks"] * 16
-        self.ws = K.new_workspace(self.dc)
+        self.ws = K.new_workspace(self.dc, case["G"], case["W"])
         free0 = np.full(case["num_blocks"] + 8, -1, np.int32)
         free0[:free_prefix] = np.arange(free_prefix) + 10**6
         self.fl = dev(free0)
@@ -235,19 +235,19 @@ class Run:
         self.nv = dev(np.zeros((B, H), np.int32))
         self.stats = None
 
-    def fused(self, kind, lse32, a_enc, pool, budget, recent, accumulate=False):
+    def fused(self, kind, lse32, a32, pool, budget, recent, accumulate=False):
         flags = KIND[kind][0] | (K.ACCUMULATE if accumulate else 0)
         self.stats = K.evict(self.dc, self.q, dev(lse32), self.qp, self.case["scale"],
                              self.case["G"], flags, budget, recent, self.score, self.vic, self.nv,
                              self.fl, self.fc, self.ws, pool_kernel=pool,
-                             a=dev(a_enc) if a_enc is not None else None)
+                             a=dev(a32) if a32 is not None else None)
         torch.cuda.synchronize()
 
-    def three_calls(self, kind, lse32, a_enc, pool, budget, recent, accumulate=False):
+    def three_calls(self, kind, lse32, a32, pool, budget, recent, accumulate=False):
         flags = KIND[kind][0] | (K.ACCUMULATE if accumulate else 0)
         kw = {KIND[kind][2]: self.score}
         K.score(self.dc, self.q, dev(lse32), self.qp, self.case["scale"], self.case["G"], flags,
-                pool, a=dev(a_enc) if a_enc is not None else None, **kw)
+                pool, a=dev(a32) if a32 is not None else None, **kw)
         K.select(self.dc, self.score, budget, recent, self.vic, self.nv, self.ws)
         self.stats = K.compact(self.dc, self.vic, self.nv, self.fl, self.fc, self.ws,
                                score_row=self.score)

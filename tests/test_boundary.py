@@ -32,7 +32,11 @@ def test_exports_every_declared_function():
     assert set(names) == set(K.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvev_abi_version() == K.ABI_VERSION == 14
+    header = open(HEADER).read() if "HEADER" in globals() else open(
+        os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                     "kvev.h")).read()
+    declared = int(re.search(r"#define KVEV_ABI_VERSION (\d+)", header).group(1))
+    assert L.kvev_abi_version() == K.ABI_VERSION == declared
     for code in (0, -1, -2, -3, -4):
         assert K.strerror(code)
 
@@ -105,7 +109,9 @@ def test_bad_cache_refused_everywhere(kw):
     (dict(), K.DROP | K.SUM | K.ACCUMULATE, 1, K.EINVAL),
     (dict(a=None), K.DROP, 1, K.EINVAL),
     (dict(group=64, obs_window=65), K.SUM, 1, K.EUNSUPPORTED),
-    (dict(group=8, obs_window=64), K.DROP, 1, K.EUNSUPPORTED),   # 512 DROP rows exceed LDS
+    # 512 DROP rows exceed one workgroup's LDS: split over workgroups, whose
+    # raw sums need the workspace (none given here)
+    (dict(group=8, obs_window=64), K.DROP, 1, K.ENOSPACE),
 ])
 def test_score_refusals(wkw, flags, pool, expect):
     assert score(cache(), window(**wkw), flags, pool) == expect
@@ -219,7 +225,12 @@ def test_evict_refusals_of_the_parts():
     assert evict(c, window(), cap=31) == K.ENOSPACE          # free list smaller than the pool
     assert evict(c, window(), ws=None, ws_bytes=ws) == K.ENOSPACE
     assert evict(c, window(), ws_bytes=ws - 1) == K.ENOSPACE
-    assert evict(c, window(group=8, obs_window=64), flags=K.DROP, pool=1) == K.EUNSUPPORTED
+    assert evict(c, window(group=64, obs_window=65), flags=K.DROP, pool=1) == K.EUNSUPPORTED
+    # a split window needs room for its raw sums past the main workspace
+    ws_big = L.kvev_workspace_bytes(ctypes.byref(c), 8, 64)
+    assert ws_big > ws
+    assert evict(c, window(group=8, obs_window=64), flags=K.DROP, pool=1,
+                 ws_bytes=ws) == K.ENOSPACE
 
 
 def test_misaligned_score_refused():

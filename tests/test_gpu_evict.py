@@ -83,11 +83,11 @@ def test_evict_equals_three_calls(name, over, kind, pool, budget, recent, ragged
     cfg = synth.CONFIGS[name].scaled(**over)
     seq = _ragged(cfg.B, cfg.Hkv, cfg.L, 5) if ragged else None
     case = synth.make_case(cfg, seq_len=seq, spare_blocks=5)
-    lse32, a_enc = _inputs(case, kind)
+    lse32, a32 = _inputs(case, kind)
     f = Run(case)
-    f.fused(kind, lse32, a_enc, pool, budget, recent)
+    f.fused(kind, lse32, a32, pool, budget, recent)
     t = Run(case)
-    t.three_calls(kind, lse32, a_enc, pool, budget, recent)
+    t.three_calls(kind, lse32, a32, pool, budget, recent)
     _assert_same(f.state(), t.state(), case["seq_len"])
 
 
@@ -147,13 +147,13 @@ ORACLE_CASES = [
 def test_evict_matches_oracle(name, over, kind, pool, budget, recent):
     cfg = synth.CONFIGS[name].scaled(**over)
     case = synth.make_case(cfg)
-    lse32, a_enc = _inputs(case, kind)
+    lse32, a32 = _inputs(case, kind)
     kg, ko, key = KIND[kind]
-    orc = oracle.score(case, lse32, ko, pool, a_enc=a_enc)[key]
+    orc = oracle.score(case, lse32, ko, pool, a32=a32)[key]
     o32 = orc.astype(np.float32)
     ov, on = oracle.select(np.nan_to_num(o32, nan=0.0), case["seq_len"], budget, recent)
     f = Run(case, free_prefix=0)
-    f.fused(kind, lse32, a_enc, pool, budget, recent)
+    f.fused(kind, lse32, a32, pool, budget, recent)
     st = f.state()
     # the oracle's own chain: its victims, then its compaction of them carrying its scores
     new, ofl, ofc, ostats = oracle.compact(case, ov, on, score_row=np.nan_to_num(o32, nan=0.0),

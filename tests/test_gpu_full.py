@@ -50,12 +50,12 @@ def _evict_full(name):
     case = synth.make_case(cfg)
     _say(f"{name}: oracle window inputs")
     lse64, a64 = oracle.lse_a(case, want_a=(kind == "drop"))
-    lse32, a_enc = rounded_window_inputs(case, lse64, a64)
+    lse32, a32 = rounded_window_inputs(case, lse64, a64)
     _say(f"{name}: oracle scores")
-    o32 = oracle.score(case, lse32, ko, cfg.pool_kernel, a_enc=a_enc)[key].astype(np.float32)
+    o32 = oracle.score(case, lse32, ko, cfg.pool_kernel, a32=a32)[key].astype(np.float32)
     _say(f"{name}: kvev_score on the full cache")
     r = Run(case, free_prefix=0)
-    a_dev = dev(a_enc) if a_enc is not None else None
+    a_dev = dev(a32) if a32 is not None else None
     out = K.score(r.dc, r.q, dev(lse32), r.qp, case["scale"], case["G"], kg, cfg.pool_kernel,
                   **{key: r.dc.score_buffer()}, a=a_dev)
     torch.cuda.synchronize()
@@ -64,7 +64,7 @@ def _evict_full(name):
     _say(f"{name}: scores within tolerance, worst relative error {worst:.2e}")
     del out
     _say(f"{name}: kvev_evict")
-    r.fused(kind, lse32, a_enc, cfg.pool_kernel, cfg.budget, cfg.recent)
+    r.fused(kind, lse32, a32, cfg.pool_kernel, cfg.budget, cfg.recent)
     st = r.state()
     ov, on = oracle.select(np.nan_to_num(o32, nan=0.0), case["seq_len"], cfg.budget, cfg.recent)
     new, ofl, ofc, ostats = oracle.compact(case, ov, on, score_row=np.nan_to_num(o32, nan=0.0),

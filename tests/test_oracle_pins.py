@@ -121,7 +121,8 @@ def test_equal_keys_uniform_closed_form():
     q_pos = np.array([[30, 31, 35, 38, 39], [20, 25, 26, 33, 39]], np.int32)
     case = manual_case(k, k, q, q_pos, dtype="f32", scale=0.3)
     lse64, _ = oracle.lse_a(case)
-    np.testing.assert_allclose(lse64 - 0.3 * np.einsum("bhwd,d->bhw", q.astype(np.float32).astype(np.float64), krow.astype(np.float32).astype(np.float64)),
+    sc32 = float(np.float32(0.3))  # the scale as both sides receive it
+    np.testing.assert_allclose(lse64 - sc32 * np.einsum("bhwd,d->bhw", q.astype(np.float32).astype(np.float64), krow.astype(np.float32).astype(np.float64)),
                                np.log(q_pos + 1.0)[:, None, :].repeat(Hkv * G, 1), rtol=0, atol=1e-12)
     lse32, _ = rounded_window_inputs(case, lse64)
     s = oracle.score(case, lse32, oracle.SUM)["sum"]
@@ -222,8 +223,8 @@ def test_dropkv_lemma1_brute_force(seed):
     q = np.zeros((1, 1, 1, D)); q[..., :4] = r.normal(0, 1, 4)
     case = manual_case(k, v, q, np.array([[n - 1]]), dtype="f32", scale=1.0)
     lse64, a64 = oracle.lse_a(case, want_a=True)
-    lse32, a_enc = rounded_window_inputs(case, lse64, a64)
-    drop = oracle.score(case, lse32, oracle.DROP, a_enc=a_enc)["drop"][0, 0, :n]
+    lse32, a32 = rounded_window_inputs(case, lse64, a64)
+    drop = oracle.score(case, lse32, oracle.DROP, a32=a32)["drop"][0, 0, :n]
     kk = k[0, 0].astype(np.float32).astype(np.float64)
     vv = v[0, 0].astype(np.float32).astype(np.float64)
     qq = q[0, 0, 0].astype(np.float32).astype(np.float64)
@@ -251,7 +252,7 @@ def test_dropkv_worked_example():
     a_page = np.zeros((1, 1, 1, D)); a_page[..., 0] = g["a"]
     assert abs((p * vals).sum() - g["a"]) < 1e-12
     lse32 = np.zeros((1, 1, 1), np.float32)
-    out = oracle.score(case, lse32, oracle.DROP | oracle.SUM, a_enc=a_page.astype(np.float32))
+    out = oracle.score(case, lse32, oracle.DROP | oracle.SUM, a32=a_page.astype(np.float32))
     drop, attn = out["drop"][0, 0, :n], out["sum"][0, 0, :n]
     # printed to two decimals
     np.testing.assert_allclose(np.round(drop, g["printed_decimals"]), g["scores_printed"], atol=1e-12)
@@ -283,9 +284,9 @@ def test_dropkv_zero_when_values_equal_output():
     q = r.normal(0, 1, (1, 4, 3, D))
     case = manual_case(k, v, q, np.array([[n - 3, n - 2, n - 1]]), dtype="f32", scale=0.125)
     lse64, a64 = oracle.lse_a(case, want_a=True)
-    lse32, a_enc = rounded_window_inputs(case, lse64, a64)
-    assert np.array_equal(a_enc[0, 0, 0], c.astype(np.float32))
-    d = oracle.score(case, lse32, oracle.DROP, a_enc=a_enc)["drop"][0, :, :n]
+    lse32, a32 = rounded_window_inputs(case, lse64, a64)
+    assert np.array_equal(a32[0, 0, 0], c.astype(np.float32))
+    d = oracle.score(case, lse32, oracle.DROP, a32=a32)["drop"][0, :, :n]
     assert np.all(d == 0.0)
 
 
@@ -296,8 +297,8 @@ def test_dropkv_lone_key_is_never_evicted_first():
     q = np.zeros((1, 1, 1, D))
     case = manual_case(k, v, q, np.array([[0]]), dtype="f32")
     lse64, a64 = oracle.lse_a(case, want_a=True)
-    lse32, a_enc = rounded_window_inputs(case, lse64, a64)
-    d = oracle.score(case, lse32, oracle.DROP, a_enc=a_enc)["drop"][0, 0, :n]
+    lse32, a32 = rounded_window_inputs(case, lse64, a64)
+    d = oracle.score(case, lse32, oracle.DROP, a32=a32)["drop"][0, 0, :n]
     assert d[0] == np.inf and np.all(d[1:] == 0.0)
 
 

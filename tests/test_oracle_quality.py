@@ -27,8 +27,8 @@ def _scored(name, flag, key, **kw):
     cfg = synth.CONFIGS[name].scaled(**kw)
     case = synth.make_case(cfg)
     lse, a = oracle.lse_a(case, want_a=bool(flag & oracle.DROP))
-    lse32, a_enc = rounded_window_inputs(case, lse, a if flag & oracle.DROP else None)
-    sc = oracle.score(case, lse32, flag, cfg.pool_kernel, a_enc=a_enc)[key]
+    lse32, a32 = rounded_window_inputs(case, lse, a if flag & oracle.DROP else None)
+    sc = oracle.score(case, lse32, flag, cfg.pool_kernel, a32=a32)[key]
     # the generator lays tokens out in slot order: slot s holds position s
     U = cfg.B * cfg.Hkv
     assert np.array_equal(case["pos"].reshape(U, -1)[:, :cfg.L], np.tile(np.arange(cfg.L), (U, 1)))
