@@ -13,7 +13,9 @@
  * - Every data pointer is a DEVICE pointer owned by the caller (for example a
  *   torch tensor's data_ptr()).  The library allocates nothing, frees nothing
  *   and keeps no state of its own (what persists between calls lives in the
- *   caller's workspace); calls on different workspaces are independent.
+ *   caller's workspace); calls on different workspaces are independent.  The
+ *   one exception is kvev_evict_noalloc, whose workspace is a static device
+ *   array per GPU (its address is looked up once per device and kept).
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Each
  *   call only enqueues work on that stream and never synchronises.  Calls that
  *   share a workspace or touch the same cache must be ordered on one stream.
@@ -55,7 +57,9 @@ extern "C" {
 #endif
 
 #define KVEV_BLOCK_SIZE 16
-#define KVEV_ABI_VERSION 15
+#define KVEV_ABI_VERSION 16
+/* bytes of the static device array kvev_evict_noalloc works in, per GPU */
+#define KVEV_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 
 typedef enum {
   KVEV_OK = 0,
@@ -266,6 +270,35 @@ int kvev_evict(const kvev_cache *cache, const kvev_window *win, int32_t flags,
                int32_t *victims, int32_t *n_victims, int32_t *free_list, int32_t *free_count,
                int32_t free_capacity, int64_t *stats, void *workspace, size_t ws_bytes,
                void *stream);
+
+/*
+ * kvev_evict_noalloc -- kvev_evict for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments (minus the workspace), results and errors
+ * as kvev_evict; the same two kernels run, plus one fill kernel first.
+ * It allocates nothing: its workspace is a static device array of
+ * KVEV_NOALLOC_SCRATCH_BYTES (128 MiB) that every GPU the library runs on
+ * holds until the process ends.  The array keeps the last call's contents;
+ * each call zeroes the part that must start at zero (the selection state and
+ * the pass's counters) with the fill kernel, so no earlier call, failed or
+ * not, leaves anything behind.
+ * Limit: the pass needs its state plus 12 bytes per slot of every head
+ * (batch * kv_heads * max_blocks * 16 slots), plus 4 * P more per slot when
+ * the window's rows are too many for one workgroup's LDS and are split over
+ * P workgroups per tile (large DropKV windows, as kvev_score describes); a
+ * shape that needs more than the array returns KVEV_ENOSPACE before any work
+ * is enqueued.  Example: 32 heads of 32768 slots need 12.6 MB.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (two streams, two host threads) race and corrupt each other's results,
+ * so order them.  The device current at the call must be the stream's; the
+ * first call on a device looks the array's address up (hipGetSymbolAddress)
+ * and keeps it: make that first call outside graph capture.
+ */
+int kvev_evict_noalloc(const kvev_cache *cache, const kvev_window *win, int32_t flags,
+                       int32_t pool_kernel, int32_t budget, int32_t recent_window, float *score,
+                       int32_t *victims, int32_t *n_victims, int32_t *free_list,
+                       int32_t *free_count, int32_t free_capacity, int64_t *stats,
+                       void *stream);
 
 /*
  * kvev_measure -- block-level waste of an eviction ([VTOK] section 2, Eq. 1

@@ -29,7 +29,8 @@ SUM, POOL, DROP, ACCUMULATE = 1, 2, 4, 8
 BLOCK_SIZE = 16
 
 # the functions include/kvev.h declares
-EXPORTS = ("kvev_score", "kvev_select", "kvev_compact", "kvev_evict", "kvev_measure",
+EXPORTS = ("kvev_score", "kvev_select", "kvev_compact", "kvev_evict", "kvev_evict_noalloc",
+           "kvev_measure",
            "kvev_h2o_step", "kvev_h2o_workspace_bytes", "kvev_vtok_evict",
            "kvev_vtok_evict_workspace_bytes", "kvev_vtok_reclaim", "kvev_vtok_workspace_bytes",
            "kvev_vtok_digest", "kvev_vtok_check", "kvev_vtok_check_workspace_bytes",
@@ -38,7 +39,7 @@ EXPORTS = ("kvev_score", "kvev_select", "kvev_compact", "kvev_evict", "kvev_meas
            "kvev_vtok_map_workspace_bytes",
            "kvev_window_attn",
            "kvev_workspace_bytes", "kvev_strerror", "kvev_abi_version")
-ABI_VERSION = 15
+ABI_VERSION = 16
 
 
 class KvevError(RuntimeError):
@@ -82,6 +83,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kvev_select.argtypes = [P, P, i32, i32, P, P, P, sz, P]
     L.kvev_compact.argtypes = [P, P, P, P, P, P, i32, P, P, sz, P]
     L.kvev_evict.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P, P, i32, P, P, sz, P]
+    L.kvev_evict_noalloc.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P, P, i32, P, P]
     L.kvev_window_attn.argtypes = [P, P, P, P, P, sz, P]
     L.kvev_measure.argtypes = [P, P, P, i32, i32, P, P]
     L.kvev_h2o_step.argtypes = [P, P, P, P, P, i32, ctypes.c_float, P, i32, i32, P, P, P, P, P,
@@ -114,7 +116,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kvev_strerror.argtypes = [ctypes.c_int]
     L.kvev_strerror.restype = ctypes.c_char_p
     L.kvev_abi_version.argtypes = []
-    for f in (L.kvev_score, L.kvev_select, L.kvev_compact, L.kvev_evict, L.kvev_window_attn,
+    for f in (L.kvev_score, L.kvev_select, L.kvev_compact, L.kvev_evict, L.kvev_evict_noalloc,
+              L.kvev_window_attn,
               L.kvev_measure, L.kvev_h2o_step, L.kvev_vtok_evict, L.kvev_vtok_reclaim,
               L.kvev_vtok_digest, L.kvev_vtok_check, L.kvev_select_shared,
               L.kvev_select_budgets, L.kvev_ring_step, L.kvev_ring_init, L.kvev_vtok_sync,
@@ -407,6 +410,33 @@ def evict(cache: Cache, q: torch.Tensor, lse: torch.Tensor, q_pos: torch.Tensor,
                       _ptr(free_list), _ptr(free_count), free_list.numel(), _ptr(stats),
                       _ptr(workspace), workspace.numel(), _stream(stream))
     _check(rc, "kvev_evict")
+    return stats
+
+
+def evict_noalloc(cache: Cache, q: torch.Tensor, lse: torch.Tensor, q_pos: torch.Tensor,
+                  scale: float, group: int, flags: int, budget: int, recent_window: int,
+                  score_row: torch.Tensor, victims: torch.Tensor, n_victims: torch.Tensor,
+                  free_list: torch.Tensor, free_count: torch.Tensor, stats: torch.Tensor,
+                  pool_kernel: int = 1, a: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """kvev_evict_noalloc: kvev_evict in the library's static per-GPU scratch
+    array (no workspace; the C call allocates nothing).  Every argument,
+    stats included, is the caller's."""
+    L = load_library()
+    c = cache.struct()
+    w = _window(cache, q, lse, q_pos, scale, group, a)
+    n = cache.units * cache.max_slots
+    _need(score_row, "score_row", torch.float32, n)
+    _need(victims, "victims", torch.int32, n)
+    _need(n_victims, "n_victims", torch.int32, cache.units)
+    _need(free_list, "free_list", torch.int32)
+    _need(free_count, "free_count", torch.int32, 1)
+    _need(stats, "stats", torch.int64, 5)
+    rc = L.kvev_evict_noalloc(ctypes.byref(c), ctypes.byref(w), flags, pool_kernel, budget,
+                              recent_window, _ptr(score_row), _ptr(victims), _ptr(n_victims),
+                              _ptr(free_list), _ptr(free_count), free_list.numel(), _ptr(stats),
+                              _stream(stream))
+    _check(rc, "kvev_evict_noalloc")
     return stats
 
 

@@ -7,9 +7,11 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
 #include "kvev.h"
 #include "kvev_kernels.h"
@@ -43,6 +45,13 @@ bool valid_cache(const kvev_cache *c) {
 int elem_bytes(const kvev_cache *c) { return c->dtype == KVEV_BF16 ? 2 : 4; }
 
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Zeroes n16 16-byte words (a fill kernel, not a memset, so that callers
+// may capture it in a graph).
+__global__ __launch_bounds__(256) void clear16_kernel(uint4 *p, size_t n16) {
+  for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
 
 // Workspace = [persistent state | scratch].  The state (selection
 // histograms, per-head compaction accumulators) must be zero before
@@ -744,11 +753,19 @@ int kvev_compact(const kvev_cache *cache, const int32_t *victims, const int32_t 
   return map_err(kvev::launch_compact(a, static_cast<hipStream_t>(stream)));
 }
 
-int kvev_evict(const kvev_cache *cache, const kvev_window *win, int32_t flags,
+}  // extern "C"
+
+namespace {
+
+// kvev_evict on the workspace `workspace` (ws_bytes long), a split window's
+// raw sums at parts_off (past the pass's own layout); clear_state first
+// zeroes the state part with a fill kernel (the no-allocation entry point,
+// whose static array keeps the last call's contents).
+int evict_impl(const kvev_cache *cache, const kvev_window *win, int32_t flags,
                int32_t pool_kernel, int32_t budget, int32_t recent_window, float *score,
                int32_t *victims, int32_t *n_victims, int32_t *free_list, int32_t *free_count,
                int32_t free_capacity, int64_t *stats, void *workspace, size_t ws_bytes,
-               void *stream) {
+               size_t parts_off, bool clear_state, void *stream) {
   if (!valid_cache(cache) || !score || !victims || !n_victims || !free_list || !free_count ||
       !stats)
     return KVEV_EINVAL;
@@ -774,9 +791,11 @@ int kvev_evict(const kvev_cache *cache, const kvev_window *win, int32_t flags,
     return KVEV_EUNSUPPORTED;  // 1M slots per head
   const size_t parts_bytes = score_parts_bytes(cache, win->group, win->obs_window,
                                                kind == KVEV_DROP, kind != KVEV_DROP);
-  if (!workspace || ws_bytes < main_layout_total(cache) + parts_bytes) return KVEV_ENOSPACE;
+  // the pass uses the state, its own scratch (E) and the split rows' sums
+  if (parts_off < E.total) return KVEV_EINVAL;
+  if (!workspace || ws_bytes < parts_off + parts_bytes) return KVEV_ENOSPACE;
   uint8_t *ws = static_cast<uint8_t *>(workspace);
-  set_score_parts(a, cache, ws + main_layout_total(cache));
+  set_score_parts(a, cache, ws + parts_off);
   a.prev = score;  // ACCUMULATE: the running sums are in the output row
   a.head_err = reinterpret_cast<uint32_t *>(ws + S.fin_err);
   a.hist = reinterpret_cast<uint32_t *>(ws + S.hist);
@@ -819,11 +838,77 @@ int kvev_evict(const kvev_cache *cache, const kvev_window *win, int32_t flags,
   f.free_capacity = free_capacity;
   if ((int64_t)f.units * f.kh > INT32_MAX) return KVEV_EUNSUPPORTED;
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (clear_state) {
+    const size_t n16 = S.total / 16;  // S.total is a multiple of 256
+    hipLaunchKernelGGL(clear16_kernel, dim3((unsigned)std::min<size_t>((n16 + 255) / 256, 1024)),
+                       dim3(256), 0, st, reinterpret_cast<uint4 *>(ws), n16);
+    rc = map_err(hipGetLastError());
+    if (rc) return rc;
+  }
   rc = map_err(kvev::launch_score(a, cache->dtype == KVEV_BF16, cache->head_dim,
                                   kind == KVEV_DROP, st));
   if (rc) return rc;
   return map_err(kvev::launch_finish(f, st));
 }
+
+// The no-allocation entry point's scratch: one static array per GPU.  Host
+// code never passes the array's name to a kernel (on the host it is only a
+// stand-in): each device's address is looked up once, with that device
+// current, and kept.
+constexpr size_t kNoAllocBytes = KVEV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<uint8_t *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_of_current_device(uint8_t **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KVEV_EDEVICE;
+  if (dev < 0 || dev >= kMaxDevices) return KVEV_EUNSUPPORTED;
+  uint8_t *p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void *addr = nullptr;
+      if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr)
+        return KVEV_EDEVICE;
+      p = static_cast<uint8_t *>(addr);
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return KVEV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvev_evict(const kvev_cache *cache, const kvev_window *win, int32_t flags,
+               int32_t pool_kernel, int32_t budget, int32_t recent_window, float *score,
+               int32_t *victims, int32_t *n_victims, int32_t *free_list, int32_t *free_count,
+               int32_t free_capacity, int64_t *stats, void *workspace, size_t ws_bytes,
+               void *stream) {
+  return evict_impl(cache, win, flags, pool_kernel, budget, recent_window, score, victims,
+                    n_victims, free_list, free_count, free_capacity, stats, workspace, ws_bytes,
+                    valid_cache(cache) ? main_layout_total(cache) : 0, false, stream);
+}
+
+int kvev_evict_noalloc(const kvev_cache *cache, const kvev_window *win, int32_t flags,
+                       int32_t pool_kernel, int32_t budget, int32_t recent_window, float *score,
+                       int32_t *victims, int32_t *n_victims, int32_t *free_list,
+                       int32_t *free_count, int32_t free_capacity, int64_t *stats,
+                       void *stream) {
+  if (!valid_cache(cache)) return KVEV_EINVAL;
+  uint8_t *ws = nullptr;
+  const int rc = scratch_of_current_device(&ws);
+  if (rc) return rc;
+  return evict_impl(cache, win, flags, pool_kernel, budget, recent_window, score, victims,
+                    n_victims, free_list, free_count, free_capacity, stats, ws, kNoAllocBytes,
+                    evict_layout(cache).total, true, stream);
+}
+
 
 int kvev_window_attn(const kvev_cache *cache, const kvev_window *win, float *lse_out,
                      float *a_out, void *workspace, size_t ws_bytes, void *stream) {
