@@ -9,12 +9,10 @@ workloads run at their real shapes:
   kvev_score.
 * DropKV residual scoring, 128K context (B1, 8 KV heads x 8): kvev_evict with
   the residual score, every head against the oracle's chain.
-* Block-aware eviction, one 64000-token layer of the 70B GQA shape (B16,
-  8 KV heads x 8, about 4.2 GB of K+V), for two of the eight layers: the
-  three calls, sampled heads against the oracle's chain, every head against
-  the definitions (victims = the m smallest (score, slot) pairs of the
-  head's own scores by a full sort; kept rows in order; the closed-form
-  block count).
+* Block-aware eviction of the 70B GQA shape: each of its eight 64000-token
+  layers (B16, 8 KV heads x 8, about 4.2 GB of K+V each, its own seeded
+  data) through kvev_evict, every head of every layer against the oracle's
+  chain (scores, victims, compaction) and the closed-form block count.
 * H2O decode accumulation (B8, 8 KV heads x 4, 4096 -> 4352 tokens): the 256
   decode steps of ACCUMULATE scoring, then select and compact, every head
   against the oracle run through the same schedule.
@@ -31,9 +29,8 @@ import torch
 import kv_cache_eviction_qk_amd as K
 import oracle
 import synth
-from tests.gpu_helpers import (KIND, TOL, Run, assert_scores_close, brute_force_victims,
-                               check_compaction_by_definition, check_eviction_vs_oracle_chain,
-                               dev, device_cache, host)
+from tests.gpu_helpers import (KIND, TOL, Run, assert_scores_close,
+                               check_eviction_vs_oracle_chain, dev, device_cache, host)
 from tests.helpers import rounded_window_inputs
 
 pytestmark = pytest.mark.gpu
@@ -43,11 +40,13 @@ def _say(msg):
     print(f"[full] {msg}", flush=True)
 
 
-def _evict_full(name):
+def _evict_full(name, layer=0):
     cfg = synth.CONFIGS[name]
     kind = cfg.flags[0]
     kg, ko, key = KIND[kind]
-    case = synth.make_case(cfg)
+    case = synth.make_case(cfg, layer=layer)
+    if layer:
+        name = f"{name} layer {layer}"
     _say(f"{name}: oracle window inputs")
     lse64, a64 = oracle.lse_a(case, want_a=(kind == "drop"))
     lse32, a32 = rounded_window_inputs(case, lse64, a64)
@@ -87,64 +86,12 @@ def test_dropkv_128k_full_size():
     assert st["stats"][0] == 8 * (8192 - (6553 + 15) // 16)
 
 
-@pytest.mark.parametrize("layer", [0, 7])
+@pytest.mark.parametrize("layer", range(8))
 def test_block_evict_64k_layer_full_size(layer):
-    cfg = synth.CONFIGS["block_evict_64k"]
-    case = synth.make_case(cfg, layer=layer)
-    U = case["B"] * case["Hkv"]
-    ms = case["max_blocks"] * 16
-    sample = list(range(0, U, 9))  # 15 heads across the batch and the heads
-    _say(f"layer {layer}: window LSE (oracle on {len(sample)} sampled heads)")
-    r = Run(case, free_prefix=0)
-    ws_wa = K.new_workspace(r.dc, case["G"], case["W"])
-    lse_dev, _ = K.window_attn(r.dc, r.q, r.qp, case["scale"], case["G"], ws_wa)
-    torch.cuda.synchronize()
-    del ws_wa
-    lse64, _ = oracle.lse_a(case, units=sample)
-    lse32 = host(lse_dev).copy()
-    Hq = case["Hkv"] * case["G"]
-    for u in sample:
-        b, h = divmod(u, case["Hkv"])
-        rows = slice(h * case["G"], (h + 1) * case["G"])
-        lse32[b, rows] = lse64[b, rows].astype(np.float32)
-    assert lse32.shape == (case["B"], Hq, case["W"])
-    _say(f"layer {layer}: oracle scores on the sampled heads")
-    o = oracle.score(case, lse32, oracle.SUM, 1, units=sample)["sum"]
-    _say(f"layer {layer}: kvev_score, kvev_select, kvev_compact")
-    K.score(r.dc, r.q, dev(lse32), r.qp, case["scale"], case["G"], K.SUM, 1, sum=r.score)
-    gscore = host(r.score)
-    K.select(r.dc, r.score, cfg.budget, cfg.recent, r.vic, r.nv, r.ws)
-    r.stats = K.compact(r.dc, r.vic, r.nv, r.fl, r.fc, r.ws)
-    torch.cuda.synchronize()
-    st = r.state()
-    seq = case["seq_len"].reshape(-1)
-    so = o.reshape(U, ms)[sample]
-    sg = gscore.reshape(U, ms)[sample]
-    assert_scores_close(sg[None], so[None], seq[sample][None], TOL[cfg.dtype], "sum")
-    # every head: the victims are the m smallest (score, slot) pairs of the
-    # head's own scores, and the compaction follows them
-    gv = st["vic"].reshape(U, ms)
-    moved = at_risk = 0
-    for u in range(U):
-        n = int(seq[u])
-        m = int(st["nv"].reshape(-1)[u])
-        want = brute_force_victims(gscore.reshape(U, ms)[u, :n], n, cfg.budget, cfg.recent)
-        assert m == want.size and np.array_equal(gv[u, :m], want), u
-        mv, ar = check_compaction_by_definition(case, st, u, gv[u, :m])
-        moved += mv
-        at_risk += ar
-    assert st["stats"][0] == U * (4000 - 2000)  # 64000 -> 32000 tokens per head
-    assert st["stats"][1] == moved and st["stats"][3] == at_risk
-    assert st["stats"][2] == moved * 4 * case["D"] * 2
-    # sampled heads: the oracle's own chain
-    o32 = np.nan_to_num(o.astype(np.float32), nan=0.0)
-    ov, on = oracle.select(o32, case["seq_len"], cfg.budget, cfg.recent)
-    new, ofl, ofc, ostats = oracle.compact(case, ov, on,
-                                           free_list=np.full(case["num_blocks"] + 8, -1, np.int32))
-    nd = check_eviction_vs_oracle_chain(case, st, ov, on, new, ofl, ofc, ostats, o32,
-                                        TOL[cfg.dtype], units=sample)
-    _say(f"layer {layer}: stats {st['stats'].tolist()}, {nd} sampled heads with victims "
-         f"differing inside the tolerance band")
+    """Each of the eight layers (its own seeded keys, values, queries and
+    planted heavy hitters), every one of its 128 heads against the oracle."""
+    st = _evict_full("block_evict_64k", layer)
+    assert st["stats"][0] == 16 * 8 * (4000 - 2000)  # 64000 -> 32000 tokens per head
 
 
 def test_h2o_decode_4k_full_schedule():
