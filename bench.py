@@ -56,6 +56,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", action="store_true",
                     help="only run the timed steps (for rocprofv3 runs)")
+    ap.add_argument("--window-attn", action="store_true",
+                    help="time the window forward helper (kvev_window_attn: LSE, and the "
+                         "output for DropKV) on the workload's cache and window instead, one "
+                         "JSON line (not the benchmark's metric)")
     return ap.parse_args()
 
 
@@ -99,6 +103,8 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     cfg = synth.CONFIGS[args.workload]
+    if args.window_attn:
+        return bench_window_attn(args, cfg)
     if args.workload == "h2o_stream_870":
         return bench_h2o_stream(args, cfg)
     if args.workload == "vtok_reclaim_64k":
@@ -850,6 +856,55 @@ def _vtok_bytes(U, rows, nsrc, alloc_blocks, row_bytes):
     and pushed (12), live count written (4).  Per allocated block of a head:
     block id and live count read by the plan (8)."""
     return rows * (4 * row_bytes + 16) + nsrc * (32 + 16 + 12 + 4) + alloc_blocks * 8
+
+
+def bench_window_attn(args, cfg):
+    """kvev_window_attn on the workload's prompt cache (every head at length L)
+    and window (G x W rows per KV head; W = 1 for the decode workloads, one
+    decode step's query): the LSE, plus the output for DropKV.  Algorithmic
+    bytes: the keys (and values when the output is wanted) read once, the
+    queries read, the LSE and output written; partials excluded."""
+    import numpy as np
+    import torch
+
+    import kv_cache_eviction_qk_amd as K
+    import synth
+    case = synth.make_case(cfg)
+    want_a = cfg.flags[0] == "drop"
+
+    def dev(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+
+    dc = K.Cache(dev(case["k_pool"]), dev(case["v_pool"]), dev(case["block_table"]),
+                 dev(case["seq_len"]), dev(case["pos"]))
+    q, qp = dev(case["q"]), dev(case["q_pos"])
+    G, W, D = cfg.G, cfg.W, cfg.D
+    ws = K.new_workspace(dc, G, W)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    a = torch.empty(q.shape, dtype=torch.float32, device="cuda") if want_a else None
+    for _ in range(args.warmup):
+        K.window_attn(dc, q, qp, cfg.softmax_scale, G, ws, want_a=want_a, lse_out=lse, a_out=a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        K.window_attn(dc, q, qp, cfg.softmax_scale, G, ws, want_a=want_a, lse_out=lse, a_out=a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    units = cfg.B * cfg.Hkv
+    eb = 2 if cfg.dtype == "bf16" else 4
+    tokens = int(case["seq_len"].sum())
+    rows = units * G * W
+    nbytes = tokens * D * eb * (2 if want_a else 1) + rows * D * eb + rows * 4 * (1 + (D if want_a else 0))
+    print(json.dumps({"kernel": "window_attn", "workload": cfg.name, "rows_per_kv_head": G * W,
+                      "tokens": tokens, "want_a": want_a, "ms_per_call": ms,
+                      "algorithmic_bytes": nbytes, "hbm_gbs": nbytes / ms / 1e6,
+                      "hbm_frac": nbytes / ms / 1e6 / HBM_PEAK_GBS, "steps": args.steps}),
+          flush=True)
 
 
 def bench_vtok(args, cfg):

@@ -602,9 +602,14 @@ size_t kvev_vtok_check_workspace_bytes(const kvev_cache *cache);
  * "Log-sum-exp"; "Why does the Triton kernel matter").
  *     lse_out[b][hq][w] = log sum_{pos_j <= q_pos[w]} exp(scale * q.k_j)   (fp32)
  *     a_out[b][hq][w][:] = sum_j exp(scale * q.k_j - lse) v_j           (fp32, may be NULL)
- * fp32 arithmetic throughout.  A query that attends no key gets lse = -inf
- * and a = 0.  Workspace: at least kvev_workspace_bytes(cache, group, W).
- * Errors as for kvev_score; KVEV_ENOSPACE for a short workspace.
+ * q.k on the MFMA (cache-dtype inputs, fp32 sums); for the output the
+ * weights enter the MFMA as a bf16 high part plus a bf16 low part (bf16
+ * caches: each weight to a relative 2^-16) or in fp32 (fp32 caches), with
+ * fp32 sums; the chunks of keys are merged in fp32.  A query that attends no
+ * key gets lse = -inf and a = 0; the slots of a block id outside the pool
+ * are skipped (attended by no query).  Bitwise reproducible.  Workspace: at
+ * least kvev_workspace_bytes(cache, group, W).  Errors as for kvev_score;
+ * KVEV_ENOSPACE for a short workspace.
  */
 int kvev_window_attn(const kvev_cache *cache, const kvev_window *win, float *lse_out,
                      float *a_out, void *workspace, size_t ws_bytes, void *stream);

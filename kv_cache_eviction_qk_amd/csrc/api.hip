@@ -18,8 +18,7 @@
 
 namespace {
 
-constexpr int kWaChunk = 2048;        // keys per window-attention workgroup
-constexpr int kWaRowsPerWg = 128;     // window rows per window-attention workgroup
+constexpr int kWaMaxChunk = 8192;     // keys per window-attention chunk, at most
 constexpr size_t kMaxLds = 160 * 1024;
 #ifndef KV_TILE_MAX
 #define KV_TILE_MAX 256
@@ -165,19 +164,45 @@ CompactLayout compact_layout(const kvev_cache *c) {
 
 size_t compact_layout_total(const kvev_cache *c) { return compact_layout(c).total; }
 
+// Window attention's launch shape: 256 threads with one row tile per wave up
+// to 4 tiles, two per wave up to 8, then 512 threads with two per wave and
+// as many workgroups per chunk as 16 tiles need; chunks of a multiple of 32
+// keys, for about 512 workgroups, of at least 256 keys and 8 per window row
+// (so that the partials stay small beside the keys), at most kWaMaxChunk.
+struct WaShape {
+  int threads, rt_wave, row_parts, chunk_slots, chunks;
+};
+
+WaShape wa_shape(const kvev_cache *c, int rows) {
+  WaShape s{};
+  const int T = (rows + 15) / 16;
+  s.threads = T <= 8 ? 256 : 512;
+  s.rt_wave = T <= 4 ? 1 : 2;
+  const int tiles_per_wg = (s.threads / 64) * s.rt_wave;
+  s.row_parts = (T + tiles_per_wg - 1) / tiles_per_wg;
+  const int64_t units = (int64_t)c->batch * c->kv_heads;
+  const int64_t max_slots = (int64_t)c->max_blocks * KVEV_BLOCK_SIZE;
+  const int64_t want = (512 + units * s.row_parts - 1) / (units * s.row_parts);
+  int64_t cs = (max_slots + want - 1) / want;
+  cs = std::max<int64_t>(cs, std::max<int64_t>(256, (int64_t)rows * 8));
+  cs = std::min<int64_t>(cs, kWaMaxChunk);
+  cs = (cs + 31) / 32 * 32;
+  s.chunk_slots = (int)cs;
+  s.chunks = (int)((max_slots + cs - 1) / cs);
+  return s;
+}
+
 struct WaLayout {
   size_t part_m, part_l, part_acc, total;
-  int chunks, rows_pad;
+  int chunks;
 };
 
 WaLayout wa_layout(const kvev_cache *c, int group, int obs_window) {
   WaLayout L{};
   const size_t units = (size_t)c->batch * c->kv_heads;
-  const size_t max_slots = (size_t)c->max_blocks * KVEV_BLOCK_SIZE;
   const int rows = group * obs_window;
-  L.chunks = (int)((max_slots + kWaChunk - 1) / kWaChunk);
-  L.rows_pad = ((rows + kWaRowsPerWg - 1) / kWaRowsPerWg) * kWaRowsPerWg;
-  const size_t parts = units * (size_t)L.rows_pad * L.chunks;
+  L.chunks = wa_shape(c, rows).chunks;
+  const size_t parts = units * (size_t)rows * L.chunks;
   size_t off = state_layout(c).total;
   L.part_m = off; off = a256(off + parts * 4);
   L.part_l = off; off = a256(off + parts * 4);
@@ -939,9 +964,17 @@ int kvev_window_attn(const kvev_cache *cache, const kvev_window *win, float *lse
   a.max_blocks = cache->max_blocks;
   a.num_blocks = cache->num_blocks;
   a.rows = win->group * win->obs_window;
-  a.chunk_slots = kWaChunk;
-  a.chunks = L.chunks;
+  const WaShape sh = wa_shape(cache, a.rows);
+  a.chunk_slots = sh.chunk_slots;
+  a.chunks = sh.chunks;
+  a.threads = sh.threads;
+  a.rt_wave = sh.rt_wave;
+  a.row_parts = sh.row_parts;
+  if ((int64_t)a.units * a.row_parts > 65535) return KVEV_EUNSUPPORTED;  // grid rows
   a.want_a = a_out ? 1 : 0;
+  if (kvev::window_attn_lds_bytes(cache->dtype == KVEV_BF16, cache->head_dim, a.want_a,
+                                  a.chunk_slots) > kMaxLds - 1024)
+    return KVEV_EUNSUPPORTED;
   a.scale = win->scale;
   return map_err(kvev::launch_window_attn(a, cache->dtype == KVEV_BF16, cache->head_dim,
                                           static_cast<hipStream_t>(stream)));

@@ -223,6 +223,7 @@ struct WindowAttnArgs {
   float *a_out;                        // fp32 [B][Hq][W][D]
   float *part_m, *part_l, *part_acc;   // workspace partials
   int32_t units, Hkv, G, W, max_blocks, num_blocks, rows, chunk_slots, chunks, want_a;
+  int32_t threads, rt_wave, row_parts;  // workgroup size, row tiles per wave, workgroups per chunk
   float scale;
 };
 
@@ -248,6 +249,10 @@ constexpr int kVtokMaxSources = 4096;  // vtoken.hip: sources per head and call
 // score.hip: DropKV terms with p >= 1/4 queued for the exact pass, per staged
 // window row (weights of one row sum to 1: at most four reach 1/4)
 constexpr int kExactPerRow = 4;
+
+// LDS bytes of one window-attention workgroup (chunk_slots keys per chunk).
+__host__ __device__ size_t window_attn_lds_bytes(int bf16, int head_dim, int want_a,
+                                                 int chunk_slots);
 
 // LDS bytes of one score workgroup (hist: with the tile's key histogram).
 __host__ __device__ size_t score_lds_bytes(int bf16, int head_dim, int drop, int row_tiles,
