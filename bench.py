@@ -67,13 +67,20 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+API_SRC = os.path.join(ROOT, "kv_cache_eviction_qk_amd", "csrc", "api.hip")
+
+
 def source_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """sha256 (16 hex digits) of a kernel source followed by api.hip, which
+    sets the kernel's launch shape (tiles, workgroup size)."""
+    h = hashlib.sha256(open(path, "rb").read())
+    h.update(open(API_SRC, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(workload, kernel_src, kernel="score", sha_key="score_source_sha256_16"):
     """HBM bytes per launch of a kernel from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source."""
+    summary, if it was taken on the current kernel source and launch code."""
     p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.json")
     if not os.path.exists(p):
         return None
@@ -325,6 +332,14 @@ def main():
                    "block_size": 16, "accumulate": "fp32"},
         "pipeline_hbm_frac": pass_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS,
         "pipeline_bytes": pass_bytes,
+        # the whole timed pass (the metric's scope) against HBM: the pass's
+        # algorithmic bytes over ms_per_step; "roofline" below is the
+        # dominant kernel's alone
+        "pass_roofline": {"scope": f"one {args.path} pass (score + select + compact)",
+                          "bound": "hbm", "achieved": pass_bytes / (ms_step / 1e3) / 1e9,
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": pass_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+                          "algorithmic_bytes": pass_bytes, "ms": ms_step},
         "separate_calls_ms": {"score": t_score, "select": t_select, "compact": t_compact},
         "wall_s": wall,
         "blocks_freed_per_pass": int(st[0]),
@@ -668,8 +683,8 @@ def cpu_baseline_decode(case, cfg):
 
     import oracle
     import synth
-    threads = oracle.default_threads()
     B, Hkv = cfg.B, cfg.Hkv
+    threads = baseline_threads(B * Hkv)
     acc = np.zeros((B, Hkv, case["max_blocks"] * 16), np.float32)
     steps, scored, dt = 8, 0, 0.0
     for t in range(steps):
@@ -685,7 +700,7 @@ def cpu_baseline_decode(case, cfg):
         scored += B * n
     return {"value": scored / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"the first {steps} accumulated scoring steps of all {B * Hkv} KV heads; "
-                      f"{dt:.1f} s (select and compact not included)"}
+                      f"{dt:.1f} s (select and compact not included)", **host_cpu()}
 
 
 def bench_ring_stream(args, cfg):
@@ -845,7 +860,7 @@ def cpu_baseline_ring(case, cfg, fill):
     dt = time.perf_counter() - t0
     return {"value": cfg.B * n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{n} dropping steps of all {cfg.B * cfg.Hkv} KV heads at {cfg.budget} "
-                      f"tokens; {dt:.1f} s"}
+                      f"tokens; {dt:.1f} s", **host_cpu()}
 
 
 def _vtok_bytes(U, rows, nsrc, alloc_blocks, row_bytes):
@@ -1107,7 +1122,7 @@ def cpu_baseline_vtok(cfg, theta, max_sources):
             break
     return {"value": U * sub.L * reps / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} x marks + reclamation of {U} of {cfg.B * cfg.Hkv} KV heads "
-                      f"(a 2-sequence slice, {sub.L} tokens each); {dt:.1f} s"}
+                      f"(a 2-sequence slice, {sub.L} tokens each); {dt:.1f} s", **host_cpu()}
 
 
 def cpu_baseline_h2o(case, cfg, fill):
@@ -1137,7 +1152,27 @@ def cpu_baseline_h2o(case, cfg, fill):
     dt = time.perf_counter() - t0
     return {"value": cfg.B * n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{n} pruning steps of all {cfg.B * cfg.Hkv} KV heads at {cfg.budget} "
-                      f"tokens; {dt:.1f} s"}
+                      f"tokens; {dt:.1f} s", **host_cpu()}
+
+
+def host_cpu():
+    """The host CPU's model name and the CPUs this process may run on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cpus_visible": len(os.sched_getaffinity(0))}
+
+
+def baseline_threads(units):
+    """Oracle threads: one head per thread at most, within the host's share
+    of 16 CPUs per GPU (the oracle splits its work over heads)."""
+    import oracle
+    return max(1, min(oracle.default_threads(), units))
 
 
 def cpu_baseline(case, cfg, kind):
@@ -1146,8 +1181,8 @@ def cpu_baseline(case, cfg, kind):
     import numpy as np
 
     import oracle
-    threads = oracle.default_threads()
     units = cfg.B * cfg.Hkv
+    threads = baseline_threads(units)
     # every head of the workload when that stays within about 20 thread-seconds
     sample = list(range(units))
     log(f"cpu baseline: oracle on {len(sample)} of {units} KV heads, {threads} threads")
@@ -1173,7 +1208,7 @@ def cpu_baseline(case, cfg, kind):
     tokens = cfg.L * len(sample) / cfg.Hkv   # scored tokens the sample covers
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(sample)} of {units} KV heads (full context {cfg.L}); "
-                      f"{dt:.1f} s of score+select+compact"}
+                      f"{dt:.1f} s of score+select+compact", **host_cpu()}
 
 
 if __name__ == "__main__":

@@ -35,6 +35,10 @@
  *   expect to be zero and leave zero when their work completes; the rest is
  *   scratch.  Do not modify it between calls; calls sharing it must be
  *   ordered on one stream.  After a KVEV_EDEVICE return, zero it again.
+ *   The vToken entry points size their workspace with their own queries
+ *   (kvev_vtok_*_workspace_bytes) and write only past that state part, so
+ *   one buffer of the larger size may serve both; kvev_h2o_step's workspace
+ *   is its own (see there).
  *
  * Cache layout (one layer)
  * ------------------------

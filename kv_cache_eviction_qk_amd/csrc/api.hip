@@ -550,6 +550,11 @@ kvev::SelHead sel_head(const kvev_cache *cache, int32_t *n_victims, int32_t budg
 
 namespace {
 
+// The vToken entry points' scratch starts past the state part, so that a
+// buffer shared with kvev_select / kvev_compact / kvev_evict keeps its
+// zero state.
+size_t vtok_base(const kvev_cache *c) { return state_layout(c).total; }
+
 // Workspace of kvev_vtok_reclaim (scratch only).
 struct VtokLayout {
   size_t plan, src, srcoff, dstw, dst_off, push_off, tpos, tscore, misc, total;
@@ -558,7 +563,7 @@ struct VtokLayout {
 VtokLayout vtok_layout(const kvev_cache *c, int32_t max_sources) {
   VtokLayout L{};
   const size_t units = (size_t)c->batch * c->kv_heads, ms = (size_t)max_sources;
-  size_t off = 0;
+  size_t off = vtok_base(c);
   L.plan = off; off = a256(off + units * 8 * 4);
   L.src = off; off = a256(off + units * ms * 4);
   L.srcoff = off; off = a256(off + units * ms * 4);
@@ -572,9 +577,9 @@ VtokLayout vtok_layout(const kvev_cache *c, int32_t max_sources) {
   return L;
 }
 
-// Workspace of kvev_vtok_evict: a claim word per slot.
+// Workspace of kvev_vtok_evict: a claim word per slot, past the state part.
 size_t vtok_evict_ws(const kvev_cache *c) {
-  return a256((size_t)c->batch * c->kv_heads * c->max_blocks * KVEV_BLOCK_SIZE * 4);
+  return vtok_base(c) + a256((size_t)c->batch * c->kv_heads * c->max_blocks * KVEV_BLOCK_SIZE * 4);
 }
 
 bool misaligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
@@ -645,7 +650,7 @@ int kvev_vtok_evict(const kvev_cache *cache, uint8_t *live, int32_t *block_live,
   a.victims = victims;
   a.n_victims = n_victims;
   a.status = status;
-  a.claim = static_cast<int32_t *>(workspace);
+  a.claim = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(workspace) + vtok_base(cache));
   return map_err(kvev::launch_vtok_evict(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -699,7 +704,7 @@ int kvev_vtok_digest(const kvev_cache *cache, const uint8_t *live, uint64_t *dig
 }
 
 size_t kvev_vtok_check_workspace_bytes(const kvev_cache *cache) {
-  return valid_cache(cache) ? a256(((size_t)cache->num_blocks + 1) / 2 * 8) : 0;
+  return valid_cache(cache) ? vtok_base(cache) + a256(((size_t)cache->num_blocks + 1) / 2 * 8) : 0;
 }
 
 int kvev_vtok_check(const kvev_cache *cache, const uint8_t *live, const int32_t *block_live,
@@ -716,8 +721,9 @@ int kvev_vtok_check(const kvev_cache *cache, const uint8_t *live, const int32_t 
   a.free_list = const_cast<int32_t *>(free_list);
   a.free_count = const_cast<int32_t *>(free_count);
   a.free_capacity = free_capacity;
-  return map_err(kvev::launch_vtok_check(a, static_cast<int32_t *>(workspace), out,
-                                         static_cast<hipStream_t>(stream)));
+  return map_err(kvev::launch_vtok_check(
+      a, reinterpret_cast<int32_t *>(static_cast<uint8_t *>(workspace) + vtok_base(cache)), out,
+      static_cast<hipStream_t>(stream)));
 }
 
 int kvev_score(const kvev_cache *cache, const kvev_window *win, int32_t flags,
@@ -1120,7 +1126,7 @@ int kvev_vtok_sync(const kvev_cache *cache, uint8_t *live, int32_t *block_live,
 size_t kvev_vtok_map_workspace_bytes(const kvev_cache *cache) {
   if (!valid_cache(cache)) return 0;
   const size_t chunks = ((size_t)cache->max_blocks * KVEV_BLOCK_SIZE + 4095) / 4096;
-  return a256((size_t)cache->batch * cache->kv_heads * chunks * 4);
+  return vtok_base(cache) + a256((size_t)cache->batch * cache->kv_heads * chunks * 4);
 }
 
 int kvev_vtok_slot_mapping(const kvev_cache *cache, const uint8_t *live, int32_t *slots,
@@ -1132,7 +1138,7 @@ int kvev_vtok_slot_mapping(const kvev_cache *cache, const uint8_t *live, int32_t
   a.map_slots = slots;
   a.map_pos = positions;
   a.map_count = count;
-  a.map_chunk = static_cast<int32_t *>(workspace);
+  a.map_chunk = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(workspace) + vtok_base(cache));
   a.map_chunks = (a.max_slots + 4095) / 4096;
   return map_err(kvev::launch_vtok_slot_mapping(a, static_cast<hipStream_t>(stream)));
 }

@@ -505,12 +505,10 @@ size_t h2o_lds_bytes(const H2oArgs &a, int head_dim) {
 template <bool BF16, int D>
 static hipError_t launch_t(const H2oArgs &a, size_t lds, hipStream_t s) {
   auto fn = h2o_step_kernel<BF16, D>;
-  static size_t lds_set = 0;  // largest dynamic LDS size enabled for this variant
-  if (lds > 65536 && lds > lds_set) {
+  if (lds > 65536) {  // idempotent: set on every such launch, no cached state
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    lds_set = lds;
   }
   hipLaunchKernelGGL(fn, dim3((unsigned)(a.units * a.split)), dim3(kThreads), lds, s, a);
   return hipGetLastError();

@@ -351,12 +351,10 @@ template <bool BF16, int LPT>
 static hipError_t launch_t(const RingArgs &a, hipStream_t s) {
   auto fn = ring_step_kernel<BF16, LPT>;
   const size_t lds = ring_lds_bytes(a);
-  static size_t lds_set = 0;  // largest dynamic LDS size enabled for this variant
-  if (lds > 65536 && lds > lds_set) {
+  if (lds > 65536) {  // idempotent: set on every such launch, no cached state
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    lds_set = lds;
   }
   hipLaunchKernelGGL(fn, dim3((unsigned)a.units), dim3(kThreads), lds, s, a);
   return hipGetLastError();

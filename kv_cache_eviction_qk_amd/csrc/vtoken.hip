@@ -478,12 +478,10 @@ hipError_t launch_vtok_reclaim(const VtokArgs &a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t adm_lds = (size_t)a.units * 2 * sizeof(int);
-  static size_t lds_set = 0;  // largest dynamic LDS size enabled for the admission kernel
-  if (adm_lds > 49152 && adm_lds > lds_set) {
+  if (adm_lds > 49152) {  // idempotent: set on every such launch, no cached state
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(vtok_admit_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)adm_lds);
     if (e != hipSuccess) return e;
-    lds_set = adm_lds;
   }
   hipLaunchKernelGGL(vtok_admit_kernel, dim3(1), dim3(kAdmitThreads), adm_lds, s, a);
   e = hipGetLastError();

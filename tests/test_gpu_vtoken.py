@@ -529,3 +529,37 @@ def test_algorithm1_runtime_loop():
             assert np.array_equal(g[key], st[key]), (step, key)
         assert np.array_equal(host(d.c.seq_len), st["seq_len"])
         assert gfc == fc and np.array_equal(gfl[:gfc], fl[:fc]), step
+
+
+def test_vtoken_calls_leave_a_shared_workspace_state_alone():
+    """The vToken calls write only past the workspace's state part: on one
+    buffer shared with kvev_select, a selection after marks and a
+    reclamation gives the victims a fresh buffer gives (claim words at the
+    start of the buffer would have left its selection histograms non-zero)."""
+    st, fl, fc = _state(5, B=2, Hkv=3, max_blocks=12)
+    d = Dev(st, fl, fc)
+    r = rng(55)
+    U, ms = 6, 12 * 16
+    vic = np.full((2, 3, ms), -1, np.int32)
+    nv = np.zeros((2, 3), np.int32)
+    for u in range(U):
+        b, h = divmod(u, 3)
+        cand = np.flatnonzero(st["live"][b, h])
+        v = np.sort(r.permutation(cand)[:cand.size // 2])
+        vic[b, h, :v.size] = v
+        nv[b, h] = v.size
+    n = max(K.new_vtok_evict_workspace(d.c).numel(), K.new_vtok_workspace(d.c, 8).numel(),
+            K.new_workspace(d.c).numel())
+    shared = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    K.vtok_evict(d.c, d.live, d.block_live, dev(vic), dev(nv), shared)
+    K.vtok_reclaim(d.c, d.live, d.block_live, 0.0, 8, d.fl, d.fc, shared, score=d.score)
+    scores = dev(r.uniform(0, 1, (2, 3, ms)).astype(np.float32))
+    v1, n1 = K.select(d.c, scores, 40, 4, workspace=shared)
+    v2, n2 = K.select(d.c, scores, 40, 4, workspace=K.new_workspace(d.c))
+    torch.cuda.synchronize()
+    n1, n2, v1, v2 = host(n1), host(n2), host(v1), host(v2)
+    assert int(n1.sum()) > 0 and np.array_equal(n1, n2)
+    for b in range(2):
+        for h in range(3):
+            m = int(n1[b, h])
+            assert np.array_equal(v1[b, h, :m], v2[b, h, :m]), (b, h)
