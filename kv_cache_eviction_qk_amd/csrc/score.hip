@@ -78,6 +78,13 @@ __device__ __forceinline__ int remap_xcd(int id, int n) {
   return (id % 8) * (n / 8) + id / 8;
 }
 
+// min(v, 0) for any v that is not a NaN (a NaN gives 0, as fmaxf(-v, 0)
+// would), as one integer min on the bits: a negative float is a negative
+// integer, any other is not.
+__device__ __forceinline__ float min_zero(float v) {
+  return __int_as_float(min(__float_as_int(v), 0));
+}
+
 // fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint32_t bf16_bits(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -384,12 +391,13 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) psum[i] += __builtin_amdgcn_exp2f(x[i][e]);
       } else {
-        bool hot = false;  // a weight of at least 2^-12 in the wave
+        // a weight of at least 2^-12 in the wave (the lane's largest x)
+        float hx = x[0][0];
 #pragma unroll
         for (int i = 0; i < NB; ++i)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) hot |= x[i][e] >= -12.f;
-        if (!__any(hot)) {
+          for (int e = 0; e < 4; ++e) hx = fmaxf(hx, x[i][e]);
+        if (!__any(hx >= -12.f)) {
           // p < 2^-12: p/(1-p) = p + p^2 within a relative p^2 (< 2^-24);
           // the sums hold term/sqrt(2): sqrt(-av) = ||a - v|| / sqrt(2)
           float pp[NB][4];
@@ -408,7 +416,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               pdrop[i] = fmaf(fmaf(pp[i][e], pp[i][e], pp[i][e]),
-                              __builtin_amdgcn_sqrtf(fmaxf(-av[i][e], 0.f)), pdrop[i]);
+                              __builtin_amdgcn_sqrtf(-min_zero(av[i][e])), pdrop[i]);
         } else {
           uint32_t slow = 0;  // terms with p >= 1/4: queued for the exact pass
 #pragma unroll
@@ -420,7 +428,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
               // only the wave's own blocks queue (clamped re-reads are dropped)
               const bool exact = !fast_only && x[i][e] >= -2.f && cur + i < wb1;
               slow |= (exact ? 1u : 0u) << (i * 4 + e);
-              const float X = fmaxf(-av[i][e], 0.f);  // ||a - v||^2 / 2
+              const float X = -min_zero(av[i][e]);  // ||a - v||^2 / 2
               const float om = 1.f - p;
               const float t = p * X * __builtin_amdgcn_rsqf(fmaxf(X * om * om, __FLT_MIN__));
               pdrop[i] += exact ? 0.f : t;
