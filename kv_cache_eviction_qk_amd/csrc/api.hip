@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void clear16_kernel(uint4 *p, size_t n16) {
 // all entry points; selection and compaction use disjoint parts of it, so
 // the fused call can pass the threshold from one to the other.
 struct StateLayout {
-  size_t hist, hist2, head_acc, fin_err, fin_nmem, fin_arrive, fin_marks, fin_done, fin_ctr,
+  size_t hist, hist2, head_acc, fin_err, fin_nmem, fin_arrive, fin_marks, fin_done, fin_bctr, fin_ctr,
       fin_acc, total;
   int marks_per_head;
 };
@@ -80,6 +80,7 @@ StateLayout state_layout(const kvev_cache *c) {
   L.fin_arrive = off; off = a256(off + units * 4);
   L.fin_marks = off; off = a256(off + units * (size_t)L.marks_per_head * 4);
   L.fin_done = off; off = a256(off + units * 4);
+  L.fin_bctr = off; off = a256(off + units * 4);
   L.fin_ctr = off; off = a256(off + 4 * 4);
   L.fin_acc = off; off = a256(off + 4 * 8);
   L.total = off;
@@ -856,6 +857,7 @@ int evict_impl(const kvev_cache *cache, const kvev_window *win, int32_t flags,
   f.marks = reinterpret_cast<uint32_t *>(ws + S.fin_marks);
   f.head_done = reinterpret_cast<uint32_t *>(ws + S.fin_done);
   f.ctr = reinterpret_cast<uint32_t *>(ws + S.fin_ctr);
+  f.bctr = reinterpret_cast<uint32_t *>(ws + S.fin_bctr);
   f.acc = reinterpret_cast<unsigned long long *>(ws + S.fin_acc);
   f.units = cache->batch * cache->kv_heads;
   f.max_blocks = cache->max_blocks;

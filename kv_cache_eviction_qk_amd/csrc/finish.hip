@@ -4,20 +4,22 @@
 // The scoring pass has written every live slot's eviction score to a
 // workspace row and added the top 11 bits of each candidate's order key to
 // its head's histogram.  Each KV head then gets kh workgroups of 1024
-// threads.  A workgroup takes its (head, part k) from a ticket counter, so
-// every workgroup with a lower ticket is already resident or done.
+// threads, parts k = 0 .. kh - 1.
 //
 //  1. Threshold.  From the histogram every workgroup of the head knows the
-//     bucket b holding the m-th smallest key.  Each collects, over its own
-//     share of the candidate slots, the keys below b per 1024-slot chunk and
-//     the bucket's (key, slot) members with the histogram of their key bits
-//     20..10, and publishes them; after the head's workgroups have all
-//     arrived, each reads what all published and finds, in LDS, the key T
-//     and the cut slot of the m-th smallest (key, slot) pair (sub-bucket from
-//     the second histogram, a radix pass over the last 10 bits, rank counting
-//     among equal keys).  Victims are the candidates with key < T, or key ==
-//     T and slot <= cut: equal scores evict the lower position ([SNAP]
-//     "Tie-breaking").
+//     bucket b holding the m-th smallest key.  The key T and the cut slot of
+//     the m-th smallest (key, slot) pair then come from the bucket's members:
+//     the histogram of their key bits 20..10 gives the sub-bucket, a radix
+//     pass over the last 10 bits gives T, rank counting among equal keys the
+//     cut.  Victims are the candidates with key < T, or key == T and slot <=
+//     cut: equal scores evict the lower position ([SNAP] "Tie-breaking").
+//     A head of at most kRes groups (32768 slots) is selected locally: each
+//     of its workgroups holds all its keys in registers and finds T, the cut
+//     and the victims per 1024-slot chunk itself, with no exchange.  A longer
+//     head shares the work: each workgroup takes its share of the slots,
+//     publishes the keys below b per chunk, the bucket's members and their
+//     histogram, waits for the head's workgroups to arrive, and reads what
+//     all published.
 //  2. Victim list.  Each workgroup writes the victims of its share's groups
 //     at their offsets, in ascending slot order.
 //  3. Compaction ([H2O] "PagedAttention Memory Integration"; [VTOK] section
@@ -35,11 +37,18 @@
 //     and leaves the state words zero for the next call.
 //
 // Waits and hand-offs.  A workgroup waits only for workgroups of its own
-// head: at the head's arrival counter, and for the marks of lower batches.
-// Tickets are taken in dispatch order, so when a workgroup of a later head is
-// resident every workgroup of this head has been dispatched, and a head
-// needs only kh workgroups at once: every wait ends (each also has a spin
-// limit, status bit 8, so no wave can loop forever).  Published values are
+// head: for the marks of lower batches, and, when the head shares its
+// selection, at the head's arrival counter.  When every head is selected
+// locally (max_slots <= 32768), a workgroup's head and part come from its
+// index, so its loads go out at once and, as dispatch deals workgroups to the
+// 8 XCDs round robin, a head's workgroups share one XCD's L2; its batches
+// come from a per-head ticket taken before the compaction, so a batch waits
+// only for batches that running workgroups have claimed.  Otherwise a
+// launch-wide ticket, taken in dispatch order, names the head and part: when
+// a workgroup of a later head is resident every workgroup of this head has
+// been dispatched, and a head needs only kh workgroups at once.  Every wait
+// ends (each also has a spin limit, status bit 8, so no wave can loop
+// forever).  Published values are
 // written with agent-scope atomic stores and read with agent-scope atomic
 // loads (both bypass the per-XCD L2, which is not coherent across XCDs), and
 // the arrival add is issued after s_waitcnt has seen every one of those
@@ -75,7 +84,7 @@ constexpr int kRes = 8;                 // groups of a share whose keys stay in 
 constexpr int kBatchRanks = 256;        // destination ranks per batch
 constexpr int kMem = 4096;              // sub-bucket members kept in LDS
 constexpr int kTie = 2048;              // keys equal to T ranked by counting
-constexpr int kPreBlk = 1024;           // source block ids prefetched per batch (4 groups)
+constexpr int kPreBlk = 2048;           // block ids held in LDS (a head of kRes groups: all)
 constexpr unsigned kSpinLimit = 1u << 20;  // polls of a wait before it gives up (status bit 8)
 
 constexpr int kChunk = kSelectChunk;    // victim offsets are kept per 1024-slot chunk
@@ -138,6 +147,23 @@ __device__ int block_scan(int v, int *wtot, int *total) {
   return before + incl - v;
 }
 
+// The (head, part) of a ticket.  With the heads a multiple of 8, ticket t
+// goes to head 8 * ((t / 8) / kh) + t % 8, part (t / 8) % kh: when tickets
+// follow dispatch order, which deals workgroups to the 8 XCDs round robin,
+// a head's workgroups share one XCD and its L2 (they all read the head's
+// scores).  Within a head the parts' tickets increase with the part, which is
+// all the waits need.
+__device__ __forceinline__ void ticket_head(int t, int units, int kh, int &u, int &k) {
+  if (units % 8 == 0) {
+    const int slot = t >> 3;
+    u = (slot / kh) * 8 + (t & 7);
+    k = slot % kh;
+  } else {
+    u = t / kh;
+    k = t % kh;
+  }
+}
+
 // Wave 0 polls *p until it reads at least `want` (the caller then barriers).
 __device__ void wait_count(const uint32_t *p, uint32_t want, unsigned long long *acc) {
   if (threadIdx.x >= kWave) return;
@@ -197,10 +223,46 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
   FinLds &L = *reinterpret_cast<FinLds *>(smem);
   const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
 
-  if (tid == 0) L.ticket = atomicAdd(&P.ctr[0], 1u);
-  __syncthreads();
-  const int ticket = (int)L.ticket;
-  const int u = ticket / P.kh, k = ticket % P.kh;
+  // Every head of at most kRes groups (the whole launch when max_slots
+  // allows): the histogram and all keys of the head this workgroup's index
+  // maps to are loaded before the ticket returns, and kept when the ticket
+  // names the same head (the usual case), else loaded again.
+  const bool spec = PR <= 16 && P.max_slots <= kRes * kGrp;
+  uint32_t kr[kRes][4];
+  uint32_t hv[kSelectBins / kFT];
+  auto load_head = [&](int uh) {
+    const float *sch = P.sc + (size_t)uh * P.max_slots;
+#pragma unroll
+    for (int q = 0; q < kRes; ++q) {
+      const int s = min(q * kGrp + 4 * tid, P.max_slots - 4);
+      const float4 v = *reinterpret_cast<const float4 *>(sch + s);
+      kr[q][0] = score_key(v.x);
+      kr[q][1] = score_key(v.y);
+      kr[q][2] = score_key(v.z);
+      kr[q][3] = score_key(v.w);
+    }
+    const uint32_t *hgh = P.hist + (size_t)uh * kSelectBins;
+#pragma unroll
+    for (int q = 0; q < kSelectBins / kFT; ++q) hv[q] = hgh[tid + q * kFT];
+  };
+  // Heads of at most kRes groups (every head, when max_slots allows) are
+  // selected locally with no wait before the compaction: a workgroup's head
+  // and part come from its index (so its loads go out at once, and with
+  // round-robin dispatch a head's workgroups share an XCD), and the
+  // compaction's batches are handed out by a per-head ticket.  Otherwise a
+  // launch-wide ticket, taken in dispatch order, names the head and part:
+  // the shared selection waits for every workgroup of the head.
+  int u, k, ticket;
+  if (spec) {
+    ticket = (int)blockIdx.x;
+    ticket_head(ticket, P.units, P.kh, u, k);
+    load_head(u);
+  } else {
+    if (tid == 0) L.ticket = atomicAdd(&P.ctr[0], 1u);
+    __syncthreads();
+    ticket = (int)L.ticket;
+    ticket_head(ticket, P.units, P.kh, u, k);
+  }
   const size_t urow = (size_t)u * P.max_slots;
   const int n = P.seq_len[u];
   const bool consistent = n >= 0 && n <= P.max_slots;
@@ -233,9 +295,14 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
     const int nch_all = (n + kChunk - 1) / kChunk;
     const int gpp = (ngrp + P.kh - 1) / P.kh;     // groups per share
     const int g_lo = min(k * gpp, ngrp), g_hi = min(g_lo + gpp, ngrp);
-    // keys of the share held in registers (not beside the widest rows' pieces)
-    const bool res = PR <= 16 && g_hi - g_lo <= kRes;
-    uint32_t kr[kRes][4];
+    // A head of at most kRes groups is selected locally: every workgroup of
+    // the head holds all its keys in registers and finds the threshold
+    // itself, with no exchange; longer heads share the work (each its share,
+    // published and read back).  Keys held in registers: the whole head, or
+    // the share (not beside the widest rows' pieces).
+    const bool local = PR <= 16 && ngrp_all <= kRes;
+    const int r_lo = local ? 0 : g_lo, r_hi = local ? ngrp_all : g_hi;
+    const bool res = PR <= 16 && r_hi - r_lo <= kRes;
     // this thread's 4 keys of group g (slots g*4096 + 4*tid + e)
     auto load4 = [&](int g, uint32_t (&o)[4]) {
       const int s = min(g * kGrp + 4 * tid, P.max_slots - 4);
@@ -246,10 +313,10 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
       o[3] = score_key(v.w);
     };
     auto keys_of = [&](int g, uint32_t (&o)[4]) {
-      if (res && g >= g_lo && g < g_hi) {
+      if (res && g >= r_lo && g < r_hi) {
 #pragma unroll
         for (int q = 0; q < kRes; ++q)
-          if (q == g - g_lo) {
+          if (q == g - r_lo) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = kr[q][e];
           }
@@ -257,23 +324,27 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
         load4(g, o);
       }
     };
-    const uint32_t *hg = P.hist + (size_t)u * kSelectBins;
-    uint32_t hv[kSelectBins / kFT];
+    if (!spec) {
+      const uint32_t *hg = P.hist + (size_t)u * kSelectBins;
 #pragma unroll
-    for (int q = 0; q < kSelectBins / kFT; ++q) hv[q] = hg[tid + q * kFT];
+      for (int q = 0; q < kSelectBins / kFT; ++q) hv[q] = hg[tid + q * kFT];
+    }
     // block ids of the share's first groups, where a batch's sources mostly
     // lie (batch k of a head usually draws on group k)
     const int32_t *btu = P.block_table + (size_t)u * P.max_blocks;
-    const int pb0 = g_lo * (kGrp / kBlock);
-    const int pbid = !bad && pb0 + tid < blocks_of(n) ? btu[pb0 + tid] : 0;
+    const int pb0 = spec ? 0 : g_lo * (kGrp / kBlock);
+    int pbid[kPreBlk / kFT];
+#pragma unroll
+    for (int q = 0; q < kPreBlk / kFT; ++q)
+      pbid[q] = !bad && pb0 + tid + q * kFT < blocks_of(n) ? btu[pb0 + tid + q * kFT] : 0;
     // and the destination block ids of this workgroup's first batch
     const int pdid = !bad && tid < kBatchRanks / kBlock &&
                              k * (kBatchRanks / kBlock) + tid < blocks_of(n - m)
                          ? btu[k * (kBatchRanks / kBlock) + tid] : 0;
-    if (res) {
+    if (res && !spec) {
 #pragma unroll
       for (int q = 0; q < kRes; ++q)
-        if (q < g_hi - g_lo) load4(g_lo + q, kr[q]);
+        if (q < r_hi - r_lo) load4(r_lo + q, kr[q]);
     }
 #pragma unroll
     for (int q = 0; q < kSelectBins / kFT; ++q) {
@@ -291,107 +362,163 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
     wg_rank_bin<kSelectBins>(L.h, (uint32_t)m, &L.r);
     const uint32_t bkt = L.r.bin;
     const uint32_t need = (uint32_t)m - L.r.below;  // rank inside the bucket
-    // ---- own share: keys below the bucket per chunk (a wave covers 256
-    // slots of a group: chunk = 4 g + wave / 4), the bucket's members (counted
-    // first, so one atomic per workgroup reserves their place), and the
-    // histogram of their key bits 20..10
+    uint32_t pre, need2;
+    int nmem = 0;
     uint2 *gmem = P.mem + urow;
-    uint32_t *gbel = P.gbelow + (size_t)u * P.chunks;
-    for (int g = g_lo; g < g_hi; ++g) {
-      uint32_t kk[4];
-      keys_of(g, kk);
-      uint32_t below = 0, mine = 0;
+    if (local) {
+      // ---- the whole head: keys below the bucket per chunk (a wave covers
+      // 256 slots of a group: chunk = 4 g + wave / 4) and the histogram of
+      // the bucket members' key bits 20..10
+      // (groups in compile-time order: the keys stay in named registers)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int s = g * kGrp + 4 * tid + e;
-        const bool in = s < nc;
-        const uint32_t top = kk[e] >> 21;
-        below += (uint32_t)__popcll(__ballot(in && top < bkt));
-        const bool mb = in && top == bkt;
-        if (mb) atomicAdd(&L.h2[(kk[e] >> 10) & 2047u], 1u);
-        mine += (uint32_t)__popcll(__ballot(mb));
+      for (int g = 0; g < kRes; ++g) {
+        if (g >= ngrp) break;
+        const uint32_t(&kk)[4] = kr[g];
+        uint32_t below = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s = g * kGrp + 4 * tid + e;
+          const bool in = s < nc;
+          const uint32_t top = kk[e] >> 21;
+          below += (uint32_t)__popcll(__ballot(in && top < bkt));
+          if (in && top == bkt) atomicAdd(&L.h2[(kk[e] >> 10) & 2047u], 1u);
+        }
+        if (lane == 0 && below) atomicAdd(&L.cv[4 * g + wv / 4], below);
       }
-      if (lane == 0) {
-        if (below) atomicAdd(&L.cv[4 * g + wv / 4], below);
-        if (mine) atomicAdd(&L.nown, mine);
+      for (int i = tid; i < 1024; i += kFT) L.h[i] = 0;
+      __syncthreads();
+      wg_rank_bin<kSelectBins>(L.h2, need, &L.r);
+      pre = (bkt << 11) | L.r.bin;  // key >> 10 of T
+      need2 = need - L.r.below;
+      // the bucket's members below the sub-bucket are victims (per chunk);
+      // the sub-bucket's keys get the histogram of their last 10 bits and go
+      // to LDS (the first kMem of them)
+#pragma unroll
+      for (int g = 0; g < kRes; ++g) {
+        if (g >= ngrp) break;
+        const uint32_t(&kk)[4] = kr[g];
+        uint32_t below = 0;  // the wave's 256 slots lie in one chunk
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s = g * kGrp + 4 * tid + e;
+          const bool mb = s < nc && (kk[e] >> 21) == bkt;
+          const uint32_t p = kk[e] >> 10;
+          below += (uint32_t)__popcll(__ballot(mb && p < pre));
+          const bool sb = mb && p == pre;
+          if (sb) atomicAdd(&L.h[kk[e] & 1023u], 1u);
+          const uint64_t sm = __ballot(sb);
+          if (sm) {
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&L.nsub, (uint32_t)__popcll(sm));
+            base = __shfl(base, 0);
+            const uint32_t j = base + (uint32_t)ballot_prefix(sm);
+            if (sb && j < (uint32_t)kMem) L.sub[j] = make_uint2(kk[e], (uint32_t)s);
+          }
+        }
+        if (lane == 0 && below) atomicAdd(&L.cv[4 * g + wv / 4], below);
       }
-    }
-    __syncthreads();
-    if (tid == 0) L.mbase = L.nown ? atomicAdd(&P.nmem[u], L.nown) : 0u;
-    if (tid == 0) L.nown = 0;
-    for (int c = 4 * g_lo + tid; c < min(4 * g_hi, nch); c += kFT) st_agent(gbel + c, L.cv[c]);
-    uint32_t *h2g = P.hist2 + (size_t)u * kSelectBins;
+    } else {
+      // ---- own share: keys below the bucket per chunk (a wave covers 256
+      // slots of a group: chunk = 4 g + wave / 4), the bucket's members (counted
+      // first, so one atomic per workgroup reserves their place), and the
+      // histogram of their key bits 20..10
+      uint32_t *gbel = P.gbelow + (size_t)u * P.chunks;
+      for (int g = g_lo; g < g_hi; ++g) {
+        uint32_t kk[4];
+        keys_of(g, kk);
+        uint32_t below = 0, mine = 0;
 #pragma unroll
-    for (int q = 0; q < kSelectBins / kFT; ++q)
-      if (L.h2[tid + q * kFT]) atomicAdd(&h2g[tid + q * kFT], L.h2[tid + q * kFT]);
-    __syncthreads();
-    const uint32_t mbase = L.mbase;
-    for (int g = g_lo; g < g_hi; ++g) {
-      uint32_t kk[4];
-      keys_of(g, kk);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int s = g * kGrp + 4 * tid + e;
-        const bool mb = s < nc && (kk[e] >> 21) == bkt;
-        const uint64_t mm = __ballot(mb);
-        if (mm) {
-          uint32_t base = 0;
-          if (lane == 0) base = atomicAdd(&L.nown, (uint32_t)__popcll(mm));
-          base = __shfl(base, 0);
-          if (mb) st_agent2(gmem + mbase + base + (uint32_t)ballot_prefix(mm),
-                            make_uint2(kk[e], (uint32_t)s));
+        for (int e = 0; e < 4; ++e) {
+          const int s = g * kGrp + 4 * tid + e;
+          const bool in = s < nc;
+          const uint32_t top = kk[e] >> 21;
+          below += (uint32_t)__popcll(__ballot(in && top < bkt));
+          const bool mb = in && top == bkt;
+          if (mb) atomicAdd(&L.h2[(kk[e] >> 10) & 2047u], 1u);
+          mine += (uint32_t)__popcll(__ballot(mb));
+        }
+        if (lane == 0) {
+          if (below) atomicAdd(&L.cv[4 * g + wv / 4], below);
+          if (mine) atomicAdd(&L.nown, mine);
         }
       }
-    }
-    // ---- arrive, then wait for every workgroup of the head
-    wait_mem();
-    __syncthreads();
-    if (tid == 0) atomicAdd(&P.arrive[u], 1u);
-    wait_count(&P.arrive[u], (uint32_t)P.kh, acc);
-    __syncthreads();
-    // ---- what the head's workgroups published: one round of loads
-    const int nmem = (int)ld_agent(&P.nmem[u]);
+      __syncthreads();
+      if (tid == 0) L.mbase = L.nown ? atomicAdd(&P.nmem[u], L.nown) : 0u;
+      if (tid == 0) L.nown = 0;
+      for (int c = 4 * g_lo + tid; c < min(4 * g_hi, nch); c += kFT) st_agent(gbel + c, L.cv[c]);
+      uint32_t *h2g = P.hist2 + (size_t)u * kSelectBins;
 #pragma unroll
-    for (int q = 0; q < kSelectBins / kFT; ++q) hv[q] = ld_agent(&h2g[tid + q * kFT]);
-    uint32_t cb = tid < nch ? ld_agent(gbel + tid) : 0u;
-    uint2 pr[4];  // the first members, read before their count is known
+      for (int q = 0; q < kSelectBins / kFT; ++q)
+        if (L.h2[tid + q * kFT]) atomicAdd(&h2g[tid + q * kFT], L.h2[tid + q * kFT]);
+      __syncthreads();
+      const uint32_t mbase = L.mbase;
+      for (int g = g_lo; g < g_hi; ++g) {
+        uint32_t kk[4];
+        keys_of(g, kk);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      pr[q] = q * kFT + tid < P.max_slots ? ld_agent2(gmem + q * kFT + tid) : make_uint2(0u, 0u);
-    for (int c = tid + kFT; c < nch; c += kFT) L.cv[c] = ld_agent(gbel + c);
-    if (tid < nch) L.cv[tid] = cb;
+        for (int e = 0; e < 4; ++e) {
+          const int s = g * kGrp + 4 * tid + e;
+          const bool mb = s < nc && (kk[e] >> 21) == bkt;
+          const uint64_t mm = __ballot(mb);
+          if (mm) {
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&L.nown, (uint32_t)__popcll(mm));
+            base = __shfl(base, 0);
+            if (mb) st_agent2(gmem + mbase + base + (uint32_t)ballot_prefix(mm),
+                              make_uint2(kk[e], (uint32_t)s));
+          }
+        }
+      }
+      // ---- arrive, then wait for every workgroup of the head
+      wait_mem();
+      __syncthreads();
+      if (tid == 0) atomicAdd(&P.arrive[u], 1u);
+      wait_count(&P.arrive[u], (uint32_t)P.kh, acc);
+      __syncthreads();
+      // ---- what the head's workgroups published: one round of loads
+      nmem = (int)ld_agent(&P.nmem[u]);
 #pragma unroll
-    for (int q = 0; q < kSelectBins / kFT; ++q) L.h2[tid + q * kFT] = hv[q];
-    for (int i = tid; i < 1024; i += kFT) L.h[i] = 0;
-    __syncthreads();
-    wg_rank_bin<kSelectBins>(L.h2, need, &L.r);
-    const uint32_t pre = (bkt << 11) | L.r.bin;  // key >> 10 of T
-    const uint32_t need2 = need - L.r.below;
-    // every member: those below the sub-bucket are victims (per chunk); the
-    // sub-bucket's keys get the histogram of their last 10 bits and go to LDS
-    // (the first kMem of them)
-    for (int i0 = 0; i0 < nmem; i0 += 4 * kFT) {
-      if (i0 > 0) {
+      for (int q = 0; q < kSelectBins / kFT; ++q) hv[q] = ld_agent(&h2g[tid + q * kFT]);
+      uint32_t cb = tid < nch ? ld_agent(gbel + tid) : 0u;
+      uint2 pr[4];  // the first members, read before their count is known
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        pr[q] = q * kFT + tid < P.max_slots ? ld_agent2(gmem + q * kFT + tid) : make_uint2(0u, 0u);
+      for (int c = tid + kFT; c < nch; c += kFT) L.cv[c] = ld_agent(gbel + c);
+      if (tid < nch) L.cv[tid] = cb;
+#pragma unroll
+      for (int q = 0; q < kSelectBins / kFT; ++q) L.h2[tid + q * kFT] = hv[q];
+      for (int i = tid; i < 1024; i += kFT) L.h[i] = 0;
+      __syncthreads();
+      wg_rank_bin<kSelectBins>(L.h2, need, &L.r);
+      pre = (bkt << 11) | L.r.bin;  // key >> 10 of T
+      need2 = need - L.r.below;
+      // every member: those below the sub-bucket are victims (per chunk); the
+      // sub-bucket's keys get the histogram of their last 10 bits and go to LDS
+      // (the first kMem of them)
+      for (int i0 = 0; i0 < nmem; i0 += 4 * kFT) {
+        if (i0 > 0) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int i = i0 + q * kFT + tid;
+            pr[q] = i < nmem ? ld_agent2(gmem + i) : make_uint2(0u, 0u);
+          }
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int i = i0 + q * kFT + tid;
-          pr[q] = i < nmem ? ld_agent2(gmem + i) : make_uint2(0u, 0u);
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bool v = i0 + q * kFT + tid < nmem;
-        const uint32_t p = pr[q].x >> 10;
-        if (v && p < pre) atomicAdd(&L.cv[pr[q].y / kChunk], 1u);
-        const bool sb = v && p == pre;
-        if (sb) atomicAdd(&L.h[pr[q].x & 1023u], 1u);
-        const uint64_t sm = __ballot(sb);
-        if (sm) {
-          uint32_t base = 0;
-          if (lane == 0) base = atomicAdd(&L.nsub, (uint32_t)__popcll(sm));
-          base = __shfl(base, 0);
-          const uint32_t j = base + (uint32_t)ballot_prefix(sm);
-          if (sb && j < (uint32_t)kMem) L.sub[j] = pr[q];
+          const bool v = i0 + q * kFT + tid < nmem;
+          const uint32_t p = pr[q].x >> 10;
+          if (v && p < pre) atomicAdd(&L.cv[pr[q].y / kChunk], 1u);
+          const bool sb = v && p == pre;
+          if (sb) atomicAdd(&L.h[pr[q].x & 1023u], 1u);
+          const uint64_t sm = __ballot(sb);
+          if (sm) {
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&L.nsub, (uint32_t)__popcll(sm));
+            base = __shfl(base, 0);
+            const uint32_t j = base + (uint32_t)ballot_prefix(sm);
+            if (sb && j < (uint32_t)kMem) L.sub[j] = pr[q];
+          }
         }
       }
     }
@@ -402,6 +529,17 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
     auto for_sub = [&](auto &&f) {
       if (sub_lds) {
         for (int i = tid; i < nsub; i += kFT) f(L.sub[i].x, (int)L.sub[i].y);
+      } else if (local) {
+#pragma unroll
+        for (int g = 0; g < kRes; ++g) {
+          if (g >= ngrp) break;
+          const uint32_t(&kk)[4] = kr[g];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int s = g * kGrp + 4 * tid + e;
+            if (s < nc && (kk[e] >> 10) == pre) f(kk[e], s);
+          }
+        }
       } else {
         for (int i = tid; i < nmem; i += kFT) {
           const uint2 p = ld_agent2(gmem + i);
@@ -535,17 +673,29 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
         return lo;
       };
       int b0 = pb0;  // first block whose id L.blk holds
-      L.blk[tid] = pbid;
-      for (int rho = k; rho < nbatch; rho += P.kh) {
+#pragma unroll
+      for (int q = 0; q < kPreBlk / kFT; ++q) L.blk[tid + q * kFT] = pbid[q];
+      // the first batch: the per-head ticket (local selection), else the part
+      if (spec && tid == 0) L.ticket = atomicAdd(&P.bctr[u], 1u);
+      __syncthreads();
+      const int kb = spec ? (int)L.ticket : k;
+      for (int rho = kb; rho < nbatch; rho += P.kh) {
         const int R0 = rho * kBatchRanks, R1 = min(R0 + kBatchRanks, n2);
         const int gs = chunk_of_rank(R0) / 4;  // group of the first source
         // block ids: the destinations', and the first source groups' unless
         // the prefetched ones cover them (loads in flight while the groups
         // are ranked)
         const bool fresh = gs * (kGrp / kBlock) < b0 || gs * (kGrp / kBlock) >= b0 + kPreBlk;
-        const int bid = fresh && gs * (kGrp / kBlock) + tid < blocks_of(n)
-                            ? bt[gs * (kGrp / kBlock) + tid] : 0;
-        const int did = rho == k ? pdid
+        int bid[kPreBlk / kFT];
+#pragma unroll
+        for (int q = 0; q < kPreBlk / kFT; ++q) {
+          const int bi = gs * (kGrp / kBlock) + tid + q * kFT;
+          bid[q] = fresh && bi < blocks_of(n) ? bt[bi] : 0;
+        }
+        // (a head held whole in L.blk: every id from LDS)
+        const int did = spec ? (tid < kBatchRanks / kBlock && R0 / kBlock + tid < blocks_of(n2)
+                                    ? L.blk[R0 / kBlock + tid] : 0)
+                        : rho == k ? pdid  // prefetched for batch k
                         : tid < kBatchRanks / kBlock && R0 / kBlock + tid < blocks_of(n2)
                             ? bt[R0 / kBlock + tid] : 0;
         // rank each kept slot of group g; record the sources of [R0, R1)
@@ -573,7 +723,8 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
         }
         if (fresh) {
           __syncthreads();  // the previous batch's readers of blk are done
-          L.blk[tid] = bid;
+#pragma unroll
+          for (int q = 0; q < kPreBlk / kFT; ++q) L.blk[tid + q * kFT] = bid[q];
           b0 = gs * (kGrp / kBlock);
         }
         if (tid < kBatchRanks / kBlock) L.dblk[tid] = did;
@@ -705,7 +856,10 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
         st_agent(&P.arrive[u], 0u);
       }
     }
-    if (tid == 0) st_agent(&P.head_done[u], 0u);
+    if (tid == 0) {
+      st_agent(&P.head_done[u], 0u);
+      st_agent(&P.bctr[u], 0u);
+    }
   }
   __syncthreads();
   if (tid == 0)

@@ -101,6 +101,7 @@ struct FinishArgs {
   // and arrivals per head, per-batch "sources read" marks, workgroups done
   // per head, the ticket and done counters, and the stat accumulators
   uint32_t *head_err, *hist, *hist2, *nmem, *arrive, *marks, *head_done, *ctr;
+  uint32_t *bctr;  // per head: batch tickets of the compaction
   unsigned long long *acc;      // [4]: blocks freed, rows moved, at-risk rows, status bits
   // scratch: the bucket's (key, slot) members [units][max_slots], keys below
   // the bucket per 1024-slot chunk [units][chunks]
