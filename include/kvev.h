@@ -61,7 +61,7 @@ extern "C" {
 #endif
 
 #define KVEV_BLOCK_SIZE 16
-#define KVEV_ABI_VERSION 16
+#define KVEV_ABI_VERSION 17
 /* bytes of the static device array kvev_evict_noalloc works in, per GPU */
 #define KVEV_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 
@@ -409,28 +409,40 @@ size_t kvev_h2o_workspace_bytes(const kvev_cache *cache, int32_t group, int32_t 
  * new token enters with a zero ring.  Below the budget it is appended (a
  * block popped from the free list when its logical block has none; heads
  * appending in the same step may take the blocks in any order).  At the
- * budget one token is dropped: ring sums S (index 0 upward, fp32; 0 for the
- * new token), max-pooled over the pool_kernel tokens centred on each in
- * position order (clamped at both ends); the smallest (pooled, position)
- * among the tokens at least recent_window positions older than t (the new
- * token included when recent_window == 0) is dropped, and the new token
- * overwrites a dropped cached token's slot (K, V, pos, a zero ring).
+ * budget one token is dropped: ring sums S (fp32; 0 for the new token),
+ * max-pooled over the pool_kernel tokens centred on each in position order
+ * (clamped at both ends); the smallest (pooled, position) among the tokens
+ * at least recent_window positions older than t (the new token included
+ * when recent_window == 0) is dropped, and the new token overwrites a
+ * dropped cached token's slot (K, V, pos, a zero ring).  S is summed as:
+ * the entries other than the one the step writes, index 0 upward, then the
+ * step's weight (a null step: all entries, index 0 upward).
  * evicted_pos: int32 [batch][kv_heads], -1 appended, else the dropped
  * position; -2 (seq_len outside [0, budget], ring index or a rank out of
  * range), -3 (no free block), -4 (a block id out of range) leave the head
- * unchanged.  Positions of a head must be distinct.  One 1024-thread
- * workgroup per head on `stream`.
+ * unchanged.  Positions of a head must be distinct.  One launch on
+ * `stream`; each head is split over several 1024-thread workgroups that
+ * hand their partial results to the last one through the workspace.
+ * Workspace: at least kvev_ring_workspace_bytes(cache, group, budget)
+ * bytes, zero-filled once before its first use (its leading part holds
+ * per-head arrival counters that every call leaves zero); it may not alias
+ * another entry point's workspace while both are in use.
  * Errors: KVEV_EINVAL for NULL pointers, a bad cache, group < 1,
  * recent_window outside [0, budget), obs_window < 1, an even or
  * non-positive pool_kernel, budget above the capacity; KVEV_EUNSUPPORTED
  * for group > 8, budget > 4096, group * (budget + 1) > 16384 or pool_kernel
- * > 2 * budget + 1.
+ * > 2 * budget + 1; KVEV_ENOSPACE for a missing or short workspace.
  */
 int kvev_ring_step(const kvev_cache *cache, float *hist, int32_t *ring, int32_t *rank,
                    const void *q, const void *k_new, const void *v_new, const int32_t *t_pos,
                    const int32_t *observe, int32_t group, float scale, int32_t budget,
                    int32_t recent_window, int32_t obs_window, int32_t pool_kernel,
-                   int32_t *free_list, int32_t *free_count, int32_t *evicted_pos, void *stream);
+                   int32_t *free_list, int32_t *free_count, int32_t *evicted_pos,
+                   void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes kvev_ring_step needs for this cache, group and budget; 0
+ * for a bad cache or a group / budget it refuses. */
+size_t kvev_ring_workspace_bytes(const kvev_cache *cache, int32_t group, int32_t budget);
 
 /*
  * kvev_ring_init -- the ring state of a cache for kvev_ring_step: every

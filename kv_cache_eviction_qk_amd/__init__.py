@@ -35,11 +35,11 @@ EXPORTS = ("kvev_score", "kvev_select", "kvev_compact", "kvev_evict", "kvev_evic
            "kvev_vtok_evict_workspace_bytes", "kvev_vtok_reclaim", "kvev_vtok_workspace_bytes",
            "kvev_vtok_digest", "kvev_vtok_check", "kvev_vtok_check_workspace_bytes",
            "kvev_select_shared", "kvev_select_shared_workspace_bytes", "kvev_select_budgets",
-           "kvev_ring_step", "kvev_ring_init", "kvev_vtok_sync", "kvev_vtok_slot_mapping",
+           "kvev_ring_step", "kvev_ring_workspace_bytes", "kvev_ring_init", "kvev_vtok_sync", "kvev_vtok_slot_mapping",
            "kvev_vtok_map_workspace_bytes",
            "kvev_window_attn",
            "kvev_workspace_bytes", "kvev_strerror", "kvev_abi_version")
-ABI_VERSION = 16
+ABI_VERSION = 17
 
 
 class KvevError(RuntimeError):
@@ -99,7 +99,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.kvev_select_shared.argtypes = [P, P, i32, i32, P, P, P, sz, P]
     L.kvev_select_budgets.argtypes = [P, P, P, P, P, P, P, sz, P]
     L.kvev_ring_step.argtypes = [P, P, P, P, P, P, P, P, P, i32, ctypes.c_float, i32, i32, i32,
-                                 i32, P, P, P, P]
+                                 i32, P, P, P, P, sz, P]
+    L.kvev_ring_workspace_bytes.argtypes = [P, i32, i32]
+    L.kvev_ring_workspace_bytes.restype = sz
     L.kvev_ring_init.argtypes = [P, P, P, P, i32, P]
     L.kvev_vtok_sync.argtypes = [P, P, P, P, P, P, P]
     L.kvev_vtok_slot_mapping.argtypes = [P, P, P, P, P, P, sz, P]
@@ -673,11 +675,14 @@ def vtok_check(cache: Cache, live: torch.Tensor, block_live: torch.Tensor,
 
 class RingState:
     """The SnapKV ring-buffer state of a cache: hist fp32 [B, Hkv, W,
-    max_slots], ring int32 [B, Hkv], rank int32 [B, Hkv, max_slots]."""
+    max_slots], ring int32 [B, Hkv], rank int32 [B, Hkv, max_slots], and
+    the step's zero-filled workspace per (group, budget), allocated by the
+    first step that needs it (take that step before capturing a graph)."""
 
     def __init__(self, cache: Cache, obs_window: int, stream=None):
         B, Hkv, dev_ = cache.batch, cache.kv_heads, cache.k_pool.device
         self.W = obs_window
+        self.ws = {}
         self.hist = torch.empty((B, Hkv, obs_window, cache.max_slots), dtype=torch.float32,
                                 device=dev_)
         self.ring = torch.empty((B, Hkv), dtype=torch.int32, device=dev_)
@@ -708,10 +713,17 @@ def ring_step(cache: Cache, state: RingState, q: torch.Tensor, k_new: torch.Tens
     if evicted is None:
         evicted = torch.empty((B, Hkv), dtype=torch.int32, device=q.device)
     _need(evicted, "evicted", torch.int32, B * Hkv)
+    ws = state.ws.get((group, budget))
+    if ws is None:
+        n = L.kvev_ring_workspace_bytes(ctypes.byref(c), group, budget)
+        if n == 0:
+            raise KvevError(EUNSUPPORTED, "kvev_ring_workspace_bytes")
+        ws = state.ws[(group, budget)] = torch.zeros(n, dtype=torch.uint8, device=q.device)
     _check(L.kvev_ring_step(ctypes.byref(c), _ptr(state.hist), _ptr(state.ring), _ptr(state.rank),
                             _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(t_pos), _ptr(observe), group,
                             scale, budget, recent, state.W, pool_kernel, _ptr(free_list),
-                            _ptr(free_count), _ptr(evicted), _stream(stream)), "kvev_ring_step")
+                            _ptr(free_count), _ptr(evicted), _ptr(ws), ws.numel(),
+                            _stream(stream)), "kvev_ring_step")
     return evicted
 
 

@@ -272,6 +272,28 @@ H2oLayout h2o_layout(const kvev_cache *c, int32_t group, int32_t budget) {
   return L;
 }
 
+// Workspace of kvev_ring_step: [arrival counters] (state, zero between
+// calls) then the parts' e values, the other ring entries' sums and (max,
+// sum) per row.
+struct RingLayout {
+  size_t arrive, e, rsum, ml, total;
+  int np, nbmax;
+};
+
+RingLayout ring_layout(const kvev_cache *c, int32_t group, int32_t budget) {
+  RingLayout L{};
+  const size_t units = (size_t)c->batch * c->kv_heads;
+  L.nbmax = (budget + KVEV_BLOCK_SIZE - 1) / KVEV_BLOCK_SIZE;
+  L.np = L.nbmax * KVEV_BLOCK_SIZE;
+  size_t off = 0;
+  L.arrive = off; off = a256(off + units * 4);
+  L.e = off; off = a256(off + units * (size_t)group * L.np * 4);
+  L.rsum = off; off = a256(off + units * (size_t)L.np * 4);
+  L.ml = off; off = a256(off + units * (size_t)kvev::kRingMaxSplit * 32 * 4);
+  L.total = off;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1066,11 +1088,19 @@ int kvev_ring_init(const kvev_cache *cache, float *hist, int32_t *ring, int32_t 
   return map_err(kvev::launch_ring_init(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t kvev_ring_workspace_bytes(const kvev_cache *cache, int32_t group, int32_t budget) {
+  if (!valid_cache(cache) || group < 1 || group > kvev::kRingMaxGroup || budget < 1 ||
+      budget > kvev::kRingMaxBudget)
+    return 0;
+  return ring_layout(cache, group, budget).total;
+}
+
 int kvev_ring_step(const kvev_cache *cache, float *hist, int32_t *ring, int32_t *rank,
                    const void *q, const void *k_new, const void *v_new, const int32_t *t_pos,
                    const int32_t *observe, int32_t group, float scale, int32_t budget,
                    int32_t recent_window, int32_t obs_window, int32_t pool_kernel,
-                   int32_t *free_list, int32_t *free_count, int32_t *evicted_pos, void *stream) {
+                   int32_t *free_list, int32_t *free_count, int32_t *evicted_pos,
+                   void *workspace, size_t ws_bytes, void *stream) {
   if (!valid_cache(cache) || !hist || !ring || !rank || !q || !k_new || !v_new || !t_pos ||
       !observe || !free_list || !free_count || !evicted_pos)
     return KVEV_EINVAL;
@@ -1081,6 +1111,9 @@ int kvev_ring_step(const kvev_cache *cache, float *hist, int32_t *ring, int32_t 
   if (group > kvev::kRingMaxGroup || budget > kvev::kRingMaxBudget ||
       (int64_t)group * (budget + 1) > 16384 || pool_kernel > 2 * budget + 1)
     return KVEV_EUNSUPPORTED;
+  const RingLayout L = ring_layout(cache, group, budget);
+  if (!workspace || ws_bytes < L.total) return KVEV_ENOSPACE;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
   kvev::RingArgs a{};
   a.k_pool = static_cast<uint8_t *>(cache->k_pool);
   a.v_pool = static_cast<uint8_t *>(cache->v_pool);
@@ -1108,6 +1141,16 @@ int kvev_ring_step(const kvev_cache *cache, float *hist, int32_t *ring, int32_t 
   a.budget = budget;
   a.recent = recent_window;
   a.pool_kernel = pool_kernel;
+  a.e = reinterpret_cast<uint32_t *>(ws + L.e);
+  a.rsum = reinterpret_cast<uint32_t *>(ws + L.rsum);
+  a.ml = reinterpret_cast<uint32_t *>(ws + L.ml);
+  a.arrive = reinterpret_cast<uint32_t *>(ws + L.arrive);
+  a.nbmax = L.nbmax;
+  a.np = L.np;
+  // enough workgroups to cover the CUs, at most one per block of the budget
+  const int want = (256 + a.units - 1) / a.units;
+  a.split = std::max(1, std::min({want, kvev::kRingMaxSplit, L.nbmax}));
+  a.cb = (L.nbmax + a.split - 1) / a.split;
   a.c1 = scale * 1.4426950408889634f;
   return map_err(kvev::launch_ring_step(a, cache->dtype == KVEV_BF16, cache->head_dim,
                                         static_cast<hipStream_t>(stream)));

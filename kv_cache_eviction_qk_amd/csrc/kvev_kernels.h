@@ -199,6 +199,7 @@ hipError_t launch_select_shared(const SharedArgs &a, hipStream_t s);
 constexpr int kRingMaxGroup = 8;
 constexpr int kRingMaxBudget = 4096;
 constexpr int kRingMaxBlocks = kRingMaxBudget / 16 + 1;
+constexpr int kRingMaxSplit = 8;       // workgroups per head
 struct RingArgs {
   uint8_t *k_pool, *v_pool;
   int32_t *block_table, *seq_len, *pos;
@@ -208,12 +209,17 @@ struct RingArgs {
   const int32_t *t_pos, *observe;      // [B]
   int32_t *free_list, *free_count;
   int32_t *evicted;                    // [units]
+  // workspace: e values [units][G][np], the other ring entries' sums
+  // [units][np], part maxima and sums [units][8][32]; state (zero between
+  // calls): arrival counters [units]
+  uint32_t *e, *rsum, *ml, *arrive;
   int32_t units, Hkv, G, W, max_blocks, max_slots, num_blocks, budget, recent, pool_kernel;
+  int32_t split, cb, nbmax, np;        // parts per head, blocks per part, budget blocks, e stride
   float c1;                            // softmax scale * log2(e)
 };
 hipError_t launch_ring_step(const RingArgs &a, int bf16, int head_dim, hipStream_t s);
 hipError_t launch_ring_init(const RingArgs &a, hipStream_t s);
-size_t ring_lds_bytes(const RingArgs &a);
+size_t ring_lds_bytes(const RingArgs &a);  // dynamic LDS of one workgroup
 
 struct WindowAttnArgs {
   const uint8_t *k_pool, *v_pool;

@@ -416,13 +416,13 @@ def test_ring_step_refusals():
     L = K.load_library()
     c = cache(max_blocks=8)
 
-    def call(group=4, budget=64, recent=8, W=4, pool=3, ptrs=None, cc=None):
+    def call(group=4, budget=64, recent=8, W=4, pool=3, ptrs=None, cc=None, ws_bytes=1 << 30):
         p = dict(h=FAKE, r=FAKE, k=FAKE, q=FAKE, kn=FAKE, vn=FAKE, t=FAKE, o=FAKE, fl=FAKE,
-                 fc=FAKE, ev=FAKE)
+                 fc=FAKE, ev=FAKE, ws=FAKE)
         p.update(ptrs or {})
         return L.kvev_ring_step(ctypes.byref(cc or c), p["h"], p["r"], p["k"], p["q"], p["kn"],
                                 p["vn"], p["t"], p["o"], group, 0.1, budget, recent, W, pool,
-                                p["fl"], p["fc"], p["ev"], None)
+                                p["fl"], p["fc"], p["ev"], p["ws"], ws_bytes, None)
 
     for name in ("h", "r", "k", "q", "kn", "vn", "t", "o", "fl", "fc", "ev"):
         assert call(ptrs={name: None}) == K.EINVAL, name
@@ -438,6 +438,15 @@ def test_ring_step_refusals():
     assert call(cc=big, group=1, budget=4097) == K.EUNSUPPORTED
     assert call(cc=big, group=8, budget=2048) == K.EUNSUPPORTED   # 8 * 2049 > 16384
     assert call(pool=131) == K.EUNSUPPORTED
+    need = L.kvev_ring_workspace_bytes(ctypes.byref(c), 4, 64)
+    assert need > 0
+    assert call(ptrs={"ws": None}) == K.ENOSPACE
+    assert call(ws_bytes=need - 1) == K.ENOSPACE
+    # the size query refuses what the step refuses
+    assert L.kvev_ring_workspace_bytes(ctypes.byref(c), 0, 64) == 0
+    assert L.kvev_ring_workspace_bytes(ctypes.byref(c), 9, 64) == 0
+    assert L.kvev_ring_workspace_bytes(ctypes.byref(c), 4, 4097) == 0
+    assert L.kvev_ring_workspace_bytes(None, 4, 64) == 0
     assert L.kvev_ring_init(ctypes.byref(c), None, FAKE, FAKE, 4, None) == K.EINVAL
     assert L.kvev_ring_init(ctypes.byref(c), FAKE, FAKE, FAKE, 0, None) == K.EINVAL
 

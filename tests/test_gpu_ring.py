@@ -70,6 +70,7 @@ class Dev:
     def load_ring(self, st):
         self.ring = K.RingState.__new__(K.RingState)
         self.ring.W = st["hist"].shape[2]
+        self.ring.ws = {}
         self.ring.hist = dev(st["hist"])
         self.ring.ring = dev(st["ring"])
         self.ring.rank = dev(st["rank"])
@@ -131,30 +132,36 @@ def _compare(pre, o, oev, g, gev, t, budget, recent, pool, wide, ring0, observe,
     return diverged
 
 
-def _ring_case(seed, dtype, B, Hkv, G, D, budget, n0, W):
-    keys, vals, qs = _stream_inputs(seed, B, Hkv, G, D, 512)
+def _ring_case(seed, dtype, B, Hkv, G, D, budget, n0, W, steps=40):
+    keys, vals, qs = _stream_inputs(seed, B, Hkv, G, D, max(512, n0 + steps))
     st = _state(keys, vals, n0, budget + 1, G, dtype=dtype)
     st = oracle.ring_state(st, W)
     return st, keys, vals, qs
 
 
 CASES = [
-    # dtype, D, G, budget, recent, W, pool, n0
+    # dtype, D, G, budget, recent, W, pool, n0[, B, Hkv, steps]
     ("bf16", 128, 4, 100, 20, 8, 7, 96),
     ("f32", 64, 2, 40, 0, 3, 1, 38),
     ("bf16", 64, 8, 57, 1, 5, 5, 50),
     ("f32", 128, 4, 48, 6, 16, 3, 44),
+    # budgets over 1024 (four slots per thread in the last workgroup), rings
+    # of more than 32 entries, a pooling radius past 8
+    ("bf16", 64, 2, 1300, 40, 40, 19, 1290),
+    # 256 heads: one workgroup per head, whose 700 slots exceed one pass of
+    # its thread pairs over the ring entries
+    ("bf16", 64, 1, 700, 16, 6, 5, 694, 32, 8, 10),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
 def test_isolated_steps(case):
-    dtype, D, G, budget, recent, W, pool, n0 = case
-    B, Hkv = 2, 3
-    st, keys, vals, qs = _ring_case(7 + D + G, dtype, B, Hkv, G, D, budget, n0, W)
+    dtype, D, G, budget, recent, W, pool, n0 = case[:8]
+    B, Hkv, steps = case[8:] if len(case) > 8 else (2, 3, 40)
+    st, keys, vals, qs = _ring_case(7 + D + G, dtype, B, Hkv, G, D, budget, n0, W, steps)
     d = Dev(st, np.full(st["num_blocks"], -1, np.int32), 0)
     drops = 0
-    for i, t in enumerate(range(n0, n0 + 40)):
+    for i, t in enumerate(range(n0, n0 + steps)):
         observe = np.array([int((t + b) % 5 != 0) for b in range(B)], np.int32)
         q, k, v = _enc(qs[t], st), _enc(keys[:, :, t], st), _enc(vals[:, :, t], st)
         tp = np.full(B, t, np.int32)
@@ -167,7 +174,7 @@ def test_isolated_steps(case):
         drops += int((oev >= 0).sum())
         st = o
     assert drops > 0
-    _say(f"{case}: {drops} drops over 40 steps")
+    _say(f"{case}: {drops} drops over {steps} steps")
 
 
 def test_free_running_chain_full_decode_shape():
