@@ -20,8 +20,8 @@
 //         counts the new token) and e = exp2(logit - m) of its slots; at the
 //         budget, for each of its slots the sum of the ring entries other
 //         than the one this step writes (index order).  All of it goes to
-//         the workspace with agent-scope stores, then one acquire-release
-//         agent-scope atomic on the head's arrival counter.
+//         the workspace with agent-scope atomic stores; once they have
+//         completed, one agent-scope atomic on the head's arrival counter.
 //   final (the workgroup that arrives last): the checks (block ids, ranks);
 //         lse of each row from the parts' (m, l) in order; each cached
 //         slot's weight, the sum over the rows (ascending) of
@@ -274,13 +274,17 @@ __global__ __launch_bounds__(kThreads) void ring_step_kernel(const RingArgs P) {
     cst(ML + w * 32 + tid, __float_as_uint(s_m[tid]));
     cst(ML + w * 32 + 16 + tid, __float_as_uint(s_l[tid]));
   }
-  // every published value has completed before the arrival; the arrival
-  // releases them (the barrier orders the other waves' stores before it)
-  // and, in the last part, acquires every other part's
+  // Hand-off: every value another workgroup reads is written and read with
+  // agent-scope atomics (stores through to the agent's coherence point,
+  // loads from it), and each wave waits for its stores to complete before
+  // the barrier that precedes the arrival; the last part's loads are issued
+  // after its arrival returned.  A release/acquire arrival would add the L2
+  // write-back and invalidate that plain (non-atomic) data needs; nothing
+  // here hands over plain data.
   drain();
   __syncthreads();
   if (tid == 0)
-    s_last = __hip_atomic_fetch_add(P.arrive + u, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+    s_last = __hip_atomic_fetch_add(P.arrive + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
              (uint32_t)(S - 1);
   __syncthreads();
   if (!s_last) return;
