@@ -233,9 +233,13 @@ size_t kvev_select_shared_workspace_bytes(const kvev_cache *cache);
  * free_list: int32 [free_capacity] device array; free_count: one int32 on
  * the device.  At most 4096 KV heads (batch * kv_heads) per call.  stats: int64[5] on the device = {blocks_freed, rows_moved,
  * bytes_moved (K and V rows moved, read + write), at_risk_rows (kept rows
- * whose source lies inside the compacted range and is staged through the
- * workspace first), status (0, or a bit set per inconsistent head: bit 0
- * victims not ascending / out of range, bit 1 seq_len above capacity)}.
+ * whose source lies inside the compacted range), status (0, or a bit set per
+ * inconsistent head: bit 0 victims not ascending / out of range, bit 1
+ * seq_len above capacity)}.  The at-risk rows of a head are staged through
+ * the workspace when there are at most 4096 of them; a head with more is
+ * moved by one workgroup in ascending rounds of destination ranks, each
+ * round's rows all read before any is written, so the workspace holds at
+ * most 4096 staged rows a head.
  * Errors: KVEV_EINVAL for NULL pointers or a bad cache; KVEV_ENOSPACE when
  * free_capacity < num_blocks (the list must be able to hold the whole pool)
  * or ws_bytes < kvev_workspace_bytes(cache, 1, 1); KVEV_EUNSUPPORTED above 4096

@@ -138,7 +138,7 @@ SelectLayout select_layout(const kvev_cache *c) {
 }
 
 struct CompactLayout {
-  size_t src_of, new_pos, new_score, stage_k, stage_v, head_info, fc0, total;
+  size_t src_of, src_row, new_pos, new_score, stage_k, stage_v, head_info, fc0, total;
   int chunks, stage_rows;
 };
 
@@ -148,11 +148,12 @@ CompactLayout compact_layout(const kvev_cache *c) {
   const size_t max_slots = (size_t)c->max_blocks * KVEV_BLOCK_SIZE;
   const size_t row_bytes = (size_t)c->head_dim * elem_bytes(c);
   L.chunks = (int)((max_slots + kvev::kCompactChunk - 1) / kvev::kCompactChunk);
-  // At-risk rows are staged at their destination rank: up to n' - 1 rows of
-  // a head (evicting only slot 0 shifts every other row).
-  L.stage_rows = (int)max_slots;
+  // At-risk rows are staged up to kCompactStageRows a head (a head with more
+  // is compacted in rank order by one workgroup, staging nothing).
+  L.stage_rows = (int)std::min<size_t>(max_slots, kvev::kCompactStageRows);
   size_t off = select_layout(c).total;
   L.src_of = off; off = a256(off + units * max_slots * 4);
+  L.src_row = off; off = a256(off + units * max_slots * 4);
   L.new_pos = off; off = a256(off + units * max_slots * 4);
   L.new_score = off; off = a256(off + units * max_slots * 4);
   L.stage_k = off; off = a256(off + units * (size_t)L.stage_rows * row_bytes);
@@ -529,6 +530,7 @@ void fill_compact_args(kvev_cache *cache, float *score_or_null, int32_t *free_li
   a.free_count = free_count;
   a.stats = stats;
   a.src_of = reinterpret_cast<int32_t *>(ws + L.src_of);
+  a.src_row = reinterpret_cast<int32_t *>(ws + L.src_row);
   a.new_pos = reinterpret_cast<int32_t *>(ws + L.new_pos);
   a.new_score = reinterpret_cast<float *>(ws + L.new_score);
   a.stage_k = ws + L.stage_k;

@@ -3,15 +3,21 @@
 // Kept slot s of rank r moves to slot r (r <= s).  Done in parallel this has
 // one hazard: a destination row r < n' may still be the source of another
 // kept token.  Those sources are exactly the kept slots in [first victim, n')
-// ("at risk"); they are copied to the workspace first.  Two launches:
+// ("at risk"); they are copied to the workspace first, up to stage_rows of a
+// head.  A head with more at-risk rows is moved by one workgroup in rank
+// order instead, staging nothing: rounds of destination ranks in ascending
+// order, every load of a round returned before any store (a source never
+// lies below its destination, so no later round reads a slot an earlier one
+// wrote, and within a round the loads precede the stores).  Three launches:
 //   prep    (1024-slot chunk of one head per workgroup): finds the chunk's
 //           victims, ranks the kept slots, records for each destination rank
 //           its source (physical row, staged copy, or "stays") and the kept
 //           pos / score values, and copies the at-risk rows to the workspace.
 //           Reads the cache only.  Each chunk adds its counts into one 64-bit
 //           word of the head (arrivals, chunks with errors, rows moved, rows
-//           staged) with a single atomic; the chunk that arrives last records
-//           the head's totals, so no chunk reads another's memory.
+//           staged) with a single atomic, whose previous value also gives
+//           the chunk's first staging row; the chunk that arrives last
+//           records the head's totals, so no chunk reads another's memory.
 //           The chunk's victims come from the caller's ascending victim list
 //           (256 evenly spaced samples bracket them, one range load fetches
 //           them).
@@ -24,6 +30,9 @@
 //           [ceil(n'/16), ceil(n/16)) to the free list in (b, h, block)
 //           order, clears their table entries, sets seq_len = n' and adds the
 //           head's stats.
+//   inorder (one 1024-thread workgroup per head): moves the rows of the
+//           heads whose at-risk rows did not fit, in ascending rounds of
+//           destination ranks; the other heads return at once.
 // ([H2O] "PagedAttention Memory Integration"; [VTOK] section 3.3, stage 3
 // and section 3.5, invariants I1, I2 and I4.)
 #include <hip/hip_runtime.h>
@@ -41,13 +50,15 @@ constexpr int kChunk = kCompactChunk;   // slots per prep workgroup
 constexpr int kPerThread = kChunk / kThreads;
 constexpr int kMaxUnits = kCompactMaxUnits;
 constexpr int kRange = 4096;            // victims a prep workgroup stages in LDS
+constexpr int kSeqThreads = 1024;       // in-order kernel: threads per head
+constexpr int kSeqRows = 8;             // in-order kernel: rows per thread and round
 
 struct PrepLds {
-  int stage_s[kChunk], stage_i[kChunk];  // at-risk slots and their staging rows
+  int stage_s[kChunk];                   // at-risk slots, in staging order
   int blk_l[kChunk / kBlock];            // block ids of the chunk's logical blocks
   int wave_tot[kThreads / kWave];
   int r0s[kThreads / kWave], r1s[kThreads / kWave];
-  int s_err, s_nstage;
+  int s_err, s_nstage, s_base;
 };
 
 // Exclusive prefix sum over a 256-thread workgroup.
@@ -119,21 +130,49 @@ __device__ bool settle_trivial(const CompactArgs &P, int u, int c, int n, int m)
     hi[3] = 0;
     hi[4] = 0;
     hi[5] = 0;
+    hi[6] = 0;
   }
   return true;
 }
 
+// A chunk's arrival (thread 0): its counts go into the head's 64-bit word
+// (bits 0-10 chunks, 11-21 chunks with errors, 22-42 rows moved, 43-63 rows
+// staged; each at most 2^20 per head).  The staged count before it is the
+// chunk's first staging row.  The chunk that arrives last has the totals: it
+// records the head's error state, freed blocks, counts and whether the head
+// moves in rank order (more at-risk rows than stage_rows), and clears the
+// word for the next call.  s_err must be final (its writes precede a
+// barrier).
+__device__ void arrive(const CompactArgs &P, int u, int n, int m, int moved, int staged,
+                       PrepLds &S) {
+  const unsigned long long mine = 1ull | ((unsigned long long)(S.s_err ? 1 : 0) << 11) |
+                                  ((unsigned long long)moved << 22) |
+                                  ((unsigned long long)staged << 43);
+  const unsigned long long old = atomicAdd(&P.head_acc[u], mine);
+  S.s_base = (int)(old >> 43);
+  if ((old & 2047ull) != (unsigned long long)(P.chunks - 1)) return;
+  const unsigned long long tot = old + mine;
+  const int err = ((tot >> 11) & 2047ull) ? 1 : 0;
+  int32_t *hi = P.head_info + (size_t)u * 8;
+  hi[2] = err;
+  hi[3] = err ? 0 : blocks_of(n) - blocks_of(n - m);
+  hi[4] = (int)((tot >> 22) & 0x1fffffull);
+  hi[5] = (int)(tot >> 43);
+  hi[6] = (int)(tot >> 43) > P.stage_rows ? 1 : 0;
+  atomicExch(&P.head_acc[u], 0ull);  // state for the next call
+}
+
 // Ranks the kept slots of the chunk [s0, s1) (thread t owns the slots
-// s0 + 4t .. s0 + 4t + 3), records their sources and new pos / score, copies
-// the at-risk rows to the workspace and returns the chunk's moved / staged
-// counts.  j0: victims of the head before s0.  With victims_out, also writes
+// s0 + 4t .. s0 + 4t + 3), records their sources and new pos / score, makes
+// the chunk's arrival and copies the at-risk rows to the workspace when they
+// fit.  j0: victims of the head before s0.  With victims_out, also writes
 // the chunk's victims at their list positions.  The at-risk list is built
 // first, so the staging loads are in flight while the rank records are
 // stored.
-__device__ void rank_and_stage(const CompactArgs &P, int u, int s0, int s1, int n2, int m, int j0,
+__device__ void rank_and_stage(const CompactArgs &P, int u, int s0, int s1, int n, int m, int j0,
                                const bool (&vic)[kPerThread], const int (&posv)[kPerThread],
-                               const float (&scv)[kPerThread], int32_t *victims_out, PrepLds &S,
-                               int &moved, int &staged) {
+                               const float (&scv)[kPerThread], int32_t *victims_out, PrepLds &S) {
+  const int n2 = n - m;
   const int tid = threadIdx.x;
   const size_t urow = (size_t)u * P.max_slots;
   int kept = 0;
@@ -147,7 +186,7 @@ __device__ void rank_and_stage(const CompactArgs &P, int u, int s0, int s1, int 
   // of each victim; at-risk slots to the staging list
   int r = (s0 - j0) + excl;  // kept slots before s0, plus those before mine in the chunk
   int jv = j0 + (min(tid * kPerThread, max(0, s1 - s0)) - excl);  // victims before mine
-  int rq[kPerThread], srcq[kPerThread], jq[kPerThread];
+  int rq[kPerThread], srcq[kPerThread], rowq[kPerThread], jq[kPerThread];
   int my_err = 0, my_moved = 0, my_staged = 0;
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
@@ -155,6 +194,7 @@ __device__ void rank_and_stage(const CompactArgs &P, int u, int s0, int s1, int 
     rq[q] = -1;
     jq[q] = -1;
     srcq[q] = -1;
+    rowq[q] = -1;
     if (s >= s1) continue;
     if (vic[q]) {
       if (jv >= 0 && jv < m) jq[q] = jv;
@@ -163,35 +203,38 @@ __device__ void rank_and_stage(const CompactArgs &P, int u, int s0, int s1, int 
       continue;
     }
     if (r < 0 || r >= n2) { my_err = 1; ++r; continue; }
+    const int blk = S.blk_l[(s - s0) / kBlock];
+    const int row = (blk >= 0 && blk < P.num_blocks) ? blk * kBlock + s % kBlock : 0;
     int src;
     if (r == s) {
       src = -1;                       // stays in place
-    } else if (s < n2) {              // at risk: staged (at row r) before the gather
-      src = -2 - r;
-      ++my_staged;
+    } else if (s < n2) {              // at risk: staged before the gather (local index)
       const int k = atomicAdd(&S.s_nstage, 1);
+      src = -2 - k;
+      ++my_staged;
       S.stage_s[k] = s;
-      S.stage_i[k] = r;
     } else {                          // slots >= n' are never written: read in place
-      const int blk = S.blk_l[(s - s0) / kBlock];
-      src = (blk >= 0 && blk < P.num_blocks) ? blk * kBlock + s % kBlock : 0;
+      src = row;
     }
     my_moved += src != -1 ? 1 : 0;
     rq[q] = r;
     srcq[q] = src;
+    rowq[q] = src != -1 ? row : -1;
     ++r;
   }
   if (my_err) atomicOr(&S.s_err, 1);
   block_sum2(my_moved, my_staged, S);  // barriers: the list and s_err are complete
-  moved = my_moved;
-  staged = my_staged;
+  if (tid == 0) arrive(P, u, n, m, my_moved, my_staged, S);
+  __syncthreads();
+  const int sbase = S.s_base;  // the chunk's first staging row
+  const bool fits = sbase + S.s_nstage <= P.stage_rows;
 
   // staging copy of the at-risk K and V rows in 16-byte pieces, four K and
   // four V pieces per thread and round: indices past the end repeat the last
   // piece (the same bytes again), a block id outside the pool (flagged
   // above) reads block 0, so loads and stores need no branches
   const int pshift = __ffs(P.row_bytes / 16) - 1;  // 16-byte pieces per row: 8, 16 or 32
-  const int total = S.s_nstage << pshift;
+  const int total = fits ? S.s_nstage << pshift : 0;  // else the head moves in rank order
   uint4 kv[4], vv[4];
   size_t dst[4];
   auto stage_load = [&](int base) {
@@ -203,7 +246,7 @@ __device__ void rank_and_stage(const CompactArgs &P, int u, int s0, int s1, int 
       int blk = S.blk_l[(s - s0) / kBlock];
       blk = (blk >= 0 && blk < P.num_blocks) ? blk : 0;
       const size_t src = ((size_t)blk * kBlock + s % kBlock) * P.row_bytes + (size_t)part * 16;
-      dst[q] = ((size_t)u * P.stage_rows + S.stage_i[k]) * P.row_bytes + (size_t)part * 16;
+      dst[q] = ((size_t)u * P.stage_rows + sbase + k) * P.row_bytes + (size_t)part * 16;
       kv[q] = ld16(P.k_pool + src);
       vv[q] = ld16(P.v_pool + src);
     }
@@ -222,7 +265,8 @@ __device__ void rank_and_stage(const CompactArgs &P, int u, int s0, int s1, int 
     const int s = s0 + tid * kPerThread + q;
     if (victims_out && jq[q] >= 0) victims_out[urow + jq[q]] = s;
     if (rq[q] >= 0) {
-      P.src_of[urow + rq[q]] = srcq[q];
+      P.src_of[urow + rq[q]] = srcq[q] <= -2 ? -2 - (sbase + (-2 - srcq[q])) : srcq[q];
+      P.src_row[urow + rq[q]] = rowq[q];
       P.new_pos[urow + rq[q]] = posv[q];
       if (P.score) P.new_score[urow + rq[q]] = scv[q];
     }
@@ -232,32 +276,6 @@ __device__ void rank_and_stage(const CompactArgs &P, int u, int s0, int s1, int 
     stage_load(base);
     stage_store();
   }
-}
-
-// Every chunk of a head with victims arrives here with one 64-bit atomic
-// add: bits 0-10 count the chunks, 11-21 the chunks with errors, 22-42 the
-// rows moved and 43-63 the rows staged (each at most 2^20 per head).  The
-// chunk that arrives last has the totals in the returned value: it records
-// the head's error state, freed blocks and counts, and clears the word.
-__device__ void prep_finish(const CompactArgs &P, int u, int n, int m, int moved, int staged,
-                            PrepLds &S) {
-  // s_err is final: its last writes precede a barrier (rank_and_stage's
-  // sums, or the sample counts of the victim-list form); no barrier here, so
-  // no wait for the staging stores
-  if (threadIdx.x != 0) return;
-  const unsigned long long mine = 1ull | ((unsigned long long)(S.s_err ? 1 : 0) << 11) |
-                                  ((unsigned long long)moved << 22) |
-                                  ((unsigned long long)staged << 43);
-  const unsigned long long old = atomicAdd(&P.head_acc[u], mine);
-  if ((old & 2047ull) != (unsigned long long)(P.chunks - 1)) return;
-  const unsigned long long tot = old + mine;
-  const int err = ((tot >> 11) & 2047ull) ? 1 : 0;
-  int32_t *hi = P.head_info + (size_t)u * 8;
-  hi[2] = err;
-  hi[3] = err ? 0 : blocks_of(n) - blocks_of(n - m);
-  hi[4] = (int)((tot >> 22) & 0x1fffffull);
-  hi[5] = (int)(tot >> 43);
-  atomicExch(&P.head_acc[u], 0ull);  // state for the next call
 }
 
 __device__ void prep_common_start(const CompactArgs &P, int u, int c) {
@@ -316,7 +334,6 @@ __global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArg
   }
   const bool live_chunk = s0 < n;
   const int s1 = live_chunk ? min(s0 + kChunk, n) : s0;
-  int moved = 0, staged = 0;
   int posv[kPerThread];
   float scv[kPerThread];
 #pragma unroll
@@ -387,21 +404,27 @@ __global__ __launch_bounds__(kThreads) void compact_prep_kernel(const CompactArg
       const int s = s0 + tid * kPerThread + q;
       vf[q] = s < s1 && flag[s - s0];
     }
-    rank_and_stage(P, u, s0, s1, n - m, m, j0, vf, posv, scv, nullptr, S, moved, staged);
+    rank_and_stage(P, u, s0, s1, n, m, j0, vf, posv, scv, nullptr, S);
+  } else if (tid == 0) {
+    // a chunk past the head's length arrives with nothing (s_err is final:
+    // its writes precede the sample counts' barrier)
+    arrive(P, u, n, m, 0, 0, S);
   }
-  prep_finish(P, u, n, m, moved, staged, S);
 }
 
 // Persistent grid over (head, row range) items.  A prefix pass reads each
 // head's record once and keeps in LDS the item and free-list offsets of every
 // head.  Item 0 of a head records its stats and seq_len; every item appends
 // its share of the head's freed blocks and moves up to rows_per_item rows.
+// A head that moves in rank order is one item that moves no rows (the
+// in-order kernel after this one moves them).
 __global__ __launch_bounds__(kThreads) void compact_gather_kernel(const CompactArgs P) {
   extern __shared__ int gsm[];
   const int U = P.units, RC = P.rows_per_item;
   int *item_start = gsm;            // [U + 1]
   int *free_start = gsm + U + 1;    // [U + 1]
   int *n2_l = gsm + 2 * (U + 1);    // [U]: rows kept, -1 = the head does not move
+  int *seq_l = gsm + 3 * U + 2;     // [U]: 1 = the head moves in rank order
   __shared__ int wave_tot[kThreads / kWave];
   __shared__ int s_tot[2];
   const int tid = threadIdx.x;
@@ -415,8 +438,10 @@ __global__ __launch_bounds__(kThreads) void compact_gather_kernel(const CompactA
       const int n = hi[0], m = hi[1], err = hi[2];
       fr = head_freed(P, n, m, err);
       const bool moves = !err && n >= 0 && n <= P.max_slots && m > 0 && m <= n;
-      cnt = moves ? max(1, (n - m + RC - 1) / RC) : 1;
+      const bool seq = moves && hi[6] != 0;
+      cnt = moves && !seq ? max(1, (n - m + RC - 1) / RC) : 1;
       n2_l[u] = moves ? n - m : -1;
+      seq_l[u] = seq ? 1 : 0;
     }
     const int ex_i = block_exclusive_scan(cnt, wave_tot);
     const int ex_f = block_exclusive_scan(fr, wave_tot);
@@ -452,9 +477,10 @@ __global__ __launch_bounds__(kThreads) void compact_gather_kernel(const CompactA
     const int u = lo, k = item - item_start[u];
     const int nitems = item_start[u + 1] - item_start[u];
     const int n2 = n2_l[u];
+    const bool seq = seq_l[u] != 0;
     const int fr = room ? free_start[u + 1] - free_start[u] : 0;  // > 0 only if the head moves
     const int r0 = k * RC;
-    const bool rows = n2 > 0 && r0 < n2;
+    const bool rows = !seq && n2 > 0 && r0 < n2;
     const int r1 = rows ? min(r0 + RC, n2) : 0;
     // this item's share of the head's emptied tail blocks [lb0, lb0 + fr)
     const int f0 = fr > 0 ? (int)((long long)fr * k / nitems) : 0;
@@ -575,13 +601,70 @@ __global__ __launch_bounds__(kThreads) void compact_gather_kernel(const CompactA
   }
 }
 
+// The heads that move in rank order (more at-risk rows than the staging
+// holds), one 1024-thread workgroup each, after the gather: ascending rounds
+// of destination ranks, every load of a round returned before any of its
+// stores.  A source never lies below its destination, so no round reads a
+// slot that an earlier round wrote, and within a round the loads precede the
+// stores.  Other heads return at once.
+__global__ __launch_bounds__(kSeqThreads) void compact_inorder_kernel(const CompactArgs P) {
+  const int u = blockIdx.x, tid = threadIdx.x;
+  const int32_t *hi = P.head_info + (size_t)u * 8;
+  const int n = hi[0], m = hi[1], err = hi[2], seq = hi[6];
+  if (!seq || err || n < 0 || n > P.max_slots || m <= 0 || m > n) return;
+  const int n2 = n - m;
+  const int32_t *bt = P.block_table + (size_t)u * P.max_blocks;
+  const size_t urow = (size_t)u * P.max_slots;
+  const int pshift = __ffs(P.row_bytes / 16) - 1;  // 16-byte pieces per row: 8, 16 or 32
+  const int rpr = kSeqThreads >> pshift;           // rows per step of a round
+  const int part = tid & ((1 << pshift) - 1);
+  const int pool_rows = P.num_blocks * kBlock;
+  for (int rb = 0; rb < n2; rb += kSeqRows * rpr) {
+    // the round's destinations (past the head: its last row again, the
+    // same bytes), their sources' pool rows (-1: the row stays), blocks,
+    // new pos and score
+    int rq[kSeqRows], srow[kSeqRows], db[kSeqRows], npos[kSeqRows];
+    float nsc[kSeqRows];
+#pragma unroll
+    for (int i = 0; i < kSeqRows; ++i) {
+      rq[i] = min(rb + i * rpr + (tid >> pshift), n2 - 1);
+      srow[i] = P.src_row[urow + rq[i]];
+      db[i] = bt[rq[i] / kBlock];
+      npos[i] = P.new_pos[urow + rq[i]];
+      nsc[i] = P.score ? P.new_score[urow + rq[i]] : 0.f;
+    }
+    size_t dsto[kSeqRows];
+    uint4 kv[kSeqRows], vv[kSeqRows];
+#pragma unroll
+    for (int i = 0; i < kSeqRows; ++i) {
+      dsto[i] = ((size_t)db[i] * kBlock + rq[i] % kBlock) * P.row_bytes + ((size_t)part << 4);
+      const bool pooled = srow[i] >= 0 && srow[i] < pool_rows;
+      const size_t so = pooled ? (size_t)srow[i] * P.row_bytes + ((size_t)part << 4) : dsto[i];
+      kv[i] = ld16(P.k_pool + so);
+      vv[i] = ld16(P.v_pool + so);
+    }
+    // every load of the round has returned before any thread stores
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kSeqRows; ++i) {
+      st16_nt(P.k_pool + dsto[i], kv[i]);
+      st16_nt(P.v_pool + dsto[i], vv[i]);
+      P.pos[urow + rq[i]] = npos[i];
+      if (P.score) P.score[urow + rq[i]] = nsc[i];
+    }
+  }
+}
+
 static hipError_t launch_gather(const CompactArgs &a, hipStream_t s) {
   // enough workgroups to cover every item of a full cache, capped
   // kept rows per head are at most rows_cap (the fused path: the budget)
   const long long items =
       (long long)a.units * std::max(1, (a.rows_cap + a.rows_per_item - 1) / a.rows_per_item);
   const int grid = (int)(items < 2048 ? (items > 0 ? items : 1) : 2048);
-  const size_t lds = sizeof(int) * (3 * (size_t)a.units + 2);  // item / free offsets, rows kept
+  const size_t lds = sizeof(int) * (4 * (size_t)a.units + 2);  // item / free offsets, rows kept, order
   hipLaunchKernelGGL(compact_gather_kernel, dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
@@ -590,7 +673,10 @@ hipError_t launch_compact(const CompactArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(compact_prep_kernel, dim3(a.chunks, a.units), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_gather(a, s);
+  e = launch_gather(a, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(compact_inorder_kernel, dim3(a.units), dim3(kSeqThreads), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace kvev

@@ -74,10 +74,12 @@ struct CompactArgs {
   int64_t *stats;
   // workspace regions
   int32_t *src_of;              // [units][max_slots]: source of each destination rank
+  int32_t *src_row;             // [units][max_slots]: pool row of each moved rank's source (-1: stays)
   int32_t *new_pos;             // [units][max_slots]: pos of each kept rank
   float *new_score;             // [units][max_slots]: score of each kept rank
   uint8_t *stage_k, *stage_v;   // [units][stage_rows][row_bytes]: at-risk rows
-  int32_t *head_info;           // [units][8]: n, m, error, blocks freed, rows moved, staged
+  int32_t *head_info;           // [units][8]: n, m, error, blocks freed, rows moved, staged,
+                                // in order (more at-risk rows than stage_rows)
   unsigned long long *head_acc; // [units] persistent state (zero between calls): prep
                                 // chunks done, chunks with errors, rows moved, staged
   int32_t *fc0;                 // free_count before the call
@@ -245,6 +247,7 @@ constexpr int kSelectMaxChunks = 1024;  // chunks per head: up to 1M slots
 constexpr int kHistChunk = 4096;        // slots per select histogram workgroup
 constexpr int kCompactMaxUnits = 4096;  // compact.hip gather limit
 constexpr int kCompactChunk = 1024;     // compact.hip prep chunk (slots)
+constexpr int kCompactStageRows = 4096; // compact.hip: at-risk rows staged per head at most
 // Prep packs a head's chunk arrivals into 11 bits.
 static_assert(kSelectMaxChunks * kSelectChunk / kCompactChunk < 2048,
               "chunk arrivals are counted in 11 bits");

@@ -247,6 +247,24 @@ def test_compact_bit_exact_on_oracle_victims(pattern, dtype, D):
     _assert_compaction_equal(case, new, ofl, ofc, ostats, g)
 
 
+@pytest.mark.parametrize("pattern,dtype,D", [("first_only", "bf16", 128), ("random", "bf16", 128),
+                                             ("every_other", "bf16", 128), ("tail", "bf16", 128),
+                                             ("first_only", "f32", 64)])
+def test_compact_beyond_the_staging_cap(pattern, dtype, D):
+    """Heads with more than 4096 at-risk rows (20000 tokens: evicting slot 0
+    shifts 19999 rows, half evicted leaves about 5000) move in rank order
+    without staging; in the same call shorter heads (8000 and 12000 tokens
+    with half evicted: 2000-3000 at-risk rows; 17 and 0 tokens) stage theirs.
+    Bit-exact against the oracle."""
+    cfg = synth.CONFIGS["snapkv_prefill_32k"].scaled(B=2, Hkv=3, L=20000, D=D, dtype=dtype)
+    seq = np.array([[20000, 19999, 8000], [17, 12000, 0]], np.int32)
+    case = synth.make_case(cfg, seq_len=seq, spare_blocks=5)
+    vic, nv = _pattern_victims(case["seq_len"], case["max_blocks"] * 16, pattern)
+    new, ofl, ofc, ostats, g = _compact_both(case, vic, nv, with_score=(D == 128))
+    _assert_compaction_equal(case, new, ofl, ofc, ostats, g)
+    assert ostats[3] > 4096 or pattern == "tail"
+
+
 def test_compact_rejects_unsorted_victims_and_leaves_cache():
     """Victims not strictly ascending: the head is left unchanged and a status
     bit is set; the other heads are compacted."""
