@@ -352,10 +352,15 @@ def main():
                      "algorithmic_bytes": score_bytes, "launch_ms": t_score_alone},
         # the compaction call (prep + gather) of the separate-call passes: where
         # many kept rows move, it outlasts the scoring
-        "compact_roofline": {"call": "kvev_compact (prep + gather)", "bound": "hbm",
+        "compact_roofline": {"call": "kvev_compact (prep + gather + in-order)", "bound": "hbm",
                              "achieved": compact_bytes / (t_compact / 1e3) / 1e9,
                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": compact_bytes / (t_compact / 1e3) / 1e9 / HBM_PEAK_GBS,
+                             "traffic": read_traffic(
+                                 args.workload,
+                                 os.path.join(ROOT, "kv_cache_eviction_qk_amd", "csrc",
+                                              "compact.hip"),
+                                 kernel="compact", sha_key="source_sha256_16"),
                              "algorithmic_bytes": compact_bytes, "call_ms": t_compact},
         "cpu_baseline": cpu,
     }
