@@ -100,6 +100,7 @@ struct FinLds {
   int32_t sblk[kBatchRanks];         // source block id of each rank (-1: stays)
   int32_t dblk[kBatchRanks / kBlock];  // destination block ids of the batch
   int32_t wtot[kFW];                 // scan scratch
+  int32_t rtot[kFW];                 // rank_bin_all's scan scratch
   RankOut r;
   uint32_t ticket, nsub, nt, cut, nown, mbase;
   int32_t moved, at_risk, last;
@@ -147,6 +148,58 @@ __device__ int block_scan(int v, int *wtot, int *total) {
   return before + incl - v;
 }
 
+// The bin holding the rank-th smallest key (1-based) of a histogram of NBINS
+// bins, and the count below it, by the whole workgroup: PER bins a thread,
+// a wave scan, the waves' totals through LDS.  out = {0, 0} when no bin holds
+// it (rank 0 or above the total).  Ends with a barrier.
+template <int NBINS>
+__device__ void rank_bin_all(const uint32_t *h, uint32_t rank, RankOut *out, int *wtot) {
+  constexpr int PER = NBINS >= kFT ? NBINS / kFT : 1;
+  static_assert(PER == 1 || PER == 2, "one or two bins a thread");
+  // (used for the 2048-bin steps; the smaller ones stay on one wave, which
+  // keeps the kernel within its registers)
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
+  const bool act = tid * PER < NBINS;
+  uint32_t x[PER], mine = 0;
+  if constexpr (PER == 2) {
+    const uint2 v = act ? *reinterpret_cast<const uint2 *>(h + 2 * tid) : make_uint2(0u, 0u);
+    x[0] = v.x;
+    x[1] = v.y;
+  } else {
+    x[0] = act ? h[tid] : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) mine += x[i];
+  uint32_t incl = wave_incl_scan(mine);
+  if (lane == kWave - 1) wtot[wv] = (int)incl;
+  __syncthreads();
+  uint32_t before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kFW; ++w) {
+    const uint32_t t = (uint32_t)wtot[w];
+    before += w < wv ? t : 0u;
+    total += t;
+  }
+  incl += before;
+  const uint32_t excl = incl - mine;
+  if (act && excl < rank && rank <= incl) {
+    uint32_t acc = excl, bin = (uint32_t)(tid * PER + PER - 1);
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (!found && acc + x[i] >= rank) {
+        bin = (uint32_t)(tid * PER + i);
+        found = true;
+      }
+      if (!found) acc += x[i];
+    }
+    out->bin = bin;
+    out->below = acc;
+  }
+  if (tid == 0 && !(rank > 0 && rank <= total)) *out = RankOut{0, 0};
+  __syncthreads();
+}
+
 // The (head, part) of a ticket.  With the heads a multiple of 8, ticket t
 // goes to head 8 * ((t / 8) / kh) + t % 8, part (t / 8) % kh: when tickets
 // follow dispatch order, which deals workgroups to the 8 XCDs round robin,
@@ -184,15 +237,24 @@ __device__ void wait_count(const uint32_t *p, uint32_t want, unsigned long long 
 struct Prefix {
   long long b, t;
 };
-__device__ Prefix freed_prefix_load(const FinishArgs &P, int u) {
+__device__ __forceinline__ int head_freed(const FinishArgs &P, int n, int e) {
+  if (n < 0 || n > P.max_slots || e != 0) return 0;
+  const int m = max(0, n - P.budget);
+  return m > 0 ? blocks_of(n) - blocks_of(n - m) : 0;
+}
+// pn, pe: the length and error flag of head threadIdx.x, loaded earlier
+// when there are at most kFT heads (one head a thread), else ignored.
+__device__ Prefix freed_prefix_load(const FinishArgs &P, int u, int pn, int pe) {
   Prefix x{0, 0};
+  if (P.units <= kFT) {
+    const int i = threadIdx.x;
+    const int fr = i < P.units ? head_freed(P, pn, pe) : 0;
+    x.t = fr;
+    x.b = i < u ? fr : 0;
+    return x;
+  }
   for (int i = threadIdx.x; i < P.units; i += kFT) {
-    const int n = P.seq_len[i];
-    int fr = 0;
-    if (n >= 0 && n <= P.max_slots && P.head_err[i] == 0) {
-      const int m = max(0, n - P.budget);
-      if (m > 0) fr = blocks_of(n) - blocks_of(n - m);
-    }
+    const int fr = head_freed(P, P.seq_len[i], P.head_err[i]);
     x.t += fr;
     x.b += i < u ? fr : 0;
   }
@@ -217,7 +279,10 @@ __device__ void freed_prefix(Prefix x, FinLds &L, int &before, int &total) {
   total = (int)L.pre_tot[1];
 }
 
-template <int PR>  // 16-byte pieces of one K (or V) row: 8, 16 or 32
+// PR: 16-byte pieces of one K (or V) row (8, 16 or 32); SPEC: every head
+// fits the local selection (PR <= 16 and max_slots <= kRes * kGrp), so a
+// workgroup's head and part come from its index.
+template <int PR, bool SPEC>
 __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
   extern __shared__ __align__(16) uint8_t smem[];
   FinLds &L = *reinterpret_cast<FinLds *>(smem);
@@ -227,23 +292,33 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
   // allows): the histogram and all keys of the head this workgroup's index
   // maps to are loaded before the ticket returns, and kept when the ticket
   // names the same head (the usual case), else loaded again.
-  const bool spec = PR <= 16 && P.max_slots <= kRes * kGrp;
+  constexpr bool spec = SPEC;
   uint32_t kr[kRes][4];
   uint32_t hv[kSelectBins / kFT];
   auto load_head = [&](int uh) {
+    // the histogram first: the first rank step needs only it, and loads
+    // complete in order, so the keys stream in behind that step
+    const uint32_t *hgh = P.hist + (size_t)uh * kSelectBins;
+#pragma unroll
+    for (int q = 0; q < kSelectBins / kFT; ++q) hv[q] = hgh[tid + q * kFT];
+    // the raw score bits (turned into keys by keys_from_raw before their
+    // first use, so that all the loads go out at once)
     const float *sch = P.sc + (size_t)uh * P.max_slots;
 #pragma unroll
     for (int q = 0; q < kRes; ++q) {
       const int s = min(q * kGrp + 4 * tid, P.max_slots - 4);
-      const float4 v = *reinterpret_cast<const float4 *>(sch + s);
-      kr[q][0] = score_key(v.x);
-      kr[q][1] = score_key(v.y);
-      kr[q][2] = score_key(v.z);
-      kr[q][3] = score_key(v.w);
+      const uint4 v = *reinterpret_cast<const uint4 *>(sch + s);
+      kr[q][0] = v.x;
+      kr[q][1] = v.y;
+      kr[q][2] = v.z;
+      kr[q][3] = v.w;
     }
-    const uint32_t *hgh = P.hist + (size_t)uh * kSelectBins;
+  };
+  auto keys_from_raw = [&]() {
 #pragma unroll
-    for (int q = 0; q < kSelectBins / kFT; ++q) hv[q] = hgh[tid + q * kFT];
+    for (int q = 0; q < kRes; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kr[q][e] = score_key(__uint_as_float(kr[q][e]));
   };
   // Heads of at most kRes groups (every head, when max_slots allows) are
   // selected locally with no wait before the compaction: a workgroup's head
@@ -256,25 +331,33 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
   if (spec) {
     ticket = (int)blockIdx.x;
     ticket_head(ticket, P.units, P.kh, u, k);
-    load_head(u);
   } else {
     if (tid == 0) L.ticket = atomicAdd(&P.ctr[0], 1u);
     __syncthreads();
     ticket = (int)L.ticket;
     ticket_head(ticket, P.units, P.kh, u, k);
   }
+  // the small loads first (loads complete in order: waiting for the length
+  // must not wait for the keys), then the head's histogram and keys
   const size_t urow = (size_t)u * P.max_slots;
   const int n = P.seq_len[u];
+  const int herr = P.head_err[u];
+  // every head's length and error flag, for the free-list prefix at the end
+  // (one head a thread when there are at most kFT; used only then)
+  const int pi = min(tid, P.units - 1);
+  const int pn = P.seq_len[pi];
+  const int pe = P.head_err[pi];
+  if (spec) load_head(u);
+  // nothing that waits for a load moves above the last of them
+  __builtin_amdgcn_sched_barrier(0);
   const bool consistent = n >= 0 && n <= P.max_slots;
   const int m = consistent ? max(0, n - P.budget) : 0;
   const int nc = consistent ? max(0, n - P.recent) : 0;
   const int n2 = n - m;
-  const bool bad = consistent && P.head_err[u] != 0;
+  const bool bad = consistent && herr != 0;
   const float *sc = P.sc + urow;
   float *so = P.score_out + urow;
   unsigned long long *acc = P.acc;
-  // the head's free-list offset and the total, for the head's last workgroup
-  const Prefix pfx = freed_prefix_load(P, u);
 
   if (!consistent) {
     if (k == 0 && tid == 0) {
@@ -359,12 +442,13 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
       L.at_risk = 0;
     }
     __syncthreads();
-    wg_rank_bin<kSelectBins>(L.h, (uint32_t)m, &L.r);
+    rank_bin_all<kSelectBins>(L.h, (uint32_t)m, &L.r, L.rtot);
     const uint32_t bkt = L.r.bin;
     const uint32_t need = (uint32_t)m - L.r.below;  // rank inside the bucket
     uint32_t pre, need2;
     int nmem = 0;
     uint2 *gmem = P.mem + urow;
+    if (spec) keys_from_raw();  // the loads went out before the first rank step
     if (local) {
       // ---- the whole head: keys below the bucket per chunk (a wave covers
       // 256 slots of a group: chunk = 4 g + wave / 4) and the histogram of
@@ -387,7 +471,7 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
       }
       for (int i = tid; i < 1024; i += kFT) L.h[i] = 0;
       __syncthreads();
-      wg_rank_bin<kSelectBins>(L.h2, need, &L.r);
+      rank_bin_all<kSelectBins>(L.h2, need, &L.r, L.rtot);
       pre = (bkt << 11) | L.r.bin;  // key >> 10 of T
       need2 = need - L.r.below;
       // the bucket's members below the sub-bucket are victims (per chunk);
@@ -490,7 +574,7 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
       for (int q = 0; q < kSelectBins / kFT; ++q) L.h2[tid + q * kFT] = hv[q];
       for (int i = tid; i < 1024; i += kFT) L.h[i] = 0;
       __syncthreads();
-      wg_rank_bin<kSelectBins>(L.h2, need, &L.r);
+      rank_bin_all<kSelectBins>(L.h2, need, &L.r, L.rtot);
       pre = (bkt << 11) | L.r.bin;  // key >> 10 of T
       need2 = need - L.r.below;
       // every member: those below the sub-bucket are victims (per chunk); the
@@ -824,7 +908,8 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
   if (tid == 0) L.last = atomicAdd(&P.head_done[u], 1u) == (uint32_t)(P.kh - 1) ? 1 : 0;
   __syncthreads();
   int before, total;
-  freed_prefix(pfx, L, before, total);
+  // the head's free-list offset and the total, for the head's last workgroup
+  freed_prefix(freed_prefix_load(P, u, pn, pe), L, before, total);
   const int fc0 = *P.free_count;
   const bool room = fc0 >= 0 && (long long)fc0 + total <= (long long)P.free_capacity;
   if (L.last) {
@@ -903,10 +988,17 @@ int finish_parts(int units, int rows_cap) {
 hipError_t launch_finish(const FinishArgs &a, hipStream_t s) {
   const size_t lds = sizeof(FinLds);
   const dim3 grid((unsigned)(a.units * a.kh));
+  const bool spec = a.max_slots <= kRes * kGrp;  // with PR <= 16
   switch (a.row_bytes / 16) {
-    case 8: hipLaunchKernelGGL(evict_finish_kernel<8>, grid, dim3(kFT), lds, s, a); break;
-    case 16: hipLaunchKernelGGL(evict_finish_kernel<16>, grid, dim3(kFT), lds, s, a); break;
-    case 32: hipLaunchKernelGGL(evict_finish_kernel<32>, grid, dim3(kFT), lds, s, a); break;
+    case 8:
+      if (spec) hipLaunchKernelGGL((evict_finish_kernel<8, true>), grid, dim3(kFT), lds, s, a);
+      else hipLaunchKernelGGL((evict_finish_kernel<8, false>), grid, dim3(kFT), lds, s, a);
+      break;
+    case 16:
+      if (spec) hipLaunchKernelGGL((evict_finish_kernel<16, true>), grid, dim3(kFT), lds, s, a);
+      else hipLaunchKernelGGL((evict_finish_kernel<16, false>), grid, dim3(kFT), lds, s, a);
+      break;
+    case 32: hipLaunchKernelGGL((evict_finish_kernel<32, false>), grid, dim3(kFT), lds, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
