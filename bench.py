@@ -10,7 +10,8 @@ vtok_reclaim_64k times vToken's liveness marks and lazy reclamation of one
 64000-token layer; --workload snap_ring_870 times SnapKV's decode-time ring
 buffer step; --workload h2o_decode_4k times H2O's decode-time accumulation:
 256 steps of accumulated scoring over a growing 4096-token cache, then one
-selection and compaction to the budget.)
+selection and compaction to the budget.  --hbm-probe measures the plain HBM
+read rate of the GPU with the probe library instead.)
 
 A step is the whole eviction path for one layer's cache: scoring (SnapKV
 window sum + max-pool over the last W prompt queries), selection (budget,
@@ -56,6 +57,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", action="store_true",
                     help="only run the timed steps (for rocprofv3 runs)")
+    ap.add_argument("--hbm-probe", action="store_true",
+                    help="measure the plain HBM read rate instead (libkvev_probe.so over a "
+                         "1 GiB buffer: contiguous, 4 KiB blocks in order, 4 KiB blocks "
+                         "through a shuffled list), one JSON line (not the benchmark's metric)")
     ap.add_argument("--window-attn", action="store_true",
                     help="time the window forward helper (kvev_window_attn: LSE, and the "
                          "output for DropKV) on the workload's cache and window instead, one "
@@ -109,6 +114,8 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.hbm_probe:
+        return bench_hbm_probe(args)
     cfg = synth.CONFIGS[args.workload]
     if args.window_attn:
         return bench_window_attn(args, cfg)
@@ -877,6 +884,72 @@ def _vtok_bytes(U, rows, nsrc, alloc_blocks, row_bytes):
     block id and live count read by the plan (8)."""
     return rows * (4 * row_bytes + 16) + nsrc * (32 + 16 + 12 + 4) + alloc_blocks * 8
 
+
+
+def bench_hbm_probe(args):
+    """Plain read rate of this GPU's HBM: every byte of a 1 GiB buffer read
+    once per launch, for three access shapes and a sweep of loads in flight
+    and grid sizes.  Each launch is timed with HIP events on the stream it
+    runs on, after a 1 GiB read of another buffer has evicted L2 and the
+    Infinity Cache; the median of `reps` launches is reported."""
+    import numpy as np
+    import torch
+
+    from kv_cache_eviction_qk_amd import build as kbuild
+
+    path = kbuild.PROBE_OUT
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run python -m kv_cache_eviction_qk_amd.build")
+    L = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    L.kvev_probe_read.argtypes = [ctypes.c_int, ctypes.c_int, P, ctypes.c_size_t, P,
+                                  ctypes.c_int, P, P]
+    L.kvev_probe_read.restype = ctypes.c_int
+    nbytes = 1 << 30
+    nblk = nbytes // 4096
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")  # xor of the words: 0
+    scrub = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    perm = np.random.default_rng(0).permutation(nblk).astype(np.int32)
+    assert perm.min() == 0 and perm.max() == nblk - 1
+    lists = {"identity": torch.arange(nblk, dtype=torch.int32, device="cuda"),
+             "shuffled": torch.from_numpy(perm).cuda()}
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    reps = max(3, args.steps if args.steps <= 9 else 5)
+    shapes = (("contiguous", 0, None), ("4KiB blocks in order", 1, "identity"),
+              ("4KiB blocks shuffled", 1, "shuffled"))
+    rows, best = [], {}
+    for name, pattern, lst in shapes:
+        lp = lists[lst].data_ptr() if lst else None
+        for depth in (4, 8, 16):
+            for grid in (1024, 2048, 4096, 8192):
+                ts = []
+                for _ in range(reps):
+                    scrub.sum()
+                    torch.cuda.synchronize()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    rc = L.kvev_probe_read(pattern, depth, buf.data_ptr(), nbytes, lp, grid,
+                                           sink.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    if rc != 0:
+                        raise RuntimeError(f"kvev_probe_read returned {rc}")
+                    ts.append(e0.elapsed_time(e1) / 1e3)
+                t = sorted(ts)[len(ts) // 2]
+                gbs = nbytes / t / 1e9
+                rows.append({"shape": name, "depth": depth, "grid": grid, "us": t * 1e6,
+                             "GB/s": round(gbs, 1)})
+                log(f"{name:22s} depth {depth:2d} grid {grid:5d}: {gbs:7.1f} GB/s")
+                if gbs > best.get(name, (0,))[0]:
+                    best[name] = (round(gbs, 1), depth, grid)
+    assert int(sink.item()) == 0
+    print(json.dumps({"metric": "hbm_read_rate", "unit": "GB/s", "bytes_per_launch": nbytes,
+                      "reps": reps, "peak": HBM_PEAK_GBS,
+                      "best": {k: {"GB/s": v[0], "depth": v[1], "grid": v[2],
+                                   "frac_of_peak": round(v[0] / HBM_PEAK_GBS, 3)}
+                               for k, v in best.items()},
+                      "sweep": rows}), flush=True)
 
 def bench_window_attn(args, cfg):
     """kvev_window_attn on the workload's prompt cache (every head at length L)

@@ -3,8 +3,9 @@
     python -m kv_cache_eviction_qk_amd.build          # compile every source
 
 Each .hip source is compiled to an object with hipcc for gfx950 (in
-parallel), then linked into ``kv_cache_eviction_qk_amd/libkvev.so``.  Packed
-FP32 instructions are disabled in device code.
+parallel), then linked into ``kv_cache_eviction_qk_amd/libkvev.so``; the HBM
+read-rate probe (csrc/probe/) is built into ``libkvev_probe.so`` beside it.
+Packed FP32 instructions are disabled in device code.
 """
 from __future__ import annotations
 
@@ -19,6 +20,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libkvev.so")
+# the HBM read-rate probe, a library of its own (only the benchmark's probe mode loads it)
+PROBE_SRC = os.path.join(CSRC, "probe", "hbm_read_probe.hip")
+PROBE_OUT = os.path.join(HERE, "libkvev_probe.so")
 BUILD_DIR = os.path.join(ROOT, "_build", "kvev")
 ARCH = os.environ.get("KVEV_OFFLOAD_ARCH", "gfx950")
 
@@ -62,7 +66,18 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, OUT)
+    build_probe()
     return OUT
+
+
+def build_probe() -> str:
+    tmp = PROBE_OUT + ".tmp"
+    cmd = [_hipcc(), *HIPCC_FLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_OUT)
+    return PROBE_OUT
 
 
 if __name__ == "__main__":

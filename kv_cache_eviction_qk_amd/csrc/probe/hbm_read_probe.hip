@@ -1,0 +1,107 @@
+// hbm_read_probe.hip -- plain HBM read-rate probe (gfx950), the measured
+// read ceiling that the eviction kernels' roofline fractions are read
+// against.  Not part of the eviction path: it lives in its own library,
+// libkvev_probe.so, which only the benchmark's probe mode loads.
+//
+// Every pattern reads each byte of a buffer of nbytes (a multiple of 4096)
+// exactly once with 16-byte vector loads and folds the words into an xor so
+// the loads cannot be dropped; the single store is conditional on a value
+// the buffer's contents never produce, so the kernel moves no bytes to HBM.
+//   pattern 0  contiguous: grid-stride over 16-byte units, DEPTH loads in
+//              flight per lane, consecutive lanes on consecutive units
+//   pattern 1  4 KiB blocks through a block list (the paged cache's access
+//              shape): each wave takes DEPTH/4 list entries per iteration,
+//              one 4 KiB block = four 1 KiB coalesced wave loads
+// With the identity list pattern 1 reads the blocks in address order; with
+// a shuffled list it reads them in the list's order.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+constexpr int kThreads = 256;
+constexpr int kBlockBytes = 4096;
+constexpr int kUnitsPerBlock = kBlockBytes / 16;
+
+template <int DEPTH>
+__global__ __launch_bounds__(kThreads) void hbm_read_contiguous(const uint4 *buf, size_t n16,
+                                                                uint32_t *sink) {
+  const size_t lanes = (size_t)gridDim.x * kThreads;
+  uint32_t acc = 0;
+  for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += lanes * DEPTH) {
+    uint4 v[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const size_t j = i + (size_t)d * lanes;
+      v[d] = j < n16 ? buf[j] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) acc ^= v[d].x ^ v[d].y ^ v[d].z ^ v[d].w;
+  }
+  if (acc == 0xA5A5A5A5u) sink[0] = acc;
+}
+
+template <int DEPTH>
+__global__ __launch_bounds__(kThreads) void hbm_read_blocks(const uint4 *buf, const int32_t *list,
+                                                            int nblk, uint32_t *sink) {
+  constexpr int kPerIter = DEPTH / 4;
+  const int lane = threadIdx.x & 63;
+  const int wave = (blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int waves = (gridDim.x * kThreads) >> 6;
+  uint32_t acc = 0;
+  for (int b0 = wave * kPerIter; b0 < nblk; b0 += waves * kPerIter) {
+    uint4 v[DEPTH];
+#pragma unroll
+    for (int h = 0; h < kPerIter; ++h) {
+      const int e = min(b0 + h, nblk - 1);
+      const uint4 *blk = buf + (size_t)list[e] * kUnitsPerBlock;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[h * 4 + q] = blk[q * 64 + lane];
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) acc ^= v[d].x ^ v[d].y ^ v[d].z ^ v[d].w;
+  }
+  if (acc == 0xA5A5A5A5u) sink[0] = acc;
+}
+
+template <int DEPTH>
+hipError_t launch(int pattern, const void *buf, size_t nbytes, const int32_t *list, int grid,
+                  uint32_t *sink, hipStream_t s) {
+  if (pattern == 0)
+    hipLaunchKernelGGL(hbm_read_contiguous<DEPTH>, dim3(grid), dim3(kThreads), 0, s,
+                       (const uint4 *)buf, nbytes / 16, sink);
+  else
+    hipLaunchKernelGGL(hbm_read_blocks<DEPTH>, dim3(grid), dim3(kThreads), 0, s,
+                       (const uint4 *)buf, list, (int)(nbytes / kBlockBytes), sink);
+  return hipGetLastError();
+}
+}  // namespace
+
+// kvev_probe_read -- one launch of a read pattern over buf.
+//   pattern  0 contiguous, 1 4 KiB blocks through `list`
+//   depth    16-byte loads in flight per lane: 4, 8 or 16
+//   buf      device buffer of nbytes; nbytes a positive multiple of 4096 with
+//            nbytes / 4096 < 2^31
+//   list     pattern 1: device array of nbytes / 4096 block indices, each in
+//            [0, nbytes / 4096) (the caller checks this); unused for pattern 0
+//   grid     workgroups of 256 threads, 1 .. 65536
+//   sink     device word, written only if the xor of the whole buffer equals
+//            0xA5A5A5A5 (the caller fills the buffer so that it does not)
+//   stream   hipStream_t, or null for the null stream
+// Returns 0, or -1 for a bad argument (nothing launched), or the hipError_t of
+// the launch.
+extern "C" int kvev_probe_read(int pattern, int depth, const void *buf, size_t nbytes,
+                               const int32_t *list, int grid, uint32_t *sink, void *stream) {
+  if (pattern < 0 || pattern > 1 || !buf || !sink || nbytes == 0 || nbytes % kBlockBytes ||
+      nbytes / kBlockBytes >= (size_t)INT32_MAX || grid < 1 || grid > 65536 ||
+      (pattern == 1 && !list))
+    return -1;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  switch (depth) {
+    case 4: e = launch<4>(pattern, buf, nbytes, list, grid, sink, s); break;
+    case 8: e = launch<8>(pattern, buf, nbytes, list, grid, sink, s); break;
+    case 16: e = launch<16>(pattern, buf, nbytes, list, grid, sink, s); break;
+    default: return -1;
+  }
+  return (int)e;
+}

@@ -472,3 +472,24 @@ def test_vtok_sync_and_mapping_refusals():
     assert L.kvev_vtok_sync(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, None) == K.EINVAL
     assert L.kvev_vtok_slot_mapping(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20,
                                     None) == K.EINVAL
+
+
+def test_read_probe_library_refuses_bad_arguments():
+    """The HBM read-rate probe (libkvev_probe.so, the benchmark's --hbm-probe
+    mode) is built beside the eviction library and checks its arguments on
+    the host before any launch."""
+    from kv_cache_eviction_qk_amd import build as kbuild
+    if not os.path.exists(kbuild.PROBE_OUT):
+        pytest.skip("libkvev_probe.so not built")
+    L = ctypes.CDLL(kbuild.PROBE_OUT)
+    f = L.kvev_probe_read
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    ok = dict(pattern=1, depth=8, buf=FAKE, nbytes=1 << 20, lst=FAKE, grid=64, sink=FAKE)
+    for bad in (dict(pattern=2), dict(pattern=-1), dict(depth=6), dict(buf=None),
+                dict(nbytes=0), dict(nbytes=4097), dict(nbytes=1 << 43), dict(lst=None),
+                dict(grid=0), dict(grid=65537), dict(sink=None)):
+        a = dict(ok, **bad)
+        assert f(a["pattern"], a["depth"], a["buf"], a["nbytes"], a["lst"], a["grid"], a["sink"],
+                 None) == -1, bad
