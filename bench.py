@@ -61,6 +61,10 @@ def parse():
                     help="measure the plain HBM read rate instead (libkvev_probe.so over a "
                          "1 GiB buffer: contiguous, 4 KiB blocks in order, 4 KiB blocks "
                          "through a shuffled list), one JSON line (not the benchmark's metric)")
+    ap.add_argument("--overlap-probe", action="store_true",
+                    help="measure how much fp32 VALU work overlaps the MFMA units (libkvev_probe.so, "
+                         "one workgroup per CU, two waves per SIMD), one JSON line (not the "
+                         "benchmark's metric)")
     ap.add_argument("--window-attn", action="store_true",
                     help="time the window forward helper (kvev_window_attn: LSE, and the "
                          "output for DropKV) on the workload's cache and window instead, one "
@@ -116,6 +120,8 @@ def main():
     torch.cuda.set_device(0)
     if args.hbm_probe:
         return bench_hbm_probe(args)
+    if args.overlap_probe:
+        return bench_overlap_probe(args)
     cfg = synth.CONFIGS[args.workload]
     if args.window_attn:
         return bench_window_attn(args, cfg)
@@ -950,6 +956,46 @@ def bench_hbm_probe(args):
                                    "frac_of_peak": round(v[0] / HBM_PEAK_GBS, 3)}
                                for k, v in best.items()},
                       "sweep": rows}), flush=True)
+
+def bench_overlap_probe(args):
+    """How much fp32 VALU work overlaps the MFMA units: the probe library's
+    overlap kernel (256 workgroups of 8 waves, one per CU) in six modes, each
+    timed with HIP events on its launch stream (best of 3), reported as ns
+    per iteration of the probe's loop."""
+    import torch
+
+    from kv_cache_eviction_qk_amd import build as kbuild
+
+    path = kbuild.PROBE_OUT
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run python -m kv_cache_eviction_qk_amd.build")
+    L = ctypes.CDLL(path)
+    L.kvev_probe_overlap.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    L.kvev_probe_overlap.restype = ctypes.c_int
+    grid, iters = 256, 20000
+    out = torch.zeros(grid * 512, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    names = ["8 MFMA a wave", "32 FMA a wave", "8 MFMA + 32 FMA, same wave",
+             "8 MFMA on even waves, 32 FMA on odd waves", "16 exp2 + 16 mul a wave",
+             "8 MFMA + 16 exp2 + 16 mul, same wave"]
+    res = {}
+    for mode in range(6):
+        ts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = L.kvev_probe_overlap(mode, grid, iters, out.data_ptr(),
+                                      ctypes.c_void_p(stream.cuda_stream))
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"kvev_probe_overlap returned {rc}")
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        res[names[mode]] = round(min(ts) * 1e9 / iters, 2)
+        log(f"{names[mode]:45s} {res[names[mode]]:8.2f} ns/iteration")
+    print(json.dumps({"metric": "mfma_valu_overlap", "unit": "ns per iteration", "grid": grid,
+                      "threads": 512, "iterations": iters, "modes": res}), flush=True)
 
 def bench_window_attn(args, cfg):
     """kvev_window_attn on the workload's prompt cache (every head at length L)

@@ -1,7 +1,8 @@
-// hbm_read_probe.hip -- plain HBM read-rate probe (gfx950), the measured
-// read ceiling that the eviction kernels' roofline fractions are read
-// against.  Not part of the eviction path: it lives in its own library,
-// libkvev_probe.so, which only the benchmark's probe mode loads.
+// hbm_read_probe.hip -- hardware probes (gfx950) that the eviction kernels'
+// measurements are read against: the plain HBM read rate (the read ceiling
+// of the roofline fractions) and how much vector-ALU work overlaps the matrix
+// cores.  Not part of the eviction path: they live in their own library,
+// libkvev_probe.so, which only the benchmark's probe modes load.
 //
 // Every pattern reads each byte of a buffer of nbytes (a multiple of 4096)
 // exactly once with 16-byte vector loads and folds the words into an xor so
@@ -104,4 +105,81 @@ extern "C" int kvev_probe_read(int pattern, int depth, const void *buf, size_t n
     default: return -1;
   }
   return (int)e;
+}
+
+// ---- MFMA / VALU overlap.  Every thread of a 512-thread workgroup (8 waves,
+// two per SIMD) runs `iters` iterations; per iteration a wave does, by mode:
+//   0  8 v_mfma_f32_16x16x32_bf16 on 8 independent accumulators
+//   1  32 fp32 FMAs on 16 independent chains
+//   2  both of the above in the same wave
+//   3  the MFMAs on even waves, the FMAs on odd waves
+//   4  16 exp2 (with a multiply each) on 16 chains
+//   5  the MFMAs and the exp2 chains in the same wave
+// Each thread writes one float of `out` (grid * 512 floats), its own index.
+namespace {
+typedef float ofloatx4 __attribute__((ext_vector_type(4)));
+typedef short obf16x8 __attribute__((ext_vector_type(8)));
+
+template <int MODE>
+__global__ __launch_bounds__(512) void mfma_valu_overlap(int iters, float seed, float *out) {
+  const int tid = threadIdx.x, wv = tid >> 6;
+  obf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (short)(0x3f80 + (tid & 7) + i);
+    b[i] = (short)(0x3f80 + i);
+  }
+  ofloatx4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = ofloatx4{0.f, 0.f, 0.f, 0.f};
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = seed * (float)(tid + i);
+  const bool do_mfma = MODE == 0 || MODE == 2 || MODE == 5 || (MODE == 3 && (wv & 1) == 0);
+  const bool do_fma = MODE == 1 || MODE == 2 || (MODE == 3 && (wv & 1) == 1);
+  const bool do_exp = MODE == 4 || MODE == 5;
+  for (int it = 0; it < iters; ++it) {
+    if (do_mfma) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[i], 0, 0, 0);
+    }
+    if (do_fma) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = fmaf(v[i], 0.999f, 0.001f);
+    }
+    if (do_exp) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = __builtin_amdgcn_exp2f(v[i]) * 0.5f;
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += v[i];
+  out[(size_t)blockIdx.x * 512 + tid] = s;
+}
+}  // namespace
+
+// kvev_probe_overlap -- one launch of overlap mode `mode` (0..5, above) with
+// `grid` workgroups (1 .. 65536) of 512 threads and `iters` (1 .. 2^24)
+// iterations; out: device array of grid * 512 floats.  Returns 0, -1 for a
+// bad argument (nothing launched), or the hipError_t of the launch.
+extern "C" int kvev_probe_overlap(int mode, int grid, int iters, float *out, void *stream) {
+  if (mode < 0 || mode > 5 || grid < 1 || grid > 65536 || iters < 1 || iters > (1 << 24) || !out)
+    return -1;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 g(grid), t(512);
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(mfma_valu_overlap<0>, g, t, 0, s, iters, 1e-3f, out); break;
+    case 1: hipLaunchKernelGGL(mfma_valu_overlap<1>, g, t, 0, s, iters, 1e-3f, out); break;
+    case 2: hipLaunchKernelGGL(mfma_valu_overlap<2>, g, t, 0, s, iters, 1e-3f, out); break;
+    case 3: hipLaunchKernelGGL(mfma_valu_overlap<3>, g, t, 0, s, iters, 1e-3f, out); break;
+    case 4: hipLaunchKernelGGL(mfma_valu_overlap<4>, g, t, 0, s, iters, 1e-3f, out); break;
+    default: hipLaunchKernelGGL(mfma_valu_overlap<5>, g, t, 0, s, iters, 1e-3f, out); break;
+  }
+  return (int)hipGetLastError();
 }

@@ -493,3 +493,11 @@ def test_read_probe_library_refuses_bad_arguments():
         a = dict(ok, **bad)
         assert f(a["pattern"], a["depth"], a["buf"], a["nbytes"], a["lst"], a["grid"], a["sink"],
                  None) == -1, bad
+    g = L.kvev_probe_overlap
+    g.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    g.restype = ctypes.c_int
+    ok = dict(mode=0, grid=256, iters=100, out=FAKE)
+    for bad in (dict(mode=-1), dict(mode=6), dict(grid=0), dict(grid=65537), dict(iters=0),
+                dict(iters=(1 << 24) + 1), dict(out=None)):
+        a = dict(ok, **bad)
+        assert g(a["mode"], a["grid"], a["iters"], a["out"], None) == -1, bad
