@@ -1008,7 +1008,8 @@ def bench_overlap_probe(args):
     """How much fp32 VALU work overlaps the MFMA units: the probe library's
     overlap kernel (256 workgroups of 8 waves, one per CU) in six modes, each
     timed with HIP events on its launch stream (best of 3), reported as ns
-    per iteration of the probe's loop."""
+    per iteration of the probe's loop; then the barrier probe (does a
+    workgroup barrier wait for outstanding stores?), in ns per round."""
     import torch
 
     from kv_cache_eviction_qk_amd import build as kbuild
@@ -1041,8 +1042,32 @@ def bench_overlap_probe(args):
             ts.append(e0.elapsed_time(e1) * 1e-3)
         res[names[mode]] = round(min(ts) * 1e9 / iters, 2)
         log(f"{names[mode]:45s} {res[names[mode]]:8.2f} ns/iteration")
+    # and whether a workgroup barrier waits for the waves' outstanding stores
+    L.kvev_probe_barrier.argtypes = L.kvev_probe_overlap.argtypes
+    L.kvev_probe_barrier.restype = ctypes.c_int
+    bgrid, biters = 256, 2000
+    bout = torch.zeros(bgrid * 1024, dtype=torch.float32, device="cuda")
+    bnames = ["LDS exchange between barriers", "a nontemporal store before each barrier",
+              "the store and an explicit s_waitcnt vmcnt(0)"]
+    bres = {}
+    for mode in range(3):
+        ts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = L.kvev_probe_barrier(mode, bgrid, biters, bout.data_ptr(),
+                                      ctypes.c_void_p(stream.cuda_stream))
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"kvev_probe_barrier returned {rc}")
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        bres[bnames[mode]] = round(min(ts) * 1e9 / biters, 1)
+        log(f"{bnames[mode]:45s} {bres[bnames[mode]]:8.1f} ns/round")
     print(json.dumps({"metric": "mfma_valu_overlap", "unit": "ns per iteration", "grid": grid,
-                      "threads": 512, "iterations": iters, "modes": res}), flush=True)
+                      "threads": 512, "iterations": iters, "modes": res,
+                      "barrier_ns_per_round": bres, "barrier_grid": bgrid,
+                      "barrier_threads": 1024}), flush=True)
 
 def bench_window_attn(args, cfg):
     """kvev_window_attn on the workload's prompt cache (every head at length L)

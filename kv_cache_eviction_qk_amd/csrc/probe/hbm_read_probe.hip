@@ -1,7 +1,7 @@
 // hbm_read_probe.hip -- hardware probes (gfx950) that the eviction kernels'
 // measurements are read against: the plain HBM read rate (the read ceiling
-// of the roofline fractions) and how much vector-ALU work overlaps the matrix
-// cores.  Not part of the eviction path: they live in their own library,
+// of the roofline fractions), how much vector-ALU work overlaps the matrix
+// cores, and whether a workgroup barrier waits for outstanding stores.  Not part of the eviction path: they live in their own library,
 // libkvev_probe.so, which only the benchmark's probe modes load.
 //
 // Every pattern reads each byte of a buffer of nbytes (a multiple of 4096)
@@ -181,5 +181,43 @@ extern "C" int kvev_probe_overlap(int mode, int grid, int iters, float *out, voi
     case 4: hipLaunchKernelGGL(mfma_valu_overlap<4>, g, t, 0, s, iters, 1e-3f, out); break;
     default: hipLaunchKernelGGL(mfma_valu_overlap<5>, g, t, 0, s, iters, 1e-3f, out); break;
   }
+  return (int)hipGetLastError();
+}
+
+// ---- does a workgroup barrier wait for the waves' outstanding global
+// stores?  1024-thread workgroups run `iters` rounds of an LDS exchange
+// between two barriers; by mode, each thread first issues nothing (0), one
+// nontemporal store of its own float of `out` (1), or that store and an
+// explicit wait for it (2).  out: grid * 1024 floats, one per thread.
+namespace {
+template <int MODE>
+__global__ __launch_bounds__(1024) void store_barrier(float *out, int iters) {
+  __shared__ float s[1024];
+  float acc = (float)threadIdx.x;
+  float *o = out + (size_t)blockIdx.x * 1024 + threadIdx.x;
+  for (int it = 0; it < iters; ++it) {
+    if (MODE >= 1) __builtin_nontemporal_store(acc, o);
+    if (MODE == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    s[threadIdx.x] = acc;
+    __syncthreads();
+    acc += s[(threadIdx.x + 1) & 1023];
+    __syncthreads();
+  }
+  if (acc == 12345.f) o[0] = acc;
+}
+}  // namespace
+
+// kvev_probe_barrier -- one launch of barrier mode `mode` (0..2, above) with
+// `grid` (1 .. 65536) workgroups and `iters` (1 .. 2^24) rounds; out: device
+// array of grid * 1024 floats.  Returns 0, -1 for a bad argument (nothing
+// launched), or the hipError_t of the launch.
+extern "C" int kvev_probe_barrier(int mode, int grid, int iters, float *out, void *stream) {
+  if (mode < 0 || mode > 2 || grid < 1 || grid > 65536 || iters < 1 || iters > (1 << 24) || !out)
+    return -1;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 g(grid), t(1024);
+  if (mode == 0) hipLaunchKernelGGL(store_barrier<0>, g, t, 0, s, out, iters);
+  else if (mode == 1) hipLaunchKernelGGL(store_barrier<1>, g, t, 0, s, out, iters);
+  else hipLaunchKernelGGL(store_barrier<2>, g, t, 0, s, out, iters);
   return (int)hipGetLastError();
 }

@@ -501,3 +501,10 @@ def test_read_probe_library_refuses_bad_arguments():
                 dict(iters=(1 << 24) + 1), dict(out=None)):
         a = dict(ok, **bad)
         assert g(a["mode"], a["grid"], a["iters"], a["out"], None) == -1, bad
+    h = L.kvev_probe_barrier
+    h.argtypes = g.argtypes
+    h.restype = ctypes.c_int
+    for bad in (dict(mode=-1), dict(mode=3), dict(grid=0), dict(grid=65537), dict(iters=0),
+                dict(out=None)):
+        a = dict(ok, **bad)
+        assert h(a["mode"], a["grid"], a["iters"], a["out"], None) == -1, bad
