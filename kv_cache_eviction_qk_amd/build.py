@@ -36,6 +36,15 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source extra flags.  finish.hip takes its compaction ticket with an
+# atomic whose result is read only much later; the compiler's atomic optimizer
+# would rewrite that atomic into a wave-wide form that reads the result at once,
+# so the issuing wave would wait there for every load issued before it (the
+# head's keys).  Its other atomics are issued by one lane or go to divergent
+# LDS addresses, where the optimizer has nothing to combine.
+FILE_FLAGS = {"finish.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
+
 def _hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -49,7 +58,8 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-        cmd = [hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+               "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

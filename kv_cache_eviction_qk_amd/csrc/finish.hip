@@ -347,7 +347,14 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
   const int pi = min(tid, P.units - 1);
   const int pn = P.seq_len[pi];
   const int pe = P.head_err[pi];
+  // the free count (only the launch's last workgroup writes it, at the end)
+  const int fc0 = *P.free_count;
   if (spec) load_head(u);
+  // the compaction's first batch: a per-head ticket, taken now so that its
+  // round trip overlaps the selection (batches go out in ticket order, each
+  // to a running workgroup, so a wait for a lower batch always ends)
+  uint32_t ticket0 = 0;
+  if (spec && tid == 0) ticket0 = atomicAdd(&P.bctr[u], 1u);
   // nothing that waits for a load moves above the last of them
   __builtin_amdgcn_sched_barrier(0);
   const bool consistent = n >= 0 && n <= P.max_slots;
@@ -760,7 +767,7 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
 #pragma unroll
       for (int q = 0; q < kPreBlk / kFT; ++q) L.blk[tid + q * kFT] = pbid[q];
       // the first batch: the per-head ticket (local selection), else the part
-      if (spec && tid == 0) L.ticket = atomicAdd(&P.bctr[u], 1u);
+      if (spec && tid == 0) L.ticket = ticket0;
       __syncthreads();
       const int kb = spec ? (int)L.ticket : k;
       for (int rho = kb; rho < nbatch; rho += P.kh) {
@@ -910,7 +917,6 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
   int before, total;
   // the head's free-list offset and the total, for the head's last workgroup
   freed_prefix(freed_prefix_load(P, u, pn, pe), L, before, total);
-  const int fc0 = *P.free_count;
   const bool room = fc0 >= 0 && (long long)fc0 + total <= (long long)P.free_capacity;
   if (L.last) {
     if (consistent && m > 0) {
@@ -953,8 +959,10 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
   if (!L.last) return;
   // ---- the last workgroup of the launch: lengths, free count, stats, state
   for (int i = tid; i < P.units; i += kFT) {
-    const int ni = P.seq_len[i];
-    if (ni >= 0 && ni <= P.max_slots && P.head_err[i] == 0) P.seq_len[i] = min(ni, P.budget);
+    // (at most kFT heads: this thread's length and flag were loaded at entry)
+    const int ni = P.units <= kFT ? pn : P.seq_len[i];
+    const int ei = P.units <= kFT ? pe : (int)P.head_err[i];
+    if (ni >= 0 && ni <= P.max_slots && ei == 0) P.seq_len[i] = min(ni, P.budget);
     st_agent(&P.head_err[i], 0u);
   }
   if (tid == 0) {
