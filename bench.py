@@ -102,6 +102,24 @@ def read_traffic(workload, kernel_src, kernel="score", sha_key="score_source_sha
     return d.get("hbm_bytes_per_launch")
 
 
+def read_pass_traffic(workload):
+    """HBM bytes per fused pass (score kernel + evict_finish_kernel) from the
+    committed counter summary, if taken on the current kernel and launch code."""
+    p = os.path.join(ROOT, "profiles", f"pass_{workload}_hbm_counters.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except ValueError:
+        return None
+    h = hashlib.sha256()
+    for f in ("score.hip", "finish.hip", "api.hip"):
+        h.update(open(os.path.join(ROOT, "kv_cache_eviction_qk_amd", "csrc", f), "rb").read())
+    if d.get("source_sha256_16") != h.hexdigest()[:16]:
+        return None
+    return d.get("hbm_bytes_per_pass")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -396,7 +414,9 @@ def main():
                           "bound": "hbm", "achieved": pass_bytes / (ms_step / 1e3) / 1e9,
                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": pass_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS,
-                          "algorithmic_bytes": pass_bytes, "ms": ms_step},
+                          "algorithmic_bytes": pass_bytes, "ms": ms_step,
+                          "traffic": (read_pass_traffic(args.workload)
+                                      if args.path == "fused" else None)},
         "separate_calls_ms": {"score": t_score, "select": t_select, "compact": t_compact},
         # fused passes of independent caches alternating on two streams (not the headline)
         "two_stream_ms_per_pass": two_stream_ms,
