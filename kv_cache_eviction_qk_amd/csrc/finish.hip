@@ -100,6 +100,7 @@ struct FinLds {
   int32_t sblk[kBatchRanks];         // source block id of each rank (-1: stays)
   int32_t dblk[kBatchRanks / kBlock];  // destination block ids of the batch
   int32_t wtot[kFW];                 // scan scratch
+  int32_t wsum[2][kFW];              // chunk_scan's wave totals (two rows, alternating)
   int32_t rtot[kFW];                 // rank_bin_all's scan scratch
   RankOut r;
   uint32_t ticket, nsub, nt, cut, nown, mbase;
@@ -129,23 +130,24 @@ __device__ __forceinline__ void st_agent2(uint2 *p, uint2 v) {
 // Every earlier memory access of this thread has completed.
 __device__ __forceinline__ void wait_mem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Exclusive prefix sum of v over the 1024 threads (every thread must call);
-// *total receives the sum.
-__device__ int block_scan(int v, int *wtot, int *total) {
+// Exclusive prefix sum of v over the threads of this thread's 1024-slot
+// chunk of a group (4 slots a thread: a chunk is 4 waves, wave w in chunk
+// w / 4): the wave's own prefix plus the totals of the chunk's earlier waves,
+// through LDS with one barrier (every thread must call).  Consecutive calls
+// alternate between the two rows of wsum (*parity flips), so a call never
+// overwrites totals that a slower thread still reads from the previous one.
+__device__ int chunk_scan(int v, int (*wsum)[kFW], int *parity) {
   const int lane = lane_id(), wv = threadIdx.x / kWave;
   const int incl = (int)wave_incl_scan((uint32_t)v);
+  int *row = wsum[*parity];
+  *parity ^= 1;
+  if (lane == kWave - 1) row[wv] = incl;
   __syncthreads();
-  if (lane == kWave - 1) wtot[wv] = incl;
-  __syncthreads();
-  int before = 0, all = 0;
+  int before = incl - v;
 #pragma unroll
-  for (int w = 0; w < kFW; ++w) {
-    const int t = wtot[w];
-    before += w < wv ? t : 0;
-    all += t;
-  }
-  *total = all;
-  return before + incl - v;
+  for (int w = 0; w < 3; ++w)
+    if ((wv & ~3) + w < wv) before += row[(wv & ~3) + w];
+  return before;
 }
 
 // The bin holding the rank-th smallest key (1-based) of a histogram of NBINS
@@ -720,6 +722,7 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
     };
 
     // ------------------------------------------------------------ victim list
+    int scan_parity = 0;  // chunk_scan's row
     if (k == 0 && tid == 0) P.n_victims[u] = m;
     int32_t *vout = P.victims + urow;
     for (int g = g_lo; g < g_hi; ++g) {
@@ -728,8 +731,8 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
       bool v[4];
       vic4(g, kk, v);
       const int cnt = (int)v[0] + (int)v[1] + (int)v[2] + (int)v[3];
-      int tot;
-      int o = (int)L.cv[4 * g] + block_scan(cnt, L.wtot, &tot);
+      // victims before the chunk, then before this thread within it
+      int o = (int)L.cv[4 * g + wv / 4] + chunk_scan(cnt, L.wsum, &scan_parity);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if (v[e]) {
@@ -801,8 +804,8 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
             const int s = g * kGrp + 4 * tid + e;
             kc += (s < n && !v[e]) ? 1 : 0;
           }
-          int tot;
-          int r = kbc(4 * g) + block_scan(kc, L.wtot, &tot);
+          // kept slots before the chunk, then before this thread within it
+          int r = kbc(4 * g + wv / 4) + chunk_scan(kc, L.wsum, &scan_parity);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int s = g * kGrp + 4 * tid + e;
