@@ -281,6 +281,25 @@ def main():
     # step's victims: naive (holes left in place) vs after compaction
     waste = K.measure(pristine.seq_len, victims, n_victims)
 
+    # ---- each pass timed on its own, after a restore and a cache flush of its
+    # own (the keys come from HBM every time): median, p10 and p90
+    per_pass_us = None
+    if args.path == "fused":
+        for i in range(steps):
+            restore(i)
+        ts = []
+        for i in range(steps):
+            flush_caches()
+            q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            q0.record()
+            step(i)
+            q1.record()
+            torch.cuda.synchronize()
+            ts.append(q0.elapsed_time(q1) * 1e3)
+        ts = np.array(ts)
+        per_pass_us = {"median": float(np.median(ts)), "p10": float(np.percentile(ts, 10)),
+                       "p90": float(np.percentile(ts, 90)), "n": int(steps)}
+
     # ---- the scoring kernel alone (kvev_score, same launch configuration):
     # `steps` back-to-back launches between two HIP events on their stream,
     # each reading its own copy of the cache after one flush, so its keys
@@ -417,6 +436,11 @@ def main():
                           "algorithmic_bytes": pass_bytes, "ms": ms_step,
                           "traffic": (read_pass_traffic(args.workload)
                                       if args.path == "fused" else None)},
+        # every KV head of every scored token: B * Hkv * L head-rows a pass
+        "head_rows_per_s": B * Hkv * n * steps / (ms_total / 1e3),
+        # each pass alone, after its own flush (not the headline, which is the
+        # back-to-back passes)
+        "per_pass_us": per_pass_us,
         "separate_calls_ms": {"score": t_score, "select": t_select, "compact": t_compact},
         # fused passes of independent caches alternating on two streams (not the headline)
         "two_stream_ms_per_pass": two_stream_ms,
