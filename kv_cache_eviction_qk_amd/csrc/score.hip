@@ -130,12 +130,16 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
   extern __shared__ __align__(16) uint8_t smem[];
 
   const int RT = P.rt_part;  // row tiles this workgroup stages
-  uint4 *qfrag = reinterpret_cast<uint4 *>(smem);
-  uint4 *afrag = qfrag + RT * U * kWave;          // hi (or fp32), then lo
-  float *lse2 = reinterpret_cast<float *>(afrag + AF * RT * U * kWave);
-  int *qposr = reinterpret_cast<int *>(lse2 + RT * 16);
-  float *an2 = reinterpret_cast<float *>(qposr + RT * 16);
-  float *S_lds = an2 + (DROP ? RT * 16 : 0);
+  // Per row tile, its fragments side by side (q, then a: hi and lo, or
+  // fp32), and its per-row values side by side (LSE in log2 units, query
+  // position, ||a||^2): one pointer each walks the row tiles.
+  constexpr int NC = 1 + AF;            // staged fragment copies per row tile
+  constexpr int NS = DROP ? 3 : 2;      // per-row values per row tile
+  uint4 *frag = reinterpret_cast<uint4 *>(smem);
+  float *rowd = reinterpret_cast<float *>(frag + (size_t)RT * NC * U * kWave);
+  auto fragu = [&](int rt, int c, int j) { return frag + ((size_t)(rt * NC + c) * U + j) * kWave; };
+  auto rowv = [&](int r, int k) { return rowd + ((r >> 4) * NS + k) * 16 + (r & 15); };
+  float *S_lds = rowd + RT * NS * 16;
   const int span_blocks = P.tile_blocks + 2 * P.halo_blocks;
   float *D_lds = S_lds + span_blocks * 16;
   // DropKV's exact-term queue: entry = window row << 16 | span slot, its term
@@ -193,10 +197,10 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
   auto stage_pair = [&](int pr_) {
     const int rt = pr_ / U, j = pr_ % U;
     const int r = min(rt * 16 + lr, rows - 1), cc = lg * U + j;
-    ld16_to_lds(qsrc + (size_t)r * ROWB + cc * 16, qfrag + (size_t)pr_ * kWave);
+    ld16_to_lds(qsrc + (size_t)r * ROWB + cc * 16, fragu(rt, 0, j));
     if constexpr (DROP && !BF16)  // fp32 caches: a's fp32 rows are the fragments
       ld16_to_lds(reinterpret_cast<const uint8_t *>(asrc) + (size_t)r * ROWB + cc * 16,
-                  afrag + (size_t)pr_ * kWave);
+                  fragu(rt, 1, j));
   };
   if (n <= 0 || n > max_slots) return;  // empty or inconsistent head: nothing to score
   const int nb = (n + kBlock - 1) / kBlock;
@@ -253,21 +257,21 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
   // ---- the rest of the window-row staging while the first key blocks stream in
   if ((int)threadIdx.x < RT * 16) {
     const bool live = (int)threadIdx.x < rows;
-    lse2[threadIdx.x] = live ? lse_v * kLog2e : __builtin_inff();  // padding rows: p = 0
-    qposr[threadIdx.x] = live ? qpos_v : INT_MAX;
+    *rowv(threadIdx.x, 0) = live ? lse_v * kLog2e : __builtin_inff();  // padding rows: p = 0
+    *reinterpret_cast<int *>(rowv(threadIdx.x, 1)) = live ? qpos_v : INT_MAX;
   }
   for (int pr_ = wv + kQ * kWaves; pr_ < npairs; pr_ += kWaves) stage_pair(pr_);  // large windows
   for (int r = threadIdx.x + kThreads; r < RT * 16; r += kThreads) {
     const bool live = r < rows;
     const int rr = min(r, rows - 1);
-    lse2[r] = live ? P.lse[row0 + rr] * kLog2e : __builtin_inff();
-    qposr[r] = live ? P.q_pos[(size_t)b * P.W + ((rb + rr) % P.W)] : INT_MAX;
+    *rowv(r, 0) = live ? P.lse[row0 + rr] * kLog2e : __builtin_inff();
+    *reinterpret_cast<int *>(rowv(r, 1)) =
+        live ? P.q_pos[(size_t)b * P.W + ((rb + rr) % P.W)] : INT_MAX;
   }
   if constexpr (DROP) {
     if constexpr (BF16) {
       // a's fp32 rows as bf16 high and low parts, in fragment order: unit x
       // of pair x / 64 holds 8 elements of row rt*16 + (x%64)%16
-      uint4 *alo = afrag + RT * U * kWave;
       for (int x = threadIdx.x; x < RT * U * kWave; x += kThreads) {
         const int pr_ = x / kWave, ln = x % kWave;
         const int rt = pr_ / U, j = pr_ % U;
@@ -284,8 +288,8 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
           hw[i] = h0 | (h1 << 16);
           lw[i] = l0 | (l1 << 16);
         }
-        afrag[x] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        alo[x] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        fragu(rt, 1, j)[ln] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        fragu(rt, 2, j)[ln] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       }
     }
     // ||a||^2 of each row from its fp32 values, d ascending
@@ -302,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
           ss = fmaf(f.w, f.w, ss);
         }
       }
-      an2[r] = ss;
+      *rowv(r, 2) = ss;
     }
   }
   if (want_hist)
@@ -343,16 +347,16 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
       uint4 qa[U], aa[U], al[U];
 #pragma unroll
       for (int j = 0; j < U; ++j) {
-        qa[j] = qfrag[(rt * U + j) * kWave + l];
-        if constexpr (DROP) aa[j] = afrag[(rt * U + j) * kWave + l];
-        if constexpr (DROP && BF16) al[j] = afrag[((RT + rt) * U + j) * kWave + l];
+        qa[j] = fragu(rt, 0, j)[l];
+        if constexpr (DROP) aa[j] = fragu(rt, 1, j)[l];
+        if constexpr (DROP && BF16) al[j] = fragu(rt, 2, j)[l];
       }
-      const float4 L = *reinterpret_cast<const float4 *>(&lse2[rt * 16 + lg * 4]);
+      const float4 L = *reinterpret_cast<const float4 *>(rowv(rt * 16 + lg * 4, 0));
       const float Le[4] = {L.x, L.y, L.z, L.w};
       // acc = q.k; av starts at -(||a||^2 + ||v||^2)/2 and ends at -||a - v||^2/2
       floatx4 acc[NB], av[NB];
       if constexpr (DROP) {
-        const float4 A2 = *reinterpret_cast<const float4 *>(&an2[rt * 16 + lg * 4]);
+        const float4 A2 = *reinterpret_cast<const float4 *>(rowv(rt * 16 + lg * 4, 2));
         const float Ae[4] = {A2.x, A2.y, A2.z, A2.w};
 #pragma unroll
         for (int i = 0; i < NB; ++i)
@@ -377,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[i][e] = fmaf(acc[i][e], c1, -Le[e]);
       if (need_mask) {
-        const int4 Qp = *reinterpret_cast<const int4 *>(&qposr[rt * 16 + lg * 4]);
+        const int4 Qp = *reinterpret_cast<const int4 *>(rowv(rt * 16 + lg * 4, 1));
         const int Qe[4] = {Qp.x, Qp.y, Qp.z, Qp.w};
 #pragma unroll
         for (int i = 0; i < NB; ++i)
@@ -397,6 +401,11 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
         for (int i = 0; i < NB; ++i)
 #pragma unroll
           for (int e = 0; e < 4; ++e) hx = fmaxf(hx, x[i][e]);
+        // this row tile's terms and weights per key, added to the running
+        // sums after either branch (the branches carry only these)
+        float dd[NB], ds[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) dd[i] = ds[i] = 0.f;
         if (!__any(hx >= -12.f)) {
           // p < 2^-12: p/(1-p) = p + p^2 within a relative p^2 (< 2^-24);
           // the sums hold term/sqrt(2): sqrt(-av) = ||a - v|| / sqrt(2)
@@ -409,14 +418,14 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
 #pragma unroll
             for (int i = 0; i < NB; ++i)
 #pragma unroll
-              for (int e = 0; e < 4; ++e) psum[i] += pp[i][e];
+              for (int e = 0; e < 4; ++e) ds[i] += pp[i][e];
           }
 #pragma unroll
           for (int i = 0; i < NB; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              pdrop[i] = fmaf(fmaf(pp[i][e], pp[i][e], pp[i][e]),
-                              __builtin_amdgcn_sqrtf(-min_zero(av[i][e])), pdrop[i]);
+              dd[i] = fmaf(fmaf(pp[i][e], pp[i][e], pp[i][e]),
+                           __builtin_amdgcn_sqrtf(-min_zero(av[i][e])), dd[i]);
         } else {
           uint32_t slow = 0;  // terms with p >= 1/4: queued for the exact pass
 #pragma unroll
@@ -424,14 +433,14 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float p = __builtin_amdgcn_exp2f(x[i][e]);
-              if (want_sum) psum[i] += p;
+              if (want_sum) ds[i] += p;
               // only the wave's own blocks queue (clamped re-reads are dropped)
               const bool exact = !fast_only && x[i][e] >= -2.f && cur + i < wb1;
               slow |= (exact ? 1u : 0u) << (i * 4 + e);
               const float X = -min_zero(av[i][e]);  // ||a - v||^2 / 2
               const float om = 1.f - p;
               const float t = p * X * __builtin_amdgcn_rsqf(fmaxf(X * om * om, __FLT_MIN__));
-              pdrop[i] += exact ? 0.f : t;
+              dd[i] += exact ? 0.f : t;
             }
           }
           if (__any(slow != 0)) {
@@ -453,6 +462,11 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const ScoreArgs P) {
               }
             }
           }
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          psum[i] += ds[i];
+          pdrop[i] += dd[i];
         }
       }
     }
