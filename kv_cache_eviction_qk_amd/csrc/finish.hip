@@ -203,15 +203,17 @@ __device__ void rank_bin_all(const uint32_t *h, uint32_t rank, RankOut *out, int
 }
 
 // The (head, part) of a ticket.  With the heads a multiple of 8, ticket t
-// goes to head 8 * ((t / 8) / kh) + t % 8, part (t / 8) % kh: when tickets
-// follow dispatch order, which deals workgroups to the 8 XCDs round robin,
-// a head's workgroups share one XCD and its L2 (they all read the head's
-// scores).  Within a head the parts' tickets increase with the part, which is
-// all the waits need.
+// goes to head (t % 8) * (units / 8) + (t / 8) / kh, part (t / 8) % kh: when
+// tickets follow dispatch order, which deals workgroups to the 8 XCDs round
+// robin, XCD x runs the heads [x * units/8, (x+1) * units/8), the heads whose
+// tiles the score kernel ran there, so each head's scores and histogram are
+// read from the L2 that took their writes.  A head's tickets lie within 8 * kh
+// consecutive ones, and within a head the parts' tickets increase with the
+// part, which is all the waits need.
 __device__ __forceinline__ void ticket_head(int t, int units, int kh, int &u, int &k) {
   if (units % 8 == 0) {
     const int slot = t >> 3;
-    u = (slot / kh) * 8 + (t & 7);
+    u = (t & 7) * (units / 8) + slot / kh;
     k = slot % kh;
   } else {
     u = t / kh;
