@@ -99,7 +99,6 @@ struct FinLds {
   int32_t src[kBatchRanks];          // source slot of each rank of a batch
   int32_t sblk[kBatchRanks];         // source block id of each rank (-1: stays)
   int32_t dblk[kBatchRanks / kBlock];  // destination block ids of the batch
-  int32_t wtot[kFW];                 // scan scratch
   int32_t wsum[2][kFW];              // chunk_scan's wave totals (two rows, alternating)
   int32_t rtot[kFW];                 // rank_bin_all's scan scratch
   RankOut r;
