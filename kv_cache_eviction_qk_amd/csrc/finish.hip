@@ -16,10 +16,12 @@
 //     A head of at most kRes groups (32768 slots) is selected locally: each
 //     of its workgroups holds all its keys in registers and finds T, the cut
 //     and the victims per 1024-slot chunk itself, with no exchange.  A longer
-//     head shares the work: each workgroup takes its share of the slots,
-//     publishes the keys below b per chunk, the bucket's members and their
-//     histogram, waits for the head's workgroups to arrive, and reads what
-//     all published.
+//     head shares the work in two rounds over each workgroup's share of the
+//     slots: first the histogram of the bucket members' key bits 20..10 is
+//     summed over the head (one arrival), which gives the sub-bucket; then
+//     each workgroup publishes its chunks' victim counts (keys below b and
+//     members below the sub-bucket) and the sub-bucket's keys, and after a
+//     second arrival every workgroup reads them all.
 //  2. Victim list.  Each workgroup writes the victims of its share's groups
 //     at their offsets, in ascending slot order.
 //  3. Compaction ([H2O] "PagedAttention Memory Integration"; [VTOK] section
@@ -38,7 +40,7 @@
 //
 // Waits and hand-offs.  A workgroup waits only for workgroups of its own
 // head: for the marks of lower batches, and, when the head shares its
-// selection, at the head's arrival counter.  When every head is selected
+// selection, twice at the head's arrival counter.  When every head is selected
 // locally (max_slots <= 32768), a workgroup's head and part come from its
 // index, so its loads go out at once and, as dispatch deals workgroups to the
 // 8 XCDs round robin, a head's workgroups share one XCD's L2; its batches
@@ -102,7 +104,7 @@ struct FinLds {
   int32_t wsum[2][kFW];              // chunk_scan's wave totals (two rows, alternating)
   int32_t rtot[kFW];                 // rank_bin_all's scan scratch
   RankOut r;
-  uint32_t ticket, nsub, nt, cut, nown, mbase;
+  uint32_t ticket, nsub, nt, cut;
   int32_t moved, at_risk, last;
   unsigned long long pre_tot[2];
 };
@@ -217,6 +219,20 @@ __device__ __forceinline__ void ticket_head(int t, int units, int kh, int &u, in
   } else {
     u = t / kh;
     k = t % kh;
+  }
+}
+
+// Adds 1 to cv[c] for every lane with `take`: one atomic for the wave when its
+// valid lanes share one chunk (members arrive in slot order, so they usually
+// do), else one a lane.  Every lane of the wave calls it; lane 0 is valid
+// whenever any lane is.
+__device__ __forceinline__ void count_chunk(uint32_t *cv, bool valid, bool take, uint32_t c) {
+  const uint32_t c0 = (uint32_t)__shfl((int)c, 0);
+  const uint64_t t = __ballot(take);
+  if (__all(!valid || c == c0)) {
+    if (lane_id() == 0 && t) atomicAdd(&cv[c0], (uint32_t)__popcll(t));
+  } else if (take) {
+    atomicAdd(&cv[c], 1u);
   }
 }
 
@@ -391,7 +407,7 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
     // A head of at most kRes groups is selected locally: every workgroup of
     // the head holds all its keys in registers and finds the threshold
     // itself, with no exchange; longer heads share the work (each its share,
-    // published and read back).  Keys held in registers: the whole head, or
+    // published and read back in two rounds).  Keys held in registers: the whole head, or
     // the share (not beside the widest rows' pieces).
     const bool local = PR <= 16 && ngrp_all <= kRes;
     const int r_lo = local ? 0 : g_lo, r_hi = local ? ngrp_all : g_hi;
@@ -447,7 +463,6 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
     for (int i = tid; i <= kMaxChunks; i += kFT) L.cv[i] = 0;
     if (tid == 0) {
       L.nsub = 0;
-      L.nown = 0;
       L.moved = 0;
       L.at_risk = 0;
     }
@@ -512,74 +527,37 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
         if (lane == 0 && below) atomicAdd(&L.cv[4 * g + wv / 4], below);
       }
     } else {
-      // ---- own share: keys below the bucket per chunk (a wave covers 256
-      // slots of a group: chunk = 4 g + wave / 4), the bucket's members (counted
-      // first, so one atomic per workgroup reserves their place), and the
-      // histogram of their key bits 20..10
+      // ---- own share, first pass: keys below the bucket per chunk (a wave
+      // covers 256 slots of a group: chunk = 4 g + wave / 4), and the
+      // histogram of the bucket members' key bits 20..10, added to the head's
       uint32_t *gbel = P.gbelow + (size_t)u * P.chunks;
       for (int g = g_lo; g < g_hi; ++g) {
         uint32_t kk[4];
         keys_of(g, kk);
-        uint32_t below = 0, mine = 0;
+        uint32_t below = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int s = g * kGrp + 4 * tid + e;
           const bool in = s < nc;
           const uint32_t top = kk[e] >> 21;
           below += (uint32_t)__popcll(__ballot(in && top < bkt));
-          const bool mb = in && top == bkt;
-          if (mb) atomicAdd(&L.h2[(kk[e] >> 10) & 2047u], 1u);
-          mine += (uint32_t)__popcll(__ballot(mb));
+          if (in && top == bkt) atomicAdd(&L.h2[(kk[e] >> 10) & 2047u], 1u);
         }
-        if (lane == 0) {
-          if (below) atomicAdd(&L.cv[4 * g + wv / 4], below);
-          if (mine) atomicAdd(&L.nown, mine);
-        }
+        if (lane == 0 && below) atomicAdd(&L.cv[4 * g + wv / 4], below);
       }
       __syncthreads();
-      if (tid == 0) L.mbase = L.nown ? atomicAdd(&P.nmem[u], L.nown) : 0u;
-      if (tid == 0) L.nown = 0;
-      for (int c = 4 * g_lo + tid; c < min(4 * g_hi, nch); c += kFT) st_agent(gbel + c, L.cv[c]);
       uint32_t *h2g = P.hist2 + (size_t)u * kSelectBins;
 #pragma unroll
       for (int q = 0; q < kSelectBins / kFT; ++q)
         if (L.h2[tid + q * kFT]) atomicAdd(&h2g[tid + q * kFT], L.h2[tid + q * kFT]);
-      __syncthreads();
-      const uint32_t mbase = L.mbase;
-      for (int g = g_lo; g < g_hi; ++g) {
-        uint32_t kk[4];
-        keys_of(g, kk);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int s = g * kGrp + 4 * tid + e;
-          const bool mb = s < nc && (kk[e] >> 21) == bkt;
-          const uint64_t mm = __ballot(mb);
-          if (mm) {
-            uint32_t base = 0;
-            if (lane == 0) base = atomicAdd(&L.nown, (uint32_t)__popcll(mm));
-            base = __shfl(base, 0);
-            if (mb) st_agent2(gmem + mbase + base + (uint32_t)ballot_prefix(mm),
-                              make_uint2(kk[e], (uint32_t)s));
-          }
-        }
-      }
       // ---- arrive, then wait for every workgroup of the head
       wait_mem();
       __syncthreads();
       if (tid == 0) atomicAdd(&P.arrive[u], 1u);
       wait_count(&P.arrive[u], (uint32_t)P.kh, acc);
       __syncthreads();
-      // ---- what the head's workgroups published: one round of loads
-      nmem = (int)ld_agent(&P.nmem[u]);
 #pragma unroll
       for (int q = 0; q < kSelectBins / kFT; ++q) hv[q] = ld_agent(&h2g[tid + q * kFT]);
-      uint32_t cb = tid < nch ? ld_agent(gbel + tid) : 0u;
-      uint2 pr[4];  // the first members, read before their count is known
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        pr[q] = q * kFT + tid < P.max_slots ? ld_agent2(gmem + q * kFT + tid) : make_uint2(0u, 0u);
-      for (int c = tid + kFT; c < nch; c += kFT) L.cv[c] = ld_agent(gbel + c);
-      if (tid < nch) L.cv[tid] = cb;
 #pragma unroll
       for (int q = 0; q < kSelectBins / kFT; ++q) L.h2[tid + q * kFT] = hv[q];
       for (int i = tid; i < 1024; i += kFT) L.h[i] = 0;
@@ -587,33 +565,46 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
       rank_bin_all<kSelectBins>(L.h2, need, &L.r, L.rtot);
       pre = (bkt << 11) | L.r.bin;  // key >> 10 of T
       need2 = need - L.r.below;
-      // every member: those below the sub-bucket are victims (per chunk); the
-      // sub-bucket's keys get the histogram of their last 10 bits and go to LDS
-      // (the first kMem of them)
-      for (int i0 = 0; i0 < nmem; i0 += 4 * kFT) {
-        if (i0 > 0) {
+      // ---- own share, second pass: the bucket's members below the sub-bucket
+      // join their chunk's victims, and the sub-bucket's keys are published
+      // (each wave reserves its place with one atomic)
+      for (int g = g_lo; g < g_hi; ++g) {
+        uint32_t kk[4];
+        keys_of(g, kk);
+        uint32_t below = 0;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int i = i0 + q * kFT + tid;
-            pr[q] = i < nmem ? ld_agent2(gmem + i) : make_uint2(0u, 0u);
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const bool v = i0 + q * kFT + tid < nmem;
-          const uint32_t p = pr[q].x >> 10;
-          if (v && p < pre) atomicAdd(&L.cv[pr[q].y / kChunk], 1u);
-          const bool sb = v && p == pre;
-          if (sb) atomicAdd(&L.h[pr[q].x & 1023u], 1u);
+        for (int e = 0; e < 4; ++e) {
+          const int s = g * kGrp + 4 * tid + e;
+          const bool mb = s < nc && (kk[e] >> 21) == bkt;
+          const uint32_t p = kk[e] >> 10;
+          below += (uint32_t)__popcll(__ballot(mb && p < pre));
+          const bool sb = mb && p == pre;
           const uint64_t sm = __ballot(sb);
           if (sm) {
             uint32_t base = 0;
-            if (lane == 0) base = atomicAdd(&L.nsub, (uint32_t)__popcll(sm));
+            if (lane == 0) base = atomicAdd(&P.nmem[u], (uint32_t)__popcll(sm));
             base = __shfl(base, 0);
-            const uint32_t j = base + (uint32_t)ballot_prefix(sm);
-            if (sb && j < (uint32_t)kMem) L.sub[j] = pr[q];
+            if (sb) st_agent2(gmem + base + (uint32_t)ballot_prefix(sm), make_uint2(kk[e], (uint32_t)s));
           }
         }
+        if (lane == 0 && below) atomicAdd(&L.cv[4 * g + wv / 4], below);
+      }
+      __syncthreads();
+      for (int c = 4 * g_lo + tid; c < min(4 * g_hi, nch); c += kFT) st_agent(gbel + c, L.cv[c]);
+      // ---- arrive again, then read every chunk's count and the sub-bucket
+      wait_mem();
+      __syncthreads();
+      if (tid == 0) atomicAdd(&P.arrive[u], 1u);
+      wait_count(&P.arrive[u], 2u * (uint32_t)P.kh, acc);
+      __syncthreads();
+      nmem = (int)ld_agent(&P.nmem[u]);  // the sub-bucket's keys, all workgroups
+      for (int c = tid; c < nch; c += kFT) L.cv[c] = ld_agent(gbel + c);
+      if (tid == 0) L.nsub = (uint32_t)nmem;
+      // their last 10 bits' histogram, and the first kMem of them in LDS
+      for (int i = tid; i < nmem; i += kFT) {
+        const uint2 pk = ld_agent2(gmem + i);
+        atomicAdd(&L.h[pk.x & 1023u], 1u);
+        if (i < kMem) L.sub[i] = pk;
       }
     }
     __syncthreads();
