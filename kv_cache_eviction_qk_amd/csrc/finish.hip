@@ -106,7 +106,7 @@ struct FinLds {
   RankOut r;
   uint32_t ticket, nsub, nt, cut;
   int32_t moved, at_risk, last;
-  unsigned long long pre_tot[2];
+  unsigned long long pre_w[2][kFW];   // freed_prefix's wave sums
 };
 
 __device__ __forceinline__ int blocks_of(int n) { return (n + kBlock - 1) / kBlock; }
@@ -279,23 +279,40 @@ __device__ Prefix freed_prefix_load(const FinishArgs &P, int u, int pn, int pe) 
   }
   return x;
 }
-__device__ void freed_prefix(Prefix x, FinLds &L, int &before, int &total) {
-  long long b = x.b, t = x.t;
+// One barrier: per-wave sums through LDS.  Where units * max_blocks stays
+// below 2^31 (every shape in practice) the wave sums are 32-bit prefix sums
+// on DPP lane moves; otherwise 64-bit sums over lane shuffles, so that an
+// inconsistent table (a total above the pool) cannot wrap around.
+__device__ void freed_prefix(const FinishArgs &P, Prefix x, FinLds &L, long long &before,
+                             long long &total) {
+  const int wv = threadIdx.x / kWave;
+  unsigned long long bw, tw;
+  if ((long long)P.units * P.max_blocks < (1ll << 31)) {
+    bw = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan((uint32_t)x.b), kWave - 1);
+    tw = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan((uint32_t)x.t), kWave - 1);
+  } else {
+    long long b = x.b, t = x.t;
 #pragma unroll
-  for (int o = kWave / 2; o >= 1; o >>= 1) {
-    b += __shfl_xor(b, o);
-    t += __shfl_xor(t, o);
+    for (int o = kWave / 2; o >= 1; o >>= 1) {
+      b += __shfl_xor(b, o);
+      t += __shfl_xor(t, o);
+    }
+    bw = (unsigned long long)b;
+    tw = (unsigned long long)t;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) L.pre_tot[0] = L.pre_tot[1] = 0;
-  __syncthreads();
   if (lane_id() == 0) {
-    atomicAdd(&L.pre_tot[0], (unsigned long long)b);
-    atomicAdd(&L.pre_tot[1], (unsigned long long)t);
+    L.pre_w[0][wv] = bw;
+    L.pre_w[1][wv] = tw;
   }
   __syncthreads();
-  before = (int)L.pre_tot[0];
-  total = (int)L.pre_tot[1];
+  unsigned long long sb = 0, st = 0;
+#pragma unroll
+  for (int w = 0; w < kFW; ++w) {
+    sb += L.pre_w[0][w];
+    st += L.pre_w[1][w];
+  }
+  before = (long long)sb;
+  total = (long long)st;
 }
 
 // PR: 16-byte pieces of one K (or V) row (8, 16 or 32); SPEC: every head
@@ -909,9 +926,9 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
   __syncthreads();
   if (tid == 0) L.last = atomicAdd(&P.head_done[u], 1u) == (uint32_t)(P.kh - 1) ? 1 : 0;
   __syncthreads();
-  int before, total;
+  long long before, total;
   // the head's free-list offset and the total, for the head's last workgroup
-  freed_prefix(freed_prefix_load(P, u, pn, pe), L, before, total);
+  freed_prefix(P, freed_prefix_load(P, u, pn, pe), L, before, total);
   const bool room = fc0 >= 0 && (long long)fc0 + total <= (long long)P.free_capacity;
   if (L.last) {
     if (consistent && m > 0) {
@@ -965,7 +982,7 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
     const unsigned long long moved = atomicExch(&acc[1], 0ull);
     const unsigned long long risk = atomicExch(&acc[2], 0ull);
     unsigned long long status = atomicExch(&acc[3], 0ull);
-    if (room) *P.free_count = fc0 + total;
+    if (room) *P.free_count = (int)(fc0 + total);
     else status |= 4ull;
     P.stats[0] = (int64_t)freed;
     P.stats[1] = (int64_t)moved;
