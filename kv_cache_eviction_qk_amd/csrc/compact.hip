@@ -64,12 +64,7 @@ struct PrepLds {
 // Exclusive prefix sum over a 256-thread workgroup.
 __device__ int block_exclusive_scan(int v, int *wave_tot) {
   const int lane = lane_id(), wv = threadIdx.x / kWave;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
-  }
+  const int incl = (int)wave_incl_scan((uint32_t)v);
   if (lane == kWave - 1) wave_tot[wv] = incl;
   __syncthreads();
   int before = 0;

@@ -159,8 +159,8 @@ template <int NBINS>
 __device__ void rank_bin_all(const uint32_t *h, uint32_t rank, RankOut *out, int *wtot) {
   constexpr int PER = NBINS >= kFT ? NBINS / kFT : 1;
   static_assert(PER == 1 || PER == 2, "one or two bins a thread");
-  // (used for the 2048-bin steps; the smaller ones stay on one wave, which
-  // keeps the kernel within its registers)
+  // (the 2048-bin steps and the last 10 bits' 1024 bins; the tie ranks'
+  // 256-bin steps stay on one wave)
   const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
   const bool act = tid * PER < NBINS;
   uint32_t x[PER], mine = 0;
@@ -649,7 +649,7 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
         }
       }
     };
-    wg_rank_bin<1024>(L.h, need2, &L.r);
+    rank_bin_all<1024>(L.h, need2, &L.r, L.rtot);
     const uint32_t T = (pre << 10) | L.r.bin;
     const uint32_t eT = need2 - L.r.below;  // keys equal to T that are victims
     const uint32_t cnt_t = L.h[L.r.bin];

@@ -36,19 +36,6 @@ constexpr int kHeadCand = 4096;     // bucket pairs refine keeps in LDS
 constexpr int kHeadTie = 2048;      // keys equal to T ranked in LDS
 
 // Inclusive scan of v over the 64 lanes of a wave.
-// Inclusive prefix sum over the wave's 64 lanes, on DPP lane moves (no LDS
-// round trips): shifts by 1, 2, 4 and 8 within each row of 16 lanes, then
-// lane 15 of each row added into the next row, and lane 31 into rows 2 and
-// 3.  A lane with no source reads 0.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  return v;
-}
 
 struct RankOut {
   uint32_t bin, below;
