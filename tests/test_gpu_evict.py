@@ -162,3 +162,34 @@ def test_evict_matches_oracle(name, over, kind, pool, budget, recent):
     nd = check_eviction_vs_oracle_chain(case, st, ov, on, new, ofl, ofc, ostats, o32,
                                         TOL[cfg.dtype])
     print(f"{name}: {nd} heads with victims differing inside the tolerance band", flush=True)
+
+
+def test_evict_on_two_streams_equals_sequential():
+    """Independent caches (the layers of one model) evicted concurrently on
+    two streams, each with its own workspace and outputs, end bit-exact equal
+    to the same evictions run one after the other on one stream."""
+    import torch
+
+    cfg = synth.CONFIGS["snapkv_prefill_32k"].scaled(B=2, Hkv=4, L=3001)
+    cases = [synth.make_case(cfg.scaled(seed=cfg.seed + i), seq_len=_ragged(2, 4, 3001, 11 + i))
+             for i in range(4)]
+    inputs = [_inputs(c, "pool")[0] for c in cases]
+    seq_runs = [Run(c) for c in cases]
+    for r, lse32 in zip(seq_runs, inputs):
+        r.fused("pool", lse32, None, 7, 700, 32)
+    par_runs = [Run(c) for c in cases]
+    lses = [dev(x) for x in inputs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    cur = torch.cuda.current_stream()
+    for s in streams:
+        s.wait_stream(cur)
+    for i, (r, lse) in enumerate(zip(par_runs, lses)):
+        with torch.cuda.stream(streams[i % 2]):
+            r.stats = K.evict(r.dc, r.q, lse, r.qp, r.case["scale"], r.case["G"], K.POOL, 700, 32,
+                              r.score, r.vic, r.nv, r.fl, r.fc, r.ws, pool_kernel=7)
+    for s in streams:
+        cur.wait_stream(s)
+    torch.cuda.synchronize()
+    for a, b, c in zip(seq_runs, par_runs, cases):
+        _assert_same(a.state(), b.state(), c["seq_len"])
