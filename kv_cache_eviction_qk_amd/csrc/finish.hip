@@ -88,6 +88,7 @@ constexpr int kMem = 4096;              // sub-bucket members kept in LDS
 constexpr int kTie = 2048;              // keys equal to T ranked by counting
 constexpr int kPreBlk = 2048;           // block ids held in LDS (a head of kRes groups: all)
 constexpr unsigned kSpinLimit = 1u << 20;  // polls of a wait before it gives up (status bit 8)
+constexpr int kMaxHeadParts = 128;      // workgroups of one head (see finish_parts)
 
 constexpr int kChunk = kSelectChunk;    // victim offsets are kept per 1024-slot chunk
 constexpr int kMaxChunks = kSelectMaxChunks;
@@ -999,10 +1000,15 @@ __global__ __launch_bounds__(kFT) void evict_finish_kernel(const FinishArgs P) {
 size_t finish_lds_bytes() { return sizeof(FinLds); }
 
 int finish_parts(int units, int rows_cap) {
-  // enough workgroups to cover the CUs twice, at most one per batch of ranks
+  // enough workgroups to cover the CUs twice, at most one per batch of ranks,
+  // and at most kMaxHeadParts: a head that shares its selection waits until
+  // all its workgroups have arrived, so they must fit on the chip at once.
+  // The kernel runs one 1024-thread workgroup per CU (its registers), and
+  // half of gfx950's 256 CUs keeps a head's workgroups resident even beside
+  // a second launch of this kernel on another stream.
   const int batches = std::max(1, (rows_cap + kBatchRanks - 1) / kBatchRanks);
   const int want = std::max(1, (512 + units - 1) / units);
-  return std::min(batches, want);
+  return std::min({batches, want, kMaxHeadParts});
 }
 
 hipError_t launch_finish(const FinishArgs &a, hipStream_t s) {

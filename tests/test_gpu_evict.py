@@ -193,3 +193,31 @@ def test_evict_on_two_streams_equals_sequential():
     torch.cuda.synchronize()
     for a, b, c in zip(seq_runs, par_runs, cases):
         _assert_same(a.state(), b.state(), c["seq_len"])
+
+
+@pytest.mark.parametrize("kind,pool", [("sum", 1), ("pool", 5)])
+def test_evict_at_the_slot_limit_matches_oracle(kind, pool):
+    """One head at the library's largest size: 1,048,576 slots (65536 blocks,
+    1024 selection chunks), 8 short of full.  The fused pass (score, the
+    selection shared by 512 workgroups, compaction) against the oracle's
+    chain, as above."""
+    cfg = synth.CONFIGS["tiny_f32"].scaled(B=1, Hkv=1, G=1, W=1, L=(1 << 20) - 8)
+    case = synth.make_case(cfg)
+    assert case["max_blocks"] * 16 == 1 << 20
+    lse32, a32 = _inputs(case, kind)
+    kg, ko, key = KIND[kind]
+    orc = oracle.score(case, lse32, ko, pool, a32=a32)[key]
+    o32 = orc.astype(np.float32)
+    budget, recent = 300_000, 64
+    ov, on = oracle.select(np.nan_to_num(o32, nan=0.0), case["seq_len"], budget, recent)
+    f = Run(case, free_prefix=0)
+    f.fused(kind, lse32, a32, pool, budget, recent)
+    st = f.state()
+    new, ofl, ofc, ostats = oracle.compact(case, ov, on, score_row=np.nan_to_num(o32, nan=0.0),
+                                           free_list=np.full(case["num_blocks"] + 8, -1, np.int32),
+                                           free_count=0)
+    nd = check_eviction_vs_oracle_chain(case, st, ov, on, new, ofl, ofc, ostats, o32,
+                                        TOL[cfg.dtype])
+    assert int(st["stats"][0]) == (case["seq_len"][0, 0] + 15) // 16 - (budget + 15) // 16
+    print(f"slot limit, {kind}: {nd} heads with victims differing inside the tolerance band",
+          flush=True)
