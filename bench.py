@@ -1448,7 +1448,8 @@ def cpu_baseline(case, cfg, kind):
     tokens = cfg.L * len(sample) / cfg.Hkv   # scored tokens the sample covers
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(sample)} of {units} KV heads (full context {cfg.L}); "
-                      f"{dt:.1f} s of score+select+compact", **host_cpu()}
+                      f"{dt:.1f} s of score+select+compact on {threads} threads "
+                      f"(about {dt * threads:.0f} thread-seconds)", **host_cpu()}
 
 
 if __name__ == "__main__":
